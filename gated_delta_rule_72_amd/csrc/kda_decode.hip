@@ -1,0 +1,121 @@
+// kda_decode.hip -- one recurrent KDA step per (sequence, head), streaming the
+// state from HBM exactly once.
+//
+// Page "Kimi (AI)", section "Kimi Delta Attention (KDA)": the state is d_v x d_k
+// (rows are value channels, the forget gate diag(alpha_t) scales rows), so each
+// row s_i evolves on its own:
+//     a_i = s_i . k          (old row; the prediction is alpha_i a_i)
+//     c_i = s_i . q
+//     u_i = beta (v_i - alpha_i a_i)
+//     s_i <- alpha_i s_i + u_i k
+//     o_i = s_i(new) . q = alpha_i c_i + u_i (k . q)
+// so one read and one write of S suffice; the read-out uses the updated state.
+//
+// Layout of the work: one 256-thread workgroup per (sequence, head).  Eight
+// consecutive lanes own one row; lane j of the group holds the float4 chunks
+// j, j+8, j+16, ... of the row, so each load instruction of the group covers a
+// contiguous 128-byte line.  All state loads of a thread are issued before any
+// arithmetic, keeping D_V*D_K*4/256 bytes per thread in flight.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T, int D_K, int D_V>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    float* __restrict__ S, T* __restrict__ o) {
+    constexpr int ROWS_PER_PASS = 256 / 8;          // 32 row slots
+    constexpr int P = D_V / ROWS_PER_PASS;          // rows per thread
+    constexpr int M = D_K / 32;                     // float4 chunks per lane per row
+    static_assert(D_V % ROWS_PER_PASS == 0 && D_K % 32 == 0, "unsupported head size");
+
+    const int64_t head = blockIdx.x;                // (b * H + h)
+    const int lane8 = threadIdx.x & 7;
+    const int slot = threadIdx.x >> 3;
+
+    float* Sh = S + head * (int64_t)(D_V * D_K);
+    const T* qh = q + head * D_K;
+    const T* kh = k + head * D_K;
+
+    // state rows first: the bulk of the traffic
+    f32x4 s[P][M];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const float* row = Sh + (int64_t)(slot + p * ROWS_PER_PASS) * D_K;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            s[p][m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row) + lane8 + 8 * m);
+    }
+    f32x4 kk[M], qq[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        kk[m] = Elem<T>::load4(kh + 4 * (lane8 + 8 * m));
+        qq[m] = Elem<T>::load4(qh + 4 * (lane8 + 8 * m));
+    }
+    float vi[P], ai[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int i = slot + p * ROWS_PER_PASS;
+        vi[p] = Elem<T>::load(v + head * D_V + i);
+        ai[p] = alpha[head * D_V + i];
+    }
+    const float bt = beta[head];
+
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        kq += kk[m][0] * qq[m][0] + kk[m][1] * qq[m][1] + kk[m][2] * qq[m][2] + kk[m][3] * qq[m][3];
+    kq = sum8(kq);
+
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a += s[p][m][e] * kk[m][e];
+                c += s[p][m][e] * qq[m][e];
+            }
+        }
+        a = sum8(a);
+        c = sum8(c);
+        const float u = bt * (vi[p] - ai[p] * a);
+        float* row = Sh + (int64_t)(slot + p * ROWS_PER_PASS) * D_K;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            f32x4 n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n[e] = ai[p] * s[p][m][e] + u * kk[m][e];
+            __builtin_nontemporal_store(n, reinterpret_cast<f32x4*>(row) + lane8 + 8 * m);
+        }
+        if (lane8 == 0) Elem<T>::store(o + head * D_V + slot + p * ROWS_PER_PASS, ai[p] * c + u * kq);
+    }
+}
+
+template <typename T, int D_K, int D_V>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t heads = (int64_t)a.batch * a.n_heads;
+    if (heads == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_step_kernel<T, D_K, D_V>), dim3((unsigned)heads), dim3(256), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.alpha, a.beta, a.S, static_cast<T*>(a.o));
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_decode_t<T, 128, 128>(a, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_decode_t<T, 64, 64>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_decode_t<T, 128, 64>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_decode_t<T, 64, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_decode_dt<uint16_t>(a, stream) : launch_decode_dt<float>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,51 @@
+// kda_internal.h -- argument bundles and launcher declarations between the
+// C ABI layer (kda_api.hip) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* S;
+    void* o;
+    int32_t batch, n_heads, d_k, d_v;
+    bool bf16;
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* S0;           // may be null (zeros)
+    const int32_t* cu_seqlens;  // may be null (equal lengths)
+    int32_t n_seq, n_tok, n_heads, d_k, d_v;
+    bool bf16;
+    void* o;
+    float* S_T;                // may be null
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Chunk length of the chunkwise prefill (tokens solved together).
+constexpr int PREFILL_CHUNK_BF16 = 64;
+constexpr int PREFILL_CHUNK_F32 = 32;
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_valu_bf16(const PrefillArgs& a, hipStream_t stream);
+
+// Workspace bytes the prefill launchers need (the varlen schedule).
+size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
+
+}  // namespace kda

@@ -1,0 +1,156 @@
+"""Python binding of libkda: the C ABI of include/kda.h, one function per entry point.
+
+Argument marshalling only -- every step of the computation runs in the HIP
+kernels of libkda.so.  Tensors are torch tensors on the GPU (PyTorch provides
+device memory and the current stream); there is no CPU fallback, and a missing
+library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_DEVICE = 3
+KDA_ERR_WORKSPACE = 4
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+
+EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
+            "kda_decode_step")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so with argument types set (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libkda.so not found at {LIB_PATH}; build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.kda_abi_version.restype = ctypes.c_int
+    L.kda_abi_version.argtypes = []
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_prefill_workspace_size.restype = sz
+    L.kda_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    L.kda_prefill.restype = ctypes.c_int
+    L.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                              vp, vp, vp, sz, vp]
+    L.kda_decode_step.restype = ctypes.c_int
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().kda_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(status).decode()
+
+
+def workspace_size(n_seq: int, n_tok: int, n_heads: int, d_k: int, d_v: int, dtype_code: int) -> int:
+    return int(lib().kda_prefill_workspace_size(n_seq, n_tok, n_heads, d_k, d_v, dtype_code))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkda takes GPU tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libkda takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def kda_prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *, n_seq: Optional[int] = None,
+                o=None, S_T=None, want_state: bool = True, workspace=None):
+    """Chunkwise KDA prefill over packed sequences.
+
+    q, k: [n_tok, H, d_k]; v: [n_tok, H, d_v] (bf16 or f32, same dtype)
+    alpha: [n_tok, H, d_v] f32; beta: [n_tok, H] f32
+    S0: [n_seq, H, d_v, d_k] f32 or None (zeros)
+    cu_seqlens: int32 [n_seq+1] on the GPU, or None with n_seq equal sequences
+    (n_seq defaults to 1).  Returns (o, S_T); S_T is None if want_state is
+    False.  S_T may be passed as S0 for an in-place continuation.
+    """
+    torch = _torch()
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        n_seq = cu_seqlens.shape[0] - 1
+    elif n_seq is None:
+        n_seq = S0.shape[0] if S0 is not None else 1
+    if o is None:
+        o = torch.empty((n_tok, H, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
+    ws_bytes = workspace_size(n_seq, n_tok, H, dk, dv, dt)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                           _ptr(cu_seqlens), n_seq, n_tok, H, dk, dv, dt, _ptr(o), _ptr(S_T),
+                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                           _stream(q))
+    if st != KDA_OK:
+        raise KdaError("kda_prefill", st)
+    return o, S_T
+
+
+def kda_decode_step(q, k, v, alpha, beta, S, o=None):
+    """One decode step for every (sequence, head): S is updated in place.
+
+    q, k: [B, H, d_k]; v: [B, H, d_v]; alpha: [B, H, d_v] f32; beta: [B, H] f32;
+    S: [B, H, d_v, d_k] f32.  Returns o [B, H, d_v] in q's dtype.
+    """
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o),
+                               B, H, dk, dv, dt, _stream(q))
+    if st != KDA_OK:
+        raise KdaError("kda_decode_step", st)
+    return o

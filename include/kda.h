@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of libkda, Kimi Delta Attention (KDA) prefill and decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Kimi (AI)", section "Kimi Delta Attention (KDA)"):
+ * per (sequence, head) a memory matrix S of d_v x d_k float32 values -- rows
+ * index value channels, columns key channels, as in the naive linear-attention
+ * equation S_t = sum_i v_i k_i^T of that section -- is carried through the
+ * section's three steps for every token t:
+ *     forget gating    S~  = diag(alpha_t) S_{t-1}     (alpha_t scales rows)
+ *     predict          v~  = S~ k_t
+ *     memory updating  S_t = S~ + beta_t (v_t - v~) k_t^T
+ * and the output is the linear-attention read-out o_t = S_t q_t, taken with
+ * the updated state.  No 1/sqrt(d_k) or other scaling is applied to q or k.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, contiguous
+ *     in the layouts given below and 16-byte aligned.  The library keeps no
+ *     device memory of its own between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream) and return as soon as the work is enqueued.  The library is
+ *     reentrant; calls on different streams may run concurrently if their
+ *     buffers do not overlap.
+ *   - Arguments are validated on the host before any HIP call.  An invalid
+ *     argument returns an error status and enqueues nothing.  A failed kernel
+ *     launch returns KDA_ERR_DEVICE.  On any error the contents of the
+ *     outputs are undefined.  Nothing aborts the process.
+ *   - NaN and Inf inputs are not checked; they propagate.
+ *   - d_k and d_v must each be 64 or 128.
+ *   - alpha is taken as given (the gate after its activation); the kernels
+ *     assume that the sum of log(alpha) over any 64 consecutive tokens of a
+ *     value channel stays above -80 (a decay factor of ~1e-35); alpha == 0
+ *     exactly is outside that domain for prefill, and is exact for decode.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, bad cu_seqlens shape */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k = 96) */
+    KDA_ERR_DEVICE = 3,           /* a HIP call or kernel launch failed */
+    KDA_ERR_WORKSPACE = 4         /* workspace missing or smaller than kda_prefill_workspace_size */
+} kda_status;
+
+typedef enum {
+    KDA_DTYPE_F32 = 0,  /* q, k, v and o are float32 */
+    KDA_DTYPE_BF16 = 1  /* q, k, v and o are bfloat16; o is rounded to nearest even */
+} kda_dtype;
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/*
+ * Bytes of device workspace kda_prefill needs for these sizes (0 is possible).
+ * Returns 0 as well for sizes that kda_prefill would reject.
+ */
+size_t kda_prefill_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                  int32_t d_k, int32_t d_v, kda_dtype dt);
+
+/*
+ * Prefill: runs every token of n_seq packed sequences through the recurrence
+ * (chunkwise: each chunk of consecutive tokens is solved in parallel, the
+ * state is carried from chunk to chunk), writes every output o_t and the final
+ * state of every (sequence, head).
+ *
+ *   q, k        [n_tok, n_heads, d_k]   dtype dt
+ *   v           [n_tok, n_heads, d_v]   dtype dt
+ *   alpha       [n_tok, n_heads, d_v]   float32, forget gate per value channel
+ *   beta        [n_tok, n_heads]        float32, one scalar per (token, head)
+ *   S0          [n_seq, n_heads, d_v, d_k] float32 row-major, or NULL = zeros
+ *   cu_seqlens  device int32 [n_seq+1]: sequence n owns tokens
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1.  Must start at 0, be
+ *               nondecreasing and end at n_tok (not checked on the device:
+ *               the host never reads it, so no synchronisation is implied).
+ *               NULL = n_seq sequences of n_tok/n_seq tokens each (n_tok must
+ *               then be a multiple of n_seq).  Empty sequences are allowed and
+ *               give S_T = S0.
+ *   o           [n_tok, n_heads, d_v]   dtype dt (written)
+ *   S_T         [n_seq, n_heads, d_v, d_k] float32 (written), or NULL.  May be
+ *               the same buffer as S0 (in-place continuation); any other
+ *               overlap between inputs and outputs is not allowed.
+ *   workspace   device scratch of at least kda_prefill_workspace_size(...)
+ *               bytes (may be NULL when that size is 0); its contents need no
+ *               initialisation and are clobbered.
+ * n_seq >= 1, n_tok >= 0, n_heads >= 1.
+ */
+kda_status kda_prefill(const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta,
+                       const float* S0, const int32_t* cu_seqlens,
+                       int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                       int32_t d_k, int32_t d_v, kda_dtype dt,
+                       void* o, float* S_T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode step: one new token for each of `batch` sequences (recurrent form,
+ * constant memory per sequence -- the section's "linear time and constant
+ * memory").  The state is read once and written once, in place.
+ *
+ *   q, k    [batch, n_heads, d_k]  dtype dt
+ *   v       [batch, n_heads, d_v]  dtype dt
+ *   alpha   [batch, n_heads, d_v]  float32
+ *   beta    [batch, n_heads]       float32
+ *   S       [batch, n_heads, d_v, d_k] float32, in/out: S_{t-1} in, S_t out
+ *   o       [batch, n_heads, d_v]  dtype dt (written): o_t = S_t q_t
+ * batch >= 0 (0 enqueues nothing), n_heads >= 1.  S must not overlap any
+ * other argument.
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta,
+                           float* S, void* o,
+                           int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
+                           kda_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,113 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+symbol include/kda.h declares, and rejects bad arguments on the host before any
+HIP call (these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_72_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+A = 0x10000  # a 16-byte aligned fake device address; never dereferenced (rejected on host)
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return kda.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = declared_symbols()
+    assert set(syms) == set(kda.EXPORTED)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_version_and_status_strings(L):
+    assert L.kda_abi_version() == 1
+    for code, name in [(0, "KDA_OK"), (1, "KDA_ERR_INVALID_ARGUMENT"), (2, "KDA_ERR_UNSUPPORTED"),
+                       (3, "KDA_ERR_DEVICE"), (4, "KDA_ERR_WORKSPACE")]:
+        assert L.kda_status_string(code).decode() == name
+    assert L.kda_status_string(99).decode() == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_size(L):
+    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 1) == 256
+    assert L.kda_prefill_workspace_size(65, 1000, 16, 128, 128, 1) == 512
+    assert L.kda_prefill_workspace_size(0, 1000, 16, 128, 128, 1) == 0
+    assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
+
+
+def prefill(L, **kw):
+    args = dict(q=A, k=A + 0x100000, v=A + 0x200000, alpha=A + 0x300000, beta=A + 0x400000,
+                S0=None, cu=None, n_seq=2, n_tok=64, H=2, dk=64, dv=64, dt=1,
+                o=A + 0x500000, S_T=A + 0x600000, ws=A + 0x700000, ws_bytes=256, stream=None)
+    args.update(kw)
+    return L.kda_prefill(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S0"],
+                         args["cu"], args["n_seq"], args["n_tok"], args["H"], args["dk"], args["dv"],
+                         args["dt"], args["o"], args["S_T"], args["ws"], args["ws_bytes"],
+                         args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(n_seq=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(n_tok=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(n_tok=63), kda.KDA_ERR_INVALID_ARGUMENT),          # not a multiple of n_seq, no cu_seqlens
+    (dict(q=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(k=A + 0x100008), kda.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    (dict(S_T=A + 0x600004), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(o=A), kda.KDA_ERR_INVALID_ARGUMENT),              # o overlaps q
+    (dict(S0=A + 0x600000 + 16, S_T=A + 0x600000), kda.KDA_ERR_INVALID_ARGUMENT),  # partial overlap
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+    (dict(ws_bytes=128), kda.KDA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_on_host(L, kw, status):
+    assert prefill(L, **kw) == status
+
+
+def decode(L, **kw):
+    args = dict(q=A, k=A + 0x100000, v=A + 0x200000, alpha=A + 0x300000, beta=A + 0x400000,
+                S=A + 0x1000000, o=A + 0x500000, B=4, H=2, dk=128, dv=128, dt=1, stream=None)
+    args.update(kw)
+    return L.kda_decode_step(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S"],
+                             args["o"], args["B"], args["H"], args["dk"], args["dv"], args["dt"],
+                             args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(S=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(alpha=A + 0x300002), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(S=A), kda.KDA_ERR_INVALID_ARGUMENT),              # S overlaps q
+    (dict(o=A + 0x1000000 + 64), kda.KDA_ERR_INVALID_ARGUMENT),  # o inside S
+    (dict(B=0), kda.KDA_OK),                                # nothing to do, nothing enqueued
+])
+def test_decode_rejects_on_host(L, kw, status):
+    assert decode(L, **kw) == status
+
+
+def test_binding_refuses_cpu_tensors(L):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 64, 64))

@@ -1,0 +1,175 @@
+"""GPU parity of kda_prefill against the fp64 oracle (through the C ABI).
+
+Small cases run the oracle on everything; the full-size workloads run the GPU
+on the whole problem, in the launch configuration the benchmark times, and the
+oracle on sampled (sequence, head) pairs (heads are independent, so a sampled
+pair is reproduced exactly by the oracle run on that pair alone)."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_72_amd import inputs as I
+from tests import helpers as Hh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_72_amd import kda
+    kda.lib()
+    return torch
+
+
+def gpu_prefill(torch, inp, varlen=True, S_T_alias=False, want_state=True):
+    from gated_delta_rule_72_amd import kda
+    d = Hh.upload_prefill(inp)
+    cu = d["cu_seqlens"] if varlen else None
+    S_T = None
+    if S_T_alias:
+        assert d["S0"] is not None
+        S_T = d["S0"]
+    o, S = kda.kda_prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], cu,
+                           n_seq=inp.n_seq, S_T=S_T, want_state=want_state)
+    torch.cuda.synchronize()
+    return Hh.from_device(o), (None if S is None else Hh.from_device(S))
+
+
+def check_full(inp, o, S):
+    import oracle
+    o_ref, S_ref = oracle.prefill(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta,
+                                  None if inp.S0 is None else inp.S0.astype(np.float64),
+                                  inp.cu_seqlens)
+    tol = Hh.tol_for(inp.dtype)
+    Hh.check("o", o, o_ref, Hh.o_slices(inp.cu_seqlens, inp.H), tol)
+    if S is not None:
+        Hh.check("S_T", S, S_ref, Hh.s_slices(inp.n_seq, inp.H), tol)
+
+
+def check_sampled(inp, o, S, pairs):
+    tol = Hh.tol_for(inp.dtype)
+    by_seq = {}
+    for n, h in pairs:
+        by_seq.setdefault(n, []).append(h)
+    for n, hs in sorted(by_seq.items()):
+        ref = Hh.oracle_prefill_subset(inp, [n], sorted(set(hs)))
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        for h in sorted(set(hs)):
+            o_ref, S_ref = ref[(n, h)]
+            if e > s:
+                Hh.check(f"o[seq={n},h={h}]", o[s:e, h], o_ref, [(Ellipsis,)], tol)
+            Hh.check(f"S_T[seq={n},h={h}]", S[n, h], S_ref, [(Ellipsis,)], tol)
+
+
+# ------------------------------------------------------------ small, exhaustive
+@pytest.mark.parametrize("lens,H,dk,dv,dtype,alpha_kind,s0", [
+    ([256], 1, 64, 64, "f32", "sigmoid_n21", 0.0),              # the tiny fp32 workload's shape
+    ([200, 77, 1, 64], 2, 64, 64, "f32", "sigmoid_n21", 0.02),  # ragged tails, len 1
+    ([130, 33], 2, 128, 128, "f32", "exp_softplus", 0.02),
+    ([96], 3, 128, 64, "f32", "exp_softplus", 0.0),
+    ([70], 2, 64, 128, "f32", "exp_softplus", 0.02),
+    ([300, 64, 129], 4, 128, 128, "bf16", "exp_softplus", 0.02),
+    ([513], 2, 64, 64, "bf16", "exp_softplus", 0.0),
+    ([191, 2], 3, 128, 64, "bf16", "exp_softplus", 0.02),
+    ([250], 2, 64, 128, "bf16", "sigmoid_n21", 0.02),
+    ([0, 100, 0, 65], 2, 128, 128, "bf16", "exp_softplus", 0.02),  # empty sequences
+])
+def test_prefill_matches_oracle(torch_cuda, lens, H, dk, dv, dtype, alpha_kind, s0):
+    print(f"prefill lens={lens} H={H} dk={dk} dv={dv} {dtype} {alpha_kind} s0={s0}", flush=True)
+    inp = I.make_prefill(9000 + sum(lens) + H, lens, H, dk, dv, dtype, alpha_kind, s0)
+    o, S = gpu_prefill(torch_cuda, inp)
+    check_full(inp, o, S)
+
+
+def test_tiny_fp32_workload(torch_cuda):
+    inp = I.workload_prefill(1)
+    print("prefill workload 1 (tiny fp32)", flush=True)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=False)
+    check_full(inp, o, S)
+
+
+def test_single_layer_workload(torch_cuda):
+    inp = I.workload_prefill(2)
+    print("prefill workload 2 (single layer, H=8, T=4096)", flush=True)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=False)
+    check_full(inp, o, S)
+
+
+def test_dense_and_varlen_calls_agree(torch_cuda):
+    inp = I.make_prefill(31, [256, 256, 256], 4, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill dense vs varlen", flush=True)
+    o1, S1 = gpu_prefill(torch_cuda, inp, varlen=False)
+    o2, S2 = gpu_prefill(torch_cuda, inp, varlen=True)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_in_place_state_and_no_state(torch_cuda):
+    inp = I.make_prefill(32, [190, 70], 2, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill S_T aliasing S0, and S_T = NULL", flush=True)
+    o1, S1 = gpu_prefill(torch_cuda, inp)
+    o2, S2 = gpu_prefill(torch_cuda, inp, S_T_alias=True)
+    o3, _ = gpu_prefill(torch_cuda, inp, want_state=False)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2) and np.array_equal(o1, o3)
+
+
+def test_deterministic(torch_cuda):
+    inp = I.make_prefill(33, [333, 64], 4, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill run twice", flush=True)
+    o1, S1 = gpu_prefill(torch_cuda, inp)
+    o2, S2 = gpu_prefill(torch_cuda, inp)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_split_prefill_and_decode_continue_the_state(torch_cuda):
+    """prefill(T1) then prefill(T2, S0=S_T) == prefill(T1+T2); T decode steps == prefill(T)."""
+    from gated_delta_rule_72_amd import kda
+    torch = torch_cuda
+    T, T1 = 200, 136
+    inp = I.make_prefill(34, [T], 2, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill split vs whole, decode vs prefill", flush=True)
+    d = Hh.upload_prefill(inp)
+    o, S = kda.kda_prefill(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], None)
+    oa, Sa = kda.kda_prefill(d["q"][:T1], d["k"][:T1], d["v"][:T1], d["alpha"][:T1].contiguous(),
+                             d["beta"][:T1].contiguous(), d["S0"], None)
+    ob, Sb = kda.kda_prefill(d["q"][T1:], d["k"][T1:], d["v"][T1:], d["alpha"][T1:].contiguous(),
+                             d["beta"][T1:].contiguous(), Sa, None)
+    Sd = d["S0"].clone()
+    od = [kda.kda_decode_step(d["q"][t:t + 1].contiguous(), d["k"][t:t + 1].contiguous(),
+                              d["v"][t:t + 1].contiguous(), d["alpha"][t:t + 1].contiguous(),
+                              d["beta"][t:t + 1].contiguous(), Sd) for t in range(T)]
+    torch.cuda.synchronize()
+    o, S = Hh.from_device(o), Hh.from_device(S)
+    osplit = np.concatenate([Hh.from_device(oa), Hh.from_device(ob)])
+    tol = Hh.TOL_BF16
+    sl = [(slice(None), h) for h in range(2)]
+    Hh.check("o split vs whole", osplit, o, sl, tol)
+    Hh.check("S split vs whole", Hh.from_device(Sb), S, Hh.s_slices(1, 2), tol)
+    odec = np.concatenate([Hh.from_device(x) for x in od])
+    Hh.check("o decode vs prefill", odec, o, sl, tol)
+    Hh.check("S decode vs prefill", Hh.from_device(Sd)[None], S, Hh.s_slices(1, 2), tol)
+
+
+# ----------------------------------------------------------- full size, sampled
+def test_batched_workload_sampled(torch_cuda):
+    inp = I.workload_prefill(3)
+    print("prefill workload 3 (B=4, H=32, T=8192) full size, sampled oracle", flush=True)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=False)
+    rng = np.random.default_rng(3)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, 4, 6), rng.integers(0, 32, 6))]
+    pairs += [(0, 0), (3, 31)]
+    check_sampled(inp, o, S, pairs)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+def test_varlen_workload_sampled(torch_cuda):
+    inp = I.workload_prefill(5)
+    print(f"prefill workload 5 (64 packed sequences, {inp.n_tok} tokens, H=16), sampled oracle",
+          flush=True)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=True)
+    lens = np.diff(inp.cu_seqlens)
+    shortest, longest = int(np.argmin(lens)), int(np.argmax(lens))
+    pairs = [(shortest, 0), (shortest, 15), (longest, 7), (5, 3), (40, 12)]
+    check_sampled(inp, o, S, pairs)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
