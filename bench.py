@@ -1,0 +1,236 @@
+"""Benchmark of the KDA hot path on one MI355X: prefill tokens/s (the batched
+prefill workload, H=32, d=128) and decode state GB/s, each against its roofline.
+
+One "step" is one kda_prefill call over the batched prefill workload
+(B=4 sequences x T=8192 tokens, H=32 heads, d_k=d_v=128, bf16 q/k/v, fp32
+alpha/beta/state, S0 ~ N(0, 0.02^2)), inputs resident in HBM.  Prints one JSON
+line.  The decode workload (B=256, H=32, 1024 successive steps, 537 MB fp32
+state) is timed in the same run and reported under "decode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/sec (H=32,d=128) + decode state GB/s; % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PREFILL_BYTES_PER_HEAD_TOKEN = 768 + 512 + 4 + 256   # q,k,v bf16 + alpha fp32 + beta + o bf16
+PREFILL_FLOPS_PER_HEAD_TOKEN = 180224                # nominal chunked flops at C=64, d=128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--decode-steps", type=int, default=1024)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def upload(x, dtype, dev):
+    import torch
+    if dtype == "bf16" and x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def rel(a, b):
+    d = a - b
+    return float(np.abs(d).max() / np.abs(b).max()), float(np.linalg.norm(d) / np.linalg.norm(b))
+
+
+def bench_prefill(args, torch, kda, I):
+    dev = "cuda:0"
+    wid = 3
+    w = I.WORKLOADS[wid]
+    t0 = time.time()
+    inp = I.workload_prefill(wid)
+    log(f"[bench] generated prefill inputs in {time.time() - t0:.1f}s")
+    q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+    alpha, beta = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev)
+    S0 = upload(inp.S0, "f32", dev)
+    B, T, H, d = w["n_seq"], w["T"], w["H"], w["dk"]
+    o = torch.empty((B * T, H, d), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(launch_ms))
+    head_tokens = B * T * H
+    alg_bytes = head_tokens * PREFILL_BYTES_PER_HEAD_TOKEN + 2 * B * H * d * d * 4
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    nominal_tflops = head_tokens * PREFILL_FLOPS_PER_HEAD_TOKEN / (avg_ms * 1e-3) / 1e12
+    res = dict(
+        tokens_per_s=B * T * args.steps / wall, ms_per_step=wall * 1e3 / args.steps,
+        launch_ms=dict(avg=avg_ms, min=float(np.min(launch_ms)), max=float(np.max(launch_ms))),
+        roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="prefill (chunkwise, fused)", alg_bytes_per_launch=alg_bytes,
+                      mfma_nominal_tflops=round(nominal_tflops, 1),
+                      mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
+    )
+    return res, inp, o, S_T
+
+
+def cpu_baseline_prefill(inp, o_gpu, S_gpu):
+    """The oracle on a bounded sample: sequence 0, all heads, all 8192 tokens."""
+    import oracle
+    s, e = int(inp.cu_seqlens[0]), int(inp.cu_seqlens[1])
+    q, k, v = (inp.f32(n)[s:e] for n in ("q", "k", "v"))
+    a, b = inp.alpha[s:e], inp.beta[s:e]
+    S0 = inp.S0[0:1].astype(np.float64)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    o_ref, S_ref = oracle.prefill(q, k, v, a, b, S0)
+    dt = time.perf_counter() - t0
+    tokens = e - s
+    og = o_gpu[s:e].float().cpu().numpy().astype(np.float64)
+    Sg = S_gpu[0:1].cpu().numpy().astype(np.float64)
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for h in range(inp.H):
+        m, r = rel(og[:, h], o_ref[:, h])
+        ms, rs = rel(Sg[0, h], S_ref[0, h])
+        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms), max(worst[3], rs)]
+    cpu = dict(value=round(tokens / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
+               sample=f"sequence 0 of the batched prefill workload: {tokens} tokens x {inp.H} heads "
+                      f"(1/{inp.n_seq} of a step), fp64 C oracle, {dt:.2f}s wall",
+               cpu_model=platform.processor() or platform.machine())
+    parity = dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
+                  scope="sequence 0, all 32 heads, worst (sequence, head) slice")
+    return cpu, parity
+
+
+def bench_decode(args, torch, kda, I):
+    dev = "cuda:0"
+    w = I.WORKLOADS[4]
+    n = args.decode_steps
+    t0 = time.time()
+    dec = I.workload_decode(4, n_steps=n)
+    log(f"[bench] generated {n} decode steps in {time.time() - t0:.1f}s")
+    q, k, v = (upload(getattr(dec, x), "bf16", dev) for x in ("q", "k", "v"))
+    alpha, beta = upload(dec.alpha, "f32", dev), upload(dec.beta, "f32", dev)
+    S_init = upload(dec.S0, "f32", dev)
+    S = S_init.clone()
+    B, H, d = w["B"], w["H"], w["dk"]
+    outs = torch.empty((n, B, H, d), dtype=torch.bfloat16, device=dev)
+    qs, ks, vs, as_, bs, os_ = ([x[t] for t in range(n)] for x in (q, k, v, alpha, beta, outs))
+    # warm-up on a scratch state
+    Sw = S_init.clone()
+    for t in range(min(8, n)):
+        kda.kda_decode_step(qs[t], ks[t], vs[t], as_[t], bs[t], Sw, o=os_[t])
+    torch.cuda.synchronize()
+    S.copy_(S_init)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for t in range(n):
+        kda.kda_decode_step(qs[t], ks[t], vs[t], as_[t], bs[t], S, o=os_[t])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1)
+    state_bytes = B * H * d * d * 4
+    step_bytes = 2 * state_bytes + B * H * PREFILL_BYTES_PER_HEAD_TOKEN
+    steps_per_s = n / (ms * 1e-3)
+    gbs = step_bytes * steps_per_s / 1e9
+    res = dict(
+        workload=f"decode B={B} H={H} d_k=d_v={d} bf16, {n} successive steps, fp32 state in HBM",
+        steps_per_s=round(steps_per_s, 1), tokens_per_s=round(steps_per_s * B, 1),
+        ms_total=round(ms, 3), wall_s=round(wall, 3), us_per_step=round(ms * 1e3 / n, 2),
+        state_GBps=round(2 * state_bytes * steps_per_s / 1e9, 1),
+        roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_step",
+                      alg_bytes_per_launch=step_bytes),
+    )
+    # parity on sampled (b, h) pairs over all n steps
+    import oracle
+    rng = np.random.default_rng(4)
+    picks = list(zip(rng.integers(0, B, 4).tolist(), rng.integers(0, H, 4).tolist()))
+    og = outs.float().cpu().numpy()
+    Sg = S.cpu().numpy()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for b, h in picks:
+        sub = lambda x: x[:, b:b + 1, h:h + 1]
+        o_ref, S_ref = oracle.decode(sub(dec.f32("q")), sub(dec.f32("k")), sub(dec.f32("v")),
+                                     sub(dec.alpha), sub(dec.beta),
+                                     dec.S0[b:b + 1, h:h + 1].astype(np.float64))
+        m, r = rel(og[:, b, h].astype(np.float64), o_ref[:, 0, 0])
+        ms_, rs = rel(Sg[b, h].astype(np.float64), S_ref[0, 0])
+        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms_), max(worst[3], rs)]
+    res["parity"] = dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2],
+                         S_rms_rel=worst[3], scope=f"{len(picks)} sampled (b, h) pairs, all steps")
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU launch: run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gated_delta_rule_72_amd import inputs as I
+    from gated_delta_rule_72_amd import kda
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kda.lib()
+    pre, inp, o, S_T = bench_prefill(args, torch, kda, I)
+    log(f"[bench] prefill: {pre['tokens_per_s']:.4g} tokens/s, kernel {pre['launch_ms']['avg']:.3f} ms")
+    line = dict(
+        metric=METRIC, value=round(pre["tokens_per_s"], 1), unit="tokens/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=round(pre["ms_per_step"], 4),
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="batched_prefill: B=4 sequences x T=8192 tokens, H=32, d_k=d_v=128, "
+                             "bf16 q/k/v, fp32 alpha/beta/state, S0~N(0,0.02^2)",
+                    global_batch=4, seq_len=8192, heads=32, d_k=128, d_v=128, chunk=64),
+        roofline=pre["roofline"], launch_ms=pre["launch_ms"],
+    )
+    if not args.no_cpu:
+        cpu, parity = cpu_baseline_prefill(inp, o, S_T)
+        line["cpu_baseline"] = cpu
+        line["parity"] = parity
+        log(f"[bench] oracle: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
+    del inp, o, S_T
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = bench_decode(args, torch, kda, I)
+        log(f"[bench] decode: {line['decode']['steps_per_s']:.4g} steps/s, "
+            f"{line['decode']['roofline']['achieved']:.4g} GB/s")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

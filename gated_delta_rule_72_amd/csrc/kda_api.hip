@@ -8,9 +8,11 @@
 
 namespace {
 
+// Vector-loaded tensors need 16-byte alignment; beta and cu_seqlens are read
+// as scalars and need only their element alignment.
 constexpr size_t kAlign = 16;
 
-bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+bool aligned(const void* p, size_t a = kAlign) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool supported_dim(int32_t d) { return d == 64 || d == 128; }
 
@@ -60,9 +62,11 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const float*
     if (!cu_seqlens && (n_tok % n_seq) != 0) return KDA_ERR_INVALID_ARGUMENT;
     const bool has_tokens = n_tok > 0;
     if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
-    const void* ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_T, workspace};
+    const void* ptrs[] = {q, k, v, alpha, S0, o, S_T, workspace};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return KDA_ERR_INVALID_ARGUMENT;
+    if ((beta && !aligned(beta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return KDA_ERR_INVALID_ARGUMENT;
     // outputs may not overlap inputs, except S_T == S0 exactly
     const size_t eb = elem_bytes(dt);
     const size_t nt = static_cast<size_t>(n_tok), nh = static_cast<size_t>(n_heads);
@@ -99,9 +103,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
     if (batch == 0) return KDA_OK;
     if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARGUMENT;
-    const void* ptrs[] = {q, k, v, alpha, beta, S, o};
+    const void* ptrs[] = {q, k, v, alpha, S, o};
     for (const void* p : ptrs)
         if (!aligned(p)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(beta, 4)) return KDA_ERR_INVALID_ARGUMENT;
     const size_t eb = elem_bytes(dt);
     const size_t heads = static_cast<size_t>(batch) * n_heads;
     const size_t s_bytes = heads * d_v * d_k * 4, o_bytes = heads * d_v * eb;

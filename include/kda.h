@@ -15,8 +15,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, contiguous
- *     in the layouts given below and 16-byte aligned.  The library keeps no
- *     device memory of its own between calls.
+ *     in the layouts given below and 16-byte aligned, except beta and
+ *     cu_seqlens, which need 4-byte alignment.  The library keeps no device
+ *     memory of its own between calls.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream) and return as soon as the work is enqueued.  The library is
  *     reentrant; calls on different streams may run concurrently if their

@@ -98,6 +98,7 @@ def decode(L, **kw):
     (dict(dk=32), kda.KDA_ERR_UNSUPPORTED),
     (dict(S=None), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(alpha=A + 0x300002), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=A + 0x400002), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(S=A), kda.KDA_ERR_INVALID_ARGUMENT),              # S overlaps q
     (dict(o=A + 0x1000000 + 64), kda.KDA_ERR_INVALID_ARGUMENT),  # o inside S
     (dict(B=0), kda.KDA_OK),                                # nothing to do, nothing enqueued

@@ -148,7 +148,7 @@ def test_split_prefill_and_decode_continue_the_state(torch_cuda):
     Hh.check("S split vs whole", Hh.from_device(Sb), S, Hh.s_slices(1, 2), tol)
     odec = np.concatenate([Hh.from_device(x) for x in od])
     Hh.check("o decode vs prefill", odec, o, sl, tol)
-    Hh.check("S decode vs prefill", Hh.from_device(Sd)[None], S, Hh.s_slices(1, 2), tol)
+    Hh.check("S decode vs prefill", Hh.from_device(Sd), S, Hh.s_slices(1, 2), tol)
 
 
 # ----------------------------------------------------------- full size, sampled
