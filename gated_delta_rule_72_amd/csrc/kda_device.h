@@ -28,6 +28,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats to packed bf16 (low half = a), round to nearest even, on the
+// hardware converter (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
+}
+
+// hi + lo split of two floats: hi = bf16(x), lo = bf16(x - hi); packed pairs.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // Element loaders: float or bf16 (carried as uint16_t) to float.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -74,6 +88,15 @@ __device__ __forceinline__ float sum16(float x) {
     x = sum8(x);
     x += dpp_mov<DPP_ROW_MIRROR>(x);
     return x;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, which makes every wave wait for its outstanding global loads and
+// stores (the next chunk's prefetch, the output stores) at each barrier.
+__device__ __forceinline__ void block_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 }  // namespace kda

@@ -8,25 +8,28 @@
 //   G[t,i] = sum_{s<=t} log alpha[s,i]          (per-row cumulative log-decay)
 //   L      = strictly_lower(diag(beta) K K^T)    (decay-free beta-weighted Gram)
 //   A      = (I + L)^{-1} diag(beta)             (unit-lower WY/UT solve)
-//   U      = A (V (.) e^{-G}) - (A K) S^T        (decay-normalised errors)
+//   U      = A (V (.) e^{-G} - K S^T)            (decay-normalised errors)
 //   O      = e^{G} (.) (Q S^T + tril(Q K^T) U)   (tril keeps the diagonal: o_t = S_t q_t)
 //   S'     = diag(e^{G[C-1,:]}) (S + U^T K)
 // The decayed Gram of value row i is D_i L D_i^{-1} with D_i = diag(e^{G[:,i]}),
 // so one decay-free solve serves every row; the decay moves onto V, O and S as
-// elementwise scalings.  Chunks that cross the end of a sequence are padded
-// with k = q = v = 0, alpha = 1, beta = 0 tokens, which change nothing.
+// elementwise scalings.  Token rows past the end of a sequence read as k = q =
+// v = 0, beta = 0 and log alpha = 0, which change nothing.
 //
 // Work decomposition: one workgroup of 8 waves per (sequence, head, block of
-// 64 value rows); the workgroup walks its sequence chunk by chunk, holding S^T
-// in fp32 MFMA accumulators (one 32x32 tile per wave) across the whole scan,
-// with a bf16 copy in LDS as the operand of Q S^T and W S^T.  The next chunk's
-// q/k/v/alpha/beta are loaded into registers while the current chunk computes.
+// 64 value rows) walks its sequence chunk by chunk, holding S^T in fp32 MFMA
+// accumulators (one 32x32 tile per wave) for the whole scan, with a bf16 copy
+// in LDS as the operand of Q S^T and K S^T.  The S-independent solve runs on
+// waves 0-3 while waves 4-7 form Q S^T and K S^T.  The next chunk's inputs are
+// loaded into registers while the current chunk computes; barriers order LDS
+// only, so those loads (and the output stores) stay in flight across them.
 //
 // Precision: q, k, v are exact bf16 inputs.  Computed operands are carried as
 // hi + lo bf16 pairs (x = hi + lo to ~2^-16 relative) where the error budget
-// needs it -- A, V e^{-G}, U and P = tril(Q K^T) -- and as single bf16 for
-// W = A K and S (the state itself stays fp32).  Products of split operands
-// take three MFMAs (hi*hi + lo*hi + hi*lo).
+// needs it -- A, V e^{-G} - K S^T, U and P = tril(Q K^T) -- and S is a single
+// bf16 copy of the fp32 state.  A product of two split operands takes three
+// MFMAs (hi*hi + lo*hi + hi*lo).  The solve itself runs in fp32 (VALU forward
+// substitution on 16x16 diagonal blocks, fp32 MFMA for the off-diagonal blocks).
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
@@ -39,6 +42,10 @@ constexpr int BV = 64;                 // value rows per workgroup
 constexpr int NW = 8;                  // waves per workgroup
 constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int PAD = 8;                 // bf16 row padding (16 bytes) against bank conflicts
+// word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------- MFMA helpers
 // v_mfma_f32_32x32x16_bf16 operand layout: lane l supplies row (l & 31) of A
@@ -50,12 +57,27 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* base, int pitch, int row0
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
 
+// The same for v_mfma_f32_16x16x32_bf16: row (l & 15), reduction indices 8 * (l >> 4) ...
+__device__ __forceinline__ bf16x8 frag16(const uint16_t* base, int pitch, int row0, int k0, int lane) {
+    const uint16_t* p = base + (row0 + (lane & 15)) * pitch + k0 + 8 * (lane >> 4);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16f(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Accumulator layout of a 32x32 tile: register r of lane l holds
-// D[row = 8*(r/4) + 4*(l>>5) + (r&3)][col = l & 31].
+// D[row = 8*(r/4) + 4*(l>>5) + (r&3)][col = l & 31]; of a 16x16 tile: register
+// r holds D[4*(l>>4) + r][l & 15].
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
@@ -63,44 +85,57 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+// Order this wave's own LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Buffer resource over [p, p + bytes): loads past the end return 0 and stores
+// past the end are dropped, so a chunk's rows beyond its sequence need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
+}
+
 // Shared-memory layout (bytes).  Regions are reused across the phases of a
-// chunk; the comments give each region's tenants in order.
+// chunk; the comments give each region's tenants in order.  Each region is its
+// own __shared__ array, so the compiler knows that accesses to different
+// regions never alias and can move loads ahead of unrelated stores.
 template <int DK>
 struct Smem {
     static constexpr int KP = DK + PAD;     // pitch of [t][j] bf16 rows
     static constexpr int CP = C + PAD;      // pitch of [x][t] bf16 rows (length C)
-    static constexpr int LP = C + 4;        // pitch of C x C fp32 rows
-    static constexpr int max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
-    // R0: K as [t][j] (Gram products) -> solve scratch X fp32 [t][s] -> -W bf16 [t][j]
+    static constexpr int LP = C + 4;        // pitch of [x][t] fp32 rows (length C)
+    static constexpr int mx(int a, int b) { return a > b ? a : b; }
+    static constexpr int HILO = 2 * C * CP * 2;  // a C x C (or BV x C) hi/lo bf16 pair
+    // R0: K [t][j] -> solve temporaries (fp32 32x36) -> A hi/lo [t][s]
     static constexpr int R0 = 0;
-    static constexpr int R0_SZ = max3(C * KP * 2, C * LP * 4, 0);
-    // R1: Q as [t][j]
+    static constexpr int R0_SZ = mx(mx(C * KP * 2, 32 * 36 * 4), HILO);
+    // R1: Q [t][j] -> Y^T hi/lo [i][t]
     static constexpr int R1 = R0 + R0_SZ;
-    static constexpr int R1_SZ = C * KP * 2;
-    // R2: K^T as [j][t]
+    static constexpr int R1_SZ = mx(C * KP * 2, HILO);
+    // R2: K^T [j][t]
     static constexpr int R2 = R1 + R1_SZ;
     static constexpr int R2_SZ = DK * CP * 2;
-    // R3: L fp32 [t][s] -> U^T hi, lo bf16 [i][t]
+    // R3: L fp32 [t][s] -> U^T hi/lo [i][t]
     static constexpr int R3 = R2 + R2_SZ;
-    static constexpr int R3_SZ = max3(C * LP * 4, 2 * BV * CP * 2, 0);
-    // R4: solve temporaries fp32 -> A hi, lo bf16 [t][s]
+    static constexpr int R3_SZ = mx(C * LP * 4, HILO);
+    // R4: (I + L)^{-1} fp32 [t][s]
     static constexpr int R4 = R3 + R3_SZ;
-    static constexpr int R4_SZ = 2 * C * CP * 2;
-    // R5: P = tril(Q K^T) hi, lo bf16 [t][s]
+    static constexpr int R4_SZ = C * LP * 4;
+    // R5: P = tril(Q K^T) hi/lo [t][s]
     static constexpr int R5 = R4 + R4_SZ;
-    static constexpr int R5_SZ = 2 * C * CP * 2;
-    // R6: V^T raw bf16 [i][t] -> X^T = (V e^{-G})^T hi, lo bf16 [i][t]
+    static constexpr int R5_SZ = HILO;
+    // R6: X^T = (V e^{-G})^T fp32 [i][t] -> O bf16 [t][i] (stored at the next chunk)
     static constexpr int R6 = R5 + R5_SZ;
-    static constexpr int R6_SZ = 2 * BV * CP * 2;
+    static constexpr int R6_SZ = mx(BV * LP * 4, C * (BV + PAD) * 2);
     // R7: S bf16 [i][j] (operand copy of the fp32 state)
     static constexpr int R7 = R6 + R6_SZ;
     static constexpr int R7_SZ = BV * KP * 2;
-    // R8: G fp32 [t][i]
+    // R8: G fp32 [t][i] (first the per-part local prefix sums of log alpha)
+    static constexpr int GP = BV + 4;       // pitch of G rows
     static constexpr int R8 = R7 + R7_SZ;
-    static constexpr int R8_SZ = C * BV * 4;
-    // R9: beta [C], gamma [BV], partial scan sums [8][BV]
+    static constexpr int R8_SZ = C * GP * 4;
+    // R9: beta [C], gamma [BV]
     static constexpr int R9 = R8 + R8_SZ;
-    static constexpr int R9_SZ = (C + BV + 8 * BV) * 4;
+    static constexpr int R9_SZ = (C + BV) * 4;
     static constexpr int TOTAL = R9 + R9_SZ;
 };
 
@@ -117,46 +152,53 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, CP = SM::CP, LP = SM::LP;
-    constexpr int JT = DK / 32;          // 32-wide tiles along d_k
-    constexpr int KQ_CHUNKS = C * DK / 8;  // 16-byte pieces of a K (or Q) chunk
-    constexpr int KQ_PER_T = (KQ_CHUNKS + NT - 1) / NT;
-    constexpr int A_CHUNKS = C * BV / 4;   // float4 pieces of an alpha block
-    constexpr int A_PER_T = A_CHUNKS / NT;
-    static_assert(A_CHUNKS % NT == 0 && C * BV / 8 == NT, "thread mapping");
+    constexpr int KP = SM::KP, CP = SM::CP, LP = SM::LP, GP = SM::GP;
+    constexpr int OP = BV + PAD;           // pitch of the staged O rows
+    constexpr int JT = DK / 32;            // 32-wide tiles along d_k
 
-    __shared__ __align__(16) unsigned char smem[SM::TOTAL];
-    uint16_t* Kc = reinterpret_cast<uint16_t*>(smem + SM::R0);
-    float* Xs = reinterpret_cast<float*>(smem + SM::R0);
-    uint16_t* Wn = reinterpret_cast<uint16_t*>(smem + SM::R0);
-    uint16_t* Qc = reinterpret_cast<uint16_t*>(smem + SM::R1);
-    uint16_t* Kt = reinterpret_cast<uint16_t*>(smem + SM::R2);
-    float* Lf = reinterpret_cast<float*>(smem + SM::R3);
-    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(smem + SM::R3);
-    uint16_t* Ut_lo = Ut_hi + BV * CP;
-    float* Rtmp = reinterpret_cast<float*>(smem + SM::R4);
-    uint16_t* A_hi = reinterpret_cast<uint16_t*>(smem + SM::R4);
+    __shared__ __align__(16) unsigned char r0[SM::R0_SZ];
+    __shared__ __align__(16) unsigned char r1[SM::R1_SZ];
+    __shared__ __align__(16) unsigned char r2[SM::R2_SZ];
+    __shared__ __align__(16) unsigned char r3[SM::R3_SZ];
+    __shared__ __align__(16) unsigned char r4[SM::R4_SZ];
+    __shared__ __align__(16) unsigned char r5[SM::R5_SZ];
+    __shared__ __align__(16) unsigned char r6[SM::R6_SZ];
+    __shared__ __align__(16) unsigned char r7[SM::R7_SZ];
+    __shared__ __align__(16) unsigned char r8[SM::R8_SZ];
+    __shared__ __align__(16) unsigned char r9[SM::R9_SZ];
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(r0);
+    float* Rtmp = reinterpret_cast<float*>(r0);
+    uint16_t* A_hi = reinterpret_cast<uint16_t*>(r0);
     uint16_t* A_lo = A_hi + C * CP;
-    uint16_t* P_hi = reinterpret_cast<uint16_t*>(smem + SM::R5);
+    uint16_t* Qc = reinterpret_cast<uint16_t*>(r1);
+    uint16_t* Yt_hi = reinterpret_cast<uint16_t*>(r1);
+    uint16_t* Yt_lo = Yt_hi + BV * CP;
+    uint16_t* Kt = reinterpret_cast<uint16_t*>(r2);
+    float* Lf = reinterpret_cast<float*>(r3);
+    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(r3);
+    uint16_t* Ut_lo = Ut_hi + BV * CP;
+    float* Xs = reinterpret_cast<float*>(r4);
+    uint16_t* P_hi = reinterpret_cast<uint16_t*>(r5);
     uint16_t* P_lo = P_hi + C * CP;
-    uint16_t* Xt_hi = reinterpret_cast<uint16_t*>(smem + SM::R6);
-    uint16_t* Xt_lo = Xt_hi + BV * CP;
-    uint16_t* Sb = reinterpret_cast<uint16_t*>(smem + SM::R7);
-    float* Gs = reinterpret_cast<float*>(smem + SM::R8);
-    float* bs = reinterpret_cast<float*>(smem + SM::R9);
+    float* Xf = reinterpret_cast<float*>(r6);
+    uint16_t* Os = reinterpret_cast<uint16_t*>(r6);
+    uint16_t* Sb = reinterpret_cast<uint16_t*>(r7);
+    float* Gs = reinterpret_cast<float*>(r8);
+    float* bs = reinterpret_cast<float*>(r9);
     float* gam = bs + C;
-    float* psum = gam + BV;
 
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index is uniform: keep it (and every tile offset derived from it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t H = n_heads;
     const int h = u.head;
     const int i0 = u.vblk * BV;
+    const int64_t row_qk = H * DK, row_v = H * DV;  // element strides between tokens
 
-    // ---- state: wave w owns S^T tile (j-tile jt, i-tile it) in fp32 accumulators
+    // ---- state: wave w owns S^T tile (j-tile s_jt, i-tile s_it) in fp32 accumulators
     const bool owns_s = wave < 2 * JT;
     const int s_jt = wave % JT, s_it = wave / JT;
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
@@ -169,319 +211,426 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         }
     }
 
-    // ---- register prefetch of one chunk's inputs
-    u16x8 pk[KQ_PER_T], pq[KQ_PER_T], pv;
-    f32x4 pa[A_PER_T];
+    // ---- register prefetch of one chunk's inputs.
+    // K, Q: thread (row pair tp, 16-byte chunk c) holds rows 2tp, 2tp+1 (with
+    // d_k = 64 the upper four waves repeat the lower four).
+    // V, alpha: thread (column gi = lane, rows 8*gpart .. 8*gpart+7), gpart = wave.
+    const int kq_tp = lane & 31, kq_c = (2 * wave + (lane >> 5)) % (DK / 8);
+    const int gpart = wave;
+    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {};
+    uint16_t pv[8];
+    float pa[8];
     float pb = 0.f;
+    // Every load is unconditional (rows past the sequence end read as zeros
+    // through the buffer range), which keeps the compiler's count of
+    // outstanding memory operations exact.
     auto prefetch = [&](int64_t tc, int n) {
-#pragma unroll
-        for (int p = 0; p < KQ_PER_T; ++p) {
-            const int idx = tid + NT * p;
-            const int t = idx / (DK / 8), c = idx % (DK / 8);
-            pk[p] = u16x8{};
-            pq[p] = u16x8{};
-            if (idx < KQ_CHUNKS && t < n) {
-                const int64_t g = ((tc + t) * H + h) * DK + 8 * c;
-                pk[p] = *reinterpret_cast<const u16x8*>(k + g);
-                pq[p] = *reinterpret_cast<const u16x8*>(q + g);
-            }
-        }
+        const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
         {
-            const int t = tid / (BV / 8), c = tid % (BV / 8);
-            pv = u16x8{};
-            if (t < n) pv = *reinterpret_cast<const u16x8*>(v + ((tc + t) * H + h) * DV + i0 + 8 * c);
+            const int64_t bytes = ((n - 1) * row_qk + DK) * 2;
+            const auto rk = make_rsrc(k + tok0 * DK, bytes);
+            const auto rq = make_rsrc(q + tok0 * DK, bytes);
+            const int off0 = static_cast<int>((2 * kq_tp) * row_qk + 8 * kq_c) * 2;
+            const int off1 = off0 + static_cast<int>(row_qk) * 2;
+            pk0 = __builtin_amdgcn_raw_buffer_load_b128(rk, off0, 0, 0);
+            pk1 = __builtin_amdgcn_raw_buffer_load_b128(rk, off1, 0, 0);
+            pq0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
+            pq1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off1, 0, 0);
         }
+        const auto rv = make_rsrc(v + tok0 * DV + i0, ((n - 1) * row_v + BV) * 2);
+        const auto ra = make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4);
 #pragma unroll
-        for (int p = 0; p < A_PER_T; ++p) {
-            const int idx = tid + NT * p;
-            const int t = idx / (BV / 4), c = idx % (BV / 4);
-            pa[p] = f32x4{1.f, 1.f, 1.f, 1.f};
-            if (t < n) pa[p] = *reinterpret_cast<const f32x4*>(alpha + ((tc + t) * H + h) * DV + i0 + 4 * c);
+        for (int e = 0; e < 8; ++e) {
+            const int off = static_cast<int>((8 * gpart + e) * row_v + lane);
+            pv[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, off * 2, 0, 0);
+            pa[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, off * 4, 0, 0));
         }
-        if (tid < C) pb = tid < n ? beta[(tc + tid) * H + h] : 0.f;
+        const auto rb = make_rsrc(beta + tok0, ((n - 1) * H + 1) * 4);
+        pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(lane * H) * 4, 0, 0));
     };
 
     auto chunk_len = [&](int64_t tc) { return static_cast<int>(min<int64_t>(C, u.t1 - tc)); };
 
+    // staged O rows of a finished chunk -> global, one 16-byte store per thread
+    auto store_o = [&](int64_t tc, int n, int td) {
+        const int t = td >> 3, c = td & 7;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(Os + t * OP + 8 * c);
+        const auto ro = make_rsrc(o + (tc * H + h) * DV + i0, ((n - 1) * row_v + BV) * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
+    };
+
     if (u.t0 < u.t1) prefetch(u.t0, chunk_len(u.t0));
 
-    // bf16 copy of the entering state for the S-side products
-    auto write_state_copy = [&]() {
+    // bf16 copy of the state for the S-side products (S^T registers 4rb..4rb+3
+    // hold 4 consecutive key channels j of one value row i)
+    auto write_state_copy = [&](int ln) {
         if (owns_s) {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                // registers 4rb..4rb+3 hold 4 consecutive j of one i
-                const int j = 32 * s_jt + 8 * rb + 4 * (lane >> 5), i = 32 * s_it + (lane & 31);
-                u16x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_bits(accS[4 * rb + e]);
-                *reinterpret_cast<u16x4*>(Sb + i * KP + j) = w;
+                const int j = 32 * s_jt + 8 * rb + 4 * (ln >> 5), i = 32 * s_it + (ln & 31);
+                uint2 w;
+                w.x = pack_bf16(accS[4 * rb], accS[4 * rb + 1]);
+                w.y = pack_bf16(accS[4 * rb + 2], accS[4 * rb + 3]);
+                *reinterpret_cast<uint2*>(Sb + i * KP + j) = w;
             }
         }
     };
-    write_state_copy();
+    write_state_copy(lane);
 
+    int64_t prev_tc = -1;
+    int prev_n = 0;
     for (int64_t tc = u.t0; tc < u.t1; tc += C) {
         const int n = chunk_len(tc);
-        __syncthreads();  // B0: the previous chunk is done with every buffer
+        // Lane-derived values are recomputed every chunk from an opaque copy of
+        // the lane id, so the compiler does not hoist dozens of loop-invariant
+        // LDS addresses into registers (which spills).
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int ln = lane_o;
+        const int td = ln + 64 * wave;
+        const int g16 = ln >> 4, m16 = ln & 15;
+        block_sync();  // the previous chunk is done with every buffer
 
-        // ================= P0: stage the prefetched chunk into LDS
+        // ======== stage this chunk; log-decay local scan (into G); previous
+        // chunk's O out; next chunk's loads in (they fly while this chunk computes)
+        {
+            const int rr = 2 * (ln & 31), c = (2 * wave + (ln >> 5)) % (DK / 8);
+            *reinterpret_cast<u32x4*>(Kc + rr * KP + 8 * c) = pk0;
+            *reinterpret_cast<u32x4*>(Kc + (rr + 1) * KP + 8 * c) = pk1;
+            *reinterpret_cast<u32x4*>(Qc + rr * KP + 8 * c) = pq0;
+            *reinterpret_cast<u32x4*>(Qc + (rr + 1) * KP + 8 * c) = pq1;
 #pragma unroll
-        for (int p = 0; p < KQ_PER_T; ++p) {
-            const int idx = tid + NT * p;
-            if (idx < KQ_CHUNKS) {
-                const int t = idx / (DK / 8), c = idx % (DK / 8);
-                *reinterpret_cast<u16x8*>(Kc + t * KP + 8 * c) = pk[p];
-                *reinterpret_cast<u16x8*>(Qc + t * KP + 8 * c) = pq[p];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Kt[(8 * c + e) * CP + t] = pk[p][e];
+            for (int e = 0; e < 8; ++e) {
+                // bf16 e of row rr (low half) and of row rr + 1 (high half)
+                const uint32_t lo = pk0[e >> 1] >> (16 * (e & 1)), hi = pk1[e >> 1] >> (16 * (e & 1));
+                *reinterpret_cast<uint32_t*>(Kt + (8 * c + e) * CP + rr) = (lo & 0xffffu) | (hi << 16);
             }
         }
-        {
-            const int t = tid / (BV / 8), c = tid % (BV / 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Xt_hi[(8 * c + e) * CP + t] = pv[e];  // raw V^T
-        }
-#pragma unroll
-        for (int p = 0; p < A_PER_T; ++p) {
-            const int idx = tid + NT * p;
-            const int t = idx / (BV / 4), c = idx % (BV / 4);
-            f32x4 la;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) la[e] = __logf(pa[p][e]);
-            *reinterpret_cast<f32x4*>(Gs + t * BV + 4 * c) = la;
-        }
-        if (tid < C) bs[tid] = pb;
-        // next chunk's loads fly while this one computes
-        if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C));
-        __syncthreads();  // B1
-
-        // ================= P1: local scans of G; Gram products on waves 0..5
-        const int gi = tid % BV, gpart = tid / BV;  // column i, rows 8*gpart .. 8*gpart+7
+        if (td < C) bs[td] = pb;
         float gl[8];
+        float vcur[8];
         {
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                acc += Gs[(8 * gpart + e) * BV + gi];
+                acc += (8 * gpart + e < n) ? __logf(pa[e]) : 0.f;
                 gl[e] = acc;
-            }
-            psum[gpart * BV + gi] = acc;
-        }
-        if (wave < 6) {
-            // tiles (0,0), (1,0), (1,1) of L (waves 0-2) and of P (waves 3-5)
-            const int tileid = wave % 3;
-            const int tb = tileid == 0 ? 0 : 1, sb = tileid == 2 ? 1 : 0;
-            const uint16_t* Aop = wave < 3 ? Kc : Qc;
-            f32x16 acc = {};
-#pragma unroll
-            for (int kk = 0; kk < DK; kk += 16)
-                acc = mfma(frag(Aop, KP, 32 * tb, kk, lane), frag(Kc, KP, 32 * sb, kk, lane), acc);
-            const int col = 32 * sb + (lane & 31);
-            if (wave < 3) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * tb + acc_row(r, lane);
-                    Lf[row * LP + col] = col < row ? bs[row] * acc[r] : 0.f;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * tb + acc_row(r, lane);
-                    uint16_t hi, lo;
-                    split_bf16(col <= row ? acc[r] : 0.f, hi, lo);
-                    P_hi[row * CP + col] = hi;
-                    P_lo[row * CP + col] = lo;
-                }
-            }
-        } else if (wave == 6) {
-            // upper-right 32x32 block of P is zero
-            for (int x = lane; x < 32 * 32; x += 64) {
-                const int row = x / 32, col = 32 + x % 32;
-                P_hi[row * CP + col] = 0;
-                P_lo[row * CP + col] = 0;
+                Gs[(8 * gpart + e) * GP + ln] = acc;
+                vcur[e] = bf16_bits_to_f32(pv[e]);
             }
         }
-        __syncthreads();  // B2
+        if (prev_tc >= 0) store_o(prev_tc, prev_n, td);
+        if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C));
+        block_sync();
 
-        // ================= P2: finish G, gamma, X = V e^{-G}; diagonal 16x16 inverses
-        {
-            float off = 0.f;
-            for (int p = 0; p < gpart; ++p) off += psum[p * BV + gi];
-            uint16_t xh[8], xl[8];
-            const u16x8 vraw = *reinterpret_cast<const u16x8*>(Xt_hi + gi * CP + 8 * gpart);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float g = gl[e] + off;
-                Gs[(8 * gpart + e) * BV + gi] = g;
-                split_bf16(bf16_bits_to_f32(vraw[e]) * __expf(-g), xh[e], xl[e]);
-            }
-            if (gpart == 7) gam[gi] = __expf(gl[7] + off);
-            u16x8 wh, wl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                wh[e] = xh[e];
-                wl[e] = xl[e];
-            }
-            *reinterpret_cast<u16x8*>(Xt_hi + gi * CP + 8 * gpart) = wh;
-            *reinterpret_cast<u16x8*>(Xt_lo + gi * CP + 8 * gpart) = wl;
-        }
+        // ======== Gram products.  Wave 0: the four 16x16 diagonal blocks of L and
+        // their inverses T_b = (I + L_bb)^{-1} (forward substitution, lane =
+        // (block, column)).  Waves 1-3: the rest of L = strictly_lower(diag(beta)
+        // K K^T) (tile (1,0) and the two sub-diagonal 16x16 blocks).  Waves 4-6:
+        // P = tril(Q K^T) as hi/lo bf16, formed transposed (D[s][t]) so that each
+        // lane holds 4 consecutive s of one row t.
         if (wave == 0) {
-            // T_b = (I + L_bb)^{-1} for the four 16x16 diagonal blocks; lane = (block, column)
-            const int b = lane >> 4, c = lane & 15;
+            f32x4 d[4] = {};
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += 32) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const bf16x8 kf = frag16(Kc, KP, 16 * b, kk, ln);
+                    d[b] = mfma16(kf, kf, d[b]);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * b + 4 * g16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * g16 + r;  // within the block
+                    Lf[(16 * b + row) * LP + 16 * b + m16] = m16 < row ? b4[r] * d[b][r] : 0.f;
+                }
+            }
+            wave_lds_sync();
+            const int b = g16, c = m16;
+            const float* Lb = Lf + (16 * b) * LP + 16 * b;
+            // all 36 row pieces of the strictly lower block first, then the
+            // substitution: no LDS round trip inside the dependent chain
+            f32x4 lrow[36];
+#pragma unroll
+            for (int r = 1, p = 0; r < 16; ++r)
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4, ++p) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
+            for (int r = 0, p = 0; r < 16; ++r) {
+                float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= Lf[(16 * b + r) * LP + 16 * b + s] * x[s];
-                x[r] = r < c ? 0.f : acc;
+                for (int s4 = 0; s4 < r; s4 += 4, ++p) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (s4 + e < r) {
+                            if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
+                            else acc0 -= lrow[p][e] * x[s4 + e];
+                        }
+                    }
+                }
+                x[r] = acc0 + acc1;  // zero for r < c: every x[s], s < r < c, is zero
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
-        }
-        __syncthreads();  // B3
-
-        // ================= P3: off-diagonal blocks of (I + L)^{-1}, block row by block row
-        // X[bi, :bi] = T_bi * ( - sum_{m < bi} L[bi, m] X[m, :bi] )
-#pragma unroll 1
-        for (int bi = 1; bi < 4; ++bi) {
-            const int ncol = 16 * bi;
-            for (int x = tid; x < 16 * ncol; x += NT) {
-                const int r = x / ncol, col = x % ncol;
-                const int mstart = col / 16;
-                float acc = 0.f;
-                for (int s = 16 * mstart; s < 16 * bi; ++s)
-                    acc -= Lf[(16 * bi + r) * LP + s] * Xs[s * LP + col];
-                Rtmp[r * 48 + col] = acc;
+        } else if (wave == 1) {
+            // tile (1,0): rows 32-63 x cols 0-31
+            f32x16 acc = {};
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += 16)
+                acc = mfma(frag(Kc, KP, 32, kk, ln), frag(Kc, KP, 0, kk, ln), acc);
+            f32x4 b4[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (ln >> 5));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 + acc_row(r, ln);
+                Lf[row * LP + (ln & 31)] = b4[r >> 2][r & 3] * acc[r];
             }
-            __syncthreads();
-            for (int x = tid; x < 16 * ncol; x += NT) {
-                const int r = x / ncol, col = x % ncol;
-                float acc = 0.f;
-                for (int s = 0; s <= r; ++s) acc += Xs[(16 * bi + r) * LP + 16 * bi + s] * Rtmp[s * 48 + col];
-                Xs[(16 * bi + r) * LP + col] = acc;
+        } else if (wave < 4) {
+            // the 16x16 blocks (16..31, 0..15) (wave 2) and (48..63, 32..47) (wave 3)
+            const int R = wave == 2 ? 16 : 48, Cc = R - 16;
+            f32x4 d = {};
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += 32)
+                d = mfma16(frag16(Kc, KP, R, kk, ln), frag16(Kc, KP, Cc, kk, ln), d);
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + R + 4 * g16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
+        } else if (wave < 7) {
+            // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1)
+            const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
+            f32x16 acc = {};
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += 16)
+                acc = mfma(frag(Kc, KP, 32 * sb, kk, ln), frag(Qc, KP, 32 * tb, kk, ln), acc);
+            const int t = 32 * tb + (ln & 31);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int s0 = 32 * sb + 8 * rb + 4 * (ln >> 5);
+                float pv4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv4[e] = s0 + e <= t ? acc[4 * rb + e] : 0.f;
+                uint2 wh, wl;
+                split_bf16x2(pv4[0], pv4[1], wh.x, wl.x);
+                split_bf16x2(pv4[2], pv4[3], wh.y, wl.y);
+                *reinterpret_cast<uint2*>(P_hi + t * CP + s0) = wh;
+                *reinterpret_cast<uint2*>(P_lo + t * CP + s0) = wl;
             }
-            __syncthreads();
         }
-        // A = X diag(beta) as hi/lo bf16, zero above the diagonal
-        for (int x = tid; x < C * C; x += NT) {
-            const int t = x / C, s = x % C;
-            uint16_t hi, lo;
-            split_bf16(s <= t ? Xs[t * LP + s] * bs[s] : 0.f, hi, lo);
-            A_hi[t * CP + s] = hi;
-            A_lo[t * CP + s] = lo;
-        }
-        __syncthreads();  // B4
+        block_sync();
 
-        // ================= P4: W = A K (all waves), U0 = A X (waves 0..3)
+        // ======== finish G and X^T = (V e^{-G})^T (all waves, thread = (column ln,
+        // 8 rows)); solve level 2 (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for
+        // the 16x16 blocks (16, 0) and (48, 32); waves 4-7: O^T = S Q^T and K S^T
+        float gfin[8];
         {
-            // W tiles: (tb, jb); 2*JT tiles over the waves
-            f32x16 accW = {};
-            const bool has_w = wave < 2 * JT;
-            const int w_tb = wave / JT, w_jb = wave % JT;
-            if (has_w) {
+            float off = 0.f;
+            for (int p = 0; p < gpart; ++p) off += Gs[(8 * p + 7) * GP + ln];
+            f32x4 x0, x1;
 #pragma unroll
-                for (int kk = 0; kk < 64; kk += 16) {
-                    if (kk < 32 * (w_tb + 1)) {
-                        const bf16x8 bk = frag(Kt, CP, 32 * w_jb, kk, lane);
-                        accW = mfma(frag(A_hi, CP, 32 * w_tb, kk, lane), bk, accW);
-                        accW = mfma(frag(A_lo, CP, 32 * w_tb, kk, lane), bk, accW);
-                    }
-                }
+            for (int e = 0; e < 8; ++e) {
+                gfin[e] = gl[e] + off;
+                const float xv = vcur[e] * __expf(-gfin[e]);
+                if (e < 4) x0[e] = xv;
+                else x1[e - 4] = xv;
             }
-            f32x16 accU = {};
-            const int u_tb = wave >> 1, u_ib = wave & 1;  // waves 0..3
-            if (wave < 4) {
-#pragma unroll
-                for (int kk = 0; kk < 64; kk += 16) {
-                    if (kk < 32 * (u_tb + 1)) {
-                        const bf16x8 ah = frag(A_hi, CP, 32 * u_tb, kk, lane);
-                        const bf16x8 al = frag(A_lo, CP, 32 * u_tb, kk, lane);
-                        const bf16x8 xh = frag(Xt_hi, CP, 32 * u_ib, kk, lane);
-                        const bf16x8 xl = frag(Xt_lo, CP, 32 * u_ib, kk, lane);
-                        accU = mfma(ah, xh, accU);
-                        accU = mfma(al, xh, accU);
-                        accU = mfma(ah, xl, accU);
-                    }
-                }
-            }
-            // -W as bf16 [t][j] into R0 (the solve scratch is dead after B4)
-            if (has_w) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = 32 * w_tb + acc_row(r, lane), j = 32 * w_jb + (lane & 31);
-                    Wn[t * KP + j] = f32_to_bf16_bits(-accW[r]);
-                }
-            }
-            __syncthreads();  // B5
-
-            // ============= P5: U = U0 - W S^T (waves 0..3); Q S^T (waves 4..7)
-            f32x16 accO = {};
-            const int o_tb = (wave - 4) >> 1, o_ib = (wave - 4) & 1;
-            if (wave < 4) {
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += 16)
-                    accU = mfma(frag(Wn, KP, 32 * u_tb, kk, lane), frag(Sb, KP, 32 * u_ib, kk, lane), accU);
-                // U^T hi/lo [i][t]: registers 4rb..4rb+3 are 4 consecutive t of one i
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int t = 32 * u_tb + 8 * rb + 4 * (lane >> 5), i = 32 * u_ib + (lane & 31);
-                    u16x4 wh, wl;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        uint16_t hi, lo;
-                        split_bf16(accU[4 * rb + e], hi, lo);
-                        wh[e] = hi;
-                        wl[e] = lo;
-                    }
-                    *reinterpret_cast<u16x4*>(Ut_hi + i * CP + t) = wh;
-                    *reinterpret_cast<u16x4*>(Ut_lo + i * CP + t) = wl;
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < DK; kk += 16)
-                    accO = mfma(frag(Qc, KP, 32 * o_tb, kk, lane), frag(Sb, KP, 32 * o_ib, kk, lane), accO);
-            }
-            __syncthreads();  // B6
-
-            // ============= P6: O = e^G (Q S^T + P U) (waves 4..7); S^T += K^T U, decay (all)
-            if (wave >= 4) {
-#pragma unroll
-                for (int kk = 0; kk < 64; kk += 16) {
-                    if (kk < 32 * (o_tb + 1)) {
-                        const bf16x8 ph = frag(P_hi, CP, 32 * o_tb, kk, lane);
-                        const bf16x8 pl = frag(P_lo, CP, 32 * o_tb, kk, lane);
-                        const bf16x8 uh = frag(Ut_hi, CP, 32 * o_ib, kk, lane);
-                        const bf16x8 ul = frag(Ut_lo, CP, 32 * o_ib, kk, lane);
-                        accO = mfma(ph, uh, accO);
-                        accO = mfma(pl, uh, accO);
-                        accO = mfma(ph, ul, accO);
-                    }
-                }
-                const int i = 32 * o_ib + (lane & 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int t = 32 * o_tb + acc_row(r, lane);
-                    if (t < n) {
-                        const float val = __expf(Gs[t * BV + i]) * accO[r];
-                        o[((tc + t) * H + h) * DV + i0 + i] = f32_to_bf16_bits(val);
-                    }
-                }
-            }
-            if (owns_s) {
-#pragma unroll
-                for (int kk = 0; kk < 64; kk += 16) {
-                    const bf16x8 kt = frag(Kt, CP, 32 * s_jt, kk, lane);
-                    accS = mfma(kt, frag(Ut_hi, CP, 32 * s_it, kk, lane), accS);
-                    accS = mfma(kt, frag(Ut_lo, CP, 32 * s_it, kk, lane), accS);
-                }
-                const float gm = gam[32 * s_it + (lane & 31)];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) accS[r] *= gm;
-            }
-            write_state_copy();  // Sb is not read again in this chunk (last reader: P5)
+            if (gpart == 7) gam[ln] = __expf(gfin[7]);
+            *reinterpret_cast<f32x4*>(Xf + ln * LP + 8 * gpart) = x0;
+            *reinterpret_cast<f32x4*>(Xf + ln * LP + 8 * gpart + 4) = x1;
         }
+        f32x16 accO = {}, accY = {};
+        const int o_ib = (wave - 4) >> 1, o_tb = (wave - 4) & 1;  // O^T tile (i-tile, t-tile)
+        const int y_tb = o_tb, y_ib = o_ib;  // (K S^T) tile (t-tile, i-tile): shares the S operand
+        if (wave < 2) {
+            const int R = 16 * (2 * wave + 1), Cc = 16 * (2 * wave);
+            float la[4], xa[4], ta[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                la[kk] = Lf[(R + m16) * LP + Cc + 4 * kk + g16];
+                xa[kk] = Xs[(Cc + 4 * kk + g16) * LP + Cc + m16];
+                ta[kk] = Xs[(R + m16) * LP + R + 4 * g16 + kk];
+            }
+            f32x4 y = {};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) y = mfma16f(la[kk], xa[kk], y);
+            // y (row 4*g16 + r, column m16) feeds the next product directly as its B
+            // operand: step r uses reduction index 4*g16 + r, matched on the A side
+            f32x4 z = {};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z = mfma16f(ta[r], y[r], z);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
+        } else if (wave >= 4) {
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += 16) {
+                const bf16x8 sf = frag(Sb, KP, 32 * o_ib, kk, ln);
+                accO = mfma(sf, frag(Qc, KP, 32 * o_tb, kk, ln), accO);
+                accY = mfma(frag(Kc, KP, 32 * y_tb, kk, ln), sf, accY);
+            }
+        }
+        block_sync();
+
+        // ======== final G into LDS (all); solve level 3a (waves 0-3): Y2 = L[32:64,
+        // 0:32] X[0:32, 0:32], one 16x16 quadrant (qr, qc) per wave, into Rtmp
+        // [32][36]; waves 4-7: Y = X - K S^T -> Y^T hi/lo [i][t]
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gs[(8 * gpart + e) * GP + ln] = gfin[e];
+        const int qr = wave >> 1, qc = wave & 1;
+        if (wave < 4) {
+            float la[8], xa[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                la[kk] = Lf[(32 + 16 * qr + m16) * LP + 4 * kk + g16];
+                xa[kk] = Xs[(4 * kk + g16) * LP + 16 * qc + m16];
+            }
+            f32x4 y = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (kk >= 4 * qc)  // X[0:32, 0:32] is lower triangular by 16x16 blocks
+                    y = mfma16f(la[kk], xa[kk], y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * 36 + 16 * qc + m16] = y[r];
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                // registers 4rb..4rb+3: 4 consecutive t of one i
+                const int t = 32 * y_tb + 8 * rb + 4 * (ln >> 5), i = 32 * y_ib + (ln & 31);
+                const f32x4 xv = *reinterpret_cast<const f32x4*>(Xf + i * LP + t);
+                uint2 wh, wl;
+                split_bf16x2(xv[0] - accY[4 * rb], xv[1] - accY[4 * rb + 1], wh.x, wl.x);
+                split_bf16x2(xv[2] - accY[4 * rb + 2], xv[3] - accY[4 * rb + 3], wh.y, wl.y);
+                *reinterpret_cast<uint2*>(Yt_hi + i * CP + t) = wh;
+                *reinterpret_cast<uint2*>(Yt_lo + i * CP + t) = wl;
+            }
+        }
+        block_sync();
+
+        // ======== solve level 3b (waves 0-3): X[32:64, 0:32] = -X[32:64, 32:64] Y2
+        if (wave < 4) {
+            float xa[8], ra[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                xa[kk] = Xs[(32 + 16 * qr + m16) * LP + 32 + 4 * kk + g16];
+                ra[kk] = Rtmp[(4 * kk + g16) * 36 + 16 * qc + m16];
+            }
+            f32x4 z = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (kk < 4 * (qr + 1))  // X[32:64, 32:64] is lower triangular by blocks
+                    z = mfma16f(xa[kk], ra[kk], z);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Xs[(32 + 16 * qr + 4 * g16 + r) * LP + 16 * qc + m16] = -z[r];
+        }
+        block_sync();
+
+        // ======== A = (I + L)^{-1} diag(beta) as hi/lo bf16, zero above the diagonal;
+        // each thread converts 8 consecutive entries of one row
+        {
+            const int t = td >> 3, s0 = 8 * (td & 7);
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + s0);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + s0 + 4);
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = e < 4 ? x0[e] * b0[e] : x1[e - 4] * b1[e - 4];
+                av[e] = s0 + e <= t ? xv : 0.f;
+            }
+            u32x4 wh, wl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t a, b;
+                split_bf16x2(av[2 * e], av[2 * e + 1], a, b);
+                wh[e] = a;
+                wl[e] = b;
+            }
+            *reinterpret_cast<u32x4*>(A_hi + t * CP + s0) = wh;
+            *reinterpret_cast<u32x4*>(A_lo + t * CP + s0) = wl;
+        }
+        block_sync();
+
+        // ======== U = A Y (waves 0-3) -> U^T hi/lo [i][t]
+        if (wave < 4) {
+            const int u_tb = wave >> 1, u_ib = wave & 1;
+            f32x16 accU = {};
+#pragma unroll
+            for (int kk = 0; kk < 64; kk += 16) {
+                if (kk < 32 * (u_tb + 1)) {  // A is lower triangular
+                    const bf16x8 ah = frag(A_hi, CP, 32 * u_tb, kk, ln);
+                    const bf16x8 al = frag(A_lo, CP, 32 * u_tb, kk, ln);
+                    const bf16x8 yh = frag(Yt_hi, CP, 32 * u_ib, kk, ln);
+                    const bf16x8 yl = frag(Yt_lo, CP, 32 * u_ib, kk, ln);
+                    accU = mfma(ah, yh, accU);
+                    accU = mfma(al, yh, accU);
+                    accU = mfma(ah, yl, accU);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int t = 32 * u_tb + 8 * rb + 4 * (ln >> 5), i = 32 * u_ib + (ln & 31);
+                uint2 wh, wl;
+                split_bf16x2(accU[4 * rb], accU[4 * rb + 1], wh.x, wl.x);
+                split_bf16x2(accU[4 * rb + 2], accU[4 * rb + 3], wh.y, wl.y);
+                *reinterpret_cast<uint2*>(Ut_hi + i * CP + t) = wh;
+                *reinterpret_cast<uint2*>(Ut_lo + i * CP + t) = wl;
+            }
+        }
+        block_sync();
+
+        // ======== O^T = e^G (S Q^T + U^T P^T) staged as bf16 O [t][i] (waves 4-7);
+        // S^T = diag(gamma)(S^T + K^T U) (all waves)
+        if (wave >= 4) {
+#pragma unroll
+            for (int kk = 0; kk < 64; kk += 16) {
+                if (kk < 32 * (o_tb + 1)) {  // P is lower triangular
+                    const bf16x8 uh = frag(Ut_hi, CP, 32 * o_ib, kk, ln);
+                    const bf16x8 ul = frag(Ut_lo, CP, 32 * o_ib, kk, ln);
+                    const bf16x8 ph = frag(P_hi, CP, 32 * o_tb, kk, ln);
+                    const bf16x8 pl = frag(P_lo, CP, 32 * o_tb, kk, ln);
+                    accO = mfma(uh, ph, accO);
+                    accO = mfma(ul, ph, accO);
+                    accO = mfma(uh, pl, accO);
+                }
+            }
+            const int t = 32 * o_tb + (ln & 31);
+            f32x4 g4[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + t * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int i = 32 * o_ib + 8 * rb + 4 * (ln >> 5);
+                uint2 w;
+                w.x = pack_bf16(__expf(g4[rb][0]) * accO[4 * rb], __expf(g4[rb][1]) * accO[4 * rb + 1]);
+                w.y = pack_bf16(__expf(g4[rb][2]) * accO[4 * rb + 2], __expf(g4[rb][3]) * accO[4 * rb + 3]);
+                *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
+            }
+        }
+        if (owns_s) {
+#pragma unroll
+            for (int kk = 0; kk < 64; kk += 16) {
+                const bf16x8 kt = frag(Kt, CP, 32 * s_jt, kk, ln);
+                accS = mfma(kt, frag(Ut_hi, CP, 32 * s_it, kk, ln), accS);
+                accS = mfma(kt, frag(Ut_lo, CP, 32 * s_it, kk, ln), accS);
+            }
+            const float gm = gam[32 * s_it + (ln & 31)];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accS[r] *= gm;
+        }
+        write_state_copy(ln);  // the last readers of the old copy were S Q^T and K S^T
+        prev_tc = tc;
+        prev_n = n;
+    }
+    if (prev_tc >= 0) {
+        block_sync();
+        store_o(prev_tc, prev_n, tid);
     }
 
     if (S_T && owns_s) {
