@@ -8,6 +8,10 @@ line.  The decode workload (B=256, H=32, 1024 successive steps, 537 MB fp32
 state) is timed in the same run and reported under "decode".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+       python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
+                                             a 1 GiB device copy for calibration, 3 prefill
+                                             launches, 8 decode steps)
+       python bench.py --summarize DIR      (print the per-kernel table of a rocprofv3 run)
 """
 from __future__ import annotations
 
@@ -42,7 +46,65 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=1024)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--traffic-probe", action="store_true")
+    p.add_argument("--summarize", default=None)
     return p.parse_args()
+
+
+def traffic_probe():
+    """Fixed, short GPU work for hardware-counter runs."""
+    import torch
+    from gated_delta_rule_72_amd import inputs as I
+    from gated_delta_rule_72_amd import kda
+    kda.lib()
+    dev = "cuda:0"
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)  # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)  # calibration: reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    del src, dst
+    inp = I.workload_prefill(3)
+    q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+    alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
+    for _ in range(3):
+        kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=inp.n_seq)
+    torch.cuda.synchronize()
+    del q, k, v, alpha, beta, S0
+    dec = I.workload_decode(4, n_steps=8)
+    d = {x: upload(getattr(dec, x), dec.dtype if x in "qkv" else "f32", dev)
+         for x in ("q", "k", "v", "alpha", "beta")}
+    S = upload(dec.S0, "f32", dev)
+    for t in range(8):
+        kda.kda_decode_step(d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], S)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+
+
+def summarize(path):
+    """Per-kernel table (calls, mean duration, and any counters) of a rocprofv3 run."""
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+    if not dbs:
+        sys.exit(f"no rocprofv3 results under {path}")
+    for db in dbs:
+        con = sqlite3.connect(db)
+        print(f"# {os.path.relpath(db, path)}")
+        rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration) "
+                           "from kernels group by name order by sum(duration) desc").fetchall()
+        print(f"{'kernel':70s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        for name, n, avg, mn, mx in rows:
+            print(f"{name[:70]:70s} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f}")
+        try:
+            crow = con.execute("select name, counter_name, count(distinct dispatch_id), "
+                               "sum(counter_value) / count(distinct dispatch_id) from pmc_events "
+                               "group by name, counter_name").fetchall()
+        except sqlite3.Error:
+            crow = []
+        if crow:
+            print(f"{'kernel':70s} {'counter':>14s} {'dispatches':>10s} {'per_dispatch':>16s}")
+            for name, cn, n, val in crow:
+                print(f"{name[:70]:70s} {cn:>14s} {n:10d} {val:16.1f}")
 
 
 def upload(x, dtype, dev):
@@ -198,6 +260,12 @@ def bench_decode(args, torch, kda, I):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
               "multi-GPU launch: run it with --gpus 1.", file=sys.stderr)

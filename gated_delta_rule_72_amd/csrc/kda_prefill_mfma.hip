@@ -85,6 +85,11 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+// Compiler-only fence: the LDS operand loads above it are issued before the
+// matrix instructions below it, so their latencies overlap instead of each
+// MFMA waiting for its own freshly issued load.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
 // Order this wave's own LDS writes before its later LDS reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -102,12 +107,15 @@ template <int DK>
 struct Smem {
     static constexpr int KP = DK + PAD;     // pitch of [t][j] bf16 rows
     static constexpr int CP = C + PAD;      // pitch of [x][t] bf16 rows (length C)
-    static constexpr int LP = C + 4;        // pitch of [x][t] fp32 rows (length C)
+    // pitch of C x C fp32 rows: 80 = 16 mod 64 makes the column-wise operand
+    // loads of the fp32 matrix-core solve (rows 4k + g, columns m) hit distinct banks
+    static constexpr int LP = C + 16;
+    static constexpr int RP = 48;           // pitch of the 32 x 32 solve temporary
     static constexpr int mx(int a, int b) { return a > b ? a : b; }
     static constexpr int HILO = 2 * C * CP * 2;  // a C x C (or BV x C) hi/lo bf16 pair
-    // R0: K [t][j] -> solve temporaries (fp32 32x36) -> A hi/lo [t][s]
+    // R0: K [t][j] -> solve temporary (fp32 32 x RP) -> A hi/lo [t][s]
     static constexpr int R0 = 0;
-    static constexpr int R0_SZ = mx(mx(C * KP * 2, 32 * 36 * 4), HILO);
+    static constexpr int R0_SZ = mx(mx(C * KP * 2, 32 * RP * 4), HILO);
     // R1: Q [t][j] -> Y^T hi/lo [i][t]
     static constexpr int R1 = R0 + R0_SZ;
     static constexpr int R1_SZ = mx(C * KP * 2, HILO);
@@ -117,25 +125,25 @@ struct Smem {
     // R3: L fp32 [t][s] -> U^T hi/lo [i][t]
     static constexpr int R3 = R2 + R2_SZ;
     static constexpr int R3_SZ = mx(C * LP * 4, HILO);
-    // R4: (I + L)^{-1} fp32 [t][s]
+    // R4: (I + L)^{-1} fp32 [t][s] -> O bf16 [t][i] (stored at the next chunk)
     static constexpr int R4 = R3 + R3_SZ;
-    static constexpr int R4_SZ = C * LP * 4;
+    static constexpr int R4_SZ = mx(C * LP * 4, C * (BV + PAD) * 2);
     // R5: P = tril(Q K^T) hi/lo [t][s]
     static constexpr int R5 = R4 + R4_SZ;
     static constexpr int R5_SZ = HILO;
-    // R6: X^T = (V e^{-G})^T fp32 [i][t] -> O bf16 [t][i] (stored at the next chunk)
+    // R6: V bf16 [t][i] as loaded
     static constexpr int R6 = R5 + R5_SZ;
-    static constexpr int R6_SZ = mx(BV * LP * 4, C * (BV + PAD) * 2);
+    static constexpr int R6_SZ = C * (BV + PAD) * 2;
     // R7: S bf16 [i][j] (operand copy of the fp32 state)
     static constexpr int R7 = R6 + R6_SZ;
     static constexpr int R7_SZ = BV * KP * 2;
-    // R8: G fp32 [t][i] (first the per-part local prefix sums of log alpha)
+    // R8: log alpha -> per-part local prefix sums -> G, fp32 [t][i]
     static constexpr int GP = BV + 4;       // pitch of G rows
     static constexpr int R8 = R7 + R7_SZ;
     static constexpr int R8_SZ = C * GP * 4;
-    // R9: beta [C], gamma [BV]
+    // R9: beta [C], gamma [BV], partial scan sums [8][BV]
     static constexpr int R9 = R8 + R8_SZ;
-    static constexpr int R9_SZ = (C + BV) * 4;
+    static constexpr int R9_SZ = (C + BV + 8 * BV) * 4;
     static constexpr int TOTAL = R9 + R9_SZ;
 };
 
@@ -152,8 +160,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, CP = SM::CP, LP = SM::LP, GP = SM::GP;
-    constexpr int OP = BV + PAD;           // pitch of the staged O rows
+    constexpr int KP = SM::KP, CP = SM::CP, LP = SM::LP, GP = SM::GP, RP = SM::RP;
+    constexpr int OP = BV + PAD;           // pitch of the staged O and V rows
     constexpr int JT = DK / 32;            // 32-wide tiles along d_k
 
     __shared__ __align__(16) unsigned char r0[SM::R0_SZ];
@@ -178,14 +186,15 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
     uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(r3);
     uint16_t* Ut_lo = Ut_hi + BV * CP;
     float* Xs = reinterpret_cast<float*>(r4);
+    uint16_t* Os = reinterpret_cast<uint16_t*>(r4);
     uint16_t* P_hi = reinterpret_cast<uint16_t*>(r5);
     uint16_t* P_lo = P_hi + C * CP;
-    float* Xf = reinterpret_cast<float*>(r6);
-    uint16_t* Os = reinterpret_cast<uint16_t*>(r6);
+    uint16_t* Vr = reinterpret_cast<uint16_t*>(r6);
     uint16_t* Sb = reinterpret_cast<uint16_t*>(r7);
     float* Gs = reinterpret_cast<float*>(r8);
     float* bs = reinterpret_cast<float*>(r9);
     float* gam = bs + C;
+    float* psum = gam + BV;
 
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
@@ -211,19 +220,19 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         }
     }
 
-    // ---- register prefetch of one chunk's inputs.
+    // ---- register prefetch of one chunk's inputs; every load moves 16 bytes
+    // per lane, so one wave instruction covers 1 KB of whole cache lines.
     // K, Q: thread (row pair tp, 16-byte chunk c) holds rows 2tp, 2tp+1 (with
     // d_k = 64 the upper four waves repeat the lower four).
-    // V, alpha: thread (column gi = lane, rows 8*gpart .. 8*gpart+7), gpart = wave.
+    // V: thread (row td/8, 8 values at 8*(td%8)); alpha: rows td/16 and 32 + td/16,
+    // 4 values at 4*(td%16); beta: wave 0, lane = token.
     const int kq_tp = lane & 31, kq_c = (2 * wave + (lane >> 5)) % (DK / 8);
     const int gpart = wave;
-    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {};
-    uint16_t pv[8];
-    float pa[8];
+    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {}, pv = {};
+    f32x4 pa0 = {}, pa1 = {};
     float pb = 0.f;
-    // Every load is unconditional (rows past the sequence end read as zeros
-    // through the buffer range), which keeps the compiler's count of
-    // outstanding memory operations exact.
+    // Rows past the sequence end read as zeros through the buffer range, so
+    // no load needs a per-row branch.
     auto prefetch = [&](int64_t tc, int n) {
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
         {
@@ -237,16 +246,18 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             pq0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
             pq1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off1, 0, 0);
         }
-        const auto rv = make_rsrc(v + tok0 * DV + i0, ((n - 1) * row_v + BV) * 2);
-        const auto ra = make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int off = static_cast<int>((8 * gpart + e) * row_v + lane);
-            pv[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, off * 2, 0, 0);
-            pa[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, off * 4, 0, 0));
+        {
+            const auto rv = make_rsrc(v + tok0 * DV + i0, ((n - 1) * row_v + BV) * 2);
+            pv = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2, 0, 0);
+            const auto ra = make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4);
+            const int offa = static_cast<int>((tid >> 4) * row_v + 4 * (tid & 15)) * 4;
+            pa0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, 0));
+            pa1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + static_cast<int>(32 * row_v) * 4, 0, 0));
         }
-        const auto rb = make_rsrc(beta + tok0, ((n - 1) * H + 1) * 4);
-        pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(lane * H) * 4, 0, 0));
+        if (wave == 0) {  // beta of token `lane`: one cache line per token, so one wave only
+            const auto rb = make_rsrc(beta + tok0, ((n - 1) * H + 1) * 4);
+            pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(lane * H) * 4, 0, 0));
+        }
     };
 
     auto chunk_len = [&](int64_t tc) { return static_cast<int>(min<int64_t>(C, u.t1 - tc)); };
@@ -307,17 +318,18 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             }
         }
         if (td < C) bs[td] = pb;
-        float gl[8];
-        float vcur[8];
+        *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pv;
         {
-            float acc = 0.f;
+            // log alpha, 0 for rows past the sequence end (they read as alpha = 0)
+            const int t = td >> 4, c = 4 * (td & 15);
+            f32x4 l0, l1;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc += (8 * gpart + e < n) ? __logf(pa[e]) : 0.f;
-                gl[e] = acc;
-                Gs[(8 * gpart + e) * GP + ln] = acc;
-                vcur[e] = bf16_bits_to_f32(pv[e]);
+            for (int e = 0; e < 4; ++e) {
+                l0[e] = t < n ? __logf(pa0[e]) : 0.f;
+                l1[e] = t + 32 < n ? __logf(pa1[e]) : 0.f;
             }
+            *reinterpret_cast<f32x4*>(Gs + t * GP + c) = l0;
+            *reinterpret_cast<f32x4*>(Gs + (t + 32) * GP + c) = l1;
         }
         if (prev_tc >= 0) store_o(prev_tc, prev_n, td);
         if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C));
@@ -329,16 +341,28 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         // K K^T) (tile (1,0) and the two sub-diagonal 16x16 blocks).  Waves 4-6:
         // P = tril(Q K^T) as hi/lo bf16, formed transposed (D[s][t]) so that each
         // lane holds 4 consecutive s of one row t.
+        // local prefix sums of log alpha: thread (column ln, rows 8*gpart .. 8*gpart+7)
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc += Gs[(8 * gpart + e) * GP + ln];
+                Gs[(8 * gpart + e) * GP + ln] = acc;
+            }
+            psum[gpart * BV + ln] = acc;
+        }
         if (wave == 0) {
             f32x4 d[4] = {};
+            bf16x8 kf[4][DK / 32];
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += 32) {
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const bf16x8 kf = frag16(Kc, KP, 16 * b, kk, ln);
-                    d[b] = mfma16(kf, kf, d[b]);
-                }
-            }
+                for (int kk = 0; kk < DK / 32; ++kk) kf[b][kk] = frag16(Kc, KP, 16 * b, 32 * kk, ln);
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) d[b] = mfma16(kf[b][kk], kf[b][kk], d[b]);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * b + 4 * g16);
@@ -351,37 +375,55 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             wave_lds_sync();
             const int b = g16, c = m16;
             const float* Lb = Lf + (16 * b) * LP + 16 * b;
-            // all 36 row pieces of the strictly lower block first, then the
-            // substitution: no LDS round trip inside the dependent chain
+            // Row pieces of the strictly lower block are loaded in two batches
+            // (rows 1-9, then rows 10-15 once rows 0-5 are done), so no LDS round
+            // trip sits inside the dependent substitution chain.
             f32x4 lrow[36];
+            auto load_rows = [&](int r_lo, int r_hi) {
 #pragma unroll
-            for (int r = 1, p = 0; r < 16; ++r)
+                for (int r = 1, p = 0; r < 16; ++r)
 #pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4, ++p) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+                    for (int s4 = 0; s4 < r; s4 += 4, ++p)
+                        if (r >= r_lo && r < r_hi) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+            };
             float x[16];
+            auto solve_rows = [&](int r_lo, int r_hi) {
 #pragma unroll
-            for (int r = 0, p = 0; r < 16; ++r) {
-                float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
+                for (int r = 0, p = 0; r < 16; ++r) {
+                    float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4, ++p) {
+                    for (int s4 = 0; s4 < r; s4 += 4, ++p) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (s4 + e < r) {
-                            if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
-                            else acc0 -= lrow[p][e] * x[s4 + e];
+                        for (int e = 0; e < 4; ++e) {
+                            if (r >= r_lo && r < r_hi && s4 + e < r) {
+                                if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
+                                else acc0 -= lrow[p][e] * x[s4 + e];
+                            }
                         }
                     }
+                    if (r >= r_lo && r < r_hi) x[r] = acc0 + acc1;  // zero for r < c
                 }
-                x[r] = acc0 + acc1;  // zero for r < c: every x[s], s < r < c, is zero
-            }
+            };
+            load_rows(1, 10);
+            issue_fence();
+            solve_rows(0, 6);
+            load_rows(10, 16);
+            issue_fence();
+            solve_rows(6, 16);
 #pragma unroll
             for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
         } else if (wave == 1) {
             // tile (1,0): rows 32-63 x cols 0-31
             f32x16 acc = {};
+            bf16x8 fa[DK / 16], fb[DK / 16];
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += 16)
-                acc = mfma(frag(Kc, KP, 32, kk, ln), frag(Kc, KP, 0, kk, ln), acc);
+            for (int kk = 0; kk < DK / 16; ++kk) {
+                fa[kk] = frag(Kc, KP, 32, 16 * kk, ln);
+                fb[kk] = frag(Kc, KP, 0, 16 * kk, ln);
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
             f32x4 b4[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (ln >> 5));
@@ -394,9 +436,15 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             // the 16x16 blocks (16..31, 0..15) (wave 2) and (48..63, 32..47) (wave 3)
             const int R = wave == 2 ? 16 : 48, Cc = R - 16;
             f32x4 d = {};
+            bf16x8 fa[DK / 32], fb[DK / 32];
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += 32)
-                d = mfma16(frag16(Kc, KP, R, kk, ln), frag16(Kc, KP, Cc, kk, ln), d);
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                fa[kk] = frag16(Kc, KP, R, 32 * kk, ln);
+                fb[kk] = frag16(Kc, KP, Cc, 32 * kk, ln);
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) d = mfma16(fa[kk], fb[kk], d);
             const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + R + 4 * g16);
 #pragma unroll
             for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
@@ -404,9 +452,15 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1)
             const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
             f32x16 acc = {};
+            bf16x8 fa[DK / 16], fb[DK / 16];
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += 16)
-                acc = mfma(frag(Kc, KP, 32 * sb, kk, ln), frag(Qc, KP, 32 * tb, kk, ln), acc);
+            for (int kk = 0; kk < DK / 16; ++kk) {
+                fa[kk] = frag(Kc, KP, 32 * sb, 16 * kk, ln);
+                fb[kk] = frag(Qc, KP, 32 * tb, 16 * kk, ln);
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
             const int t = 32 * tb + (ln & 31);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
@@ -423,24 +477,15 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         }
         block_sync();
 
-        // ======== finish G and X^T = (V e^{-G})^T (all waves, thread = (column ln,
-        // 8 rows)); solve level 2 (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for
-        // the 16x16 blocks (16, 0) and (48, 32); waves 4-7: O^T = S Q^T and K S^T
-        float gfin[8];
+        // ======== finish G and gamma (all waves, thread = (column ln, 8 rows));
+        // solve level 2 (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for the 16x16
+        // blocks (16, 0) and (48, 32); waves 4-7: O^T = S Q^T and K S^T
         {
             float off = 0.f;
-            for (int p = 0; p < gpart; ++p) off += Gs[(8 * p + 7) * GP + ln];
-            f32x4 x0, x1;
+            for (int p = 0; p < gpart; ++p) off += psum[p * BV + ln];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                gfin[e] = gl[e] + off;
-                const float xv = vcur[e] * __expf(-gfin[e]);
-                if (e < 4) x0[e] = xv;
-                else x1[e - 4] = xv;
-            }
-            if (gpart == 7) gam[ln] = __expf(gfin[7]);
-            *reinterpret_cast<f32x4*>(Xf + ln * LP + 8 * gpart) = x0;
-            *reinterpret_cast<f32x4*>(Xf + ln * LP + 8 * gpart + 4) = x1;
+            for (int e = 0; e < 8; ++e) Gs[(8 * gpart + e) * GP + ln] += off;
+            if (gpart == 7) gam[ln] = __expf(Gs[63 * GP + ln]);
         }
         f32x16 accO = {}, accY = {};
         const int o_ib = (wave - 4) >> 1, o_tb = (wave - 4) & 1;  // O^T tile (i-tile, t-tile)
@@ -454,6 +499,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                 xa[kk] = Xs[(Cc + 4 * kk + g16) * LP + Cc + m16];
                 ta[kk] = Xs[(R + m16) * LP + R + 4 * g16 + kk];
             }
+            issue_fence();
             f32x4 y = {};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) y = mfma16f(la[kk], xa[kk], y);
@@ -465,20 +511,30 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
         } else if (wave >= 4) {
+            // two batches of four reduction steps bound the operand registers
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += 16) {
-                const bf16x8 sf = frag(Sb, KP, 32 * o_ib, kk, ln);
-                accO = mfma(sf, frag(Qc, KP, 32 * o_tb, kk, ln), accO);
-                accY = mfma(frag(Kc, KP, 32 * y_tb, kk, ln), sf, accY);
+            for (int half = 0; half < DK / 64; ++half) {
+                bf16x8 fs[4], fq[4], fk[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int k0 = 64 * half + 16 * kk;
+                    fs[kk] = frag(Sb, KP, 32 * o_ib, k0, ln);
+                    fq[kk] = frag(Qc, KP, 32 * o_tb, k0, ln);
+                    fk[kk] = frag(Kc, KP, 32 * y_tb, k0, ln);
+                }
+                issue_fence();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    accO = mfma(fs[kk], fq[kk], accO);
+                    accY = mfma(fk[kk], fs[kk], accY);
+                }
             }
         }
         block_sync();
 
-        // ======== final G into LDS (all); solve level 3a (waves 0-3): Y2 = L[32:64,
-        // 0:32] X[0:32, 0:32], one 16x16 quadrant (qr, qc) per wave, into Rtmp
-        // [32][36]; waves 4-7: Y = X - K S^T -> Y^T hi/lo [i][t]
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Gs[(8 * gpart + e) * GP + ln] = gfin[e];
+        // ======== solve level 3a (waves 0-3): Y2 = L[32:64, 0:32] X[0:32, 0:32], one
+        // 16x16 quadrant (qr, qc) per wave, into Rtmp [32][RP]; waves 4-7:
+        // Y = V e^{-G} - K S^T -> Y^T hi/lo [i][t]
         const int qr = wave >> 1, qc = wave & 1;
         if (wave < 4) {
             float la[8], xa[8];
@@ -487,6 +543,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                 la[kk] = Lf[(32 + 16 * qr + m16) * LP + 4 * kk + g16];
                 xa[kk] = Xs[(4 * kk + g16) * LP + 16 * qc + m16];
             }
+            issue_fence();
             f32x4 y = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
@@ -494,13 +551,16 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                     y = mfma16f(la[kk], xa[kk], y);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * 36 + 16 * qc + m16] = y[r];
+            for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * RP + 16 * qc + m16] = y[r];
         } else {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 // registers 4rb..4rb+3: 4 consecutive t of one i
                 const int t = 32 * y_tb + 8 * rb + 4 * (ln >> 5), i = 32 * y_ib + (ln & 31);
-                const f32x4 xv = *reinterpret_cast<const f32x4*>(Xf + i * LP + t);
+                float xv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __expf(-Gs[(t + e) * GP + i]);
                 uint2 wh, wl;
                 split_bf16x2(xv[0] - accY[4 * rb], xv[1] - accY[4 * rb + 1], wh.x, wl.x);
                 split_bf16x2(xv[2] - accY[4 * rb + 2], xv[3] - accY[4 * rb + 3], wh.y, wl.y);
@@ -516,8 +576,9 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 xa[kk] = Xs[(32 + 16 * qr + m16) * LP + 32 + 4 * kk + g16];
-                ra[kk] = Rtmp[(4 * kk + g16) * 36 + 16 * qc + m16];
+                ra[kk] = Rtmp[(4 * kk + g16) * RP + 16 * qc + m16];
             }
+            issue_fence();
             f32x4 z = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
@@ -560,16 +621,23 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         if (wave < 4) {
             const int u_tb = wave >> 1, u_ib = wave & 1;
             f32x16 accU = {};
+            bf16x8 ah[4], al[4], yh[4], yl[4];
 #pragma unroll
-            for (int kk = 0; kk < 64; kk += 16) {
-                if (kk < 32 * (u_tb + 1)) {  // A is lower triangular
-                    const bf16x8 ah = frag(A_hi, CP, 32 * u_tb, kk, ln);
-                    const bf16x8 al = frag(A_lo, CP, 32 * u_tb, kk, ln);
-                    const bf16x8 yh = frag(Yt_hi, CP, 32 * u_ib, kk, ln);
-                    const bf16x8 yl = frag(Yt_lo, CP, 32 * u_ib, kk, ln);
-                    accU = mfma(ah, yh, accU);
-                    accU = mfma(al, yh, accU);
-                    accU = mfma(ah, yl, accU);
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (u_tb + 1)) {  // A is lower triangular
+                    ah[kk] = frag(A_hi, CP, 32 * u_tb, 16 * kk, ln);
+                    al[kk] = frag(A_lo, CP, 32 * u_tb, 16 * kk, ln);
+                    yh[kk] = frag(Yt_hi, CP, 32 * u_ib, 16 * kk, ln);
+                    yl[kk] = frag(Yt_lo, CP, 32 * u_ib, 16 * kk, ln);
+                }
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (u_tb + 1)) {
+                    accU = mfma(ah[kk], yh[kk], accU);
+                    accU = mfma(al[kk], yh[kk], accU);
+                    accU = mfma(ah[kk], yl[kk], accU);
                 }
             }
 #pragma unroll
@@ -587,23 +655,31 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         // ======== O^T = e^G (S Q^T + U^T P^T) staged as bf16 O [t][i] (waves 4-7);
         // S^T = diag(gamma)(S^T + K^T U) (all waves)
         if (wave >= 4) {
+            bf16x8 uh[4], ul[4], ph[4], pl[4];
 #pragma unroll
-            for (int kk = 0; kk < 64; kk += 16) {
-                if (kk < 32 * (o_tb + 1)) {  // P is lower triangular
-                    const bf16x8 uh = frag(Ut_hi, CP, 32 * o_ib, kk, ln);
-                    const bf16x8 ul = frag(Ut_lo, CP, 32 * o_ib, kk, ln);
-                    const bf16x8 ph = frag(P_hi, CP, 32 * o_tb, kk, ln);
-                    const bf16x8 pl = frag(P_lo, CP, 32 * o_tb, kk, ln);
-                    accO = mfma(uh, ph, accO);
-                    accO = mfma(ul, ph, accO);
-                    accO = mfma(uh, pl, accO);
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (o_tb + 1)) {  // P is lower triangular
+                    uh[kk] = frag(Ut_hi, CP, 32 * o_ib, 16 * kk, ln);
+                    ul[kk] = frag(Ut_lo, CP, 32 * o_ib, 16 * kk, ln);
+                    ph[kk] = frag(P_hi, CP, 32 * o_tb, 16 * kk, ln);
+                    pl[kk] = frag(P_lo, CP, 32 * o_tb, 16 * kk, ln);
                 }
             }
-            const int t = 32 * o_tb + (ln & 31);
+            const int tq = 32 * o_tb + (ln & 31);
             f32x4 g4[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
-                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + t * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
+                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + tq * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 2 * (o_tb + 1)) {
+                    accO = mfma(uh[kk], ph[kk], accO);
+                    accO = mfma(ul[kk], ph[kk], accO);
+                    accO = mfma(uh[kk], pl[kk], accO);
+                }
+            }
+            const int t = tq;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 const int i = 32 * o_ib + 8 * rb + 4 * (ln >> 5);
@@ -614,13 +690,20 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             }
         }
         if (owns_s) {
+            bf16x8 kt[4], uh[4], ul[4];
 #pragma unroll
-            for (int kk = 0; kk < 64; kk += 16) {
-                const bf16x8 kt = frag(Kt, CP, 32 * s_jt, kk, ln);
-                accS = mfma(kt, frag(Ut_hi, CP, 32 * s_it, kk, ln), accS);
-                accS = mfma(kt, frag(Ut_lo, CP, 32 * s_it, kk, ln), accS);
+            for (int kk = 0; kk < 4; ++kk) {
+                kt[kk] = frag(Kt, CP, 32 * s_jt, 16 * kk, ln);
+                uh[kk] = frag(Ut_hi, CP, 32 * s_it, 16 * kk, ln);
+                ul[kk] = frag(Ut_lo, CP, 32 * s_it, 16 * kk, ln);
             }
             const float gm = gam[32 * s_it + (ln & 31)];
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                accS = mfma(kt[kk], uh[kk], accS);
+                accS = mfma(kt[kk], ul[kk], accS);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) accS[r] *= gm;
         }
