@@ -38,6 +38,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch recorded in profiles/traffic.json, or None when the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    import json
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    m = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "gated_delta_rule_72_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    if m.hexdigest()[:16] != rec["source_sha256"]:
+        return None
+    return int(1024 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -159,7 +179,7 @@ def bench_prefill(args, torch, kda, I):
         tokens_per_s=B * T * args.steps / wall, ms_per_step=wall * 1e3 / args.steps,
         launch_ms=dict(avg=avg_ms, min=float(np.min(launch_ms)), max=float(np.max(launch_ms))),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic("prefill"),
                       kernel="prefill (chunkwise, fused)", alg_bytes_per_launch=alg_bytes,
                       mfma_nominal_tflops=round(nominal_tflops, 1),
                       mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
@@ -235,7 +255,8 @@ def bench_decode(args, torch, kda, I):
         ms_total=round(ms, 3), wall_s=round(wall, 3), us_per_step=round(ms * 1e3 / n, 2),
         state_GBps=round(2 * state_bytes * steps_per_s / 1e9, 1),
         roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_step",
+                      frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("decode"),
+                      kernel="decode_step",
                       alg_bytes_per_launch=step_bytes),
     )
     # parity on sampled (b, h) pairs over all n steps
