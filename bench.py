@@ -152,9 +152,11 @@ def bench_prefill(args, torch, kda, I):
     B, T, H, d = w["n_seq"], w["T"], w["H"], w["dk"]
     o = torch.empty((B * T, H, d), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, kda.workspace_size(B, B * T, H, d, d, kda.KDA_DTYPE_BF16)), dtype=torch.uint8,
+                     device=dev)
 
     def step():
-        kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T)
+        kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T, workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -43,9 +43,10 @@ constexpr int PREFILL_CHUNK_F32 = 32;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill_valu_bf16(const PrefillArgs& a, hipStream_t stream);
 
-// Workspace bytes the prefill launchers need (the varlen schedule).
+// Workspace bytes of the fp32 prefill (the varlen schedule) and of the bf16
+// prefill (schedule, chunk offsets and the per-(chunk, head) solved A blocks).
 size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
+size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads);
 
 }  // namespace kda

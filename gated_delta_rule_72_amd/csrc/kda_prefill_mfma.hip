@@ -1,5 +1,5 @@
-// kda_prefill_mfma.hip -- fused chunkwise KDA prefill for bf16 inputs on
-// CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// kda_prefill_mfma.hip -- chunkwise KDA prefill for bf16 inputs on CDNA4
+// matrix cores (bf16 MFMA with fp32 accumulation).
 //
 // Method: page "Kimi (AI)", section "Kimi Delta Attention (KDA)" -- the state S
 // is d_v x d_k (rows = value channels) and the forget gate diag(alpha_t) scales
@@ -16,20 +16,20 @@
 // elementwise scalings.  Token rows past the end of a sequence read as k = q =
 // v = 0, beta = 0 and log alpha = 0, which change nothing.
 //
-// Work decomposition: one workgroup of 8 waves per (sequence, head, block of
-// 64 value rows) walks its sequence chunk by chunk, holding S^T in fp32 MFMA
-// accumulators (one 32x32 tile per wave) for the whole scan, with a bf16 copy
-// in LDS as the operand of Q S^T and K S^T.  The S-independent solve runs on
-// waves 0-3 while waves 4-7 form Q S^T and K S^T.  The next chunk's inputs are
-// loaded into registers while the current chunk computes; barriers order LDS
-// only, so those loads (and the output stores) stay in flight across them.
+// Two kernels.  A depends on k and beta only, never on S, so chunk_solve_kernel
+// solves it for every (chunk, head) at once and hands it to the scan through
+// the workspace as hi/lo bf16.  scan_kernel then walks each sequence chunk by
+// chunk with only the S-dependent products on its critical path: one
+// workgroup of 8 waves per (sequence, head, block of 64 value rows) holds S^T
+// in fp32 MFMA accumulators for the whole scan, with four workgroup barriers
+// per chunk.
 //
 // Precision: q, k, v are exact bf16 inputs.  Computed operands are carried as
 // hi + lo bf16 pairs (x = hi + lo to ~2^-16 relative) where the error budget
 // needs it -- A, V e^{-G} - K S^T, U and P = tril(Q K^T) -- and S is a single
 // bf16 copy of the fp32 state.  A product of two split operands takes three
-// MFMAs (hi*hi + lo*hi + hi*lo).  The solve itself runs in fp32 (VALU forward
-// substitution on 16x16 diagonal blocks, fp32 MFMA for the off-diagonal blocks).
+// MFMAs (hi*hi + lo*hi + hi*lo).  The solve runs in fp32: VALU forward
+// substitution on 16x16 diagonal blocks, fp32 MFMA for the off-diagonal blocks.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
@@ -38,10 +38,16 @@ namespace kda {
 namespace {
 
 constexpr int C = PREFILL_CHUNK_BF16;  // 64 tokens per chunk
-constexpr int BV = 64;                 // value rows per workgroup
-constexpr int NW = 8;                  // waves per workgroup
-constexpr int NT = NW * 64;            // threads per workgroup
+constexpr int BV = 64;                 // value rows per scan workgroup
 constexpr int PAD = 8;                 // bf16 row padding (16 bytes) against bank conflicts
+constexpr int CP = C + PAD;            // pitch of bf16 rows of length C
+constexpr int LP = C + 4;              // pitch of fp32 rows of length C
+// A of one (chunk, head): the three nonzero 32x32 blocks (rows 0-31 x cols 0-31,
+// rows 32-63 x cols 0-31, rows 32-63 x cols 32-63), each as hi then lo bf16,
+// row-major; entries above the diagonal are zero.
+constexpr int A_BLOCK_ELEMS = 32 * 32;
+constexpr int A_RECORD_BYTES = 3 * 2 * A_BLOCK_ELEMS * 2;
+constexpr int A_RECORD_PIECES = A_RECORD_BYTES / 16;  // 16-byte pieces
 // word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -71,6 +77,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15].
 __device__ __forceinline__ f32x4 mfma16f(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -79,11 +86,6 @@ __device__ __forceinline__ f32x4 mfma16f(float a, float b, f32x4 c) {
 // D[row = 8*(r/4) + 4*(l>>5) + (r&3)][col = l & 31]; of a 16x16 tile: register
 // r holds D[4*(l>>4) + r][l & 15].
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16_bits(x);
-    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-}
 
 // Compiler-only fence: the LDS operand loads above it are issued before the
 // matrix instructions below it, so their latencies overlap instead of each
@@ -99,102 +101,372 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
 }
 
-// Shared-memory layout (bytes).  Regions are reused across the phases of a
-// chunk; the comments give each region's tenants in order.  Each region is its
-// own __shared__ array, so the compiler knows that accesses to different
-// regions never alias and can move loads ahead of unrelated stores.
-template <int DK>
-struct Smem {
-    static constexpr int KP = DK + PAD;     // pitch of [t][j] bf16 rows
-    static constexpr int CP = C + PAD;      // pitch of [x][t] bf16 rows (length C)
-    // pitch of C x C fp32 rows: 80 = 16 mod 64 makes the column-wise operand
-    // loads of the fp32 matrix-core solve (rows 4k + g, columns m) hit distinct banks
-    static constexpr int LP = C + 16;
-    static constexpr int RP = 48;           // pitch of the 32 x 32 solve temporary
-    static constexpr int mx(int a, int b) { return a > b ? a : b; }
-    static constexpr int HILO = 2 * C * CP * 2;  // a C x C (or BV x C) hi/lo bf16 pair
-    // R0: K [t][j] -> solve temporary (fp32 32 x RP) -> A hi/lo [t][s]
-    static constexpr int R0 = 0;
-    static constexpr int R0_SZ = mx(mx(C * KP * 2, 32 * RP * 4), HILO);
-    // R1: Q [t][j] -> Y^T hi/lo [i][t]
-    static constexpr int R1 = R0 + R0_SZ;
-    static constexpr int R1_SZ = mx(C * KP * 2, HILO);
-    // R2: K^T [j][t]
-    static constexpr int R2 = R1 + R1_SZ;
-    static constexpr int R2_SZ = DK * CP * 2;
-    // R3: L fp32 [t][s] -> U^T hi/lo [i][t]
-    static constexpr int R3 = R2 + R2_SZ;
-    static constexpr int R3_SZ = mx(C * LP * 4, HILO);
-    // R4: (I + L)^{-1} fp32 [t][s] -> O bf16 [t][i] (stored at the next chunk)
-    static constexpr int R4 = R3 + R3_SZ;
-    static constexpr int R4_SZ = mx(C * LP * 4, C * (BV + PAD) * 2);
-    // R5: P = tril(Q K^T) hi/lo [t][s]
-    static constexpr int R5 = R4 + R4_SZ;
-    static constexpr int R5_SZ = HILO;
-    // R6: V bf16 [t][i] as loaded
-    static constexpr int R6 = R5 + R5_SZ;
-    static constexpr int R6_SZ = C * (BV + PAD) * 2;
-    // R7: S bf16 [i][j] (operand copy of the fp32 state)
-    static constexpr int R7 = R6 + R6_SZ;
-    static constexpr int R7_SZ = BV * KP * 2;
-    // R8: log alpha -> per-part local prefix sums -> G, fp32 [t][i]
-    static constexpr int GP = BV + 4;       // pitch of G rows
-    static constexpr int R8 = R7 + R7_SZ;
-    static constexpr int R8_SZ = C * GP * 4;
-    // R9: beta [C], gamma [BV], partial scan sums [8][BV]
-    static constexpr int R9 = R8 + R8_SZ;
-    static constexpr int R9_SZ = (C + BV + 8 * BV) * 4;
-    static constexpr int TOTAL = R9 + R9_SZ;
+__device__ inline int64_t seq_start(int seq, int n_seq, int n_tok, const int32_t* cu) {
+    return cu ? static_cast<int64_t>(cu[seq]) : static_cast<int64_t>(seq) * (n_tok / n_seq);
+}
+
+// Token range [t0, t0 + n) of global chunk gc; chunk_off[m] is the first global
+// chunk of sequence m and chunk_off[n_seq] the number of chunks.
+struct ChunkRef {
+    int64_t t0;
+    int n;
 };
+
+__device__ inline ChunkRef chunk_ref(int gc, int n_seq, int n_tok, const int32_t* cu,
+                                     const int32_t* chunk_off) {
+    int lo = 0, hi = n_seq;  // chunk_off[lo] <= gc < chunk_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= gc) lo = mid;
+        else hi = mid;
+    }
+    const int64_t s0 = seq_start(lo, n_seq, n_tok, cu), s1 = seq_start(lo + 1, n_seq, n_tok, cu);
+    ChunkRef r;
+    r.t0 = s0 + static_cast<int64_t>(gc - chunk_off[lo]) * C;
+    r.n = static_cast<int>(min<int64_t>(C, s1 - r.t0));
+    return r;
+}
 
 }  // namespace
 
+// ============================================================================
+// chunk_offsets_kernel: chunk_off[m] = sum_{m' < m} ceil(len_m' / C) for
+// m = 0 .. n_seq; one workgroup.
+// ============================================================================
+__global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __restrict__ cu, int n_seq,
+                                                             int n_tok, int32_t* __restrict__ chunk_off) {
+    __shared__ int32_t part[1024];
+    const int tid = static_cast<int>(threadIdx.x);
+    int32_t carry = 0;
+    for (int base = 0; base < n_seq; base += 1024) {
+        const int m = base + tid;
+        int32_t cnt = 0;
+        if (m < n_seq) {
+            const int64_t len = seq_start(m + 1, n_seq, n_tok, cu) - seq_start(m, n_seq, n_tok, cu);
+            cnt = static_cast<int32_t>((len + C - 1) / C);
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
+            const int32_t add = tid >= d ? part[tid - d] : 0;
+            __syncthreads();
+            part[tid] += add;
+            __syncthreads();
+        }
+        if (m < n_seq) chunk_off[m] = carry + part[tid] - cnt;
+        carry += part[1023];
+        __syncthreads();
+    }
+    if (tid == 0) chunk_off[n_seq] = carry;
+}
+
+// ============================================================================
+// chunk_solve_kernel: A = (I + L)^{-1} diag(beta) of one (chunk, head) per
+// workgroup of 4 waves, written as the A record described above.  The inverse
+// X = (I + L)^{-1} is built by blocks: 16x16 diagonal blocks by forward
+// substitution, then X21 = -X22 L21 X11 at 16 and at 32 rows.
+// ============================================================================
+template <int DK>
+__global__ __launch_bounds__(256) void chunk_solve_kernel(
+    const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
+    uint16_t* __restrict__ arec) {
+    constexpr int KP = DK + PAD;
+    constexpr int RP = 36;  // pitch of the 32x32 fp32 temporary
+    __shared__ __align__(16) uint16_t Kc[C * KP];  // K [t][j]; later the solve temporary
+    __shared__ __align__(16) float Lf[C * LP];     // L [t][s]
+    __shared__ __align__(16) float Xs[C * LP];     // X = (I + L)^{-1} [t][s]
+    __shared__ __align__(16) float bs[C];
+    static_assert(32 * RP * 4 <= C * KP * 2, "temporary fits in the K buffer");
+    float* Rtmp = reinterpret_cast<float*>(Kc);
+
+    const int gc = static_cast<int>(blockIdx.x) / n_heads, h = static_cast<int>(blockIdx.x) % n_heads;
+    if (gc >= max_chunks || gc >= chunk_off[n_seq]) return;
+    const ChunkRef ch = chunk_ref(gc, n_seq, n_tok, cu_seqlens, chunk_off);
+    const int64_t H = n_heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g16 = lane >> 4, m16 = lane & 15;
+
+    // ---- K and beta of the chunk (rows past the sequence end read as zero)
+    {
+        const int64_t tok0 = ch.t0 * H + h;
+        const auto rk = make_rsrc(k + tok0 * DK, ((ch.n - 1) * H * DK + DK) * 2);
+        constexpr int PIECES = C * DK / 8;
+#pragma unroll
+        for (int p = 0; p < PIECES / 256; ++p) {
+            const int idx = tid + 256 * p, t = idx / (DK / 8), c = idx % (DK / 8);
+            const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(
+                rk, static_cast<int>(t * H * DK + 8 * c) * 2, 0, 0);
+            *reinterpret_cast<u32x4*>(Kc + t * KP + 8 * c) = val;
+        }
+        if (tid < C) {
+            const auto rb = make_rsrc(beta + tok0, ((ch.n - 1) * H + 1) * 4);
+            bs[tid] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(tid * H) * 4, 0, 0));
+        }
+    }
+    block_sync();
+
+    // ---- L = strictly_lower(diag(beta) K K^T).  Wave 0: the four 16x16 diagonal
+    // blocks, then their inverses T_b = (I + L_bb)^{-1} (lane = (block, column)).
+    // Wave 1: rows 32-63 x cols 0-31.  Waves 2, 3: the blocks (16..31, 0..15) and
+    // (48..63, 32..47).
+    if (wave == 0) {
+        f32x4 d[4] = {};
+        bf16x8 kf[4][DK / 32];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) kf[b][kk] = frag16(Kc, KP, 16 * b, 32 * kk, lane);
+        issue_fence();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) d[b] = mfma16(kf[b][kk], kf[b][kk], d[b]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * b + 4 * g16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g16 + r;  // within the block
+                Lf[(16 * b + row) * LP + 16 * b + m16] = m16 < row ? b4[r] * d[b][r] : 0.f;
+            }
+        }
+        wave_lds_sync();
+        const int b = g16, c = m16;
+        const float* Lb = Lf + (16 * b) * LP + 16 * b;
+        // The strictly lower rows are loaded in two batches ahead of the
+        // substitution, so no LDS round trip sits inside its dependent chain.
+        // Piece p enumerates (row r = 1..15, columns s4..s4+3 < r + 3).
+        f32x4 lrow[36];
+        auto load_rows = [&](int r_lo, int r_hi) {
+#pragma unroll
+            for (int r = 1, p = 0; r < 16; ++r)
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4, ++p)
+                    if (r >= r_lo && r < r_hi) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+        };
+        float x[16];
+        auto solve_rows = [&](int r_lo, int r_hi) {
+#pragma unroll
+            for (int r = 1, p = 0; r < 16; ++r) {
+                float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4, ++p) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (r >= r_lo && r < r_hi && s4 + e < r) {
+                            if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
+                            else acc0 -= lrow[p][e] * x[s4 + e];
+                        }
+                    }
+                }
+                if (r >= r_lo && r < r_hi) x[r] = acc0 + acc1;  // zero for r < c
+            }
+        };
+        x[0] = c == 0 ? 1.f : 0.f;
+        load_rows(1, 10);
+        issue_fence();
+        solve_rows(1, 6);
+        load_rows(10, 16);
+        issue_fence();
+        solve_rows(6, 16);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
+    } else if (wave == 1) {
+        f32x16 acc = {};
+        bf16x8 fa[DK / 16], fb[DK / 16];
+#pragma unroll
+        for (int kk = 0; kk < DK / 16; ++kk) {
+            fa[kk] = frag(Kc, KP, 32, 16 * kk, lane);
+            fb[kk] = frag(Kc, KP, 0, 16 * kk, lane);
+        }
+        issue_fence();
+#pragma unroll
+        for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
+        f32x4 b4[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (lane >> 5));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lf[(32 + acc_row(r, lane)) * LP + (lane & 31)] = b4[r >> 2][r & 3] * acc[r];
+    } else {
+        const int R = wave == 2 ? 16 : 48, Cc = R - 16;
+        f32x4 d = {};
+        bf16x8 fa[DK / 32], fb[DK / 32];
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            fa[kk] = frag16(Kc, KP, R, 32 * kk, lane);
+            fb[kk] = frag16(Kc, KP, Cc, 32 * kk, lane);
+        }
+        issue_fence();
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) d = mfma16(fa[kk], fb[kk], d);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + R + 4 * g16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
+    }
+    block_sync();
+
+    // ---- 16-row level (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for the 16x16
+    // blocks (16, 0) and (48, 32)
+    if (wave < 2) {
+        const int R = 16 * (2 * wave + 1), Cc = 16 * (2 * wave);
+        float la[4], xa[4], ta[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            la[kk] = Lf[(R + m16) * LP + Cc + 4 * kk + g16];
+            xa[kk] = Xs[(Cc + 4 * kk + g16) * LP + Cc + m16];
+            ta[kk] = Xs[(R + m16) * LP + R + 4 * g16 + kk];
+        }
+        issue_fence();
+        f32x4 y = {};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) y = mfma16f(la[kk], xa[kk], y);
+        // y (row 4*g16 + r, column m16) feeds the next product directly as its B
+        // operand: step r uses reduction index 4*g16 + r, matched on the A side
+        f32x4 z = {};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z = mfma16f(ta[r], y[r], z);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
+    }
+    block_sync();
+
+    // ---- 32-row level, first half: Y2 = L[32:64, 0:32] X[0:32, 0:32], one 16x16
+    // quadrant per wave
+    const int qr = wave >> 1, qc = wave & 1;
+    {
+        float la[8], xa[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            la[kk] = Lf[(32 + 16 * qr + m16) * LP + 4 * kk + g16];
+            xa[kk] = Xs[(4 * kk + g16) * LP + 16 * qc + m16];
+        }
+        issue_fence();
+        f32x4 y = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            if (kk >= 4 * qc) y = mfma16f(la[kk], xa[kk], y);  // X[0:32, 0:32] is block-lower
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * RP + 16 * qc + m16] = y[r];
+    }
+    block_sync();
+
+    // ---- second half: X[32:64, 0:32] = -X[32:64, 32:64] Y2
+    {
+        float xa[8], ra[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            xa[kk] = Xs[(32 + 16 * qr + m16) * LP + 32 + 4 * kk + g16];
+            ra[kk] = Rtmp[(4 * kk + g16) * RP + 16 * qc + m16];
+        }
+        issue_fence();
+        f32x4 z = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            if (kk < 4 * (qr + 1)) z = mfma16f(xa[kk], ra[kk], z);  // X[32:64, 32:64] is block-lower
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[(32 + 16 * qr + 4 * g16 + r) * LP + 16 * qc + m16] = -z[r];
+    }
+    block_sync();
+
+    // ---- A = X diag(beta) -> the record.  Item = (block, row, 8-column piece);
+    // entries above the diagonal (never written in Xs) are selected away.
+    uint16_t* rec = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
+    for (int item = tid; item < 3 * 32 * 4; item += 256) {
+        const int blk = item >> 7, row = (item >> 2) & 31, c8 = 8 * (item & 3);
+        const int t = (blk == 0 ? 0 : 32) + row, s0 = (blk == 2 ? 32 : 0) + c8;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + s0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + s0 + 4);
+        float av[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = e < 4 ? x0[e] * b0[e] : x1[e - 4] * b1[e - 4];
+            av[e] = s0 + e <= t ? xv : 0.f;
+        }
+        u32x4 wh, wl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t a, b;
+            split_bf16x2(av[2 * e], av[2 * e + 1], a, b);
+            wh[e] = a;
+            wl[e] = b;
+        }
+        uint16_t* dst = rec + blk * 2 * A_BLOCK_ELEMS + row * 32 + c8;
+        *reinterpret_cast<u32x4*>(dst) = wh;
+        *reinterpret_cast<u32x4*>(dst + A_BLOCK_ELEMS) = wl;
+    }
+}
+
+// ============================================================================
+// scan_kernel: the S-dependent chunk products, one workgroup of 8 waves per
+// (sequence, head, block of 64 value rows).
+// ============================================================================
+template <int DK>
+struct ScanSmem {
+    static constexpr int KP = DK + PAD;     // pitch of K, Q, S rows (bf16)
+    static constexpr int GP = BV + 4;       // pitch of G rows (fp32)
+    static constexpr int OP = BV + PAD;     // pitch of V and O rows (bf16)
+    static constexpr int mx(int a, int b) { return a > b ? a : b; }
+    static constexpr int HILO = 2 * C * CP * 2;
+    // each region is its own __shared__ array, so the compiler knows accesses to
+    // different regions never alias and can move loads ahead of unrelated stores
+    static constexpr int RK = mx(C * KP * 2, HILO);   // K [t][j], then U^T hi/lo [i][t]
+    static constexpr int RQ = C * KP * 2;             // Q [t][j]
+    static constexpr int RKT = DK * CP * 2;           // K^T [j][t]
+    static constexpr int RV = C * OP * 2;             // V [t][i]
+    static constexpr int RG = C * GP * 4;             // G [t][i]
+    static constexpr int RA = HILO;                   // A hi/lo [t][s]
+    static constexpr int RP = HILO;                   // P hi/lo [t][s]
+    static constexpr int RY = mx(HILO, C * OP * 2);   // Y^T hi/lo [i][t], then O [t][i]
+    static constexpr int RS = BV * KP * 2;            // S bf16 [i][j]
+    static constexpr int RB = BV * 4;                 // gamma = e^{G[C-1, :]}
+    static constexpr int TOTAL = RK + RQ + RKT + RV + RG + RA + RP + RY + RS + RB;
+};
+
 template <int DK, int DV>
-__global__ __launch_bounds__(NT) void prefill_mfma_kernel(
+__global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta,
-    const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
+    const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
+    const uint16_t* __restrict__ arec, int n_seq, int n_tok, int n_heads,
     uint16_t* __restrict__ o, float* __restrict__ S_T) {
-    using SM = Smem<DK>;
+    using SM = ScanSmem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, CP = SM::CP, LP = SM::LP, GP = SM::GP, RP = SM::RP;
-    constexpr int OP = BV + PAD;           // pitch of the staged O and V rows
-    constexpr int JT = DK / 32;            // 32-wide tiles along d_k
+    constexpr int KP = SM::KP, GP = SM::GP, OP = SM::OP;
+    constexpr int JT = DK / 32;  // 32-wide tiles along d_k
 
-    __shared__ __align__(16) unsigned char r0[SM::R0_SZ];
-    __shared__ __align__(16) unsigned char r1[SM::R1_SZ];
-    __shared__ __align__(16) unsigned char r2[SM::R2_SZ];
-    __shared__ __align__(16) unsigned char r3[SM::R3_SZ];
-    __shared__ __align__(16) unsigned char r4[SM::R4_SZ];
-    __shared__ __align__(16) unsigned char r5[SM::R5_SZ];
-    __shared__ __align__(16) unsigned char r6[SM::R6_SZ];
-    __shared__ __align__(16) unsigned char r7[SM::R7_SZ];
-    __shared__ __align__(16) unsigned char r8[SM::R8_SZ];
-    __shared__ __align__(16) unsigned char r9[SM::R9_SZ];
-    uint16_t* Kc = reinterpret_cast<uint16_t*>(r0);
-    float* Rtmp = reinterpret_cast<float*>(r0);
-    uint16_t* A_hi = reinterpret_cast<uint16_t*>(r0);
-    uint16_t* A_lo = A_hi + C * CP;
-    uint16_t* Qc = reinterpret_cast<uint16_t*>(r1);
-    uint16_t* Yt_hi = reinterpret_cast<uint16_t*>(r1);
-    uint16_t* Yt_lo = Yt_hi + BV * CP;
-    uint16_t* Kt = reinterpret_cast<uint16_t*>(r2);
-    float* Lf = reinterpret_cast<float*>(r3);
-    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(r3);
+    __shared__ __align__(16) unsigned char rk_[SM::RK];
+    __shared__ __align__(16) unsigned char rq_[SM::RQ];
+    __shared__ __align__(16) unsigned char rkt_[SM::RKT];
+    __shared__ __align__(16) unsigned char rv_[SM::RV];
+    __shared__ __align__(16) unsigned char rg_[SM::RG];
+    __shared__ __align__(16) unsigned char ra_[SM::RA];
+    __shared__ __align__(16) unsigned char rp_[SM::RP];
+    __shared__ __align__(16) unsigned char ry_[SM::RY];
+    __shared__ __align__(16) unsigned char rs_[SM::RS];
+    __shared__ __align__(16) unsigned char rb_[SM::RB];
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(rk_);
+    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(rk_);
     uint16_t* Ut_lo = Ut_hi + BV * CP;
-    float* Xs = reinterpret_cast<float*>(r4);
-    uint16_t* Os = reinterpret_cast<uint16_t*>(r4);
-    uint16_t* P_hi = reinterpret_cast<uint16_t*>(r5);
+    uint16_t* Qc = reinterpret_cast<uint16_t*>(rq_);
+    uint16_t* Kt = reinterpret_cast<uint16_t*>(rkt_);
+    uint16_t* Vr = reinterpret_cast<uint16_t*>(rv_);
+    float* Gs = reinterpret_cast<float*>(rg_);
+    uint16_t* A_hi = reinterpret_cast<uint16_t*>(ra_);
+    uint16_t* A_lo = A_hi + C * CP;
+    uint16_t* P_hi = reinterpret_cast<uint16_t*>(rp_);
     uint16_t* P_lo = P_hi + C * CP;
-    uint16_t* Vr = reinterpret_cast<uint16_t*>(r6);
-    uint16_t* Sb = reinterpret_cast<uint16_t*>(r7);
-    float* Gs = reinterpret_cast<float*>(r8);
-    float* bs = reinterpret_cast<float*>(r9);
-    float* gam = bs + C;
-    float* psum = gam + BV;
+    uint16_t* Yt_hi = reinterpret_cast<uint16_t*>(ry_);
+    uint16_t* Yt_lo = Yt_hi + BV * CP;
+    uint16_t* Os = reinterpret_cast<uint16_t*>(ry_);
+    uint16_t* Sb = reinterpret_cast<uint16_t*>(rs_);
+    float* gam = reinterpret_cast<float*>(rb_);
 
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
@@ -206,8 +478,10 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
     const int h = u.head;
     const int i0 = u.vblk * BV;
     const int64_t row_qk = H * DK, row_v = H * DV;  // element strides between tokens
+    const int chunk0 = chunk_off[u.seq];
 
-    // ---- state: wave w owns S^T tile (j-tile s_jt, i-tile s_it) in fp32 accumulators
+    // ---- state: wave w < 2 * JT owns the S^T tile (j-tile s_jt, i-tile s_it)
+    // in fp32 accumulators
     const bool owns_s = wave < 2 * JT;
     const int s_jt = wave % JT, s_it = wave / JT;
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
@@ -220,20 +494,17 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         }
     }
 
-    // ---- register prefetch of one chunk's inputs; every load moves 16 bytes
-    // per lane, so one wave instruction covers 1 KB of whole cache lines.
-    // K, Q: thread (row pair tp, 16-byte chunk c) holds rows 2tp, 2tp+1 (with
-    // d_k = 64 the upper four waves repeat the lower four).
-    // V: thread (row td/8, 8 values at 8*(td%8)); alpha: rows td/16 and 32 + td/16,
-    // 4 values at 4*(td%16); beta: wave 0, lane = token.
+    // ---- register prefetch of one chunk's inputs; every load moves 16 bytes per lane.
+    // K, Q: thread (row pair tp, 16-byte piece c) holds rows 2tp, 2tp+1 (with
+    //   d_k = 64 the upper four waves repeat the lower four).
+    // V: row tid/8, 8 values at 8*(tid%8).
+    // alpha: lane = token, wave w = the 8 value rows 8w..8w+7 (the decay scan runs
+    //   across lanes).
+    // A record: pieces tid and tid + 512.
     const int kq_tp = lane & 31, kq_c = (2 * wave + (lane >> 5)) % (DK / 8);
-    const int gpart = wave;
-    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {}, pv = {};
+    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {}, pv = {}, pA0 = {}, pA1 = {};
     f32x4 pa0 = {}, pa1 = {};
-    float pb = 0.f;
-    // Rows past the sequence end read as zeros through the buffer range, so
-    // no load needs a per-row branch.
-    auto prefetch = [&](int64_t tc, int n) {
+    auto prefetch = [&](int64_t tc, int n, int gc) {
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
         {
             const int64_t bytes = ((n - 1) * row_qk + DK) * 2;
@@ -248,15 +519,18 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         }
         {
             const auto rv = make_rsrc(v + tok0 * DV + i0, ((n - 1) * row_v + BV) * 2);
-            pv = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2, 0, 0);
+            pv = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2,
+                                                       0, 0);
             const auto ra = make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4);
-            const int offa = static_cast<int>((tid >> 4) * row_v + 4 * (tid & 15)) * 4;
+            const int offa = static_cast<int>(lane * row_v + 8 * wave) * 4;
             pa0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, 0));
-            pa1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + static_cast<int>(32 * row_v) * 4, 0, 0));
+            pa1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + 16, 0, 0));
         }
-        if (wave == 0) {  // beta of token `lane`: one cache line per token, so one wave only
-            const auto rb = make_rsrc(beta + tok0, ((n - 1) * H + 1) * 4);
-            pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(lane * H) * 4, 0, 0));
+        {
+            const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
+            const auto rr = make_rsrc(recp, A_RECORD_BYTES);
+            pA0 = __builtin_amdgcn_raw_buffer_load_b128(rr, tid * 16, 0, 0);
+            pA1 = __builtin_amdgcn_raw_buffer_load_b128(rr, (tid + 512) * 16, 0, 0);  // past the end for tid >= 256
         }
     };
 
@@ -270,7 +544,12 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
     };
 
-    if (u.t0 < u.t1) prefetch(u.t0, chunk_len(u.t0));
+    // one 16-byte piece of an A record -> A hi/lo [t][s]
+    auto stage_a = [&](u32x4 val, int piece) {
+        const int blk = piece >> 8, half = (piece >> 7) & 1, row = (piece >> 2) & 31, c8 = 8 * (piece & 3);
+        uint16_t* dst = (half ? A_lo : A_hi) + ((blk == 0 ? 0 : 32) + row) * CP + (blk == 2 ? 32 : 0) + c8;
+        *reinterpret_cast<u32x4*>(dst) = val;
+    };
 
     // bf16 copy of the state for the S-side products (S^T registers 4rb..4rb+3
     // hold 4 consecutive key channels j of one value row i)
@@ -286,11 +565,14 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
             }
         }
     };
+
+    if (u.t0 < u.t1) prefetch(u.t0, chunk_len(u.t0), chunk0);
     write_state_copy(lane);
 
     int64_t prev_tc = -1;
     int prev_n = 0;
-    for (int64_t tc = u.t0; tc < u.t1; tc += C) {
+    int gc = chunk0;
+    for (int64_t tc = u.t0; tc < u.t1; tc += C, ++gc) {
         const int n = chunk_len(tc);
         // Lane-derived values are recomputed every chunk from an opaque copy of
         // the lane id, so the compiler does not hoist dozens of loop-invariant
@@ -299,11 +581,10 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o;
         const int td = ln + 64 * wave;
-        const int g16 = ln >> 4, m16 = ln & 15;
         block_sync();  // the previous chunk is done with every buffer
 
-        // ======== stage this chunk; log-decay local scan (into G); previous
-        // chunk's O out; next chunk's loads in (they fly while this chunk computes)
+        // ======== stage this chunk, run the decay scan in registers, store the
+        // previous chunk's O, issue the next chunk's loads
         {
             const int rr = 2 * (ln & 31), c = (2 * wave + (ln >> 5)) % (DK / 8);
             *reinterpret_cast<u32x4*>(Kc + rr * KP + 8 * c) = pk0;
@@ -317,242 +598,56 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                 *reinterpret_cast<uint32_t*>(Kt + (8 * c + e) * CP + rr) = (lo & 0xffffu) | (hi << 16);
             }
         }
-        if (td < C) bs[td] = pb;
         *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pv;
+        stage_a(pA0, td);
+        if (td < A_RECORD_PIECES - 512) stage_a(pA1, td + 512);
         {
-            // log alpha, 0 for rows past the sequence end (they read as alpha = 0)
-            const int t = td >> 4, c = 4 * (td & 15);
-            f32x4 l0, l1;
+            // G[t, 8w+e] = inclusive scan over t (= lanes) of log alpha; rows past
+            // the sequence end (they read as alpha = 0) contribute 0
+            f32x4 g0, g1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                l0[e] = t < n ? __logf(pa0[e]) : 0.f;
-                l1[e] = t + 32 < n ? __logf(pa1[e]) : 0.f;
+                g0[e] = wave_inclusive_scan(ln < n ? __logf(pa0[e]) : 0.f);
+                g1[e] = wave_inclusive_scan(ln < n ? __logf(pa1[e]) : 0.f);
             }
-            *reinterpret_cast<f32x4*>(Gs + t * GP + c) = l0;
-            *reinterpret_cast<f32x4*>(Gs + (t + 32) * GP + c) = l1;
+            *reinterpret_cast<f32x4*>(Gs + ln * GP + 8 * wave) = g0;
+            *reinterpret_cast<f32x4*>(Gs + ln * GP + 8 * wave + 4) = g1;
+            if (ln == 63) {
+                f32x4 e0, e1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    e0[e] = __expf(g0[e]);
+                    e1[e] = __expf(g1[e]);
+                }
+                *reinterpret_cast<f32x4*>(gam + 8 * wave) = e0;
+                *reinterpret_cast<f32x4*>(gam + 8 * wave + 4) = e1;
+            }
         }
         if (prev_tc >= 0) store_o(prev_tc, prev_n, td);
-        if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C));
+        if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C), gc + 1);
         block_sync();
 
-        // ======== Gram products.  Wave 0: the four 16x16 diagonal blocks of L and
-        // their inverses T_b = (I + L_bb)^{-1} (forward substitution, lane =
-        // (block, column)).  Waves 1-3: the rest of L = strictly_lower(diag(beta)
-        // K K^T) (tile (1,0) and the two sub-diagonal 16x16 blocks).  Waves 4-6:
-        // P = tril(Q K^T) as hi/lo bf16, formed transposed (D[s][t]) so that each
-        // lane holds 4 consecutive s of one row t.
-        // local prefix sums of log alpha: thread (column ln, rows 8*gpart .. 8*gpart+7)
-        {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc += Gs[(8 * gpart + e) * GP + ln];
-                Gs[(8 * gpart + e) * GP + ln] = acc;
-            }
-            psum[gpart * BV + ln] = acc;
-        }
-        if (wave == 0) {
-            f32x4 d[4] = {};
-            bf16x8 kf[4][DK / 32];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) kf[b][kk] = frag16(Kc, KP, 16 * b, 32 * kk, ln);
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) d[b] = mfma16(kf[b][kk], kf[b][kk], d[b]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * b + 4 * g16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * g16 + r;  // within the block
-                    Lf[(16 * b + row) * LP + 16 * b + m16] = m16 < row ? b4[r] * d[b][r] : 0.f;
-                }
-            }
-            wave_lds_sync();
-            const int b = g16, c = m16;
-            const float* Lb = Lf + (16 * b) * LP + 16 * b;
-            // Row pieces of the strictly lower block are loaded in two batches
-            // (rows 1-9, then rows 10-15 once rows 0-5 are done), so no LDS round
-            // trip sits inside the dependent substitution chain.
-            f32x4 lrow[36];
-            auto load_rows = [&](int r_lo, int r_hi) {
-#pragma unroll
-                for (int r = 1, p = 0; r < 16; ++r)
-#pragma unroll
-                    for (int s4 = 0; s4 < r; s4 += 4, ++p)
-                        if (r >= r_lo && r < r_hi) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
-            };
-            float x[16];
-            auto solve_rows = [&](int r_lo, int r_hi) {
-#pragma unroll
-                for (int r = 0, p = 0; r < 16; ++r) {
-                    float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-                    for (int s4 = 0; s4 < r; s4 += 4, ++p) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (r >= r_lo && r < r_hi && s4 + e < r) {
-                                if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
-                                else acc0 -= lrow[p][e] * x[s4 + e];
-                            }
-                        }
-                    }
-                    if (r >= r_lo && r < r_hi) x[r] = acc0 + acc1;  // zero for r < c
-                }
-            };
-            load_rows(1, 10);
-            issue_fence();
-            solve_rows(0, 6);
-            load_rows(10, 16);
-            issue_fence();
-            solve_rows(6, 16);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
-        } else if (wave == 1) {
-            // tile (1,0): rows 32-63 x cols 0-31
-            f32x16 acc = {};
-            bf16x8 fa[DK / 16], fb[DK / 16];
-#pragma unroll
-            for (int kk = 0; kk < DK / 16; ++kk) {
-                fa[kk] = frag(Kc, KP, 32, 16 * kk, ln);
-                fb[kk] = frag(Kc, KP, 0, 16 * kk, ln);
-            }
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
-            f32x4 b4[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (ln >> 5));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 + acc_row(r, ln);
-                Lf[row * LP + (ln & 31)] = b4[r >> 2][r & 3] * acc[r];
-            }
-        } else if (wave < 4) {
-            // the 16x16 blocks (16..31, 0..15) (wave 2) and (48..63, 32..47) (wave 3)
-            const int R = wave == 2 ? 16 : 48, Cc = R - 16;
-            f32x4 d = {};
-            bf16x8 fa[DK / 32], fb[DK / 32];
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                fa[kk] = frag16(Kc, KP, R, 32 * kk, ln);
-                fb[kk] = frag16(Kc, KP, Cc, 32 * kk, ln);
-            }
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) d = mfma16(fa[kk], fb[kk], d);
-            const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + R + 4 * g16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
-        } else if (wave < 7) {
-            // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1)
-            const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
-            f32x16 acc = {};
-            bf16x8 fa[DK / 16], fb[DK / 16];
-#pragma unroll
-            for (int kk = 0; kk < DK / 16; ++kk) {
-                fa[kk] = frag(Kc, KP, 32 * sb, 16 * kk, ln);
-                fb[kk] = frag(Qc, KP, 32 * tb, 16 * kk, ln);
-            }
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
-            const int t = 32 * tb + (ln & 31);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int s0 = 32 * sb + 8 * rb + 4 * (ln >> 5);
-                float pv4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pv4[e] = s0 + e <= t ? acc[4 * rb + e] : 0.f;
-                uint2 wh, wl;
-                split_bf16x2(pv4[0], pv4[1], wh.x, wl.x);
-                split_bf16x2(pv4[2], pv4[3], wh.y, wl.y);
-                *reinterpret_cast<uint2*>(P_hi + t * CP + s0) = wh;
-                *reinterpret_cast<uint2*>(P_lo + t * CP + s0) = wl;
-            }
-        }
-        block_sync();
-
-        // ======== finish G and gamma (all waves, thread = (column ln, 8 rows));
-        // solve level 2 (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for the 16x16
-        // blocks (16, 0) and (48, 32); waves 4-7: O^T = S Q^T and K S^T
-        {
-            float off = 0.f;
-            for (int p = 0; p < gpart; ++p) off += psum[p * BV + ln];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Gs[(8 * gpart + e) * GP + ln] += off;
-            if (gpart == 7) gam[ln] = __expf(Gs[63 * GP + ln]);
-        }
-        f32x16 accO = {}, accY = {};
+        // ======== waves 0-3: K S^T, then Y = V e^{-G} - K S^T -> Y^T hi/lo [i][t];
+        // waves 4-7: O^T = S Q^T (kept in registers), and waves 4-6 the tiles of
+        // P = tril(Q K^T) hi/lo (formed transposed, D[s][t], so each lane holds 4
+        // consecutive s of one t)
+        f32x16 accO = {};
         const int o_ib = (wave - 4) >> 1, o_tb = (wave - 4) & 1;  // O^T tile (i-tile, t-tile)
-        const int y_tb = o_tb, y_ib = o_ib;  // (K S^T) tile (t-tile, i-tile): shares the S operand
-        if (wave < 2) {
-            const int R = 16 * (2 * wave + 1), Cc = 16 * (2 * wave);
-            float la[4], xa[4], ta[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                la[kk] = Lf[(R + m16) * LP + Cc + 4 * kk + g16];
-                xa[kk] = Xs[(Cc + 4 * kk + g16) * LP + Cc + m16];
-                ta[kk] = Xs[(R + m16) * LP + R + 4 * g16 + kk];
-            }
-            issue_fence();
-            f32x4 y = {};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) y = mfma16f(la[kk], xa[kk], y);
-            // y (row 4*g16 + r, column m16) feeds the next product directly as its B
-            // operand: step r uses reduction index 4*g16 + r, matched on the A side
-            f32x4 z = {};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) z = mfma16f(ta[r], y[r], z);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
-        } else if (wave >= 4) {
-            // two batches of four reduction steps bound the operand registers
+        if (wave < 4) {
+            const int y_tb = wave >> 1, y_ib = wave & 1;
+            f32x16 accY = {};
 #pragma unroll
             for (int half = 0; half < DK / 64; ++half) {
-                bf16x8 fs[4], fq[4], fk[4];
+                bf16x8 fk[4], fs[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const int k0 = 64 * half + 16 * kk;
-                    fs[kk] = frag(Sb, KP, 32 * o_ib, k0, ln);
-                    fq[kk] = frag(Qc, KP, 32 * o_tb, k0, ln);
-                    fk[kk] = frag(Kc, KP, 32 * y_tb, k0, ln);
+                    fk[kk] = frag(Kc, KP, 32 * y_tb, 64 * half + 16 * kk, ln);
+                    fs[kk] = frag(Sb, KP, 32 * y_ib, 64 * half + 16 * kk, ln);
                 }
                 issue_fence();
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    accO = mfma(fs[kk], fq[kk], accO);
-                    accY = mfma(fk[kk], fs[kk], accY);
-                }
+                for (int kk = 0; kk < 4; ++kk) accY = mfma(fk[kk], fs[kk], accY);
             }
-        }
-        block_sync();
-
-        // ======== solve level 3a (waves 0-3): Y2 = L[32:64, 0:32] X[0:32, 0:32], one
-        // 16x16 quadrant (qr, qc) per wave, into Rtmp [32][RP]; waves 4-7:
-        // Y = V e^{-G} - K S^T -> Y^T hi/lo [i][t]
-        const int qr = wave >> 1, qc = wave & 1;
-        if (wave < 4) {
-            float la[8], xa[8];
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                la[kk] = Lf[(32 + 16 * qr + m16) * LP + 4 * kk + g16];
-                xa[kk] = Xs[(4 * kk + g16) * LP + 16 * qc + m16];
-            }
-            issue_fence();
-            f32x4 y = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                if (kk >= 4 * qc)  // X[0:32, 0:32] is lower triangular by 16x16 blocks
-                    y = mfma16f(la[kk], xa[kk], y);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * RP + 16 * qc + m16] = y[r];
-        } else {
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 // registers 4rb..4rb+3: 4 consecutive t of one i
@@ -560,100 +655,101 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                 float xv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __expf(-Gs[(t + e) * GP + i]);
+                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __expf(-Gs[(t + e) * GP + i]) -
+                            accY[4 * rb + e];
                 uint2 wh, wl;
-                split_bf16x2(xv[0] - accY[4 * rb], xv[1] - accY[4 * rb + 1], wh.x, wl.x);
-                split_bf16x2(xv[2] - accY[4 * rb + 2], xv[3] - accY[4 * rb + 3], wh.y, wl.y);
+                split_bf16x2(xv[0], xv[1], wh.x, wl.x);
+                split_bf16x2(xv[2], xv[3], wh.y, wl.y);
                 *reinterpret_cast<uint2*>(Yt_hi + i * CP + t) = wh;
                 *reinterpret_cast<uint2*>(Yt_lo + i * CP + t) = wl;
             }
+        } else {
+#pragma unroll
+            for (int half = 0; half < DK / 64; ++half) {
+                bf16x8 fs[4], fq[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    fs[kk] = frag(Sb, KP, 32 * o_ib, 64 * half + 16 * kk, ln);
+                    fq[kk] = frag(Qc, KP, 32 * o_tb, 64 * half + 16 * kk, ln);
+                }
+                issue_fence();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) accO = mfma(fs[kk], fq[kk], accO);
+            }
+            if (wave < 7) {
+                // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1); (1,0) is all zero
+                const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
+                f32x16 acc = {};
+#pragma unroll
+                for (int half = 0; half < DK / 64; ++half) {
+                    bf16x8 fa[4], fb[4];
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        fa[kk] = frag(Kc, KP, 32 * sb, 64 * half + 16 * kk, ln);
+                        fb[kk] = frag(Qc, KP, 32 * tb, 64 * half + 16 * kk, ln);
+                    }
+                    issue_fence();
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) acc = mfma(fa[kk], fb[kk], acc);
+                }
+                const int t = 32 * tb + (ln & 31);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int s0 = 32 * sb + 8 * rb + 4 * (ln >> 5);
+                    float pv4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv4[e] = s0 + e <= t ? acc[4 * rb + e] : 0.f;
+                    uint2 wh, wl;
+                    split_bf16x2(pv4[0], pv4[1], wh.x, wl.x);
+                    split_bf16x2(pv4[2], pv4[3], wh.y, wl.y);
+                    *reinterpret_cast<uint2*>(P_hi + t * CP + s0) = wh;
+                    *reinterpret_cast<uint2*>(P_lo + t * CP + s0) = wl;
+                }
+            }
         }
         block_sync();
 
-        // ======== solve level 3b (waves 0-3): X[32:64, 0:32] = -X[32:64, 32:64] Y2
-        if (wave < 4) {
-            float xa[8], ra[8];
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                xa[kk] = Xs[(32 + 16 * qr + m16) * LP + 32 + 4 * kk + g16];
-                ra[kk] = Rtmp[(4 * kk + g16) * RP + 16 * qc + m16];
-            }
-            issue_fence();
-            f32x4 z = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                if (kk < 4 * (qr + 1))  // X[32:64, 32:64] is lower triangular by blocks
-                    z = mfma16f(xa[kk], ra[kk], z);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Xs[(32 + 16 * qr + 4 * g16 + r) * LP + 16 * qc + m16] = -z[r];
-        }
-        block_sync();
-
-        // ======== A = (I + L)^{-1} diag(beta) as hi/lo bf16, zero above the diagonal;
-        // each thread converts 8 consecutive entries of one row
+        // ======== U = A Y on 16x16 tiles (t-block tr; i-blocks ic, ic + 1), all
+        // waves -> U^T hi/lo [i][t]
         {
-            const int t = td >> 3, s0 = 8 * (td & 7);
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + s0);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + s0 + 4);
-            float av[8];
+            const int tr = wave >> 1, ic = 2 * (wave & 1);
+            f32x4 acc0 = {}, acc1 = {};
+            const int nks = tr < 2 ? 1 : 2;  // A is lower triangular: s < 16 (tr + 1)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = e < 4 ? x0[e] * b0[e] : x1[e - 4] * b1[e - 4];
-                av[e] = s0 + e <= t ? xv : 0.f;
-            }
-            u32x4 wh, wl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t a, b;
-                split_bf16x2(av[2 * e], av[2 * e + 1], a, b);
-                wh[e] = a;
-                wl[e] = b;
-            }
-            *reinterpret_cast<u32x4*>(A_hi + t * CP + s0) = wh;
-            *reinterpret_cast<u32x4*>(A_lo + t * CP + s0) = wl;
-        }
-        block_sync();
-
-        // ======== U = A Y (waves 0-3) -> U^T hi/lo [i][t]
-        if (wave < 4) {
-            const int u_tb = wave >> 1, u_ib = wave & 1;
-            f32x16 accU = {};
-            bf16x8 ah[4], al[4], yh[4], yl[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (u_tb + 1)) {  // A is lower triangular
-                    ah[kk] = frag(A_hi, CP, 32 * u_tb, 16 * kk, ln);
-                    al[kk] = frag(A_lo, CP, 32 * u_tb, 16 * kk, ln);
-                    yh[kk] = frag(Yt_hi, CP, 32 * u_ib, 16 * kk, ln);
-                    yl[kk] = frag(Yt_lo, CP, 32 * u_ib, 16 * kk, ln);
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks < nks) {
+                    const bf16x8 ah = frag16(A_hi, CP, 16 * tr, 32 * ks, ln);
+                    const bf16x8 al = frag16(A_lo, CP, 16 * tr, 32 * ks, ln);
+                    const bf16x8 y0h = frag16(Yt_hi, CP, 16 * ic, 32 * ks, ln);
+                    const bf16x8 y0l = frag16(Yt_lo, CP, 16 * ic, 32 * ks, ln);
+                    const bf16x8 y1h = frag16(Yt_hi, CP, 16 * ic + 16, 32 * ks, ln);
+                    const bf16x8 y1l = frag16(Yt_lo, CP, 16 * ic + 16, 32 * ks, ln);
+                    issue_fence();
+                    acc0 = mfma16(ah, y0h, acc0);
+                    acc1 = mfma16(ah, y1h, acc1);
+                    acc0 = mfma16(al, y0h, acc0);
+                    acc1 = mfma16(al, y1h, acc1);
+                    acc0 = mfma16(ah, y0l, acc0);
+                    acc1 = mfma16(ah, y1l, acc1);
                 }
             }
-            issue_fence();
+            // lane (column i, group g) holds rows t = 16 tr + 4 g + r
+            const int t = 16 * tr + 4 * (ln >> 4);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (u_tb + 1)) {
-                    accU = mfma(ah[kk], yh[kk], accU);
-                    accU = mfma(al[kk], yh[kk], accU);
-                    accU = mfma(ah[kk], yl[kk], accU);
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int t = 32 * u_tb + 8 * rb + 4 * (ln >> 5), i = 32 * u_ib + (ln & 31);
+            for (int half = 0; half < 2; ++half) {
+                const f32x4& a = half ? acc1 : acc0;
+                const int i = 16 * (ic + half) + (ln & 15);
                 uint2 wh, wl;
-                split_bf16x2(accU[4 * rb], accU[4 * rb + 1], wh.x, wl.x);
-                split_bf16x2(accU[4 * rb + 2], accU[4 * rb + 3], wh.y, wl.y);
+                split_bf16x2(a[0], a[1], wh.x, wl.x);
+                split_bf16x2(a[2], a[3], wh.y, wl.y);
                 *reinterpret_cast<uint2*>(Ut_hi + i * CP + t) = wh;
                 *reinterpret_cast<uint2*>(Ut_lo + i * CP + t) = wl;
             }
         }
         block_sync();
 
-        // ======== O^T = e^G (S Q^T + U^T P^T) staged as bf16 O [t][i] (waves 4-7);
-        // S^T = diag(gamma)(S^T + K^T U) (all waves)
+        // ======== waves 4-7: O^T = e^G (S Q^T + U^T P^T), staged as bf16 O [t][i];
+        // S^T = diag(gamma) (S^T + K^T U) on the state-owning waves
         if (wave >= 4) {
             bf16x8 uh[4], ul[4], ph[4], pl[4];
 #pragma unroll
@@ -665,11 +761,11 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                     pl[kk] = frag(P_lo, CP, 32 * o_tb, 16 * kk, ln);
                 }
             }
-            const int tq = 32 * o_tb + (ln & 31);
+            const int t = 32 * o_tb + (ln & 31);
             f32x4 g4[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
-                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + tq * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
+                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + t * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
             issue_fence();
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -679,7 +775,6 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
                     accO = mfma(uh[kk], pl[kk], accO);
                 }
             }
-            const int t = tq;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 const int i = 32 * o_ib + 8 * rb + 4 * (ln >> 5);
@@ -707,7 +802,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) accS[r] *= gm;
         }
-        write_state_copy(ln);  // the last readers of the old copy were S Q^T and K S^T
+        write_state_copy(ln);  // the old copy's last readers (K S^T, S Q^T) are two barriers back
         prev_tc = tc;
         prev_n = n;
     }
@@ -725,29 +820,58 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------- launchers
+// Workspace of the bf16 path, each part 256-byte aligned:
+//   order      n_seq int32 (longest-first schedule; varlen only)
+//   chunk_off  n_seq + 1 int32
+//   A records  (n_tok / C + n_seq) x n_heads x A_RECORD_BYTES (an upper bound
+//              on the number of chunks times heads)
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static int64_t chunk_bound(int32_t n_seq, int32_t n_tok) { return static_cast<int64_t>(n_tok) / C + n_seq; }
+
+size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads) {
+    return align256(static_cast<size_t>(n_seq) * 4) + align256((static_cast<size_t>(n_seq) + 1) * 4) +
+           static_cast<size_t>(chunk_bound(n_seq, n_tok)) * static_cast<size_t>(n_heads) * A_RECORD_BYTES;
+}
+
 template <int DK, int DV>
-static hipError_t launch_mfma_t(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int NVB = DV / BV;
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    const size_t off_chunk = align256(static_cast<size_t>(a.n_seq) * 4);
+    const size_t off_rec = off_chunk + align256((static_cast<size_t>(a.n_seq) + 1) * 4);
+    int32_t* order = reinterpret_cast<int32_t*>(ws);
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + off_chunk);
+    uint16_t* arec = reinterpret_cast<uint16_t*>(ws + off_rec);
+    hipError_t e;
+    if (a.cu_seqlens) {
+        if ((e = launch_schedule(a.cu_seqlens, a.n_seq, order, stream)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.n_seq, a.n_tok,
+                       chunk_off);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
+    if (a.n_tok > 0) {
+        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(mc * a.n_heads)), dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(a.k), a.beta, a.cu_seqlens, chunk_off, a.n_seq,
+                           a.n_tok, a.n_heads, static_cast<int>(mc), arec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((prefill_mfma_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
-                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.alpha, a.beta, a.S0, a.cu_seqlens, order,
-                       a.n_seq, a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), a.S_T);
+    hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.alpha, a.S0, a.cu_seqlens,
+                       a.cu_seqlens ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads,
+                       static_cast<uint16_t*>(a.o), a.S_T);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    const int32_t* order = nullptr;
-    if (a.cu_seqlens) {
-        int32_t* ord = static_cast<int32_t*>(a.workspace);
-        const hipError_t e = launch_schedule(a.cu_seqlens, a.n_seq, ord, stream);
-        if (e != hipSuccess) return e;
-        order = ord;
-    }
-    if (a.d_k == 128 && a.d_v == 128) return launch_mfma_t<128, 128>(a, order, stream);
-    if (a.d_k == 64 && a.d_v == 64) return launch_mfma_t<64, 64>(a, order, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_mfma_t<128, 64>(a, order, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_mfma_t<64, 128>(a, order, stream);
+    if (a.d_k == 128 && a.d_v == 128) return launch_bf16_t<128, 128>(a, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bf16_t<64, 64>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bf16_t<128, 64>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bf16_t<64, 128>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -205,8 +205,4 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
     return launch_valu_dt<float>(a, stream);
 }
 
-hipError_t launch_prefill_valu_bf16(const PrefillArgs& a, hipStream_t stream) {
-    return launch_valu_dt<uint16_t>(a, stream);
-}
-
 }  // namespace kda

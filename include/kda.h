@@ -67,6 +67,13 @@ const char* kda_status_string(kda_status s);
 /*
  * Bytes of device workspace kda_prefill needs for these sizes (0 is possible).
  * Returns 0 as well for sizes that kda_prefill would reject.
+ *   KDA_DTYPE_F32:  the longest-first schedule of the packed sequences
+ *                   (n_seq int32, rounded up to 256 bytes).
+ *   KDA_DTYPE_BF16: the schedule, the first chunk of every sequence
+ *                   ((n_seq + 1) int32, rounded up to 256 bytes), and the
+ *                   solved within-chunk system A = (I + L)^{-1} diag(beta) of
+ *                   every (chunk, head) -- 12 KiB each, for at most
+ *                   n_tok / 64 + n_seq chunks of 64 tokens.
  */
 size_t kda_prefill_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
                                   int32_t d_k, int32_t d_v, kda_dtype dt);
@@ -95,7 +102,9 @@ size_t kda_prefill_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
  *               overlap between inputs and outputs is not allowed.
  *   workspace   device scratch of at least kda_prefill_workspace_size(...)
  *               bytes (may be NULL when that size is 0); its contents need no
- *               initialisation and are clobbered.
+ *               initialisation and are clobbered.  It may not overlap any other
+ *               argument.  Calls that share one workspace must be ordered
+ *               (the same stream, or events between them).
  * n_seq >= 1, n_tok >= 0, n_heads >= 1.
  */
 kda_status kda_prefill(const void* q, const void* k, const void* v,

@@ -43,8 +43,14 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_size(L):
-    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 1) == 256
-    assert L.kda_prefill_workspace_size(65, 1000, 16, 128, 128, 1) == 512
+    # fp32: the longest-first schedule (n_seq int32, 256-byte aligned)
+    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 0) == 256
+    assert L.kda_prefill_workspace_size(65, 1000, 16, 128, 128, 0) == 512
+    # bf16: schedule + chunk offsets (n_seq + 1 int32) + one 12 KiB block of the solved
+    # A = (I + L)^{-1} diag(beta) per (chunk, head), for at most n_tok // 64 + n_seq chunks
+    rec = 3 * 2 * 32 * 32 * 2
+    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 1) == 256 + 512 + (15 + 64) * 16 * rec
+    assert L.kda_prefill_workspace_size(1, 0, 4, 64, 64, 1) == 256 + 256 + 1 * 4 * rec
     assert L.kda_prefill_workspace_size(0, 1000, 16, 128, 128, 1) == 0
     assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
 
@@ -77,6 +83,7 @@ def prefill(L, **kw):
     (dict(S0=A + 0x600000 + 16, S_T=A + 0x600000), kda.KDA_ERR_INVALID_ARGUMENT),  # partial overlap
     (dict(ws=None), kda.KDA_ERR_WORKSPACE),
     (dict(ws_bytes=128), kda.KDA_ERR_WORKSPACE),
+    (dict(ws=A + 0x500000, ws_bytes=1 << 20), kda.KDA_ERR_INVALID_ARGUMENT),  # workspace overlaps o
 ])
 def test_prefill_rejects_on_host(L, kw, status):
     assert prefill(L, **kw) == status
