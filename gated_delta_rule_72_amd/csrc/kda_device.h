@@ -75,26 +75,6 @@ __device__ __forceinline__ float dpp_mov(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_mov_rows(float x) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave, in lane order.  Within each
-// 16-lane row: row_shr by 1, 2, 4, 8 (lanes shifted in from outside the row read
-// 0).  Across rows: row_bcast:15 adds lane 15 of a row to the next row (rows 1
-// and 3), then row_bcast:31 adds lane 31 to rows 2 and 3.
-__device__ __forceinline__ float wave_inclusive_scan(float x) {
-    x += dpp_mov<0x111>(x);
-    x += dpp_mov<0x112>(x);
-    x += dpp_mov<0x114>(x);
-    x += dpp_mov<0x118>(x);
-    x += dpp_mov_rows<0x142, 0xA>(x);
-    x += dpp_mov_rows<0x143, 0xC>(x);
-    return x;
-}
-
 // Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
 __device__ __forceinline__ float sum8(float x) {
     x += dpp_mov<DPP_QUAD_XOR1>(x);

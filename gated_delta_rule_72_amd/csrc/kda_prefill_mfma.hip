@@ -101,6 +101,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
 }
 
+// Inclusive prefix over the four 16-lane rows of a wave: lane-row r (= lane >> 4)
+// returns x_0 + ... + x_r of the values at its position in rows 0..r.  Built on the
+// gfx950 row swaps: permlane16_swap exchanges the odd rows of its first operand
+// with the even rows of its second, permlane32_swap the upper half of the first
+// with the lower half of the second.
+__device__ __forceinline__ float lane_row_scan4(float x, int lrow) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float a = __uint_as_float(s16[0]);  // rows (x0, x0, x2, x2)
+    const float b = __uint_as_float(s16[1]);  // rows (x1, x1, x3, x3)
+    const float y = x + ((lrow & 1) ? a : 0.f);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(0u, __float_as_uint(a + b), false, false);
+    return y + __uint_as_float(s32[0]);  // rows 2, 3 add x0 + x1
+}
+
+// The value of lane-row 3 at this lane's position, in every lane-row.
+__device__ __forceinline__ float lane_row_last(float x) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const unsigned b = s16[1];  // rows (x1, x1, x3, x3)
+    const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __uint_as_float(s32[1]);  // (x3, x3, x3, x3)
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
+// receives element (i % 4) of the 8 bytes addressed by lane 4e + i / 4, as its
+// element e.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 __device__ inline int64_t seq_start(int seq, int n_seq, int n_tok, const int32_t* cu) {
     return cu ? static_cast<int64_t>(cu[seq]) : static_cast<int64_t>(seq) * (n_tok / n_seq);
 }
@@ -414,9 +446,8 @@ struct ScanSmem {
     static constexpr int HILO = 2 * C * CP * 2;
     // each region is its own __shared__ array, so the compiler knows accesses to
     // different regions never alias and can move loads ahead of unrelated stores
-    static constexpr int RK = mx(C * KP * 2, HILO);   // K [t][j], then U^T hi/lo [i][t]
-    static constexpr int RQ = C * KP * 2;             // Q [t][j]
-    static constexpr int RKT = DK * CP * 2;           // K^T [j][t]
+    static constexpr int RK = C * KP * 2;             // K [t][j]
+    static constexpr int RQ = mx(C * KP * 2, HILO);   // Q [t][j], then U^T hi/lo [i][t]
     static constexpr int RV = C * OP * 2;             // V [t][i]
     static constexpr int RG = C * GP * 4;             // G [t][i]
     static constexpr int RA = HILO;                   // A hi/lo [t][s]
@@ -424,7 +455,8 @@ struct ScanSmem {
     static constexpr int RY = mx(HILO, C * OP * 2);   // Y^T hi/lo [i][t], then O [t][i]
     static constexpr int RS = BV * KP * 2;            // S bf16 [i][j]
     static constexpr int RB = BV * 4;                 // gamma = e^{G[C-1, :]}
-    static constexpr int TOTAL = RK + RQ + RKT + RV + RG + RA + RP + RY + RS + RB;
+    static constexpr int RT = 2 * 8 * BV * 4;         // per-wave totals of log alpha, two chunks
+    static constexpr int TOTAL = RK + RQ + RV + RG + RA + RP + RY + RS + RB + RT;
 };
 
 template <int DK, int DV>
@@ -443,7 +475,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     __shared__ __align__(16) unsigned char rk_[SM::RK];
     __shared__ __align__(16) unsigned char rq_[SM::RQ];
-    __shared__ __align__(16) unsigned char rkt_[SM::RKT];
     __shared__ __align__(16) unsigned char rv_[SM::RV];
     __shared__ __align__(16) unsigned char rg_[SM::RG];
     __shared__ __align__(16) unsigned char ra_[SM::RA];
@@ -451,11 +482,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __align__(16) unsigned char ry_[SM::RY];
     __shared__ __align__(16) unsigned char rs_[SM::RS];
     __shared__ __align__(16) unsigned char rb_[SM::RB];
+    __shared__ __align__(16) unsigned char rt_[SM::RT];
     uint16_t* Kc = reinterpret_cast<uint16_t*>(rk_);
-    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(rk_);
-    uint16_t* Ut_lo = Ut_hi + BV * CP;
     uint16_t* Qc = reinterpret_cast<uint16_t*>(rq_);
-    uint16_t* Kt = reinterpret_cast<uint16_t*>(rkt_);
+    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(rq_);
+    uint16_t* Ut_lo = Ut_hi + BV * CP;
     uint16_t* Vr = reinterpret_cast<uint16_t*>(rv_);
     float* Gs = reinterpret_cast<float*>(rg_);
     uint16_t* A_hi = reinterpret_cast<uint16_t*>(ra_);
@@ -467,6 +498,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     uint16_t* Os = reinterpret_cast<uint16_t*>(ry_);
     uint16_t* Sb = reinterpret_cast<uint16_t*>(rs_);
     float* gam = reinterpret_cast<float*>(rb_);
+    float* Tot = reinterpret_cast<float*>(rt_);  // [2][8][BV]
 
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
@@ -494,53 +526,64 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
     }
 
-    // ---- register prefetch of one chunk's inputs; every load moves 16 bytes per lane.
-    // K, Q: thread (row pair tp, 16-byte piece c) holds rows 2tp, 2tp+1 (with
-    //   d_k = 64 the upper four waves repeat the lower four).
+    // ---- register prefetch of a chunk's inputs, two chunks ahead (two register
+    // sets in turn); every load moves 16 bytes per lane.
+    // K, Q: piece tid (and tid + 512) of the row-major chunk, whole rows per load.
     // V: row tid/8, 8 values at 8*(tid%8).
-    // alpha: lane = token, wave w = the 8 value rows 8w..8w+7 (the decay scan runs
-    //   across lanes).
+    // alpha: wave w holds token rows 8w..8w+7, lane-row r = lane/16 the rows
+    //   8w + r (a0) and 8w + 4 + r (a1), values 4*(lane%16)..+3.
     // A record: pieces tid and tid + 512.
-    const int kq_tp = lane & 31, kq_c = (2 * wave + (lane >> 5)) % (DK / 8);
-    u32x4 pk0 = {}, pk1 = {}, pq0 = {}, pq1 = {}, pv = {}, pA0 = {}, pA1 = {};
-    f32x4 pa0 = {}, pa1 = {};
-    auto prefetch = [&](int64_t tc, int n, int gc) {
+    // The loads (and the O store below) are issued unconditionally: a chunk past
+    // the end gets an empty buffer range, so nothing is accessed.  Uniform control
+    // flow lets the compiler count outstanding memory operations exactly, instead
+    // of waiting for all of them where a conditional path merges.
+    constexpr int PPR = DK / 8;  // 16-byte pieces per row of q or k
+    struct Pf {
+        u32x4 k0, k1, q0, q1, v, A0, A1;
+        f32x4 a0, a1;
+    };
+    auto prefetch = [&](Pf& pf, int64_t tc, int n, int gc) {
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
+        const bool any = n > 0;
         {
-            const int64_t bytes = ((n - 1) * row_qk + DK) * 2;
+            const int64_t bytes = any ? ((n - 1) * row_qk + DK) * 2 : 0;
             const auto rk = make_rsrc(k + tok0 * DK, bytes);
             const auto rq = make_rsrc(q + tok0 * DK, bytes);
-            const int off0 = static_cast<int>((2 * kq_tp) * row_qk + 8 * kq_c) * 2;
-            const int off1 = off0 + static_cast<int>(row_qk) * 2;
-            pk0 = __builtin_amdgcn_raw_buffer_load_b128(rk, off0, 0, 0);
-            pk1 = __builtin_amdgcn_raw_buffer_load_b128(rk, off1, 0, 0);
-            pq0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
-            pq1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off1, 0, 0);
+            const int off0 = static_cast<int>((tid / PPR) * row_qk + 8 * (tid % PPR)) * 2;
+            const int off1 = off0 + static_cast<int>(32 * row_qk) * 2;
+            pf.k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, off0, 0, 0);
+            pf.q0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
+            if constexpr (DK == 128) {
+                pf.k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, off1, 0, 0);
+                pf.q1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off1, 0, 0);
+            }
         }
         {
-            const auto rv = make_rsrc(v + tok0 * DV + i0, ((n - 1) * row_v + BV) * 2);
-            pv = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2,
-                                                       0, 0);
-            const auto ra = make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4);
-            const int offa = static_cast<int>(lane * row_v + 8 * wave) * 4;
-            pa0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, 0));
-            pa1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + 16, 0, 0));
+            const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
+            pf.v = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2,
+                                                         0, 0);
+            const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
+            const int offa = static_cast<int>((8 * wave + (lane >> 4)) * row_v + 4 * (lane & 15)) * 4;
+            pf.a0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, 0));
+            pf.a1 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + static_cast<int>(4 * row_v) * 4, 0, 0));
         }
         {
             const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
-            const auto rr = make_rsrc(recp, A_RECORD_BYTES);
-            pA0 = __builtin_amdgcn_raw_buffer_load_b128(rr, tid * 16, 0, 0);
-            pA1 = __builtin_amdgcn_raw_buffer_load_b128(rr, (tid + 512) * 16, 0, 0);  // past the end for tid >= 256
+            const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
+            pf.A0 = __builtin_amdgcn_raw_buffer_load_b128(rr, tid * 16, 0, 0);
+            pf.A1 = __builtin_amdgcn_raw_buffer_load_b128(rr, (tid + 512) * 16, 0, 0);  // past the end for tid >= 256
         }
     };
 
-    auto chunk_len = [&](int64_t tc) { return static_cast<int>(min<int64_t>(C, u.t1 - tc)); };
+    auto chunk_len = [&](int64_t tc) { return static_cast<int>(max<int64_t>(0, min<int64_t>(C, u.t1 - tc))); };
 
     // staged O rows of a finished chunk -> global, one 16-byte store per thread
+    // (n = 0: nothing is stored)
     auto store_o = [&](int64_t tc, int n, int td) {
         const int t = td >> 3, c = td & 7;
         const u32x4 val = *reinterpret_cast<const u32x4*>(Os + t * OP + 8 * c);
-        const auto ro = make_rsrc(o + (tc * H + h) * DV + i0, ((n - 1) * row_v + BV) * 2);
+        const auto ro = make_rsrc(o + (tc * H + h) * DV + i0, n > 0 ? ((n - 1) * row_v + BV) * 2 : 0);
         __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
     };
 
@@ -566,13 +609,53 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
     };
 
-    if (u.t0 < u.t1) prefetch(u.t0, chunk_len(u.t0), chunk0);
+    // The log-decay cumsum G of a chunk is formed in two steps one chunk apart,
+    // so the prefix across waves never needs a barrier of its own:
+    // local_scan -- each wave's inclusive prefix over its 8 token rows, kept in
+    //   the alpha registers; the wave's totals go to Tot[parity][wave];
+    // finalize   -- after a barrier, add the totals of the waves before (the
+    //   rows before this wave's) and write G [t][i] and gamma.
+    // Rows past the sequence end contribute log alpha = 0.
+    auto local_scan = [&](Pf& pf, int n, int par, int ln) {
+        const int lr = ln >> 4, t = 8 * wave + lr;
+        f32x4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x0[e] = lane_row_scan4(t < n ? __logf(pf.a0[e]) : 0.f, lr);
+            x1[e] = lane_row_scan4(t + 4 < n ? __logf(pf.a1[e]) : 0.f, lr) + lane_row_last(x0[e]);
+        }
+        pf.a0 = x0;
+        pf.a1 = x1;
+        if (lr == 3) *reinterpret_cast<f32x4*>(Tot + (par * 8 + wave) * BV + 4 * (ln & 15)) = x1;
+    };
+    auto finalize = [&](const Pf& pf, int par, int ln) {
+        const int lr = ln >> 4, i = 4 * (ln & 15);
+        f32x4 carry = {};
+        for (int b = 0; b < wave; ++b) carry += *reinterpret_cast<const f32x4*>(Tot + (par * 8 + b) * BV + i);
+        const f32x4 g0 = pf.a0 + carry, g1 = pf.a1 + carry;
+        *reinterpret_cast<f32x4*>(Gs + (8 * wave + lr) * GP + i) = g0;
+        *reinterpret_cast<f32x4*>(Gs + (8 * wave + 4 + lr) * GP + i) = g1;
+        if (wave == 7 && lr == 3) {
+            f32x4 e1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) e1[e] = __expf(g1[e]);
+            *reinterpret_cast<f32x4*>(gam + i) = e1;
+        }
+    };
+
+    Pf pf0 = {}, pf1 = {};
+    prefetch(pf0, u.t0, chunk_len(u.t0), chunk0);
+    prefetch(pf1, u.t0 + C, chunk_len(u.t0 + C), chunk0 + 1);
+    local_scan(pf0, chunk_len(u.t0), 0, lane);
     write_state_copy(lane);
 
-    int64_t prev_tc = -1;
+    int64_t prev_tc = u.t0;
     int prev_n = 0;
-    int gc = chunk0;
-    for (int64_t tc = u.t0; tc < u.t1; tc += C, ++gc) {
+    // chunk c: stage it from pf (whose alpha registers hold its local prefix),
+    // pre-scan the next chunk's alpha in nx, then reuse pf for chunk c + 2
+    auto chunk_step = [&](Pf& pf, Pf& nx, int c) {
+        const int64_t tc = u.t0 + static_cast<int64_t>(c) * C;
+        const int gc = chunk0 + c;
         const int n = chunk_len(tc);
         // Lane-derived values are recomputed every chunk from an opaque copy of
         // the lane id, so the compiler does not hoist dozens of loop-invariant
@@ -583,48 +666,21 @@ __global__ __launch_bounds__(512) void scan_kernel(
         const int td = ln + 64 * wave;
         block_sync();  // the previous chunk is done with every buffer
 
-        // ======== stage this chunk, run the decay scan in registers, store the
-        // previous chunk's O, issue the next chunk's loads
-        {
-            const int rr = 2 * (ln & 31), c = (2 * wave + (ln >> 5)) % (DK / 8);
-            *reinterpret_cast<u32x4*>(Kc + rr * KP + 8 * c) = pk0;
-            *reinterpret_cast<u32x4*>(Kc + (rr + 1) * KP + 8 * c) = pk1;
-            *reinterpret_cast<u32x4*>(Qc + rr * KP + 8 * c) = pq0;
-            *reinterpret_cast<u32x4*>(Qc + (rr + 1) * KP + 8 * c) = pq1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // bf16 e of row rr (low half) and of row rr + 1 (high half)
-                const uint32_t lo = pk0[e >> 1] >> (16 * (e & 1)), hi = pk1[e >> 1] >> (16 * (e & 1));
-                *reinterpret_cast<uint32_t*>(Kt + (8 * c + e) * CP + rr) = (lo & 0xffffu) | (hi << 16);
-            }
+        // ======== stage this chunk and finish its G, pre-scan the next chunk's
+        // alpha, store the previous chunk's O, issue the loads two chunks ahead
+        *reinterpret_cast<u32x4*>(Kc + (td / PPR) * KP + 8 * (td % PPR)) = pf.k0;
+        *reinterpret_cast<u32x4*>(Qc + (td / PPR) * KP + 8 * (td % PPR)) = pf.q0;
+        if constexpr (DK == 128) {
+            *reinterpret_cast<u32x4*>(Kc + (32 + td / PPR) * KP + 8 * (td % PPR)) = pf.k1;
+            *reinterpret_cast<u32x4*>(Qc + (32 + td / PPR) * KP + 8 * (td % PPR)) = pf.q1;
         }
-        *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pv;
-        stage_a(pA0, td);
-        if (td < A_RECORD_PIECES - 512) stage_a(pA1, td + 512);
-        {
-            // G[t, 8w+e] = inclusive scan over t (= lanes) of log alpha; rows past
-            // the sequence end (they read as alpha = 0) contribute 0
-            f32x4 g0, g1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                g0[e] = wave_inclusive_scan(ln < n ? __logf(pa0[e]) : 0.f);
-                g1[e] = wave_inclusive_scan(ln < n ? __logf(pa1[e]) : 0.f);
-            }
-            *reinterpret_cast<f32x4*>(Gs + ln * GP + 8 * wave) = g0;
-            *reinterpret_cast<f32x4*>(Gs + ln * GP + 8 * wave + 4) = g1;
-            if (ln == 63) {
-                f32x4 e0, e1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    e0[e] = __expf(g0[e]);
-                    e1[e] = __expf(g1[e]);
-                }
-                *reinterpret_cast<f32x4*>(gam + 8 * wave) = e0;
-                *reinterpret_cast<f32x4*>(gam + 8 * wave + 4) = e1;
-            }
-        }
-        if (prev_tc >= 0) store_o(prev_tc, prev_n, td);
-        if (tc + C < u.t1) prefetch(tc + C, chunk_len(tc + C), gc + 1);
+        *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pf.v;
+        stage_a(pf.A0, td);
+        if (td < A_RECORD_PIECES - 512) stage_a(pf.A1, td + 512);
+        finalize(pf, c & 1, ln);
+        local_scan(nx, chunk_len(tc + C), (c + 1) & 1, ln);
+        store_o(prev_tc, prev_n, td);
+        prefetch(pf, tc + 2 * C, chunk_len(tc + 2 * C), gc + 2);
         block_sync();
 
         // ======== waves 0-3: K S^T, then Y = V e^{-G} - K S^T -> Y^T hi/lo [i][t];
@@ -785,10 +841,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
             }
         }
         if (owns_s) {
+            // K^T operand (rows j, reduction over t) read from row-major K with the
+            // transposing load: in 16-lane group g, lane m addresses token row
+            // 16kk + 8(g>>1) + m/4 (+4 for the second half) at key channels
+            // 32 s_jt + 16(g&1) + 4(m%4) .. +3
+            const int g = ln >> 4, m = ln & 15;
+            const uint16_t* ktb = Kc + (8 * (g >> 1) + (m >> 2)) * KP + 32 * s_jt + 16 * (g & 1) + 4 * (m & 3);
             bf16x8 kt[4], uh[4], ul[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                kt[kk] = frag(Kt, CP, 32 * s_jt, 16 * kk, ln);
+                const s16x4 t0 = lds_read_tr16(ktb + 16 * kk * KP), t1 = lds_read_tr16(ktb + (16 * kk + 4) * KP);
+                kt[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
                 uh[kk] = frag(Ut_hi, CP, 32 * s_it, 16 * kk, ln);
                 ul[kk] = frag(Ut_lo, CP, 32 * s_it, 16 * kk, ln);
             }
@@ -805,8 +868,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
         write_state_copy(ln);  // the old copy's last readers (K S^T, S Q^T) are two barriers back
         prev_tc = tc;
         prev_n = n;
+    };
+    // Whole pairs of chunks, then an odd last one: every path into a step has
+    // issued the same memory operations, so the compiler's wait counts stay exact.
+    const int n_chunks = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
+    for (int c = 0; c + 1 < n_chunks; c += 2) {
+        chunk_step(pf0, pf1, c);
+        chunk_step(pf1, pf0, c + 1);
     }
-    if (prev_tc >= 0) {
+    if (n_chunks & 1) chunk_step(pf0, pf1, n_chunks - 1);
+    if (prev_n > 0) {
         block_sync();
         store_o(prev_tc, prev_n, tid);
     }
