@@ -5,7 +5,7 @@
 // is d_v x d_k (rows = value channels) and the forget gate diag(alpha_t) scales
 // its rows.  A per-row scalar decay commutes with everything on the key side,
 // so within a chunk of C tokens (S entering the chunk):
-//   G[t,i] = sum_{s<=t} log alpha[s,i]          (per-row cumulative log-decay)
+//   G[t,i] = sum_{s<=t} log alpha[s,i]          (per-row cumulative log-decay; kept in log2 units)
 //   L      = strictly_lower(diag(beta) K K^T)    (decay-free beta-weighted Gram)
 //   A      = (I + L)^{-1} diag(beta)             (unit-lower WY/UT solve)
 //   U      = A (V (.) e^{-G} - K S^T)            (decay-normalised errors)
@@ -99,28 +99,6 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // past the end are dropped, so a chunk's rows beyond its sequence need no branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
-}
-
-// Inclusive prefix over the four 16-lane rows of a wave: lane-row r (= lane >> 4)
-// returns x_0 + ... + x_r of the values at its position in rows 0..r.  Built on the
-// gfx950 row swaps: permlane16_swap exchanges the odd rows of its first operand
-// with the even rows of its second, permlane32_swap the upper half of the first
-// with the lower half of the second.
-__device__ __forceinline__ float lane_row_scan4(float x, int lrow) {
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float a = __uint_as_float(s16[0]);  // rows (x0, x0, x2, x2)
-    const float b = __uint_as_float(s16[1]);  // rows (x1, x1, x3, x3)
-    const float y = x + ((lrow & 1) ? a : 0.f);
-    const auto s32 = __builtin_amdgcn_permlane32_swap(0u, __float_as_uint(a + b), false, false);
-    return y + __uint_as_float(s32[0]);  // rows 2, 3 add x0 + x1
-}
-
-// The value of lane-row 3 at this lane's position, in every lane-row.
-__device__ __forceinline__ float lane_row_last(float x) {
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const unsigned b = s16[1];  // rows (x1, x1, x3, x3)
-    const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-    return __uint_as_float(s32[1]);  // (x3, x3, x3, x3)
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -527,11 +505,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
     }
 
     // ---- register prefetch of a chunk's inputs, two chunks ahead (two register
-    // sets in turn); every load moves 16 bytes per lane.
-    // K, Q: piece tid (and tid + 512) of the row-major chunk, whole rows per load.
+    // sets in turn); every load reads whole rows.
+    // K, Q: 16-byte piece tid (and tid + 512) of the row-major chunk.
     // V: row tid/8, 8 values at 8*(tid%8).
-    // alpha: wave w holds token rows 8w..8w+7, lane-row r = lane/16 the rows
-    //   8w + r (a0) and 8w + 4 + r (a1), values 4*(lane%16)..+3.
+    // alpha: wave w holds token rows 8w..8w+7, lane = value row (one 256-byte
+    //   token row per load).
     // A record: pieces tid and tid + 512.
     // The loads (and the O store below) are issued unconditionally: a chunk past
     // the end gets an empty buffer range, so nothing is accessed.  Uniform control
@@ -540,7 +518,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     constexpr int PPR = DK / 8;  // 16-byte pieces per row of q or k
     struct Pf {
         u32x4 k0, k1, q0, q1, v, A0, A1;
-        f32x4 a0, a1;
+        float a[8];
     };
     auto prefetch = [&](Pf& pf, int64_t tc, int n, int gc) {
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
@@ -563,10 +541,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
             pf.v = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2,
                                                          0, 0);
             const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
-            const int offa = static_cast<int>((8 * wave + (lane >> 4)) * row_v + 4 * (lane & 15)) * 4;
-            pf.a0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa, 0, 0));
-            pf.a1 = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, offa + static_cast<int>(4 * row_v) * 4, 0, 0));
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                pf.a[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                        ra, static_cast<int>((8 * wave + r) * row_v + lane) * 4, 0, 0));
         }
         {
             const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
@@ -609,38 +587,32 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
     };
 
+    // G is kept in base-2 units (log2 alpha summed; e^{G} = 2^{G}), so every log
+    // and exp below is one hardware instruction (v_log_f32 / v_exp_f32).  alpha
+    // is taken to be a normal fp32 number in (0, 1].
     // The log-decay cumsum G of a chunk is formed in two steps one chunk apart,
     // so the prefix across waves never needs a barrier of its own:
-    // local_scan -- each wave's inclusive prefix over its 8 token rows, kept in
-    //   the alpha registers; the wave's totals go to Tot[parity][wave];
+    // local_scan -- each wave's inclusive prefix over its 8 token rows (in
+    //   registers: a lane holds one value row), kept in the alpha registers; the
+    //   wave's totals go to Tot[parity][wave];
     // finalize   -- after a barrier, add the totals of the waves before (the
     //   rows before this wave's) and write G [t][i] and gamma.
     // Rows past the sequence end contribute log alpha = 0.
     auto local_scan = [&](Pf& pf, int n, int par, int ln) {
-        const int lr = ln >> 4, t = 8 * wave + lr;
-        f32x4 x0, x1;
+        float run = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x0[e] = lane_row_scan4(t < n ? __logf(pf.a0[e]) : 0.f, lr);
-            x1[e] = lane_row_scan4(t + 4 < n ? __logf(pf.a1[e]) : 0.f, lr) + lane_row_last(x0[e]);
+        for (int r = 0; r < 8; ++r) {
+            run += 8 * wave + r < n ? __builtin_amdgcn_logf(pf.a[r]) : 0.f;
+            pf.a[r] = run;
         }
-        pf.a0 = x0;
-        pf.a1 = x1;
-        if (lr == 3) *reinterpret_cast<f32x4*>(Tot + (par * 8 + wave) * BV + 4 * (ln & 15)) = x1;
+        Tot[(par * 8 + wave) * BV + ln] = run;
     };
     auto finalize = [&](const Pf& pf, int par, int ln) {
-        const int lr = ln >> 4, i = 4 * (ln & 15);
-        f32x4 carry = {};
-        for (int b = 0; b < wave; ++b) carry += *reinterpret_cast<const f32x4*>(Tot + (par * 8 + b) * BV + i);
-        const f32x4 g0 = pf.a0 + carry, g1 = pf.a1 + carry;
-        *reinterpret_cast<f32x4*>(Gs + (8 * wave + lr) * GP + i) = g0;
-        *reinterpret_cast<f32x4*>(Gs + (8 * wave + 4 + lr) * GP + i) = g1;
-        if (wave == 7 && lr == 3) {
-            f32x4 e1;
+        float carry = 0.f;
+        for (int b = 0; b < wave; ++b) carry += Tot[(par * 8 + b) * BV + ln];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) e1[e] = __expf(g1[e]);
-            *reinterpret_cast<f32x4*>(gam + i) = e1;
-        }
+        for (int r = 0; r < 8; ++r) Gs[(8 * wave + r) * GP + ln] = pf.a[r] + carry;
+        if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(pf.a[7] + carry);
     };
 
     Pf pf0 = {}, pf1 = {};
@@ -711,7 +683,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 float xv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __expf(-Gs[(t + e) * GP + i]) -
+                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __builtin_amdgcn_exp2f(-Gs[(t + e) * GP + i]) -
                             accY[4 * rb + e];
                 uint2 wh, wl;
                 split_bf16x2(xv[0], xv[1], wh.x, wl.x);
@@ -835,8 +807,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int rb = 0; rb < 4; ++rb) {
                 const int i = 32 * o_ib + 8 * rb + 4 * (ln >> 5);
                 uint2 w;
-                w.x = pack_bf16(__expf(g4[rb][0]) * accO[4 * rb], __expf(g4[rb][1]) * accO[4 * rb + 1]);
-                w.y = pack_bf16(__expf(g4[rb][2]) * accO[4 * rb + 2], __expf(g4[rb][3]) * accO[4 * rb + 3]);
+                w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[rb][0]) * accO[4 * rb],
+                                __builtin_amdgcn_exp2f(g4[rb][1]) * accO[4 * rb + 1]);
+                w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[rb][2]) * accO[4 * rb + 2],
+                                __builtin_amdgcn_exp2f(g4[rb][3]) * accO[4 * rb + 3]);
                 *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
             }
         }
