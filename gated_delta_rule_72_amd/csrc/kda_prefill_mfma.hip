@@ -89,8 +89,13 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 
 // Compiler-only fence: the LDS operand loads above it are issued before the
 // matrix instructions below it, so their latencies overlap instead of each
-// MFMA waiting for its own freshly issued load.
-__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+// MFMA waiting for its own freshly issued load.  The asm keeps the loads above
+// it; the scheduling barrier keeps the machine scheduler from sinking them
+// back between the MFMAs (which it otherwise does to save registers).
+__device__ __forceinline__ void issue_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // Order this wave's own LDS writes before its later LDS reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -177,18 +182,23 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 // substitution, then X21 = -X22 L21 X11 at 16 and at 32 rows.
 // ============================================================================
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_solve_kernel(
+__global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
     uint16_t* __restrict__ arec) {
     constexpr int KP = DK + PAD;
     constexpr int RP = 36;  // pitch of the 32x32 fp32 temporary
-    __shared__ __align__(16) uint16_t Kc[C * KP];  // K [t][j]; later the solve temporary
-    __shared__ __align__(16) float Lf[C * LP];     // L [t][s]
-    __shared__ __align__(16) float Xs[C * LP];     // X = (I + L)^{-1} [t][s]
+    constexpr int KX = (C * KP * 2 > C * LP * 4) ? C * KP * 2 : C * LP * 4;
+    // K is dead once L is formed, so X reuses its space; the 32x32 temporary of
+    // the last level reuses rows 0-16 of L, which only the 16-row level reads.
+    // 35 KB in all, so four workgroups share a CU.
+    __shared__ __align__(16) unsigned char kx_[KX];  // K [t][j], then X = (I + L)^{-1} [t][s]
+    __shared__ __align__(16) float Lf[C * LP];       // L [t][s]
     __shared__ __align__(16) float bs[C];
-    static_assert(32 * RP * 4 <= C * KP * 2, "temporary fits in the K buffer");
-    float* Rtmp = reinterpret_cast<float*>(Kc);
+    static_assert(32 * RP <= 17 * LP, "temporary fits in rows 0-16 of L");
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(kx_);
+    float* Xs = reinterpret_cast<float*>(kx_);
+    float* Rtmp = Lf;
 
     const int gc = static_cast<int>(blockIdx.x) / n_heads, h = static_cast<int>(blockIdx.x) % n_heads;
     if (gc >= max_chunks || gc >= chunk_off[n_seq]) return;
@@ -219,9 +229,11 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(
     block_sync();
 
     // ---- L = strictly_lower(diag(beta) K K^T).  Wave 0: the four 16x16 diagonal
-    // blocks, then their inverses T_b = (I + L_bb)^{-1} (lane = (block, column)).
+    // blocks, then their inverses T_b = (I + L_bb)^{-1} (lane = (block, column)),
+    // kept in registers until K's space is free.
     // Wave 1: rows 32-63 x cols 0-31.  Waves 2, 3: the blocks (16..31, 0..15) and
     // (48..63, 32..47).
+    float x[16];
     if (wave == 0) {
         f32x4 d[4] = {};
         bf16x8 kf[4][DK / 32];
@@ -257,7 +269,6 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(
                 for (int s4 = 0; s4 < r; s4 += 4, ++p)
                     if (r >= r_lo && r < r_hi) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
         };
-        float x[16];
         auto solve_rows = [&](int r_lo, int r_hi) {
 #pragma unroll
             for (int r = 1, p = 0; r < 16; ++r) {
@@ -282,8 +293,6 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(
         load_rows(10, 16);
         issue_fence();
         solve_rows(6, 16);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
     } else if (wave == 1) {
         f32x16 acc = {};
         bf16x8 fa[DK / 16], fb[DK / 16];
@@ -315,6 +324,12 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + R + 4 * g16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
+    }
+    block_sync();
+    if (wave == 0) {
+        const int b = g16, c = m16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
     }
     block_sync();
 
@@ -414,28 +429,67 @@ __global__ __launch_bounds__(256) void chunk_solve_kernel(
 // ============================================================================
 // scan_kernel: the S-dependent chunk products, one workgroup of 8 waves per
 // (sequence, head, block of 64 value rows).
+//
+// Waves 0-3, the chain waves, each own 16 value rows i of the state -- S^T[j][i]
+// for every key channel j, as fp32 MFMA accumulators in 16x16 tiles -- and run
+// the chunk's S-dependent chain for those rows in registers:
+//   Y = X - K S^T            (X = V 2^{-G})
+//   U = A Y
+//   S^T <- diag(gamma) (S^T + K^T U)
+// A 16x16 accumulator tile holds, in lane (column n = l % 16, group g = l / 16),
+// rows 4g..4g+3.  Two tiles stacked along the row index give a lane the 8 rows
+// {4g..4g+3, 16+4g..16+4g+3}; taken as the 8 reduction indices of a
+// v_mfma_f32_16x16x32_bf16 B operand (the A operand reads the same indices,
+// two 8-byte pieces per lane), Y, U and S feed the next product straight from
+// the accumulators.
+// Waves 4-7, the out waves, form P = tril(Q K^T) (waves 4-6) and the outputs
+// O^T = 2^{G} (S Q^T + U^T P^T) of the same 16-row blocks, from the copies of S
+// and U that the chain waves leave in LDS.
+// Three barriers per chunk: staging | Y, U; P, S Q^T | S update; U^T P^T.
 // ============================================================================
 template <int DK>
 struct ScanSmem {
-    static constexpr int KP = DK + PAD;     // pitch of K, Q, S rows (bf16)
-    static constexpr int GP = BV + 4;       // pitch of G rows (fp32)
-    static constexpr int OP = BV + PAD;     // pitch of V and O rows (bf16)
-    static constexpr int mx(int a, int b) { return a > b ? a : b; }
+    static constexpr int KP = DK + PAD;         // pitch of K, Q, S rows (bf16)
+    static constexpr int GP = BV + 4;           // pitch of G rows (fp32)
+    static constexpr int OP = BV + PAD;         // pitch of V and O rows (bf16)
     static constexpr int HILO = 2 * C * CP * 2;
     // each region is its own __shared__ array, so the compiler knows accesses to
     // different regions never alias and can move loads ahead of unrelated stores
-    static constexpr int RK = C * KP * 2;             // K [t][j]
-    static constexpr int RQ = mx(C * KP * 2, HILO);   // Q [t][j], then U^T hi/lo [i][t]
-    static constexpr int RV = C * OP * 2;             // V [t][i]
-    static constexpr int RG = C * GP * 4;             // G [t][i]
-    static constexpr int RA = HILO;                   // A hi/lo [t][s]
-    static constexpr int RP = HILO;                   // P hi/lo [t][s]
-    static constexpr int RY = mx(HILO, C * OP * 2);   // Y^T hi/lo [i][t], then O [t][i]
-    static constexpr int RS = BV * KP * 2;            // S bf16 [i][j]
-    static constexpr int RB = BV * 4;                 // gamma = e^{G[C-1, :]}
-    static constexpr int RT = 2 * 8 * BV * 4;         // per-wave totals of log alpha, two chunks
-    static constexpr int TOTAL = RK + RQ + RV + RG + RA + RP + RY + RS + RB + RT;
+    static constexpr int RK = C * KP * 2;       // K [t][j]
+    static constexpr int RQ = C * KP * 2;       // Q [t][j]
+    static constexpr int RS = BV * KP * 2;      // S bf16 [i][j], the state entering the chunk
+    static constexpr int RA = HILO;             // A hi/lo [t][s]
+    static constexpr int RP = HILO;             // P hi/lo [t][s]
+    static constexpr int RU = 2 * BV * CP * 2;  // U^T hi/lo [i][t]
+    static constexpr int RV = C * OP * 2;       // V [t][i]
+    static constexpr int RO = C * OP * 2;       // O [t][i], staged for the store
+    static constexpr int RG = C * GP * 4;       // G [t][i] (log2 units)
+    static constexpr int RB = BV * 4;           // gamma = 2^{G[C-1, :]}
+    static constexpr int RT = 2 * 8 * BV * 4;   // per-wave totals of log2 alpha, two chunks
+    static constexpr int TOTAL = RK + RQ + RS + RA + RP + RU + RV + RO + RG + RB + RT;
 };
+
+// 16x16x32 operand whose 8 reduction values per lane are the stacked-tile
+// indices {4g..4g+3, 16+4g..16+4g+3} (g = lane / 16) past k0, from a row-major
+// [row][k] buffer: row row0 + lane % 16.
+__device__ __forceinline__ bf16x8 frag_st(const uint16_t* base, int pitch, int row0, int k0, int lane) {
+    const uint16_t* p = base + (row0 + (lane & 15)) * pitch + k0 + 4 * (lane >> 4);
+    const u16x4 lo = *reinterpret_cast<const u16x4*>(p);
+    const u16x4 hi = *reinterpret_cast<const u16x4*>(p + 16);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The stacked-tile B operand of two 16x16 accumulator tiles a (first 16 rows)
+// and b (next 16), rounded to bf16 as hi + lo parts.
+__device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split_bf16x2(a[0], a[1], h0, l0);
+    split_bf16x2(a[2], a[3], h1, l1);
+    split_bf16x2(b[0], b[1], h2, l2);
+    split_bf16x2(b[2], b[3], h3, l3);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
+}
 
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void scan_kernel(
@@ -449,32 +503,33 @@ __global__ __launch_bounds__(512) void scan_kernel(
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
     constexpr int KP = SM::KP, GP = SM::GP, OP = SM::OP;
-    constexpr int JT = DK / 32;  // 32-wide tiles along d_k
+    constexpr int NJ = DK / 16;   // 16-row tiles of S^T along j
+    constexpr int NM = DK / 32;   // 32-wide reduction steps over j
+    constexpr int PPR = DK / 8;   // 16-byte pieces per row of q or k
 
     __shared__ __align__(16) unsigned char rk_[SM::RK];
     __shared__ __align__(16) unsigned char rq_[SM::RQ];
-    __shared__ __align__(16) unsigned char rv_[SM::RV];
-    __shared__ __align__(16) unsigned char rg_[SM::RG];
+    __shared__ __align__(16) unsigned char rs_[SM::RS];
     __shared__ __align__(16) unsigned char ra_[SM::RA];
     __shared__ __align__(16) unsigned char rp_[SM::RP];
-    __shared__ __align__(16) unsigned char ry_[SM::RY];
-    __shared__ __align__(16) unsigned char rs_[SM::RS];
+    __shared__ __align__(16) unsigned char ru_[SM::RU];
+    __shared__ __align__(16) unsigned char rv_[SM::RV];
+    __shared__ __align__(16) unsigned char ro_[SM::RO];
+    __shared__ __align__(16) unsigned char rg_[SM::RG];
     __shared__ __align__(16) unsigned char rb_[SM::RB];
     __shared__ __align__(16) unsigned char rt_[SM::RT];
     uint16_t* Kc = reinterpret_cast<uint16_t*>(rk_);
     uint16_t* Qc = reinterpret_cast<uint16_t*>(rq_);
-    uint16_t* Ut_hi = reinterpret_cast<uint16_t*>(rq_);
-    uint16_t* Ut_lo = Ut_hi + BV * CP;
-    uint16_t* Vr = reinterpret_cast<uint16_t*>(rv_);
-    float* Gs = reinterpret_cast<float*>(rg_);
+    uint16_t* Sx = reinterpret_cast<uint16_t*>(rs_);
     uint16_t* A_hi = reinterpret_cast<uint16_t*>(ra_);
     uint16_t* A_lo = A_hi + C * CP;
     uint16_t* P_hi = reinterpret_cast<uint16_t*>(rp_);
     uint16_t* P_lo = P_hi + C * CP;
-    uint16_t* Yt_hi = reinterpret_cast<uint16_t*>(ry_);
-    uint16_t* Yt_lo = Yt_hi + BV * CP;
-    uint16_t* Os = reinterpret_cast<uint16_t*>(ry_);
-    uint16_t* Sb = reinterpret_cast<uint16_t*>(rs_);
+    uint16_t* Ux_hi = reinterpret_cast<uint16_t*>(ru_);
+    uint16_t* Ux_lo = Ux_hi + BV * CP;
+    uint16_t* Vr = reinterpret_cast<uint16_t*>(rv_);
+    uint16_t* Os = reinterpret_cast<uint16_t*>(ro_);
+    float* Gs = reinterpret_cast<float*>(rg_);
     float* gam = reinterpret_cast<float*>(rb_);
     float* Tot = reinterpret_cast<float*>(rt_);  // [2][8][BV]
 
@@ -484,28 +539,49 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int lane = tid & 63;
     // the wave index is uniform: keep it (and every tile offset derived from it) scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wave < 4;
+    const int blk = wave & 3;  // value rows 16 blk .. 16 blk + 15 of this workgroup's block
     const int64_t H = n_heads;
     const int h = u.head;
     const int i0 = u.vblk * BV;
     const int64_t row_qk = H * DK, row_v = H * DV;  // element strides between tokens
     const int chunk0 = chunk_off[u.seq];
 
-    // ---- state: wave w < 2 * JT owns the S^T tile (j-tile s_jt, i-tile s_it)
-    // in fp32 accumulators
-    const bool owns_s = wave < 2 * JT;
-    const int s_jt = wave % JT, s_it = wave / JT;
+    // ---- state of the chain waves: Sacc[jt] = S^T rows 16 jt .. 16 jt + 15 (key
+    // channels), columns = this wave's 16 value rows
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
-    f32x16 accS = {};
-    if (owns_s) {
+    f32x4 Sacc[NJ];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = 32 * s_jt + acc_row(r, lane), i = 32 * s_it + (lane & 31);
-            accS[r] = S0 ? S0[s_base + static_cast<int64_t>(i) * DK + j] : 0.f;
-        }
+    for (int jt = 0; jt < NJ; ++jt) Sacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (chain && S0) {
+        const float* src = S0 + s_base + static_cast<int64_t>(16 * blk + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) Sacc[jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
     }
+    // negated bf16 copy of S as the B operands of K (-S)^T, one per 32-wide j step
+    bf16x8 Sb[NM];
+    auto pack_state = [&](int ln) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            u32x4 w;
+            w[0] = pack_bf16(-Sacc[2 * m][0], -Sacc[2 * m][1]);
+            w[1] = pack_bf16(-Sacc[2 * m][2], -Sacc[2 * m][3]);
+            w[2] = pack_bf16(-Sacc[2 * m + 1][0], -Sacc[2 * m + 1][1]);
+            w[3] = pack_bf16(-Sacc[2 * m + 1][2], -Sacc[2 * m + 1][3]);
+            Sb[m] = __builtin_bit_cast(bf16x8, w);
+        }
+        // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
+        uint16_t* dst = Sx + (16 * blk + (ln & 15)) * KP + 4 * (ln >> 4);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            uint2 w;
+            w.x = pack_bf16(Sacc[jt][0], Sacc[jt][1]);
+            w.y = pack_bf16(Sacc[jt][2], Sacc[jt][3]);
+            *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+        }
+    };
 
-    // ---- register prefetch of a chunk's inputs, two chunks ahead (two register
-    // sets in turn); every load reads whole rows.
+    // ---- register prefetch of the next chunk's inputs; every load reads whole rows.
     // K, Q: 16-byte piece tid (and tid + 512) of the row-major chunk.
     // V: row tid/8, 8 values at 8*(tid%8).
     // alpha: wave w holds token rows 8w..8w+7, lane = value row (one 256-byte
@@ -513,14 +589,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // A record: pieces tid and tid + 512.
     // The loads (and the O store below) are issued unconditionally: a chunk past
     // the end gets an empty buffer range, so nothing is accessed.  Uniform control
-    // flow lets the compiler count outstanding memory operations exactly, instead
-    // of waiting for all of them where a conditional path merges.
-    constexpr int PPR = DK / 8;  // 16-byte pieces per row of q or k
+    // flow lets the compiler count outstanding memory operations exactly.
     struct Pf {
         u32x4 k0, k1, q0, q1, v, A0, A1;
         float a[8];
     };
-    auto prefetch = [&](Pf& pf, int64_t tc, int n, int gc) {
+    Pf pf = {};
+    auto prefetch = [&](int64_t tc, int n, int gc) {
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
         const bool any = n > 0;
         {
@@ -567,30 +642,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     // one 16-byte piece of an A record -> A hi/lo [t][s]
     auto stage_a = [&](u32x4 val, int piece) {
-        const int blk = piece >> 8, half = (piece >> 7) & 1, row = (piece >> 2) & 31, c8 = 8 * (piece & 3);
-        uint16_t* dst = (half ? A_lo : A_hi) + ((blk == 0 ? 0 : 32) + row) * CP + (blk == 2 ? 32 : 0) + c8;
+        const int b = piece >> 8, half = (piece >> 7) & 1, row = (piece >> 2) & 31, c8 = 8 * (piece & 3);
+        uint16_t* dst = (half ? A_lo : A_hi) + ((b == 0 ? 0 : 32) + row) * CP + (b == 2 ? 32 : 0) + c8;
         *reinterpret_cast<u32x4*>(dst) = val;
-    };
-
-    // bf16 copy of the state for the S-side products (S^T registers 4rb..4rb+3
-    // hold 4 consecutive key channels j of one value row i)
-    auto write_state_copy = [&](int ln) {
-        if (owns_s) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int j = 32 * s_jt + 8 * rb + 4 * (ln >> 5), i = 32 * s_it + (ln & 31);
-                uint2 w;
-                w.x = pack_bf16(accS[4 * rb], accS[4 * rb + 1]);
-                w.y = pack_bf16(accS[4 * rb + 2], accS[4 * rb + 3]);
-                *reinterpret_cast<uint2*>(Sb + i * KP + j) = w;
-            }
-        }
     };
 
     // G is kept in base-2 units (log2 alpha summed; e^{G} = 2^{G}), so every log
     // and exp below is one hardware instruction (v_log_f32 / v_exp_f32).  alpha
     // is taken to be a normal fp32 number in (0, 1].
-    // The log-decay cumsum G of a chunk is formed in two steps one chunk apart,
+    // The log-decay cumsum G of a chunk is formed in two steps one phase apart,
     // so the prefix across waves never needs a barrier of its own:
     // local_scan -- each wave's inclusive prefix over its 8 token rows (in
     //   registers: a lane holds one value row), kept in the alpha registers; the
@@ -598,7 +658,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // finalize   -- after a barrier, add the totals of the waves before (the
     //   rows before this wave's) and write G [t][i] and gamma.
     // Rows past the sequence end contribute log alpha = 0.
-    auto local_scan = [&](Pf& pf, int n, int par, int ln) {
+    auto local_scan = [&](int n, int par, int ln) {
         float run = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -607,25 +667,26 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
         Tot[(par * 8 + wave) * BV + ln] = run;
     };
-    auto finalize = [&](const Pf& pf, int par, int ln) {
+    auto finalize = [&](int par, int ln) {
         float carry = 0.f;
-        for (int b = 0; b < wave; ++b) carry += Tot[(par * 8 + b) * BV + ln];
+#pragma unroll
+        for (int b = 0; b < 7; ++b) {
+            const float tb = Tot[(par * 8 + b) * BV + ln];
+            carry += b < wave ? tb : 0.f;
+        }
 #pragma unroll
         for (int r = 0; r < 8; ++r) Gs[(8 * wave + r) * GP + ln] = pf.a[r] + carry;
         if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(pf.a[7] + carry);
     };
 
-    Pf pf0 = {}, pf1 = {};
-    prefetch(pf0, u.t0, chunk_len(u.t0), chunk0);
-    prefetch(pf1, u.t0 + C, chunk_len(u.t0 + C), chunk0 + 1);
-    local_scan(pf0, chunk_len(u.t0), 0, lane);
-    write_state_copy(lane);
+    prefetch(u.t0, chunk_len(u.t0), chunk0);
+    local_scan(chunk_len(u.t0), 0, lane);
+    if (chain) pack_state(lane);
 
     int64_t prev_tc = u.t0;
     int prev_n = 0;
-    // chunk c: stage it from pf (whose alpha registers hold its local prefix),
-    // pre-scan the next chunk's alpha in nx, then reuse pf for chunk c + 2
-    auto chunk_step = [&](Pf& pf, Pf& nx, int c) {
+    const int n_chunks = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
+    for (int c = 0; c < n_chunks; ++c) {
         const int64_t tc = u.t0 + static_cast<int64_t>(c) * C;
         const int gc = chunk0 + c;
         const int n = chunk_len(tc);
@@ -636,10 +697,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o;
         const int td = ln + 64 * wave;
+        const int g = ln >> 4, m16 = ln & 15;
         block_sync();  // the previous chunk is done with every buffer
 
-        // ======== stage this chunk and finish its G, pre-scan the next chunk's
-        // alpha, store the previous chunk's O, issue the loads two chunks ahead
+        // ======== stage this chunk and finish its G, store the previous chunk's
+        // O, issue the next chunk's loads
         *reinterpret_cast<u32x4*>(Kc + (td / PPR) * KP + 8 * (td % PPR)) = pf.k0;
         *reinterpret_cast<u32x4*>(Qc + (td / PPR) * KP + 8 * (td % PPR)) = pf.q0;
         if constexpr (DK == 128) {
@@ -649,63 +711,81 @@ __global__ __launch_bounds__(512) void scan_kernel(
         *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pf.v;
         stage_a(pf.A0, td);
         if (td < A_RECORD_PIECES - 512) stage_a(pf.A1, td + 512);
-        finalize(pf, c & 1, ln);
-        local_scan(nx, chunk_len(tc + C), (c + 1) & 1, ln);
+        finalize(c & 1, ln);
         store_o(prev_tc, prev_n, td);
-        prefetch(pf, tc + 2 * C, chunk_len(tc + 2 * C), gc + 2);
+        prefetch(tc + C, chunk_len(tc + C), gc + 1);
         block_sync();
 
-        // ======== waves 0-3: K S^T, then Y = V e^{-G} - K S^T -> Y^T hi/lo [i][t];
-        // waves 4-7: O^T = S Q^T (kept in registers), and waves 4-6 the tiles of
-        // P = tril(Q K^T) hi/lo (formed transposed, D[s][t], so each lane holds 4
-        // consecutive s of one t)
-        f32x16 accO = {};
-        const int o_ib = (wave - 4) >> 1, o_tb = (wave - 4) & 1;  // O^T tile (i-tile, t-tile)
-        if (wave < 4) {
-            const int y_tb = wave >> 1, y_ib = wave & 1;
-            f32x16 accY = {};
+        f32x4 Oacc[4];
+        bf16x8 Uh[2], Ul[2];
+        if (chain) {
+            // ======== Y = X - K S^T, then U = A Y, for value rows i = 16 blk + m16
+            // (lane column); rows t = 16 tt + 4g + r of tile tt
+            f32x4 Y[4];
+            {
+                const int i = 16 * blk + m16;
 #pragma unroll
-            for (int half = 0; half < DK / 64; ++half) {
-                bf16x8 fk[4], fs[4];
+                for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    fk[kk] = frag(Kc, KP, 32 * y_tb, 64 * half + 16 * kk, ln);
-                    fs[kk] = frag(Sb, KP, 32 * y_ib, 64 * half + 16 * kk, ln);
-                }
-                issue_fence();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) accY = mfma(fk[kk], fs[kk], accY);
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * tt + 4 * g + r;
+                        Y[tt][r] = bf16_bits_to_f32(Vr[t * OP + i]) * __builtin_amdgcn_exp2f(-Gs[t * GP + i]);
+                    }
             }
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                // registers 4rb..4rb+3: 4 consecutive t of one i
-                const int t = 32 * y_tb + 8 * rb + 4 * (ln >> 5), i = 32 * y_ib + (ln & 31);
-                float xv[4];
+            for (int m = 0; m < NM; ++m) {
+                bf16x8 kf[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    xv[e] = bf16_bits_to_f32(Vr[(t + e) * OP + i]) * __builtin_amdgcn_exp2f(-Gs[(t + e) * GP + i]) -
-                            accY[4 * rb + e];
-                uint2 wh, wl;
-                split_bf16x2(xv[0], xv[1], wh.x, wl.x);
-                split_bf16x2(xv[2], xv[3], wh.y, wl.y);
-                *reinterpret_cast<uint2*>(Yt_hi + i * CP + t) = wh;
-                *reinterpret_cast<uint2*>(Yt_lo + i * CP + t) = wl;
+                for (int tt = 0; tt < 4; ++tt) kf[tt] = frag_st(Kc, KP, 16 * tt, 32 * m, ln);
+                issue_fence();
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Y[tt] = mfma16(kf[tt], Sb[m], Y[tt]);
+            }
+            bf16x8 Yh[2], Yl[2];
+            split_stack(Y[0], Y[1], Yh[0], Yl[0]);
+            split_stack(Y[2], Y[3], Yh[1], Yl[1]);
+            // A is lower triangular: t-tiles 0, 1 need s < 32 only
+            f32x4 U[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const bf16x8 ah0 = frag_st(A_hi, CP, 16 * tt, 0, ln), al0 = frag_st(A_lo, CP, 16 * tt, 0, ln);
+                bf16x8 ah1 = {}, al1 = {};
+                if (tt >= 2) {
+                    ah1 = frag_st(A_hi, CP, 16 * tt, 32, ln);
+                    al1 = frag_st(A_lo, CP, 16 * tt, 32, ln);
+                }
+                issue_fence();
+                U[tt] = mfma16(ah0, Yh[0], U[tt]);
+                U[tt] = mfma16(al0, Yh[0], U[tt]);
+                U[tt] = mfma16(ah0, Yl[0], U[tt]);
+                if (tt >= 2) {
+                    U[tt] = mfma16(ah1, Yh[1], U[tt]);
+                    U[tt] = mfma16(al1, Yh[1], U[tt]);
+                    U[tt] = mfma16(ah1, Yl[1], U[tt]);
+                }
+            }
+            split_stack(U[0], U[1], Uh[0], Ul[0]);
+            split_stack(U[2], U[3], Uh[1], Ul[1]);
+            // U^T hi/lo [i][t] for the out waves: the stacked packs hold t = 32 m +
+            // 4g .. +3 (words 0, 1) and 32 m + 16 + 4g .. +3 (words 2, 3)
+            {
+                const int i = 16 * blk + m16;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const u32x4 wh = __builtin_bit_cast(u32x4, Uh[m]), wl = __builtin_bit_cast(u32x4, Ul[m]);
+                    *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 4 * g) = uint2{wh[0], wh[1]};
+                    *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 16 + 4 * g) = uint2{wh[2], wh[3]};
+                    *reinterpret_cast<uint2*>(Ux_lo + i * CP + 32 * m + 4 * g) = uint2{wl[0], wl[1]};
+                    *reinterpret_cast<uint2*>(Ux_lo + i * CP + 32 * m + 16 + 4 * g) = uint2{wl[2], wl[3]};
+                }
             }
         } else {
-#pragma unroll
-            for (int half = 0; half < DK / 64; ++half) {
-                bf16x8 fs[4], fq[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    fs[kk] = frag(Sb, KP, 32 * o_ib, 64 * half + 16 * kk, ln);
-                    fq[kk] = frag(Qc, KP, 32 * o_tb, 64 * half + 16 * kk, ln);
-                }
-                issue_fence();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) accO = mfma(fs[kk], fq[kk], accO);
-            }
+            // ======== waves 4-6: P = tril(Q K^T) hi/lo [t][s], formed transposed
+            // (32x32 tile D[s][t], so each lane holds 4 consecutive s of one t);
+            // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1), and (1,0) is all zero
             if (wave < 7) {
-                // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1); (1,0) is all zero
                 const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
                 f32x16 acc = {};
 #pragma unroll
@@ -734,134 +814,99 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     *reinterpret_cast<uint2*>(P_lo + t * CP + s0) = wl;
                 }
             }
-        }
-        block_sync();
-
-        // ======== U = A Y on 16x16 tiles (t-block tr; i-blocks ic, ic + 1), all
-        // waves -> U^T hi/lo [i][t]
-        {
-            const int tr = wave >> 1, ic = 2 * (wave & 1);
-            f32x4 acc0 = {}, acc1 = {};
-            const int nks = tr < 2 ? 1 : 2;  // A is lower triangular: s < 16 (tr + 1)
+            // O^T = S Q^T for value rows 16 blk + 4g + r (tile rows) and tokens
+            // t = 16 tt + m16 (tile column)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks < nks) {
-                    const bf16x8 ah = frag16(A_hi, CP, 16 * tr, 32 * ks, ln);
-                    const bf16x8 al = frag16(A_lo, CP, 16 * tr, 32 * ks, ln);
-                    const bf16x8 y0h = frag16(Yt_hi, CP, 16 * ic, 32 * ks, ln);
-                    const bf16x8 y0l = frag16(Yt_lo, CP, 16 * ic, 32 * ks, ln);
-                    const bf16x8 y1h = frag16(Yt_hi, CP, 16 * ic + 16, 32 * ks, ln);
-                    const bf16x8 y1l = frag16(Yt_lo, CP, 16 * ic + 16, 32 * ks, ln);
-                    issue_fence();
-                    acc0 = mfma16(ah, y0h, acc0);
-                    acc1 = mfma16(ah, y1h, acc1);
-                    acc0 = mfma16(al, y0h, acc0);
-                    acc1 = mfma16(al, y1h, acc1);
-                    acc0 = mfma16(ah, y0l, acc0);
-                    acc1 = mfma16(ah, y1l, acc1);
-                }
-            }
-            // lane (column i, group g) holds rows t = 16 tr + 4 g + r
-            const int t = 16 * tr + 4 * (ln >> 4);
+            for (int tt = 0; tt < 4; ++tt) Oacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x4& a = half ? acc1 : acc0;
-                const int i = 16 * (ic + half) + (ln & 15);
-                uint2 wh, wl;
-                split_bf16x2(a[0], a[1], wh.x, wl.x);
-                split_bf16x2(a[2], a[3], wh.y, wl.y);
-                *reinterpret_cast<uint2*>(Ut_hi + i * CP + t) = wh;
-                *reinterpret_cast<uint2*>(Ut_lo + i * CP + t) = wl;
+            for (int m = 0; m < NM; ++m) {
+                const bf16x8 sf = frag16(Sx, KP, 16 * blk, 32 * m, ln);
+                bf16x8 qf[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) qf[tt] = frag16(Qc, KP, 16 * tt, 32 * m, ln);
+                issue_fence();
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Oacc[tt] = mfma16(sf, qf[tt], Oacc[tt]);
             }
         }
         block_sync();
 
-        // ======== waves 4-7: O^T = e^G (S Q^T + U^T P^T), staged as bf16 O [t][i];
-        // S^T = diag(gamma) (S^T + K^T U) on the state-owning waves
-        if (wave >= 4) {
-            bf16x8 uh[4], ul[4], ph[4], pl[4];
+        if (chain) {
+            // ======== S^T += K^T U, then the decay: the K^T operand (rows j,
+            // reduction t) comes from row-major K through the transposing read --
+            // in 16-lane group g, lane m16 addresses token row 32 m + 4g + m16/4
+            // (+16 for the second half) at key channels 16 jt + 4 (m16 % 4) .. +3
+            const uint16_t* ktb = Kc + (4 * g + (m16 >> 2)) * KP + 4 * (m16 & 3);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (o_tb + 1)) {  // P is lower triangular
-                    uh[kk] = frag(Ut_hi, CP, 32 * o_ib, 16 * kk, ln);
-                    ul[kk] = frag(Ut_lo, CP, 32 * o_ib, 16 * kk, ln);
-                    ph[kk] = frag(P_hi, CP, 32 * o_tb, 16 * kk, ln);
-                    pl[kk] = frag(P_lo, CP, 32 * o_tb, 16 * kk, ln);
+            for (int jt = 0; jt < NJ; jt += 2) {
+                bf16x8 kt[2][2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const s16x4 t0 = lds_read_tr16(ktb + (32 * m) * KP + 16 * (jt + a));
+                        const s16x4 t1 = lds_read_tr16(ktb + (32 * m + 16) * KP + 16 * (jt + a));
+                        kt[a][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                issue_fence();
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        Sacc[jt + a] = mfma16(kt[a][m], Uh[m], Sacc[jt + a]);
+                        Sacc[jt + a] = mfma16(kt[a][m], Ul[m], Sacc[jt + a]);
+                    }
+            }
+            const float gm = gam[16 * blk + m16];
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) Sacc[jt] *= gm;
+            pack_state(ln);
+        } else {
+            // ======== O^T += U^T P^T (P is lower triangular: t-tiles 0, 1 need s < 32),
+            // then O = 2^{G} O, staged as bf16 [t][i]
+            const bf16x8 uh0 = frag16(Ux_hi, CP, 16 * blk, 0, ln), ul0 = frag16(Ux_lo, CP, 16 * blk, 0, ln);
+            const bf16x8 uh1 = frag16(Ux_hi, CP, 16 * blk, 32, ln), ul1 = frag16(Ux_lo, CP, 16 * blk, 32, ln);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const bf16x8 ph0 = frag16(P_hi, CP, 16 * tt, 0, ln), pl0 = frag16(P_lo, CP, 16 * tt, 0, ln);
+                bf16x8 ph1 = {}, pl1 = {};
+                if (tt >= 2) {
+                    ph1 = frag16(P_hi, CP, 16 * tt, 32, ln);
+                    pl1 = frag16(P_lo, CP, 16 * tt, 32, ln);
+                }
+                issue_fence();
+                Oacc[tt] = mfma16(uh0, ph0, Oacc[tt]);
+                Oacc[tt] = mfma16(ul0, ph0, Oacc[tt]);
+                Oacc[tt] = mfma16(uh0, pl0, Oacc[tt]);
+                if (tt >= 2) {
+                    Oacc[tt] = mfma16(uh1, ph1, Oacc[tt]);
+                    Oacc[tt] = mfma16(ul1, ph1, Oacc[tt]);
+                    Oacc[tt] = mfma16(uh1, pl1, Oacc[tt]);
                 }
             }
-            const int t = 32 * o_tb + (ln & 31);
-            f32x4 g4[4];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                g4[rb] = *reinterpret_cast<const f32x4*>(Gs + t * GP + 32 * o_ib + 8 * rb + 4 * (ln >> 5));
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 2 * (o_tb + 1)) {
-                    accO = mfma(uh[kk], ph[kk], accO);
-                    accO = mfma(ul[kk], ph[kk], accO);
-                    accO = mfma(uh[kk], pl[kk], accO);
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int i = 32 * o_ib + 8 * rb + 4 * (ln >> 5);
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = 16 * tt + m16, i = 16 * blk + 4 * g;
+                const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gs + t * GP + i);
                 uint2 w;
-                w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[rb][0]) * accO[4 * rb],
-                                __builtin_amdgcn_exp2f(g4[rb][1]) * accO[4 * rb + 1]);
-                w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[rb][2]) * accO[4 * rb + 2],
-                                __builtin_amdgcn_exp2f(g4[rb][3]) * accO[4 * rb + 3]);
+                w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[0]) * Oacc[tt][0], __builtin_amdgcn_exp2f(g4[1]) * Oacc[tt][1]);
+                w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[2]) * Oacc[tt][2], __builtin_amdgcn_exp2f(g4[3]) * Oacc[tt][3]);
                 *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
             }
         }
-        if (owns_s) {
-            // K^T operand (rows j, reduction over t) read from row-major K with the
-            // transposing load: in 16-lane group g, lane m addresses token row
-            // 16kk + 8(g>>1) + m/4 (+4 for the second half) at key channels
-            // 32 s_jt + 16(g&1) + 4(m%4) .. +3
-            const int g = ln >> 4, m = ln & 15;
-            const uint16_t* ktb = Kc + (8 * (g >> 1) + (m >> 2)) * KP + 32 * s_jt + 16 * (g & 1) + 4 * (m & 3);
-            bf16x8 kt[4], uh[4], ul[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const s16x4 t0 = lds_read_tr16(ktb + 16 * kk * KP), t1 = lds_read_tr16(ktb + (16 * kk + 4) * KP);
-                kt[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-                uh[kk] = frag(Ut_hi, CP, 32 * s_it, 16 * kk, ln);
-                ul[kk] = frag(Ut_lo, CP, 32 * s_it, 16 * kk, ln);
-            }
-            const float gm = gam[32 * s_it + (ln & 31)];
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                accS = mfma(kt[kk], uh[kk], accS);
-                accS = mfma(kt[kk], ul[kk], accS);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) accS[r] *= gm;
-        }
-        write_state_copy(ln);  // the old copy's last readers (K S^T, S Q^T) are two barriers back
+        local_scan(chunk_len(tc + C), (c + 1) & 1, ln);
         prev_tc = tc;
         prev_n = n;
-    };
-    // Whole pairs of chunks, then an odd last one: every path into a step has
-    // issued the same memory operations, so the compiler's wait counts stay exact.
-    const int n_chunks = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
-    for (int c = 0; c + 1 < n_chunks; c += 2) {
-        chunk_step(pf0, pf1, c);
-        chunk_step(pf1, pf0, c + 1);
     }
-    if (n_chunks & 1) chunk_step(pf0, pf1, n_chunks - 1);
     if (prev_n > 0) {
         block_sync();
         store_o(prev_tc, prev_n, tid);
     }
 
-    if (S_T && owns_s) {
+    if (S_T && chain) {
+        float* dst = S_T + s_base + static_cast<int64_t>(16 * blk + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = 32 * s_jt + acc_row(r, lane), i = 32 * s_it + (lane & 31);
-            S_T[s_base + static_cast<int64_t>(i) * DK + j] = accS[r];
-        }
+        for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = Sacc[jt];
     }
 }
 
