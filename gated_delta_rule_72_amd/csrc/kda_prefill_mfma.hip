@@ -449,15 +449,21 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
 // ============================================================================
 template <int DK>
 struct ScanSmem {
-    static constexpr int KP = DK + PAD;         // pitch of K, Q, S rows (bf16)
+    // Row pitches (bf16) are chosen per access pattern: with the pitch in dwords
+    // = 4 (mod 8), the 16-row 8-byte operand reads and the 32-row 16-byte reads
+    // are free of bank conflicts; with 0 (mod 8), the transposing reads and the
+    // 16-row 16-byte reads are.  K is read both ways; Q and the S copy are read
+    // by 16-row 16-byte loads.
+    static constexpr int KP = DK + PAD;         // pitch of K rows
+    static constexpr int QP = DK + 2 * PAD;     // pitch of Q and S rows
     static constexpr int GP = BV + 4;           // pitch of G rows (fp32)
     static constexpr int OP = BV + PAD;         // pitch of V and O rows (bf16)
     static constexpr int HILO = 2 * C * CP * 2;
     // each region is its own __shared__ array, so the compiler knows accesses to
     // different regions never alias and can move loads ahead of unrelated stores
     static constexpr int RK = C * KP * 2;       // K [t][j]
-    static constexpr int RQ = C * KP * 2;       // Q [t][j]
-    static constexpr int RS = BV * KP * 2;      // S bf16 [i][j], the state entering the chunk
+    static constexpr int RQ = C * QP * 2;       // Q [t][j]
+    static constexpr int RS = BV * QP * 2;      // S bf16 [i][j], the state entering the chunk
     static constexpr int RA = HILO;             // A hi/lo [t][s]
     static constexpr int RP = HILO;             // P hi/lo [t][s]
     static constexpr int RU = 2 * BV * CP * 2;  // U^T hi/lo [i][t]
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, GP = SM::GP, OP = SM::OP;
+    constexpr int KP = SM::KP, QP = SM::QP, GP = SM::GP, OP = SM::OP;
     constexpr int NJ = DK / 16;   // 16-row tiles of S^T along j
     constexpr int NM = DK / 32;   // 32-wide reduction steps over j
     constexpr int PPR = DK / 8;   // 16-byte pieces per row of q or k
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             Sb[m] = __builtin_bit_cast(bf16x8, w);
         }
         // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
-        uint16_t* dst = Sx + (16 * blk + (ln & 15)) * KP + 4 * (ln >> 4);
+        uint16_t* dst = Sx + (16 * blk + (ln & 15)) * QP + 4 * (ln >> 4);
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
             uint2 w;
@@ -703,10 +709,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
         // ======== stage this chunk and finish its G, store the previous chunk's
         // O, issue the next chunk's loads
         *reinterpret_cast<u32x4*>(Kc + (td / PPR) * KP + 8 * (td % PPR)) = pf.k0;
-        *reinterpret_cast<u32x4*>(Qc + (td / PPR) * KP + 8 * (td % PPR)) = pf.q0;
+        *reinterpret_cast<u32x4*>(Qc + (td / PPR) * QP + 8 * (td % PPR)) = pf.q0;
         if constexpr (DK == 128) {
             *reinterpret_cast<u32x4*>(Kc + (32 + td / PPR) * KP + 8 * (td % PPR)) = pf.k1;
-            *reinterpret_cast<u32x4*>(Qc + (32 + td / PPR) * KP + 8 * (td % PPR)) = pf.q1;
+            *reinterpret_cast<u32x4*>(Qc + (32 + td / PPR) * QP + 8 * (td % PPR)) = pf.q1;
         }
         *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pf.v;
         stage_a(pf.A0, td);
@@ -794,7 +800,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
                         fa[kk] = frag(Kc, KP, 32 * sb, 64 * half + 16 * kk, ln);
-                        fb[kk] = frag(Qc, KP, 32 * tb, 64 * half + 16 * kk, ln);
+                        fb[kk] = frag(Qc, QP, 32 * tb, 64 * half + 16 * kk, ln);
                     }
                     issue_fence();
 #pragma unroll
@@ -820,10 +826,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int tt = 0; tt < 4; ++tt) Oacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const bf16x8 sf = frag16(Sx, KP, 16 * blk, 32 * m, ln);
+                const bf16x8 sf = frag16(Sx, QP, 16 * blk, 32 * m, ln);
                 bf16x8 qf[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) qf[tt] = frag16(Qc, KP, 16 * tt, 32 * m, ln);
+                for (int tt = 0; tt < 4; ++tt) qf[tt] = frag16(Qc, QP, 16 * tt, 32 * m, ln);
                 issue_fence();
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) Oacc[tt] = mfma16(sf, qf[tt], Oacc[tt]);
