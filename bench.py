@@ -182,7 +182,8 @@ def bench_prefill(args, torch, kda, I):
         launch_ms=dict(avg=avg_ms, min=float(np.min(launch_ms)), max=float(np.max(launch_ms))),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic("prefill"),
-                      kernel="prefill (chunkwise, fused)", alg_bytes_per_launch=alg_bytes,
+                      kernel="prefill call: chunk_offsets_kernel + chunk_solve_kernel + scan_kernel",
+                      alg_bytes_per_launch=alg_bytes,
                       mfma_nominal_tflops=round(nominal_tflops, 1),
                       mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
     )
@@ -190,30 +191,31 @@ def bench_prefill(args, torch, kda, I):
 
 
 def cpu_baseline_prefill(inp, o_gpu, S_gpu):
-    """The oracle on a bounded sample: sequence 0, all heads, all 8192 tokens."""
+    """The oracle on one whole step (all sequences and heads), timed on the host
+    cores; its outputs also give the step's parity against the GPU."""
     import oracle
-    s, e = int(inp.cu_seqlens[0]), int(inp.cu_seqlens[1])
-    q, k, v = (inp.f32(n)[s:e] for n in ("q", "k", "v"))
-    a, b = inp.alpha[s:e], inp.beta[s:e]
-    S0 = inp.S0[0:1].astype(np.float64)
+    q, k, v = (inp.f32(n) for n in ("q", "k", "v"))
+    S0 = inp.S0.astype(np.float64)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
-    o_ref, S_ref = oracle.prefill(q, k, v, a, b, S0)
+    o_ref, S_ref = oracle.prefill(q, k, v, inp.alpha, inp.beta, S0, inp.cu_seqlens)
     dt = time.perf_counter() - t0
-    tokens = e - s
-    og = o_gpu[s:e].float().cpu().numpy().astype(np.float64)
-    Sg = S_gpu[0:1].cpu().numpy().astype(np.float64)
+    tokens = int(inp.cu_seqlens[-1])
+    og = o_gpu.float().cpu().numpy()
+    Sg = S_gpu.cpu().numpy()
     worst = [0.0, 0.0, 0.0, 0.0]
-    for h in range(inp.H):
-        m, r = rel(og[:, h], o_ref[:, h])
-        ms, rs = rel(Sg[0, h], S_ref[0, h])
-        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms), max(worst[3], rs)]
+    for n in range(inp.n_seq):
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        for h in range(inp.H):
+            m, r = rel(og[s:e, h].astype(np.float64), o_ref[s:e, h])
+            ms, rs = rel(Sg[n, h].astype(np.float64), S_ref[n, h])
+            worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms), max(worst[3], rs)]
     cpu = dict(value=round(tokens / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
-               sample=f"sequence 0 of the batched prefill workload: {tokens} tokens x {inp.H} heads "
-                      f"(1/{inp.n_seq} of a step), fp64 C oracle, {dt:.2f}s wall",
+               sample=f"one whole step of the batched prefill workload ({inp.n_seq} sequences x "
+                      f"{tokens // inp.n_seq} tokens x {inp.H} heads), fp64 C oracle, {dt:.2f}s wall",
                cpu_model=platform.processor() or platform.machine())
     parity = dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
-                  scope="sequence 0, all 32 heads, worst (sequence, head) slice")
+                  scope=f"all {inp.n_seq} sequences x {inp.H} heads, worst (sequence, head) slice")
     return cpu, parity
 
 
