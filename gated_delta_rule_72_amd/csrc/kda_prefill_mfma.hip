@@ -30,6 +30,8 @@
 // bf16 copy of the fp32 state.  A product of two split operands takes three
 // MFMAs (hi*hi + lo*hi + hi*lo).  The solve runs in fp32: VALU forward
 // substitution on 16x16 diagonal blocks, fp32 MFMA for the off-diagonal blocks.
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
@@ -176,10 +178,12 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 }
 
 // ============================================================================
-// chunk_solve_kernel: A = (I + L)^{-1} diag(beta) of one (chunk, head) per
-// workgroup of 4 waves, written as the A record described above.  The inverse
-// X = (I + L)^{-1} is built by blocks: 16x16 diagonal blocks by forward
-// substitution, then X21 = -X22 L21 X11 at 16 and at 32 rows.
+// chunk_solve_kernel: A = (I + L)^{-1} diag(beta) of every (chunk, head), each
+// written as the A record described above.  Workgroups of 4 waves loop over the
+// (chunk, head) items, four per CU, loading the next item's K and beta while
+// they solve the current one.  The inverse X = (I + L)^{-1} is built by blocks:
+// 16x16 diagonal blocks by forward substitution, then X21 = -X22 L21 X11 at 16
+// and at 32 rows.
 // ============================================================================
 template <int DK>
 __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
@@ -200,33 +204,50 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     float* Xs = reinterpret_cast<float*>(kx_);
     float* Rtmp = Lf;
 
-    const int gc = static_cast<int>(blockIdx.x) / n_heads, h = static_cast<int>(blockIdx.x) % n_heads;
-    if (gc >= max_chunks || gc >= chunk_off[n_seq]) return;
-    const ChunkRef ch = chunk_ref(gc, n_seq, n_tok, cu_seqlens, chunk_off);
     const int64_t H = n_heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g16 = lane >> 4, m16 = lane & 15;
+    const int total = min(chunk_off[n_seq], max_chunks) * n_heads;  // (chunk, head) items
 
-    // ---- K and beta of the chunk (rows past the sequence end read as zero)
-    {
-        const int64_t tok0 = ch.t0 * H + h;
-        const auto rk = make_rsrc(k + tok0 * DK, ((ch.n - 1) * H * DK + DK) * 2);
-        constexpr int PIECES = C * DK / 8;
+    // ---- loads of one item's K and beta into registers (rows past the sequence
+    // end read as zero; an item past the last gets empty ranges)
+    constexpr int PIECES = C * DK / 8 / 256;  // 16-byte pieces of K per thread
+    u32x4 pk[PIECES];
+    float pb;
+    auto fetch = [&](int w) {
+        const bool any = w < total;
+        const int wc = any ? w : 0;
+        const ChunkRef ch = chunk_ref(wc / n_heads, n_seq, n_tok, cu_seqlens, chunk_off);
+        const int64_t tok0 = ch.t0 * H + wc % n_heads;
+        const auto rk = make_rsrc(k + tok0 * DK, any ? ((ch.n - 1) * H * DK + DK) * 2 : 0);
 #pragma unroll
-        for (int p = 0; p < PIECES / 256; ++p) {
+        for (int p = 0; p < PIECES; ++p) {
             const int idx = tid + 256 * p, t = idx / (DK / 8), c = idx % (DK / 8);
-            const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(
-                rk, static_cast<int>(t * H * DK + 8 * c) * 2, 0, 0);
-            *reinterpret_cast<u32x4*>(Kc + t * KP + 8 * c) = val;
+            pk[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, static_cast<int>(t * H * DK + 8 * c) * 2, 0, 0);
         }
-        if (tid < C) {
-            const auto rb = make_rsrc(beta + tok0, ((ch.n - 1) * H + 1) * 4);
-            bs[tid] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(tid * H) * 4, 0, 0));
-        }
+        const auto rb = make_rsrc(beta + tok0, any ? ((ch.n - 1) * H + 1) * 4 : 0);
+        pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, static_cast<int>(lane * H) * 4, 0, 0));
+    };
+
+    fetch(blockIdx.x);
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    // lane-derived values are rebuilt every item from an opaque copy of the lane
+    // id, so the compiler does not hoist dozens of loop-invariant LDS addresses
+    // into registers (which spills)
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int tid = lane_o + 64 * wave, g16 = lane_o >> 4, m16 = lane_o & 15;
+    const int lane = lane_o;
+    const int gc = w / n_heads, h = w % n_heads;
+#pragma unroll
+    for (int p = 0; p < PIECES; ++p) {
+        const int idx = tid + 256 * p, t = idx / (DK / 8), c = idx % (DK / 8);
+        *reinterpret_cast<u32x4*>(Kc + t * KP + 8 * c) = pk[p];
     }
+    if (tid < C) bs[tid] = pb;
     block_sync();
+    fetch(w + gridDim.x);
 
     // ---- L = strictly_lower(diag(beta) K K^T).  Wave 0: the four 16x16 diagonal
     // blocks, then their inverses T_b = (I + L_bb)^{-1} (lane = (block, column)),
@@ -236,16 +257,15 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     float x[16];
     if (wave == 0) {
         f32x4 d[4] = {};
-        bf16x8 kf[4][DK / 32];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            bf16x8 kf[4];
 #pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) kf[b][kk] = frag16(Kc, KP, 16 * b, 32 * kk, lane);
-        issue_fence();
+            for (int b = 0; b < 4; ++b) kf[b] = frag16(Kc, KP, 16 * b, 32 * kk, lane);
+            issue_fence();
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) d[b] = mfma16(kf[b][kk], kf[b][kk], d[b]);
+            for (int b = 0; b < 4; ++b) d[b] = mfma16(kf[b], kf[b], d[b]);
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * b + 4 * g16);
@@ -258,52 +278,56 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
         wave_lds_sync();
         const int b = g16, c = m16;
         const float* Lb = Lf + (16 * b) * LP + 16 * b;
-        // The strictly lower rows are loaded in two batches ahead of the
-        // substitution, so no LDS round trip sits inside its dependent chain.
-        // Piece p enumerates (row r = 1..15, columns s4..s4+3 < r + 3).
+        // Each strictly lower row is loaded one row ahead of its use, so no LDS
+        // round trip sits inside the dependent substitution chain.  Piece p
+        // enumerates (row r = 1..15, columns s4..s4+3 < r + 3).
         f32x4 lrow[36];
-        auto load_rows = [&](int r_lo, int r_hi) {
-#pragma unroll
-            for (int r = 1, p = 0; r < 16; ++r)
-#pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4, ++p)
-                    if (r >= r_lo && r < r_hi) lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+        auto first_piece = [](int r) {
+            int p = 0;
+            for (int rr = 1; rr < r; ++rr) p += (rr + 3) / 4;
+            return p;
         };
-        auto solve_rows = [&](int r_lo, int r_hi) {
+        auto load_row = [&](int r) {
 #pragma unroll
-            for (int r = 1, p = 0; r < 16; ++r) {
-                float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
+            for (int s4 = 0, p = first_piece(r); s4 < r; s4 += 4, ++p)
+                lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+        };
+        auto solve_row = [&](int r) {
+            float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int s4 = 0; s4 < r; s4 += 4, ++p) {
+            for (int s4 = 0, p = first_piece(r); s4 < r; s4 += 4, ++p) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (r >= r_lo && r < r_hi && s4 + e < r) {
-                            if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
-                            else acc0 -= lrow[p][e] * x[s4 + e];
-                        }
+                for (int e = 0; e < 4; ++e) {
+                    if (s4 + e < r) {
+                        if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
+                        else acc0 -= lrow[p][e] * x[s4 + e];
                     }
                 }
-                if (r >= r_lo && r < r_hi) x[r] = acc0 + acc1;  // zero for r < c
             }
+            x[r] = acc0 + acc1;  // zero for r < c
         };
         x[0] = c == 0 ? 1.f : 0.f;
-        load_rows(1, 10);
-        issue_fence();
-        solve_rows(1, 6);
-        load_rows(10, 16);
-        issue_fence();
-        solve_rows(6, 16);
+        load_row(1);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            if (r + 1 < 16) load_row(r + 1);
+            issue_fence();
+            solve_row(r);
+        }
     } else if (wave == 1) {
         f32x16 acc = {};
-        bf16x8 fa[DK / 16], fb[DK / 16];
 #pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) {
-            fa[kk] = frag(Kc, KP, 32, 16 * kk, lane);
-            fb[kk] = frag(Kc, KP, 0, 16 * kk, lane);
+        for (int half = 0; half < DK / 64; ++half) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                fa[kk] = frag(Kc, KP, 32, 64 * half + 16 * kk, lane);
+                fb[kk] = frag(Kc, KP, 0, 64 * half + 16 * kk, lane);
+            }
+            issue_fence();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma(fa[kk], fb[kk], acc);
         }
-        issue_fence();
-#pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(fa[kk], fb[kk], acc);
         f32x4 b4[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (lane >> 5));
@@ -423,6 +447,8 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
         uint16_t* dst = rec + blk * 2 * A_BLOCK_ELEMS + row * 32 + c8;
         *reinterpret_cast<u32x4*>(dst) = wh;
         *reinterpret_cast<u32x4*>(dst + A_BLOCK_ELEMS) = wl;
+    }
+    block_sync();  // X, read above, shares its space with the next item's K
     }
 }
 
@@ -949,8 +975,12 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
     if (a.n_tok > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(mc * a.n_heads)), dim3(256), 0,
-                           stream, static_cast<const uint16_t*>(a.k), a.beta, a.cu_seqlens, chunk_off, a.n_seq,
+        // as many workgroups as stay resident (four per CU); each loops over items
+        int dev = 0, n_cu = 0;
+        if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        const int64_t grid = std::min<int64_t>(mc * a.n_heads, 4 * static_cast<int64_t>(n_cu));
+        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, static_cast<const uint16_t*>(a.k), a.beta, a.cu_seqlens, chunk_off, a.n_seq,
                            a.n_tok, a.n_heads, static_cast<int>(mc), arec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
