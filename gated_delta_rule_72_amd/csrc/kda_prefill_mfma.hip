@@ -497,7 +497,7 @@ struct ScanSmem {
     static constexpr int RO = C * OP * 2;       // O [t][i], staged for the store
     static constexpr int RG = C * GP * 4;       // G [t][i] (log2 units)
     static constexpr int RB = BV * 4;           // gamma = 2^{G[C-1, :]}
-    static constexpr int RT = 2 * 8 * BV * 4;   // per-wave totals of log2 alpha, two chunks
+    static constexpr int RT = 2 * 4 * BV * 4;   // loader-wave totals of log2 alpha, two chunks
     static constexpr int TOTAL = RK + RQ + RS + RA + RP + RU + RV + RO + RG + RB + RT;
 };
 
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     uint16_t* Os = reinterpret_cast<uint16_t*>(ro_);
     float* Gs = reinterpret_cast<float*>(rg_);
     float* gam = reinterpret_cast<float*>(rb_);
-    float* Tot = reinterpret_cast<float*>(rt_);  // [2][8][BV]
+    float* Tot = reinterpret_cast<float*>(rt_);  // [2][4][BV]
 
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
@@ -571,105 +571,119 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int lane = tid & 63;
     // the wave index is uniform: keep it (and every tile offset derived from it) scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool chain = wave < 4;
-    const int blk = wave & 3;  // value rows 16 blk .. 16 blk + 15 of this workgroup's block
+    const bool chain = wave < 2;                 // chain waves 0, 1
+    const bool outw = wave == 2 || wave == 3;    // out waves 2, 3
+    const int rb = 32 * (wave & 1);  // first of the 32 value rows of a chain or out wave
     const int64_t H = n_heads;
     const int h = u.head;
     const int i0 = u.vblk * BV;
     const int64_t row_qk = H * DK, row_v = H * DV;  // element strides between tokens
     const int chunk0 = chunk_off[u.seq];
 
-    // ---- state of the chain waves: Sacc[jt] = S^T rows 16 jt .. 16 jt + 15 (key
-    // channels), columns = this wave's 16 value rows
+    // ---- state of the chain waves: R[(ib) * NJ + (jt)] = S^T rows 16 jt .. 16 jt + 15 (key
+    // channels), columns = value rows rb + 16 ib .. +15
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
-    f32x4 Sacc[NJ];
+    // One register array holds each role's long-lived values, so the register
+    // allocator (which cannot know that a wave keeps one role) does not keep every
+    // role's set live at once: chain waves keep S^T at [NJ ib + jt] and the U^T
+    // packs at CARRY0 + ..; out waves the O^T accumulators at CARRY0 + ..; loader
+    // waves the loaded pieces of K, Q, V, the A record and alpha.
+    constexpr int CARRY0 = 2 * NJ;
+    constexpr int NKQ = C * PPR / 256;   // 16-byte pieces of K (and of Q) per loader thread
+    constexpr int NV = C * (BV / 8) / 256;
+    constexpr int NA = A_RECORD_PIECES / 256;
+    constexpr int PK0 = 0, PQ0 = NKQ, PV0 = 2 * NKQ, PA0 = 2 * NKQ + NV, PL0 = 2 * NKQ + NV + NA;
+    constexpr int RN = (CARRY0 + 8 > PL0 + 4) ? CARRY0 + 8 : PL0 + 4;
+    f32x4 R[RN];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) Sacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < RN; ++x) R[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (chain && S0) {
-        const float* src = S0 + s_base + static_cast<int64_t>(16 * blk + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) Sacc[jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
+        for (int ib = 0; ib < 2; ++ib) {
+            const float* src =
+                S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) R[(ib) * NJ + (jt)] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
+        }
     }
-    // negated bf16 copy of S as the B operands of K (-S)^T, one per 32-wide j step
-    bf16x8 Sb[NM];
+    // negated bf16 copy of S as the B operand of K (-S)^T for the 32-wide j step m
+    auto neg_state = [&](int ib, int m) {
+        u32x4 w;
+        w[0] = pack_bf16(-R[(ib) * NJ + (2 * m)][0], -R[(ib) * NJ + (2 * m)][1]);
+        w[1] = pack_bf16(-R[(ib) * NJ + (2 * m)][2], -R[(ib) * NJ + (2 * m)][3]);
+        w[2] = pack_bf16(-R[(ib) * NJ + (2 * m + 1)][0], -R[(ib) * NJ + (2 * m + 1)][1]);
+        w[3] = pack_bf16(-R[(ib) * NJ + (2 * m + 1)][2], -R[(ib) * NJ + (2 * m + 1)][3]);
+        return __builtin_bit_cast(bf16x8, w);
+    };
     auto pack_state = [&](int ln) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            u32x4 w;
-            w[0] = pack_bf16(-Sacc[2 * m][0], -Sacc[2 * m][1]);
-            w[1] = pack_bf16(-Sacc[2 * m][2], -Sacc[2 * m][3]);
-            w[2] = pack_bf16(-Sacc[2 * m + 1][0], -Sacc[2 * m + 1][1]);
-            w[3] = pack_bf16(-Sacc[2 * m + 1][2], -Sacc[2 * m + 1][3]);
-            Sb[m] = __builtin_bit_cast(bf16x8, w);
-        }
-        // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
-        uint16_t* dst = Sx + (16 * blk + (ln & 15)) * QP + 4 * (ln >> 4);
+        for (int ib = 0; ib < 2; ++ib) {
+            // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
+            uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * QP + 4 * (ln >> 4);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-            uint2 w;
-            w.x = pack_bf16(Sacc[jt][0], Sacc[jt][1]);
-            w.y = pack_bf16(Sacc[jt][2], Sacc[jt][3]);
-            *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            for (int jt = 0; jt < NJ; ++jt) {
+                uint2 w;
+                w.x = pack_bf16(R[(ib) * NJ + (jt)][0], R[(ib) * NJ + (jt)][1]);
+                w.y = pack_bf16(R[(ib) * NJ + (jt)][2], R[(ib) * NJ + (jt)][3]);
+                *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            }
         }
     };
 
-    // ---- register prefetch of the next chunk's inputs; every load reads whole rows.
-    // K, Q: 16-byte piece tid (and tid + 512) of the row-major chunk.
-    // V: row tid/8, 8 values at 8*(tid%8).
-    // alpha: wave w holds token rows 8w..8w+7, lane = value row (one 256-byte
-    //   token row per load).
-    // A record: pieces tid and tid + 512.
+    // ---- loads of the next chunk's inputs by the loader waves (4-7), issued while
+    // the chain and out waves compute; every load reads whole rows.  Loader
+    // thread ht = tid - 256 holds 16-byte pieces ht + 256 p of K, Q (row-major),
+    // V and the A record; alpha: loader wave w holds token rows 16 (w - 4) ..
+    // +15, lane = value row (one 256-byte token row per load).
     // The loads (and the O store below) are issued unconditionally: a chunk past
     // the end gets an empty buffer range, so nothing is accessed.  Uniform control
     // flow lets the compiler count outstanding memory operations exactly.
-    struct Pf {
-        u32x4 k0, k1, q0, q1, v, A0, A1;
-        float a[8];
-    };
-    Pf pf = {};
+    const bool loader = wave >= 4;
     auto prefetch = [&](int64_t tc, int n, int gc) {
+        const int ht = tid - 256;
         const int64_t tok0 = tc * H + h;  // (token tc, head h) row index
         const bool any = n > 0;
-        {
-            const int64_t bytes = any ? ((n - 1) * row_qk + DK) * 2 : 0;
-            const auto rk = make_rsrc(k + tok0 * DK, bytes);
-            const auto rq = make_rsrc(q + tok0 * DK, bytes);
-            const int off0 = static_cast<int>((tid / PPR) * row_qk + 8 * (tid % PPR)) * 2;
-            const int off1 = off0 + static_cast<int>(32 * row_qk) * 2;
-            pf.k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, off0, 0, 0);
-            pf.q0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
-            if constexpr (DK == 128) {
-                pf.k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, off1, 0, 0);
-                pf.q1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off1, 0, 0);
-            }
-        }
-        {
-            const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
-            pf.v = __builtin_amdgcn_raw_buffer_load_b128(rv, static_cast<int>((tid >> 3) * row_v + 8 * (tid & 7)) * 2,
-                                                         0, 0);
-            const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
+        const int64_t bytes = any ? ((n - 1) * row_qk + DK) * 2 : 0;
+        const auto rk = make_rsrc(k + tok0 * DK, bytes);
+        const auto rq = make_rsrc(q + tok0 * DK, bytes);
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                pf.a[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                        ra, static_cast<int>((8 * wave + r) * row_v + lane) * 4, 0, 0));
+        for (int p = 0; p < NKQ; ++p) {
+            const int idx = ht + 256 * p;
+            const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
+            R[PK0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
         }
-        {
-            const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
-            const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
-            pf.A0 = __builtin_amdgcn_raw_buffer_load_b128(rr, tid * 16, 0, 0);
-            pf.A1 = __builtin_amdgcn_raw_buffer_load_b128(rr, (tid + 512) * 16, 0, 0);  // past the end for tid >= 256
+        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = ht + 256 * p;
+            R[PV0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                rv, static_cast<int>((idx / (BV / 8)) * row_v + 8 * (idx % (BV / 8))) * 2, 0, 0));
         }
+        const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
+        const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
+#pragma unroll
+        for (int p = 0; p < NA; ++p)
+            R[PA0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (ht + 256 * p) * 16, 0, 0));
+        const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            R[PL0 + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                ra, static_cast<int>((16 * (wave - 4) + r) * row_v + lane) * 4, 0, 0));
     };
 
     auto chunk_len = [&](int64_t tc) { return static_cast<int>(max<int64_t>(0, min<int64_t>(C, u.t1 - tc))); };
 
-    // staged O rows of a finished chunk -> global, one 16-byte store per thread
-    // (n = 0: nothing is stored)
-    auto store_o = [&](int64_t tc, int n, int td) {
-        const int t = td >> 3, c = td & 7;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(Os + t * OP + 8 * c);
+    // staged O rows of a finished chunk -> global by the out waves (2, 3), four
+    // 16-byte pieces per thread (n = 0: nothing is stored)
+    auto store_o = [&](int64_t tc, int n, int ln) {
         const auto ro = make_rsrc(o + (tc * H + h) * DV + i0, n > 0 ? ((n - 1) * row_v + BV) * 2 : 0);
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int idx = ln + 64 * (wave - 2) + 128 * p, t = idx >> 3, c = idx & 7;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(Os + t * OP + 8 * c);
+            __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
+        }
     };
 
     // one 16-byte piece of an A record -> A hi/lo [t][s]
@@ -684,35 +698,55 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // is taken to be a normal fp32 number in (0, 1].
     // The log-decay cumsum G of a chunk is formed in two steps one phase apart,
     // so the prefix across waves never needs a barrier of its own:
-    // local_scan -- each wave's inclusive prefix over its 8 token rows (in
+    // local_scan -- each loader wave's inclusive prefix over its 16 token rows (in
     //   registers: a lane holds one value row), kept in the alpha registers; the
-    //   wave's totals go to Tot[parity][wave];
-    // finalize   -- after a barrier, add the totals of the waves before (the
-    //   rows before this wave's) and write G [t][i] and gamma.
+    //   wave's totals go to Tot[parity][wave - 4];
+    // finalize   -- after a barrier, add the totals of the loader waves before
+    //   (the rows before this wave's) and write G [t][i]; wave 7 writes gamma.
     // Rows past the sequence end contribute log alpha = 0.
     auto local_scan = [&](int n, int par, int ln) {
         float run = 0.f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            run += 8 * wave + r < n ? __builtin_amdgcn_logf(pf.a[r]) : 0.f;
-            pf.a[r] = run;
+        for (int r = 0; r < 16; ++r) {
+            run += 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
+            R[PL0 + r / 4][r % 4] = run;
         }
-        Tot[(par * 8 + wave) * BV + ln] = run;
+        Tot[(par * 4 + wave - 4) * BV + ln] = run;
     };
     auto finalize = [&](int par, int ln) {
         float carry = 0.f;
 #pragma unroll
-        for (int b = 0; b < 7; ++b) {
-            const float tb = Tot[(par * 8 + b) * BV + ln];
-            carry += b < wave ? tb : 0.f;
+        for (int b = 0; b < 3; ++b) {
+            const float tb = Tot[(par * 4 + b) * BV + ln];
+            carry += b < wave - 4 ? tb : 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) Gs[(8 * wave + r) * GP + ln] = pf.a[r] + carry;
-        if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(pf.a[7] + carry);
+        for (int r = 0; r < 16; ++r) Gs[(16 * (wave - 4) + r) * GP + ln] = R[PL0 + r / 4][r % 4] + carry;
+        if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(R[PL0 + 3][3] + carry);
+    };
+    // loaded pieces -> LDS
+    auto stage = [&](int ln) {
+        const int ht = ln + 64 * (wave - 4);
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int idx = ht + 256 * p;
+            *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PK0 + p]);
+            *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
+        }
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = ht + 256 * p;
+            *reinterpret_cast<u32x4*>(Vr + (idx / (BV / 8)) * OP + 8 * (idx % (BV / 8))) =
+                __builtin_bit_cast(u32x4, R[PV0 + p]);
+        }
+#pragma unroll
+        for (int p = 0; p < NA; ++p) stage_a(__builtin_bit_cast(u32x4, R[PA0 + p]), ht + 256 * p);
     };
 
-    prefetch(u.t0, chunk_len(u.t0), chunk0);
-    local_scan(chunk_len(u.t0), 0, lane);
+    if (loader) {
+        prefetch(u.t0, chunk_len(u.t0), chunk0);
+        local_scan(chunk_len(u.t0), 0, lane);
+    }
     if (chain) pack_state(lane);
 
     int64_t prev_tc = u.t0;
@@ -728,40 +762,36 @@ __global__ __launch_bounds__(512) void scan_kernel(
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o;
-        const int td = ln + 64 * wave;
         const int g = ln >> 4, m16 = ln & 15;
         block_sync();  // the previous chunk is done with every buffer
 
-        // ======== stage this chunk and finish its G, store the previous chunk's
-        // O, issue the next chunk's loads
-        *reinterpret_cast<u32x4*>(Kc + (td / PPR) * KP + 8 * (td % PPR)) = pf.k0;
-        *reinterpret_cast<u32x4*>(Qc + (td / PPR) * QP + 8 * (td % PPR)) = pf.q0;
-        if constexpr (DK == 128) {
-            *reinterpret_cast<u32x4*>(Kc + (32 + td / PPR) * KP + 8 * (td % PPR)) = pf.k1;
-            *reinterpret_cast<u32x4*>(Qc + (32 + td / PPR) * QP + 8 * (td % PPR)) = pf.q1;
+        // ======== the loaders stage this chunk and finish its G; the out waves
+        // store the previous chunk's O
+        if (loader) {
+            stage(ln);
+            finalize(c & 1, ln);
+        } else if (outw) {
+            store_o(prev_tc, prev_n, ln);
         }
-        *reinterpret_cast<u32x4*>(Vr + (td >> 3) * OP + 8 * (td & 7)) = pf.v;
-        stage_a(pf.A0, td);
-        if (td < A_RECORD_PIECES - 512) stage_a(pf.A1, td + 512);
-        finalize(c & 1, ln);
-        store_o(prev_tc, prev_n, td);
-        prefetch(tc + C, chunk_len(tc + C), gc + 1);
         block_sync();
 
-        f32x4 Oacc[4];
-        bf16x8 Uh[2], Ul[2];
+        // carried across the middle barrier in one register array: the U^T packs of
+        // a chain wave (hi at 2 ib + m, lo at 4 + 2 ib + m) or the O^T accumulators of
+        // an out wave (4 ib + tt)
         if (chain) {
-            // ======== Y = X - K S^T, then U = A Y, for value rows i = 16 blk + m16
-            // (lane column); rows t = 16 tt + 4g + r of tile tt
-            f32x4 Y[4];
-            {
-                const int i = 16 * blk + m16;
+            // ======== Y = X - K S^T, then U = A Y, for value rows i = rb + 16 ib + m16
+            // (lane column); rows t = 16 tt + 4g + r of tile tt.  Every K and A
+            // fragment serves both 16-row blocks ib.
+            f32x4 Y[2][4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int i = rb + 16 * ib + m16;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 16 * tt + 4 * g + r;
-                        Y[tt][r] = bf16_bits_to_f32(Vr[t * OP + i]) * __builtin_amdgcn_exp2f(-Gs[t * GP + i]);
+                        Y[ib][tt][r] = bf16_bits_to_f32(Vr[t * OP + i]) * __builtin_amdgcn_exp2f(-Gs[t * GP + i]);
                     }
             }
 #pragma unroll
@@ -771,15 +801,20 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 for (int tt = 0; tt < 4; ++tt) kf[tt] = frag_st(Kc, KP, 16 * tt, 32 * m, ln);
                 issue_fence();
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) Y[tt] = mfma16(kf[tt], Sb[m], Y[tt]);
-            }
-            bf16x8 Yh[2], Yl[2];
-            split_stack(Y[0], Y[1], Yh[0], Yl[0]);
-            split_stack(Y[2], Y[3], Yh[1], Yl[1]);
-            // A is lower triangular: t-tiles 0, 1 need s < 32 only
-            f32x4 U[4];
+                for (int ib = 0; ib < 2; ++ib) {
+                    const bf16x8 sb = neg_state(ib, m);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) U[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int tt = 0; tt < 4; ++tt) Y[ib][tt] = mfma16(kf[tt], sb, Y[ib][tt]);
+                }
+            }
+            bf16x8 Yh[2][2], Yl[2][2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                split_stack(Y[ib][0], Y[ib][1], Yh[ib][0], Yl[ib][0]);
+                split_stack(Y[ib][2], Y[ib][3], Yh[ib][1], Yl[ib][1]);
+            }
+            // A is lower triangular: t-tiles 0, 1 need s < 32 only
+            f32x4 U[2][4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const bf16x8 ah0 = frag_st(A_hi, CP, 16 * tt, 0, ln), al0 = frag_st(A_lo, CP, 16 * tt, 0, ln);
@@ -789,36 +824,72 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     al1 = frag_st(A_lo, CP, 16 * tt, 32, ln);
                 }
                 issue_fence();
-                U[tt] = mfma16(ah0, Yh[0], U[tt]);
-                U[tt] = mfma16(al0, Yh[0], U[tt]);
-                U[tt] = mfma16(ah0, Yl[0], U[tt]);
-                if (tt >= 2) {
-                    U[tt] = mfma16(ah1, Yh[1], U[tt]);
-                    U[tt] = mfma16(al1, Yh[1], U[tt]);
-                    U[tt] = mfma16(ah1, Yl[1], U[tt]);
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    f32x4 acc = mfma16(ah0, Yh[ib][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                    acc = mfma16(al0, Yh[ib][0], acc);
+                    acc = mfma16(ah0, Yl[ib][0], acc);
+                    if (tt >= 2) {
+                        acc = mfma16(ah1, Yh[ib][1], acc);
+                        acc = mfma16(al1, Yh[ib][1], acc);
+                        acc = mfma16(ah1, Yl[ib][1], acc);
+                    }
+                    U[ib][tt] = acc;
                 }
             }
-            split_stack(U[0], U[1], Uh[0], Ul[0]);
-            split_stack(U[2], U[3], Uh[1], Ul[1]);
             // U^T hi/lo [i][t] for the out waves: the stacked packs hold t = 32 m +
             // 4g .. +3 (words 0, 1) and 32 m + 16 + 4g .. +3 (words 2, 3)
-            {
-                const int i = 16 * blk + m16;
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const int i = rb + 16 * ib + m16;
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    const u32x4 wh = __builtin_bit_cast(u32x4, Uh[m]), wl = __builtin_bit_cast(u32x4, Ul[m]);
+                    bf16x8 uh, ul;
+                    split_stack(U[ib][2 * m], U[ib][2 * m + 1], uh, ul);
+                    R[CARRY0 + 2 * ib + m] = __builtin_bit_cast(f32x4, uh);
+                    R[CARRY0 + 4 + 2 * ib + m] = __builtin_bit_cast(f32x4, ul);
+                    const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 4 * g) = uint2{wh[0], wh[1]};
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 16 + 4 * g) = uint2{wh[2], wh[3]};
                     *reinterpret_cast<uint2*>(Ux_lo + i * CP + 32 * m + 4 * g) = uint2{wl[0], wl[1]};
                     *reinterpret_cast<uint2*>(Ux_lo + i * CP + 32 * m + 16 + 4 * g) = uint2{wl[2], wl[3]};
                 }
             }
+        } else if (outw) {
+            // ======== O^T = S Q^T for value rows rb + 16 ib + 4g + r (tile rows) and
+            // tokens t = 16 tt + m16 (tile column); every Q fragment serves both blocks
+            f32x4 Oacc[2][4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Oacc[ib][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                bf16x8 sf[2], qf[4];
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) sf[ib] = frag16(Sx, QP, rb + 16 * ib, 32 * m, ln);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) qf[tt] = frag16(Qc, QP, 16 * tt, 32 * m, ln);
+                issue_fence();
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) Oacc[ib][tt] = mfma16(sf[ib], qf[tt], Oacc[ib][tt]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) R[CARRY0 + 4 * ib + tt] = Oacc[ib][tt];
         } else {
-            // ======== waves 4-6: P = tril(Q K^T) hi/lo [t][s], formed transposed
-            // (32x32 tile D[s][t], so each lane holds 4 consecutive s of one t);
-            // P^T tiles (s-tile, t-tile) = (0,0), (0,1), (1,1), and (1,0) is all zero
-            if (wave < 7) {
-                const int sb = wave == 6 ? 1 : 0, tb = wave == 4 ? 0 : 1;
+            if (wave >= 6) {
+            // ======== P = tril(Q K^T) hi/lo [t][s], formed transposed (32x32 tile
+            // D[s][t], so each lane holds 4 consecutive s of one t).  P^T tiles
+            // (s-tile, t-tile): wave 6 takes (0,0) and (1,1), wave 7 (0,1); (1,0) is
+            // all zero.
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                if (wave == 7 && pt == 1) break;
+                const int sb = (wave == 6 && pt == 1) ? 1 : 0, tb = wave == 7 ? 1 : sb;
                 f32x16 acc = {};
 #pragma unroll
                 for (int half = 0; half < DK / 64; ++half) {
@@ -834,11 +905,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 }
                 const int t = 32 * tb + (ln & 31);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int s0 = 32 * sb + 8 * rb + 4 * (ln >> 5);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int s0 = 32 * sb + 8 * q4 + 4 * (ln >> 5);
                     float pv4[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pv4[e] = s0 + e <= t ? acc[4 * rb + e] : 0.f;
+                    for (int e = 0; e < 4; ++e) pv4[e] = s0 + e <= t ? acc[4 * q4 + e] : 0.f;
                     uint2 wh, wl;
                     split_bf16x2(pv4[0], pv4[1], wh.x, wl.x);
                     split_bf16x2(pv4[2], pv4[3], wh.y, wl.y);
@@ -846,20 +917,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     *reinterpret_cast<uint2*>(P_lo + t * CP + s0) = wl;
                 }
             }
-            // O^T = S Q^T for value rows 16 blk + 4g + r (tile rows) and tokens
-            // t = 16 tt + m16 (tile column)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) Oacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const bf16x8 sf = frag16(Sx, QP, 16 * blk, 32 * m, ln);
-                bf16x8 qf[4];
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) qf[tt] = frag16(Qc, QP, 16 * tt, 32 * m, ln);
-                issue_fence();
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) Oacc[tt] = mfma16(sf, qf[tt], Oacc[tt]);
             }
+            // ======== the loaders (4, 5 at once, 6, 7 after P) issue the next
+            // chunk's loads, off the chain waves' path
+            prefetch(tc + C, chunk_len(tc + C), gc + 1);
         }
         block_sync();
 
@@ -870,34 +931,48 @@ __global__ __launch_bounds__(512) void scan_kernel(
             // (+16 for the second half) at key channels 16 jt + 4 (m16 % 4) .. +3
             const uint16_t* ktb = Kc + (4 * g + (m16 >> 2)) * KP + 4 * (m16 & 3);
 #pragma unroll
-            for (int jt = 0; jt < NJ; jt += 2) {
-                bf16x8 kt[2][2];
+            for (int jt = 0; jt < NJ; ++jt) {
+                bf16x8 kt[2];
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const s16x4 t0 = lds_read_tr16(ktb + (32 * m) * KP + 16 * (jt + a));
-                        const s16x4 t1 = lds_read_tr16(ktb + (32 * m + 16) * KP + 16 * (jt + a));
-                        kt[a][m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
+                for (int m = 0; m < 2; ++m) {
+                    const s16x4 t0 = lds_read_tr16(ktb + (32 * m) * KP + 16 * jt);
+                    const s16x4 t1 = lds_read_tr16(ktb + (32 * m + 16) * KP + 16 * jt);
+                    kt[m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
                 issue_fence();
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        Sacc[jt + a] = mfma16(kt[a][m], Uh[m], Sacc[jt + a]);
-                        Sacc[jt + a] = mfma16(kt[a][m], Ul[m], Sacc[jt + a]);
+                    for (int ib = 0; ib < 2; ++ib) {
+                        const bf16x8 uh = __builtin_bit_cast(bf16x8, R[CARRY0 + 2 * ib + m]);
+                        const bf16x8 ul = __builtin_bit_cast(bf16x8, R[CARRY0 + 4 + 2 * ib + m]);
+                        R[(ib) * NJ + (jt)] = mfma16(kt[m], uh, R[(ib) * NJ + (jt)]);
+                        R[(ib) * NJ + (jt)] = mfma16(kt[m], ul, R[(ib) * NJ + (jt)]);
                     }
             }
-            const float gm = gam[16 * blk + m16];
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) Sacc[jt] *= gm;
+            for (int ib = 0; ib < 2; ++ib) {
+                const float gm = gam[rb + 16 * ib + m16];
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt) R[(ib) * NJ + (jt)] *= gm;
+            }
             pack_state(ln);
-        } else {
+        } else if (outw) {
             // ======== O^T += U^T P^T (P is lower triangular: t-tiles 0, 1 need s < 32),
             // then O = 2^{G} O, staged as bf16 [t][i]
-            const bf16x8 uh0 = frag16(Ux_hi, CP, 16 * blk, 0, ln), ul0 = frag16(Ux_lo, CP, 16 * blk, 0, ln);
-            const bf16x8 uh1 = frag16(Ux_hi, CP, 16 * blk, 32, ln), ul1 = frag16(Ux_lo, CP, 16 * blk, 32, ln);
+            f32x4 Oacc[2][4];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Oacc[ib][tt] = R[CARRY0 + 4 * ib + tt];
+            bf16x8 uh[2][2], ul[2][2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    uh[ib][m] = frag16(Ux_hi, CP, rb + 16 * ib, 32 * m, ln);
+                    ul[ib][m] = frag16(Ux_lo, CP, rb + 16 * ib, 32 * m, ln);
+                }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const bf16x8 ph0 = frag16(P_hi, CP, 16 * tt, 0, ln), pl0 = frag16(P_lo, CP, 16 * tt, 0, ln);
@@ -907,38 +982,48 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     pl1 = frag16(P_lo, CP, 16 * tt, 32, ln);
                 }
                 issue_fence();
-                Oacc[tt] = mfma16(uh0, ph0, Oacc[tt]);
-                Oacc[tt] = mfma16(ul0, ph0, Oacc[tt]);
-                Oacc[tt] = mfma16(uh0, pl0, Oacc[tt]);
-                if (tt >= 2) {
-                    Oacc[tt] = mfma16(uh1, ph1, Oacc[tt]);
-                    Oacc[tt] = mfma16(ul1, ph1, Oacc[tt]);
-                    Oacc[tt] = mfma16(uh1, pl1, Oacc[tt]);
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    Oacc[ib][tt] = mfma16(uh[ib][0], ph0, Oacc[ib][tt]);
+                    Oacc[ib][tt] = mfma16(ul[ib][0], ph0, Oacc[ib][tt]);
+                    Oacc[ib][tt] = mfma16(uh[ib][0], pl0, Oacc[ib][tt]);
+                    if (tt >= 2) {
+                        Oacc[ib][tt] = mfma16(uh[ib][1], ph1, Oacc[ib][tt]);
+                        Oacc[ib][tt] = mfma16(ul[ib][1], ph1, Oacc[ib][tt]);
+                        Oacc[ib][tt] = mfma16(uh[ib][1], pl1, Oacc[ib][tt]);
+                    }
                 }
             }
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int t = 16 * tt + m16, i = 16 * blk + 4 * g;
-                const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gs + t * GP + i);
-                uint2 w;
-                w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[0]) * Oacc[tt][0], __builtin_amdgcn_exp2f(g4[1]) * Oacc[tt][1]);
-                w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[2]) * Oacc[tt][2], __builtin_amdgcn_exp2f(g4[3]) * Oacc[tt][3]);
-                *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
-            }
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int t = 16 * tt + m16, i = rb + 16 * ib + 4 * g;
+                    const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gs + t * GP + i);
+                    uint2 w;
+                    w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[0]) * Oacc[ib][tt][0],
+                                    __builtin_amdgcn_exp2f(g4[1]) * Oacc[ib][tt][1]);
+                    w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[2]) * Oacc[ib][tt][2],
+                                    __builtin_amdgcn_exp2f(g4[3]) * Oacc[ib][tt][3]);
+                    *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
+                }
         }
-        local_scan(chunk_len(tc + C), (c + 1) & 1, ln);
+        if (loader) local_scan(chunk_len(tc + C), (c + 1) & 1, ln);
         prev_tc = tc;
         prev_n = n;
     }
     if (prev_n > 0) {
         block_sync();
-        store_o(prev_tc, prev_n, tid);
+        if (outw) store_o(prev_tc, prev_n, lane);
     }
 
     if (S_T && chain) {
-        float* dst = S_T + s_base + static_cast<int64_t>(16 * blk + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = Sacc[jt];
+        for (int ib = 0; ib < 2; ++ib) {
+            float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[(ib) * NJ + (jt)];
+        }
     }
 }
 
