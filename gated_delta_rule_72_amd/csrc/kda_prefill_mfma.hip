@@ -453,13 +453,13 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
 }
 
 // ============================================================================
-// scan_kernel: the S-dependent chunk products, one workgroup of 8 waves per
-// (sequence, head, block of 64 value rows).
+// scan_kernel: the S-dependent chunk products, one workgroup of 8 waves (two per
+// SIMD) per (sequence, head, block of 64 value rows).
 //
-// Waves 0-3, the chain waves, each own 16 value rows i of the state -- S^T[j][i]
+// Waves 0, 1, the chain waves, each own 32 value rows i of the state -- S^T[j][i]
 // for every key channel j, as fp32 MFMA accumulators in 16x16 tiles -- and run
 // the chunk's S-dependent chain for those rows in registers:
-//   Y = X - K S^T            (X = V 2^{-G})
+//   Y = X - K S^T            (X = V 2^{-G}, formed by the loader waves)
 //   U = A Y
 //   S^T <- diag(gamma) (S^T + K^T U)
 // A 16x16 accumulator tile holds, in lane (column n = l % 16, group g = l / 16),
@@ -468,9 +468,10 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
 // v_mfma_f32_16x16x32_bf16 B operand (the A operand reads the same indices,
 // two 8-byte pieces per lane), Y, U and S feed the next product straight from
 // the accumulators.
-// Waves 4-7, the out waves, form P = tril(Q K^T) (waves 4-6) and the outputs
-// O^T = 2^{G} (S Q^T + U^T P^T) of the same 16-row blocks, from the copies of S
-// and U that the chain waves leave in LDS.
+// Waves 2, 3, the out waves, form the outputs O^T = 2^{G} (S Q^T + U^T P^T) of
+// the same 32-row blocks from the bf16 copies of S and U that the chain waves
+// leave in LDS.  Waves 4-7, the loader waves, load each chunk one chunk ahead,
+// stage it and form G and X; waves 6, 7 also form P = tril(Q K^T).
 // Three barriers per chunk: staging | Y, U; P, S Q^T | S update; U^T P^T.
 // ============================================================================
 template <int DK>
@@ -493,12 +494,13 @@ struct ScanSmem {
     static constexpr int RA = HILO;             // A hi/lo [t][s]
     static constexpr int RP = HILO;             // P hi/lo [t][s]
     static constexpr int RU = 2 * BV * CP * 2;  // U^T hi/lo [i][t]
-    static constexpr int RV = C * OP * 2;       // V [t][i]
+    static constexpr int XP = C + 8;            // pitch of X^T rows (fp32)
+    static constexpr int RX = BV * XP * 4;      // X^T [i][t] = V 2^{-G}, transposed
     static constexpr int RO = C * OP * 2;       // O [t][i], staged for the store
     static constexpr int RG = C * GP * 4;       // G [t][i] (log2 units)
     static constexpr int RB = BV * 4;           // gamma = 2^{G[C-1, :]}
     static constexpr int RT = 2 * 4 * BV * 4;   // loader-wave totals of log2 alpha, two chunks
-    static constexpr int TOTAL = RK + RQ + RS + RA + RP + RU + RV + RO + RG + RB + RT;
+    static constexpr int TOTAL = RK + RQ + RS + RA + RP + RU + RX + RO + RG + RB + RT;
 };
 
 // 16x16x32 operand whose 8 reduction values per lane are the stacked-tile
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, QP = SM::QP, GP = SM::GP, OP = SM::OP;
+    constexpr int KP = SM::KP, QP = SM::QP, GP = SM::GP, OP = SM::OP, XP = SM::XP;
     constexpr int NJ = DK / 16;   // 16-row tiles of S^T along j
     constexpr int NM = DK / 32;   // 32-wide reduction steps over j
     constexpr int PPR = DK / 8;   // 16-byte pieces per row of q or k
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __align__(16) unsigned char ra_[SM::RA];
     __shared__ __align__(16) unsigned char rp_[SM::RP];
     __shared__ __align__(16) unsigned char ru_[SM::RU];
-    __shared__ __align__(16) unsigned char rv_[SM::RV];
+    __shared__ __align__(16) unsigned char rx_[SM::RX];
     __shared__ __align__(16) unsigned char ro_[SM::RO];
     __shared__ __align__(16) unsigned char rg_[SM::RG];
     __shared__ __align__(16) unsigned char rb_[SM::RB];
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     uint16_t* P_lo = P_hi + C * CP;
     uint16_t* Ux_hi = reinterpret_cast<uint16_t*>(ru_);
     uint16_t* Ux_lo = Ux_hi + BV * CP;
-    uint16_t* Vr = reinterpret_cast<uint16_t*>(rv_);
+    float* XT = reinterpret_cast<float*>(rx_);
     uint16_t* Os = reinterpret_cast<uint16_t*>(ro_);
     float* Gs = reinterpret_cast<float*>(rg_);
     float* gam = reinterpret_cast<float*>(rb_);
@@ -590,9 +592,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // waves the loaded pieces of K, Q, V, the A record and alpha.
     constexpr int CARRY0 = 2 * NJ;
     constexpr int NKQ = C * PPR / 256;   // 16-byte pieces of K (and of Q) per loader thread
-    constexpr int NV = C * (BV / 8) / 256;
     constexpr int NA = A_RECORD_PIECES / 256;
-    constexpr int PK0 = 0, PQ0 = NKQ, PV0 = 2 * NKQ, PA0 = 2 * NKQ + NV, PL0 = 2 * NKQ + NV + NA;
+    constexpr int PK0 = 0, PQ0 = NKQ, PV0 = 2 * NKQ, PA0 = PV0 + 4, PL0 = PA0 + NA;
     constexpr int RN = (CARRY0 + 8 > PL0 + 4) ? CARRY0 + 8 : PL0 + 4;
     f32x4 R[RN];
 #pragma unroll
@@ -632,9 +633,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     // ---- loads of the next chunk's inputs by the loader waves (4-7), issued while
     // the chain and out waves compute; every load reads whole rows.  Loader
-    // thread ht = tid - 256 holds 16-byte pieces ht + 256 p of K, Q (row-major),
-    // V and the A record; alpha: loader wave w holds token rows 16 (w - 4) ..
-    // +15, lane = value row (one 256-byte token row per load).
+    // thread ht = tid - 256 holds 16-byte pieces ht + 256 p of K, Q (row-major)
+    // and the A record; V and alpha: loader wave w holds token rows 16 (w - 4) ..
+    // +15, lane = value row (one token row of the block per load).
     // The loads (and the O store below) are issued unconditionally: a chunk past
     // the end gets an empty buffer range, so nothing is accessed.  Uniform control
     // flow lets the compiler count outstanding memory operations exactly.
@@ -653,23 +654,19 @@ __global__ __launch_bounds__(512) void scan_kernel(
             R[PK0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
             R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
         }
-        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
-#pragma unroll
-        for (int p = 0; p < NV; ++p) {
-            const int idx = ht + 256 * p;
-            R[PV0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                rv, static_cast<int>((idx / (BV / 8)) * row_v + 8 * (idx % (BV / 8))) * 2, 0, 0));
-        }
         const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
         const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
 #pragma unroll
         for (int p = 0; p < NA; ++p)
             R[PA0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (ht + 256 * p) * 16, 0, 0));
+        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
         const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            R[PL0 + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                ra, static_cast<int>((16 * (wave - 4) + r) * row_v + lane) * 4, 0, 0));
+        for (int r = 0; r < 16; ++r) {
+            const int e = static_cast<int>((16 * (wave - 4) + r) * row_v + lane);
+            R[PV0 + r / 4][r % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b16(rv, e * 2, 0, 0));
+            R[PL0 + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, e * 4, 0, 0));
+        }
     };
 
     auto chunk_len = [&](int64_t tc) { return static_cast<int>(max<int64_t>(0, min<int64_t>(C, u.t1 - tc))); };
@@ -702,7 +699,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
     //   registers: a lane holds one value row), kept in the alpha registers; the
     //   wave's totals go to Tot[parity][wave - 4];
     // finalize   -- after a barrier, add the totals of the loader waves before
-    //   (the rows before this wave's) and write G [t][i]; wave 7 writes gamma.
+    //   (the rows before this wave's), write G [t][i] and X^T [i][t] = V 2^{-G}
+    //   (the chain waves' initial Y); wave 7 writes gamma.
     // Rows past the sequence end contribute log alpha = 0.
     auto local_scan = [&](int n, int par, int ln) {
         float run = 0.f;
@@ -720,8 +718,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const float tb = Tot[(par * 4 + b) * BV + ln];
             carry += b < wave - 4 ? tb : 0.f;
         }
+        float* xt = XT + ln * XP + 16 * (wave - 4);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Gs[(16 * (wave - 4) + r) * GP + ln] = R[PL0 + r / 4][r % 4] + carry;
+        for (int p = 0; p < 4; ++p) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gv = R[PL0 + p][e] + carry;
+                Gs[(16 * (wave - 4) + 4 * p + e) * GP + ln] = gv;
+                x[e] = bf16_bits_to_f32(static_cast<uint16_t>(__float_as_uint(R[PV0 + p][e]))) * __builtin_amdgcn_exp2f(-gv);
+            }
+            *reinterpret_cast<f32x4*>(xt + 4 * p) = x;
+        }
         if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(R[PL0 + 3][3] + carry);
     };
     // loaded pieces -> LDS
@@ -732,12 +740,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const int idx = ht + 256 * p;
             *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PK0 + p]);
             *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
-        }
-#pragma unroll
-        for (int p = 0; p < NV; ++p) {
-            const int idx = ht + 256 * p;
-            *reinterpret_cast<u32x4*>(Vr + (idx / (BV / 8)) * OP + 8 * (idx % (BV / 8))) =
-                __builtin_bit_cast(u32x4, R[PV0 + p]);
         }
 #pragma unroll
         for (int p = 0; p < NA; ++p) stage_a(__builtin_bit_cast(u32x4, R[PA0 + p]), ht + 256 * p);
@@ -782,57 +784,66 @@ __global__ __launch_bounds__(512) void scan_kernel(
             // ======== Y = X - K S^T, then U = A Y, for value rows i = rb + 16 ib + m16
             // (lane column); rows t = 16 tt + 4g + r of tile tt.  Every K and A
             // fragment serves both 16-row blocks ib.
+            // Y starts as X (four consecutive t of one value row per read); K
+            // fragments are loaded one step ahead of their use.
             f32x4 Y[2][4];
+            bf16x8 kf[2][4];
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i = rb + 16 * ib + m16;
+            for (int tt = 0; tt < 4; ++tt) kf[0][tt] = frag_st(Kc, KP, 16 * tt, 0, ln);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * tt + 4 * g + r;
-                        Y[ib][tt][r] = bf16_bits_to_f32(Vr[t * OP + i]) * __builtin_amdgcn_exp2f(-Gs[t * GP + i]);
-                    }
-            }
+                    Y[ib][tt] = *reinterpret_cast<const f32x4*>(XT + (rb + 16 * ib + m16) * XP + 16 * tt + 4 * g);
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                bf16x8 kf[4];
+                if (m + 1 < NM) {
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) kf[tt] = frag_st(Kc, KP, 16 * tt, 32 * m, ln);
+                    for (int tt = 0; tt < 4; ++tt) kf[(m + 1) & 1][tt] = frag_st(Kc, KP, 16 * tt, 32 * (m + 1), ln);
+                }
                 issue_fence();
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
                     const bf16x8 sb = neg_state(ib, m);
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) Y[ib][tt] = mfma16(kf[tt], sb, Y[ib][tt]);
+                    for (int tt = 0; tt < 4; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
                 }
             }
+            bf16x8 af[2][4];
+            af[0][0] = frag_st(A_hi, CP, 0, 0, ln);
+            af[0][1] = frag_st(A_lo, CP, 0, 0, ln);
+            issue_fence();
             bf16x8 Yh[2][2], Yl[2][2];
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
                 split_stack(Y[ib][0], Y[ib][1], Yh[ib][0], Yl[ib][0]);
                 split_stack(Y[ib][2], Y[ib][3], Yh[ib][1], Yl[ib][1]);
             }
-            // A is lower triangular: t-tiles 0, 1 need s < 32 only
+            // U = A Y.  A is lower triangular: t-tiles 0, 1 need s < 32 only.  The
+            // fragments of t-tile tt + 1 are loaded while tile tt computes.
             f32x4 U[2][4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const bf16x8 ah0 = frag_st(A_hi, CP, 16 * tt, 0, ln), al0 = frag_st(A_lo, CP, 16 * tt, 0, ln);
-                bf16x8 ah1 = {}, al1 = {};
-                if (tt >= 2) {
-                    ah1 = frag_st(A_hi, CP, 16 * tt, 32, ln);
-                    al1 = frag_st(A_lo, CP, 16 * tt, 32, ln);
+                bf16x8* cur = af[tt & 1];
+                bf16x8* nxt = af[(tt + 1) & 1];
+                if (tt + 1 < 4) {
+                    nxt[0] = frag_st(A_hi, CP, 16 * (tt + 1), 0, ln);
+                    nxt[1] = frag_st(A_lo, CP, 16 * (tt + 1), 0, ln);
+                    if (tt + 1 >= 2) {
+                        nxt[2] = frag_st(A_hi, CP, 16 * (tt + 1), 32, ln);
+                        nxt[3] = frag_st(A_lo, CP, 16 * (tt + 1), 32, ln);
+                    }
                 }
                 issue_fence();
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    f32x4 acc = mfma16(ah0, Yh[ib][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                    acc = mfma16(al0, Yh[ib][0], acc);
-                    acc = mfma16(ah0, Yl[ib][0], acc);
+                    f32x4 acc = mfma16(cur[0], Yh[ib][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                    acc = mfma16(cur[1], Yh[ib][0], acc);
+                    acc = mfma16(cur[0], Yl[ib][0], acc);
                     if (tt >= 2) {
-                        acc = mfma16(ah1, Yh[ib][1], acc);
-                        acc = mfma16(al1, Yh[ib][1], acc);
-                        acc = mfma16(ah1, Yl[ib][1], acc);
+                        acc = mfma16(cur[2], Yh[ib][1], acc);
+                        acc = mfma16(cur[3], Yh[ib][1], acc);
+                        acc = mfma16(cur[2], Yl[ib][1], acc);
                     }
                     U[ib][tt] = acc;
                 }
