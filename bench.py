@@ -7,6 +7,10 @@ alpha/beta/state, S0 ~ N(0, 0.02^2)), inputs resident in HBM.  Prints one JSON
 line.  The decode workload (B=256, H=32, 1024 successive steps, 537 MB fp32
 state) is timed in the same run and reported under "decode".
 
+Warm-up: W untimed steps, then more untimed steps until at least SETTLE_S seconds
+of GPU work have run, so the timed steps see settled clocks (the first ~20 ms of
+work on an idle MI355X run up to 25% slower).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
        python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
                                              a 1 GiB device copy for calibration, 3 prefill
@@ -61,8 +65,8 @@ def measured_traffic(kernel):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--decode-steps", type=int, default=1024)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
@@ -139,6 +143,21 @@ def rel(a, b):
     return float(np.abs(d).max() / np.abs(b).max()), float(np.linalg.norm(d) / np.linalg.norm(b))
 
 
+SETTLE_S = 0.25
+
+
+def settle(step, warmup, torch):
+    """warmup untimed steps, then more until SETTLE_S seconds of GPU work have run."""
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(args, torch, kda, I):
     dev = "cuda:0"
     wid = 3
@@ -158,9 +177,7 @@ def bench_prefill(args, torch, kda, I):
     def step():
         kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settle(step, args.warmup, torch)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -235,9 +252,14 @@ def bench_decode(args, torch, kda, I):
     qs, ks, vs, as_, bs, os_ = ([x[t] for t in range(n)] for x in (q, k, v, alpha, beta, outs))
     # warm-up on a scratch state
     Sw = S_init.clone()
-    for t in range(min(8, n)):
+    it = [0]
+
+    def wstep():
+        t = it[0] % n
         kda.kda_decode_step(qs[t], ks[t], vs[t], as_[t], bs[t], Sw, o=os_[t])
-    torch.cuda.synchronize()
+        it[0] += 1
+
+    settle(wstep, min(8, n), torch)
     S.copy_(S_init)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
