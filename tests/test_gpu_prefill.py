@@ -173,3 +173,16 @@ def test_varlen_workload_sampled(torch_cuda):
     pairs = [(shortest, 0), (shortest, 15), (longest, 7), (5, 3), (40, 12)]
     check_sampled(inp, o, S, pairs)
     assert np.isfinite(o).all() and np.isfinite(S).all()
+
+
+def test_long_sequence_sampled(torch_cuda):
+    """One sequence of 65,573 tokens (1,025 chunks, a ragged last chunk): the state
+    crosses a thousand chunk boundaries in fp32 registers, and token offsets run
+    past 2^16 rows."""
+    T = 65536 + 37
+    inp = I.make_prefill(35, [T], 4, 128, 128, "bf16", "exp_softplus", 0.02)
+    print(f"prefill one sequence of {T} tokens, H=4, sampled oracle", flush=True)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=False)
+    check_sampled(inp, o, S, [(0, 0), (0, 3)])
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+
