@@ -11,10 +11,15 @@ Warm-up: W untimed steps, then more untimed steps until at least SETTLE_S second
 of GPU work have run, so the timed steps see settled clocks (the first ~20 ms of
 work on an idle MI355X run up to 25% slower).
 
+The same workload with one forget gate per (token, head) (kda_prefill_scalar_gate,
+Gated DeltaNet) is timed as well and reported under "scalar_gate".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+                       [--no-scalar-gate]
        python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
                                              a 1 GiB device copy for calibration, 3 prefill
-                                             launches, 8 decode steps)
+                                             launches, 3 scalar-gate prefill launches,
+                                             8 decode steps)
        python bench.py --summarize DIR      (print the per-kernel table of a rocprofv3 run)
 """
 from __future__ import annotations
@@ -35,6 +40,8 @@ METRIC = "KDA prefill tokens/sec (H=32,d=128) + decode state GB/s; % of roofline
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PREFILL_BYTES_PER_HEAD_TOKEN = 768 + 512 + 4 + 256   # q,k,v bf16 + alpha fp32 + beta + o bf16
+# with one gate per (token, head) (scalar gate): alpha is 4 bytes per head-token
+PREFILL_BYTES_PER_HEAD_TOKEN_SCALAR_GATE = 768 + 4 + 4 + 256
 PREFILL_FLOPS_PER_HEAD_TOKEN = 180224                # nominal chunked flops at C=64, d=128
 
 
@@ -70,6 +77,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=1024)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-scalar-gate", action="store_true")
     p.add_argument("--traffic-probe", action="store_true")
     p.add_argument("--summarize", default=None)
     return p.parse_args()
@@ -92,6 +100,12 @@ def traffic_probe():
     alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
     for _ in range(3):
         kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=inp.n_seq)
+    torch.cuda.synchronize()
+    del alpha
+    sg = I.workload_prefill(3, gate="scalar")
+    alpha = upload(sg.alpha, "f32", dev)   # q, k, v, beta and S0 are the same draws
+    for _ in range(3):
+        kda.kda_prefill_scalar_gate(q, k, v, alpha, beta, S0, None, n_seq=inp.n_seq)
     torch.cuda.synchronize()
     del q, k, v, alpha, beta, S0
     dec = I.workload_decode(4, n_steps=8)
@@ -158,15 +172,19 @@ def settle(step, warmup, torch):
         torch.cuda.synchronize()
 
 
-def bench_prefill(args, torch, kda, I):
+def bench_prefill(args, torch, kda, I, gate="channel"):
+    """Times kda_prefill (gate="channel") or kda_prefill_scalar_gate (gate="scalar")
+    on the batched prefill workload."""
     dev = "cuda:0"
     wid = 3
     w = I.WORKLOADS[wid]
     t0 = time.time()
-    inp = I.workload_prefill(wid)
-    log(f"[bench] generated prefill inputs in {time.time() - t0:.1f}s")
+    inp = I.workload_prefill(wid, gate=gate)
+    log(f"[bench] generated prefill inputs ({gate} gate) in {time.time() - t0:.1f}s")
     q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
     alpha, beta = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev)
+    fn = kda.kda_prefill if gate == "channel" else kda.kda_prefill_scalar_gate
+    per_head_token = PREFILL_BYTES_PER_HEAD_TOKEN if gate == "channel" else PREFILL_BYTES_PER_HEAD_TOKEN_SCALAR_GATE
     S0 = upload(inp.S0, "f32", dev)
     B, T, H, d = w["n_seq"], w["T"], w["H"], w["dk"]
     o = torch.empty((B * T, H, d), dtype=torch.bfloat16, device=dev)
@@ -175,7 +193,7 @@ def bench_prefill(args, torch, kda, I):
                      device=dev)
 
     def step():
-        kda.kda_prefill(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T, workspace=ws)
+        fn(q, k, v, alpha, beta, S0, None, n_seq=B, o=o, S_T=S_T, workspace=ws)
 
     settle(step, args.warmup, torch)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -191,20 +209,40 @@ def bench_prefill(args, torch, kda, I):
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = float(np.mean(launch_ms))
     head_tokens = B * T * H
-    alg_bytes = head_tokens * PREFILL_BYTES_PER_HEAD_TOKEN + 2 * B * H * d * d * 4
+    alg_bytes = head_tokens * per_head_token + 2 * B * H * d * d * 4
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     nominal_tflops = head_tokens * PREFILL_FLOPS_PER_HEAD_TOKEN / (avg_ms * 1e-3) / 1e12
     res = dict(
         tokens_per_s=B * T * args.steps / wall, ms_per_step=wall * 1e3 / args.steps,
         launch_ms=dict(avg=avg_ms, min=float(np.min(launch_ms)), max=float(np.max(launch_ms))),
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic("prefill"),
+                      frac=round(achieved / HBM_PEAK_GBS, 4),
+                      traffic=measured_traffic("prefill" if gate == "channel" else "prefill_scalar_gate"),
                       kernel="prefill call: chunk_offsets_kernel + chunk_solve_kernel + scan_kernel",
                       alg_bytes_per_launch=alg_bytes,
                       mfma_nominal_tflops=round(nominal_tflops, 1),
                       mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
     )
     return res, inp, o, S_T
+
+
+def sampled_parity_scalar_gate(inp, o_gpu, S_gpu, pairs):
+    """Worst (sequence, head) parity of the scalar-gate call on sampled pairs."""
+    import oracle
+    og = o_gpu.float().cpu().numpy()
+    Sg = S_gpu.cpu().numpy()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for n, h in pairs:
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        sub = lambda x: x[s:e, h:h + 1]
+        o_ref, S_ref = oracle.prefill_scalar_gate(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")),
+                                                  sub(inp.alpha), sub(inp.beta),
+                                                  inp.S0[n:n + 1, h:h + 1].astype(np.float64))
+        m, r = rel(og[s:e, h].astype(np.float64), o_ref[:, 0])
+        ms, rs = rel(Sg[n, h].astype(np.float64), S_ref[0, 0])
+        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms), max(worst[3], rs)]
+    return dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
+                scope=f"{len(pairs)} sampled (sequence, head) pairs, whole sequences")
 
 
 def cpu_baseline_prefill(inp, o_gpu, S_gpu):
@@ -340,6 +378,18 @@ def main():
         log(f"[bench] oracle: {cpu['value']:.4g} tokens/s on {cpu['cores']} threads")
     del inp, o, S_T
     torch.cuda.empty_cache()
+    if not args.no_scalar_gate:
+        sg, inp, o, S_T = bench_prefill(args, torch, kda, I, gate="scalar")
+        line["scalar_gate"] = dict(
+            workload="batched prefill workload with one forget gate per (token, head) "
+                     "(Gated DeltaNet), kda_prefill_scalar_gate",
+            tokens_per_s=round(sg["tokens_per_s"], 1), ms_per_step=round(sg["ms_per_step"], 4),
+            launch_ms=sg["launch_ms"], roofline=sg["roofline"],
+            parity=sampled_parity_scalar_gate(inp, o, S_T, [(0, 0), (1, 9), (2, 17), (3, 31)]))
+        log(f"[bench] scalar-gate prefill: {sg['tokens_per_s']:.4g} tokens/s, "
+            f"kernel {sg['launch_ms']['avg']:.3f} ms")
+        del inp, o, S_T
+        torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = bench_decode(args, torch, kda, I)
         log(f"[bench] decode: {line['decode']['steps_per_s']:.4g} steps/s, "

@@ -10,6 +10,8 @@
 //     s_i <- alpha_i s_i + u_i k
 //     o_i = s_i(new) . q = alpha_i c_i + u_i (k . q)
 // so one read and one write of S suffice; the read-out uses the updated state.
+// With a scalar gate (Gated DeltaNet) alpha_i is the (sequence, head)'s one
+// value for every row; without a gate (the delta rule) it is 1.
 //
 // Layout of the work: one workgroup of 8 D_V threads (at most 1024) per
 // (sequence, head).  Eight consecutive lanes own one row; lane j of the group
@@ -27,7 +29,7 @@ namespace kda {
 // threads per workgroup: eight per state row, at most 1024
 constexpr int decode_threads(int d_v) { return 8 * d_v < 1024 ? 8 * d_v : 1024; }
 
-template <typename T, int D_K, int D_V>
+template <typename T, int D_K, int D_V, int GATE>
 __global__ __launch_bounds__(1024) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(
     for (int p = 0; p < P; ++p) {
         const int i = slot + p * ROWS_PER_PASS;
         vi[p] = Elem<T>::load(v + head * D_V + i);
-        ai[p] = alpha[head * D_V + i];
+        ai[p] = GATE == GATE_CHANNEL ? alpha[head * D_V + i] : GATE == GATE_SCALAR ? alpha[head] : 1.f;
     }
     const float bt = beta[head];
 
@@ -101,22 +103,32 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(
     }
 }
 
-template <typename T, int D_K, int D_V>
+template <typename T, int D_K, int D_V, int GATE>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t heads = (int64_t)a.batch * a.n_heads;
     if (heads == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_step_kernel<T, D_K, D_V>), dim3((unsigned)heads), dim3(decode_threads(D_V)), 0, stream,
+    hipLaunchKernelGGL((decode_step_kernel<T, D_K, D_V, GATE>), dim3((unsigned)heads), dim3(decode_threads(D_V)), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.alpha, a.beta, a.S, static_cast<T*>(a.o));
     return hipGetLastError();
 }
 
+template <typename T, int GATE>
+static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_decode_t<T, 128, 128, GATE>(a, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_decode_t<T, 64, 64, GATE>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_decode_t<T, 128, 64, GATE>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_decode_t<T, 64, 128, GATE>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 template <typename T>
 static hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_decode_t<T, 128, 128>(a, stream);
-    if (a.d_k == 64 && a.d_v == 64) return launch_decode_t<T, 64, 64>(a, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_decode_t<T, 128, 64>(a, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_decode_t<T, 64, 128>(a, stream);
+    switch (a.gate) {
+        case GATE_CHANNEL: return launch_decode_g<T, GATE_CHANNEL>(a, stream);
+        case GATE_SCALAR: return launch_decode_g<T, GATE_SCALAR>(a, stream);
+        case GATE_NONE: return launch_decode_g<T, GATE_NONE>(a, stream);
+    }
     return hipErrorInvalidValue;
 }
 

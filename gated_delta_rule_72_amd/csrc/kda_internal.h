@@ -8,6 +8,14 @@
 
 namespace kda {
 
+// Layout of the forget gate alpha.
+//   GATE_CHANNEL  [.., H, d_v]: one gate per value channel (KDA, page "Kimi (AI)",
+//                 section "Kimi Delta Attention (KDA)")
+//   GATE_SCALAR   [.., H]: one gate per (token, head) for every row -- the
+//                 scalar-gated delta rule (Gated DeltaNet) that KDA refines
+//   GATE_NONE     no gate (alpha = 1): the plain delta rule; alpha is NULL
+enum Gate : int { GATE_CHANNEL = 0, GATE_SCALAR = 1, GATE_NONE = 2 };
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -18,6 +26,7 @@ struct DecodeArgs {
     void* o;
     int32_t batch, n_heads, d_k, d_v;
     bool bf16;
+    Gate gate;
 };
 
 struct PrefillArgs {
@@ -34,6 +43,7 @@ struct PrefillArgs {
     float* S_T;                // may be null
     void* workspace;
     size_t workspace_bytes;
+    Gate gate;
 };
 
 // Chunk length of the chunkwise prefill (tokens solved together).

@@ -15,6 +15,10 @@
 // so one decay-free solve serves every row; the decay moves onto V, O and S as
 // elementwise scalings.  Token rows past the end of a sequence read as k = q =
 // v = 0, beta = 0 and log alpha = 0, which change nothing.
+// The gate comes in three layouts (template parameter GATE): one value per
+// value channel (KDA), one per (token, head) shared by every row (the
+// scalar-gated delta rule, Gated DeltaNet, which KDA refines), or none (the
+// delta rule, G = 0).  Only the loads of alpha and the log of G differ.
 //
 // Two kernels.  A depends on k and beta only, never on S, so chunk_solve_kernel
 // solves it for every (chunk, head) at once and hands it to the scan through
@@ -525,7 +529,7 @@ __device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16
     lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int GATE>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
@@ -660,12 +664,19 @@ __global__ __launch_bounds__(512) void scan_kernel(
         for (int p = 0; p < NA; ++p)
             R[PA0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (ht + 256 * p) * 16, 0, 0));
         const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
-        const auto ra = make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0);
+        // alpha: a value row per lane (per-channel gate), or the token's one gate,
+        // the same address in every lane (scalar gate); nothing without a gate
+        const auto ra = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
+                        : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, any ? ((n - 1) * H + 1) * 4 : 0)
+                                              : make_rsrc(alpha, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int e = static_cast<int>((16 * (wave - 4) + r) * row_v + lane);
             R[PV0 + r / 4][r % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b16(rv, e * 2, 0, 0));
-            R[PL0 + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, e * 4, 0, 0));
+            if constexpr (GATE != GATE_NONE) {
+                const int ea = GATE == GATE_CHANNEL ? e : static_cast<int>((16 * (wave - 4) + r) * H);
+                R[PL0 + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, ea * 4, 0, 0));
+            }
         }
     };
 
@@ -706,7 +717,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
         float run = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            run += 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
+            if constexpr (GATE != GATE_NONE)
+                run += 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
             R[PL0 + r / 4][r % 4] = run;
         }
         Tot[(par * 4 + wave - 4) * BV + ln] = run;
@@ -1053,7 +1065,7 @@ size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_head
            static_cast<size_t>(chunk_bound(n_seq, n_tok)) * static_cast<size_t>(n_heads) * A_RECORD_BYTES;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int GATE>
 static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int NVB = DV / BV;
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
@@ -1081,7 +1093,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+    hipLaunchKernelGGL((scan_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.alpha, a.S0, a.cu_seqlens,
                        a.cu_seqlens ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads,
@@ -1089,11 +1101,21 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int GATE>
+static hipError_t launch_bf16_g(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_bf16_t<128, 128, GATE>(a, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bf16_t<64, 64, GATE>(a, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bf16_t<128, 64, GATE>(a, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bf16_t<64, 128, GATE>(a, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_bf16_t<128, 128>(a, stream);
-    if (a.d_k == 64 && a.d_v == 64) return launch_bf16_t<64, 64>(a, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_bf16_t<128, 64>(a, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_bf16_t<64, 128>(a, stream);
+    switch (a.gate) {
+        case GATE_CHANNEL: return launch_bf16_g<GATE_CHANNEL>(a, stream);
+        case GATE_SCALAR: return launch_bf16_g<GATE_SCALAR>(a, stream);
+        case GATE_NONE: return launch_bf16_g<GATE_NONE>(a, stream);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -16,14 +16,16 @@
 //   O       = exp(G) (.) (Q S^T + tril(Q K^T) U)    tril keeps the diagonal
 //   S'      = diag(exp(G[n,:])) (S + U^T K)
 // A partial last chunk is padded with k = q = v = 0, alpha = 1, beta = 0
-// tokens, which leave every quantity above unchanged.
+// tokens, which leave every quantity above unchanged.  GATE selects the
+// layout of alpha: per value channel, one scalar per (token, head) for every
+// row, or none (alpha = 1).
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
 
 namespace kda {
 
-template <typename T, int DK, int DV, int BV>
+template <typename T, int DK, int DV, int BV, int GATE>
 __global__ __launch_bounds__(256) void prefill_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -74,7 +76,9 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
             const int t = x / BV, i = x % BV;
             const int64_t g = ((tc + t) * H + h) * DV + i0 + i;
             Xs[t][i] = t < n ? Elem<T>::load(v + g) : 0.f;
-            Gs[t][i] = t < n ? logf(alpha[g]) : 0.f;
+            if constexpr (GATE == GATE_CHANNEL) Gs[t][i] = t < n ? logf(alpha[g]) : 0.f;
+            else if constexpr (GATE == GATE_SCALAR) Gs[t][i] = t < n ? logf(alpha[(tc + t) * H + h]) : 0.f;
+            else Gs[t][i] = 0.f;
         }
         if (tid < C) bs[tid] = tid < n ? beta[(tc + tid) * H + h] : 0.f;
         __syncthreads();
@@ -172,17 +176,26 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
     }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int GATE>
 static hipError_t launch_valu_t(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
     constexpr int BV = 32;
     constexpr int NVB = DV / BV;
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, BV>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, BV, GATE>), dim3(static_cast<unsigned>(grid)),
                        dim3(256), 0, stream, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.alpha, a.beta,
                        a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
                        static_cast<T*>(a.o), a.S_T);
     return hipGetLastError();
+}
+
+template <typename T, int GATE>
+static hipError_t launch_valu_g(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_valu_t<T, 128, 128, GATE>(a, order, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_valu_t<T, 64, 64, GATE>(a, order, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_valu_t<T, 128, 64, GATE>(a, order, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_valu_t<T, 64, 128, GATE>(a, order, stream);
+    return hipErrorInvalidValue;
 }
 
 template <typename T>
@@ -194,10 +207,11 @@ static hipError_t launch_valu_dt(const PrefillArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         order = ord;
     }
-    if (a.d_k == 128 && a.d_v == 128) return launch_valu_t<T, 128, 128>(a, order, stream);
-    if (a.d_k == 64 && a.d_v == 64) return launch_valu_t<T, 64, 64>(a, order, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_valu_t<T, 128, 64>(a, order, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_valu_t<T, 64, 128>(a, order, stream);
+    switch (a.gate) {
+        case GATE_CHANNEL: return launch_valu_g<T, GATE_CHANNEL>(a, order, stream);
+        case GATE_SCALAR: return launch_valu_g<T, GATE_SCALAR>(a, order, stream);
+        case GATE_NONE: return launch_valu_g<T, GATE_NONE>(a, order, stream);
+    }
     return hipErrorInvalidValue;
 }
 

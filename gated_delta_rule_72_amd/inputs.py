@@ -17,6 +17,9 @@ Recipe (every draw is independent; see also ``WORKLOADS``):
   * alpha (float32, one value per (token, head, value channel)):
       "sigmoid_n21"    sigmoid(N(2, 1))
       "exp_softplus"   exp(-0.1 * softplus(N(0, 1)))
+    With gate="scalar" alpha is one value per (token, head), same
+    distributions, drawn from its own tensor number; with gate="none" there is
+    no alpha (None).
   * beta (float32, one scalar per (token, head)): sigmoid(N(0, 1)).
   * S0 (float32, [n_seq, H, d_v, d_k]): N(0, std^2) per element, or zeros.
   * Variable lengths: integers uniform on [lo, hi] inclusive from
@@ -37,7 +40,8 @@ import numpy as np
 BLOCK_ELEMS = 1 << 22
 
 # Tensor numbers inside a seed (fixed: changing them changes every workload).
-_T_Q, _T_K, _T_V, _T_ALPHA, _T_BETA, _T_S0 = 0, 1, 2, 3, 4, 5
+_T_Q, _T_K, _T_V, _T_ALPHA, _T_BETA, _T_S0, _T_ALPHA_SCALAR = 0, 1, 2, 3, 4, 5, 6
+GATES = ("channel", "scalar", "none")
 
 
 # ---------------------------------------------------------------- rounding ---
@@ -170,7 +174,7 @@ class PrefillInputs:
     q: np.ndarray            # [n_tok, H, d_k]  uint16 bf16 bits or float32
     k: np.ndarray            # [n_tok, H, d_k]
     v: np.ndarray            # [n_tok, H, d_v]
-    alpha: np.ndarray        # [n_tok, H, d_v]  float32
+    alpha: Optional[np.ndarray]  # [n_tok, H, d_v] float32; [n_tok, H] (scalar gate); None (no gate)
     beta: np.ndarray         # [n_tok, H]       float32
     S0: Optional[np.ndarray]  # [n_seq, H, d_v, d_k] float32, or None (zeros)
     cu_seqlens: np.ndarray   # [n_seq+1] int64
@@ -208,7 +212,7 @@ class DecodeInputs:
     q: np.ndarray       # [n_steps, B, H, d_k]
     k: np.ndarray
     v: np.ndarray       # [n_steps, B, H, d_v]
-    alpha: np.ndarray   # [n_steps, B, H, d_v] float32
+    alpha: Optional[np.ndarray]  # [n_steps, B, H, d_v] float32; [n_steps, B, H] (scalar); None
     beta: np.ndarray    # [n_steps, B, H]      float32
     S0: np.ndarray      # [B, H, d_v, d_k]     float32
     dtype: str
@@ -219,8 +223,20 @@ class DecodeInputs:
         return as_f32(getattr(self, name), self.dtype)
 
 
+def draw_gate(seed, lead, dv, alpha_kind, gate):
+    """alpha of shape [*lead, dv] (per-channel), [*lead] (scalar) or None (no gate)."""
+    if gate == "channel":
+        return draw_mapped(seed, _T_ALPHA, (*lead, dv), ALPHA_KINDS[alpha_kind])
+    if gate == "scalar":
+        return draw_mapped(seed, _T_ALPHA_SCALAR, tuple(lead), ALPHA_KINDS[alpha_kind])
+    if gate == "none":
+        return None
+    raise ValueError(f"gate must be one of {GATES}")
+
+
 def make_prefill(seed: int, seq_lens, H: int, dk: int, dv: int, dtype: str = "bf16",
-                 alpha_kind: str = "exp_softplus", s0_std: float = 0.0) -> PrefillInputs:
+                 alpha_kind: str = "exp_softplus", s0_std: float = 0.0,
+                 gate: str = "channel") -> PrefillInputs:
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     cu = np.zeros(len(seq_lens) + 1, dtype=np.int64)
     np.cumsum(seq_lens, out=cu[1:])
@@ -228,26 +244,26 @@ def make_prefill(seed: int, seq_lens, H: int, dk: int, dv: int, dtype: str = "bf
     q = draw_unit_rows(seed, _T_Q, (n_tok, H), dk, dtype)
     k = draw_unit_rows(seed, _T_K, (n_tok, H), dk, dtype)
     v = draw_normal(seed, _T_V, (n_tok, H, dv), dtype)
-    alpha = draw_mapped(seed, _T_ALPHA, (n_tok, H, dv), ALPHA_KINDS[alpha_kind])
+    alpha = draw_gate(seed, (n_tok, H), dv, alpha_kind, gate)
     beta = draw_mapped(seed, _T_BETA, (n_tok, H), lambda g, n: _sigmoid(g.standard_normal(n)))
     S0 = None
     if s0_std > 0.0:
         S0 = draw_normal(seed, _T_S0, (len(seq_lens), H, dv, dk), "f32", std=s0_std)
     return PrefillInputs(q, k, v, alpha, beta, S0, cu, dtype, seed,
-                         dict(alpha_kind=alpha_kind, s0_std=s0_std))
+                         dict(alpha_kind=alpha_kind, s0_std=s0_std, gate=gate))
 
 
 def make_decode(seed: int, n_steps: int, B: int, H: int, dk: int, dv: int,
                 dtype: str = "bf16", alpha_kind: str = "exp_softplus",
-                s0_std: float = 0.02) -> DecodeInputs:
+                s0_std: float = 0.02, gate: str = "channel") -> DecodeInputs:
     q = draw_unit_rows(seed, _T_Q, (n_steps, B, H), dk, dtype)
     k = draw_unit_rows(seed, _T_K, (n_steps, B, H), dk, dtype)
     v = draw_normal(seed, _T_V, (n_steps, B, H, dv), dtype)
-    alpha = draw_mapped(seed, _T_ALPHA, (n_steps, B, H, dv), ALPHA_KINDS[alpha_kind])
+    alpha = draw_gate(seed, (n_steps, B, H), dv, alpha_kind, gate)
     beta = draw_mapped(seed, _T_BETA, (n_steps, B, H), lambda g, n: _sigmoid(g.standard_normal(n)))
     S0 = draw_normal(seed, _T_S0, (B, H, dv, dk), "f32", std=s0_std)
     return DecodeInputs(q, k, v, alpha, beta, S0, dtype, seed,
-                        dict(alpha_kind=alpha_kind, s0_std=s0_std))
+                        dict(alpha_kind=alpha_kind, s0_std=s0_std, gate=gate))
 
 
 # The five workloads: shapes and distributions of the KDA prefill/decode path.
@@ -276,18 +292,20 @@ def workload_seq_lens(wid: int) -> np.ndarray:
     return np.full(w["n_seq"], w["T"], dtype=np.int64)
 
 
-def workload_prefill(wid: int, H: Optional[int] = None, seq_lens=None) -> PrefillInputs:
-    """Inputs of a prefill workload; H / seq_lens may be overridden for reduced runs."""
+def workload_prefill(wid: int, H: Optional[int] = None, seq_lens=None,
+                     gate: str = "channel") -> PrefillInputs:
+    """Inputs of a prefill workload; H / seq_lens may be overridden for reduced runs,
+    and gate selects the layout of alpha (per channel, scalar, none)."""
     w = WORKLOADS[wid]
     assert w["kind"] == "prefill"
     lens = workload_seq_lens(wid) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
     return make_prefill(workload_seed(wid), lens, H or w["H"], w["dk"], w["dv"], w["dtype"],
-                        w["alpha_kind"], w["s0_std"])
+                        w["alpha_kind"], w["s0_std"], gate)
 
 
 def workload_decode(wid: int = 4, n_steps: Optional[int] = None, B: Optional[int] = None,
-                    H: Optional[int] = None) -> DecodeInputs:
+                    H: Optional[int] = None, gate: str = "channel") -> DecodeInputs:
     w = WORKLOADS[wid]
     assert w["kind"] == "decode"
     return make_decode(workload_seed(wid), n_steps or w["steps"], B or w["B"], H or w["H"],
-                       w["dk"], w["dv"], w["dtype"], w["alpha_kind"], w["s0_std"])
+                       w["dk"], w["dv"], w["dtype"], w["alpha_kind"], w["s0_std"], gate)

@@ -23,7 +23,7 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
-            "kda_decode_step")
+            "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate")
 
 _lib = None
 
@@ -50,11 +50,15 @@ def lib() -> ctypes.CDLL:
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_prefill_workspace_size.restype = sz
     L.kda_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
-    L.kda_prefill.restype = ctypes.c_int
-    L.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
-                              vp, vp, vp, sz, vp]
-    L.kda_decode_step.restype = ctypes.c_int
-    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    for name in ("kda_prefill", "kda_prefill_scalar_gate"):
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                       vp, vp, vp, sz, vp]
+    for name in ("kda_decode_step", "kda_decode_step_scalar_gate"):
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -111,6 +115,21 @@ def kda_prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *, n_seq: Option
     (n_seq defaults to 1).  Returns (o, S_T); S_T is None if want_state is
     False.  S_T may be passed as S0 for an in-place continuation.
     """
+    return _prefill("kda_prefill", q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state,
+                    workspace)
+
+
+def kda_prefill_scalar_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *,
+                            n_seq: Optional[int] = None, o=None, S_T=None, want_state: bool = True,
+                            workspace=None):
+    """Prefill with one forget gate per (token, head) for every row (Gated DeltaNet):
+    alpha is [n_tok, H] f32, or None for no gate (alpha = 1, the delta rule).  The
+    other arguments and the result are those of kda_prefill."""
+    return _prefill("kda_prefill_scalar_gate", q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T,
+                    want_state, workspace)
+
+
+def _prefill(fn, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state, workspace):
     torch = _torch()
     n_tok, H, dk = q.shape
     dv = v.shape[2]
@@ -128,12 +147,12 @@ def kda_prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *, n_seq: Option
     ws_bytes = workspace_size(n_seq, n_tok, H, dk, dv, dt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    st = lib().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
-                           _ptr(cu_seqlens), n_seq, n_tok, H, dk, dv, dt, _ptr(o), _ptr(S_T),
-                           _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                           _stream(q))
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                            _ptr(cu_seqlens), n_seq, n_tok, H, dk, dv, dt, _ptr(o), _ptr(S_T),
+                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _stream(q))
     if st != KDA_OK:
-        raise KdaError("kda_prefill", st)
+        raise KdaError(fn, st)
     return o, S_T
 
 
@@ -143,14 +162,24 @@ def kda_decode_step(q, k, v, alpha, beta, S, o=None):
     q, k: [B, H, d_k]; v: [B, H, d_v]; alpha: [B, H, d_v] f32; beta: [B, H] f32;
     S: [B, H, d_v, d_k] f32.  Returns o [B, H, d_v] in q's dtype.
     """
+    return _decode("kda_decode_step", q, k, v, alpha, beta, S, o)
+
+
+def kda_decode_step_scalar_gate(q, k, v, alpha, beta, S, o=None):
+    """Decode step with one forget gate per (sequence, head) for every row: alpha is
+    [B, H] f32, or None for no gate (the delta rule).  Otherwise as kda_decode_step."""
+    return _decode("kda_decode_step_scalar_gate", q, k, v, alpha, beta, S, o)
+
+
+def _decode(fn, q, k, v, alpha, beta, S, o):
     torch = _torch()
     B, H, dk = q.shape
     dv = v.shape[2]
     dt = _dtype_code(q)
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o),
-                               B, H, dk, dv, dt, _stream(q))
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o),
+                            B, H, dk, dv, dt, _stream(q))
     if st != KDA_OK:
-        raise KdaError("kda_decode_step", st)
+        raise KdaError(fn, st)
     return o

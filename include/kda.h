@@ -135,6 +135,36 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
                            kda_dtype dt, void* stream);
 
+/*
+ * Scalar-gate variants.  The transcript page ("Per dins de Kimi K3 ..."), where
+ * it introduces KDA, describes it as Gated DeltaNet with the decay control
+ * replaced by a per-channel one: Gated DeltaNet forgets with one gate for the
+ * whole state, and the delta rule without a gate is the case alpha = 1.  These
+ * two entry points run that family on the same kernels: the update is the one
+ * above with diag(alpha_t) replaced by the scalar alpha_t (or by the identity).
+ *
+ *   alpha   [n_tok, n_heads] float32 (prefill) or [batch, n_heads] (decode):
+ *           one gate per (token, head), applied to every row of S; 4-byte
+ *           aligned.  NULL: no forget gate (alpha = 1), the delta rule.
+ * Every other argument, the workspace (kda_prefill_workspace_size), the
+ * layouts, the conventions and the errors are those of kda_prefill and
+ * kda_decode_step.  The prefill domain condition on alpha applies per token:
+ * the sum of log(alpha) over 64 consecutive tokens must stay above -80.
+ */
+kda_status kda_prefill_scalar_gate(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta,
+                                   const float* S0, const int32_t* cu_seqlens,
+                                   int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                   int32_t d_k, int32_t d_v, kda_dtype dt,
+                                   void* o, float* S_T,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status kda_decode_step_scalar_gate(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       float* S, void* o,
+                                       int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                       kda_dtype dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

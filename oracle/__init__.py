@@ -138,3 +138,32 @@ def decode(q, k, v, alpha, beta, S, want_o=True):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode_f64 failed with code {rc}")
     return o, Sn
+
+
+# ------------------------------------------------------- scalar-gate family ---
+# The transcript page ("Per dins de Kimi K3 ..."), where it introduces KDA,
+# presents it as Gated DeltaNet with the decay control refined to one gate per
+# channel.  With one gate per (token, head) the forget step diag(alpha_t) S
+# becomes alpha_t S, which is the three-step update above with every row's
+# gate equal to alpha_t; no gate at all (the delta rule) is alpha_t = 1.  These
+# two functions are that reading written out: they widen the gate to one value
+# per value row and run the same recurrence.
+
+def _rows(alpha, lead, dv):
+    if alpha is None:
+        return np.ones((*lead, dv), dtype=np.float32)
+    a = _f32(alpha, lead)
+    return np.ascontiguousarray(np.repeat(a[..., None], dv, axis=-1))
+
+
+def prefill_scalar_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
+    """prefill() with alpha [n_tok, H] (one gate per token and head), or None for no gate."""
+    v = np.asarray(v)
+    return prefill(q, k, v, _rows(alpha, v.shape[:2], v.shape[2]), beta, S0, cu_seqlens, want_o)
+
+
+def decode_scalar_gate(q, k, v, alpha, beta, S, want_o=True):
+    """decode() with alpha [n_steps, B, H] (one gate per step, sequence and head), or None."""
+    v = np.asarray(v)
+    return decode(q, k, v, _rows(alpha, v.shape[:3], v.shape[3]), beta, S, want_o)
+

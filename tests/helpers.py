@@ -76,7 +76,8 @@ def upload_prefill(inp, device="cuda"):
     import torch
     d = dict(
         q=to_device(inp.q, inp.dtype, device), k=to_device(inp.k, inp.dtype, device),
-        v=to_device(inp.v, inp.dtype, device), alpha=to_device(inp.alpha, "f32", device),
+        v=to_device(inp.v, inp.dtype, device),
+        alpha=None if inp.alpha is None else to_device(inp.alpha, "f32", device),
         beta=to_device(inp.beta, "f32", device),
         S0=None if inp.S0 is None else to_device(inp.S0, "f32", device),
         cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device),

@@ -55,12 +55,12 @@ def test_workspace_size(L):
     assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
 
 
-def prefill(L, **kw):
+def prefill(L, fn="kda_prefill", **kw):
     args = dict(q=A, k=A + 0x100000, v=A + 0x200000, alpha=A + 0x300000, beta=A + 0x400000,
                 S0=None, cu=None, n_seq=2, n_tok=64, H=2, dk=64, dv=64, dt=1,
                 o=A + 0x500000, S_T=A + 0x600000, ws=A + 0x700000, ws_bytes=256, stream=None)
     args.update(kw)
-    return L.kda_prefill(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S0"],
+    return getattr(L, fn)(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S0"],
                          args["cu"], args["n_seq"], args["n_tok"], args["H"], args["dk"], args["dv"],
                          args["dt"], args["o"], args["S_T"], args["ws"], args["ws_bytes"],
                          args["stream"])
@@ -89,11 +89,11 @@ def test_prefill_rejects_on_host(L, kw, status):
     assert prefill(L, **kw) == status
 
 
-def decode(L, **kw):
+def decode(L, fn="kda_decode_step", **kw):
     args = dict(q=A, k=A + 0x100000, v=A + 0x200000, alpha=A + 0x300000, beta=A + 0x400000,
                 S=A + 0x1000000, o=A + 0x500000, B=4, H=2, dk=128, dv=128, dt=1, stream=None)
     args.update(kw)
-    return L.kda_decode_step(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S"],
+    return getattr(L, fn)(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["S"],
                              args["o"], args["B"], args["H"], args["dk"], args["dv"], args["dt"],
                              args["stream"])
 
@@ -112,6 +112,33 @@ def decode(L, **kw):
 ])
 def test_decode_rejects_on_host(L, kw, status):
     assert decode(L, **kw) == status
+
+
+# Scalar-gate entry points: alpha is [n_tok, H] (4-byte aligned) or NULL (no gate).
+# Only rejections are exercised here: an accepted call would reach the device.
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=A + 0x300002), kda.KDA_ERR_INVALID_ARGUMENT),   # not 4-byte aligned
+    (dict(alpha=None, beta=None), kda.KDA_ERR_INVALID_ARGUMENT),  # no gate is fine, no beta is not
+    (dict(alpha=None, o=A), kda.KDA_ERR_INVALID_ARGUMENT),     # o overlaps q
+    (dict(alpha=None, dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(alpha=None, ws=None), kda.KDA_ERR_WORKSPACE),
+    # the scalar gate spans n_tok * H * 4 = 512 bytes: o placed inside it overlaps
+    (dict(o=A + 0x300000 + 256), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(alpha=A + 0x500000 - 512 + 4), kda.KDA_ERR_INVALID_ARGUMENT),  # its tail overlaps o
+])
+def test_prefill_scalar_gate_rejects_on_host(L, kw, status):
+    assert prefill(L, "kda_prefill_scalar_gate", **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=A + 0x300002), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(alpha=None, S=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(alpha=None, S=A), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(alpha=A + 0x1000000), kda.KDA_ERR_INVALID_ARGUMENT),  # the gate inside S
+    (dict(alpha=None, B=0), kda.KDA_OK),
+])
+def test_decode_scalar_gate_rejects_on_host(L, kw, status):
+    assert decode(L, "kda_decode_step_scalar_gate", **kw) == status
 
 
 def test_binding_refuses_cpu_tensors(L):

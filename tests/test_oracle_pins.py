@@ -304,20 +304,32 @@ def test_value_channel_permutation_and_row_independence():
 def test_equal_rows_reduce_to_scalar_gated_delta_rule():
     """alpha_t = a_t * 1 gives S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
     the scalar-gated delta rule (Gated DeltaNet), written here in its key-side
-    product form; a_t = 1 gives the plain delta rule."""
+    product form; a_t = 1 gives the plain delta rule.  Checked on the per-channel
+    oracle with equal rows and on the scalar-gate entry points (gate [T, H], or
+    None for no gate), prefill and decode."""
     rng = np.random.default_rng(14)
     T, dk, dv = 9, 5, 4
     q, k, v, _, b, S0 = rand_case(rng, T, 1, dk, dv)
-    for scal in (f32(rng.uniform(0.3, 1.0, T)), np.ones(T, np.float32)):
-        a = np.repeat(scal[:, None, None], dv, axis=2).astype(np.float32)
-        o, S = oracle.prefill(q, k, v, a, b, S0)
+    for scal in (f32(rng.uniform(0.3, 1.0, T)), np.ones(T, np.float32), None):
+        ones = scal is None
+        sc = np.ones(T, np.float32) if ones else scal
+        a = np.repeat(sc[:, None, None], dv, axis=2).astype(np.float32)
         St = S0[0, 0].copy()
+        o_ref = np.zeros((T, dv))
         for t in range(T):
             kt = d64(k[t, 0])
-            St = float(scal[t]) * St @ (np.eye(dk) - float(b[t, 0]) * np.outer(kt, kt)) \
+            St = float(sc[t]) * St @ (np.eye(dk) - float(b[t, 0]) * np.outer(kt, kt)) \
                 + float(b[t, 0]) * np.outer(d64(v[t, 0]), kt)
-            np.testing.assert_allclose(o[t, 0], St @ d64(q[t, 0]), rtol=0, atol=1e-13)
-        np.testing.assert_allclose(S[0, 0], St, rtol=0, atol=1e-13)
+            o_ref[t] = St @ d64(q[t, 0])
+        runs = [oracle.prefill_scalar_gate(q, k, v, None if ones else sc[:, None], b, S0)]
+        dec_o, dec_S = oracle.decode_scalar_gate(q[:, None], k[:, None], v[:, None],
+                                                 None if ones else sc[:, None, None], b[:, None], S0)
+        runs.append((dec_o[:, 0], dec_S))
+        if not ones:
+            runs.append(oracle.prefill(q, k, v, a, b, S0))
+        for o, S in runs:
+            np.testing.assert_allclose(o[:, 0], o_ref, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(S[0, 0], St, rtol=0, atol=1e-13)
 
 
 def test_split_prefill_varlen_and_decode_agree():
