@@ -126,8 +126,15 @@ __device__ inline int64_t seq_start(int seq, int n_seq, int n_tok, const int32_t
     return cu ? static_cast<int64_t>(cu[seq]) : static_cast<int64_t>(seq) * (n_tok / n_seq);
 }
 
-// Token range [t0, t0 + n) of global chunk gc; chunk_off[m] is the first global
-// chunk of sequence m and chunk_off[n_seq] the number of chunks.
+// First global chunk of sequence m (m = n_seq gives the number of chunks):
+// chunk_off[m] for packed sequences of any lengths; for n_seq sequences of
+// n_tok / n_seq tokens each (chunk_off == nullptr) it is m ceil(len / C).
+__device__ inline int first_chunk(int m, int n_seq, int n_tok, const int32_t* chunk_off) {
+    if (chunk_off) return chunk_off[m];
+    return m * ((n_tok / n_seq + C - 1) / C);
+}
+
+// Token range [t0, t0 + n) of global chunk gc.
 struct ChunkRef {
     int64_t t0;
     int n;
@@ -135,15 +142,20 @@ struct ChunkRef {
 
 __device__ inline ChunkRef chunk_ref(int gc, int n_seq, int n_tok, const int32_t* cu,
                                      const int32_t* chunk_off) {
-    int lo = 0, hi = n_seq;  // chunk_off[lo] <= gc < chunk_off[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (chunk_off[mid] <= gc) lo = mid;
-        else hi = mid;
+    int lo = 0;
+    if (chunk_off) {
+        int hi = n_seq;  // chunk_off[lo] <= gc < chunk_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (chunk_off[mid] <= gc) lo = mid;
+            else hi = mid;
+        }
+    } else {
+        lo = gc / first_chunk(1, n_seq, n_tok, nullptr);  // only called while chunks exist
     }
     const int64_t s0 = seq_start(lo, n_seq, n_tok, cu), s1 = seq_start(lo + 1, n_seq, n_tok, cu);
     ChunkRef r;
-    r.t0 = s0 + static_cast<int64_t>(gc - chunk_off[lo]) * C;
+    r.t0 = s0 + static_cast<int64_t>(gc - first_chunk(lo, n_seq, n_tok, chunk_off)) * C;
     r.n = static_cast<int>(min<int64_t>(C, s1 - r.t0));
     return r;
 }
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g16 = lane >> 4, m16 = lane & 15;
-    const int total = min(chunk_off[n_seq], max_chunks) * n_heads;  // (chunk, head) items
+    const int total = min(first_chunk(n_seq, n_seq, n_tok, chunk_off), max_chunks) * n_heads;  // items
 
     // ---- loads of one item's K and beta into registers (rows past the sequence
     // end read as zero; an item past the last gets empty ranges)
@@ -584,7 +596,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int h = u.head;
     const int i0 = u.vblk * BV;
     const int64_t row_qk = H * DK, row_v = H * DV;  // element strides between tokens
-    const int chunk0 = chunk_off[u.seq];
+    const int chunk0 = first_chunk(u.seq, n_seq, n_tok, chunk_off);
 
     // ---- state of the chain waves: R[(ib) * NJ + (jt)] = S^T rows 16 jt .. 16 jt + 15 (key
     // channels), columns = value rows rb + 16 ib .. +15
@@ -1077,10 +1089,12 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     hipError_t e;
     if (a.cu_seqlens) {
         if ((e = launch_schedule(a.cu_seqlens, a.n_seq, order, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.n_seq, a.n_tok,
+                           chunk_off);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        chunk_off = nullptr;  // equal lengths: the kernels compute the offsets
     }
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.n_seq, a.n_tok,
-                       chunk_off);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
     if (a.n_tok > 0) {
         // as many workgroups as stay resident (four per CU); each loops over items
