@@ -218,7 +218,7 @@ def bench_prefill(args, torch, kda, I, gate="channel"):
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=measured_traffic("prefill" if gate == "channel" else "prefill_scalar_gate"),
-                      kernel="prefill call: chunk_offsets_kernel + chunk_solve_kernel + scan_kernel",
+                      kernel="prefill call: chunk_solve_kernel + scan_kernel",
                       alg_bytes_per_launch=alg_bytes,
                       mfma_nominal_tflops=round(nominal_tflops, 1),
                       mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
