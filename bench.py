@@ -12,10 +12,11 @@ of GPU work have run, so the timed steps see settled clocks (the first ~20 ms of
 work on an idle MI355X run up to 25% slower).
 
 The same workload with one forget gate per (token, head) (kda_prefill_scalar_gate,
-Gated DeltaNet) is timed as well and reported under "scalar_gate".
+Gated DeltaNet) is timed as well and reported under "scalar_gate", and the tiny fp32,
+single-layer and varlen prefill workloads under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
-                       [--no-scalar-gate]
+                       [--no-scalar-gate] [--no-workloads]
        python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
                                              a 1 GiB device copy for calibration, 3 prefill
                                              launches, 3 scalar-gate prefill launches,
@@ -78,6 +79,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-scalar-gate", action="store_true")
+    p.add_argument("--no-workloads", action="store_true")
     p.add_argument("--traffic-probe", action="store_true")
     p.add_argument("--summarize", default=None)
     return p.parse_args()
@@ -343,6 +345,56 @@ def bench_decode(args, torch, kda, I):
     return res
 
 
+def bench_other_workloads(args, torch, kda, I):
+    """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
+    other prefill shapes; their parity is covered by the GPU tests).  Each: inputs resident
+    in HBM, settled clocks, the mean of `steps` calls from HIP events."""
+    dev = "cuda:0"
+    out = {}
+    for wid in (1, 2, 5):
+        w = I.WORKLOADS[wid]
+        inp = I.workload_prefill(wid)
+        dt = inp.dtype
+        q, k, v = (upload(getattr(inp, n), dt, dev) for n in ("q", "k", "v"))
+        alpha, beta = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev)
+        S0 = None if inp.S0 is None else upload(inp.S0, "f32", dev)
+        varlen = wid == 5
+        cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev) if varlen else None
+        n_tok, H, dk, dv, n_seq = inp.n_tok, inp.H, inp.dk, inp.dv, inp.n_seq
+        o = torch.empty((n_tok, H, dv), dtype=q.dtype, device=dev)
+        S_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=dev)
+        code = kda.KDA_DTYPE_BF16 if dt == "bf16" else kda.KDA_DTYPE_F32
+        ws = torch.empty(max(1, kda.workspace_size(n_seq, n_tok, H, dk, dv, code)), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            kda.kda_prefill(q, k, v, alpha, beta, S0, cu, n_seq=n_seq, o=o, S_T=S_T, workspace=ws)
+
+        settle(step, args.warmup, torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        eb = 2 if dt == "bf16" else 4
+        per_ht = (2 * dk + 2 * dv) * eb + dv * 4 + 4     # q, k, v, o + alpha + beta
+        head_tokens = n_tok * H
+        alg = head_tokens * per_ht + (2 if S0 is not None else 1) * n_seq * H * dv * dk * 4
+        gbs = alg / (ms * 1e-3) / 1e9
+        out[w["name"]] = dict(
+            shape=(f"{n_seq} sequences, {n_tok} tokens, H={H}, d_k={dk}, d_v={dv}, {dt}"
+                   + (", lengths U{256..16384}, cu_seqlens" if varlen else "")),
+            ms_per_call=round(ms, 4), tokens_per_s=round(n_tok / (ms * 1e-3), 1),
+            alg_bytes=int(alg), achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        log(f"[bench] {w['name']}: {ms:.4f} ms per call, {n_tok / (ms * 1e-3):.4g} tokens/s, "
+            f"{gbs / HBM_PEAK_GBS:.3f} of HBM")
+        del q, k, v, alpha, beta, S0, cu, o, S_T, ws, inp
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -390,6 +442,8 @@ def main():
             f"kernel {sg['launch_ms']['avg']:.3f} ms")
         del inp, o, S_T
         torch.cuda.empty_cache()
+    if not args.no_workloads:
+        line["workloads"] = bench_other_workloads(args, torch, kda, I)
     if not args.no_decode:
         line["decode"] = bench_decode(args, torch, kda, I)
         log(f"[bench] decode: {line['decode']['steps_per_s']:.4g} steps/s, "

@@ -46,9 +46,9 @@ struct PrefillArgs {
     Gate gate;
 };
 
-// Chunk length of the chunkwise prefill (tokens solved together).
+// Chunk length of the chunkwise bf16 prefill (tokens solved together).  The
+// fp32 prefill runs token by token.
 constexpr int PREFILL_CHUNK_BF16 = 64;
-constexpr int PREFILL_CHUNK_F32 = 32;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

@@ -28,10 +28,11 @@
  *     outputs are undefined.  Nothing aborts the process.
  *   - NaN and Inf inputs are not checked; they propagate.
  *   - d_k and d_v must each be 64 or 128.
- *   - alpha is taken as given (the gate after its activation); the kernels
- *     assume that the sum of log(alpha) over any 64 consecutive tokens of a
- *     value channel stays above -80 (a decay factor of ~1e-35); alpha == 0
- *     exactly is outside that domain for prefill, and is exact for decode.
+ *   - alpha is taken as given (the gate after its activation).  The bf16
+ *     prefill assumes that the sum of log(alpha) over any 64 consecutive
+ *     tokens of a value channel stays above -80 (a decay factor of ~1e-35);
+ *     alpha == 0 exactly is outside that domain.  The float32 prefill and the
+ *     decode step run token by token and are exact for alpha == 0.
  */
 #ifndef KDA_H_
 #define KDA_H_

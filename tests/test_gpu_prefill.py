@@ -186,3 +186,19 @@ def test_long_sequence_sampled(torch_cuda):
     check_sampled(inp, o, S, [(0, 0), (0, 3)])
     assert np.isfinite(o).all() and np.isfinite(S).all()
 
+
+
+def test_fp32_prefill_alpha_zero_is_exact(torch_cuda):
+    """fp32 prefill runs token by token and takes no log of alpha: with alpha = 0 every
+    token forgets the past, so S_t = beta_t v_t k_t^T and o_t = beta_t (k_t . q_t) v_t
+    whatever came before (the alpha = 0 closed form), for every sequence and head."""
+    print("fp32 prefill alpha = 0", flush=True)
+    inp = I.make_prefill(7100, [40, 1, 17], 3, 64, 128, "f32", "zeros", 0.02)
+    o, S = gpu_prefill(torch_cuda, inp)
+    q, k, v = (inp.q.astype(np.float64), inp.k.astype(np.float64), inp.v.astype(np.float64))
+    b = inp.beta.astype(np.float64)
+    exp_o = (b * (q * k).sum(-1))[..., None] * v
+    np.testing.assert_allclose(o, exp_o, rtol=1e-5, atol=1e-6)
+    last = inp.cu_seqlens[1:] - 1
+    exp_S = (b[last][..., None, None] * v[last][..., :, None] * k[last][..., None, :])
+    np.testing.assert_allclose(S, exp_S, rtol=1e-5, atol=1e-6)
