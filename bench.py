@@ -345,10 +345,43 @@ def bench_decode(args, torch, kda, I):
     return res
 
 
+def workload_parity(inp, o_gpu, S_gpu, pairs=None):
+    """Worst (sequence, head) parity against the oracle: on every pair, or on the
+    sampled (sequence, head) pairs given (each run by the oracle on that pair alone)."""
+    import oracle
+    og = o_gpu.float().cpu().numpy()
+    Sg = S_gpu.cpu().numpy()
+    S0 = None if inp.S0 is None else inp.S0.astype(np.float64)
+    if pairs is None:
+        o_ref, S_ref = oracle.prefill(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta, S0,
+                                      inp.cu_seqlens)
+        pairs = [(n, h) for n in range(inp.n_seq) for h in range(inp.H)]
+        ref = lambda n, h: (o_ref[int(inp.cu_seqlens[n]):int(inp.cu_seqlens[n + 1]), h], S_ref[n, h])
+        scope = f"all {len(pairs)} (sequence, head) pairs"
+    else:
+        def ref(n, h):
+            s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+            sub = lambda x: x[s:e, h:h + 1]
+            r = oracle.prefill(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")), sub(inp.alpha),
+                               sub(inp.beta), None if S0 is None else S0[n:n + 1, h:h + 1])
+            return r[0][:, 0], r[1][0, 0]
+        scope = f"{len(pairs)} sampled (sequence, head) pairs"
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for n, h in pairs:
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        o_r, S_r = ref(n, h)
+        m, r = rel(og[s:e, h].astype(np.float64), o_r)
+        ms, rs = rel(Sg[n, h].astype(np.float64), S_r)
+        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms), max(worst[3], rs)]
+    return dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
+                scope=scope + ", worst slice")
+
+
 def bench_other_workloads(args, torch, kda, I):
     """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
-    other prefill shapes; their parity is covered by the GPU tests).  Each: inputs resident
-    in HBM, settled clocks, the mean of `steps` calls from HIP events."""
+    other prefill shapes).  Each: inputs resident in HBM, settled clocks, the mean of
+    `steps` calls from HIP events; parity of the last call against the oracle (every
+    pair for the two small workloads, three sampled pairs of the varlen one)."""
     dev = "cuda:0"
     out = {}
     for wid in (1, 2, 5):
@@ -387,7 +420,9 @@ def bench_other_workloads(args, torch, kda, I):
             shape=(f"{n_seq} sequences, {n_tok} tokens, H={H}, d_k={dk}, d_v={dv}, {dt}"
                    + (", lengths U{256..16384}, cu_seqlens" if varlen else "")),
             ms_per_call=round(ms, 4), tokens_per_s=round(n_tok / (ms * 1e-3), 1),
-            alg_bytes=int(alg), achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+            alg_bytes=int(alg), achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+            parity=workload_parity(inp, o, S_T, [(0, 0), (n_seq // 2, H // 2), (n_seq - 1, H - 1)]
+                                   if varlen else None))
         log(f"[bench] {w['name']}: {ms:.4f} ms per call, {n_tok / (ms * 1e-3):.4g} tokens/s, "
             f"{gbs / HBM_PEAK_GBS:.3f} of HBM")
         del q, k, v, alpha, beta, S0, cu, o, S_T, ws, inp
