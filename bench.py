@@ -130,11 +130,13 @@ def summarize(path):
     for db in dbs:
         con = sqlite3.connect(db)
         print(f"# {os.path.relpath(db, path)}")
-        rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration) "
-                           "from kernels group by name order by sum(duration) desc").fetchall()
-        print(f"{'kernel':70s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'max_us':>10s}")
-        for name, n, avg, mn, mx in rows:
-            print(f"{name[:70]:70s} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f}")
+        # one row per kernel and launch size (grid_x work-items), so that workloads of
+        # different shapes that run the same kernel are told apart
+        rows = con.execute("select name, grid_x, count(*), avg(duration), min(duration), max(duration) "
+                           "from kernels group by name, grid_x order by sum(duration) desc").fetchall()
+        print(f"{'kernel':62s} {'grid_x':>9s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        for name, gx, n, avg, mn, mx in rows:
+            print(f"{name[:62]:62s} {gx:9d} {n:6d} {avg / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f}")
         try:
             crow = con.execute("select name, counter_name, count(distinct dispatch_id), "
                                "sum(counter_value) / count(distinct dispatch_id) from pmc_events "
