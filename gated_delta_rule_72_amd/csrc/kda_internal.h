@@ -50,13 +50,34 @@ struct PrefillArgs {
 // fp32 prefill runs token by token.
 constexpr int PREFILL_CHUNK_BF16 = 64;
 
+// Segments per sequence for the sequence-parallel bf16 prefill (1 = one scan
+// per sequence).  Equal-length batches whose (sequence, head, 64-row block)
+// units would leave most of the 256 CUs idle have each sequence split into G
+// segments of whole 64-token chunks (G a power of two, at least two chunks per
+// segment, units x G at most 256 workgroups).  Needs d_k = d_v.
+inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v,
+                            bool varlen) {
+    if (varlen || d_k != d_v || n_tok <= 0 || n_seq < 1) return 1;
+    const int64_t units = static_cast<int64_t>(n_seq) * n_heads * (d_v / 64);
+    const int64_t len = n_tok / n_seq;
+    int g = 1;
+    while (units * 2 * g <= 256 && len % (64 * 2 * g) == 0 && len / (2 * g) >= 2 * 64) g *= 2;
+    return g;
+}
+
+// Composes the segment states of the sequence-parallel prefill (kda_segments.hip).
+template <int DK, int DV>
+hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M, int n_seq,
+                                   int G, int n_heads, float* S_start, float* S_T, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 // Workspace bytes of the fp32 prefill (the varlen schedule) and of the bf16
-// prefill (schedule, chunk offsets and the per-(chunk, head) solved A blocks).
+// prefill (schedule, chunk offsets, the per-(chunk, head) solved A blocks, and
+// for the sequence-parallel path the segment states).
 size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
-size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads);
+size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
 
 }  // namespace kda

@@ -44,6 +44,9 @@ namespace kda {
 namespace {
 
 constexpr int C = PREFILL_CHUNK_BF16;  // 64 tokens per chunk
+// scan_kernel flags: v read as zero; S0 taken as the identity (d_v = d_k)
+constexpr int SCAN_ZERO_V = 1;
+constexpr int SCAN_S0_IDENTITY = 2;
 constexpr int BV = 64;                 // value rows per scan workgroup
 constexpr int PAD = 8;                 // bf16 row padding (16 bytes) against bank conflicts
 constexpr int CP = C + PAD;            // pitch of bf16 rows of length C
@@ -547,7 +550,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
     const uint16_t* __restrict__ arec, int n_seq, int n_tok, int n_heads,
-    uint16_t* __restrict__ o, float* __restrict__ S_T) {
+    uint16_t* __restrict__ o, float* __restrict__ S_T, int flags, float* __restrict__ glog_out) {
     using SM = ScanSmem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -614,7 +617,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
     f32x4 R[RN];
 #pragma unroll
     for (int x = 0; x < RN; ++x) R[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (chain && S0) {
+    if (chain && (flags & SCAN_S0_IDENTITY)) {
+        // S0 = I (d_v = d_k): row i holds 1 at key channel i
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int row = i0 + rb + 16 * ib + (lane & 15);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[(ib) * NJ + (jt)][e] = row == 16 * jt + 4 * (lane >> 4) + e ? 1.f : 0.f;
+        }
+    } else if (chain && S0) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             const float* src =
@@ -675,7 +688,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
         for (int p = 0; p < NA; ++p)
             R[PA0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (ht + 256 * p) * 16, 0, 0));
-        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
+        // v reads as zero when the flag asks for it (an empty range)
+        const auto rv = make_rsrc(v + tok0 * DV + i0, any && !(flags & SCAN_ZERO_V) ? ((n - 1) * row_v + BV) * 2 : 0);
         // alpha: a value row per lane (per-channel gate), or the token's one gate,
         // the same address in every lane (scalar gate); nothing without a gate
         const auto ra = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
@@ -735,6 +749,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
         Tot[(par * 4 + wave - 4) * BV + ln] = run;
     };
+    float glog = 0.f;  // wave 7: this row's total log2-decay over the unit's chunks
     auto finalize = [&](int par, int ln) {
         float carry = 0.f;
 #pragma unroll
@@ -754,7 +769,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
             }
             *reinterpret_cast<f32x4*>(xt + 4 * p) = x;
         }
-        if (wave == 7) gam[ln] = __builtin_amdgcn_exp2f(R[PL0 + 3][3] + carry);
+        if (wave == 7) {
+            const float tot = R[PL0 + 3][3] + carry;
+            gam[ln] = __builtin_amdgcn_exp2f(tot);
+            glog += tot;
+        }
     };
     // loaded pieces -> LDS
     auto stage = [&](int ln) {
@@ -1052,6 +1071,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
         if (outw) store_o(prev_tc, prev_n, lane);
     }
 
+    // the unit's total log2-decay per value row, when asked for (the sequence-parallel
+    // path composes segments with it)
+    if (glog_out && wave == 7) glog_out[(static_cast<int64_t>(u.seq) * H + h) * DV + i0 + lane] = glog;
+
     if (S_T && chain) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
@@ -1072,9 +1095,24 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 static int64_t chunk_bound(int32_t n_seq, int32_t n_tok) { return static_cast<int64_t>(n_tok) / C + n_seq; }
 
-size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads) {
-    return align256(static_cast<size_t>(n_seq) * 4) + align256((static_cast<size_t>(n_seq) + 1) * 4) +
-           static_cast<size_t>(chunk_bound(n_seq, n_tok)) * static_cast<size_t>(n_heads) * A_RECORD_BYTES;
+// Segment states of the sequence-parallel path: dS and S_start
+// [n_seq G, H, d_v, d_k] and M [n_seq G, H, d_k, d_k], fp32 (d_k = d_v), then the
+// segments' log2-decays [n_seq G, H, d_v].
+static size_t segment_state_bytes(int32_t n_seq, int32_t n_heads, int32_t d_k, int32_t d_v, int G) {
+    return static_cast<size_t>(n_seq) * G * n_heads * static_cast<size_t>(d_v) * d_k * 4;
+}
+static size_t segment_log_bytes(int32_t n_seq, int32_t n_heads, int32_t d_v, int G) {
+    return align256(static_cast<size_t>(n_seq) * G * n_heads * static_cast<size_t>(d_v) * 4);
+}
+
+size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    size_t b = align256(static_cast<size_t>(n_seq) * 4) + align256((static_cast<size_t>(n_seq) + 1) * 4) +
+               align256(static_cast<size_t>(chunk_bound(n_seq, n_tok)) * static_cast<size_t>(n_heads) * A_RECORD_BYTES);
+    // the sequence-parallel path is taken only without cu_seqlens; the workspace
+    // size does not know whether cu_seqlens will be given, so it covers that case
+    const int G = prefill_segments(n_seq, n_tok, n_heads, d_k, d_v, false);
+    if (G > 1) b += 3 * segment_state_bytes(n_seq, n_heads, d_k, d_v, G) + segment_log_bytes(n_seq, n_heads, d_v, G);
+    return b;
 }
 
 template <int DK, int DV, int GATE>
@@ -1106,13 +1144,43 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
                            a.n_tok, a.n_heads, static_cast<int>(mc), arec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((scan_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.alpha, a.S0, a.cu_seqlens,
-                       a.cu_seqlens ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads,
-                       static_cast<uint16_t*>(a.o), a.S_T);
-    return hipGetLastError();
+    auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int ns, float* st,
+                    int flags, float* glog) {
+        const int64_t grid = prefill_grid(static_cast<int64_t>(ns) * a.n_heads, nvb);
+        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(vv), al, s0, a.cu_seqlens,
+                           a.cu_seqlens ? order : nullptr, chunk_off, arec, ns, a.n_tok, a.n_heads,
+                           static_cast<uint16_t*>(a.o), st, flags, glog);
+        return hipGetLastError();
+    };
+    const int G = prefill_segments(a.n_seq, a.n_tok, a.n_heads, DK, DV, a.cu_seqlens != nullptr);
+    if (G == 1) return scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, a.S0, a.n_seq, a.S_T, 0, nullptr);
+
+    // Sequence-parallel path (equal lengths, d_k = d_v, few units): every sequence
+    // is G sequences of len / G tokens, so the chunk numbering -- and the A records
+    // solved above -- stay those of the whole sequences.
+    //   1. dS: each segment's end state from a zero start, and its total log2-decay
+    //      per value row;
+    //   2. M: each segment's key-side transition, from S0 = I with v = 0 and no gate;
+    //   3. the segments' true starting states (and S_T), in order per (sequence, head);
+    //   4. every segment again from its starting state, writing o.
+    // Passes 1 and 2 write o as well; pass 4 overwrites it.
+    const int ns = a.n_seq * G;
+    const size_t off_seg = off_rec + align256(static_cast<size_t>(mc) * a.n_heads * A_RECORD_BYTES);
+    const size_t sb = segment_state_bytes(a.n_seq, a.n_heads, DK, DV, G);
+    float* dS = reinterpret_cast<float*>(ws + off_seg);
+    float* Mt = reinterpret_cast<float*>(ws + off_seg + sb);
+    float* Sst = reinterpret_cast<float*>(ws + off_seg + 2 * sb);
+    float* glog = reinterpret_cast<float*>(ws + off_seg + 3 * sb);
+    if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, nullptr, ns, dS, 0, glog)) != hipSuccess) return e;
+    if ((e = scan(scan_kernel<DK, DK, GATE_NONE>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
+                  SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr)) != hipSuccess)
+        return e;
+    if ((e = launch_combine_segments<DK, DV>(glog, a.S0, dS, Mt, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
+        hipSuccess)
+        return e;
+    return scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, Sst, ns, nullptr, 0, nullptr);
 }
 
 template <int GATE>

@@ -1,0 +1,109 @@
+// kda_segments.hip -- composition of segment states for sequence-parallel
+// prefill of long sequences.
+//
+// Within a chunk the state update is affine in the entering state S (page
+// "Kimi (AI)", section "Kimi Delta Attention (KDA)": the forget gate scales
+// rows, and the predict / update steps act on S from the right):
+//     S' = diag(gamma) S (I - K^T A^T K) + (terms that do not involve S),
+// so over a segment of whole chunks
+//     S_end = diag(Gamma) S_start M + dS,
+// with Gamma the product of the segment's gates (per value row), M the product
+// of the chunks' key-side factors (d_k x d_k, the same for every row), and dS
+// the segment's end state from a zero start.  The prefill computes dS and M for
+// every segment in parallel (two scans), this kernel walks the segments of
+// each (sequence, head) in order to get every segment's true starting state,
+// and a last scan reruns each segment from it.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// One workgroup of 128 threads per (sequence, head, block of rows): a row is
+// d_k / 4 threads of four key channels each (4 rows at d_k = 128, 8 at 64).
+// For segment g = 0 .. G-1 of sequence n:
+//     S_start[n G + g] = S                      (S = S0[n], or zeros, for g = 0)
+//     S = diag(2^{glog_g}) S M_g + dS_g
+// and S_T[n] = S after the last segment.  glog_g is the segment's total
+// log2-decay per value row, written by the scan that produced dS.  M_{g+1} and
+// dS_{g+1} are loaded into registers while segment g is composed, so each step
+// waits only for its own LDS products.
+// Layouts: dS, S_start [n_seq G, H, d_v, d_k]; M [n_seq G, H, d_k, d_k];
+// glog [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
+template <int DK, int DV>
+__global__ __launch_bounds__(128) void combine_segments_kernel(
+    const float* __restrict__ glog, const float* __restrict__ S0, const float* __restrict__ dS,
+    const float* __restrict__ M, int n_seq, int G, int n_heads, float* __restrict__ S_start,
+    float* __restrict__ S_T) {
+    constexpr int NT = 128;
+    constexpr int TPR = DK / 4;       // threads per row
+    constexpr int ROWS = NT / TPR;    // rows per workgroup
+    constexpr int NRB = DV / ROWS;    // row blocks per head
+    constexpr int MP = DK * DK / 4 / NT;  // 16-byte pieces of M per thread
+    static_assert(DV % ROWS == 0, "rows per workgroup");
+    __shared__ __align__(16) float Ms[DK * DK];
+    __shared__ __align__(16) float Ss[ROWS * DK];
+
+    const int b = blockIdx.x;
+    const int rblk = b % NRB, unit = b / NRB;
+    const int h = unit % n_heads, n = unit / n_heads;
+    if (n >= n_seq) return;
+    const int tid = threadIdx.x;
+    const int r = tid / TPR, c4 = 4 * (tid % TPR);
+    const int i = rblk * ROWS + r;  // value row
+    const int64_t H = n_heads;
+    const int64_t row_off = static_cast<int64_t>(i) * DK + c4;
+    auto seg_of = [&](int g) { return static_cast<int64_t>(n) * G + g; };
+
+    f32x4 s = S0 ? *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 mreg[MP], dnext;
+    float lnext;
+    auto load_next = [&](int g) {
+        const int64_t sg = seg_of(g);
+        const float* Mg = M + (sg * H + h) * DK * DK;
+#pragma unroll
+        for (int p = 0; p < MP; ++p) mreg[p] = *reinterpret_cast<const f32x4*>(Mg + 4 * (tid + NT * p));
+        dnext = *reinterpret_cast<const f32x4*>(dS + (sg * H + h) * DV * DK + row_off);
+        lnext = glog[(sg * H + h) * DV + i];
+    };
+    load_next(0);
+    for (int g = 0; g < G; ++g) {
+        *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
+#pragma unroll
+        for (int p = 0; p < MP; ++p) *reinterpret_cast<f32x4*>(Ms + 4 * (tid + NT * p)) = mreg[p];
+        *reinterpret_cast<f32x4*>(Ss + r * DK + c4) = s;
+        const f32x4 d = dnext;
+        const float gam = __builtin_amdgcn_exp2f(lnext);
+        if (g + 1 < G) load_next(g + 1);
+        __syncthreads();
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int k = 0; k < DK; ++k) {
+            const float sk = Ss[r * DK + k];
+            const f32x4 mk = *reinterpret_cast<const f32x4*>(Ms + k * DK + c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += sk * mk[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = gam * acc[e] + d[e];
+        __syncthreads();  // Ms and Ss are rewritten by the next segment
+    }
+    if (S_T) *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
+}
+
+template <int DK, int DV>
+hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M, int n_seq,
+                                   int G, int n_heads, float* S_start, float* S_T, hipStream_t stream) {
+    constexpr int NRB = DV / (128 / (DK / 4));
+    const int64_t grid = static_cast<int64_t>(n_seq) * n_heads * NRB;
+    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(128), 0, stream,
+                       glog, S0, dS, M, n_seq, G, n_heads, S_start, S_T);
+    return hipGetLastError();
+}
+
+template hipError_t launch_combine_segments<128, 128>(const float*, const float*, const float*, const float*, int,
+                                                      int, int, float*, float*, hipStream_t);
+template hipError_t launch_combine_segments<64, 64>(const float*, const float*, const float*, const float*, int, int,
+                                                    int, float*, float*, hipStream_t);
+
+}  // namespace kda

@@ -98,11 +98,65 @@ def test_single_layer_workload(torch_cuda):
 
 
 def test_dense_and_varlen_calls_agree(torch_cuda):
+    """Equal lengths with and without cu_seqlens.  24 units fill few CUs, so the dense
+    call takes the sequence-parallel path (2 segments per sequence) and the varlen call
+    the plain scan: both match the oracle, and each other within the tolerance."""
     inp = I.make_prefill(31, [256, 256, 256], 4, 128, 128, "bf16", "exp_softplus", 0.02)
-    print("prefill dense vs varlen", flush=True)
+    print("prefill dense (sequence-parallel) vs varlen", flush=True)
+    o1, S1 = gpu_prefill(torch_cuda, inp, varlen=False)
+    o2, S2 = gpu_prefill(torch_cuda, inp, varlen=True)
+    check_full(inp, o1, S1)
+    check_full(inp, o2, S2)
+    tol = Hh.TOL_BF16
+    Hh.check("o dense vs varlen", o1, o2, Hh.o_slices(inp.cu_seqlens, inp.H), tol)
+    Hh.check("S_T dense vs varlen", S1, S2, Hh.s_slices(inp.n_seq, inp.H), tol)
+
+
+def test_dense_and_varlen_calls_agree_bit_for_bit(torch_cuda):
+    """When the dense call runs one scan per sequence (enough units: 4 x 32 heads x 2 row
+    blocks), it is the varlen call bit for bit."""
+    inp = I.make_prefill(36, [128, 128, 128, 128], 32, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill dense vs varlen, one scan per sequence", flush=True)
     o1, S1 = gpu_prefill(torch_cuda, inp, varlen=False)
     o2, S2 = gpu_prefill(torch_cuda, inp, varlen=True)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+# Sequence-parallel path: equal-length batches with few (sequence, head) units split
+# every sequence into G segments (dS, M, composition, rerun).  G per case:
+# [1024] x 2 heads at d=128 -> 8; [2048] x 1 head at d=64 -> 16; [512, 512] x 3 -> 4.
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("lens,H,d,s0", [
+    ([1024], 2, 128, 0.02),
+    ([2048], 1, 64, 0.0),
+    ([512, 512], 3, 128, 0.0),
+])
+def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0):
+    from gated_delta_rule_72_amd import kda
+    import oracle
+    print(f"prefill sequence-parallel gate={gate} lens={lens} H={H} d={d} s0={s0}", flush=True)
+    inp = I.make_prefill(3700 + sum(lens) + H + d, lens, H, d, d, "bf16", "exp_softplus", s0, gate)
+    dd = Hh.upload_prefill(inp)
+    fn = kda.kda_prefill if gate == "channel" else kda.kda_prefill_scalar_gate
+    o, S = fn(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S0"], None, n_seq=inp.n_seq)
+    torch_cuda.cuda.synchronize()
+    ref = oracle.prefill if gate == "channel" else oracle.prefill_scalar_gate
+    o_ref, S_ref = ref(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta,
+                       None if inp.S0 is None else inp.S0.astype(np.float64), inp.cu_seqlens)
+    tol = Hh.TOL_BF16
+    Hh.check("o", Hh.from_device(o), o_ref, Hh.o_slices(inp.cu_seqlens, H), tol)
+    Hh.check("S_T", Hh.from_device(S), S_ref, Hh.s_slices(inp.n_seq, H), tol)
+
+
+def test_sequence_parallel_path_in_place_and_no_state(torch_cuda):
+    """On the sequence-parallel path, S_T may alias S0 and may be NULL: same results."""
+    inp = I.make_prefill(3800, [1024], 2, 128, 128, "bf16", "exp_softplus", 0.02)
+    print("prefill sequence-parallel: S_T aliasing S0, and S_T = NULL", flush=True)
+    o1, S1 = gpu_prefill(torch_cuda, inp, varlen=False)
+    o2, S2 = gpu_prefill(torch_cuda, inp, varlen=False, S_T_alias=True)
+    o3, _ = gpu_prefill(torch_cuda, inp, varlen=False, want_state=False)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2) and np.array_equal(o1, o3)
+    check_full(inp, o1, S1)
 
 
 def test_in_place_state_and_no_state(torch_cuda):
