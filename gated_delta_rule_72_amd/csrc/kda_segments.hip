@@ -18,85 +18,109 @@
 
 namespace kda {
 
-// One workgroup of 128 threads per (sequence, head, block of rows): a row is
-// d_k / 4 threads of four key channels each (4 rows at d_k = 128, 8 at 64).
+// One workgroup of 512 threads per (sequence, head, block of rows).  A row's
+// d_k outputs are d_k / 4 column groups of four key channels, and each product
+// S M is split over KS = 4 quarters of the reduction index k, so a thread
+// accumulates 4 columns over d_k / 4 values of k and the quarters are summed
+// through LDS (4 rows per workgroup at d_k = 128, 8 at 64).
 // For segment g = 0 .. G-1 of sequence n:
 //     S_start[n G + g] = S                      (S = S0[n], or zeros, for g = 0)
 //     S = diag(2^{glog_g}) S M_g + dS_g
 // and S_T[n] = S after the last segment.  glog_g is the segment's total
-// log2-decay per value row, written by the scan that produced dS.  M_{g+1} and
-// dS_{g+1} are loaded into registers while segment g is composed, so each step
-// waits only for its own LDS products.
+// log2-decay per value row, written by the scan that produced dS.  M_{g+1},
+// dS_{g+1} and glog_{g+1} are loaded into registers while segment g is
+// composed, so a step waits only for its own LDS products.
 // Layouts: dS, S_start [n_seq G, H, d_v, d_k]; M [n_seq G, H, d_k, d_k];
 // glog [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
 template <int DK, int DV>
-__global__ __launch_bounds__(128) void combine_segments_kernel(
+__global__ __launch_bounds__(512) void combine_segments_kernel(
     const float* __restrict__ glog, const float* __restrict__ S0, const float* __restrict__ dS,
     const float* __restrict__ M, int n_seq, int G, int n_heads, float* __restrict__ S_start,
     float* __restrict__ S_T) {
-    constexpr int NT = 128;
-    constexpr int TPR = DK / 4;       // threads per row
-    constexpr int ROWS = NT / TPR;    // rows per workgroup
-    constexpr int NRB = DV / ROWS;    // row blocks per head
+    constexpr int NT = 512;
+    constexpr int KS = 4;                 // quarters of the reduction index
+    constexpr int CG = DK / 4;            // column groups per row
+    constexpr int ROWS = NT / (CG * KS);  // rows per workgroup
+    constexpr int NRB = DV / ROWS;        // row blocks per head
+    constexpr int KQ = DK / KS;           // values of k per quarter
     constexpr int MP = DK * DK / 4 / NT;  // 16-byte pieces of M per thread
     static_assert(DV % ROWS == 0, "rows per workgroup");
     __shared__ __align__(16) float Ms[DK * DK];
     __shared__ __align__(16) float Ss[ROWS * DK];
+    __shared__ __align__(16) float Ps[KS * ROWS * DK];  // partial sums per quarter
 
     const int b = blockIdx.x;
     const int rblk = b % NRB, unit = b / NRB;
     const int h = unit % n_heads, n = unit / n_heads;
     if (n >= n_seq) return;
     const int tid = threadIdx.x;
-    const int r = tid / TPR, c4 = 4 * (tid % TPR);
+    const int c4 = 4 * (tid % CG), r = (tid / CG) % ROWS, q = tid / (CG * ROWS);
+    const bool owner = q == 0;  // the threads of quarter 0 hold the state
     const int i = rblk * ROWS + r;  // value row
     const int64_t H = n_heads;
     const int64_t row_off = static_cast<int64_t>(i) * DK + c4;
     auto seg_of = [&](int g) { return static_cast<int64_t>(n) * G + g; };
 
-    f32x4 s = S0 ? *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 mreg[MP], dnext;
-    float lnext;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if (owner && S0) s = *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off);
+    f32x4 mreg[MP], dnext = {0.f, 0.f, 0.f, 0.f};
+    float lnext = 0.f;
     auto load_next = [&](int g) {
         const int64_t sg = seg_of(g);
         const float* Mg = M + (sg * H + h) * DK * DK;
 #pragma unroll
         for (int p = 0; p < MP; ++p) mreg[p] = *reinterpret_cast<const f32x4*>(Mg + 4 * (tid + NT * p));
-        dnext = *reinterpret_cast<const f32x4*>(dS + (sg * H + h) * DV * DK + row_off);
-        lnext = glog[(sg * H + h) * DV + i];
+        if (owner) {
+            dnext = *reinterpret_cast<const f32x4*>(dS + (sg * H + h) * DV * DK + row_off);
+            lnext = glog[(sg * H + h) * DV + i];
+        }
     };
     load_next(0);
     for (int g = 0; g < G; ++g) {
-        *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
+        if (owner) {
+            *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
+            *reinterpret_cast<f32x4*>(Ss + r * DK + c4) = s;
+        }
 #pragma unroll
         for (int p = 0; p < MP; ++p) *reinterpret_cast<f32x4*>(Ms + 4 * (tid + NT * p)) = mreg[p];
-        *reinterpret_cast<f32x4*>(Ss + r * DK + c4) = s;
         const f32x4 d = dnext;
         const float gam = __builtin_amdgcn_exp2f(lnext);
         if (g + 1 < G) load_next(g + 1);
         __syncthreads();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-        for (int k = 0; k < DK; ++k) {
+        for (int kk = 0; kk < KQ; ++kk) {
+            const int k = q * KQ + kk;
             const float sk = Ss[r * DK + k];
             const f32x4 mk = *reinterpret_cast<const f32x4*>(Ms + k * DK + c4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] += sk * mk[e];
         }
+        *reinterpret_cast<f32x4*>(Ps + (q * ROWS + r) * DK + c4) = acc;
+        __syncthreads();  // partials complete; Ms and Ss are free for the next segment
+        if (owner) {
+            f32x4 t = *reinterpret_cast<const f32x4*>(Ps + r * DK + c4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = gam * acc[e] + d[e];
-        __syncthreads();  // Ms and Ss are rewritten by the next segment
+            for (int qq = 1; qq < KS; ++qq) {
+                const f32x4 pq = *reinterpret_cast<const f32x4*>(Ps + (qq * ROWS + r) * DK + c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] += pq[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] = gam * t[e] + d[e];
+        }
+        // Ps is rewritten only after the next segment's first barrier, which every
+        // owner reaches after reading it here
     }
-    if (S_T) *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
+    if (owner && S_T) *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
 }
 
 template <int DK, int DV>
 hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M, int n_seq,
                                    int G, int n_heads, float* S_start, float* S_T, hipStream_t stream) {
-    constexpr int NRB = DV / (128 / (DK / 4));
+    constexpr int NRB = DV / (512 / (DK / 4 * 4));
     const int64_t grid = static_cast<int64_t>(n_seq) * n_heads * NRB;
-    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(128), 0, stream,
+    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                        glog, S0, dS, M, n_seq, G, n_heads, S_start, S_T);
     return hipGetLastError();
 }
