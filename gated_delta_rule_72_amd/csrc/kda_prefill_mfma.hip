@@ -544,7 +544,10 @@ __device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16
     lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
 }
 
-template <int DK, int DV, int GATE>
+// SPLIT_S: the state enters K S^T as hi + lo bf16 (two MFMAs per step) instead of
+// one bf16 copy; used where no decay damps that rounding (the segment transitions
+// of the sequence-parallel path, which start from S0 = I).
+template <int DK, int DV, int GATE, bool SPLIT_S = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
@@ -643,6 +646,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
         w[1] = pack_bf16(-R[(ib) * NJ + (2 * m)][2], -R[(ib) * NJ + (2 * m)][3]);
         w[2] = pack_bf16(-R[(ib) * NJ + (2 * m + 1)][0], -R[(ib) * NJ + (2 * m + 1)][1]);
         w[3] = pack_bf16(-R[(ib) * NJ + (2 * m + 1)][2], -R[(ib) * NJ + (2 * m + 1)][3]);
+        return __builtin_bit_cast(bf16x8, w);
+    };
+    // the low half of the hi + lo split of -S (the high half is neg_state)
+    auto neg_state_lo = [&](int ib, int m) {
+        u32x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const f32x4& t = R[(ib) * NJ + (2 * m + (x >> 1))];
+            uint32_t hi, lo;
+            split_bf16x2(-t[2 * (x & 1)], -t[2 * (x & 1) + 1], hi, lo);
+            w[x] = lo;
+        }
         return __builtin_bit_cast(bf16x8, w);
     };
     auto pack_state = [&](int ln) {
@@ -850,6 +865,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     const bf16x8 sb = neg_state(ib, m);
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
+                    if constexpr (SPLIT_S) {
+                        const bf16x8 sl = neg_state_lo(ib, m);
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sl, Y[ib][tt]);
+                    }
                 }
             }
             bf16x8 af[2][4];
@@ -1162,7 +1182,9 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // solved above -- stay those of the whole sequences.
     //   1. dS: each segment's end state from a zero start, and its total log2-decay
     //      per value row;
-    //   2. M: each segment's key-side transition, from S0 = I with v = 0 and no gate;
+    //   2. M: each segment's key-side transition, from S0 = I with v = 0 and no gate,
+    //      the state split hi + lo in K S^T (nothing decays, so its rounding would
+    //      otherwise reach the composed states in full);
     //   3. the segments' true starting states (and S_T), in order per (sequence, head);
     //   4. every segment again from its starting state, writing o.
     // Passes 1 and 2 write o as well; pass 4 overwrites it.
@@ -1174,7 +1196,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     float* Sst = reinterpret_cast<float*>(ws + off_seg + 2 * sb);
     float* glog = reinterpret_cast<float*>(ws + off_seg + 3 * sb);
     if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, nullptr, ns, dS, 0, glog)) != hipSuccess) return e;
-    if ((e = scan(scan_kernel<DK, DK, GATE_NONE>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
+    if ((e = scan(scan_kernel<DK, DK, GATE_NONE, true>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
                   SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr)) != hipSuccess)
         return e;
     if ((e = launch_combine_segments<DK, DV>(glog, a.S0, dS, Mt, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=

@@ -98,10 +98,10 @@ def test_single_layer_workload(torch_cuda):
 
 
 def test_dense_and_varlen_calls_agree(torch_cuda):
-    """Equal lengths with and without cu_seqlens.  24 units fill few CUs, so the dense
-    call takes the sequence-parallel path (2 segments per sequence) and the varlen call
+    """Equal lengths with and without cu_seqlens.  6 units fill few CUs, so the dense
+    call takes the sequence-parallel path (8 segments per sequence) and the varlen call
     the plain scan: both match the oracle, and each other within the tolerance."""
-    inp = I.make_prefill(31, [256, 256, 256], 4, 128, 128, "bf16", "exp_softplus", 0.02)
+    inp = I.make_prefill(31, [1024, 1024, 1024], 1, 128, 128, "bf16", "exp_softplus", 0.02)
     print("prefill dense (sequence-parallel) vs varlen", flush=True)
     o1, S1 = gpu_prefill(torch_cuda, inp, varlen=False)
     o2, S2 = gpu_prefill(torch_cuda, inp, varlen=True)
@@ -124,18 +124,23 @@ def test_dense_and_varlen_calls_agree_bit_for_bit(torch_cuda):
 
 # Sequence-parallel path: equal-length batches with few (sequence, head) units split
 # every sequence into G segments (dS, M, composition, rerun).  G per case:
-# [1024] x 2 heads at d=128 -> 8; [2048] x 1 head at d=64 -> 16; [512, 512] x 3 -> 4.
+# [1024] x 2 heads at d=128 -> 8; [2048] x 1 head at d=64 -> 16; [2048, 2048] x 1 -> 16.
+# With the workloads' gates (alpha ~ 0.93 per token) a segment's start state decays by
+# ~1e-4 over 128 tokens, so the composition through M is also checked with alpha = 1
+# ("ones": no decay), where every segment's start state depends on it in full.
 @pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
-@pytest.mark.parametrize("lens,H,d,s0", [
-    ([1024], 2, 128, 0.02),
-    ([2048], 1, 64, 0.0),
-    ([512, 512], 3, 128, 0.0),
+@pytest.mark.parametrize("lens,H,d,s0,alpha_kind", [
+    ([1024], 2, 128, 0.02, "exp_softplus"),
+    ([2048], 1, 64, 0.0, "exp_softplus"),
+    ([2048, 2048], 1, 128, 0.02, "ones"),
+    ([1024], 2, 64, 0.02, "ones"),
 ])
-def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0):
+def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0, alpha_kind):
     from gated_delta_rule_72_amd import kda
     import oracle
-    print(f"prefill sequence-parallel gate={gate} lens={lens} H={H} d={d} s0={s0}", flush=True)
-    inp = I.make_prefill(3700 + sum(lens) + H + d, lens, H, d, d, "bf16", "exp_softplus", s0, gate)
+    print(f"prefill sequence-parallel gate={gate} lens={lens} H={H} d={d} s0={s0} {alpha_kind}",
+          flush=True)
+    inp = I.make_prefill(3700 + sum(lens) + H + d, lens, H, d, d, "bf16", alpha_kind, s0, gate)
     dd = Hh.upload_prefill(inp)
     fn = kda.kda_prefill if gate == "channel" else kda.kda_prefill_scalar_gate
     o, S = fn(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S0"], None, n_seq=inp.n_seq)
