@@ -17,6 +17,8 @@ single-layer and varlen prefill workloads under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
                        [--no-scalar-gate] [--no-workloads]
+       python bench.py --workloads-only     (only the tiny fp32, single-layer and varlen prefill
+                                             workloads, one JSON line)
        python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
                                              a 1 GiB device copy for calibration, 3 prefill
                                              launches, 3 scalar-gate prefill launches,
@@ -80,6 +82,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-scalar-gate", action="store_true")
     p.add_argument("--no-workloads", action="store_true")
+    p.add_argument("--workloads-only", action="store_true")
     p.add_argument("--traffic-probe", action="store_true")
     p.add_argument("--summarize", default=None)
     return p.parse_args()
@@ -449,6 +452,9 @@ def main():
     from gated_delta_rule_72_amd import kda
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kda.lib()
+    if args.workloads_only:
+        print(json.dumps(dict(workloads=bench_other_workloads(args, torch, kda, I))), flush=True)
+        return
     pre, inp, o, S_T = bench_prefill(args, torch, kda, I)
     log(f"[bench] prefill: {pre['tokens_per_s']:.4g} tokens/s, kernel {pre['launch_ms']['avg']:.3f} ms")
     line = dict(
