@@ -51,19 +51,19 @@ struct PrefillArgs {
 constexpr int PREFILL_CHUNK_BF16 = 64;
 
 // Segments per sequence for the sequence-parallel bf16 prefill (1 = one scan
-// per sequence).  Equal-length batches whose (sequence, head, 64-row block)
-// units would leave most of the 256 CUs idle have each sequence split into G
-// segments of whole 64-token chunks (G a power of two, at least two chunks per
-// segment, units x G at most 256 workgroups).  Each segment is scanned three
+// per sequence).  Calls whose (sequence, head, 64-row block) units would leave
+// most of the 256 CUs idle have each sequence cut into G segments of whole
+// 64-token chunks (G a power of two, units x G at most 256 workgroups, on
+// average at least two chunks per segment).  Each segment is scanned three
 // times, so the split pays only from G = 8 on (measured: G = 2 is 1.7x slower
-// than one scan, G = 4 about even, G >= 8 faster).  Needs d_k = d_v.
-inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v,
-                            bool varlen) {
-    if (varlen || d_k != d_v || n_tok <= 0 || n_seq < 1) return 1;
+// than one scan, G = 4 about even, G >= 8 faster).  Needs d_k = d_v.  Decided
+// from the sizes alone (the host never reads cu_seqlens).
+inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    if (d_k != d_v || n_tok <= 0 || n_seq < 1) return 1;
     const int64_t units = static_cast<int64_t>(n_seq) * n_heads * (d_v / 64);
-    const int64_t len = n_tok / n_seq;
+    const int64_t avg = n_tok / n_seq;
     int g = 1;
-    while (units * 2 * g <= 256 && len % (64 * 2 * g) == 0 && len / (2 * g) >= 2 * 64) g *= 2;
+    while (units * 2 * g <= 256 && avg / (2 * g) >= 2 * 64) g *= 2;
     return g >= 8 ? g : 1;
 }
 

@@ -197,6 +197,24 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
 }
 
 // ============================================================================
+// segment_cu_kernel: the token offsets of the segments of the sequence-parallel
+// prefill.  Sequence n (tokens s0 .. s1-1, c = ceil((s1 - s0) / C) chunks) becomes
+// G segments of ceil(c / G) whole chunks each (the last ones shorter or empty):
+// cu_seg[n G + g] = min(s0 + g ceil(c / G) C, s1) and cu_seg[n_seq G] = n_tok.
+// One thread per sequence.
+// ============================================================================
+__global__ __launch_bounds__(256) void segment_cu_kernel(const int32_t* __restrict__ cu, int n_seq, int n_tok,
+                                                         int G, int32_t* __restrict__ cu_seg) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= n_seq) return;
+    const int64_t s0 = seq_start(n, n_seq, n_tok, cu), s1 = seq_start(n + 1, n_seq, n_tok, cu);
+    const int64_t per = ((s1 - s0 + C - 1) / C + G - 1) / G;  // chunks per segment
+    for (int g = 0; g < G; ++g)
+        cu_seg[static_cast<int64_t>(n) * G + g] = static_cast<int32_t>(min<int64_t>(s0 + g * per * C, s1));
+    if (n == n_seq - 1) cu_seg[static_cast<int64_t>(n_seq) * G] = static_cast<int32_t>(s1);
+}
+
+// ============================================================================
 // chunk_solve_kernel: A = (I + L)^{-1} diag(beta) of every (chunk, head), each
 // written as the A record described above.  Workgroups of 4 waves loop over the
 // (chunk, head) items, four per CU, loading the next item's K and beta while
@@ -1106,11 +1124,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-// Workspace of the bf16 path, each part 256-byte aligned:
-//   order      n_seq int32 (longest-first schedule; varlen only)
-//   chunk_off  n_seq + 1 int32
-//   A records  (n_tok / C + n_seq) x n_heads x A_RECORD_BYTES (an upper bound
-//              on the number of chunks times heads)
+// A records: (n_tok / C + n_seq) bounds the number of chunks of any split of
+// n_tok tokens into n_seq sequences.
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 static int64_t chunk_bound(int32_t n_seq, int32_t n_tok) { return static_cast<int64_t>(n_tok) / C + n_seq; }
@@ -1125,61 +1140,95 @@ static size_t segment_log_bytes(int32_t n_seq, int32_t n_heads, int32_t d_v, int
     return align256(static_cast<size_t>(n_seq) * G * n_heads * static_cast<size_t>(d_v) * 4);
 }
 
+// Workspace layout of the bf16 path (each part 256-byte aligned; NS = n_seq G
+// sequences when the call is split into G segments per sequence, else n_seq):
+//   order      NS int32      longest-first schedule (packed input)
+//   chunk_off  NS + 1 int32  first chunk of every sequence (packed input)
+//   cu_seg     NS + 1 int32  segment token offsets (split calls only)
+//   A records  (n_tok / C + n_seq) x n_heads x A_RECORD_BYTES
+//   dS, M, S_start, glog     segment states (split calls only)
+struct Bf16Layout {
+    size_t order, chunk_off, cu_seg, rec, seg, total;
+};
+
+static Bf16Layout bf16_layout(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    const int G = prefill_segments(n_seq, n_tok, n_heads, d_k, d_v);
+    const size_t ns = static_cast<size_t>(n_seq) * G;
+    Bf16Layout L;
+    L.order = 0;
+    L.chunk_off = L.order + align256(ns * 4);
+    L.cu_seg = L.chunk_off + align256((ns + 1) * 4);
+    L.rec = L.cu_seg + (G > 1 ? align256((ns + 1) * 4) : 0);
+    L.seg = L.rec + align256(static_cast<size_t>(chunk_bound(n_seq, n_tok)) * n_heads * A_RECORD_BYTES);
+    L.total = L.seg;
+    if (G > 1) L.total += 3 * segment_state_bytes(n_seq, n_heads, d_k, d_v, G) + segment_log_bytes(n_seq, n_heads, d_v, G);
+    return L;
+}
+
 size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
-    size_t b = align256(static_cast<size_t>(n_seq) * 4) + align256((static_cast<size_t>(n_seq) + 1) * 4) +
-               align256(static_cast<size_t>(chunk_bound(n_seq, n_tok)) * static_cast<size_t>(n_heads) * A_RECORD_BYTES);
-    // the sequence-parallel path is taken only without cu_seqlens; the workspace
-    // size does not know whether cu_seqlens will be given, so it covers that case
-    const int G = prefill_segments(n_seq, n_tok, n_heads, d_k, d_v, false);
-    if (G > 1) b += 3 * segment_state_bytes(n_seq, n_heads, d_k, d_v, G) + segment_log_bytes(n_seq, n_heads, d_v, G);
-    return b;
+    return bf16_layout(n_seq, n_tok, n_heads, d_k, d_v).total;
 }
 
 template <int DK, int DV, int GATE>
 static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int NVB = DV / BV;
+    const Bf16Layout L = bf16_layout(a.n_seq, a.n_tok, a.n_heads, DK, DV);
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-    const size_t off_chunk = align256(static_cast<size_t>(a.n_seq) * 4);
-    const size_t off_rec = off_chunk + align256((static_cast<size_t>(a.n_seq) + 1) * 4);
-    int32_t* order = reinterpret_cast<int32_t*>(ws);
-    int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + off_chunk);
-    uint16_t* arec = reinterpret_cast<uint16_t*>(ws + off_rec);
+    int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+    uint16_t* arec = reinterpret_cast<uint16_t*>(ws + L.rec);
+    const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
     hipError_t e;
-    if (a.cu_seqlens) {
-        if ((e = launch_schedule(a.cu_seqlens, a.n_seq, order, stream)) != hipSuccess) return e;
-        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.n_seq, a.n_tok,
-                           chunk_off);
+
+    // How the sequences are cut (G = 1: one scan per sequence).  A split call whose
+    // sequences all have the same length, a multiple of G chunks, keeps the dense
+    // form: n_seq G sequences of len / G tokens, offsets computed in the kernels.
+    // Any other split call describes its segments by token offsets built on the
+    // device (cu_seg), so packed input and ragged lengths are split the same way.
+    // Segments end on chunk boundaries, so in both forms the chunks -- and the A
+    // records solved below -- are those of the whole sequences, in the same order.
+    const int G = prefill_segments(a.n_seq, a.n_tok, a.n_heads, DK, DV);
+    const int ns = a.n_seq * G;
+    const bool dense = !a.cu_seqlens && (G == 1 || (a.n_tok / a.n_seq) % (C * G) == 0);
+    const int32_t* cu = a.cu_seqlens;
+    if (G > 1 && !dense) {
+        int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + L.cu_seg);
+        hipLaunchKernelGGL(segment_cu_kernel, dim3((a.n_seq + 255) / 256), dim3(256), 0, stream, a.cu_seqlens,
+                           a.n_seq, a.n_tok, G, cu_seg);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        cu = cu_seg;
+    }
+    const int nseq_eff = cu && G > 1 ? ns : a.n_seq;  // sequences as the kernels see them
+    if (cu) {
+        if ((e = launch_schedule(cu, nseq_eff, order, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, cu, nseq_eff, a.n_tok, chunk_off);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
         chunk_off = nullptr;  // equal lengths: the kernels compute the offsets
     }
-    const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
     if (a.n_tok > 0) {
         // as many workgroups as stay resident (four per CU); each loops over items
         int dev = 0, n_cu = 0;
         if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         const int64_t grid = std::min<int64_t>(mc * a.n_heads, 4 * static_cast<int64_t>(n_cu));
-        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, static_cast<const uint16_t*>(a.k), a.beta, a.cu_seqlens, chunk_off, a.n_seq,
-                           a.n_tok, a.n_heads, static_cast<int>(mc), arec);
+        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok, a.n_heads,
+                           static_cast<int>(mc), arec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int ns, float* st,
+    auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int nsq, float* st,
                     int flags, float* glog) {
-        const int64_t grid = prefill_grid(static_cast<int64_t>(ns) * a.n_heads, nvb);
+        const int64_t grid = prefill_grid(static_cast<int64_t>(nsq) * a.n_heads, nvb);
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(vv), al, s0, a.cu_seqlens,
-                           a.cu_seqlens ? order : nullptr, chunk_off, arec, ns, a.n_tok, a.n_heads,
-                           static_cast<uint16_t*>(a.o), st, flags, glog);
+                           static_cast<const uint16_t*>(vv), al, s0, cu, cu ? order : nullptr, chunk_off, arec, nsq,
+                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog);
         return hipGetLastError();
     };
-    const int G = prefill_segments(a.n_seq, a.n_tok, a.n_heads, DK, DV, a.cu_seqlens != nullptr);
     if (G == 1) return scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, a.S0, a.n_seq, a.S_T, 0, nullptr);
 
-    // Sequence-parallel path (equal lengths, d_k = d_v, few units): every sequence
-    // is G sequences of len / G tokens, so the chunk numbering -- and the A records
-    // solved above -- stay those of the whole sequences.
+    // Sequence-parallel path (d_k = d_v, few units, long sequences):
     //   1. dS: each segment's end state from a zero start, and its total log2-decay
     //      per value row;
     //   2. M: each segment's key-side transition, from S0 = I with v = 0 and no gate,
@@ -1187,14 +1236,13 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     //      otherwise reach the composed states in full);
     //   3. the segments' true starting states (and S_T), in order per (sequence, head);
     //   4. every segment again from its starting state, writing o.
-    // Passes 1 and 2 write o as well; pass 4 overwrites it.
-    const int ns = a.n_seq * G;
-    const size_t off_seg = off_rec + align256(static_cast<size_t>(mc) * a.n_heads * A_RECORD_BYTES);
+    // Passes 1 and 2 write o as well; pass 4 overwrites it.  An empty segment has
+    // dS = 0, M = I and no decay.
     const size_t sb = segment_state_bytes(a.n_seq, a.n_heads, DK, DV, G);
-    float* dS = reinterpret_cast<float*>(ws + off_seg);
-    float* Mt = reinterpret_cast<float*>(ws + off_seg + sb);
-    float* Sst = reinterpret_cast<float*>(ws + off_seg + 2 * sb);
-    float* glog = reinterpret_cast<float*>(ws + off_seg + 3 * sb);
+    float* dS = reinterpret_cast<float*>(ws + L.seg);
+    float* Mt = reinterpret_cast<float*>(ws + L.seg + sb);
+    float* Sst = reinterpret_cast<float*>(ws + L.seg + 2 * sb);
+    float* glog = reinterpret_cast<float*>(ws + L.seg + 3 * sb);
     if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, nullptr, ns, dS, 0, glog)) != hipSuccess) return e;
     if ((e = scan(scan_kernel<DK, DK, GATE_NONE, true>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
                   SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr)) != hipSuccess)

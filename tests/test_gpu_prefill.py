@@ -153,6 +153,23 @@ def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0,
     Hh.check("S_T", Hh.from_device(S), S_ref, Hh.s_slices(inp.n_seq, H), tol)
 
 
+# Split calls that are not equal multiples of G chunks describe their segments by token
+# offsets built on the device: a ragged dense sequence (2100 tokens = 33 chunks, the last
+# partial, 2 heads: G = 16 segments of 3 chunks, the last 5 empty) and packed sequences
+# (G = 8; 77 tokens fill 2 of their 8 segments, and the empty sequence none).
+@pytest.mark.parametrize("alpha_kind", ["exp_softplus", "ones"])
+@pytest.mark.parametrize("lens,H,varlen", [
+    ([2100], 2, False),
+    ([3000, 0, 1500, 77], 2, True),
+])
+def test_sequence_parallel_path_ragged_and_packed(torch_cuda, lens, H, varlen, alpha_kind):
+    print(f"prefill sequence-parallel (segment offsets) lens={lens} H={H} varlen={varlen} {alpha_kind}",
+          flush=True)
+    inp = I.make_prefill(3900 + sum(lens) + H, lens, H, 128, 128, "bf16", alpha_kind, 0.02)
+    o, S = gpu_prefill(torch_cuda, inp, varlen=varlen)
+    check_full(inp, o, S)
+
+
 def test_sequence_parallel_path_in_place_and_no_state(torch_cuda):
     """On the sequence-parallel path, S_T may alias S0 and may be NULL: same results."""
     inp = I.make_prefill(3800, [1024], 2, 128, 128, "bf16", "exp_softplus", 0.02)
@@ -235,9 +252,9 @@ def test_varlen_workload_sampled(torch_cuda):
 
 
 def test_long_sequence_sampled(torch_cuda):
-    """One sequence of 65,573 tokens (1,025 chunks, a ragged last chunk): the state
-    crosses a thousand chunk boundaries in fp32 registers, and token offsets run
-    past 2^16 rows."""
+    """One sequence of 65,573 tokens (1,025 chunks, a ragged last chunk), 4 heads: the
+    call is split into 32 segments of 33 chunks (the last of 2) by token offsets built on
+    the device; token offsets run past 2^16 rows."""
     T = 65536 + 37
     inp = I.make_prefill(35, [T], 4, 128, 128, "bf16", "exp_softplus", 0.02)
     print(f"prefill one sequence of {T} tokens, H=4, sampled oracle", flush=True)
