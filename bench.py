@@ -384,19 +384,24 @@ def workload_parity(inp, o_gpu, S_gpu, pairs=None):
 
 def bench_other_workloads(args, torch, kda, I):
     """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
-    other prefill shapes).  Each: inputs resident in HBM, settled clocks, the mean of
-    `steps` calls from HIP events; parity of the last call against the oracle (every
-    pair for the two small workloads, three sampled pairs of the varlen one)."""
+    other prefill shapes) and on one long ragged sequence.  Each: inputs resident in HBM,
+    settled clocks, the mean of `steps` calls from HIP events; parity of the last call
+    against the oracle (every pair for the two small workloads, sampled pairs of the
+    others)."""
     dev = "cuda:0"
     out = {}
-    for wid in (1, 2, 5):
-        w = I.WORKLOADS[wid]
-        inp = I.workload_prefill(wid)
+    # the three prefill workloads, and one long sequence of ragged length (65,573 tokens,
+    # 4 heads, the batched workload's distributions), which the library splits into
+    # segments scanned in parallel
+    cases = [(I.WORKLOADS[wid]["name"], lambda wid=wid: I.workload_prefill(wid), wid == 5) for wid in (1, 2, 5)]
+    cases.append(("long_sequence", lambda: I.make_prefill(72006, [65573], 4, 128, 128, "bf16", "exp_softplus", 0.02),
+                  False))
+    for name, make, varlen in cases:
+        inp = make()
         dt = inp.dtype
         q, k, v = (upload(getattr(inp, n), dt, dev) for n in ("q", "k", "v"))
         alpha, beta = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev)
         S0 = None if inp.S0 is None else upload(inp.S0, "f32", dev)
-        varlen = wid == 5
         cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev) if varlen else None
         n_tok, H, dk, dv, n_seq = inp.n_tok, inp.H, inp.dk, inp.dv, inp.n_seq
         o = torch.empty((n_tok, H, dv), dtype=q.dtype, device=dev)
@@ -421,14 +426,14 @@ def bench_other_workloads(args, torch, kda, I):
         head_tokens = n_tok * H
         alg = head_tokens * per_ht + (2 if S0 is not None else 1) * n_seq * H * dv * dk * 4
         gbs = alg / (ms * 1e-3) / 1e9
-        out[w["name"]] = dict(
+        out[name] = dict(
             shape=(f"{n_seq} sequences, {n_tok} tokens, H={H}, d_k={dk}, d_v={dv}, {dt}"
                    + (", lengths U{256..16384}, cu_seqlens" if varlen else "")),
             ms_per_call=round(ms, 4), tokens_per_s=round(n_tok / (ms * 1e-3), 1),
             alg_bytes=int(alg), achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
             parity=workload_parity(inp, o, S_T, [(0, 0), (n_seq // 2, H // 2), (n_seq - 1, H - 1)]
-                                   if varlen else None))
-        log(f"[bench] {w['name']}: {ms:.4f} ms per call, {n_tok / (ms * 1e-3):.4g} tokens/s, "
+                                   if varlen else [(0, 0)] if name == "long_sequence" else None))
+        log(f"[bench] {name}: {ms:.4f} ms per call, {n_tok / (ms * 1e-3):.4g} tokens/s, "
             f"{gbs / HBM_PEAK_GBS:.3f} of HBM")
         del q, k, v, alpha, beta, S0, cu, o, S_T, ws, inp
         torch.cuda.empty_cache()
