@@ -25,8 +25,10 @@
 // the workspace as hi/lo bf16.  scan_kernel then walks each sequence chunk by
 // chunk with only the S-dependent products on its critical path: one
 // workgroup of 8 waves per (sequence, head, block of 64 value rows) holds S^T
-// in fp32 MFMA accumulators for the whole scan, with four workgroup barriers
-// per chunk.
+// in fp32 MFMA accumulators for the whole scan, with three workgroup barriers
+// per chunk.  Calls with few (sequence, head) units cut every sequence into
+// segments that the same scan runs in parallel, composed in between
+// (kda_segments.hip; the launcher at the end of this file).
 //
 // Precision: q, k, v are exact bf16 inputs.  Computed operands are carried as
 // hi + lo bf16 pairs (x = hi + lo to ~2^-16 relative) where the error budget
