@@ -375,3 +375,26 @@ def test_rejects_malformed_cu_seqlens():
         oracle.prefill(q, k, v, a, b, None, np.array([0, 3, 5]))
     with pytest.raises(RuntimeError):
         oracle.prefill(q, k, v, a, b, None, np.array([0, 4, 2, 6]))
+
+
+def test_segment_composition_identity():
+    """The update is affine in the entering state, with the gate on the left (rows) and
+    a key-side factor on the right: over any run of tokens
+        S_end = diag(Gamma) S_start M + dS,
+    where Gamma is the product of the gates per row, M is what the recurrence makes of
+    S_start = I with v = 0 and no gate, and dS is the run from S_start = 0.  Composing
+    the runs of consecutive segments reproduces the whole sequence (the identity the
+    sequence-parallel prefill relies on), for uneven segment lengths."""
+    rng = np.random.default_rng(16)
+    T, dk, dv = 23, 5, 5
+    q, k, v, a, b, S0 = rand_case(rng, T, 1, dk, dv)
+    _, S_whole = oracle.prefill(q, k, v, a, b, S0)
+    S = S0[0, 0].copy()
+    for s, e in ((0, 7), (7, 8), (8, 19), (19, 23)):
+        sl = slice(s, e)
+        _, dS = oracle.prefill(q[sl], k[sl], v[sl], a[sl], b[sl], None)
+        _, M = oracle.prefill(q[sl], k[sl], np.zeros_like(v[sl]), np.ones_like(a[sl]), b[sl],
+                              np.eye(dk)[None, None])
+        gamma = np.prod(d64(a[sl, 0]), axis=0)
+        S = gamma[:, None] * (S @ M[0, 0]) + dS[0, 0]
+    np.testing.assert_allclose(S, S_whole[0, 0], rtol=0, atol=1e-12)
