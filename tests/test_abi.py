@@ -55,6 +55,38 @@ def test_workspace_size(L):
     assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
 
 
+def test_workspace_size_of_split_calls(L):
+    """Calls with few (sequence, head) units are split into G segments per sequence
+    (G >= 8, units x G <= 256, on average two chunks or more per segment); their
+    workspace adds the segment bookkeeping and states.  Layout, 256-byte aligned parts:
+    order NS int32, chunk offsets NS+1, segment offsets NS+1 (split calls only),
+    A records (n_tok/64 + n_seq) x H x 12 KiB, then dS, M, S_start (NS x H x d x d fp32
+    each) and the log2-decays (NS x H x d fp32), NS = n_seq G."""
+    al = lambda x: (x + 255) // 256 * 256
+    rec = 3 * 2 * 32 * 32 * 2
+
+    def split_size(n_seq, n_tok, H, d, G):
+        ns = n_seq * G
+        return (al(ns * 4) + al((ns + 1) * 4) + al((ns + 1) * 4) + al((n_tok // 64 + n_seq) * H * rec)
+                + 3 * ns * H * d * d * 4 + al(ns * H * d * 4))
+
+    # one 4096-token sequence, 8 heads, d = 128: 16 units -> G = 16
+    assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 128, 1) == split_size(1, 4096, 8, 128, 16)
+    # 65,573 tokens, 4 heads: 8 units -> G = 32
+    assert L.kda_prefill_workspace_size(1, 65573, 4, 128, 128, 1) == split_size(1, 65573, 4, 128, 32)
+    # d = 64, one head: 1 unit, 2048 tokens -> G = 16
+    assert L.kda_prefill_workspace_size(1, 2048, 1, 64, 64, 1) == split_size(1, 2048, 1, 64, 16)
+    # not split: 256 units (the batched workload), G < 8 (two sequences of 8192 tokens,
+    # 32 heads), segments too short (512 tokens, 8 heads: G would be 4), d_k != d_v, fp32
+    unsplit = lambda n_seq, n_tok, H: al(n_seq * 4) + al((n_seq + 1) * 4) + al((n_tok // 64 + n_seq) * H * rec)
+    assert L.kda_prefill_workspace_size(4, 32768, 32, 128, 128, 1) == unsplit(4, 32768, 32)
+    assert L.kda_prefill_workspace_size(2, 16384, 32, 128, 128, 1) == unsplit(2, 16384, 32)
+    assert L.kda_prefill_workspace_size(1, 512, 8, 128, 128, 1) == unsplit(1, 512, 8)
+    assert L.kda_prefill_workspace_size(1, 1024, 8, 128, 128, 1) == split_size(1, 1024, 8, 128, 8)
+    assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 64, 1) == unsplit(1, 4096, 8)
+    assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 128, 0) == 256
+
+
 def prefill(L, fn="kda_prefill", **kw):
     args = dict(q=A, k=A + 0x100000, v=A + 0x200000, alpha=A + 0x300000, beta=A + 0x400000,
                 S0=None, cu=None, n_seq=2, n_tok=64, H=2, dk=64, dv=64, dt=1,
