@@ -52,6 +52,10 @@ def _load():
     lib.kda_oracle_decode_f64.argtypes = [f32p, f32p, f32p, f32p, f32p,
                                           i64, i64, i64, i64, i64, f64p, f64p]
     lib.kda_oracle_decode_f64.restype = ctypes.c_int
+    lib.kda_oracle_prefill_keygate_f64.argtypes = lib.kda_oracle_prefill_f64.argtypes
+    lib.kda_oracle_prefill_keygate_f64.restype = ctypes.c_int
+    lib.kda_oracle_decode_keygate_f64.argtypes = lib.kda_oracle_decode_f64.argtypes
+    lib.kda_oracle_decode_keygate_f64.restype = ctypes.c_int
     lib.kda_oracle_abi_version.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -68,7 +72,7 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
+def prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True, _key_gate=False):
     """Run the recurrence over packed sequences.
 
     q, k: [n_tok, H, d_k]; v, alpha: [n_tok, H, d_v]; beta: [n_tok, H]
@@ -90,7 +94,7 @@ def prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
     q = _f32(q, (n_tok, H, dk))
     k = _f32(k, (n_tok, H, dk))
     v = _f32(v, (n_tok, H, dv))
-    alpha = _f32(alpha, (n_tok, H, dv))
+    alpha = _f32(alpha, (n_tok, H, dk if _key_gate else dv))
     beta = _f32(beta, (n_tok, H))
     s0 = None
     if S0 is not None:
@@ -100,7 +104,8 @@ def prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
     o = np.empty((n_tok, H, dv), dtype=np.float64) if want_o else None
     ST = np.empty((n_seq, H, dv, dk), dtype=np.float64)
     lib = _load()
-    rc = lib.kda_oracle_prefill_f64(
+    fn = lib.kda_oracle_prefill_keygate_f64 if _key_gate else lib.kda_oracle_prefill_f64
+    rc = fn(
         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
         _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
         None if s0 is None else _ptr(s0, ctypes.c_double), _ptr(cu, ctypes.c_int64),
@@ -111,7 +116,7 @@ def prefill(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
     return o, ST
 
 
-def decode(q, k, v, alpha, beta, S, want_o=True):
+def decode(q, k, v, alpha, beta, S, want_o=True, _key_gate=False):
     """Run n_steps single-token steps from state S (not modified; a copy is returned).
 
     q, k: [n_steps, B, H, d_k]; v, alpha: [n_steps, B, H, d_v]; beta: [n_steps, B, H]
@@ -123,14 +128,15 @@ def decode(q, k, v, alpha, beta, S, want_o=True):
     q = _f32(q)
     k = _f32(k, q.shape)
     v = _f32(v, (n_steps, B, H, dv))
-    alpha = _f32(alpha, (n_steps, B, H, dv))
+    alpha = _f32(alpha, (n_steps, B, H, dk if _key_gate else dv))
     beta = _f32(beta, (n_steps, B, H))
     Sn = np.array(S, dtype=np.float64, copy=True, order="C")
     if Sn.shape != (B, H, dv, dk):
         raise ValueError("S must be [B, H, d_v, d_k]")
     o = np.empty((n_steps, B, H, dv), dtype=np.float64) if want_o else None
     lib = _load()
-    rc = lib.kda_oracle_decode_f64(
+    fn = lib.kda_oracle_decode_keygate_f64 if _key_gate else lib.kda_oracle_decode_f64
+    rc = fn(
         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
         _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
         n_steps, B, H, dk, dv, _ptr(Sn, ctypes.c_double),
@@ -166,4 +172,19 @@ def decode_scalar_gate(q, k, v, alpha, beta, S, want_o=True):
     """decode() with alpha [n_steps, B, H] (one gate per step, sequence and head), or None."""
     v = np.asarray(v)
     return decode(q, k, v, _rows(alpha, v.shape[:3], v.shape[3]), beta, S, want_o)
+
+
+# ------------------------------------------------------- key-channel gate ---
+# The forget gate acting on the key side, S~ = S diag(alpha_t) with alpha_t in
+# R^{d_k}: the reading of the forget-gating step under which the decay falls on
+# key channels; the row form above is the one the section's equations write.
+
+def prefill_key_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, want_o=True):
+    """prefill() with alpha [n_tok, H, d_k] scaling the columns (key channels) of S."""
+    return prefill(q, k, v, alpha, beta, S0, cu_seqlens, want_o, _key_gate=True)
+
+
+def decode_key_gate(q, k, v, alpha, beta, S, want_o=True):
+    """decode() with alpha [n_steps, B, H, d_k] scaling the columns (key channels) of S."""
+    return decode(q, k, v, alpha, beta, S, want_o, _key_gate=True)
 

@@ -16,6 +16,12 @@
  *   - the read-out of the linear-attention equation, o_t = S_t q_t, taken
  *     with the post-update state (the state that already holds token t).
  *
+ * A second form, the key-channel variant, gates the state from the right,
+ * S~ = S diag(alpha_t) with alpha_t in R^{d_k} (column j scaled by
+ * alpha_t[j]); predict, update and read-out are the same.  It is the reading of
+ * the forget-gating step with the gate acting on the key side; the row form
+ * above is the one the section's equations write.
+ *
  * Everything is a plain sequential loop over tokens in double precision.
  * Independent (sequence, head) pairs are the only thing run in parallel
  * (OpenMP); within a pair nothing is blocked, fused or reordered.
@@ -40,10 +46,11 @@ int kda_oracle_abi_version(void) { return 1; }
  * axis through the recurrence, starting from S (d_v x d_k, row-major, double),
  * which is updated in place.  Token t of the unit has
  *   q at q + t*q_stride, k at k + t*k_stride   (d_k floats each),
- *   v at v + t*v_stride, alpha at a + t*a_stride (d_v floats each),
+ *   v at v + t*v_stride (d_v floats), alpha at a + t*a_stride (d_v floats, or
+ *   d_k floats when key_gate is set),
  *   beta at beta[t*b_stride], output o + t*o_stride (d_v doubles).
  */
-static void kda_unit(int64_t len, int64_t dk, int64_t dv,
+static void kda_unit(int key_gate, int64_t len, int64_t dk, int64_t dv,
                      const float* q, int64_t q_stride,
                      const float* k, int64_t k_stride,
                      const float* v, int64_t v_stride,
@@ -60,11 +67,19 @@ static void kda_unit(int64_t len, int64_t dk, int64_t dv,
         const double bt = (double)beta[t * b_stride];
         double* ot = o ? o + t * o_stride : NULL;
 
-        /* forget gating: S~ = diag(alpha_t) S_{t-1} -- row i scaled by alpha_t[i] */
-        for (int64_t i = 0; i < dv; ++i) {
-            const double ai = (double)at[i];
-            double* Si = S + i * dk;
-            for (int64_t j = 0; j < dk; ++j) Si[j] *= ai;
+        if (key_gate) {
+            /* forget gating, key-channel form: S~ = S_{t-1} diag(alpha_t) -- column j scaled by alpha_t[j] */
+            for (int64_t i = 0; i < dv; ++i) {
+                double* Si = S + i * dk;
+                for (int64_t j = 0; j < dk; ++j) Si[j] *= (double)at[j];
+            }
+        } else {
+            /* forget gating: S~ = diag(alpha_t) S_{t-1} -- row i scaled by alpha_t[i] */
+            for (int64_t i = 0; i < dv; ++i) {
+                const double ai = (double)at[i];
+                double* Si = S + i * dk;
+                for (int64_t j = 0; j < dk; ++j) Si[j] *= ai;
+            }
         }
         /* predict: v~ = S~ k_t */
         for (int64_t i = 0; i < dv; ++i) {
@@ -106,12 +121,13 @@ static void kda_unit(int64_t len, int64_t dk, int64_t dv,
  *   S_T       [n_seq, H, d_v, d_k] double
  * An empty sequence leaves S_T = S0 (or zeros).  Returns 0 on success.
  */
-int kda_oracle_prefill_f64(const float* q, const float* k, const float* v,
-                           const float* alpha, const float* beta,
-                           const double* S0, const int64_t* cu_seqlens,
-                           int64_t n_seq, int64_t H, int64_t dk, int64_t dv,
-                           double* o, double* S_T)
+static int prefill_f64(int key_gate, const float* q, const float* k, const float* v,
+                       const float* alpha, const float* beta,
+                       const double* S0, const int64_t* cu_seqlens,
+                       int64_t n_seq, int64_t H, int64_t dk, int64_t dv,
+                       double* o, double* S_T)
 {
+    const int64_t da = key_gate ? dk : dv; /* gate values per (token, head) */
     if (!q || !k || !v || !alpha || !beta || !cu_seqlens || !S_T) return KDA_ORACLE_BAD_ARG;
     if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ORACLE_BAD_ARG;
     if (cu_seqlens[0] != 0) return KDA_ORACLE_BAD_ARG;
@@ -140,11 +156,11 @@ int kda_oracle_prefill_f64(const float* q, const float* k, const float* v,
                 } else {
                     memset(S, 0, (size_t)(dv * dk) * sizeof(double));
                 }
-                kda_unit(len, dk, dv,
+                kda_unit(key_gate, len, dk, dv,
                          q + (t0 * H + h) * dk, H * dk,
                          k + (t0 * H + h) * dk, H * dk,
                          v + (t0 * H + h) * dv, H * dv,
-                         alpha + (t0 * H + h) * dv, H * dv,
+                         alpha + (t0 * H + h) * da, H * da,
                          beta + t0 * H + h, H,
                          S, o ? o + (t0 * H + h) * dv : NULL, H * dv, vp, e);
             }
@@ -153,6 +169,25 @@ int kda_oracle_prefill_f64(const float* q, const float* k, const float* v,
         free(e);
     }
     return failed ? KDA_ORACLE_NO_MEMORY : KDA_ORACLE_OK;
+}
+
+int kda_oracle_prefill_f64(const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta,
+                           const double* S0, const int64_t* cu_seqlens,
+                           int64_t n_seq, int64_t H, int64_t dk, int64_t dv,
+                           double* o, double* S_T)
+{
+    return prefill_f64(0, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, H, dk, dv, o, S_T);
+}
+
+/* The key-channel form: alpha is [n_tok, H, d_k]; everything else as above. */
+int kda_oracle_prefill_keygate_f64(const float* q, const float* k, const float* v,
+                                   const float* alpha, const float* beta,
+                                   const double* S0, const int64_t* cu_seqlens,
+                                   int64_t n_seq, int64_t H, int64_t dk, int64_t dv,
+                                   double* o, double* S_T)
+{
+    return prefill_f64(1, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, H, dk, dv, o, S_T);
 }
 
 /*
@@ -165,11 +200,12 @@ int kda_oracle_prefill_f64(const float* q, const float* k, const float* v,
  *   o        [n_steps, B, H, d_v]   double (may be NULL)
  * Steps run innermost per (b, h), so each head's state stays in cache.
  */
-int kda_oracle_decode_f64(const float* q, const float* k, const float* v,
-                          const float* alpha, const float* beta,
-                          int64_t n_steps, int64_t B, int64_t H, int64_t dk, int64_t dv,
-                          double* S, double* o)
+static int decode_f64(int key_gate, const float* q, const float* k, const float* v,
+                      const float* alpha, const float* beta,
+                      int64_t n_steps, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                      double* S, double* o)
 {
+    const int64_t da = key_gate ? dk : dv;
     if (!q || !k || !v || !alpha || !beta || !S) return KDA_ORACLE_BAD_ARG;
     if (n_steps < 0 || B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ORACLE_BAD_ARG;
     int failed = 0;
@@ -185,11 +221,11 @@ int kda_oracle_decode_f64(const float* q, const float* k, const float* v,
                 failed = 1;
             } else {
                 const int64_t step_tok = B * H; /* stride between steps, in (b,h) units */
-                kda_unit(n_steps, dk, dv,
+                kda_unit(key_gate, n_steps, dk, dv,
                          q + u * dk, step_tok * dk,
                          k + u * dk, step_tok * dk,
                          v + u * dv, step_tok * dv,
-                         alpha + u * dv, step_tok * dv,
+                         alpha + u * da, step_tok * da,
                          beta + u, step_tok,
                          S + u * dv * dk, o ? o + u * dv : NULL, step_tok * dv, vp, e);
             }
@@ -198,4 +234,21 @@ int kda_oracle_decode_f64(const float* q, const float* k, const float* v,
         free(e);
     }
     return failed ? KDA_ORACLE_NO_MEMORY : KDA_ORACLE_OK;
+}
+
+int kda_oracle_decode_f64(const float* q, const float* k, const float* v,
+                          const float* alpha, const float* beta,
+                          int64_t n_steps, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                          double* S, double* o)
+{
+    return decode_f64(0, q, k, v, alpha, beta, n_steps, B, H, dk, dv, S, o);
+}
+
+/* The key-channel form: alpha is [n_steps, B, H, d_k]. */
+int kda_oracle_decode_keygate_f64(const float* q, const float* k, const float* v,
+                                  const float* alpha, const float* beta,
+                                  int64_t n_steps, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                  double* S, double* o)
+{
+    return decode_f64(1, q, k, v, alpha, beta, n_steps, B, H, dk, dv, S, o);
 }

@@ -398,3 +398,69 @@ def test_segment_composition_identity():
         gamma = np.prod(d64(a[sl, 0]), axis=0)
         S = gamma[:, None] * (S @ M[0, 0]) + dS[0, 0]
     np.testing.assert_allclose(S, S_whole[0, 0], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------ key-channel gate (S~ = S diag(alpha))
+def key_case(rng, T, H, dk, dv):
+    q, k, v, _, b, S0 = rand_case(rng, T, H, dk, dv)
+    a = f32(rng.uniform(0.3, 1.0, (T, H, dk)))
+    return q, k, v, a, b, S0
+
+
+def test_key_gate_T1_closed_form():
+    """S_1 = S0 diag(alpha_1) + beta_1 (v_1 - S0 diag(alpha_1) k_1) k_1^T, o_1 = S_1 q_1."""
+    rng = np.random.default_rng(21)
+    q, k, v, a, b, S0 = key_case(rng, 1, 1, 4, 3)
+    St = S0[0, 0] * d64(a[0, 0])[None, :]
+    S1 = St + float(b[0, 0]) * np.outer(d64(v[0, 0]) - St @ d64(k[0, 0]), d64(k[0, 0]))
+    o, S = oracle.prefill_key_gate(q, k, v, a, b, S0)
+    np.testing.assert_allclose(S[0, 0], S1, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[0, 0], S1 @ d64(q[0, 0]), rtol=0, atol=1e-14)
+
+
+def test_key_gate_T2_from_zero_decays_the_key_side():
+    """From S0 = 0: S_1 = b1 v1 k1^T and
+    S_2 = b1 v1 (a2 * k1)^T + b2 (v2 - b1 ((a2 * k1) . k2) v1) k2^T: the gate multiplies the
+    stored key, where the row form would multiply the stored value."""
+    rng = np.random.default_rng(22)
+    q, k, v, a, b, _ = key_case(rng, 2, 1, 4, 3)
+    k1, k2, v1, v2 = d64(k[0, 0]), d64(k[1, 0]), d64(v[0, 0]), d64(v[1, 0])
+    a2, b1, b2 = d64(a[1, 0]), float(b[0, 0]), float(b[1, 0])
+    ak1 = a2 * k1
+    S2 = b1 * np.outer(v1, ak1) + b2 * np.outer(v2 - b1 * (ak1 @ k2) * v1, k2)
+    o, S = oracle.prefill_key_gate(q, k, v, a, b, None)
+    np.testing.assert_allclose(S[0, 0], S2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[1, 0], S2 @ d64(q[1, 0]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[0, 0], b1 * (k1 @ d64(q[0, 0])) * v1, rtol=0, atol=1e-14)
+
+
+def test_key_gate_equal_channels_is_the_scalar_gate_and_zero_forgets():
+    """A gate equal on every key channel scales S as a whole, like the scalar gate (and the
+    row form with equal rows); alpha = 0 forgets everything: S_t = beta_t v_t k_t^T."""
+    rng = np.random.default_rng(23)
+    q, k, v, _, b, S0 = key_case(rng, 11, 2, 5, 4)
+    sc = f32(rng.uniform(0.3, 1.0, (11, 2)))
+    o1, S1 = oracle.prefill_key_gate(q, k, v, np.repeat(sc[..., None], 5, axis=2), b, S0)
+    o2, S2 = oracle.prefill_scalar_gate(q, k, v, sc, b, S0)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(S1, S2, rtol=0, atol=1e-13)
+    o3, S3 = oracle.prefill_key_gate(q, k, v, np.zeros((11, 2, 5), np.float32), b, S0)
+    exp_S = d64(b[-1])[:, None, None] * d64(v[-1])[:, :, None] * d64(k[-1])[:, None, :]
+    np.testing.assert_allclose(S3[0], exp_S, rtol=0, atol=1e-14)
+    exp_o = (d64(b) * (d64(k) * d64(q)).sum(-1))[..., None] * d64(v)
+    np.testing.assert_allclose(o3, exp_o, rtol=0, atol=1e-14)
+
+
+def test_key_gate_key_channel_permutation():
+    """Permuting key channels (q, k, alpha and the columns of S0) permutes the columns of
+    S_T and leaves o unchanged; decode over the steps is the prefill."""
+    rng = np.random.default_rng(24)
+    q, k, v, a, b, S0 = key_case(rng, 9, 1, 6, 3)
+    p = rng.permutation(6)
+    o, S = oracle.prefill_key_gate(q, k, v, a, b, S0)
+    op, Sp = oracle.prefill_key_gate(q[..., p], k[..., p], v, a[..., p], b, S0[..., p])
+    np.testing.assert_allclose(op, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Sp, S[..., p], rtol=0, atol=1e-13)
+    od, Sd = oracle.decode_key_gate(q[:, None], k[:, None], v[:, None], a[:, None], b[:, None], S0)
+    np.testing.assert_allclose(od[:, 0], o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Sd, S, rtol=0, atol=1e-13)
