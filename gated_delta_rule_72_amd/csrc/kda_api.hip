@@ -48,14 +48,17 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
     const void* ptrs[] = {q, k, v, S0, o, S_T, workspace};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return KDA_ERR_INVALID_ARGUMENT;
-    if (alpha && !aligned(alpha, gate == kda::GATE_CHANNEL ? kAlign : 4)) return KDA_ERR_INVALID_ARGUMENT;
+    if (alpha && !aligned(alpha, gate == kda::GATE_SCALAR ? 4 : kAlign)) return KDA_ERR_INVALID_ARGUMENT;
     if ((beta && !aligned(beta, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
         return KDA_ERR_INVALID_ARGUMENT;
     // outputs may not overlap inputs, except S_T == S0 exactly
     const size_t eb = elem_bytes(dt);
     const size_t nt = static_cast<size_t>(n_tok), nh = static_cast<size_t>(n_heads);
     const size_t qk_bytes = nt * nh * d_k * eb, v_bytes = nt * nh * d_v * eb;
-    const size_t a_bytes = gate == kda::GATE_CHANNEL ? nt * nh * d_v * 4 : gate == kda::GATE_SCALAR ? nt * nh * 4 : 0;
+    const size_t a_bytes = gate == kda::GATE_CHANNEL ? nt * nh * d_v * 4
+                           : gate == kda::GATE_KEY   ? nt * nh * d_k * 4
+                           : gate == kda::GATE_SCALAR ? nt * nh * 4
+                                                      : 0;
     const size_t b_bytes = nt * nh * 4;
     const size_t s_bytes = static_cast<size_t>(n_seq) * nh * d_v * d_k * 4;
     const size_t cu_bytes = cu_seqlens ? (static_cast<size_t>(n_seq) + 1) * 4 : 0;
@@ -100,12 +103,15 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const float*
     const void* ptrs[] = {q, k, v, S, o};
     for (const void* p : ptrs)
         if (!aligned(p)) return KDA_ERR_INVALID_ARGUMENT;
-    if (alpha && !aligned(alpha, gate == kda::GATE_CHANNEL ? kAlign : 4)) return KDA_ERR_INVALID_ARGUMENT;
+    if (alpha && !aligned(alpha, gate == kda::GATE_SCALAR ? 4 : kAlign)) return KDA_ERR_INVALID_ARGUMENT;
     if (!aligned(beta, 4)) return KDA_ERR_INVALID_ARGUMENT;
     const size_t eb = elem_bytes(dt);
     const size_t heads = static_cast<size_t>(batch) * n_heads;
     const size_t s_bytes = heads * d_v * d_k * 4, o_bytes = heads * d_v * eb;
-    const size_t a_bytes = gate == kda::GATE_CHANNEL ? heads * d_v * 4 : gate == kda::GATE_SCALAR ? heads * 4 : 0;
+    const size_t a_bytes = gate == kda::GATE_CHANNEL ? heads * d_v * 4
+                           : gate == kda::GATE_KEY   ? heads * d_k * 4
+                           : gate == kda::GATE_SCALAR ? heads * 4
+                                                      : 0;
     struct Region { const void* p; size_t n; };
     const Region others[] = {{q, heads * d_k * eb}, {k, heads * d_k * eb}, {v, o_bytes},
                              {alpha, a_bytes}, {beta, heads * 4}};
@@ -175,6 +181,20 @@ kda_status kda_decode_step_scalar_gate(const void* q, const void* k, const void*
                                        void* stream) {
     return decode_impl(q, k, v, alpha, beta, S, o, batch, n_heads, d_k, d_v, dt, stream,
                        alpha ? kda::GATE_SCALAR : kda::GATE_NONE);
+}
+
+kda_status kda_prefill_key_gate(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* S0, const int32_t* cu_seqlens, int32_t n_seq,
+                                int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt, void* o,
+                                float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seq, n_tok, n_heads, d_k, d_v, dt, o, S_T,
+                        workspace, workspace_bytes, stream, kda::GATE_KEY);
+}
+
+kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v, const float* alpha,
+                                    const float* beta, float* S, void* o, int32_t batch, int32_t n_heads,
+                                    int32_t d_k, int32_t d_v, kda_dtype dt, void* stream) {
+    return decode_impl(q, k, v, alpha, beta, S, o, batch, n_heads, d_k, d_v, dt, stream, kda::GATE_KEY);
 }
 
 }  // extern "C"

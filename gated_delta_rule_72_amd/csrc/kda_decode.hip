@@ -11,7 +11,10 @@
 //     o_i = s_i(new) . q = alpha_i c_i + u_i (k . q)
 // so one read and one write of S suffice; the read-out uses the updated state.
 // With a scalar gate (Gated DeltaNet) alpha_i is the (sequence, head)'s one
-// value for every row; without a gate (the delta rule) it is 1.
+// value for every row; without a gate (the delta rule) it is 1.  With the gate
+// on key channels (S~ = S diag(alpha), alpha in R^{d_k}) the row is scaled
+// elementwise first: s~_i = s_i (.) alpha, a_i = s~_i . k, c_i = s~_i . q,
+// u_i = beta (v_i - a_i), s_i <- s~_i + u_i k, o_i = c_i + u_i (k . q).
 //
 // Layout of the work: one workgroup of 512 threads per 64 state rows of a
 // (sequence, head); a head of 128 rows takes two.  Eight consecutive lanes own
@@ -67,11 +70,23 @@ __global__ __launch_bounds__(1024) void decode_step_kernel(
         kk[m] = Elem<T>::load4(kh + 4 * (lane8 + 8 * m));
         qq[m] = Elem<T>::load4(qh + 4 * (lane8 + 8 * m));
     }
+    if constexpr (GATE == GATE_KEY) {
+        // s~ = s (.) alpha over key channels, in place
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const f32x4 ak = *reinterpret_cast<const f32x4*>(alpha + head * D_K + 4 * (lane8 + 8 * m));
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[p][m][e] *= ak[e];
+        }
+    }
     float vi[P], ai[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int i = slot + p * ROWS_PER_PASS;
         vi[p] = Elem<T>::load(v + head * D_V + i);
+        // the row's gate; 1 for the key-channel gate, already applied to the state
         ai[p] = GATE == GATE_CHANNEL ? alpha[head * D_V + i] : GATE == GATE_SCALAR ? alpha[head] : 1.f;
     }
     const float bt = beta[head];
@@ -134,6 +149,7 @@ static hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t stream) {
         case GATE_CHANNEL: return launch_decode_g<T, GATE_CHANNEL>(a, stream);
         case GATE_SCALAR: return launch_decode_g<T, GATE_SCALAR>(a, stream);
         case GATE_NONE: return launch_decode_g<T, GATE_NONE>(a, stream);
+        case GATE_KEY: return launch_decode_g<T, GATE_KEY>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -14,7 +14,9 @@ namespace kda {
 //   GATE_SCALAR   [.., H]: one gate per (token, head) for every row -- the
 //                 scalar-gated delta rule (Gated DeltaNet) that KDA refines
 //   GATE_NONE     no gate (alpha = 1): the plain delta rule; alpha is NULL
-enum Gate : int { GATE_CHANNEL = 0, GATE_SCALAR = 1, GATE_NONE = 2 };
+//   GATE_KEY      [.., H, d_k]: one gate per key channel, applied from the right
+//                 (S~ = S diag(alpha)); token-recurrent kernels only
+enum Gate : int { GATE_CHANNEL = 0, GATE_SCALAR = 1, GATE_NONE = 2, GATE_KEY = 3 };
 
 struct DecodeArgs {
     const void* q;
@@ -74,6 +76,9 @@ hipError_t launch_combine_segments(const float* glog, const float* S0, const flo
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+// Token-recurrent prefill (kda_prefill_valu.hip): float32 inputs, and the
+// key-channel gate for either input type.
+hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 // Workspace bytes of the fp32 prefill (the varlen schedule) and of the bf16

@@ -246,7 +246,6 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const int64_t H = n_heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g16 = lane >> 4, m16 = lane & 15;
     const int total = min(first_chunk(n_seq, n_seq, n_tok, chunk_off), max_chunks) * n_heads;  // items
 
     // ---- loads of one item's K and beta into registers (rows past the sequence
@@ -1265,10 +1264,13 @@ static hipError_t launch_bf16_g(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    // the key-channel gate takes the token-recurrent kernel (its decay falls inside
+    // K K^T, outside the chunk algebra above)
     switch (a.gate) {
         case GATE_CHANNEL: return launch_bf16_g<GATE_CHANNEL>(a, stream);
         case GATE_SCALAR: return launch_bf16_g<GATE_SCALAR>(a, stream);
         case GATE_NONE: return launch_bf16_g<GATE_NONE>(a, stream);
+        case GATE_KEY: return launch_prefill_recurrent(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -17,9 +17,9 @@ Recipe (every draw is independent; see also ``WORKLOADS``):
   * alpha (float32, one value per (token, head, value channel)):
       "sigmoid_n21"    sigmoid(N(2, 1))
       "exp_softplus"   exp(-0.1 * softplus(N(0, 1)))
-    With gate="scalar" alpha is one value per (token, head), same
-    distributions, drawn from its own tensor number; with gate="none" there is
-    no alpha (None).
+    With gate="scalar" alpha is one value per (token, head), and with
+    gate="key" one per (token, head, key channel), same distributions, each
+    drawn from its own tensor number; with gate="none" there is no alpha (None).
   * beta (float32, one scalar per (token, head)): sigmoid(N(0, 1)).
   * S0 (float32, [n_seq, H, d_v, d_k]): N(0, std^2) per element, or zeros.
   * Variable lengths: integers uniform on [lo, hi] inclusive from
@@ -40,8 +40,8 @@ import numpy as np
 BLOCK_ELEMS = 1 << 22
 
 # Tensor numbers inside a seed (fixed: changing them changes every workload).
-_T_Q, _T_K, _T_V, _T_ALPHA, _T_BETA, _T_S0, _T_ALPHA_SCALAR = 0, 1, 2, 3, 4, 5, 6
-GATES = ("channel", "scalar", "none")
+_T_Q, _T_K, _T_V, _T_ALPHA, _T_BETA, _T_S0, _T_ALPHA_SCALAR, _T_ALPHA_KEY = 0, 1, 2, 3, 4, 5, 6, 7
+GATES = ("channel", "scalar", "none", "key")
 
 
 # ---------------------------------------------------------------- rounding ---
@@ -223,12 +223,15 @@ class DecodeInputs:
         return as_f32(getattr(self, name), self.dtype)
 
 
-def draw_gate(seed, lead, dv, alpha_kind, gate):
-    """alpha of shape [*lead, dv] (per-channel), [*lead] (scalar) or None (no gate)."""
+def draw_gate(seed, lead, dv, alpha_kind, gate, dk=None):
+    """alpha of shape [*lead, dv] (per value channel), [*lead, dk] (per key channel),
+    [*lead] (scalar) or None (no gate)."""
     if gate == "channel":
         return draw_mapped(seed, _T_ALPHA, (*lead, dv), ALPHA_KINDS[alpha_kind])
     if gate == "scalar":
         return draw_mapped(seed, _T_ALPHA_SCALAR, tuple(lead), ALPHA_KINDS[alpha_kind])
+    if gate == "key":
+        return draw_mapped(seed, _T_ALPHA_KEY, (*lead, dk), ALPHA_KINDS[alpha_kind])
     if gate == "none":
         return None
     raise ValueError(f"gate must be one of {GATES}")
@@ -244,7 +247,7 @@ def make_prefill(seed: int, seq_lens, H: int, dk: int, dv: int, dtype: str = "bf
     q = draw_unit_rows(seed, _T_Q, (n_tok, H), dk, dtype)
     k = draw_unit_rows(seed, _T_K, (n_tok, H), dk, dtype)
     v = draw_normal(seed, _T_V, (n_tok, H, dv), dtype)
-    alpha = draw_gate(seed, (n_tok, H), dv, alpha_kind, gate)
+    alpha = draw_gate(seed, (n_tok, H), dv, alpha_kind, gate, dk)
     beta = draw_mapped(seed, _T_BETA, (n_tok, H), lambda g, n: _sigmoid(g.standard_normal(n)))
     S0 = None
     if s0_std > 0.0:
@@ -259,7 +262,7 @@ def make_decode(seed: int, n_steps: int, B: int, H: int, dk: int, dv: int,
     q = draw_unit_rows(seed, _T_Q, (n_steps, B, H), dk, dtype)
     k = draw_unit_rows(seed, _T_K, (n_steps, B, H), dk, dtype)
     v = draw_normal(seed, _T_V, (n_steps, B, H, dv), dtype)
-    alpha = draw_gate(seed, (n_steps, B, H), dv, alpha_kind, gate)
+    alpha = draw_gate(seed, (n_steps, B, H), dv, alpha_kind, gate, dk)
     beta = draw_mapped(seed, _T_BETA, (n_steps, B, H), lambda g, n: _sigmoid(g.standard_normal(n)))
     S0 = draw_normal(seed, _T_S0, (B, H, dv, dk), "f32", std=s0_std)
     return DecodeInputs(q, k, v, alpha, beta, S0, dtype, seed,

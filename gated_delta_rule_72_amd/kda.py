@@ -23,7 +23,8 @@ KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
-            "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate")
+            "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate",
+            "kda_prefill_key_gate", "kda_decode_step_key_gate")
 
 _lib = None
 
@@ -50,12 +51,12 @@ def lib() -> ctypes.CDLL:
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_prefill_workspace_size.restype = sz
     L.kda_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
-    for name in ("kda_prefill", "kda_prefill_scalar_gate"):
+    for name in ("kda_prefill", "kda_prefill_scalar_gate", "kda_prefill_key_gate"):
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                        vp, vp, vp, sz, vp]
-    for name in ("kda_decode_step", "kda_decode_step_scalar_gate"):
+    for name in ("kda_decode_step", "kda_decode_step_scalar_gate", "kda_decode_step_key_gate"):
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
@@ -129,6 +130,15 @@ def kda_prefill_scalar_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *,
                     want_state, workspace)
 
 
+def kda_prefill_key_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *,
+                         n_seq: Optional[int] = None, o=None, S_T=None, want_state: bool = True,
+                         workspace=None):
+    """Prefill with the forget gate on key channels (S~ = S diag(alpha)): alpha is
+    [n_tok, H, d_k] f32.  The other arguments and the result are those of kda_prefill."""
+    return _prefill("kda_prefill_key_gate", q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T,
+                    want_state, workspace)
+
+
 def _prefill(fn, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state, workspace):
     torch = _torch()
     n_tok, H, dk = q.shape
@@ -169,6 +179,12 @@ def kda_decode_step_scalar_gate(q, k, v, alpha, beta, S, o=None):
     """Decode step with one forget gate per (sequence, head) for every row: alpha is
     [B, H] f32, or None for no gate (the delta rule).  Otherwise as kda_decode_step."""
     return _decode("kda_decode_step_scalar_gate", q, k, v, alpha, beta, S, o)
+
+
+def kda_decode_step_key_gate(q, k, v, alpha, beta, S, o=None):
+    """Decode step with the forget gate on key channels: alpha is [B, H, d_k] f32.
+    Otherwise as kda_decode_step."""
+    return _decode("kda_decode_step_key_gate", q, k, v, alpha, beta, S, o)
 
 
 def _decode(fn, q, k, v, alpha, beta, S, o):

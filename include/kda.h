@@ -166,6 +166,35 @@ kda_status kda_decode_step_scalar_gate(const void* q, const void* k, const void*
                                        int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
                                        kda_dtype dt, void* stream);
 
+/*
+ * Key-channel-gate variants: the forget gate applied to the key side,
+ * S~ = S_{t-1} diag(alpha_t) with alpha_t in R^{d_k} (column j scaled by
+ * alpha_t[j]), then predict, update and read-out as above.  This is the
+ * reading of the section's forget-gating step under which the per-channel decay
+ * falls on key channels (the transcript page's "channel by channel" control
+ * does not say which side); kda_prefill follows the equation as the section
+ * writes it, with the gate on rows.
+ *
+ *   alpha   [n_tok, n_heads, d_k] float32 (prefill) or [batch, n_heads, d_k]
+ *           (decode), 16-byte aligned.
+ * Every other argument, the workspace, the layouts, the conventions and the
+ * errors are those of kda_prefill and kda_decode_step.  The prefill runs token
+ * by token (no chunk solve), for both input types, and is exact for alpha = 0.
+ */
+kda_status kda_prefill_key_gate(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* S0, const int32_t* cu_seqlens,
+                                int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                int32_t d_k, int32_t d_v, kda_dtype dt,
+                                void* o, float* S_T,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    float* S, void* o,
+                                    int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                    kda_dtype dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
