@@ -12,8 +12,9 @@ of GPU work have run, so the timed steps see settled clocks (the first ~20 ms of
 work on an idle MI355X run up to 25% slower).
 
 The same workload with one forget gate per (token, head) (kda_prefill_scalar_gate,
-Gated DeltaNet) is timed as well and reported under "scalar_gate", and the tiny fp32,
-single-layer and varlen prefill workloads under "workloads".
+Gated DeltaNet) is timed as well and reported under "scalar_gate", the gate on key
+channels (kda_prefill_key_gate) under "key_gate", and the tiny fp32, single-layer and varlen
+prefill workloads and one long sequence under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
                        [--no-scalar-gate] [--no-workloads]
@@ -382,6 +383,42 @@ def workload_parity(inp, o_gpu, S_gpu, pairs=None):
                 scope=scope + ", worst slice")
 
 
+def bench_key_gate(args, torch, kda, I):
+    """kda_prefill_key_gate (the gate on key channels, alpha [n_tok, H, d_k]) on the batched
+    prefill workload: the token-recurrent kernel, bf16 inputs; parity on one sampled pair."""
+    import oracle
+    dev = "cuda:0"
+    inp = I.workload_prefill(3, gate="key")
+    q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+    alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
+    B, H = inp.n_seq, inp.H
+
+    def step():
+        return kda.kda_prefill_key_gate(q, k, v, alpha, beta, S0, None, n_seq=B)
+
+    settle(step, 2, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(2, args.steps // 4)
+    e0.record()
+    for _ in range(n):
+        o, S_T = step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    s_, e_ = int(inp.cu_seqlens[1]), int(inp.cu_seqlens[2])
+    sub = lambda x: x[s_:e_, 7:8]
+    o_ref, S_ref = oracle.prefill_key_gate(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")), sub(inp.alpha),
+                                           sub(inp.beta), inp.S0[1:2, 7:8].astype(np.float64))
+    m, r = rel(o[s_:e_, 7].float().cpu().numpy().astype(np.float64), o_ref[:, 0])
+    ms_, rs = rel(S_T[1, 7].cpu().numpy().astype(np.float64), S_ref[0, 0])
+    alg = inp.n_tok * H * PREFILL_BYTES_PER_HEAD_TOKEN + 2 * B * H * inp.dv * inp.dk * 4
+    return dict(workload="batched prefill workload with the forget gate on key channels, kda_prefill_key_gate "
+                         "(token-recurrent kernel)",
+                ms_per_call=round(ms, 4), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
+                hbm_frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                parity=dict(o_max_rel=m, o_rms_rel=r, S_max_rel=ms_, S_rms_rel=rs, scope="(sequence 1, head 7)"))
+
+
 def bench_other_workloads(args, torch, kda, I):
     """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
     other prefill shapes) and on one long ragged sequence.  Each: inputs resident in HBM,
@@ -490,6 +527,10 @@ def main():
             f"kernel {sg['launch_ms']['avg']:.3f} ms")
         del inp, o, S_T
         torch.cuda.empty_cache()
+    if not args.no_scalar_gate:
+        line["key_gate"] = bench_key_gate(args, torch, kda, I)
+        log(f"[bench] key-gate prefill: {line['key_gate']['tokens_per_s']:.4g} tokens/s, "
+            f"{line['key_gate']['ms_per_call']:.3f} ms per call")
     if not args.no_workloads:
         line["workloads"] = bench_other_workloads(args, torch, kda, I)
     if not args.no_decode:
