@@ -14,7 +14,8 @@ work on an idle MI355X run up to 25% slower).
 The same workload with one forget gate per (token, head) (kda_prefill_scalar_gate,
 Gated DeltaNet) is timed as well and reported under "scalar_gate", the gate on key
 channels (kda_prefill_key_gate) under "key_gate", and the tiny fp32, single-layer and varlen
-prefill workloads and one long sequence under "workloads".
+prefill workloads and one long sequence under "workloads"; after the decode workload, its
+state taking 4 tokens per sequence in one in-place kda_prefill call ("multi_token_decode").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
                        [--no-scalar-gate] [--no-workloads]
@@ -419,6 +420,54 @@ def bench_key_gate(args, torch, kda, I):
                 parity=dict(o_max_rel=m, o_rms_rel=r, S_max_rel=ms_, S_rms_rel=rs, scope="(sequence 1, head 7)"))
 
 
+def bench_multi_token_decode(args, torch, kda, I, T=4):
+    """The decode workload's state (B=256 sequences x H=32 heads, d=128, fp32, 537 MB) taking
+    T new bf16 tokens per sequence in one kda_prefill call, continued in place (S_T = S0):
+    calls this short run token by token, reading and writing each state once."""
+    import oracle
+    dev = "cuda:0"
+    w = I.WORKLOADS[4]
+    dec = I.workload_decode(4, n_steps=T)
+    B, H, d = w["B"], w["H"], w["dk"]
+    pack = lambda x: np.ascontiguousarray(x.swapaxes(0, 1).reshape(B * T, *x.shape[2:]))  # [T,B,..] -> [B*T,..]
+    q, k, v = (upload(pack(getattr(dec, n)), "bf16", dev) for n in ("q", "k", "v"))
+    alpha, beta = upload(pack(dec.alpha), "f32", dev), upload(pack(dec.beta), "f32", dev)
+    S_init = upload(dec.S0, "f32", dev)
+    S = S_init.clone()
+    o = torch.empty((B * T, H, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        kda.kda_prefill(q, k, v, alpha, beta, S, None, n_seq=B, o=o, S_T=S)
+
+    settle(step, 3, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    S.copy_(S_init)
+    step()
+    torch.cuda.synchronize()
+    og, Sg = o.float().cpu().numpy().reshape(B, T, H, d), S.cpu().numpy()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for b, h in ((0, 0), (100, 17), (255, 31)):
+        sub = lambda x: x[:, b:b + 1, h:h + 1]
+        o_ref, S_ref = oracle.decode(sub(dec.f32("q")), sub(dec.f32("k")), sub(dec.f32("v")), sub(dec.alpha),
+                                     sub(dec.beta), dec.S0[b:b + 1, h:h + 1].astype(np.float64))
+        m, r = rel(og[b, :, h].astype(np.float64), o_ref[:, 0, 0])
+        ms_, rs = rel(Sg[b, h].astype(np.float64), S_ref[0, 0])
+        worst = [max(worst[0], m), max(worst[1], r), max(worst[2], ms_), max(worst[3], rs)]
+    alg = 2 * B * H * d * d * 4 + T * B * H * PREFILL_BYTES_PER_HEAD_TOKEN
+    gbs = alg / (ms * 1e-3) / 1e9
+    return dict(workload=f"decode workload state, {T} tokens per sequence per kda_prefill call, in place",
+                ms_per_call=round(ms, 4), tokens_per_s=round(B * T / (ms * 1e-3), 1),
+                achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                parity=dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
+                            scope="3 sampled (b, h) pairs, all tokens"))
+
+
 def bench_other_workloads(args, torch, kda, I):
     """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
     other prefill shapes) and on one long ragged sequence.  Each: inputs resident in HBM,
@@ -535,6 +584,9 @@ def main():
         line["workloads"] = bench_other_workloads(args, torch, kda, I)
     if not args.no_decode:
         line["decode"] = bench_decode(args, torch, kda, I)
+        line["multi_token_decode"] = bench_multi_token_decode(args, torch, kda, I)
+        log(f"[bench] multi-token decode (4 tokens per call): {line['multi_token_decode']['ms_per_call']:.3f} ms "
+            f"per call, {line['multi_token_decode']['hbm_frac']:.3f} of HBM")
         log(f"[bench] decode: {line['decode']['steps_per_s']:.4g} steps/s, "
             f"{line['decode']['roofline']['achieved']:.4g} GB/s")
     print(json.dumps(line), flush=True)

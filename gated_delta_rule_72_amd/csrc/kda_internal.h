@@ -76,9 +76,13 @@ hipError_t launch_combine_segments(const float* glog, const float* S0, const flo
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
-// Token-recurrent prefill (kda_prefill_valu.hip): float32 inputs, and the
-// key-channel gate for either input type.
+// Token-recurrent prefill (kda_prefill_valu.hip): float32 inputs, the
+// key-channel gate for either input type, and short bf16 calls.
 hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream);
+
+// bf16 prefill calls this short (equal lengths of at most this many tokens per
+// sequence, no cu_seqlens) run token by token: multi-token decode.
+constexpr int RECURRENT_MAX_TOKENS = 16;
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 // Workspace bytes of the fp32 prefill (the varlen schedule) and of the bf16

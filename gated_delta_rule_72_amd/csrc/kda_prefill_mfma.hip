@@ -1264,6 +1264,11 @@ static hipError_t launch_bf16_g(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    // a few tokens per sequence (multi-token decode): token by token, each state read
+    // and written once; with cu_seqlens the lengths are unknown on the host, so packed
+    // calls keep the chunked path
+    if (!a.cu_seqlens && a.n_tok > 0 && a.n_tok <= static_cast<int64_t>(RECURRENT_MAX_TOKENS) * a.n_seq)
+        return launch_prefill_recurrent(a, stream);
     // the key-channel gate takes the token-recurrent kernel (its decay falls inside
     // K K^T, outside the chunk algebra above)
     switch (a.gate) {

@@ -31,9 +31,15 @@
 // alpha, and then a = s~ . k, c = s~ . q, u = beta (v - a), s <- s~ + u k,
 // o = c + u (k . q): the per-token form needs no chunk algebra for it.  bf16
 // inputs are widened to fp32 on load and o is rounded to nearest even.
+// bf16 calls of at most 16 tokens per sequence (multi-token decode: a few new
+// tokens for each of many sequences, the state continued in place) also run
+// here: each state is read once and written once, as in the decode step, where
+// the chunked path would spend a whole 64-token chunk on every sequence.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
+
+#include <type_traits>
 
 namespace kda {
 
@@ -62,7 +68,7 @@ __device__ __forceinline__ void load_token(Token<DK, GATE>& x, const T* __restri
     x.b = beta[th];
 }
 
-template <typename T, int DK, int DV, int GATE>
+template <typename T, int DK, int DV, int GATE, int D>
 __global__ __launch_bounds__(64) void prefill_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -113,8 +119,7 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(
     };
     // a ring of D token buffers: each token is loaded D - 1 tokens ahead of its use
     // (the ring index is a compile-time constant in the unrolled body, so no
-    // registers are copied)
-    constexpr int D = 4;
+    // registers are copied); D = 1 loads each token just before its step
     Token<DK, GATE> tok[D];
 #pragma unroll
     for (int j = 0; j < D - 1; ++j)
@@ -134,15 +139,31 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(
     }
 }
 
-template <typename T, int DK, int DV, int GATE>
-static hipError_t launch_valu_t(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+// Ring depth for long calls (loads well ahead of their use), and for short bf16
+// calls, where many waves in flight matter more than a deep ring: at d = 128
+// depth 4 takes 214 VGPRs (two waves per SIMD), depth 2 128.  Multi-token decode
+// of the decode workload's state, ms per call for 1 / 4 / 16 tokens: depth 4
+// 0.248 / 0.408 / 1.05, depth 2 0.191 / 0.273 / 0.731, depth 1 0.199 / 0.275 / 0.710.
+constexpr int kRingLong = 4;
+constexpr int kRingShort = 2;
+
+template <typename T, int DK, int DV, int GATE, int D>
+static hipError_t launch_valu_d(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
     constexpr int NVB = DV / ROWS_PER_WAVE;
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(64), 0,
+    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, GATE, D>), dim3(static_cast<unsigned>(grid)), dim3(64), 0,
                        stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
                        static_cast<T*>(a.o), a.S_T);
     return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, int GATE>
+static hipError_t launch_valu_t(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+    const bool short_call = std::is_same<T, uint16_t>::value && !a.cu_seqlens &&
+                            a.n_tok <= static_cast<int64_t>(RECURRENT_MAX_TOKENS) * a.n_seq;
+    return short_call ? launch_valu_d<T, DK, DV, GATE, kRingShort>(a, order, stream)
+                      : launch_valu_d<T, DK, DV, GATE, kRingLong>(a, order, stream);
 }
 
 template <typename T, int GATE>
@@ -154,9 +175,9 @@ static hipError_t launch_valu_g(const PrefillArgs& a, const int32_t* order, hipS
     return hipErrorInvalidValue;
 }
 
-// The token-recurrent prefill: every gate for float32 inputs, and the key-channel
-// gate for bf16 inputs.  The workspace holds only the longest-first schedule
-// (packed input), at its start.
+// The token-recurrent prefill: float32 inputs, the key-channel gate, and bf16
+// calls of a few tokens per sequence (multi-token decode).  The workspace holds
+// only the longest-first schedule (packed input), at its start.
 hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream) {
     const int32_t* order = nullptr;
     if (a.cu_seqlens) {
@@ -166,7 +187,12 @@ hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream) {
         order = ord;
     }
     if (a.bf16) {
-        if (a.gate == GATE_KEY) return launch_valu_g<uint16_t, GATE_KEY>(a, order, stream);
+        switch (a.gate) {
+            case GATE_CHANNEL: return launch_valu_g<uint16_t, GATE_CHANNEL>(a, order, stream);
+            case GATE_SCALAR: return launch_valu_g<uint16_t, GATE_SCALAR>(a, order, stream);
+            case GATE_NONE: return launch_valu_g<uint16_t, GATE_NONE>(a, order, stream);
+            case GATE_KEY: return launch_valu_g<uint16_t, GATE_KEY>(a, order, stream);
+        }
         return hipErrorInvalidValue;
     }
     switch (a.gate) {

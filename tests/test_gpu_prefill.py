@@ -278,3 +278,33 @@ def test_fp32_prefill_alpha_zero_is_exact(torch_cuda):
     last = inp.cu_seqlens[1:] - 1
     exp_S = (b[last][..., None, None] * v[last][..., :, None] * k[last][..., None, :])
     np.testing.assert_allclose(S, exp_S, rtol=1e-5, atol=1e-6)
+
+
+# Multi-token decode: dense bf16 calls of at most 16 tokens per sequence run token by
+# token (each state read and written once).  Two calls in a row continue the state in
+# place (S_T = S0), against the oracle continued the same way.
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none", "key"])
+@pytest.mark.parametrize("T,B,H,d", [(4, 16, 4, 128), (1, 8, 3, 64), (16, 5, 2, 128)])
+def test_short_calls_continue_the_state_in_place(torch_cuda, gate, T, B, H, d):
+    from gated_delta_rule_72_amd import kda
+    import oracle
+    print(f"prefill short dense calls (multi-token decode) gate={gate} T={T} B={B} H={H} d={d}", flush=True)
+    fn = {"channel": kda.kda_prefill, "scalar": kda.kda_prefill_scalar_gate,
+          "none": kda.kda_prefill_scalar_gate, "key": kda.kda_prefill_key_gate}[gate]
+    ref = {"channel": oracle.prefill, "scalar": oracle.prefill_scalar_gate,
+           "none": oracle.prefill_scalar_gate, "key": oracle.prefill_key_gate}[gate]
+    tol = Hh.TOL_BF16
+    S_dev = None
+    S_ref = None
+    for call in range(2):
+        inp = I.make_prefill(7300 + 10 * call + T + B + H + d, [T] * B, H, d, d, "bf16", "exp_softplus", 0.02,
+                             gate)
+        dd = Hh.upload_prefill(inp)
+        if S_dev is None:
+            S_dev = dd["S0"]
+            S_ref = inp.S0.astype(np.float64)
+        o, S = fn(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], S_dev, None, n_seq=B, S_T=S_dev)
+        torch_cuda.cuda.synchronize()
+        o_ref, S_ref = ref(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta, S_ref, inp.cu_seqlens)
+        Hh.check(f"o call {call}", Hh.from_device(o), o_ref, Hh.o_slices(inp.cu_seqlens, H), tol)
+        Hh.check(f"S call {call}", Hh.from_device(S), S_ref, Hh.s_slices(B, H), tol)
