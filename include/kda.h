@@ -66,15 +66,21 @@ int kda_abi_version(void);
 const char* kda_status_string(kda_status s);
 
 /*
- * Bytes of device workspace kda_prefill needs for these sizes (0 is possible).
- * Returns 0 as well for sizes that kda_prefill would reject.
+ * Bytes of device workspace kda_prefill (and its gate variants) needs for these
+ * sizes (0 is possible).  Returns 0 as well for sizes that kda_prefill would
+ * reject.  The size depends on the sizes only, never on cu_seqlens.
  *   KDA_DTYPE_F32:  the longest-first schedule of the packed sequences
  *                   (n_seq int32, rounded up to 256 bytes).
  *   KDA_DTYPE_BF16: the schedule, the first chunk of every sequence
- *                   ((n_seq + 1) int32, rounded up to 256 bytes), and the
- *                   solved within-chunk system A = (I + L)^{-1} diag(beta) of
- *                   every (chunk, head) -- 12 KiB each, for at most
- *                   n_tok / 64 + n_seq chunks of 64 tokens.
+ *                   ((n_seq + 1) int32), and the solved within-chunk system
+ *                   A = (I + L)^{-1} diag(beta) of every (chunk, head) -- 12 KiB
+ *                   each, for at most n_tok / 64 + n_seq chunks of 64 tokens.
+ *                   Calls with few (sequence, head) pairs and long sequences
+ *                   (d_k = d_v) are split into G segments per sequence that are
+ *                   scanned in parallel and composed; for those the schedule and
+ *                   offsets cover n_seq G segments, plus the segments' token
+ *                   offsets, and three fp32 states of d_v x d_k and a d_v-vector
+ *                   per (segment, head).  Every part is rounded up to 256 bytes.
  */
 size_t kda_prefill_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
                                   int32_t d_k, int32_t d_v, kda_dtype dt);
