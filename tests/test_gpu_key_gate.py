@@ -56,6 +56,8 @@ def oracle_prefill(inp, seqs=None, heads=None):
     ([300, 64, 129], 4, 128, 128, "bf16", "exp_softplus", 0.02),
     ([513], 2, 64, 128, "bf16", "sigmoid_n21", 0.0),
     ([0, 100, 0, 65], 2, 128, 128, "bf16", "exp_softplus", 0.02),   # empty sequences
+    ([12, 3, 16, 1], 2, 128, 128, "bf16", "exp_softplus", 0.02),    # at most 16 tokens per sequence
+    ([9, 16, 2], 2, 64, 64, "f32", "sigmoid_n21", 0.02),
 ])
 def test_prefill_key_gate_matches_oracle(torch_cuda, lens, H, dk, dv, dtype, alpha_kind, s0):
     print(f"prefill_key_gate lens={lens} H={H} dk={dk} dv={dv} {dtype} {alpha_kind} s0={s0}", flush=True)

@@ -70,6 +70,7 @@ def check_sampled(inp, o, S, pairs):
     ([130, 33], 2, 128, 128, "f32", "exp_softplus", 0.02),
     ([96], 3, 128, 64, "f32", "exp_softplus", 0.0),
     ([70], 2, 64, 128, "f32", "exp_softplus", 0.02),
+    ([5, 16, 1, 9], 2, 64, 64, "f32", "exp_softplus", 0.02),   # at most 16 tokens per sequence
     ([300, 64, 129], 4, 128, 128, "bf16", "exp_softplus", 0.02),
     ([513], 2, 64, 64, "bf16", "exp_softplus", 0.0),
     ([191, 2], 3, 128, 64, "bf16", "exp_softplus", 0.02),
@@ -308,3 +309,37 @@ def test_short_calls_continue_the_state_in_place(torch_cuda, gate, T, B, H, d):
         o_ref, S_ref = ref(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta, S_ref, inp.cu_seqlens)
         Hh.check(f"o call {call}", Hh.from_device(o), o_ref, Hh.o_slices(inp.cu_seqlens, H), tol)
         Hh.check(f"S call {call}", Hh.from_device(S), S_ref, Hh.s_slices(B, H), tol)
+
+
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none", "key"])
+@pytest.mark.parametrize("lens,H,dk,dv,dtype,varlen", [
+    ([700, 1, 0, 333], 2, 128, 128, "f32", True),   # ragged 16-token blocks, length 1, empty
+    ([520], 3, 64, 64, "f32", False),
+    ([300, 290], 2, 128, 64, "f32", True),
+    ([257, 400], 2, 64, 128, "f32", True),
+    ([600, 301], 2, 128, 128, "bf16", True),        # bf16 reaches here with the key-channel gate
+])
+def test_long_token_recurrent_calls_match_oracle(torch_cuda, gate, lens, H, dk, dv, dtype, varlen):
+    """Long calls of the token-recurrent path (fp32 inputs, or the key-channel gate):
+    sequences averaging 256 tokens or more take the form that stages blocks of
+    tokens in LDS.  Compared in full with the oracle of each gate."""
+    from gated_delta_rule_72_amd import kda
+    import oracle
+    if dtype == "bf16" and gate != "key":
+        pytest.skip("bf16 prefill with this gate runs the chunked path")
+    print(f"long token-recurrent call gate={gate} lens={lens} H={H} dk={dk} dv={dv} {dtype} varlen={varlen}",
+          flush=True)
+    fn = {"channel": kda.kda_prefill, "scalar": kda.kda_prefill_scalar_gate,
+          "none": kda.kda_prefill_scalar_gate, "key": kda.kda_prefill_key_gate}[gate]
+    ref = {"channel": oracle.prefill, "scalar": oracle.prefill_scalar_gate,
+           "none": oracle.prefill_scalar_gate, "key": oracle.prefill_key_gate}[gate]
+    inp = I.make_prefill(7500 + sum(lens) + H + dk + dv, lens, H, dk, dv, dtype, "exp_softplus", 0.02, gate)
+    d = Hh.upload_prefill(inp)
+    o, S = fn(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"] if varlen else None,
+              n_seq=inp.n_seq)
+    torch_cuda.cuda.synchronize()
+    o_ref, S_ref = ref(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta, inp.S0.astype(np.float64),
+                       inp.cu_seqlens)
+    tol = Hh.tol_for(dtype)
+    Hh.check("o", Hh.from_device(o), o_ref, Hh.o_slices(inp.cu_seqlens, H), tol)
+    Hh.check("S_T", Hh.from_device(S), S_ref, Hh.s_slices(inp.n_seq, H), tol)
