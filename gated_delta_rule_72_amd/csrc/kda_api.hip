@@ -125,6 +125,53 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const float*
     return err == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
 }
 
+
+// Shared body of kda_prefill_backward and kda_prefill_backward_scalar_gate.
+kda_status backward_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                         const float* S0, const int32_t* cu_seqlens, const float* dO, const float* dS_T,
+                         int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt,
+                         float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dS0, void* workspace,
+                         size_t workspace_bytes, void* stream, kda::Gate gate) {
+    if (!valid_dtype(dt)) return KDA_ERR_INVALID_ARGUMENT;
+    if (n_seq < 1 || n_tok < 0 || n_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!cu_seqlens && (n_tok % n_seq) != 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (n_tok > 0 && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta)) return KDA_ERR_INVALID_ARGUMENT;
+    if (n_tok > 0 && gate != kda::GATE_NONE && (!alpha || !dalpha)) return KDA_ERR_INVALID_ARGUMENT;
+    if (gate == kda::GATE_NONE) alpha = nullptr, dalpha = nullptr;
+    const void* vec[] = {q, k, v, S0, dS_T, dq, dk, dS0, workspace};
+    for (const void* p : vec)
+        if (p && !aligned(p)) return KDA_ERR_INVALID_ARGUMENT;
+    const void* scal[] = {alpha, beta, cu_seqlens, dO, dv, dalpha, dbeta};
+    for (const void* p : scal)
+        if (p && !aligned(p, 4)) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t eb = elem_bytes(dt);
+    const size_t nt = static_cast<size_t>(n_tok), nh = static_cast<size_t>(n_heads);
+    const size_t qk_bytes = nt * nh * d_k * eb, v_bytes = nt * nh * d_v * eb;
+    const size_t a_bytes = gate == kda::GATE_CHANNEL ? nt * nh * d_v * 4 : gate == kda::GATE_SCALAR ? nt * nh * 4 : 0;
+    const size_t b_bytes = nt * nh * 4, s_bytes = static_cast<size_t>(n_seq) * nh * d_v * d_k * 4;
+    const size_t cu_bytes = cu_seqlens ? (static_cast<size_t>(n_seq) + 1) * 4 : 0;
+    const size_t need = kda::prefill_backward_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    struct Region { const void* p; size_t n; };
+    const Region ins[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {alpha, a_bytes}, {beta, b_bytes},
+                          {S0, S0 ? s_bytes : 0}, {cu_seqlens, cu_bytes}, {dO, nt * nh * d_v * 4},
+                          {dS_T, dS_T ? s_bytes : 0}};
+    const Region outs[] = {{dq, nt * nh * d_k * 4}, {dk, nt * nh * d_k * 4}, {dv, nt * nh * d_v * 4},
+                           {dalpha, a_bytes}, {dbeta, b_bytes}, {dS0, dS0 ? s_bytes : 0}, {workspace, need}};
+    // outputs (and the workspace) overlap neither the inputs nor each other
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Region& in : ins)
+            if (ranges_overlap(outs[i].p, outs[i].n, in.p, in.n)) return KDA_ERR_INVALID_ARGUMENT;
+        for (size_t j2 = i + 1; j2 < sizeof(outs) / sizeof(outs[0]); ++j2)
+            if (ranges_overlap(outs[i].p, outs[i].n, outs[j2].p, outs[j2].n)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    kda::BackwardArgs a{q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, n_tok, n_heads, d_k, d_v,
+                        dt == KDA_DTYPE_BF16, dq, dk, dv, dalpha, dbeta, dS0, workspace, gate};
+    const hipError_t err = kda::launch_prefill_backward(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_DEVICE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +242,31 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
                                     const float* beta, float* S, void* o, int32_t batch, int32_t n_heads,
                                     int32_t d_k, int32_t d_v, kda_dtype dt, void* stream) {
     return decode_impl(q, k, v, alpha, beta, S, o, batch, n_heads, d_k, d_v, dt, stream, kda::GATE_KEY);
+}
+
+size_t kda_prefill_backward_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    if (n_seq < 1 || n_tok < 0 || n_heads < 1 || !supported_dim(d_k) || !supported_dim(d_v)) return 0;
+    return kda::prefill_backward_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v);
+}
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                                const float* S0, const int32_t* cu_seqlens, const float* dO, const float* dS_T,
+                                int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v,
+                                kda_dtype dt, float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                                float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, n_tok, n_heads, d_k, d_v, dt, dq, dk,
+                         dv, dalpha, dbeta, dS0, workspace, workspace_bytes, stream, kda::GATE_CHANNEL);
+}
+
+kda_status kda_prefill_backward_scalar_gate(const void* q, const void* k, const void* v, const float* alpha,
+                                            const float* beta, const float* S0, const int32_t* cu_seqlens,
+                                            const float* dO, const float* dS_T, int32_t n_seq, int32_t n_tok,
+                                            int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt, float* dq,
+                                            float* dk, float* dv, float* dalpha, float* dbeta, float* dS0,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, n_tok, n_heads, d_k, d_v, dt, dq, dk,
+                         dv, dalpha, dbeta, dS0, workspace, workspace_bytes, stream,
+                         alpha ? kda::GATE_SCALAR : kda::GATE_NONE);
 }
 
 }  // extern "C"

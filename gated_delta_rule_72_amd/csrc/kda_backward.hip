@@ -1,0 +1,304 @@
+// kda_backward.hip -- gradients of the KDA recurrence (token-recurrent form).
+//
+// Page "Kimi (AI)", section "Kimi Delta Attention (KDA)" gives the per-token
+// steps (forget S~ = diag(alpha_t) S, predict v~ = S~ k_t, update
+// S_t = S~ + beta_t (v_t - v~) k_t^T, read-out o_t = S_t q_t); the page
+// "Kimi Linear" presents the chunked form of such layers as a training
+// method, which needs their gradients.  With a_t = S_{t-1} k_t,
+// u_t = beta_t (v_t - alpha_t a_t) and G_t = dL/dS_t, walking the tokens in
+// reverse:
+//     G_t     += dO_t q_t^T
+//     dq_t     = S_t^T dO_t              du_t = G_t k_t
+//     da_t     = -beta_t alpha_t du_t    dk_t = G_t^T u_t + S_{t-1}^T da_t
+//     dv_t     = beta_t du_t             dbeta_t = du_t . (v_t - alpha_t a_t)
+//     dalpha_t = rowsum(G_t (.) S_{t-1}) - beta_t a_t du_t
+//     G_{t-1}  = diag(alpha_t) G_t + da_t k_t^T
+// Rows of the state are independent (the gate scales rows), so one wave owns
+// 8 value rows of one (sequence, head), 8 lanes per row as in the forward
+// kernel: dv and a value-channel dalpha are per row and stored directly; dq,
+// dk, dbeta and a scalar dalpha are sums over rows, reduced over the wave's
+// rows and added into zeroed outputs with float atomics (so their last bits
+// depend on the order of the waves).
+// States: a forward pass stores the state every 16 tokens; the backward pass
+// walks the blocks in reverse, recomputes the 16 states of a block from its
+// checkpoint into the wave's own scratch, and walks those tokens in reverse.
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_schedule.h"
+
+namespace kda {
+
+constexpr int BWD_BLOCK = 16;  // tokens between state checkpoints
+
+// Checkpoint slot of block b of a sequence that starts at token t0 and is the
+// n-th: n + t0 / 16 + b.  Consecutive sequences never share a slot (a sequence
+// of L tokens has ceil(L / 16) blocks) and every slot is below
+// n_seq + n_tok / 16 + 1.
+__host__ __device__ inline int64_t bwd_slots(int32_t n_seq, int32_t n_tok) {
+    return static_cast<int64_t>(n_seq) + n_tok / BWD_BLOCK + 1;
+}
+
+// Sum over the 8 lanes that hold the same key channels of the wave's 8 rows.
+__device__ __forceinline__ float sum_rows8(float x) {
+    x += __shfl_xor(x, 8);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0.f;
+}
+
+template <typename T, int DK, int DV, int GATE>
+__global__ __launch_bounds__(64) void backward_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, const float* __restrict__ dO, const float* __restrict__ dS_T,
+    int n_seq, int n_tok, int n_heads, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
+    float* __restrict__ dS0, float* __restrict__ ckpt, float* __restrict__ sbuf) {
+    constexpr int NVB = DV / 8;
+    constexpr int M = DK / 32;
+    const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
+    if (!u.valid) return;
+    const int lane = threadIdx.x;
+    const int j = lane & 7;
+    const int row = u.vblk * 8 + (lane >> 3);
+    const int64_t H = n_heads;
+    const int h = u.head;
+    const int64_t len = u.t1 - u.t0;
+    const int nblk = static_cast<int>((len + BWD_BLOCK - 1) / BWD_BLOCK);
+    const int64_t slot0 = u.seq + u.t0 / BWD_BLOCK;
+    auto ck = [&](int b) { return ckpt + (((slot0 + b) * H + h) * DV + row) * DK; };
+    float* my = sbuf + static_cast<int64_t>(blockIdx.x) * BWD_BLOCK * 8 * DK + (lane >> 3) * DK;
+    auto col = [&](int m) { return 4 * (j + 8 * m); };
+
+    struct Tok { f32x4 k[M], q[M]; float v, a, b; };
+    auto load = [&](Tok& x, int64_t t) {
+        const int64_t th = t * H + h;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            x.k[m] = Elem<T>::load4(k + th * DK + col(m));
+            x.q[m] = Elem<T>::load4(q + th * DK + col(m));
+        }
+        x.v = Elem<T>::load(v + th * DV + row);
+        x.a = GATE == GATE_CHANNEL ? alpha[th * DV + row] : GATE == GATE_SCALAR ? alpha[th] : 1.f;
+        x.b = beta[th];
+    };
+    // a = s . k for this lane's row (all 8 lanes of the row get it)
+    auto dot_k = [&](const f32x4* s, const Tok& x) {
+        float p = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p += s[m][e] * x.k[m][e];
+        return sum8(p);
+    };
+
+    // forward: checkpoints at every block start
+    f32x4 s[M];
+    const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row) * DK;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t t = u.t0; t < u.t1; ++t) {
+        const int64_t i = t - u.t0;
+        if (i % BWD_BLOCK == 0) {
+            float* c = ck(static_cast<int>(i / BWD_BLOCK));
+#pragma unroll
+            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(c + col(m)) = s[m];
+        }
+        Tok x;
+        load(x, t);
+        const float uu = x.b * (x.v - x.a * dot_k(s, x));
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[m][e] = x.a * s[m][e] + uu * x.k[m][e];
+    }
+
+    // backward
+    f32x4 G[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        G[m] = dS_T ? *reinterpret_cast<const f32x4*>(dS_T + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int64_t tb = u.t0 + static_cast<int64_t>(b) * BWD_BLOCK;
+        const int nb = static_cast<int>(u.t1 - tb < BWD_BLOCK ? u.t1 - tb : BWD_BLOCK);
+        // the block's states S_{t-1}, t = tb .. tb + nb - 1, into this wave's scratch
+        const float* c = ck(b);
+#pragma unroll
+        for (int m = 0; m < M; ++m) s[m] = *reinterpret_cast<const f32x4*>(c + col(m));
+        for (int i = 0; i < nb; ++i) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(my + i * 8 * DK + col(m)) = s[m];
+            Tok x;
+            load(x, tb + i);
+            const float uu = x.b * (x.v - x.a * dot_k(s, x));
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[m][e] = x.a * s[m][e] + uu * x.k[m][e];
+        }
+        for (int i = nb - 1; i >= 0; --i) {
+            const int64_t t = tb + i;
+            const int64_t th = t * H + h;
+            Tok x;
+            load(x, t);
+            f32x4 sp[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) sp[m] = *reinterpret_cast<const f32x4*>(my + i * 8 * DK + col(m));
+            const float a = dot_k(sp, x);
+            const float uu = x.b * (x.v - x.a * a);
+            const float go = dO[th * DV + row];
+            // dq_t = S_t^T dO_t, with S_t = alpha S_{t-1} + u k^T; G_t += dO_t q_t^T
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 pq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pq[e] = sum_rows8(go * (x.a * sp[m][e] + uu * x.k[m][e]));
+                    G[m][e] += go * x.q[m][e];
+                }
+                if (lane < 8)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicAdd(dq + th * DK + col(m) + e, pq[e]);
+            }
+            float pdu = 0.f, pga = 0.f;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pdu += G[m][e] * x.k[m][e];
+                    pga += G[m][e] * sp[m][e];
+                }
+            const float du = sum8(pdu);
+            const float da = -x.b * x.a * du;
+            const float dal = sum8(pga) - x.b * a * du;
+            // dk_t = G^T u + S_{t-1}^T da
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                f32x4 pk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[e] = sum_rows8(uu * G[m][e] + da * sp[m][e]);
+                if (lane < 8)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicAdd(dk + th * DK + col(m) + e, pk[e]);
+            }
+            // the row's own gradients (every lane of the row holds them; lane 0 of the eight writes)
+            const float dbr = du * (x.v - x.a * a);
+            if (j == 0) {
+                dv[th * DV + row] = x.b * du;
+                if constexpr (GATE == GATE_CHANNEL) dalpha[th * DV + row] = dal;
+            }
+            const float dbs = sum_rows8(dbr);
+            if (lane == 0) atomicAdd(dbeta + th, dbs);
+            if constexpr (GATE == GATE_SCALAR) {
+                const float das = sum_rows8(dal);
+                if (lane == 0) atomicAdd(dalpha + th, das);
+            }
+            // G_{t-1} = alpha G_t + da k^T
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G[m][e] = x.a * G[m][e] + da * x.k[m][e];
+        }
+    }
+    if (dS0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(dS0 + s_row + col(m)) = G[m];
+    }
+}
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct BwdLayout {
+    size_t order, ckpt, sbuf, total;
+};
+
+BwdLayout bwd_layout(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    BwdLayout L;
+    L.order = 0;
+    L.ckpt = align_up(static_cast<size_t>(n_seq) * 4);
+    const size_t ck_bytes = static_cast<size_t>(bwd_slots(n_seq, n_tok)) * n_heads * d_v * d_k * 4;
+    L.sbuf = align_up(L.ckpt + ck_bytes);
+    const int64_t waves = prefill_grid(static_cast<int64_t>(n_seq) * n_heads, d_v / 8);
+    L.total = align_up(L.sbuf + static_cast<size_t>(waves) * BWD_BLOCK * 8 * d_k * 4);
+    return L;
+}
+
+hipError_t fill_zero(float* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, int GATE>
+hipError_t launch_bwd_t(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, hipStream_t stream) {
+    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / 8);
+    hipLaunchKernelGGL((backward_kernel<T, DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.alpha,
+                       a.beta, a.S0, a.cu_seqlens, order, a.dO, a.dS_T, a.n_seq, a.n_tok, a.n_heads, a.dq, a.dk,
+                       a.dv, a.dalpha, a.dbeta, a.dS0, ckpt, sbuf);
+    return hipGetLastError();
+}
+
+template <typename T, int GATE>
+hipError_t launch_bwd_g(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<T, 128, 128, GATE>(a, order, ckpt, sbuf, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<T, 64, 64, GATE>(a, order, ckpt, sbuf, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<T, 128, 64, GATE>(a, order, ckpt, sbuf, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bwd_t<T, 64, 128, GATE>(a, order, ckpt, sbuf, stream);
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_bwd_type(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf,
+                           hipStream_t stream) {
+    switch (a.gate) {
+        case GATE_CHANNEL: return launch_bwd_g<T, GATE_CHANNEL>(a, order, ckpt, sbuf, stream);
+        case GATE_SCALAR: return launch_bwd_g<T, GATE_SCALAR>(a, order, ckpt, sbuf, stream);
+        case GATE_NONE: return launch_bwd_g<T, GATE_NONE>(a, order, ckpt, sbuf, stream);
+        case GATE_KEY: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t prefill_backward_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    return bwd_layout(n_seq, n_tok, n_heads, d_k, d_v).total;
+}
+
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
+    const BwdLayout L = bwd_layout(a.n_seq, a.n_tok, a.n_heads, a.d_k, a.d_v);
+    char* ws = static_cast<char*>(a.workspace);
+    const int64_t nt = static_cast<int64_t>(a.n_tok) * a.n_heads;
+    // the summed gradients are accumulated with atomics into zeroed outputs
+    hipError_t e = fill_zero(a.dq, nt * a.d_k, stream);
+    if (e == hipSuccess) e = fill_zero(a.dk, nt * a.d_k, stream);
+    if (e == hipSuccess) e = fill_zero(a.dbeta, nt, stream);
+    if (e == hipSuccess && a.gate == GATE_SCALAR) e = fill_zero(a.dalpha, nt, stream);
+    if (e != hipSuccess) return e;
+    const int32_t* order = nullptr;
+    if (a.cu_seqlens) {
+        int32_t* ord = reinterpret_cast<int32_t*>(ws + L.order);
+        e = launch_schedule(a.cu_seqlens, a.n_seq, ord, stream);
+        if (e != hipSuccess) return e;
+        order = ord;
+    }
+    float* ckpt = reinterpret_cast<float*>(ws + L.ckpt);
+    float* sbuf = reinterpret_cast<float*>(ws + L.sbuf);
+    return a.bf16 ? launch_bwd_type<uint16_t>(a, order, ckpt, sbuf, stream)
+                  : launch_bwd_type<float>(a, order, ckpt, sbuf, stream);
+}
+
+}  // namespace kda

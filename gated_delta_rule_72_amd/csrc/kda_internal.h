@@ -91,4 +91,33 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
 size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
 
+// Backward of the token-recurrent prefill (kda_backward.hip): the gradients of
+// q, k, v, alpha, beta and S0 given those of o and S_T.  gate is GATE_CHANNEL,
+// GATE_SCALAR or GATE_NONE.
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* S0;            // may be null (zeros)
+    const int32_t* cu_seqlens;  // may be null (equal lengths)
+    const float* dO;
+    const float* dS_T;          // may be null (zeros)
+    int32_t n_seq, n_tok, n_heads, d_k, d_v;
+    bool bf16;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dalpha;              // null for GATE_NONE
+    float* dbeta;
+    float* dS0;                 // may be null (not wanted)
+    void* workspace;
+    Gate gate;
+};
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream);
+// Workspace bytes: the longest-first schedule, a state checkpoint every 16
+// tokens of every (sequence, head), and each wave's states within one block.
+size_t prefill_backward_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
+
 }  // namespace kda

@@ -41,6 +41,7 @@ BLOCK_ELEMS = 1 << 22
 
 # Tensor numbers inside a seed (fixed: changing them changes every workload).
 _T_Q, _T_K, _T_V, _T_ALPHA, _T_BETA, _T_S0, _T_ALPHA_SCALAR, _T_ALPHA_KEY = 0, 1, 2, 3, 4, 5, 6, 7
+_T_DO, _T_DST = 8, 9
 GATES = ("channel", "scalar", "none", "key")
 
 
@@ -312,3 +313,13 @@ def workload_decode(wid: int = 4, n_steps: Optional[int] = None, B: Optional[int
     assert w["kind"] == "decode"
     return make_decode(workload_seed(wid), n_steps or w["steps"], B or w["B"], H or w["H"],
                        w["dk"], w["dv"], w["dtype"], w["alpha_kind"], w["s0_std"], gate)
+
+
+def make_backward_grads(seed: int, inp: PrefillInputs):
+    """Gradients flowing into a prefill call: dO [n_tok, H, d_v] and dS_T
+    [n_seq, H, d_v, d_k], float32, standard normal."""
+    n_tok, H, dv = inp.v.shape
+    dk = inp.q.shape[2]
+    dO = draw_normal(seed, _T_DO, (n_tok, H, dv), "f32")
+    dS_T = draw_normal(seed, _T_DST, (inp.n_seq, H, dv, dk), "f32")
+    return dO, dS_T

@@ -24,7 +24,8 @@ KDA_DTYPE_BF16 = 1
 
 EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
             "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate",
-            "kda_prefill_key_gate", "kda_decode_step_key_gate")
+            "kda_prefill_key_gate", "kda_decode_step_key_gate", "kda_prefill_backward_workspace_size",
+            "kda_prefill_backward", "kda_prefill_backward_scalar_gate")
 
 _lib = None
 
@@ -60,6 +61,13 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    L.kda_prefill_backward_workspace_size.restype = sz
+    L.kda_prefill_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    for name in ("kda_prefill_backward", "kda_prefill_backward_scalar_gate"):
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -199,3 +207,51 @@ def _decode(fn, q, k, v, alpha, beta, S, o):
     if st != KDA_OK:
         raise KdaError(fn, st)
     return o
+
+
+def backward_workspace_size(n_seq: int, n_tok: int, n_heads: int, d_k: int, d_v: int) -> int:
+    return int(lib().kda_prefill_backward_workspace_size(n_seq, n_tok, n_heads, d_k, d_v))
+
+
+def _backward(fn, q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, want_dS0, workspace):
+    torch = _torch()
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        n_seq = cu_seqlens.shape[0] - 1
+    elif n_seq is None:
+        n_seq = S0.shape[0] if S0 is not None else 1
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grads = dict(dq=torch.empty((n_tok, H, dk), **f32), dk=torch.empty((n_tok, H, dk), **f32),
+                 dv=torch.empty((n_tok, H, dv), **f32),
+                 dalpha=None if alpha is None else torch.empty(alpha.shape, **f32),
+                 dbeta=torch.empty((n_tok, H), **f32),
+                 dS0=torch.empty((n_seq, H, dv, dk), **f32) if want_dS0 else None)
+    ws_bytes = backward_workspace_size(n_seq, n_tok, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+                            _ptr(dO), _ptr(dS_T), n_seq, n_tok, H, dk, dv, _dtype_code(q),
+                            _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dalpha"]),
+                            _ptr(grads["dbeta"]), _ptr(grads["dS0"]), _ptr(workspace), workspace.numel(),
+                            _stream(q))
+    if st != KDA_OK:
+        raise KdaError(fn, st)
+    return grads
+
+
+def kda_prefill_backward(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, *, n_seq: Optional[int] = None,
+                         want_dS0: bool = True, workspace=None):
+    """Gradients (dict dq, dk, dv, dalpha, dbeta, dS0; float32) of a kda_prefill call's
+    inputs, given dO = dL/do (float32 [n_tok, H, d_v]) and dS_T = dL/dS_T (or None)."""
+    return _backward("kda_prefill_backward", q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, want_dS0,
+                     workspace)
+
+
+def kda_prefill_backward_scalar_gate(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, *,
+                                     n_seq: Optional[int] = None, want_dS0: bool = True, workspace=None):
+    """kda_prefill_backward with alpha [n_tok, H] (one gate per token and head) or None (no gate)."""
+    return _backward("kda_prefill_backward_scalar_gate", q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq,
+                     want_dS0, workspace)

@@ -201,6 +201,57 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
                                     int32_t batch, int32_t n_heads, int32_t d_k, int32_t d_v,
                                     kda_dtype dt, void* stream);
 
+/*
+ * Backward of the prefill (training): the gradients of a scalar loss L with
+ * respect to q, k, v, alpha, beta and S0, given dO = dL/do and dS_T = dL/dS_T.
+ * The page "Kimi Linear", in its section on the linear-attention family,
+ * presents the chunked form of these layers as the way they are trained; the
+ * gradients follow from the per-token steps of page "Kimi (AI)", section
+ * "Kimi Delta Attention (KDA)", by the chain rule taken in reverse token
+ * order (the recurrence's states are recomputed from checkpoints every 16
+ * tokens, kept in the workspace).
+ *
+ *   q, k, v, alpha, beta, S0, cu_seqlens, n_seq, n_tok, n_heads, d_k, d_v, dt:
+ *               as for kda_prefill (the forward inputs of the call)
+ *   dO          [n_tok, n_heads, d_v]   float32, 4-byte aligned
+ *   dS_T        [n_seq, n_heads, d_v, d_k] float32, or NULL = zeros
+ *   dq, dk      [n_tok, n_heads, d_k]   float32 (written)
+ *   dv          [n_tok, n_heads, d_v]   float32 (written), 4-byte aligned
+ *   dalpha      shaped as alpha, float32 (written), 4-byte aligned
+ *   dbeta       [n_tok, n_heads]        float32 (written), 4-byte aligned
+ *   dS0         [n_seq, n_heads, d_v, d_k] float32 (written), or NULL
+ *   workspace   device scratch of at least kda_prefill_backward_workspace_size
+ *               bytes (never NULL), clobbered.
+ * dq, dk, dbeta (and a scalar gate's dalpha) are sums over the value rows,
+ * added up with float atomics: their last bits can differ from run to run.
+ * No output may overlap an input, another output or the workspace.  The
+ * arithmetic is fp32 for either input dtype.  Gate on key channels: not
+ * provided.
+ */
+size_t kda_prefill_backward_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                           int32_t d_k, int32_t d_v);
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* S0, const int32_t* cu_seqlens,
+                                const float* dO, const float* dS_T,
+                                int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                int32_t d_k, int32_t d_v, kda_dtype dt,
+                                float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                                float* dS0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same with one gate per (token, head): alpha and dalpha [n_tok, n_heads];
+ * alpha NULL = no gate (then dalpha is not written and may be NULL). */
+kda_status kda_prefill_backward_scalar_gate(const void* q, const void* k, const void* v,
+                                            const float* alpha, const float* beta,
+                                            const float* S0, const int32_t* cu_seqlens,
+                                            const float* dO, const float* dS_T,
+                                            int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                            int32_t d_k, int32_t d_v, kda_dtype dt,
+                                            float* dq, float* dk, float* dv, float* dalpha,
+                                            float* dbeta, float* dS0, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

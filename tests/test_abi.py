@@ -178,3 +178,59 @@ def test_binding_refuses_cpu_tensors(L):
     q = torch.zeros(4, 2, 64)
     with pytest.raises(ValueError):
         kda.kda_decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 64, 64))
+
+
+def test_backward_workspace_size(L):
+    """Backward workspace, 256-byte aligned parts: the schedule (n_seq int32), a state
+    checkpoint every 16 tokens of every (sequence, head) -- slots n_seq + n_tok // 16 + 1,
+    H x d_v x d_k fp32 each -- and each wave's 16 states of 8 rows (d_k fp32 each); one
+    wave per 8 value rows, (sequence, head) pairs padded to a multiple of 8."""
+    al = lambda x: (x + 255) // 256 * 256
+
+    def size(n_seq, n_tok, H, dk, dv):
+        waves = (n_seq * H + 7) // 8 * 8 * (dv // 8)
+        return al(n_seq * 4) + (n_seq + n_tok // 16 + 1) * H * dv * dk * 4 + waves * 16 * 8 * dk * 4
+
+    for shape in [(1, 256, 1, 64, 64), (4, 1000, 3, 128, 64), (3, 0, 2, 64, 128), (65, 4096, 8, 128, 128)]:
+        assert L.kda_prefill_backward_workspace_size(*shape) == size(*shape)
+    assert L.kda_prefill_backward_workspace_size(0, 16, 1, 64, 64) == 0
+    assert L.kda_prefill_backward_workspace_size(1, 16, 1, 96, 64) == 0
+
+
+def backward(L, fn="kda_prefill_backward", **kw):
+    M = 0x100000
+    args = dict(q=A, k=A + M, v=A + 2 * M, alpha=A + 3 * M, beta=A + 4 * M, S0=None, cu=None,
+                dO=A + 5 * M, dS_T=None, n_seq=2, n_tok=64, H=2, dk=64, dv=64, dt=1,
+                dq=A + 6 * M, dk_=A + 7 * M, dv_=A + 8 * M, dalpha=A + 9 * M, dbeta=A + 10 * M,
+                dS0=A + 11 * M, ws=A + 32 * M, ws_bytes=1 << 24, stream=None)
+    args.update(kw)
+    a = args
+    return getattr(L, fn)(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], a["cu"], a["dO"], a["dS_T"],
+                          a["n_seq"], a["n_tok"], a["H"], a["dk"], a["dv"], a["dt"], a["dq"], a["dk_"], a["dv_"],
+                          a["dalpha"], a["dbeta"], a["dS0"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["kda_prefill_backward", "kda_prefill_backward_scalar_gate"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(n_seq=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(n_tok=63), kda.KDA_ERR_INVALID_ARGUMENT),          # not a multiple of n_seq, no cu_seqlens
+    (dict(dO=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dq=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dbeta=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dq=A + 6 * 0x100000 + 8), kda.KDA_ERR_INVALID_ARGUMENT),   # misaligned
+    (dict(dv_=A + 8 * 0x100000 + 2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(dq=A + 0x100), kda.KDA_ERR_INVALID_ARGUMENT),               # dq overlaps q
+    (dict(dk_=A + 6 * 0x100000 + 0x100), kda.KDA_ERR_INVALID_ARGUMENT),  # dk overlaps dq
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+    (dict(ws_bytes=4096), kda.KDA_ERR_WORKSPACE),
+    (dict(ws=A + 11 * 0x100000), kda.KDA_ERR_INVALID_ARGUMENT),       # workspace overlaps dS0
+])
+def test_backward_rejects_on_host(L, fn, kw, status):
+    assert backward(L, fn, **kw) == status
+
+
+def test_backward_gate_needs_its_gradient(L):
+    assert backward(L, dalpha=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert backward(L, alpha=None) == kda.KDA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,75 @@
+"""GPU parity of the prefill backward (kda_prefill_backward, kda_prefill_backward_scalar_gate)
+against the fp64 backward oracle, through the C ABI.  The oracle side is pinned in
+test_oracle_backward by central finite differences of the forward oracle."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_72_amd import inputs as I
+from tests import helpers as Hh
+
+pytestmark = pytest.mark.gpu
+
+# fp32 arithmetic against fp64; gradients sum over up to d_v rows and many tokens
+TOL = dict(max_rel=2e-4, rms_rel=1e-4)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_72_amd import kda
+    kda.lib()
+    return torch
+
+
+def run(torch, inp, gate, varlen, with_dST=True, want_dS0=True, seed=0):
+    from gated_delta_rule_72_amd import kda
+    from oracle.backward import prefill_backward
+    dO, dS_T = I.make_backward_grads(9000 + seed, inp)
+    if not with_dST:
+        dS_T = None
+    d = Hh.upload_prefill(inp)
+    fn = kda.kda_prefill_backward if gate == "channel" else kda.kda_prefill_backward_scalar_gate
+    g = fn(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"] if varlen else None,
+           Hh.to_device(dO, "f32"), None if dS_T is None else Hh.to_device(dS_T, "f32"), n_seq=inp.n_seq,
+           want_dS0=want_dS0)
+    torch.cuda.synchronize()
+    ref = prefill_backward(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta,
+                           None if inp.S0 is None else inp.S0.astype(np.float64), inp.cu_seqlens, dO, dS_T, gate)
+    H = inp.H
+    sl = Hh.o_slices(inp.cu_seqlens, H)
+    for name in ("dq", "dk", "dv", "dbeta"):
+        Hh.check(name, Hh.from_device(g[name]), ref[name], sl, TOL)
+    if gate != "none":
+        Hh.check("dalpha", Hh.from_device(g["dalpha"]), ref["dalpha"], sl, TOL)
+    if want_dS0:
+        Hh.check("dS0", Hh.from_device(g["dS0"]), ref["dS0"], Hh.s_slices(inp.n_seq, H), TOL)
+    else:
+        assert g["dS0"] is None
+
+
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("lens,H,dk,dv,dtype,varlen", [
+    ([37, 1, 0, 20], 2, 64, 64, "f32", True),     # ragged blocks of 16, length 1, empty
+    ([50], 3, 128, 128, "f32", False),
+    ([33, 17], 2, 128, 64, "bf16", True),
+    ([40, 25], 2, 64, 128, "f32", True),
+    ([16, 16, 16], 1, 64, 64, "bf16", False),      # whole blocks only
+])
+def test_backward_matches_oracle(torch_cuda, gate, lens, H, dk, dv, dtype, varlen):
+    print(f"backward gate={gate} lens={lens} H={H} dk={dk} dv={dv} {dtype} varlen={varlen}", flush=True)
+    inp = I.make_prefill(9100 + sum(lens) + H + dk, lens, H, dk, dv, dtype, "exp_softplus", 0.02, gate)
+    run(torch_cuda, inp, gate, varlen, seed=sum(lens))
+
+
+def test_backward_without_state_gradients(torch_cuda):
+    print("backward: no dS_T, no dS0, no S0", flush=True)
+    inp = I.make_prefill(9201, [30, 45], 2, 128, 128, "f32", "sigmoid_n21", 0.0, "channel")
+    run(torch_cuda, inp, "channel", True, with_dST=False, want_dS0=False, seed=1)
+
+
+def test_backward_longer_sequences(torch_cuda):
+    print("backward: 2 x 400 tokens, H=2, d=128, bf16", flush=True)
+    inp = I.make_prefill(9202, [400, 400], 2, 128, 128, "bf16", "exp_softplus", 0.02, "channel")
+    run(torch_cuda, inp, "channel", False, seed=2)
