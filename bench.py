@@ -13,12 +13,13 @@ work on an idle MI355X run up to 25% slower).
 
 The same workload with one forget gate per (token, head) (kda_prefill_scalar_gate,
 Gated DeltaNet) is timed as well and reported under "scalar_gate", the gate on key
-channels (kda_prefill_key_gate) under "key_gate", and the tiny fp32, single-layer and varlen
+channels (kda_prefill_key_gate) under "key_gate", the backward of the batched call
+(kda_prefill_backward, gradients of every input) under "backward", and the tiny fp32, single-layer and varlen
 prefill workloads and one long sequence under "workloads"; after the decode workload, its
 state taking 4 tokens per sequence in one in-place kda_prefill call ("multi_token_decode").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
-                       [--no-scalar-gate] [--no-workloads]
+                       [--no-scalar-gate] [--no-backward] [--no-workloads]
        python bench.py --workloads-only     (only the tiny fp32, single-layer and varlen prefill
                                              workloads, one JSON line)
        python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
@@ -84,6 +85,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-scalar-gate", action="store_true")
     p.add_argument("--no-workloads", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--workloads-only", action="store_true")
     p.add_argument("--traffic-probe", action="store_true")
     p.add_argument("--summarize", default=None)
@@ -420,6 +422,51 @@ def bench_key_gate(args, torch, kda, I):
                 parity=dict(o_max_rel=m, o_rms_rel=r, S_max_rel=ms_, S_rms_rel=rs, scope="(sequence 1, head 7)"))
 
 
+def bench_backward(args, torch, kda, I):
+    """kda_prefill_backward (gradients of q, k, v, alpha, beta, S0) on the batched prefill
+    workload with dO, dS_T ~ N(0, 1): the token-recurrent backward kernel; parity of every
+    gradient on one sampled (sequence, head) pair against the fp64 backward oracle."""
+    from oracle.backward import prefill_backward
+    dev = "cuda:0"
+    inp = I.workload_prefill(3)
+    dO, dS_T = I.make_backward_grads(9300, inp)
+    q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+    alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
+    dO_d, dST_d = upload(dO, "f32", dev), upload(dS_T, "f32", dev)
+    B, H = inp.n_seq, inp.H
+    ws = torch.empty(kda.backward_workspace_size(B, inp.n_tok, H, inp.dk, inp.dv), dtype=torch.uint8, device=dev)
+
+    def step():
+        return kda.kda_prefill_backward(q, k, v, alpha, beta, S0, None, dO_d, dST_d, n_seq=B, workspace=ws)
+
+    settle(step, 1, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 3
+    e0.record()
+    for _ in range(n):
+        g = step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    n_, h = 2, 11
+    s_, e_ = int(inp.cu_seqlens[n_]), int(inp.cu_seqlens[n_ + 1])
+    sub = lambda x: x[s_:e_, h:h + 1]
+    ref = prefill_backward(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")), sub(inp.alpha), sub(inp.beta),
+                           inp.S0[n_:n_ + 1, h:h + 1].astype(np.float64), [0, e_ - s_], sub(dO),
+                           dS_T[n_:n_ + 1, h:h + 1], "channel")
+    parity = {}
+    for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        m, r = rel(g[name][s_:e_, h].cpu().numpy().astype(np.float64), ref[name][:, 0])
+        parity[name] = dict(max_rel=m, rms_rel=r)
+    m, r = rel(g["dS0"][n_, h].cpu().numpy().astype(np.float64), ref["dS0"][0, 0])
+    parity["dS0"] = dict(max_rel=m, rms_rel=r)
+    parity["scope"] = f"(sequence {n_}, head {h}), whole sequence"
+    return dict(workload="batched prefill workload (value-channel gate), kda_prefill_backward with dO and dS_T "
+                         "drawn N(0,1): token-recurrent backward kernel",
+                ms_per_call=round(ms, 3), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
+                workspace_bytes=ws.numel(), parity=parity)
+
+
 def bench_multi_token_decode(args, torch, kda, I, T=4):
     """The decode workload's state (B=256 sequences x H=32 heads, d=128, fp32, 537 MB) taking
     T new bf16 tokens per sequence in one kda_prefill call, continued in place (S_T = S0):
@@ -580,6 +627,10 @@ def main():
         line["key_gate"] = bench_key_gate(args, torch, kda, I)
         log(f"[bench] key-gate prefill: {line['key_gate']['tokens_per_s']:.4g} tokens/s, "
             f"{line['key_gate']['ms_per_call']:.3f} ms per call")
+    if not args.no_backward and not args.no_scalar_gate:
+        line["backward"] = bench_backward(args, torch, kda, I)
+        log(f"[bench] prefill backward: {line['backward']['ms_per_call']:.2f} ms per call, "
+            f"{line['backward']['tokens_per_s']:.4g} tokens/s")
     if not args.no_workloads:
         line["workloads"] = bench_other_workloads(args, torch, kda, I)
     if not args.no_decode:
