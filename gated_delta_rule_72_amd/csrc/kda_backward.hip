@@ -2,9 +2,10 @@
 //
 // Page "Kimi (AI)", section "Kimi Delta Attention (KDA)" gives the per-token
 // steps (forget S~ = diag(alpha_t) S, predict v~ = S~ k_t, update
-// S_t = S~ + beta_t (v_t - v~) k_t^T, read-out o_t = S_t q_t); the page
-// "Kimi Linear" presents the chunked form of such layers as a training
-// method, which needs their gradients.  With a_t = S_{t-1} k_t,
+// S_t = S~ + beta_t (v_t - v~) k_t^T, read-out o_t = S_t q_t); the
+// transcript page ("Per dins de Kimi K3 ..."), where it turns to training,
+// says the model is trained with the chunk-wise parallel algorithm, which
+// needs these gradients.  With a_t = S_{t-1} k_t,
 // u_t = beta_t (v_t - alpha_t a_t) and G_t = dL/dS_t, walking the tokens in
 // reverse:
 //     G_t     += dO_t q_t^T

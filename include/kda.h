@@ -204,9 +204,9 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
 /*
  * Backward of the prefill (training): the gradients of a scalar loss L with
  * respect to q, k, v, alpha, beta and S0, given dO = dL/do and dS_T = dL/dS_T.
- * The page "Kimi Linear", in its section on the linear-attention family,
- * presents the chunked form of these layers as the way they are trained; the
- * gradients follow from the per-token steps of page "Kimi (AI)", section
+ * The transcript page ("Per dins de Kimi K3 ..."), where it turns to
+ * training, says the model is trained with the chunk-wise parallel algorithm;
+ * the gradients follow from the per-token steps of page "Kimi (AI)", section
  * "Kimi Delta Attention (KDA)", by the chain rule taken in reverse token
  * order (the recurrence's states are recomputed from checkpoints every 16
  * tokens, kept in the workspace).

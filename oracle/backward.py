@@ -10,9 +10,9 @@ read-out uses the updated state:
     predict:  v~ = S~ k_t           ( = alpha_t (.) a_t with a_t = S_{t-1} k_t )
     update:   S_t = S~ + beta_t (v_t - v~) k_t^T      ( u_t = beta_t (v_t - v~) )
     read-out: o_t = S_t q_t
-The page "Kimi Linear" (the section on the linear-attention family) presents
-the chunked form as the way such layers are trained, which needs these
-gradients.  For a scalar loss L with dL/do_t = dO_t and dL/dS_T = dS_T, the
+The transcript page ("Per dins de Kimi K3 ..."), where it turns to training,
+says the model is trained with the chunk-wise parallel algorithm, which needs
+these gradients.  For a scalar loss L with dL/do_t = dO_t and dL/dS_T = dS_T, the
 chain rule taken through the steps in reverse order, token by token, with
 G_t = dL/dS_t (everything that depends on S_t) is:
     G_t      = (gradient flowing from S_{t+1}) + dO_t q_t^T
