@@ -29,7 +29,9 @@
 
 namespace kda {
 
-constexpr int BWD_BLOCK = 16;  // tokens between state checkpoints
+constexpr int BWD_BLOCK = 16;    // tokens between state checkpoints
+constexpr int BWD_ROWS = 64;     // value rows per workgroup
+constexpr int BWD_THREADS = 512; // eight waves of 8 rows
 
 // Checkpoint slot of block b of a sequence that starts at token t0 and is the
 // n-th: n + t0 / 16 + b.  Consecutive sequences never share a slot (a sequence
@@ -47,6 +49,32 @@ __device__ __forceinline__ float sum_rows8(float x) {
     return x;
 }
 
+// Reduce-scatter over the wave's 8 rows: x holds V = 4 M values (value c of chunk
+// m = c / 4, element c % 4) summed over the lane's row; on return lane group g
+// (lane / 8) holds in r[0 .. V/8) the sums over all 8 rows of values
+// c = g V / 8 + i.  Three butterfly steps, each keeping half of the values and
+// exchanging the other half with the partner group (xor 32, 16, 8 lanes).
+template <int V>
+__device__ __forceinline__ void reduce_scatter_rows8(const float (&x)[V], float (&r)[V / 8], int lane) {
+    float a[V / 2], b[V / 4];
+    const bool h2 = lane & 32, h1 = lane & 16, h0 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const float send = h2 ? x[i] : x[i + V / 2];
+        a[i] = (h2 ? x[i + V / 2] : x[i]) + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+        const float send = h1 ? a[i] : a[i + V / 4];
+        b[i] = (h1 ? a[i + V / 4] : a[i]) + __shfl_xor(send, 16);
+    }
+#pragma unroll
+    for (int i = 0; i < V / 8; ++i) {
+        const float send = h0 ? b[i] : b[i + V / 8];
+        r[i] = (h0 ? b[i + V / 8] : b[i]) + __shfl_xor(send, 8);
+    }
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -54,7 +82,7 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 }
 
 template <typename T, int DK, int DV, int GATE>
-__global__ __launch_bounds__(64) void backward_kernel(
+__global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
@@ -62,23 +90,32 @@ __global__ __launch_bounds__(64) void backward_kernel(
     int n_seq, int n_tok, int n_heads, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
     float* __restrict__ dS0, float* __restrict__ ckpt, float* __restrict__ sbuf) {
-    constexpr int NVB = DV / 8;
     constexpr int M = DK / 32;
-    const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
+    constexpr int NW = BWD_THREADS / 64;   // waves per workgroup, 8 rows each
+    constexpr int RW = 2 * DK + 4;         // one wave's row sums of a token: dq, dk, dbeta, scalar dalpha (padded)
+    constexpr int NSUM = 2 * DK + (GATE == GATE_SCALAR ? 2 : 1);
+    __shared__ float red[2][NW][RW];       // double-buffered by token
+    const Unit u = map_unit(blockIdx.x, n_seq, n_heads, DV / BWD_ROWS, n_tok, cu_seqlens, order);
     if (!u.valid) return;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int j = lane & 7;
-    const int row = u.vblk * 8 + (lane >> 3);
+    const int row = u.vblk * BWD_ROWS + w * 8 + (lane >> 3);
     const int64_t H = n_heads;
     const int h = u.head;
     const int64_t len = u.t1 - u.t0;
     const int nblk = static_cast<int>((len + BWD_BLOCK - 1) / BWD_BLOCK);
     const int64_t slot0 = u.seq + u.t0 / BWD_BLOCK;
     auto ck = [&](int b) { return ckpt + (((slot0 + b) * H + h) * DV + row) * DK; };
-    float* my = sbuf + static_cast<int64_t>(blockIdx.x) * BWD_BLOCK * 8 * DK + (lane >> 3) * DK;
+    float* my = sbuf + (static_cast<int64_t>(blockIdx.x) * NW + w) * BWD_BLOCK * 8 * DK + (lane >> 3) * DK;
     auto col = [&](int m) { return 4 * (j + 8 * m); };
+    // key channel of value c = (lane / 8) M / 2 + i after reduce_scatter_rows8
+    auto vcol = [&](int i) {
+        const int c = (lane >> 3) * (M / 2) + i;
+        return 4 * (j + 8 * (c / 4)) + c % 4;
+    };
 
-    struct Tok { f32x4 k[M], q[M]; float v, a, b; };
+    struct Tok { f32x4 k[M], q[M]; float v, a, b, go; };
     auto load = [&](Tok& x, int64_t t) {
         const int64_t th = t * H + h;
 #pragma unroll
@@ -89,6 +126,7 @@ __global__ __launch_bounds__(64) void backward_kernel(
         x.v = Elem<T>::load(v + th * DV + row);
         x.a = GATE == GATE_CHANNEL ? alpha[th * DV + row] : GATE == GATE_SCALAR ? alpha[th] : 1.f;
         x.b = beta[th];
+        x.go = dO[th * DV + row];
     };
     // a = s . k for this lane's row (all 8 lanes of the row get it)
     auto dot_k = [&](const f32x4* s, const Tok& x) {
@@ -99,27 +137,32 @@ __global__ __launch_bounds__(64) void backward_kernel(
             for (int e = 0; e < 4; ++e) p += s[m][e] * x.k[m][e];
         return sum8(p);
     };
-
-    // forward: checkpoints at every block start
-    f32x4 s[M];
-    const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row) * DK;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t t = u.t0; t < u.t1; ++t) {
-        const int64_t i = t - u.t0;
-        if (i % BWD_BLOCK == 0) {
-            float* c = ck(static_cast<int>(i / BWD_BLOCK));
-#pragma unroll
-            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(c + col(m)) = s[m];
-        }
-        Tok x;
-        load(x, t);
+    auto advance = [&](f32x4* s, const Tok& x) {
         const float uu = x.b * (x.v - x.a * dot_k(s, x));
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[m][e] = x.a * s[m][e] + uu * x.k[m][e];
+    };
+
+    // forward: checkpoints at every block start; each token loaded one token ahead
+    f32x4 s[M];
+    const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row) * DK;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    Tok x, xn;
+    if (len > 0) load(x, u.t0);
+    for (int64_t t = u.t0; t < u.t1; ++t) {
+        const int64_t i = t - u.t0;
+        if (t + 1 < u.t1) load(xn, t + 1);
+        if (i % BWD_BLOCK == 0) {
+            float* c = ck(static_cast<int>(i / BWD_BLOCK));
+#pragma unroll
+            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(c + col(m)) = s[m];
+        }
+        advance(s, x);
+        x = xn;
     }
 
     // backward
@@ -127,6 +170,7 @@ __global__ __launch_bounds__(64) void backward_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m)
         G[m] = dS_T ? *reinterpret_cast<const f32x4*>(dS_T + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    int par = 0;
     for (int b = nblk - 1; b >= 0; --b) {
         const int64_t tb = u.t0 + static_cast<int64_t>(b) * BWD_BLOCK;
         const int nb = static_cast<int>(u.t1 - tb < BWD_BLOCK ? u.t1 - tb : BWD_BLOCK);
@@ -134,41 +178,41 @@ __global__ __launch_bounds__(64) void backward_kernel(
         const float* c = ck(b);
 #pragma unroll
         for (int m = 0; m < M; ++m) s[m] = *reinterpret_cast<const f32x4*>(c + col(m));
+        load(x, tb);
         for (int i = 0; i < nb; ++i) {
+            if (i + 1 < nb) load(xn, tb + i + 1);
 #pragma unroll
             for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(my + i * 8 * DK + col(m)) = s[m];
-            Tok x;
-            load(x, tb + i);
-            const float uu = x.b * (x.v - x.a * dot_k(s, x));
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[m][e] = x.a * s[m][e] + uu * x.k[m][e];
+            advance(s, x);
+            x = xn;
         }
+        f32x4 sp[M], spn[M];
+        load(x, tb + nb - 1);
+#pragma unroll
+        for (int m = 0; m < M; ++m) sp[m] = *reinterpret_cast<const f32x4*>(my + (nb - 1) * 8 * DK + col(m));
         for (int i = nb - 1; i >= 0; --i) {
             const int64_t t = tb + i;
             const int64_t th = t * H + h;
-            Tok x;
-            load(x, t);
-            f32x4 sp[M];
+            if (i > 0) {
+                load(xn, t - 1);
 #pragma unroll
-            for (int m = 0; m < M; ++m) sp[m] = *reinterpret_cast<const f32x4*>(my + i * 8 * DK + col(m));
+                for (int m = 0; m < M; ++m) spn[m] = *reinterpret_cast<const f32x4*>(my + (i - 1) * 8 * DK + col(m));
+            }
             const float a = dot_k(sp, x);
             const float uu = x.b * (x.v - x.a * a);
-            const float go = dO[th * DV + row];
+            float* rw = red[par][w];
             // dq_t = S_t^T dO_t, with S_t = alpha S_{t-1} + u k^T; G_t += dO_t q_t^T
+            float pq[4 * M], rq[M / 2];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                f32x4 pq;
+            for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pq[e] = sum_rows8(go * (x.a * sp[m][e] + uu * x.k[m][e]));
-                    G[m][e] += go * x.q[m][e];
+                    pq[4 * m + e] = x.go * (x.a * sp[m][e] + uu * x.k[m][e]);
+                    G[m][e] += x.go * x.q[m][e];
                 }
-                if (lane < 8)
+            reduce_scatter_rows8<4 * M>(pq, rq, lane);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicAdd(dq + th * DK + col(m) + e, pq[e]);
-            }
+            for (int i = 0; i < M / 2; ++i) rw[vcol(i)] = rq[i];
             float pdu = 0.f, pga = 0.f;
 #pragma unroll
             for (int m = 0; m < M; ++m)
@@ -181,32 +225,44 @@ __global__ __launch_bounds__(64) void backward_kernel(
             const float da = -x.b * x.a * du;
             const float dal = sum8(pga) - x.b * a * du;
             // dk_t = G^T u + S_{t-1}^T da
+            float pk[4 * M], rk[M / 2];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                f32x4 pk;
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pk[e] = sum_rows8(uu * G[m][e] + da * sp[m][e]);
-                if (lane < 8)
+                for (int e = 0; e < 4; ++e) pk[4 * m + e] = uu * G[m][e] + da * sp[m][e];
+            reduce_scatter_rows8<4 * M>(pk, rk, lane);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicAdd(dk + th * DK + col(m) + e, pk[e]);
-            }
+            for (int i = 0; i < M / 2; ++i) rw[DK + vcol(i)] = rk[i];
             // the row's own gradients (every lane of the row holds them; lane 0 of the eight writes)
-            const float dbr = du * (x.v - x.a * a);
             if (j == 0) {
                 dv[th * DV + row] = x.b * du;
                 if constexpr (GATE == GATE_CHANNEL) dalpha[th * DV + row] = dal;
             }
-            const float dbs = sum_rows8(dbr);
-            if (lane == 0) atomicAdd(dbeta + th, dbs);
-            if constexpr (GATE == GATE_SCALAR) {
-                const float das = sum_rows8(dal);
-                if (lane == 0) atomicAdd(dalpha + th, das);
+            const float dbs = sum_rows8(du * (x.v - x.a * a));
+            const float das = GATE == GATE_SCALAR ? sum_rows8(dal) : 0.f;
+            if (lane == 0) {
+                rw[2 * DK] = dbs;
+                rw[2 * DK + 1] = das;
             }
             // G_{t-1} = alpha G_t + da k^T
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) G[m][e] = x.a * G[m][e] + da * x.k[m][e];
+            // the workgroup's row sums of this token: one atomic add per value
+            block_sync();
+            if (tid < NSUM) {
+                float acc = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) acc += red[par][ww][tid];
+                float* dst = tid < DK ? dq + th * DK + tid : tid < 2 * DK ? dk + th * DK + (tid - DK)
+                                                         : tid == 2 * DK ? dbeta + th : dalpha + th;
+                atomicAdd(dst, acc);
+            }
+            par ^= 1;  // the next token's sums go to the other buffer; this one is read before the next barrier
+            x = xn;
+#pragma unroll
+            for (int m = 0; m < M; ++m) sp[m] = spn[m];
         }
     }
     if (dS0) {
@@ -244,8 +300,9 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t stream) {
 
 template <typename T, int DK, int DV, int GATE>
 hipError_t launch_bwd_t(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, hipStream_t stream) {
-    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / 8);
-    hipLaunchKernelGGL((backward_kernel<T, DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream,
+    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / BWD_ROWS);
+    hipLaunchKernelGGL((backward_kernel<T, DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(BWD_THREADS), 0,
+                       stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.alpha,
                        a.beta, a.S0, a.cu_seqlens, order, a.dO, a.dS_T, a.n_seq, a.n_tok, a.n_heads, a.dq, a.dk,
                        a.dv, a.dalpha, a.dbeta, a.dS0, ckpt, sbuf);
