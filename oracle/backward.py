@@ -25,7 +25,15 @@ G_t = dL/dS_t (everything that depends on S_t) is:
     dL/dS_{t-1} = diag(alpha_t) G_t + da_t k_t^T
 and dS0 = dL/dS_{-1} after the first token.  A gate shared by all rows (one
 scalar per token and head) receives the sum of dalpha_t over the rows; no
-gate (alpha = 1) has no alpha gradient.  The states S_{t-1} are kept from a
+gate (alpha = 1) has no alpha gradient.
+With the gate on key channels instead, S~ = S_{t-1} diag(alpha_t) (alpha_t in
+R^{d_k}), a_t = S~ k_t, u_t = beta_t (v_t - a_t), S_t = S~ + u_t k_t^T:
+    G_t      = (gradient flowing from S_{t+1}) + dO_t q_t^T,   dq_t = S_t^T dO_t
+    du_t     = G_t k_t,  da_t = -beta_t du_t,  dv_t = beta_t du_t,
+    dbeta_t  = du_t . (v_t - a_t),  dk_t = G_t^T u_t + S~^T da_t,
+    dS~      = G_t + da_t k_t^T,
+    dalpha_t = colsum(dS~ (.) S_{t-1})           (one value per key channel)
+    dL/dS_{-1+t} = dS~ diag(alpha_t).  The states S_{t-1} are kept from a
 plain forward pass.  Plain numpy, per (sequence, head), one token at a time.
 Pinned in tests by central finite differences of the forward oracle.
 """
@@ -38,7 +46,8 @@ def prefill_backward(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, gate="
     """Gradients of L = sum(dO * o) + sum(dS_T * S_T) for one prefill call.
 
     q, k: [n_tok, H, d_k]; v, dO: [n_tok, H, d_v]; beta: [n_tok, H];
-    alpha: [n_tok, H, d_v] (gate "channel"), [n_tok, H] ("scalar") or None ("none");
+    alpha: [n_tok, H, d_v] (gate "channel"), [n_tok, H] ("scalar"), None ("none") or
+    [n_tok, H, d_k] ("key": the gate on key channels);
     S0, dS_T: [n_seq, H, d_v, d_k] or None (zeros); cu_seqlens: [n_seq + 1].
     Returns dict with dq, dk, dv, dalpha (None for "none"), dbeta, dS0 (float64).
     """
@@ -48,6 +57,8 @@ def prefill_backward(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, gate="
     dv_ = v.shape[2]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     n_seq = cu.shape[0] - 1
+    if gate == "key":
+        return _backward_key_gate(q, k, v, f(alpha), beta, S0, cu, dO, dS_T)
     if gate == "channel":
         a_rows = f(alpha)
     elif gate == "scalar":
@@ -88,4 +99,41 @@ def prefill_backward(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, gate="
             out["dS0"][n, h] = G_next
     out["dalpha"] = (dalpha_rows if gate == "channel" else dalpha_rows.sum(axis=2) if gate == "scalar"
                      else None)
+    return out
+
+
+def _backward_key_gate(q, k, v, alpha, beta, S0, cu, dO, dS_T):
+    n_tok, H, dk_ = q.shape
+    dv_ = v.shape[2]
+    n_seq = cu.shape[0] - 1
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v), dalpha=np.zeros_like(alpha),
+               dbeta=np.zeros((n_tok, H)), dS0=np.zeros((n_seq, H, dv_, dk_)))
+    for n in range(n_seq):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for h in range(H):
+            S = np.zeros((dv_, dk_)) if S0 is None else S0[n, h].copy()
+            states = [S]
+            for t in range(s, e):
+                St = S * alpha[t, h][None, :]
+                u = beta[t, h] * (v[t, h] - St @ k[t, h])
+                S = St + np.outer(u, k[t, h])
+                states.append(S)
+            G_next = np.zeros((dv_, dk_)) if dS_T is None else dS_T[n, h].copy()
+            for t in range(e - 1, s - 1, -1):
+                Sp, Snew = states[t - s], states[t - s + 1]
+                al, kt, qt, vt, bt, dOt = alpha[t, h], k[t, h], q[t, h], v[t, h], beta[t, h], dO[t, h]
+                St = Sp * al[None, :]
+                a = St @ kt
+                u = bt * (vt - a)
+                G = G_next + np.outer(dOt, qt)
+                out["dq"][t, h] = Snew.T @ dOt
+                du = G @ kt
+                da = -bt * du
+                out["dv"][t, h] = bt * du
+                out["dbeta"][t, h] = du @ (vt - a)
+                out["dk"][t, h] = G.T @ u + St.T @ da
+                dSt = G + np.outer(da, kt)
+                out["dalpha"][t, h] = (dSt * Sp).sum(axis=0)
+                G_next = dSt * al[None, :]
+            out["dS0"][n, h] = G_next
     return out

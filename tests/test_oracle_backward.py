@@ -27,17 +27,18 @@ def make_case(seed, lens, H, dk, dv, gate):
              dO=rng.standard_normal((n, H, dv)), dS_T=rng.standard_normal((len(lens), H, dv, dk)),
              cu=np.concatenate([[0], np.cumsum(lens)]).astype(np.int64))
     c["alpha"] = {"channel": dyadic(rng, (n, H, dv), 0.5, 1.0), "scalar": dyadic(rng, (n, H), 0.5, 1.0),
-                  "none": None}[gate]
+                  "none": None, "key": dyadic(rng, (n, H, dk), 0.5, 1.0)}[gate]
     return c
 
 
 def loss(c, gate):
-    fwd = {"channel": oracle.prefill, "scalar": oracle.prefill_scalar_gate, "none": oracle.prefill_scalar_gate}[gate]
+    fwd = {"channel": oracle.prefill, "scalar": oracle.prefill_scalar_gate, "none": oracle.prefill_scalar_gate,
+           "key": oracle.prefill_key_gate}[gate]
     o, S = fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["S0"], c["cu"])
     return float((o * c["dO"]).sum() + (S * c["dS_T"]).sum())
 
 
-@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none", "key"])
 def test_backward_matches_central_differences_of_the_forward(gate):
     c = make_case(11, [4, 0, 3], 2, 4, 3, gate)
     g = prefill_backward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["S0"], c["cu"], c["dO"], c["dS_T"], gate)
