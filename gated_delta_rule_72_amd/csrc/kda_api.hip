@@ -126,7 +126,7 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const float*
 }
 
 
-// Shared body of kda_prefill_backward and kda_prefill_backward_scalar_gate.
+// Shared body of kda_prefill_backward and its scalar-gate and key-gate forms.
 kda_status backward_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                          const float* S0, const int32_t* cu_seqlens, const float* dO, const float* dS_T,
                          int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt,
@@ -145,10 +145,14 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const floa
     const void* scal[] = {alpha, beta, cu_seqlens, dO, dv, dalpha, dbeta};
     for (const void* p : scal)
         if (p && !aligned(p, 4)) return KDA_ERR_INVALID_ARGUMENT;
+    if (gate == kda::GATE_KEY && alpha && !aligned(alpha)) return KDA_ERR_INVALID_ARGUMENT;  // float4 loads
     const size_t eb = elem_bytes(dt);
     const size_t nt = static_cast<size_t>(n_tok), nh = static_cast<size_t>(n_heads);
     const size_t qk_bytes = nt * nh * d_k * eb, v_bytes = nt * nh * d_v * eb;
-    const size_t a_bytes = gate == kda::GATE_CHANNEL ? nt * nh * d_v * 4 : gate == kda::GATE_SCALAR ? nt * nh * 4 : 0;
+    const size_t a_bytes = gate == kda::GATE_CHANNEL  ? nt * nh * d_v * 4
+                           : gate == kda::GATE_KEY    ? nt * nh * d_k * 4
+                           : gate == kda::GATE_SCALAR ? nt * nh * 4
+                                                      : 0;
     const size_t b_bytes = nt * nh * 4, s_bytes = static_cast<size_t>(n_seq) * nh * d_v * d_k * 4;
     const size_t cu_bytes = cu_seqlens ? (static_cast<size_t>(n_seq) + 1) * 4 : 0;
     const size_t need = kda::prefill_backward_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v);
@@ -267,6 +271,16 @@ kda_status kda_prefill_backward_scalar_gate(const void* q, const void* k, const 
     return backward_impl(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, n_tok, n_heads, d_k, d_v, dt, dq, dk,
                          dv, dalpha, dbeta, dS0, workspace, workspace_bytes, stream,
                          alpha ? kda::GATE_SCALAR : kda::GATE_NONE);
+}
+
+kda_status kda_prefill_backward_key_gate(const void* q, const void* k, const void* v, const float* alpha,
+                                         const float* beta, const float* S0, const int32_t* cu_seqlens,
+                                         const float* dO, const float* dS_T, int32_t n_seq, int32_t n_tok,
+                                         int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt, float* dq,
+                                         float* dk, float* dv, float* dalpha, float* dbeta, float* dS0,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_impl(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, n_tok, n_heads, d_k, d_v, dt, dq, dk,
+                         dv, dalpha, dbeta, dS0, workspace, workspace_bytes, stream, kda::GATE_KEY);
 }
 
 }  // extern "C"

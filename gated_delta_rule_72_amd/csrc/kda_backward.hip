@@ -14,7 +14,12 @@
 //     dv_t     = beta_t du_t             dbeta_t = du_t . (v_t - alpha_t a_t)
 //     dalpha_t = rowsum(G_t (.) S_{t-1}) - beta_t a_t du_t
 //     G_{t-1}  = diag(alpha_t) G_t + da_t k_t^T
-// Rows of the state are independent (the gate scales rows), so one wave owns
+// With the gate on key channels, S~ = S_{t-1} diag(alpha_t), a_t = S~ k_t,
+// u_t = beta_t (v_t - a_t): da_t = -beta_t du_t, dk_t = G_t^T u_t + S~^T da_t,
+// dalpha_t = column sums of (G_t + da_t k_t^T) (.) S_{t-1} and
+// G_{t-1} = (G_t + da_t k_t^T) diag(alpha_t).
+// Rows of the state are independent (every gate form updates each row on its
+// own), so one wave owns
 // 8 value rows of one (sequence, head), 8 lanes per row as in the forward
 // kernel: dv and a value-channel dalpha are per row and stored directly; dq,
 // dk, dbeta and a scalar dalpha are sums over rows, reduced over the wave's
@@ -92,8 +97,11 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     float* __restrict__ dS0, float* __restrict__ ckpt, float* __restrict__ sbuf) {
     constexpr int M = DK / 32;
     constexpr int NW = BWD_THREADS / 64;   // waves per workgroup, 8 rows each
-    constexpr int RW = 2 * DK + 4;         // one wave's row sums of a token: dq, dk, dbeta, scalar dalpha (padded)
-    constexpr int NSUM = 2 * DK + (GATE == GATE_SCALAR ? 2 : 1);
+    constexpr bool KEY = GATE == GATE_KEY;
+    // one wave's row sums of a token: dq, dk, (key-channel dalpha,) dbeta, scalar dalpha; padded
+    constexpr int OFF_DB = KEY ? 3 * DK : 2 * DK;
+    constexpr int RW = OFF_DB + 4;
+    constexpr int NSUM = OFF_DB + (GATE == GATE_SCALAR ? 2 : 1);
     __shared__ float red[2][NW][RW];       // double-buffered by token
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, DV / BWD_ROWS, n_tok, cu_seqlens, order);
     if (!u.valid) return;
@@ -115,13 +123,14 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
         return 4 * (j + 8 * (c / 4)) + c % 4;
     };
 
-    struct Tok { f32x4 k[M], q[M]; float v, a, b, go; };
+    struct Tok { f32x4 k[M], q[M], ak[KEY ? M : 1]; float v, a, b, go; };
     auto load = [&](Tok& x, int64_t t) {
         const int64_t th = t * H + h;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             x.k[m] = Elem<T>::load4(k + th * DK + col(m));
             x.q[m] = Elem<T>::load4(q + th * DK + col(m));
+            if constexpr (KEY) x.ak[m] = *reinterpret_cast<const f32x4*>(alpha + th * DK + col(m));
         }
         x.v = Elem<T>::load(v + th * DV + row);
         x.a = GATE == GATE_CHANNEL ? alpha[th * DV + row] : GATE == GATE_SCALAR ? alpha[th] : 1.f;
@@ -138,6 +147,12 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
         return sum8(p);
     };
     auto advance = [&](f32x4* s, const Tok& x) {
+        if constexpr (KEY) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[m][e] *= x.ak[m][e];
+        }
         const float uu = x.b * (x.v - x.a * dot_k(s, x));
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -198,16 +213,23 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
 #pragma unroll
                 for (int m = 0; m < M; ++m) spn[m] = *reinterpret_cast<const f32x4*>(my + (i - 1) * 8 * DK + col(m));
             }
-            const float a = dot_k(sp, x);
+            // the gated state: S~ = S_{t-1} diag(alpha) for the gate on key channels; for the
+            // others S_{t-1} itself, with the row gate applied through x.a below
+            f32x4 st[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[m][e] = KEY ? sp[m][e] * x.ak[m][e] : sp[m][e];
+            const float a = dot_k(st, x);
             const float uu = x.b * (x.v - x.a * a);
             float* rw = red[par][w];
-            // dq_t = S_t^T dO_t, with S_t = alpha S_{t-1} + u k^T; G_t += dO_t q_t^T
+            // dq_t = S_t^T dO_t, with S_t = alpha S_{t-1} + u k^T (S~ + u k^T); G_t += dO_t q_t^T
             float pq[4 * M], rq[M / 2];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pq[4 * m + e] = x.go * (x.a * sp[m][e] + uu * x.k[m][e]);
+                    pq[4 * m + e] = x.go * (x.a * st[m][e] + uu * x.k[m][e]);
                     G[m][e] += x.go * x.q[m][e];
                 }
             reduce_scatter_rows8<4 * M>(pq, rq, lane);
@@ -224,12 +246,12 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
             const float du = sum8(pdu);
             const float da = -x.b * x.a * du;
             const float dal = sum8(pga) - x.b * a * du;
-            // dk_t = G^T u + S_{t-1}^T da
+            // dk_t = G^T u + S_{t-1}^T da (S~^T da)
             float pk[4 * M], rk[M / 2];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pk[4 * m + e] = uu * G[m][e] + da * sp[m][e];
+                for (int e = 0; e < 4; ++e) pk[4 * m + e] = uu * G[m][e] + da * st[m][e];
             reduce_scatter_rows8<4 * M>(pk, rk, lane);
 #pragma unroll
             for (int i = 0; i < M / 2; ++i) rw[DK + vcol(i)] = rk[i];
@@ -241,22 +263,41 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
             const float dbs = sum_rows8(du * (x.v - x.a * a));
             const float das = GATE == GATE_SCALAR ? sum_rows8(dal) : 0.f;
             if (lane == 0) {
-                rw[2 * DK] = dbs;
-                rw[2 * DK + 1] = das;
+                rw[OFF_DB] = dbs;
+                rw[OFF_DB + 1] = das;
             }
-            // G_{t-1} = alpha G_t + da k^T
+            if constexpr (KEY) {
+                // dS~ = G_t + da k^T; dalpha_t = column sums of dS~ (.) S_{t-1}; G_{t-1} = dS~ diag(alpha)
+                float pa[4 * M], ra[M / 2];
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+                for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) G[m][e] = x.a * G[m][e] + da * x.k[m][e];
+                    for (int e = 0; e < 4; ++e) {
+                        const float ds = G[m][e] + da * x.k[m][e];
+                        pa[4 * m + e] = ds * sp[m][e];
+                        G[m][e] = ds * x.ak[m][e];
+                    }
+                reduce_scatter_rows8<4 * M>(pa, ra, lane);
+#pragma unroll
+                for (int i = 0; i < M / 2; ++i) rw[2 * DK + vcol(i)] = ra[i];
+            } else {
+                // G_{t-1} = alpha G_t + da k^T
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) G[m][e] = x.a * G[m][e] + da * x.k[m][e];
+            }
             // the workgroup's row sums of this token: one atomic add per value
             block_sync();
             if (tid < NSUM) {
                 float acc = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) acc += red[par][ww][tid];
-                float* dst = tid < DK ? dq + th * DK + tid : tid < 2 * DK ? dk + th * DK + (tid - DK)
-                                                         : tid == 2 * DK ? dbeta + th : dalpha + th;
+                float* dst = tid < DK                ? dq + th * DK + tid
+                             : tid < 2 * DK          ? dk + th * DK + (tid - DK)
+                             : tid < OFF_DB          ? dalpha + th * DK + (tid - 2 * DK)
+                             : tid == OFF_DB         ? dbeta + th
+                                                     : dalpha + th;
                 atomicAdd(dst, acc);
             }
             par ^= 1;  // the next token's sums go to the other buffer; this one is read before the next barrier
@@ -325,7 +366,7 @@ hipError_t launch_bwd_type(const BackwardArgs& a, const int32_t* order, float* c
         case GATE_CHANNEL: return launch_bwd_g<T, GATE_CHANNEL>(a, order, ckpt, sbuf, stream);
         case GATE_SCALAR: return launch_bwd_g<T, GATE_SCALAR>(a, order, ckpt, sbuf, stream);
         case GATE_NONE: return launch_bwd_g<T, GATE_NONE>(a, order, ckpt, sbuf, stream);
-        case GATE_KEY: break;
+        case GATE_KEY: return launch_bwd_g<T, GATE_KEY>(a, order, ckpt, sbuf, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -345,6 +386,7 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
     if (e == hipSuccess) e = fill_zero(a.dk, nt * a.d_k, stream);
     if (e == hipSuccess) e = fill_zero(a.dbeta, nt, stream);
     if (e == hipSuccess && a.gate == GATE_SCALAR) e = fill_zero(a.dalpha, nt, stream);
+    if (e == hipSuccess && a.gate == GATE_KEY) e = fill_zero(a.dalpha, nt * a.d_k, stream);
     if (e != hipSuccess) return e;
     const int32_t* order = nullptr;
     if (a.cu_seqlens) {

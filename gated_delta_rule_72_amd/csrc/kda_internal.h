@@ -92,8 +92,7 @@ size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
 size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
 
 // Backward of the token-recurrent prefill (kda_backward.hip): the gradients of
-// q, k, v, alpha, beta and S0 given those of o and S_T.  gate is GATE_CHANNEL,
-// GATE_SCALAR or GATE_NONE.
+// q, k, v, alpha, beta and S0 given those of o and S_T, for every gate.
 struct BackwardArgs {
     const void* q;
     const void* k;

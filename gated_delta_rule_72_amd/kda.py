@@ -25,7 +25,7 @@ KDA_DTYPE_BF16 = 1
 EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
             "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate",
             "kda_prefill_key_gate", "kda_decode_step_key_gate", "kda_prefill_backward_workspace_size",
-            "kda_prefill_backward", "kda_prefill_backward_scalar_gate")
+            "kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate")
 
 _lib = None
 
@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
     L.kda_prefill_backward_workspace_size.restype = sz
     L.kda_prefill_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
-    for name in ("kda_prefill_backward", "kda_prefill_backward_scalar_gate"):
+    for name in ("kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate"):
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
@@ -254,4 +254,11 @@ def kda_prefill_backward_scalar_gate(q, k, v, alpha, beta, S0, cu_seqlens, dO, d
                                      n_seq: Optional[int] = None, want_dS0: bool = True, workspace=None):
     """kda_prefill_backward with alpha [n_tok, H] (one gate per token and head) or None (no gate)."""
     return _backward("kda_prefill_backward_scalar_gate", q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq,
+                     want_dS0, workspace)
+
+
+def kda_prefill_backward_key_gate(q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T=None, *,
+                                  n_seq: Optional[int] = None, want_dS0: bool = True, workspace=None):
+    """kda_prefill_backward with the gate on key channels, alpha [n_tok, H, d_k]."""
+    return _backward("kda_prefill_backward_key_gate", q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq,
                      want_dS0, workspace)

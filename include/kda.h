@@ -225,8 +225,7 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
  * dq, dk, dbeta (and a scalar gate's dalpha) are sums over the value rows,
  * added up with float atomics: their last bits can differ from run to run.
  * No output may overlap an input, another output or the workspace.  The
- * arithmetic is fp32 for either input dtype.  Gate on key channels: not
- * provided.
+ * arithmetic is fp32 for either input dtype.
  */
 size_t kda_prefill_backward_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
                                            int32_t d_k, int32_t d_v);
@@ -251,6 +250,19 @@ kda_status kda_prefill_backward_scalar_gate(const void* q, const void* k, const 
                                             float* dq, float* dk, float* dv, float* dalpha,
                                             float* dbeta, float* dS0, void* workspace,
                                             size_t workspace_bytes, void* stream);
+
+/* The same with the gate on key channels (as kda_prefill_key_gate): alpha and
+ * dalpha [n_tok, n_heads, d_k] float32, alpha 16-byte aligned; dalpha_t is a
+ * sum over the value rows, added up with float atomics like dq. */
+kda_status kda_prefill_backward_key_gate(const void* q, const void* k, const void* v,
+                                         const float* alpha, const float* beta,
+                                         const float* S0, const int32_t* cu_seqlens,
+                                         const float* dO, const float* dS_T,
+                                         int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                         int32_t d_k, int32_t d_v, kda_dtype dt,
+                                         float* dq, float* dk, float* dv, float* dalpha,
+                                         float* dbeta, float* dS0, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

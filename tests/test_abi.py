@@ -210,7 +210,8 @@ def backward(L, fn="kda_prefill_backward", **kw):
                           a["dalpha"], a["dbeta"], a["dS0"], a["ws"], a["ws_bytes"], a["stream"])
 
 
-@pytest.mark.parametrize("fn", ["kda_prefill_backward", "kda_prefill_backward_scalar_gate"])
+@pytest.mark.parametrize("fn", ["kda_prefill_backward", "kda_prefill_backward_scalar_gate",
+                                "kda_prefill_backward_key_gate"])
 @pytest.mark.parametrize("kw,status", [
     (dict(dt=5), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(n_seq=0), kda.KDA_ERR_INVALID_ARGUMENT),
@@ -234,3 +235,10 @@ def test_backward_rejects_on_host(L, fn, kw, status):
 def test_backward_gate_needs_its_gradient(L):
     assert backward(L, dalpha=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert backward(L, alpha=None) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_backward_key_gate_needs_aligned_alpha(L):
+    fn = "kda_prefill_backward_key_gate"
+    assert backward(L, fn, alpha=A + 3 * 0x100000 + 4) == kda.KDA_ERR_INVALID_ARGUMENT
+    # a scalar gate is read as scalars: 4-byte alignment, so 2 bytes off is rejected
+    assert backward(L, "kda_prefill_backward_scalar_gate", alpha=A + 3 * 0x100000 + 2) == kda.KDA_ERR_INVALID_ARGUMENT

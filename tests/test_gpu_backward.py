@@ -1,4 +1,4 @@
-"""GPU parity of the prefill backward (kda_prefill_backward, kda_prefill_backward_scalar_gate)
+"""GPU parity of the prefill backward (kda_prefill_backward and its scalar-gate and key-gate forms)
 against the fp64 backward oracle, through the C ABI.  The oracle side is pinned in
 test_oracle_backward by central finite differences of the forward oracle."""
 import numpy as np
@@ -30,7 +30,8 @@ def run(torch, inp, gate, varlen, with_dST=True, want_dS0=True, seed=0):
     if not with_dST:
         dS_T = None
     d = Hh.upload_prefill(inp)
-    fn = kda.kda_prefill_backward if gate == "channel" else kda.kda_prefill_backward_scalar_gate
+    fn = {"channel": kda.kda_prefill_backward, "scalar": kda.kda_prefill_backward_scalar_gate,
+          "none": kda.kda_prefill_backward_scalar_gate, "key": kda.kda_prefill_backward_key_gate}[gate]
     g = fn(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"] if varlen else None,
            Hh.to_device(dO, "f32"), None if dS_T is None else Hh.to_device(dS_T, "f32"), n_seq=inp.n_seq,
            want_dS0=want_dS0)
@@ -49,7 +50,7 @@ def run(torch, inp, gate, varlen, with_dST=True, want_dS0=True, seed=0):
         assert g["dS0"] is None
 
 
-@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none", "key"])
 @pytest.mark.parametrize("lens,H,dk,dv,dtype,varlen", [
     ([37, 1, 0, 20], 2, 64, 64, "f32", True),     # ragged blocks of 16, length 1, empty
     ([50], 3, 128, 128, "f32", False),
@@ -73,3 +74,9 @@ def test_backward_longer_sequences(torch_cuda):
     print("backward: 2 x 400 tokens, H=2, d=128, bf16", flush=True)
     inp = I.make_prefill(9202, [400, 400], 2, 128, 128, "bf16", "exp_softplus", 0.02, "channel")
     run(torch_cuda, inp, "channel", False, seed=2)
+
+
+def test_backward_key_gate_longer_sequences(torch_cuda):
+    print("backward, key-channel gate: 2 x 300 tokens, H=2, d=128, bf16", flush=True)
+    inp = I.make_prefill(9203, [300, 300], 2, 128, 128, "bf16", "exp_softplus", 0.02, "key")
+    run(torch_cuda, inp, "key", False, seed=3)
