@@ -461,10 +461,35 @@ def bench_backward(args, torch, kda, I):
     m, r = rel(g["dS0"][n_, h].cpu().numpy().astype(np.float64), ref["dS0"][0, 0])
     parity["dS0"] = dict(max_rel=m, rms_rel=r)
     parity["scope"] = f"(sequence {n_}, head {h}), whole sequence"
+    # the same with the gate on key channels (alpha [n_tok, H, d_k])
+    del g, alpha
+    inpk = I.workload_prefill(3, gate="key")
+    alk = upload(inpk.alpha, "f32", dev)
+
+    def step_key():
+        return kda.kda_prefill_backward_key_gate(q, k, v, alk, beta, S0, None, dO_d, dST_d, n_seq=B, workspace=ws)
+
+    step_key()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        gk = step_key()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_key = e0.elapsed_time(e1) / n
+    refk = prefill_backward(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")), sub(inpk.alpha), sub(inp.beta),
+                            inp.S0[n_:n_ + 1, h:h + 1].astype(np.float64), [0, e_ - s_], sub(dO),
+                            dS_T[n_:n_ + 1, h:h + 1], "key")
+    worst = 0.0
+    for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        worst = max(worst, rel(gk[name][s_:e_, h].cpu().numpy().astype(np.float64), refk[name][:, 0])[0])
+    worst = max(worst, rel(gk["dS0"][n_, h].cpu().numpy().astype(np.float64), refk["dS0"][0, 0])[0])
     return dict(workload="batched prefill workload (value-channel gate), kda_prefill_backward with dO and dS_T "
                          "drawn N(0,1): token-recurrent backward kernel",
                 ms_per_call=round(ms, 3), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
-                workspace_bytes=ws.numel(), parity=parity)
+                workspace_bytes=ws.numel(), parity=parity,
+                key_gate=dict(ms_per_call=round(ms_key, 3), tokens_per_s=round(inp.n_tok / (ms_key * 1e-3), 1),
+                              worst_max_rel=worst, scope=parity["scope"] + ", every gradient"))
 
 
 def bench_multi_token_decode(args, torch, kda, I, T=4):
@@ -631,6 +656,7 @@ def main():
         line["backward"] = bench_backward(args, torch, kda, I)
         log(f"[bench] prefill backward: {line['backward']['ms_per_call']:.2f} ms per call, "
             f"{line['backward']['tokens_per_s']:.4g} tokens/s")
+        log(f"[bench] prefill backward, key-channel gate: {line['backward']['key_gate']['ms_per_call']:.2f} ms per call")
     if not args.no_workloads:
         line["workloads"] = bench_other_workloads(args, torch, kda, I)
     if not args.no_decode:
