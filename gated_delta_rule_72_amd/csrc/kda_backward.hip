@@ -124,18 +124,19 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     };
 
     struct Tok { f32x4 k[M], q[M], ak[KEY ? M : 1]; float v, a, b, go; };
-    auto load = [&](Tok& x, int64_t t) {
+    // a token's operands; the forward passes (full = false) need no q and no dO
+    auto load = [&](Tok& x, int64_t t, bool full) {
         const int64_t th = t * H + h;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             x.k[m] = Elem<T>::load4(k + th * DK + col(m));
-            x.q[m] = Elem<T>::load4(q + th * DK + col(m));
+            if (full) x.q[m] = Elem<T>::load4(q + th * DK + col(m));
             if constexpr (KEY) x.ak[m] = *reinterpret_cast<const f32x4*>(alpha + th * DK + col(m));
         }
         x.v = Elem<T>::load(v + th * DV + row);
         x.a = GATE == GATE_CHANNEL ? alpha[th * DV + row] : GATE == GATE_SCALAR ? alpha[th] : 1.f;
         x.b = beta[th];
-        x.go = dO[th * DV + row];
+        if (full) x.go = dO[th * DV + row];
     };
     // a = s . k for this lane's row (all 8 lanes of the row get it)
     auto dot_k = [&](const f32x4* s, const Tok& x) {
@@ -167,10 +168,10 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     for (int m = 0; m < M; ++m)
         s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
     Tok x, xn;
-    if (len > 0) load(x, u.t0);
+    if (len > 0) load(x, u.t0, false);
     for (int64_t t = u.t0; t < u.t1; ++t) {
         const int64_t i = t - u.t0;
-        if (t + 1 < u.t1) load(xn, t + 1);
+        if (t + 1 < u.t1) load(xn, t + 1, false);
         if (i % BWD_BLOCK == 0) {
             float* c = ck(static_cast<int>(i / BWD_BLOCK));
 #pragma unroll
@@ -193,23 +194,23 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
         const float* c = ck(b);
 #pragma unroll
         for (int m = 0; m < M; ++m) s[m] = *reinterpret_cast<const f32x4*>(c + col(m));
-        load(x, tb);
+        load(x, tb, false);
         for (int i = 0; i < nb; ++i) {
-            if (i + 1 < nb) load(xn, tb + i + 1);
+            if (i + 1 < nb) load(xn, tb + i + 1, false);
 #pragma unroll
             for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(my + i * 8 * DK + col(m)) = s[m];
             advance(s, x);
             x = xn;
         }
         f32x4 sp[M], spn[M];
-        load(x, tb + nb - 1);
+        load(x, tb + nb - 1, true);
 #pragma unroll
         for (int m = 0; m < M; ++m) sp[m] = *reinterpret_cast<const f32x4*>(my + (nb - 1) * 8 * DK + col(m));
         for (int i = nb - 1; i >= 0; --i) {
             const int64_t t = tb + i;
             const int64_t th = t * H + h;
             if (i > 0) {
-                load(xn, t - 1);
+                load(xn, t - 1, true);
 #pragma unroll
                 for (int m = 0; m < M; ++m) spn[m] = *reinterpret_cast<const f32x4*>(my + (i - 1) * 8 * DK + col(m));
             }
