@@ -71,20 +71,27 @@ __device__ __forceinline__ void load_token(Token<DK, GATE>& x, const T* __restri
     x.b = beta[th];
 }
 
+// Waves per workgroup of the ring form (8 rows each); a head of d_v rows takes
+// d_v / (8 W) workgroups.  Eight waves (64 rows) per workgroup measured 7% slower
+// on multi-token decode of 1 and 4 tokens (1% faster at 16).
+constexpr int kRingWaves = 1;
+
 template <typename T, int DK, int DV, int GATE, int D>
-__global__ __launch_bounds__(64) void prefill_valu_kernel(
+__global__ __launch_bounds__(64 * kRingWaves) void prefill_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
     T* __restrict__ o, float* __restrict__ S_T) {
-    constexpr int NVB = DV / ROWS_PER_WAVE;
+    constexpr int RW = ROWS_PER_WAVE * kRingWaves;  // rows per workgroup
+    constexpr int NVB = DV / RW;
     constexpr int M = DK / 32;
+    static_assert(DV % RW == 0, "rows per workgroup");
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int lane8 = lane & 7;
-    const int i = u.vblk * ROWS_PER_WAVE + (lane >> 3);  // value row of this lane
+    const int i = u.vblk * RW + (threadIdx.x >> 6) * ROWS_PER_WAVE + (lane >> 3);  // value row of this lane
     const int64_t H = n_heads;
     const int h = u.head;
 
@@ -92,7 +99,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(
     f32x4 s[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_off + 4 * (lane8 + 8 * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        s[m] = S0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S0 + s_off + 4 * (lane8 + 8 * m)))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one token of the recurrence for this lane's row
     auto step = [&](const Token<DK, GATE>& x, int64_t t) {
@@ -138,7 +146,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(
     }
     if (S_T) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(S_T + s_off + 4 * (lane8 + 8 * m)) = s[m];
+        for (int m = 0; m < M; ++m)
+            __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4*>(S_T + s_off + 4 * (lane8 + 8 * m)));
     }
 }
 
@@ -146,15 +155,18 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(
 // calls, where many waves in flight matter more than a deep ring: at d = 128
 // depth 4 takes 214 VGPRs (two waves per SIMD), depth 2 128.  Multi-token decode
 // of the decode workload's state, ms per call for 1 / 4 / 16 tokens: depth 4
-// 0.248 / 0.408 / 1.05, depth 2 0.191 / 0.273 / 0.731, depth 1 0.199 / 0.275 / 0.710.
+// 0.248 / 0.408 / 1.05, depth 2 0.191 / 0.273 / 0.731, depth 1 0.199 / 0.275 / 0.710;
+// with the state read and written non-temporally (each element is touched once),
+// depth 2 0.169 / 0.251 / 0.666.
 constexpr int kRingLong = 4;
 constexpr int kRingShort = 2;
 
 template <typename T, int DK, int DV, int GATE, int D>
 static hipError_t launch_valu_d(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
-    constexpr int NVB = DV / ROWS_PER_WAVE;
+    constexpr int NVB = DV / (ROWS_PER_WAVE * kRingWaves);
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, GATE, D>), dim3(static_cast<unsigned>(grid)), dim3(64), 0,
+    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, DV, GATE, D>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * kRingWaves), 0,
                        stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
                        static_cast<T*>(a.o), a.S_T);
