@@ -80,3 +80,20 @@ def test_backward_key_gate_longer_sequences(torch_cuda):
     print("backward, key-channel gate: 2 x 300 tokens, H=2, d=128, bf16", flush=True)
     inp = I.make_prefill(9203, [300, 300], 2, 128, 128, "bf16", "exp_softplus", 0.02, "key")
     run(torch_cuda, inp, "key", False, seed=3)
+
+
+def test_backward_of_empty_sequences_passes_dS_T_through(torch_cuda):
+    """Sequences with no tokens: S_T = S0, so dS0 = dS_T exactly, and the call writes
+    nothing else (one non-empty sequence keeps the token tensors non-empty)."""
+    print("backward: empty sequences", flush=True)
+    from gated_delta_rule_72_amd import kda
+    inp = I.make_prefill(9204, [0, 5, 0], 2, 64, 64, "f32", "exp_softplus", 0.02, "channel")
+    dO, dS_T = I.make_backward_grads(9205, inp)
+    d = Hh.upload_prefill(inp)
+    g = kda.kda_prefill_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], d["cu_seqlens"],
+                                 Hh.to_device(dO, "f32"), Hh.to_device(dS_T, "f32"))
+    torch_cuda.cuda.synchronize()
+    dS0 = Hh.from_device(g["dS0"])
+    np.testing.assert_array_equal(dS0[0], dS_T[0])
+    np.testing.assert_array_equal(dS0[2], dS_T[2])
+    run(torch_cuda, inp, "channel", True, seed=5)
