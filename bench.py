@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/sec (H=32,d=128) + decode state GB/s; % of roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed) peak
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PREFILL_BYTES_PER_HEAD_TOKEN = 768 + 512 + 4 + 256   # q,k,v bf16 + alpha fp32 + beta + o bf16
 # with one gate per (token, head) (scalar gate): alpha is 4 bytes per head-token
@@ -415,9 +416,16 @@ def bench_key_gate(args, torch, kda, I):
     m, r = rel(o[s_:e_, 7].float().cpu().numpy().astype(np.float64), o_ref[:, 0])
     ms_, rs = rel(S_T[1, 7].cpu().numpy().astype(np.float64), S_ref[0, 0])
     alg = inp.n_tok * H * PREFILL_BYTES_PER_HEAD_TOKEN + 2 * B * H * inp.dv * inp.dk * 4
+    # vector-ALU work per head-token, per value row: the key-channel gate (d_k multiplies), s.k,
+    # the update and s.q (2 d_k flops each)
+    flops = inp.n_tok * H * inp.dv * (inp.dk + 3 * 2 * inp.dk)
+    tflops = flops / (ms * 1e-3) / 1e12
     return dict(workload="batched prefill workload with the forget gate on key channels, kda_prefill_key_gate "
                          "(token-recurrent kernel)",
                 ms_per_call=round(ms, 4), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
+                roofline=dict(bound="alu", achieved=round(tflops, 2), peak=FP32_VECTOR_PEAK_TFLOPS, unit="TFLOP/s",
+                              frac=round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), flop_per_head_token=flops // (inp.n_tok * H),
+                              note="peak counts packed fp32, which the build does not emit; unpacked FMA peak is half"),
                 hbm_frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 parity=dict(o_max_rel=m, o_rms_rel=r, S_max_rel=ms_, S_rms_rel=rs, scope="(sequence 1, head 7)"))
 
