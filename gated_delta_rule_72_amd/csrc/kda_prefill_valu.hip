@@ -35,9 +35,10 @@
 // tokens for each of many sequences, the state continued in place) also run
 // here: each state is read once and written once, as in the decode step, where
 // the chunked path would spend a whole 64-token chunk on every sequence.
-// Calls whose sequences average more than 16 tokens take the staged form
-// further down, which feeds the same per-row recurrence from tokens staged in
-// LDS by blocks; the form below serves the shorter ones.
+// Calls whose sequences average more than 16 tokens (dense bf16 calls: more
+// than 8) take the staged form further down, which feeds the same per-row
+// recurrence from tokens staged in LDS by blocks; the form below serves the
+// shorter ones.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
@@ -419,13 +420,18 @@ static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipS
 #endif
 // Calls whose sequences average more than one staged block take the staged form.
 constexpr int64_t kStagedMinTokens = KDA_STAGED_MIN_TOKENS;
+constexpr int64_t kRingShortMaxTokens = 8;
 
 template <typename T, int DK, int DV, int GATE>
 static hipError_t launch_valu_t(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
-    const bool short_call = std::is_same<T, uint16_t>::value && !a.cu_seqlens &&
-                            a.n_tok <= static_cast<int64_t>(RECURRENT_MAX_TOKENS) * a.n_seq;
-    if (short_call) return launch_valu_d<T, DK, DV, GATE, kRingShort>(a, order, stream);
-    if (a.n_tok >= kStagedMinTokens * a.n_seq) return launch_staged<T, DK, DV, GATE>(a, order, stream);
+    // dense bf16 calls of at most 16 tokens per sequence (multi-token decode): the ring of
+    // two up to 8 tokens, the staged form above that (ms per call on the decode workload's
+    // state, ring / staged: 8 tokens 0.400 / 0.408, 12 tokens 0.534 / 0.515, 16 tokens
+    // 0.666 / 0.623)
+    const bool dense_bf16 = std::is_same<T, uint16_t>::value && !a.cu_seqlens;
+    if (dense_bf16 && a.n_tok <= kRingShortMaxTokens * a.n_seq)
+        return launch_valu_d<T, DK, DV, GATE, kRingShort>(a, order, stream);
+    if (dense_bf16 || a.n_tok >= kStagedMinTokens * a.n_seq) return launch_staged<T, DK, DV, GATE>(a, order, stream);
     return launch_valu_d<T, DK, DV, GATE, kRingLong>(a, order, stream);
 }
 
