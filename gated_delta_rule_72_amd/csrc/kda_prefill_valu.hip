@@ -178,7 +178,8 @@ static hipError_t launch_valu_d(const PrefillArgs& a, const int32_t* order, hipS
 // Long calls: tokens staged in LDS by blocks.  The form above has every wave
 // fetch each token's q and k (and the key-channel gates) for itself, only
 // three tokens ahead, and it waits on those loads.  Here a workgroup owns R
-// value rows of one (sequence, head), one row per 8 lanes as above; its
+// value rows of one (sequence, head), one row per 8 lanes as above (16 for the
+// smallest calls); its
 // threads together load a block of 16 tokens' q, k, v, gates and beta
 // (widened to fp32) into one of two LDS buffers while the block before is
 // computed from the other, so a block's loads have a whole block of compute to
@@ -217,38 +218,44 @@ struct StageBuf {
     float b[STAGE_TOKENS];
 };
 
-// One token's operands for one lane, read from LDS.
-template <int DK, int GATE>
+// One token's operands for one lane (L lanes per row), read from LDS.
+template <int DK, int GATE, int L>
 struct StageOps {
-    f32x4 k[DK / 32], q[DK / 32];
-    f32x4 ak[GATE == GATE_KEY ? DK / 32 : 1];
+    f32x4 k[DK / (4 * L)], q[DK / (4 * L)];
+    f32x4 ak[GATE == GATE_KEY ? DK / (4 * L) : 1];
     float v, g, b;
 };
 
-template <int DK, int GATE, int R>
-__device__ __forceinline__ void read_ops(StageOps<DK, GATE>& x, const StageBuf<DK, GATE, R>& B, int tl, int j,
+template <int DK, int GATE, int R, int L>
+__device__ __forceinline__ void read_ops(StageOps<DK, GATE, L>& x, const StageBuf<DK, GATE, R>& B, int tl, int j,
                                          int r) {
 #pragma unroll
-    for (int m = 0; m < DK / 32; ++m) {
-        x.k[m] = B.k[tl][j + 8 * m];
-        x.q[m] = B.q[tl][j + 8 * m];
-        if constexpr (GATE == GATE_KEY) x.ak[m] = B.ak[tl][j + 8 * m];
+    for (int m = 0; m < DK / (4 * L); ++m) {
+        x.k[m] = B.k[tl][j + L * m];
+        x.q[m] = B.q[tl][j + L * m];
+        if constexpr (GATE == GATE_KEY) x.ak[m] = B.ak[tl][j + L * m];
     }
     x.v = B.v[tl][r];
     x.g = GATE == GATE_CHANNEL ? B.a[tl][r] : GATE == GATE_SCALAR ? B.g[tl] : 1.f;
     x.b = B.b[tl];
 }
 
-template <typename T, int DK, int DV, int GATE, int R>
-__global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
+// Sum over each aligned group of L (8 or 16) lanes.
+template <int L>
+__device__ __forceinline__ float sum_lanes(float x) {
+    return L == 16 ? sum16(x) : sum8(x);
+}
+
+template <typename T, int DK, int DV, int GATE, int R, int L>
+__global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
     T* __restrict__ o, float* __restrict__ S_T) {
     constexpr int TB = STAGE_TOKENS;
-    constexpr int NT = 8 * R;                // threads: 8 lanes per row
-    constexpr int M = DK / 32;               // float4 chunks of a row per lane
+    constexpr int NT = L * R;                // threads: L lanes per row
+    constexpr int M = DK / (4 * L);          // float4 chunks of a row per lane
     constexpr int KN = TB * DK / 4;          // float4 groups of k (q, key gates) per block
     constexpr int KG = (KN + NT - 1) / NT;   // ... per thread
     constexpr int VN = TB * R / 4;           // float4 groups of v (value-channel gates) per block
@@ -259,8 +266,8 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, DV / R, n_tok, cu_seqlens, order);
     if (!u.valid) return;
     const int tid = threadIdx.x;
-    const int j = tid & 7;     // which chunks of the row
-    const int r = tid >> 3;    // local row of this lane
+    const int j = tid % L;     // which chunks of the row
+    const int r = tid / L;     // local row of this lane
     const int row0 = u.vblk * R;
     const int64_t H = n_heads;
     const int h = u.head;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
     f32x4 s[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + 4 * (j + 8 * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + 4 * (j + L * m)) : f32x4{0.f, 0.f, 0.f, 0.f};
 
     // this thread's share of one block, held in registers between load and store
     using Rw = Raw4<T>;
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
     };
 
     // one token for this lane's row
-    auto step = [&](const StageOps<DK, GATE>& x, int64_t t) {
+    auto step = [&](const StageOps<DK, GATE, L>& x, int64_t t) {
         if constexpr (GATE == GATE_KEY) {
 #pragma unroll
             for (int m = 0; m < M; ++m)
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
             a0 += s[m][0] * x.k[m][0] + s[m][2] * x.k[m][2];
             a1 += s[m][1] * x.k[m][1] + s[m][3] * x.k[m][3];
         }
-        const float uu = x.b * (x.v - x.g * sum8(a0 + a1));
+        const float uu = x.b * (x.v - x.g * sum_lanes<L>(a0 + a1));
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
             c0 += s[m][0] * x.q[m][0] + s[m][2] * x.q[m][2];
             c1 += s[m][1] * x.q[m][1] + s[m][3] * x.q[m][3];
         }
-        const float oo = sum8(c0 + c1);
+        const float oo = sum_lanes<L>(c0 + c1);
         if (j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
     };
 
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
         stage(buf[0]);
     }
     block_sync();
-    StageOps<DK, GATE> xa, xb;  // ping-pong: one token's operands in use, the next one's in flight
+    StageOps<DK, GATE, L> xa, xb;  // ping-pong: one token's operands in use, the next one's in flight
     for (int bi = 0; bi < nblk; ++bi) {
         const int64_t tb = u.t0 + static_cast<int64_t>(bi) * TB;
         if (bi + 1 < nblk) fetch(tb + TB);  // in flight while this block is computed
@@ -390,14 +397,14 @@ __global__ __launch_bounds__(8 * R) void prefill_staged_kernel(
     }
     if (S_T) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(S_T + s_row + 4 * (j + 8 * m)) = s[m];
+        for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(S_T + s_row + 4 * (j + L * m)) = s[m];
     }
 }
 
-template <typename T, int DK, int DV, int GATE, int R>
+template <typename T, int DK, int DV, int GATE, int R, int L = 8>
 static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / R);
-    hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R>), dim3(static_cast<unsigned>(grid)), dim3(8 * R),
+    hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
                        0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
                        static_cast<T*>(a.o), a.S_T);
@@ -405,14 +412,18 @@ static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hi
 }
 
 // Rows per workgroup: 64 when that makes at least one workgroup per CU, else
-// 32, else 16.
+// 32, else 16; the smallest calls give a row 16 lanes, so a wave's share of a
+// token is half as many instructions (against 8 lanes, ms per call: the key-
+// channel gate at 1 x 4096 tokens, H = 8, d = 128, 1.41 -> 1.11; fp32 1 x 1024,
+// H = 8: 0.297 -> 0.246; the tiny fp32 workload 0.055 -> 0.050).
+constexpr int kStagedSmallLanes = 16;
 template <typename T, int DK, int DV, int GATE>
 static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
     constexpr int64_t kCus = 256;
     const int64_t units = static_cast<int64_t>(a.n_seq) * a.n_heads;
     if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream);
     if (units * (DV / 32) >= kCus) return launch_staged_r<T, DK, DV, GATE, 32>(a, order, stream);
-    return launch_staged_r<T, DK, DV, GATE, 16>(a, order, stream);
+    return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream);
 }
 
 #ifndef KDA_STAGED_MIN_TOKENS
