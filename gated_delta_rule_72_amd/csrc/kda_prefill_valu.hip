@@ -179,7 +179,7 @@ static hipError_t launch_valu_d(const PrefillArgs& a, const int32_t* order, hipS
 // fetch each token's q and k (and the key-channel gates) for itself, only
 // three tokens ahead, and it waits on those loads.  Here a workgroup owns R
 // value rows of one (sequence, head), one row per 8 lanes as above (16 for the
-// smallest calls); its
+// smaller calls); its
 // threads together load a block of 16 tokens' q, k, v, gates and beta
 // (widened to fp32) into one of two LDS buffers while the block before is
 // computed from the other, so a block's loads have a whole block of compute to
@@ -412,17 +412,19 @@ static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hi
 }
 
 // Rows per workgroup: 64 when that makes at least one workgroup per CU, else
-// 32, else 16; the smallest calls give a row 16 lanes, so a wave's share of a
-// token is half as many instructions (against 8 lanes, ms per call: the key-
-// channel gate at 1 x 4096 tokens, H = 8, d = 128, 1.41 -> 1.11; fp32 1 x 1024,
-// H = 8: 0.297 -> 0.246; the tiny fp32 workload 0.055 -> 0.050).
+// 32, else 16.  Below 64 a row gets 16 lanes, so a wave's share of a token is
+// half as many instructions (against 8 lanes, ms per call: the key-channel gate
+// at 1 x 4096 tokens, H = 8, d = 128, 1.41 -> 1.11, at 16 x 64 tokens, H = 4,
+// 0.028 -> 0.025; fp32 1 x 1024, H = 8: 0.297 -> 0.246; the tiny fp32 workload
+// 0.055 -> 0.050).  At 64 rows, 16 lanes (1024 threads) was 1% slower on the
+// batched workload with the key-channel gate.
 constexpr int kStagedSmallLanes = 16;
 template <typename T, int DK, int DV, int GATE>
 static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
     constexpr int64_t kCus = 256;
     const int64_t units = static_cast<int64_t>(a.n_seq) * a.n_heads;
     if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream);
-    if (units * (DV / 32) >= kCus) return launch_staged_r<T, DK, DV, GATE, 32>(a, order, stream);
+    if (units * (DV / 32) >= kCus) return launch_staged_r<T, DK, DV, GATE, 32, kStagedSmallLanes>(a, order, stream);
     return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream);
 }
 
