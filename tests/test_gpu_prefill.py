@@ -343,3 +343,36 @@ def test_long_token_recurrent_calls_match_oracle(torch_cuda, gate, lens, H, dk, 
     tol = Hh.tol_for(dtype)
     Hh.check("o", Hh.from_device(o), o_ref, Hh.o_slices(inp.cu_seqlens, H), tol)
     Hh.check("S_T", Hh.from_device(S), S_ref, Hh.s_slices(inp.n_seq, H), tol)
+
+
+@pytest.mark.parametrize("dtype,gate,lens", [
+    ("f32", "channel", [300, 45]),   # staged form
+    ("f32", "scalar", [10, 7]),      # ring form (at most 16 tokens per sequence)
+    ("bf16", "key", [260, 90]),      # staged form, key-channel gate
+    ("bf16", "channel", [12, 12]),   # dense multi-token decode: staged form (more than 8 tokens)
+])
+def test_token_recurrent_in_place_no_state_and_deterministic(torch_cuda, dtype, gate, lens):
+    """The token-recurrent paths: S_T aliasing S0 gives the same results as separate
+    buffers, S_T = NULL the same o, and a second run the same bits."""
+    from gated_delta_rule_72_amd import kda
+    print(f"token-recurrent in place / no state / twice: {dtype} {gate} lens={lens}", flush=True)
+    fn = {"channel": kda.kda_prefill, "scalar": kda.kda_prefill_scalar_gate,
+          "key": kda.kda_prefill_key_gate}[gate]
+    inp = I.make_prefill(7700 + sum(lens), lens, 2, 128, 128, dtype, "exp_softplus", 0.02, gate)
+    d = Hh.upload_prefill(inp)
+    cu = d["cu_seqlens"] if len(set(lens)) > 1 else None
+
+    def call(S0, **kw):
+        o, S = fn(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S0, cu, n_seq=inp.n_seq, **kw)
+        torch_cuda.cuda.synchronize()
+        return Hh.from_device(o), (None if S is None else Hh.from_device(S))
+
+    o1, S1 = call(d["S0"])
+    o2, S2 = call(d["S0"])
+    alias = d["S0"].clone()
+    o3, S3 = call(alias, S_T=alias)
+    o4, S4 = call(d["S0"], want_state=False)
+    assert S4 is None
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    assert np.array_equal(o1, o3) and np.array_equal(S1, S3)
+    assert np.array_equal(o1, o4)
