@@ -25,16 +25,17 @@
 // dk, dbeta and a scalar dalpha are sums over rows, reduced over the wave's
 // rows and added into zeroed outputs with float atomics (so their last bits
 // depend on the order of the waves).
-// States: a forward pass stores the state every 16 tokens; the backward pass
-// walks the blocks in reverse, recomputes the 16 states of a block from its
-// checkpoint into the wave's own scratch, and walks those tokens in reverse.
+// States: a forward pass (the staged forward kernel, run first, with no o)
+// stores the state every 16 tokens; the backward pass walks the blocks in
+// reverse, recomputes the 16 states of a block from its checkpoint into the
+// wave's own scratch, and walks those tokens in reverse.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_schedule.h"
 
 namespace kda {
 
-constexpr int BWD_BLOCK = 16;    // tokens between state checkpoints
+constexpr int BWD_BLOCK = STATE_CHECKPOINT_TOKENS;  // tokens between state checkpoints
 constexpr int BWD_ROWS = 64;     // value rows per workgroup
 constexpr int BWD_THREADS = 512; // eight waves of 8 rows
 
@@ -161,25 +162,10 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
             for (int e = 0; e < 4; ++e) s[m][e] = x.a * s[m][e] + uu * x.k[m][e];
     };
 
-    // forward: checkpoints at every block start; each token loaded one token ahead
+    // the checkpoints come from the staged forward, run before this kernel
     f32x4 s[M];
     const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row) * DK;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        s[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + s_row + col(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
     Tok x, xn;
-    if (len > 0) load(x, u.t0, false);
-    for (int64_t t = u.t0; t < u.t1; ++t) {
-        const int64_t i = t - u.t0;
-        if (t + 1 < u.t1) load(xn, t + 1, false);
-        if (i % BWD_BLOCK == 0) {
-            float* c = ck(static_cast<int>(i / BWD_BLOCK));
-#pragma unroll
-            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(c + col(m)) = s[m];
-        }
-        advance(s, x);
-        x = xn;
-    }
 
     // backward
     f32x4 G[M];
@@ -398,6 +384,13 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
     }
     float* ckpt = reinterpret_cast<float*>(ws + L.ckpt);
     float* sbuf = reinterpret_cast<float*>(ws + L.sbuf);
+    if (a.n_tok > 0) {
+        // forward pass: the state entering every block of 16 tokens, into ckpt
+        const PrefillArgs fa{a.q, a.k, a.v, a.alpha, a.beta, a.S0, a.cu_seqlens, a.n_seq, a.n_tok, a.n_heads,
+                             a.d_k, a.d_v, a.bf16, nullptr, nullptr, nullptr, 0, a.gate};
+        e = launch_prefill_checkpoints(fa, order, ckpt, stream);
+        if (e != hipSuccess) return e;
+    }
     return a.bf16 ? launch_bwd_type<uint16_t>(a, order, ckpt, sbuf, stream)
                   : launch_bwd_type<float>(a, order, ckpt, sbuf, stream);
 }

@@ -115,6 +115,11 @@ struct BackwardArgs {
     Gate gate;
 };
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream);
+// Tokens between the state checkpoints the backward keeps; the staged forward
+// (kda_prefill_valu.hip) writes them for it: slot n + t0 / 16 + b holds the state
+// entering block b of sequence n (first token t0), [slot, H, d_v, d_k] fp32.
+constexpr int STATE_CHECKPOINT_TOKENS = 16;
+hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream);
 // Workspace bytes: the longest-first schedule, a state checkpoint every 16
 // tokens of every (sequence, head), and each wave's states within one block.
 size_t prefill_backward_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);

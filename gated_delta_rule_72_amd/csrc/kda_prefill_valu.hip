@@ -252,7 +252,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
-    T* __restrict__ o, float* __restrict__ S_T) {
+    T* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt) {
     constexpr int TB = STAGE_TOKENS;
     constexpr int NT = L * R;                // threads: L lanes per row
     constexpr int M = DK / (4 * L);          // float4 chunks of a row per lane
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
             c1 += s[m][1] * x.q[m][1] + s[m][3] * x.q[m][3];
         }
         const float oo = sum_lanes<L>(c0 + c1);
-        if (j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
+        if (o && j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
     };
 
     const int64_t len = u.t1 - u.t0;
@@ -381,6 +381,13 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     for (int bi = 0; bi < nblk; ++bi) {
         const int64_t tb = u.t0 + static_cast<int64_t>(bi) * TB;
         if (bi + 1 < nblk) fetch(tb + TB);  // in flight while this block is computed
+        if (ckpt) {
+            // the state entering the block, for the backward (slot: sequence index + first
+            // token / 16 + block, which never collide between sequences)
+            float* c = ckpt + (((u.seq + u.t0 / TB + bi) * H + h) * DV + row0 + r) * DK;
+#pragma unroll
+            for (int m = 0; m < M; ++m) *reinterpret_cast<f32x4*>(c + 4 * (j + L * m)) = s[m];
+        }
         const StageBuf<DK, GATE, R>& B = buf[bi & 1];
         const int nb = static_cast<int>(u.t1 - tb < TB ? u.t1 - tb : TB);
         read_ops(xa, B, 0, j, r);
@@ -402,12 +409,12 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
 }
 
 template <typename T, int DK, int DV, int GATE, int R, int L = 8>
-static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream, float* ckpt) {
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / R);
     hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
                        0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
-                       static_cast<T*>(a.o), a.S_T);
+                       static_cast<T*>(a.o), a.S_T, ckpt);
     return hipGetLastError();
 }
 
@@ -420,12 +427,41 @@ static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hi
 // batched workload with the key-channel gate.
 constexpr int kStagedSmallLanes = 16;
 template <typename T, int DK, int DV, int GATE>
-static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipStream_t stream) {
+static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipStream_t stream,
+                                float* ckpt = nullptr) {
     constexpr int64_t kCus = 256;
     const int64_t units = static_cast<int64_t>(a.n_seq) * a.n_heads;
-    if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream);
-    if (units * (DV / 32) >= kCus) return launch_staged_r<T, DK, DV, GATE, 32, kStagedSmallLanes>(a, order, stream);
-    return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream);
+    if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream, ckpt);
+    if (units * (DV / 32) >= kCus)
+        return launch_staged_r<T, DK, DV, GATE, 32, kStagedSmallLanes>(a, order, stream, ckpt);
+    return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream, ckpt);
+}
+
+template <typename T, int GATE>
+static hipError_t launch_ckpt_g(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_staged<T, 128, 128, GATE>(a, order, stream, ckpt);
+    if (a.d_k == 64 && a.d_v == 64) return launch_staged<T, 64, 64, GATE>(a, order, stream, ckpt);
+    if (a.d_k == 128 && a.d_v == 64) return launch_staged<T, 128, 64, GATE>(a, order, stream, ckpt);
+    if (a.d_k == 64 && a.d_v == 128) return launch_staged<T, 64, 128, GATE>(a, order, stream, ckpt);
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_ckpt_t(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
+    switch (a.gate) {
+        case GATE_CHANNEL: return launch_ckpt_g<T, GATE_CHANNEL>(a, order, ckpt, stream);
+        case GATE_SCALAR: return launch_ckpt_g<T, GATE_SCALAR>(a, order, ckpt, stream);
+        case GATE_NONE: return launch_ckpt_g<T, GATE_NONE>(a, order, ckpt, stream);
+        case GATE_KEY: return launch_ckpt_g<T, GATE_KEY>(a, order, ckpt, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// The backward's forward pass: the staged form run for its states only (a.o and
+// a.S_T null), storing the state entering every block of 16 tokens into ckpt.
+hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
+    static_assert(STAGE_TOKENS == STATE_CHECKPOINT_TOKENS, "checkpoint spacing");
+    return a.bf16 ? launch_ckpt_t<uint16_t>(a, order, ckpt, stream) : launch_ckpt_t<float>(a, order, ckpt, stream);
 }
 
 #ifndef KDA_STAGED_MIN_TOKENS
@@ -444,7 +480,8 @@ static hipError_t launch_valu_t(const PrefillArgs& a, const int32_t* order, hipS
     const bool dense_bf16 = std::is_same<T, uint16_t>::value && !a.cu_seqlens;
     if (dense_bf16 && a.n_tok <= kRingShortMaxTokens * a.n_seq)
         return launch_valu_d<T, DK, DV, GATE, kRingShort>(a, order, stream);
-    if (dense_bf16 || a.n_tok >= kStagedMinTokens * a.n_seq) return launch_staged<T, DK, DV, GATE>(a, order, stream);
+    if (dense_bf16 || a.n_tok >= kStagedMinTokens * a.n_seq)
+        return launch_staged<T, DK, DV, GATE>(a, order, stream);
     return launch_valu_d<T, DK, DV, GATE, kRingLong>(a, order, stream);
 }
 
