@@ -246,7 +246,9 @@ __device__ __forceinline__ float sum_lanes(float x) {
     return L == 16 ? sum16(x) : sum8(x);
 }
 
-template <typename T, int DK, int DV, int GATE, int R, int L>
+// CKPT: the backward's forward pass -- no o, and the state entering every block
+// stored into ckpt.
+template <typename T, int DK, int DV, int GATE, int R, int L, bool CKPT>
 __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
             c1 += s[m][1] * x.q[m][1] + s[m][3] * x.q[m][3];
         }
         const float oo = sum_lanes<L>(c0 + c1);
-        if (o && j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
+        if (!CKPT && j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
     };
 
     const int64_t len = u.t1 - u.t0;
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     for (int bi = 0; bi < nblk; ++bi) {
         const int64_t tb = u.t0 + static_cast<int64_t>(bi) * TB;
         if (bi + 1 < nblk) fetch(tb + TB);  // in flight while this block is computed
-        if (ckpt) {
+        if constexpr (CKPT) {
             // the state entering the block, for the backward (slot: sequence index + first
             // token / 16 + block, which never collide between sequences)
             float* c = ckpt + (((u.seq + u.t0 / TB + bi) * H + h) * DV + row0 + r) * DK;
@@ -411,7 +413,14 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
 template <typename T, int DK, int DV, int GATE, int R, int L = 8>
 static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream, float* ckpt) {
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / R);
-    hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
+    if (ckpt) {
+        hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(L * R), 0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok,
+                           a.n_heads, nullptr, nullptr, ckpt);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, false>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
                        0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
                        static_cast<T*>(a.o), a.S_T, ckpt);
