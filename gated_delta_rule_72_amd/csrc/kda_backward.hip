@@ -47,11 +47,29 @@ __host__ __device__ inline int64_t bwd_slots(int32_t n_seq, int32_t n_tok) {
     return static_cast<int64_t>(n_seq) + n_tok / BWD_BLOCK + 1;
 }
 
+// gfx950 lane-half swaps: permlane32 exchanges the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second; permlane16 exchanges the odd
+// 16-lane rows of the first with the even rows of the second.  Summing the two
+// results adds lanes 32 (or 16) apart without a trip through LDS.
+__device__ __forceinline__ void swap32(float x, float y, float& a, float& b) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void swap16(float x, float y, float& a, float& b) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+
 // Sum over the 8 lanes that hold the same key channels of the wave's 8 rows.
 __device__ __forceinline__ float sum_rows8(float x) {
+    float a, b;
+    swap32(x, x, a, b);
+    x = a + b;
+    swap16(x, x, a, b);
+    x = a + b;
     x += __shfl_xor(x, 8);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
     return x;
 }
 
@@ -59,20 +77,24 @@ __device__ __forceinline__ float sum_rows8(float x) {
 // m = c / 4, element c % 4) summed over the lane's row; on return lane group g
 // (lane / 8) holds in r[0 .. V/8) the sums over all 8 rows of values
 // c = g V / 8 + i.  Three butterfly steps, each keeping half of the values and
-// exchanging the other half with the partner group (xor 32, 16, 8 lanes).
+// exchanging the other half with the partner group (lanes 32, 16, 8 apart): the
+// first two are lane-half swaps of value pairs (i, i + V/2), then (i, i + V/4),
+// after which the lower lanes hold the lower index of the pair.
 template <int V>
 __device__ __forceinline__ void reduce_scatter_rows8(const float (&x)[V], float (&r)[V / 8], int lane) {
     float a[V / 2], b[V / 4];
-    const bool h2 = lane & 32, h1 = lane & 16, h0 = lane & 8;
+    const bool h0 = lane & 8;
 #pragma unroll
     for (int i = 0; i < V / 2; ++i) {
-        const float send = h2 ? x[i] : x[i + V / 2];
-        a[i] = (h2 ? x[i + V / 2] : x[i]) + __shfl_xor(send, 32);
+        float p, q;
+        swap32(x[i], x[i + V / 2], p, q);
+        a[i] = p + q;
     }
 #pragma unroll
     for (int i = 0; i < V / 4; ++i) {
-        const float send = h1 ? a[i] : a[i + V / 4];
-        b[i] = (h1 ? a[i + V / 4] : a[i]) + __shfl_xor(send, 16);
+        float p, q;
+        swap16(a[i], a[i + V / 4], p, q);
+        b[i] = p + q;
     }
 #pragma unroll
     for (int i = 0; i < V / 8; ++i) {
