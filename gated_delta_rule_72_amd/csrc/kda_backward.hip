@@ -62,6 +62,9 @@ __device__ __forceinline__ void swap16(float x, float y, float& a, float& b) {
     b = __uint_as_float(p[1]);
 }
 
+// DPP row_ror:8: within each 16-lane row, lane i reads lane i ^ 8.
+constexpr int DPP_ROW_ROR8 = 0x128;
+
 // Sum over the 8 lanes that hold the same key channels of the wave's 8 rows.
 __device__ __forceinline__ float sum_rows8(float x) {
     float a, b;
@@ -69,7 +72,7 @@ __device__ __forceinline__ float sum_rows8(float x) {
     x = a + b;
     swap16(x, x, a, b);
     x = a + b;
-    x += __shfl_xor(x, 8);
+    x += dpp_mov<DPP_ROW_ROR8>(x);
     return x;
 }
 
@@ -79,7 +82,8 @@ __device__ __forceinline__ float sum_rows8(float x) {
 // c = g V / 8 + i.  Three butterfly steps, each keeping half of the values and
 // exchanging the other half with the partner group (lanes 32, 16, 8 apart): the
 // first two are lane-half swaps of value pairs (i, i + V/2), then (i, i + V/4),
-// after which the lower lanes hold the lower index of the pair.
+// after which the lower lanes hold the lower index of the pair; the last a DPP
+// move within 16-lane rows.
 template <int V>
 __device__ __forceinline__ void reduce_scatter_rows8(const float (&x)[V], float (&r)[V / 8], int lane) {
     float a[V / 2], b[V / 4];
@@ -99,7 +103,7 @@ __device__ __forceinline__ void reduce_scatter_rows8(const float (&x)[V], float 
 #pragma unroll
     for (int i = 0; i < V / 8; ++i) {
         const float send = h0 ? b[i] : b[i + V / 8];
-        r[i] = (h0 ? b[i + V / 8] : b[i]) + __shfl_xor(send, 8);
+        r[i] = (h0 ? b[i + V / 8] : b[i]) + dpp_mov<DPP_ROW_ROR8>(send);
     }
 }
 
