@@ -71,14 +71,21 @@ inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32
 
 // Composes the segment states of the sequence-parallel prefill (kda_segments.hip).
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M, int n_seq,
-                                   int G, int n_heads, float* S_start, float* S_T, hipStream_t stream);
+hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M,
+                                   const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
+                                   float* S_T, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 // Token-recurrent prefill (kda_prefill_valu.hip): float32 inputs, the
 // key-channel gate for either input type, and short bf16 calls.
 hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream);
+// The token-recurrent recomputation, from S0, of the (sequence, head, block of 64
+// value rows) units that the chunked bf16 scan marked as beyond the decay range
+// of its factored form: range_flags [n_seq G, H, d_v / 64], G segments per
+// sequence (1 without the sequence-parallel split); a unit is recomputed if any
+// of its segments is marked.  Workgroups of unmarked units return at once.
+hipError_t launch_prefill_range_fixup(const PrefillArgs& a, const int32_t* range_flags, int G, hipStream_t stream);
 
 // bf16 prefill calls this short (equal lengths of at most this many tokens per
 // sequence, no cu_seqlens) run token by token: multi-token decode.

@@ -566,13 +566,26 @@ __device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16
 // SPLIT_S: the state enters K S^T as hi + lo bf16 (two MFMAs per step) instead of
 // one bf16 copy; used where no decay damps that rounding (the segment transitions
 // of the sequence-parallel path, which start from S0 = I).
+//
+// Range: X = V 2^{-G} and U grow like 2^{-G} inside a chunk, so the factored form
+// holds only while every row's log2-decay over a chunk stays above -RANGE_LOG2
+// (G is monotone for alpha in [0, 1], so the chunk total is its minimum).  Wave 7
+// checks each chunk's totals; a unit with any chunk beyond the range (alpha = 0
+// gives -inf) is marked in range_flags[unit] and does not write S_T, so that S0
+// is intact when S_T aliases it, and a token-recurrent pass recomputes exactly
+// the marked units afterwards.  Below the limit 2^{-G} stays below 2^{100}:
+// fp32 and bf16 (same exponent range) keep it, and the products with A, P and K
+// add at most a few powers of two.
+constexpr float RANGE_LOG2 = 100.f;
+
 template <int DK, int DV, int GATE, bool SPLIT_S = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
     const uint16_t* __restrict__ arec, int n_seq, int n_tok, int n_heads,
-    uint16_t* __restrict__ o, float* __restrict__ S_T, int flags, float* __restrict__ glog_out) {
+    uint16_t* __restrict__ o, float* __restrict__ S_T, int flags, float* __restrict__ glog_out,
+    int32_t* __restrict__ range_flags) {
     using SM = ScanSmem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -763,7 +776,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
     // G is kept in base-2 units (log2 alpha summed; e^{G} = 2^{G}), so every log
     // and exp below is one hardware instruction (v_log_f32 / v_exp_f32).  alpha
-    // is taken to be a normal fp32 number in (0, 1].
+    // is in [0, 1]; alpha = 0 gives G = -inf, which the range check (wave 7, in
+    // finalize) sends to the token-recurrent recomputation.
     // The log-decay cumsum G of a chunk is formed in two steps one phase apart,
     // so the prefix across waves never needs a barrier of its own:
     // local_scan -- each loader wave's inclusive prefix over its 16 token rows (in
@@ -784,6 +798,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         Tot[(par * 4 + wave - 4) * BV + ln] = run;
     };
     float glog = 0.f;  // wave 7: this row's total log2-decay over the unit's chunks
+    bool beyond = false;  // wave 7: some chunk of some row of the unit is beyond the range
     auto finalize = [&](int par, int ln) {
         float carry = 0.f;
 #pragma unroll
@@ -807,6 +822,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const float tot = R[PL0 + 3][3] + carry;
             gam[ln] = __builtin_amdgcn_exp2f(tot);
             glog += tot;
+            // (also true for a NaN total)
+            beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= -RANGE_LOG2)) != 0;
         }
     };
     // loaded pieces -> LDS
@@ -1105,16 +1122,19 @@ __global__ __launch_bounds__(512) void scan_kernel(
         prev_tc = tc;
         prev_n = n;
     }
-    if (prev_n > 0) {
-        block_sync();
-        if (outw) store_o(prev_tc, prev_n, lane);
-    }
+    __shared__ int beyond_s;
+    if (wave == 7 && lane == 0) beyond_s = beyond ? 1 : 0;
+    block_sync();
+    const bool unit_beyond = beyond_s != 0;
+    if (outw) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
+    if (range_flags && tid == 0)
+        range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
 
     // the unit's total log2-decay per value row, when asked for (the sequence-parallel
     // path composes segments with it)
     if (glog_out && wave == 7) glog_out[(static_cast<int64_t>(u.seq) * H + h) * DV + i0 + lane] = glog;
 
-    if (S_T && chain) {
+    if (S_T && chain && !unit_beyond) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
@@ -1146,10 +1166,11 @@ static size_t segment_log_bytes(int32_t n_seq, int32_t n_heads, int32_t d_v, int
 //   order      NS int32      longest-first schedule (packed input)
 //   chunk_off  NS + 1 int32  first chunk of every sequence (packed input)
 //   cu_seg     NS + 1 int32  segment token offsets (split calls only)
+//   flags      NS x n_heads x (d_v / 64) int32: units beyond the decay range
 //   A records  (n_tok / C + n_seq) x n_heads x A_RECORD_BYTES
 //   dS, M, S_start, glog     segment states (split calls only)
 struct Bf16Layout {
-    size_t order, chunk_off, cu_seg, rec, seg, total;
+    size_t order, chunk_off, cu_seg, flags, rec, seg, total;
 };
 
 static Bf16Layout bf16_layout(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
@@ -1159,7 +1180,8 @@ static Bf16Layout bf16_layout(int32_t n_seq, int32_t n_tok, int32_t n_heads, int
     L.order = 0;
     L.chunk_off = L.order + align256(ns * 4);
     L.cu_seg = L.chunk_off + align256((ns + 1) * 4);
-    L.rec = L.cu_seg + (G > 1 ? align256((ns + 1) * 4) : 0);
+    L.flags = L.cu_seg + (G > 1 ? align256((ns + 1) * 4) : 0);
+    L.rec = L.flags + align256(ns * n_heads * static_cast<size_t>(d_v / BV) * 4);
     L.seg = L.rec + align256(static_cast<size_t>(chunk_bound(n_seq, n_tok)) * n_heads * A_RECORD_BYTES);
     L.total = L.seg;
     if (G > 1) L.total += 3 * segment_state_bytes(n_seq, n_heads, d_k, d_v, G) + segment_log_bytes(n_seq, n_heads, d_v, G);
@@ -1177,6 +1199,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+    int32_t* rflags = reinterpret_cast<int32_t*>(ws + L.flags);
     uint16_t* arec = reinterpret_cast<uint16_t*>(ws + L.rec);
     const int64_t mc = chunk_bound(a.n_seq, a.n_tok);
     hipError_t e;
@@ -1219,15 +1242,23 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int nsq, float* st,
-                    int flags, float* glog) {
+                    int flags, float* glog, int32_t* rf) {
         const int64_t grid = prefill_grid(static_cast<int64_t>(nsq) * a.n_heads, nvb);
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(vv), al, s0, cu, cu ? order : nullptr, chunk_off, arec, nsq,
-                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog);
+                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog, rf);
         return hipGetLastError();
     };
-    if (G == 1) return scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, a.S0, a.n_seq, a.S_T, 0, nullptr);
+    // Units with a chunk beyond the decay range (marked in rflags by the scan, S_T left
+    // unwritten) are recomputed token by token; the pass returns at once for the others.
+    // Without a gate nothing decays, so nothing can be marked.
+    if (G == 1) {
+        if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, a.S0, a.n_seq, a.S_T, 0, nullptr,
+                      GATE == GATE_NONE ? nullptr : rflags)) != hipSuccess)
+            return e;
+        return GATE == GATE_NONE ? hipSuccess : launch_prefill_range_fixup(a, rflags, 1, stream);
+    }
 
     // Sequence-parallel path (d_k = d_v, few units, long sequences):
     //   1. dS: each segment's end state from a zero start, and its total log2-decay
@@ -1244,14 +1275,19 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     float* Mt = reinterpret_cast<float*>(ws + L.seg + sb);
     float* Sst = reinterpret_cast<float*>(ws + L.seg + 2 * sb);
     float* glog = reinterpret_cast<float*>(ws + L.seg + 3 * sb);
-    if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, nullptr, ns, dS, 0, glog)) != hipSuccess) return e;
-    if ((e = scan(scan_kernel<DK, DK, GATE_NONE, true>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
-                  SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr)) != hipSuccess)
+    int32_t* rf = GATE == GATE_NONE ? nullptr : rflags;
+    if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, nullptr, ns, dS, 0, glog, rf)) != hipSuccess)
         return e;
-    if ((e = launch_combine_segments<DK, DV>(glog, a.S0, dS, Mt, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
+    if ((e = scan(scan_kernel<DK, DK, GATE_NONE, true>, DK / BV, a.v, nullptr, nullptr, ns, Mt,
+                  SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr, nullptr)) != hipSuccess)
+        return e;
+    if ((e = launch_combine_segments<DK, DV>(glog, a.S0, dS, Mt, rf, a.n_seq, G, a.n_heads, Sst, a.S_T,
+                                             stream)) != hipSuccess)
+        return e;
+    if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, Sst, ns, nullptr, 0, nullptr, nullptr)) !=
         hipSuccess)
         return e;
-    return scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, Sst, ns, nullptr, 0, nullptr);
+    return rf ? launch_prefill_range_fixup(a, rf, G, stream) : hipSuccess;
 }
 
 template <int GATE>

@@ -248,13 +248,18 @@ __device__ __forceinline__ float sum_lanes(float x) {
 
 // CKPT: the backward's forward pass -- no o, and the state entering every block
 // stored into ckpt.
+// range_flags (or null): only the units marked there are computed (the
+// recomputation after the chunked bf16 scan, launch_prefill_range_fixup); a
+// workgroup returns at once unless one of the flag_segs segments of its
+// sequence is marked for its block of 64 value rows.
 template <typename T, int DK, int DV, int GATE, int R, int L, bool CKPT>
 __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
-    T* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt) {
+    T* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt,
+    const int32_t* __restrict__ range_flags, int flag_segs) {
     constexpr int TB = STAGE_TOKENS;
     constexpr int NT = L * R;                // threads: L lanes per row
     constexpr int M = DK / (4 * L);          // float4 chunks of a row per lane
@@ -273,6 +278,14 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const int row0 = u.vblk * R;
     const int64_t H = n_heads;
     const int h = u.head;
+    if (range_flags) {
+        static_assert(R <= 64 && 64 % R == 0, "a workgroup's rows lie in one block of 64");
+        bool marked = false;
+        for (int g = 0; g < flag_segs; ++g)
+            marked = marked ||
+                     range_flags[((static_cast<int64_t>(u.seq) * flag_segs + g) * H + h) * (DV / 64) + row0 / 64] != 0;
+        if (!marked) return;
+    }
 
     const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row0 + r) * DK;
     f32x4 s[M];
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
                 const int64_t t = tok(tb, gi / (DK / 4));
                 const int c = 4 * (gi % (DK / 4));
                 rk[p] = Rw::load(k + (t * H + h) * DK + c);
-                rq[p] = Rw::load(q + (t * H + h) * DK + c);
+                if constexpr (!CKPT) rq[p] = Rw::load(q + (t * H + h) * DK + c);  // no read-out without o
                 if constexpr (GATE == GATE_KEY) rak[p] = *reinterpret_cast<const f32x4*>(alpha + (t * H + h) * DK + c);
             }
         }
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
             if (KN % NT == 0 || gi < KN) {
                 const int tl = gi / (DK / 4), c = gi % (DK / 4);
                 B.k[tl][c] = Rw::widen(rk[p]);
-                B.q[tl][c] = Rw::widen(rq[p]);
+                if constexpr (!CKPT) B.q[tl][c] = Rw::widen(rq[p]);
                 if constexpr (GATE == GATE_KEY) B.ak[tl][c] = rak[p];
             }
         }
@@ -362,14 +375,16 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
                 else
                     s[m][e] += uu * x.k[m][e];
             }
-        float c0 = 0.f, c1 = 0.f;
+        if constexpr (!CKPT) {
+            float c0 = 0.f, c1 = 0.f;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            c0 += s[m][0] * x.q[m][0] + s[m][2] * x.q[m][2];
-            c1 += s[m][1] * x.q[m][1] + s[m][3] * x.q[m][3];
+            for (int m = 0; m < M; ++m) {
+                c0 += s[m][0] * x.q[m][0] + s[m][2] * x.q[m][2];
+                c1 += s[m][1] * x.q[m][1] + s[m][3] * x.q[m][3];
+            }
+            const float oo = sum_lanes<L>(c0 + c1);
+            if (j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
         }
-        const float oo = sum_lanes<L>(c0 + c1);
-        if (!CKPT && j == 0) Elem<T>::store(o + (t * H + h) * DV + row0 + r, oo);
     };
 
     const int64_t len = u.t1 - u.t0;
@@ -411,19 +426,20 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
 }
 
 template <typename T, int DK, int DV, int GATE, int R, int L = 8>
-static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream, float* ckpt) {
+static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hipStream_t stream, float* ckpt,
+                                  const int32_t* range_flags = nullptr, int flag_segs = 1) {
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / R);
     if (ckpt) {
         hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(L * R), 0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok,
-                           a.n_heads, nullptr, nullptr, ckpt);
+                           a.n_heads, nullptr, nullptr, ckpt, nullptr, 1);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, false>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
                        0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok, a.n_heads,
-                       static_cast<T*>(a.o), a.S_T, ckpt);
+                       static_cast<T*>(a.o), a.S_T, ckpt, range_flags, flag_segs);
     return hipGetLastError();
 }
 
@@ -533,5 +549,29 @@ hipError_t launch_prefill_recurrent(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) { return launch_prefill_recurrent(a, stream); }
+
+// The units of a chunked bf16 call that its scan marked as beyond the decay range,
+// recomputed from S0 by the staged form (64 rows per workgroup, the scan's row
+// blocks; sequences in index order).  No log of alpha is taken here, so alpha = 0
+// and any strength of decay are exact.
+template <int DK, int DV>
+static hipError_t launch_fixup_t(const PrefillArgs& a, const int32_t* range_flags, int G, hipStream_t stream) {
+    switch (a.gate) {
+        case GATE_CHANNEL:
+            return launch_staged_r<uint16_t, DK, DV, GATE_CHANNEL, 64>(a, nullptr, stream, nullptr, range_flags, G);
+        case GATE_SCALAR:
+            return launch_staged_r<uint16_t, DK, DV, GATE_SCALAR, 64>(a, nullptr, stream, nullptr, range_flags, G);
+        default: return hipErrorInvalidValue;  // no gate: nothing decays, nothing is marked
+    }
+}
+
+hipError_t launch_prefill_range_fixup(const PrefillArgs& a, const int32_t* range_flags, int G, hipStream_t stream) {
+    if (!a.bf16 || a.n_tok <= 0) return hipSuccess;
+    if (a.d_k == 128 && a.d_v == 128) return launch_fixup_t<128, 128>(a, range_flags, G, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_fixup_t<64, 64>(a, range_flags, G, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_fixup_t<128, 64>(a, range_flags, G, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_fixup_t<64, 128>(a, range_flags, G, stream);
+    return hipErrorInvalidValue;
+}
 
 }  // namespace kda

@@ -32,11 +32,15 @@ namespace kda {
 // composed, so a step waits only for its own LDS products.
 // Layouts: dS, S_start [n_seq G, H, d_v, d_k]; M [n_seq G, H, d_k, d_k];
 // glog [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
+// range_flags [n_seq G, H, d_v / 64] (or null): segments whose scan met a chunk
+// beyond the decay range of the factored form; their dS is not valid, so a
+// workgroup whose rows belong to such a segment leaves S_T unwritten (S0 stays
+// intact when S_T aliases it) for the token-recurrent pass that follows.
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void combine_segments_kernel(
     const float* __restrict__ glog, const float* __restrict__ S0, const float* __restrict__ dS,
-    const float* __restrict__ M, int n_seq, int G, int n_heads, float* __restrict__ S_start,
-    float* __restrict__ S_T) {
+    const float* __restrict__ M, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
+    float* __restrict__ S_start, float* __restrict__ S_T) {
     constexpr int NT = 512;
     constexpr int KS = 4;                 // quarters of the reduction index
     constexpr int CG = DK / 4;            // column groups per row
@@ -112,22 +116,29 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
         // Ps is rewritten only after the next segment's first barrier, which every
         // owner reaches after reading it here
     }
-    if (owner && S_T) *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
+    bool beyond = false;
+    if (range_flags) {
+        const int vb = (rblk * ROWS) / 64;  // the scan's block of 64 rows that holds these rows
+        for (int g = 0; g < G; ++g) beyond = beyond || range_flags[(seg_of(g) * H + h) * (DV / 64) + vb] != 0;
+    }
+    if (owner && S_T && !beyond)
+        *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
 }
 
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M, int n_seq,
-                                   int G, int n_heads, float* S_start, float* S_T, hipStream_t stream) {
+hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M,
+                                   const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
+                                   float* S_T, hipStream_t stream) {
     constexpr int NRB = DV / (512 / (DK / 4 * 4));
     const int64_t grid = static_cast<int64_t>(n_seq) * n_heads * NRB;
     hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       glog, S0, dS, M, n_seq, G, n_heads, S_start, S_T);
+                       glog, S0, dS, M, range_flags, n_seq, G, n_heads, S_start, S_T);
     return hipGetLastError();
 }
 
-template hipError_t launch_combine_segments<128, 128>(const float*, const float*, const float*, const float*, int,
-                                                      int, int, float*, float*, hipStream_t);
-template hipError_t launch_combine_segments<64, 64>(const float*, const float*, const float*, const float*, int, int,
-                                                    int, float*, float*, hipStream_t);
+template hipError_t launch_combine_segments<128, 128>(const float*, const float*, const float*, const float*,
+                                                      const int32_t*, int, int, int, float*, float*, hipStream_t);
+template hipError_t launch_combine_segments<64, 64>(const float*, const float*, const float*, const float*,
+                                                    const int32_t*, int, int, int, float*, float*, hipStream_t);
 
 }  // namespace kda

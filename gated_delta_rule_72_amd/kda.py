@@ -108,6 +108,50 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(name, t, shape, dtype):
+    """Raise ValueError unless tensor t (may not be None) has this shape and dtype."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _gate_shape(fn: str, n_tok: int, H: int, dk: int, dv: int):
+    """Shape of alpha for the gate form of entry point fn (None: the form takes none)."""
+    if fn.endswith("_key_gate"):
+        return (n_tok, H, dk)
+    if fn.endswith("_scalar_gate"):
+        return (n_tok, H)
+    return (n_tok, H, dv)
+
+
+def _check_qkv(q, k, v):
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be 3-d: [n_tok, H, d_k], [n_tok, H, d_k], [n_tok, H, d_v]")
+    _dtype_code(q)
+    _expect("k", k, q.shape, q.dtype)
+    if v.shape[:2] != q.shape[:2] or v.dtype != q.dtype:
+        raise ValueError(f"v must be [{q.shape[0]}, {q.shape[1]}, d_v] in {q.dtype}, got "
+                         f"{tuple(v.shape)} {v.dtype}")
+    return torch
+
+
+def _check_inputs(fn, q, k, v, alpha, beta, S0, n_seq):
+    """Shapes and dtypes of a prefill call's inputs (the C ABI sees raw pointers only)."""
+    torch = _check_qkv(q, k, v)
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    f32 = torch.float32
+    if alpha is not None or not fn.endswith("_scalar_gate"):
+        _expect("alpha", alpha, _gate_shape(fn, n_tok, H, dk, dv), f32)
+    _expect("beta", beta, (n_tok, H), f32)
+    if S0 is not None:
+        _expect("S0", S0, (n_seq, H, dv, dk), f32)
+
+
 def _stream(t) -> int:
     torch = _torch()
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -148,20 +192,24 @@ def kda_prefill_key_gate(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *,
 
 
 def _prefill(fn, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state, workspace):
-    torch = _torch()
+    torch = _check_qkv(q, k, v)
     n_tok, H, dk = q.shape
     dv = v.shape[2]
     dt = _dtype_code(q)
     if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int32 tensor")
         n_seq = cu_seqlens.shape[0] - 1
     elif n_seq is None:
         n_seq = S0.shape[0] if S0 is not None else 1
+    _check_inputs(fn, q, k, v, alpha, beta, S0, n_seq)
     if o is None:
         o = torch.empty((n_tok, H, dv), dtype=q.dtype, device=q.device)
+    _expect("o", o, (n_tok, H, dv), q.dtype)
     if S_T is None and want_state:
         S_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _expect("S_T", S_T, (n_seq, H, dv, dk), torch.float32)
     ws_bytes = workspace_size(n_seq, n_tok, H, dk, dv, dt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -196,12 +244,17 @@ def kda_decode_step_key_gate(q, k, v, alpha, beta, S, o=None):
 
 
 def _decode(fn, q, k, v, alpha, beta, S, o):
-    torch = _torch()
+    torch = _check_qkv(q, k, v)
     B, H, dk = q.shape
     dv = v.shape[2]
     dt = _dtype_code(q)
+    if alpha is not None or not fn.endswith("_scalar_gate"):
+        _expect("alpha", alpha, _gate_shape(fn, B, H, dk, dv), torch.float32)
+    _expect("beta", beta, (B, H), torch.float32)
+    _expect("S", S, (B, H, dv, dk), torch.float32)
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _expect("o", o, (B, H, dv), q.dtype)
     st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), _ptr(o),
                             B, H, dk, dv, dt, _stream(q))
     if st != KDA_OK:
@@ -214,15 +267,20 @@ def backward_workspace_size(n_seq: int, n_tok: int, n_heads: int, d_k: int, d_v:
 
 
 def _backward(fn, q, k, v, alpha, beta, S0, cu_seqlens, dO, dS_T, n_seq, want_dS0, workspace):
-    torch = _torch()
+    torch = _check_qkv(q, k, v)
     n_tok, H, dk = q.shape
     dv = v.shape[2]
     if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int32 tensor")
         n_seq = cu_seqlens.shape[0] - 1
     elif n_seq is None:
         n_seq = S0.shape[0] if S0 is not None else 1
+    _check_inputs(fn.replace("_backward", ""), q, k, v, alpha, beta, S0, n_seq)
+    # the incoming gradients are float32 whatever the input dtype (o of a bf16 call is bf16)
+    _expect("dO", dO, (n_tok, H, dv), torch.float32)
+    if dS_T is not None:
+        _expect("dS_T", dS_T, (n_seq, H, dv, dk), torch.float32)
     f32 = dict(dtype=torch.float32, device=q.device)
     grads = dict(dq=torch.empty((n_tok, H, dk), **f32), dk=torch.empty((n_tok, H, dk), **f32),
                  dv=torch.empty((n_tok, H, dv), **f32),

@@ -28,11 +28,14 @@
  *     outputs are undefined.  Nothing aborts the process.
  *   - NaN and Inf inputs are not checked; they propagate.
  *   - d_k and d_v must each be 64 or 128.
- *   - alpha is taken as given (the gate after its activation).  The bf16
- *     prefill assumes that the sum of log(alpha) over any 64 consecutive
- *     tokens of a value channel stays above -80 (a decay factor of ~1e-35);
- *     alpha == 0 exactly is outside that domain.  The float32 prefill and the
- *     decode step run token by token and are exact for alpha == 0.
+ *   - alpha is taken as given (the gate after its activation), in [0, 1];
+ *     alpha == 0 forgets a row (or, for the key-channel variants, a column)
+ *     entirely and is handled exactly by every entry point.  The bf16 prefill's
+ *     chunked form scales values by the inverse of a row's decay within a
+ *     64-token chunk; a (sequence, head, 64-row block) in which some row decays
+ *     by more than 2^-100 within one chunk (alpha == 0 included) is recomputed
+ *     token by token, from S0, inside the same call.  That costs time, never
+ *     accuracy.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -72,7 +75,9 @@ const char* kda_status_string(kda_status s);
  *   KDA_DTYPE_F32:  the longest-first schedule of the packed sequences
  *                   (n_seq int32, rounded up to 256 bytes).
  *   KDA_DTYPE_BF16: the schedule, the first chunk of every sequence
- *                   ((n_seq + 1) int32), and the solved within-chunk system
+ *                   ((n_seq + 1) int32), one int32 per (sequence, head, 64
+ *                   value rows) marking blocks that need the token-by-token
+ *                   recomputation, and the solved within-chunk system
  *                   A = (I + L)^{-1} diag(beta) of every (chunk, head) -- 12 KiB
  *                   each, for at most n_tok / 64 + n_seq chunks of 64 tokens.
  *                   Calls with few (sequence, head) pairs and long sequences
@@ -155,8 +160,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
  *           aligned.  NULL: no forget gate (alpha = 1), the delta rule.
  * Every other argument, the workspace (kda_prefill_workspace_size), the
  * layouts, the conventions and the errors are those of kda_prefill and
- * kda_decode_step.  The prefill domain condition on alpha applies per token:
- * the sum of log(alpha) over 64 consecutive tokens must stay above -80.
+ * kda_decode_step, including the handling of strong decay described at the
+ * top of this file.
  */
 kda_status kda_prefill_scalar_gate(const void* q, const void* k, const void* v,
                                    const float* alpha, const float* beta,

@@ -46,11 +46,12 @@ def test_workspace_size(L):
     # fp32: the longest-first schedule (n_seq int32, 256-byte aligned)
     assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 0) == 256
     assert L.kda_prefill_workspace_size(65, 1000, 16, 128, 128, 0) == 512
-    # bf16: schedule + chunk offsets (n_seq + 1 int32) + one 12 KiB block of the solved
+    # bf16: schedule + chunk offsets (n_seq + 1 int32) + the decay-range marks (one int32
+    # per (sequence, head, 64 value rows)) + one 12 KiB block of the solved
     # A = (I + L)^{-1} diag(beta) per (chunk, head), for at most n_tok // 64 + n_seq chunks
     rec = 3 * 2 * 32 * 32 * 2
-    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 1) == 256 + 512 + (15 + 64) * 16 * rec
-    assert L.kda_prefill_workspace_size(1, 0, 4, 64, 64, 1) == 256 + 256 + 1 * 4 * rec
+    assert L.kda_prefill_workspace_size(64, 1000, 16, 128, 128, 1) == 256 + 512 + 8192 + (15 + 64) * 16 * rec
+    assert L.kda_prefill_workspace_size(1, 0, 4, 64, 64, 1) == 256 + 256 + 256 + 1 * 4 * rec
     assert L.kda_prefill_workspace_size(0, 1000, 16, 128, 128, 1) == 0
     assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
 
@@ -60,15 +61,16 @@ def test_workspace_size_of_split_calls(L):
     (G >= 8, units x G <= 256, on average two chunks or more per segment); their
     workspace adds the segment bookkeeping and states.  Layout, 256-byte aligned parts:
     order NS int32, chunk offsets NS+1, segment offsets NS+1 (split calls only),
-    A records (n_tok/64 + n_seq) x H x 12 KiB, then dS, M, S_start (NS x H x d x d fp32
-    each) and the log2-decays (NS x H x d fp32), NS = n_seq G."""
+    decay-range marks NS x H x d/64 int32, A records (n_tok/64 + n_seq) x H x 12 KiB,
+    then dS, M, S_start (NS x H x d x d fp32 each) and the log2-decays (NS x H x d fp32),
+    NS = n_seq G."""
     al = lambda x: (x + 255) // 256 * 256
     rec = 3 * 2 * 32 * 32 * 2
 
     def split_size(n_seq, n_tok, H, d, G):
         ns = n_seq * G
-        return (al(ns * 4) + al((ns + 1) * 4) + al((ns + 1) * 4) + al((n_tok // 64 + n_seq) * H * rec)
-                + 3 * ns * H * d * d * 4 + al(ns * H * d * 4))
+        return (al(ns * 4) + al((ns + 1) * 4) + al((ns + 1) * 4) + al(ns * H * (d // 64) * 4)
+                + al((n_tok // 64 + n_seq) * H * rec) + 3 * ns * H * d * d * 4 + al(ns * H * d * 4))
 
     # one 4096-token sequence, 8 heads, d = 128: 16 units -> G = 16
     assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 128, 1) == split_size(1, 4096, 8, 128, 16)
@@ -78,12 +80,13 @@ def test_workspace_size_of_split_calls(L):
     assert L.kda_prefill_workspace_size(1, 2048, 1, 64, 64, 1) == split_size(1, 2048, 1, 64, 16)
     # not split: 256 units (the batched workload), G < 8 (two sequences of 8192 tokens,
     # 32 heads), segments too short (512 tokens, 8 heads: G would be 4), d_k != d_v, fp32
-    unsplit = lambda n_seq, n_tok, H: al(n_seq * 4) + al((n_seq + 1) * 4) + al((n_tok // 64 + n_seq) * H * rec)
+    unsplit = lambda n_seq, n_tok, H, dv=128: (al(n_seq * 4) + al((n_seq + 1) * 4) + al(n_seq * H * (dv // 64) * 4)
+                                               + al((n_tok // 64 + n_seq) * H * rec))
     assert L.kda_prefill_workspace_size(4, 32768, 32, 128, 128, 1) == unsplit(4, 32768, 32)
     assert L.kda_prefill_workspace_size(2, 16384, 32, 128, 128, 1) == unsplit(2, 16384, 32)
     assert L.kda_prefill_workspace_size(1, 512, 8, 128, 128, 1) == unsplit(1, 512, 8)
     assert L.kda_prefill_workspace_size(1, 1024, 8, 128, 128, 1) == split_size(1, 1024, 8, 128, 8)
-    assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 64, 1) == unsplit(1, 4096, 8)
+    assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 64, 1) == unsplit(1, 4096, 8, 64)
     assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 128, 0) == 256
 
 
@@ -176,8 +179,88 @@ def test_decode_scalar_gate_rejects_on_host(L, kw, status):
 def test_binding_refuses_cpu_tensors(L):
     torch = pytest.importorskip("torch")
     q = torch.zeros(4, 2, 64)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="GPU tensors only"):
         kda.kda_decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 64, 64))
+
+
+def _prefill_args(torch, n_tok=32, H=2, dk=64, dv=128, n_seq=2, dt=None):
+    dt = dt or torch.bfloat16
+    f = torch.float32
+    return dict(q=torch.zeros(n_tok, H, dk, dtype=dt), k=torch.zeros(n_tok, H, dk, dtype=dt),
+                v=torch.zeros(n_tok, H, dv, dtype=dt), alpha=torch.zeros(n_tok, H, dv, dtype=f),
+                beta=torch.zeros(n_tok, H, dtype=f), S0=torch.zeros(n_seq, H, dv, dk, dtype=f))
+
+
+@pytest.mark.parametrize("change,match", [
+    (lambda t, a: a.update(k=a["k"].float()), "k must be"),                     # k not q's dtype
+    (lambda t, a: a.update(v=a["v"][:, :1].contiguous()), "v must be"),          # v of other heads
+    (lambda t, a: a.update(alpha=a["alpha"][..., :64].contiguous()), "alpha must have shape"),  # key-gate shape
+    (lambda t, a: a.update(alpha=a["alpha"].double()), "alpha must be"),
+    (lambda t, a: a.update(alpha=None), "alpha is required"),
+    (lambda t, a: a.update(beta=a["beta"].to(t.bfloat16)), "beta must be"),
+    (lambda t, a: a.update(S0=a["S0"][:1].contiguous()), "S0 must have shape"),
+    (lambda t, a: a.update(S0=a["S0"].transpose(2, 3).contiguous()), "S0 must have shape"),
+])
+def test_binding_checks_prefill_shapes_and_dtypes(L, change, match):
+    """The binding rejects mismatched tensors with ValueError before any library call
+    (the C ABI sees raw pointers only); CPU tensors suffice, nothing reaches the device."""
+    torch = pytest.importorskip("torch")
+    a = _prefill_args(torch)
+    change(torch, a)
+    with pytest.raises(ValueError, match=match):
+        kda.kda_prefill(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, n_seq=2)
+
+
+def test_binding_checks_gate_forms(L):
+    torch = pytest.importorskip("torch")
+    a = _prefill_args(torch)
+    # the scalar gate takes [n_tok, H] (or None); the key-channel gate [n_tok, H, d_k]
+    with pytest.raises(ValueError, match=r"alpha must have shape \(32, 2\)"):
+        kda.kda_prefill_scalar_gate(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, n_seq=2)
+    with pytest.raises(ValueError, match=r"alpha must have shape \(32, 2, 64\)"):
+        kda.kda_prefill_key_gate(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, n_seq=2)
+    # no gate passes the checks and is refused only for being on the CPU
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        kda.kda_prefill_scalar_gate(a["q"], a["k"], a["v"], None, a["beta"], a["S0"], None, n_seq=2)
+    with pytest.raises(ValueError, match="o must be"):
+        kda.kda_prefill(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, n_seq=2,
+                        o=torch.zeros(32, 2, 128))
+    with pytest.raises(ValueError, match="S_T must have shape"):
+        kda.kda_prefill(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, n_seq=2,
+                        S_T=torch.zeros(2, 2, 64, 128))
+
+
+def test_binding_checks_backward_gradients(L):
+    """A bf16 call's o is bf16; the backward takes dO in float32 and says so, instead of
+    reading a half-size buffer as float32."""
+    torch = pytest.importorskip("torch")
+    a = _prefill_args(torch)
+    dO_bf16 = torch.zeros(32, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dO must be"):
+        kda.kda_prefill_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, dO_bf16, n_seq=2)
+    dO = torch.zeros(32, 2, 128)
+    with pytest.raises(ValueError, match="dS_T must have shape"):
+        kda.kda_prefill_backward(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, dO,
+                                 torch.zeros(2, 2, 128, 128), n_seq=2)
+    with pytest.raises(ValueError, match="alpha must have shape"):
+        kda.kda_prefill_backward_scalar_gate(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], None, dO,
+                                             n_seq=2)
+    with pytest.raises(ValueError, match="k must be"):
+        kda.kda_prefill_backward(a["q"], a["k"].float(), a["v"], a["alpha"], a["beta"], a["S0"], None, dO, n_seq=2)
+
+
+def test_binding_checks_decode_shapes(L):
+    torch = pytest.importorskip("torch")
+    bf = torch.bfloat16
+    q = torch.zeros(4, 2, 64, dtype=bf)
+    v = torch.zeros(4, 2, 128, dtype=bf)
+    S = torch.zeros(4, 2, 128, 64)
+    with pytest.raises(ValueError, match="alpha must have shape"):
+        kda.kda_decode_step(q, q, v, torch.zeros(4, 2, 64), torch.zeros(4, 2), S)
+    with pytest.raises(ValueError, match="S must have shape"):
+        kda.kda_decode_step(q, q, v, torch.zeros(4, 2, 128), torch.zeros(4, 2), torch.zeros(4, 2, 64, 128))
+    with pytest.raises(ValueError, match="beta must be"):
+        kda.kda_decode_step_scalar_gate(q, q, v, None, torch.zeros(4, 2, dtype=torch.float64), S)
 
 
 def test_backward_workspace_size(L):

@@ -97,3 +97,15 @@ def test_backward_of_empty_sequences_passes_dS_T_through(torch_cuda):
     np.testing.assert_array_equal(dS0[0], dS_T[0])
     np.testing.assert_array_equal(dS0[2], dS_T[2])
     run(torch_cuda, inp, "channel", True, seed=5)
+
+
+# The forward pass that writes the state checkpoints takes 64 rows per workgroup when the
+# call has a workgroup per CU or more (units x d_v / 64 >= 256), else 32 or 16 rows with 16
+# lanes per row: 64 sequences x 4 heads at d_v = 128 select 64 rows, 32 x 2 select 32.
+@pytest.mark.parametrize("n_seq,H,dtype,gate", [(64, 4, "f32", "channel"), (32, 2, "f32", "scalar"),
+                                                (64, 4, "bf16", "key")])
+def test_backward_checkpoint_variants(torch_cuda, n_seq, H, dtype, gate):
+    lens = list(np.random.default_rng(n_seq + H).integers(20, 60, n_seq))
+    print(f"backward gate={gate} {n_seq} sequences of 20-60 tokens, H={H}, d=128, {dtype}", flush=True)
+    inp = I.make_prefill(9300 + n_seq + H, lens, H, 128, 128, dtype, "exp_softplus", 0.02, gate)
+    run(torch_cuda, inp, gate, True, seed=n_seq + H)

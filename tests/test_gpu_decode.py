@@ -102,3 +102,17 @@ def test_decode_alpha_zero_and_one(torch_cuda):
     kda.kda_decode_step(d(dec.q[0]), d(dec.k[0]), d(dec.v[0]), ones, torch.zeros_like(d(dec.beta[0])), S2)
     torch.cuda.synchronize()
     assert torch.equal(S2, d(dec.S0))
+
+
+def test_decode_workload_distributions_over_all_1024_steps(torch_cuda):
+    """The decode workload's 1024 successive steps (its distributions, bf16, d=128,
+    S0 ~ N(0, 0.02^2)) on a reduced batch, B=8 sequences x H=4 heads, against the oracle
+    on every (b, h): o at every step and the state after the last."""
+    w = I.WORKLOADS[4]
+    steps = w["steps"]
+    print(f"decode B=8 H=4 d=128 bf16, all {steps} steps, every (b, h)", flush=True)
+    dec = I.make_decode(I.workload_seed(4), steps, 8, 4, w["dk"], w["dv"], w["dtype"], w["alpha_kind"], w["s0_std"])
+    o, S = run_decode_steps(torch_cuda, dec)
+    o_ref, S_ref = oracle_decode(dec, steps)
+    Hh.check("o", o, o_ref, [(slice(None), b, h) for b in range(8) for h in range(4)], Hh.TOL_BF16)
+    Hh.check("S", S, S_ref, Hh.s_slices(8, 4), Hh.TOL_BF16)
