@@ -25,7 +25,9 @@ KDA_DTYPE_BF16 = 1
 EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size", "kda_prefill",
             "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate",
             "kda_prefill_key_gate", "kda_decode_step_key_gate", "kda_prefill_backward_workspace_size",
-            "kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate")
+            "kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate",
+            "kda_prefill_noalloc")
+NOALLOC_MAX_WORKSPACE = 256 << 20  # KDA_PREFILL_NOALLOC_MAX_WORKSPACE
 
 _lib = None
 
@@ -61,6 +63,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, vp]
+    L.kda_prefill_noalloc.restype = ctypes.c_int
+    L.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp]
     L.kda_prefill_backward_workspace_size.restype = sz
     L.kda_prefill_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     for name in ("kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate"):
@@ -219,6 +223,35 @@ def _prefill(fn, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state
                             _stream(q))
     if st != KDA_OK:
         raise KdaError(fn, st)
+    return o, S_T
+
+
+def kda_prefill_noalloc(q, k, v, alpha, beta, S0=None, cu_seqlens=None, *, n_seq: Optional[int] = None,
+                        o=None, S_T=None, want_state: bool = True):
+    """kda_prefill with the library's own device workspace (no workspace argument, nothing
+    allocated by the library call).  o and S_T are allocated here unless given; callers that
+    cannot allocate pass them.  Same arguments and result as kda_prefill."""
+    torch = _check_qkv(q, k, v)
+    n_tok, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+        n_seq = cu_seqlens.shape[0] - 1
+    elif n_seq is None:
+        n_seq = S0.shape[0] if S0 is not None else 1
+    _check_inputs("kda_prefill", q, k, v, alpha, beta, S0, n_seq)
+    if o is None:
+        o = torch.empty((n_tok, H, dv), dtype=q.dtype, device=q.device)
+    _expect("o", o, (n_tok, H, dv), q.dtype)
+    if S_T is None and want_state:
+        S_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
+    if S_T is not None:
+        _expect("S_T", S_T, (n_seq, H, dv, dk), torch.float32)
+    st = lib().kda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+                                   n_seq, n_tok, H, dk, dv, _dtype_code(q), _ptr(o), _ptr(S_T), _stream(q))
+    if st != KDA_OK:
+        raise KdaError("kda_prefill_noalloc", st)
     return o, S_T
 
 

@@ -17,7 +17,8 @@
  *   - All tensor pointers are DEVICE pointers, owned by the caller, contiguous
  *     in the layouts given below and 16-byte aligned, except beta and
  *     cu_seqlens, which need 4-byte alignment.  The library keeps no device
- *     memory of its own between calls.
+ *     memory of its own between calls, except the workspace array of
+ *     kda_prefill_noalloc once that entry point has been used on a device.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream) and return as soon as the work is enqueued.  The library is
  *     reentrant; calls on different streams may run concurrently if their
@@ -126,6 +127,33 @@ kda_status kda_prefill(const void* q, const void* k, const void* v,
                        int32_t d_k, int32_t d_v, kda_dtype dt,
                        void* o, float* S_T,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc: kda_prefill with the
+ * workspace taken from a device array that the library itself holds (one per
+ * device, KDA_PREFILL_NOALLOC_MAX_WORKSPACE bytes, reserved when the library
+ * first uses it on that device and kept until the process ends).  The call
+ * itself allocates nothing.
+ *   Every argument, layout, convention and result is that of kda_prefill; the
+ *   outputs are bit-identical to kda_prefill's with a workspace of its own.
+ *   Returns KDA_ERR_WORKSPACE, before any HIP call, when
+ *   kda_prefill_workspace_size(...) for these sizes exceeds the maximum
+ *   (the batched workload of 4 x 8192 tokens, 32 heads, d = 128, bf16, needs
+ *   203 MB), and KDA_ERR_DEVICE if the array's address cannot be obtained.
+ *   The array is shared by every call on the device and keeps whatever the
+ *   last call left (nothing in it needs clearing): calls that may overlap in
+ *   time on one device -- different streams, or different threads without
+ *   ordering -- race on it and must not be made.
+ */
+#define KDA_PREFILL_NOALLOC_MAX_WORKSPACE ((size_t)256 << 20)
+
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* S0, const int32_t* cu_seqlens,
+                               int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                               int32_t d_k, int32_t d_v, kda_dtype dt,
+                               void* o, float* S_T, void* stream);
 
 /*
  * Decode step: one new token for each of `batch` sequences (recurrent form,

@@ -325,3 +325,14 @@ def test_backward_key_gate_needs_aligned_alpha(L):
     assert backward(L, fn, alpha=A + 3 * 0x100000 + 4) == kda.KDA_ERR_INVALID_ARGUMENT
     # a scalar gate is read as scalars: 4-byte alignment, so 2 bytes off is rejected
     assert backward(L, "kda_prefill_backward_scalar_gate", alpha=A + 3 * 0x100000 + 2) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_refuses_oversized_calls_on_host(L):
+    """kda_prefill_noalloc checks the workspace its sizes need against the array it holds
+    (KDA_PREFILL_NOALLOC_MAX_WORKSPACE) with host arithmetic alone, before any HIP call."""
+    assert kda.NOALLOC_MAX_WORKSPACE == 256 << 20
+    n_tok = 16 * 8192
+    assert L.kda_prefill_workspace_size(16, n_tok, 32, 128, 128, 1) > kda.NOALLOC_MAX_WORKSPACE
+    st = L.kda_prefill_noalloc(A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, None, None, 16, n_tok,
+                               32, 128, 128, 1, A + 0x500000, A + 0x600000, None)
+    assert st == kda.KDA_ERR_WORKSPACE
