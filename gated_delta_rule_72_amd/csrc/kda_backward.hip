@@ -121,7 +121,8 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     const int32_t* __restrict__ order, const float* __restrict__ dO, const float* __restrict__ dS_T,
     int n_seq, int n_tok, int n_heads, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta,
-    float* __restrict__ dS0, float* __restrict__ ckpt, float* __restrict__ sbuf) {
+    float* __restrict__ dS0, float* __restrict__ ckpt, float* __restrict__ sbuf,
+    const int32_t* __restrict__ range_flags) {
     constexpr int M = DK / 32;
     constexpr int NW = BWD_THREADS / 64;   // waves per workgroup, 8 rows each
     constexpr bool KEY = GATE == GATE_KEY;
@@ -132,6 +133,9 @@ __global__ __launch_bounds__(BWD_THREADS) void backward_kernel(
     __shared__ float red[2][NW][RW];       // double-buffered by token
     const Unit u = map_unit(blockIdx.x, n_seq, n_heads, DV / BWD_ROWS, n_tok, cu_seqlens, order);
     if (!u.valid) return;
+    // only the units marked by the chunked path, when it ran first
+    if (range_flags && range_flags[(static_cast<int64_t>(u.seq) * n_heads + u.head) * (DV / BWD_ROWS) + u.vblk] == 0)
+        return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int j = lane & 7;
@@ -330,18 +334,36 @@ namespace {
 constexpr size_t kWsAlign = 256;
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Workspace: order, chunk offsets and unit marks, then one region used either by the
+// chunked path (solved records, the states entering and the gradients leaving every
+// chunk) or by the token-recurrent path (state checkpoints every 16 tokens, each
+// wave's states within a block) -- the latter also after the chunked passes, for the
+// units they marked, when the chunked region is no longer needed.
 struct BwdLayout {
-    size_t order, ckpt, sbuf, total;
+    size_t order, chunk_off, flags, un;  // un: start of the shared region
+    size_t rec, sck, gck;                // chunked, relative to un
+    size_t ckpt, sbuf;                   // token-recurrent, relative to un
+    size_t total;
 };
 
 BwdLayout bwd_layout(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
     BwdLayout L;
     L.order = 0;
-    L.ckpt = align_up(static_cast<size_t>(n_seq) * 4);
+    L.chunk_off = align_up(static_cast<size_t>(n_seq) * 4);
+    L.flags = L.chunk_off + align_up((static_cast<size_t>(n_seq) + 1) * 4);
+    L.un = L.flags + align_up(static_cast<size_t>(n_seq) * n_heads * (d_v / BWD_ROWS) * 4);
+    const size_t mc = static_cast<size_t>(n_tok) / PREFILL_CHUNK_BF16 + n_seq;
+    const size_t st_bytes = mc * n_heads * d_v * d_k * 4;
+    L.rec = 0;
+    L.sck = align_up(mc * n_heads * 12288);  // 12 KiB solved record per (chunk, head)
+    L.gck = L.sck + align_up(st_bytes);
+    const size_t chunked = L.gck + align_up(st_bytes);
+    L.ckpt = 0;
     const size_t ck_bytes = static_cast<size_t>(bwd_slots(n_seq, n_tok)) * n_heads * d_v * d_k * 4;
-    L.sbuf = align_up(L.ckpt + ck_bytes);
+    L.sbuf = align_up(ck_bytes);
     const int64_t waves = prefill_grid(static_cast<int64_t>(n_seq) * n_heads, d_v / 8);
-    L.total = align_up(L.sbuf + static_cast<size_t>(waves) * BWD_BLOCK * 8 * d_k * 4);
+    const size_t recurrent = align_up(L.sbuf + static_cast<size_t>(waves) * BWD_BLOCK * 8 * d_k * 4);
+    L.total = L.un + (chunked > recurrent ? chunked : recurrent);
     return L;
 }
 
@@ -353,33 +375,35 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t stream) {
 }
 
 template <typename T, int DK, int DV, int GATE>
-hipError_t launch_bwd_t(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, hipStream_t stream) {
+hipError_t launch_bwd_t(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, const int32_t* rf,
+                        hipStream_t stream) {
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, DV / BWD_ROWS);
     hipLaunchKernelGGL((backward_kernel<T, DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(BWD_THREADS), 0,
                        stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.alpha,
                        a.beta, a.S0, a.cu_seqlens, order, a.dO, a.dS_T, a.n_seq, a.n_tok, a.n_heads, a.dq, a.dk,
-                       a.dv, a.dalpha, a.dbeta, a.dS0, ckpt, sbuf);
+                       a.dv, a.dalpha, a.dbeta, a.dS0, ckpt, sbuf, rf);
     return hipGetLastError();
 }
 
 template <typename T, int GATE>
-hipError_t launch_bwd_g(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<T, 128, 128, GATE>(a, order, ckpt, sbuf, stream);
-    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<T, 64, 64, GATE>(a, order, ckpt, sbuf, stream);
-    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<T, 128, 64, GATE>(a, order, ckpt, sbuf, stream);
-    if (a.d_k == 64 && a.d_v == 128) return launch_bwd_t<T, 64, 128, GATE>(a, order, ckpt, sbuf, stream);
+hipError_t launch_bwd_g(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, const int32_t* rf,
+                        hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<T, 128, 128, GATE>(a, order, ckpt, sbuf, rf, stream);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<T, 64, 64, GATE>(a, order, ckpt, sbuf, rf, stream);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<T, 128, 64, GATE>(a, order, ckpt, sbuf, rf, stream);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bwd_t<T, 64, 128, GATE>(a, order, ckpt, sbuf, rf, stream);
     return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_bwd_type(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf,
+hipError_t launch_bwd_type(const BackwardArgs& a, const int32_t* order, float* ckpt, float* sbuf, const int32_t* rf,
                            hipStream_t stream) {
     switch (a.gate) {
-        case GATE_CHANNEL: return launch_bwd_g<T, GATE_CHANNEL>(a, order, ckpt, sbuf, stream);
-        case GATE_SCALAR: return launch_bwd_g<T, GATE_SCALAR>(a, order, ckpt, sbuf, stream);
-        case GATE_NONE: return launch_bwd_g<T, GATE_NONE>(a, order, ckpt, sbuf, stream);
-        case GATE_KEY: return launch_bwd_g<T, GATE_KEY>(a, order, ckpt, sbuf, stream);
+        case GATE_CHANNEL: return launch_bwd_g<T, GATE_CHANNEL>(a, order, ckpt, sbuf, rf, stream);
+        case GATE_SCALAR: return launch_bwd_g<T, GATE_SCALAR>(a, order, ckpt, sbuf, rf, stream);
+        case GATE_NONE: return launch_bwd_g<T, GATE_NONE>(a, order, ckpt, sbuf, rf, stream);
+        case GATE_KEY: return launch_bwd_g<T, GATE_KEY>(a, order, ckpt, sbuf, rf, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -390,12 +414,44 @@ size_t prefill_backward_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_
     return bwd_layout(n_seq, n_tok, n_heads, d_k, d_v).total;
 }
 
+// The token-recurrent backward: a forward pass storing the state every 16 tokens, then the
+// reverse walk; with flags, only the marked units (whole (sequence, head) pairs).
+hipError_t launch_backward_recurrent(const BackwardArgs& a, const int32_t* order, const int32_t* flags, char* un,
+                                     hipStream_t stream) {
+    const BwdLayout L = bwd_layout(a.n_seq, a.n_tok, a.n_heads, a.d_k, a.d_v);
+    float* ckpt = reinterpret_cast<float*>(un + L.ckpt);
+    float* sbuf = reinterpret_cast<float*>(un + L.sbuf);
+    hipError_t e;
+    if (a.n_tok > 0) {
+        const PrefillArgs fa{a.q, a.k, a.v, a.alpha, a.beta, a.S0, a.cu_seqlens, a.n_seq, a.n_tok, a.n_heads,
+                             a.d_k, a.d_v, a.bf16, nullptr, nullptr, nullptr, 0, a.gate};
+        if ((e = launch_prefill_checkpoints(fa, order, ckpt, stream, flags)) != hipSuccess) return e;
+    }
+    return a.bf16 ? launch_bwd_type<uint16_t>(a, order, ckpt, sbuf, flags, stream)
+                  : launch_bwd_type<float>(a, order, ckpt, sbuf, flags, stream);
+}
+
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
     const BwdLayout L = bwd_layout(a.n_seq, a.n_tok, a.n_heads, a.d_k, a.d_v);
     char* ws = static_cast<char*>(a.workspace);
     const int64_t nt = static_cast<int64_t>(a.n_tok) * a.n_heads;
+    hipError_t e;
+    if (a.bf16 && a.gate != GATE_KEY && a.n_tok > 0) {
+        // the chunked path; the units it marks are left to the token-recurrent pass
+        BwdChunkBufs b;
+        b.order = a.cu_seqlens ? reinterpret_cast<int32_t*>(ws + L.order) : nullptr;
+        b.chunk_off = a.cu_seqlens ? reinterpret_cast<int32_t*>(ws + L.chunk_off) : nullptr;
+        b.flags = reinterpret_cast<int32_t*>(ws + L.flags);
+        b.rec = reinterpret_cast<uint16_t*>(ws + L.un + L.rec);
+        b.sck = reinterpret_cast<float*>(ws + L.un + L.sck);
+        b.gck = reinterpret_cast<float*>(ws + L.un + L.gck);
+        b.max_chunks = static_cast<int64_t>(a.n_tok) / PREFILL_CHUNK_BF16 + a.n_seq;
+        if ((e = launch_backward_forward_pass(a, b, stream)) != hipSuccess) return e;
+        if ((e = launch_backward_chunk_passes(a, b, stream)) != hipSuccess) return e;
+        return launch_backward_recurrent(a, b.order, b.flags, ws + L.un, stream);
+    }
     // the summed gradients are accumulated with atomics into zeroed outputs
-    hipError_t e = fill_zero(a.dq, nt * a.d_k, stream);
+    e = fill_zero(a.dq, nt * a.d_k, stream);
     if (e == hipSuccess) e = fill_zero(a.dk, nt * a.d_k, stream);
     if (e == hipSuccess) e = fill_zero(a.dbeta, nt, stream);
     if (e == hipSuccess && a.gate == GATE_SCALAR) e = fill_zero(a.dalpha, nt, stream);
@@ -408,17 +464,7 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         order = ord;
     }
-    float* ckpt = reinterpret_cast<float*>(ws + L.ckpt);
-    float* sbuf = reinterpret_cast<float*>(ws + L.sbuf);
-    if (a.n_tok > 0) {
-        // forward pass: the state entering every block of 16 tokens, into ckpt
-        const PrefillArgs fa{a.q, a.k, a.v, a.alpha, a.beta, a.S0, a.cu_seqlens, a.n_seq, a.n_tok, a.n_heads,
-                             a.d_k, a.d_v, a.bf16, nullptr, nullptr, nullptr, 0, a.gate};
-        e = launch_prefill_checkpoints(fa, order, ckpt, stream);
-        if (e != hipSuccess) return e;
-    }
-    return a.bf16 ? launch_bwd_type<uint16_t>(a, order, ckpt, sbuf, stream)
-                  : launch_bwd_type<float>(a, order, ckpt, sbuf, stream);
+    return launch_backward_recurrent(a, order, nullptr, ws + L.un, stream);
 }
 
 }  // namespace kda

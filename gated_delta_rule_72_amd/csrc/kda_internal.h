@@ -122,11 +122,35 @@ struct BackwardArgs {
     Gate gate;
 };
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream);
+
+// Buffers of the chunked backward (bf16 inputs; value-channel, scalar or no gate),
+// carved from the backward's workspace.
+struct BwdChunkBufs {
+    int32_t* order;      // longest-first schedule (packed input) or null
+    int32_t* chunk_off;  // first chunk of every sequence (packed input) or null
+    int32_t* flags;      // [n_seq, H, d_v / 64]: units left to the token-recurrent pass
+    uint16_t* rec;       // solved records of every (chunk, head): A for the forward, then T
+    float* sck;          // [chunks, H, d_v, d_k] state entering every chunk
+    float* gck;          // [chunks, H, d_v, d_k] gradient of the state leaving every chunk
+    int64_t max_chunks;  // n_tok / 64 + n_seq: bound on the number of chunks
+};
+// The backward's forward pass (kda_prefill_mfma.hip): schedule and chunk offsets for
+// packed input, the chunk solve, the checkpoint scan (states into sck, range marks
+// into flags), and the solve again storing T into rec (marks for tiny beta).
+hipError_t launch_backward_forward_pass(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream);
+// The chunked passes proper (kda_backward_chunk.hip): the reverse state-gradient scan
+// (gck, dS0) and the per-(chunk, head) gradients.
+hipError_t launch_backward_chunk_passes(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream);
+// The token-recurrent backward (kda_backward.hip) of the units marked in flags only
+// (null: every unit), accumulating into outputs zeroed by the caller where summed.
+hipError_t launch_backward_recurrent(const BackwardArgs& a, const int32_t* order, const int32_t* flags, char* ws,
+                                     hipStream_t stream);
 // Tokens between the state checkpoints the backward keeps; the staged forward
 // (kda_prefill_valu.hip) writes them for it: slot n + t0 / 16 + b holds the state
 // entering block b of sequence n (first token t0), [slot, H, d_v, d_k] fp32.
 constexpr int STATE_CHECKPOINT_TOKENS = 16;
-hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream);
+hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream,
+                                      const int32_t* range_flags = nullptr);
 // Workspace bytes: the longest-first schedule, a state checkpoint every 16
 // tokens of every (sequence, head), and each wave's states within one block.
 size_t prefill_backward_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);

@@ -40,132 +40,10 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mfma.h"
 #include "kda_schedule.h"
 
 namespace kda {
-namespace {
-
-constexpr int C = PREFILL_CHUNK_BF16;  // 64 tokens per chunk
-// scan_kernel flags: v read as zero; S0 taken as the identity (d_v = d_k)
-constexpr int SCAN_ZERO_V = 1;
-constexpr int SCAN_S0_IDENTITY = 2;
-constexpr int BV = 64;                 // value rows per scan workgroup
-constexpr int PAD = 8;                 // bf16 row padding (16 bytes) against bank conflicts
-constexpr int CP = C + PAD;            // pitch of bf16 rows of length C
-constexpr int LP = C + 4;              // pitch of fp32 rows of length C
-// A of one (chunk, head): the three nonzero 32x32 blocks (rows 0-31 x cols 0-31,
-// rows 32-63 x cols 0-31, rows 32-63 x cols 32-63), each as hi then lo bf16,
-// row-major; entries above the diagonal are zero.
-constexpr int A_BLOCK_ELEMS = 32 * 32;
-constexpr int A_RECORD_BYTES = 3 * 2 * A_BLOCK_ELEMS * 2;
-constexpr int A_RECORD_PIECES = A_RECORD_BYTES / 16;  // 16-byte pieces
-// word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data
-constexpr int kBufferWord3 = 0x00020000;
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// ------------------------------------------------------------- MFMA helpers
-// v_mfma_f32_32x32x16_bf16 operand layout: lane l supplies row (l & 31) of A
-// (column (l & 31) of B) and the 8 consecutive reduction indices starting at
-// 8 * (l >> 5).  Both operands are read from LDS buffers stored
-// "reduction-index contiguous": A as [m][k], B as [n][k].
-__device__ __forceinline__ bf16x8 frag(const uint16_t* base, int pitch, int row0, int k0, int lane) {
-    const uint16_t* p = base + (row0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5);
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
-
-// The same for v_mfma_f32_16x16x32_bf16: row (l & 15), reduction indices 8 * (l >> 4) ...
-__device__ __forceinline__ bf16x8 frag16(const uint16_t* base, int pitch, int row0, int k0, int lane) {
-    const uint16_t* p = base + (row0 + (lane & 15)) * pitch + k0 + 8 * (lane >> 4);
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// v_mfma_f32_16x16x4_f32: lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15].
-__device__ __forceinline__ f32x4 mfma16f(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Accumulator layout of a 32x32 tile: register r of lane l holds
-// D[row = 8*(r/4) + 4*(l>>5) + (r&3)][col = l & 31]; of a 16x16 tile: register
-// r holds D[4*(l>>4) + r][l & 15].
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// Compiler-only fence: the LDS operand loads above it are issued before the
-// matrix instructions below it, so their latencies overlap instead of each
-// MFMA waiting for its own freshly issued load.  The asm keeps the loads above
-// it; the scheduling barrier keeps the machine scheduler from sinking them
-// back between the MFMAs (which it otherwise does to save registers).
-__device__ __forceinline__ void issue_fence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// Order this wave's own LDS writes before its later LDS reads of other lanes' data.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Buffer resource over [p, p + bytes): loads past the end return 0 and stores
-// past the end are dropped, so a chunk's rows beyond its sequence need no branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i
-// receives element (i % 4) of the 8 bytes addressed by lane 4e + i / 4, as its
-// element e.
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
-
-__device__ inline int64_t seq_start(int seq, int n_seq, int n_tok, const int32_t* cu) {
-    return cu ? static_cast<int64_t>(cu[seq]) : static_cast<int64_t>(seq) * (n_tok / n_seq);
-}
-
-// First global chunk of sequence m (m = n_seq gives the number of chunks):
-// chunk_off[m] for packed sequences of any lengths; for n_seq sequences of
-// n_tok / n_seq tokens each (chunk_off == nullptr) it is m ceil(len / C).
-__device__ inline int first_chunk(int m, int n_seq, int n_tok, const int32_t* chunk_off) {
-    if (chunk_off) return chunk_off[m];
-    return m * ((n_tok / n_seq + C - 1) / C);
-}
-
-// Token range [t0, t0 + n) of global chunk gc.
-struct ChunkRef {
-    int64_t t0;
-    int n;
-};
-
-__device__ inline ChunkRef chunk_ref(int gc, int n_seq, int n_tok, const int32_t* cu,
-                                     const int32_t* chunk_off) {
-    int lo = 0;
-    if (chunk_off) {
-        int hi = n_seq;  // chunk_off[lo] <= gc < chunk_off[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (chunk_off[mid] <= gc) lo = mid;
-            else hi = mid;
-        }
-    } else {
-        lo = gc / first_chunk(1, n_seq, n_tok, nullptr);  // only called while chunks exist
-    }
-    const int64_t s0 = seq_start(lo, n_seq, n_tok, cu), s1 = seq_start(lo + 1, n_seq, n_tok, cu);
-    ChunkRef r;
-    r.t0 = s0 + static_cast<int64_t>(gc - first_chunk(lo, n_seq, n_tok, chunk_off)) * C;
-    r.n = static_cast<int>(min<int64_t>(C, s1 - r.t0));
-    return r;
-}
-
-}  // namespace
 
 // ============================================================================
 // chunk_offsets_kernel: chunk_off[m] = sum_{m' < m} ceil(len_m' / C) for
@@ -224,11 +102,16 @@ __global__ __launch_bounds__(256) void segment_cu_kernel(const int32_t* __restri
 // 16x16 diagonal blocks by forward substitution, then X21 = -X22 L21 X11 at 16
 // and at 32 rows.
 // ============================================================================
-template <int DK>
+// STORE_T (the chunked backward): the record holds T = (I + L)^{-1} itself, without
+// the diag(beta) factor, and a chunk with a token whose |beta| is below 2^-20 marks
+// every row block of its (sequence, head) in range_flags (n_vblk blocks per
+// head): the backward divides by beta there and leaves such units to its
+// token-recurrent pass.
+template <int DK, bool STORE_T = false>
 __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
-    uint16_t* __restrict__ arec) {
+    uint16_t* __restrict__ arec, int32_t* __restrict__ range_flags = nullptr, int n_vblk = 0) {
     constexpr int KP = DK + PAD;
     constexpr int RP = 36;  // pitch of the 32x32 fp32 temporary
     constexpr int KX = (C * KP * 2 > C * LP * 4) ? C * KP * 2 : C * LP * 4;
@@ -284,6 +167,14 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
         *reinterpret_cast<u32x4*>(Kc + t * KP + 8 * c) = pk[p];
     }
     if (tid < C) bs[tid] = pb;
+    if constexpr (STORE_T) {
+        if (wave == 0) {
+            const ChunkRef ch = chunk_ref(gc, n_seq, n_tok, cu_seqlens, chunk_off);
+            const bool tiny = lane < ch.n && !(fabsf(pb) >= 0x1p-20f);
+            if (__builtin_amdgcn_ballot_w64(tiny) != 0 && lane < n_vblk)
+                range_flags[(static_cast<int64_t>(ch.seq) * n_heads + h) * n_vblk + lane] = 1;
+        }
+    }
     block_sync();
     fetch(w + gridDim.x);
 
@@ -471,8 +362,8 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
         float av[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float xv = e < 4 ? x0[e] * b0[e] : x1[e - 4] * b1[e - 4];
-            av[e] = s0 + e <= t ? xv : 0.f;
+            const float xv = e < 4 ? x0[e] : x1[e - 4];
+            av[e] = s0 + e <= t ? (STORE_T ? xv : xv * (e < 4 ? b0[e] : b1[e - 4])) : 0.f;
         }
         u32x4 wh, wl;
 #pragma unroll
@@ -541,28 +432,6 @@ struct ScanSmem {
     static constexpr int TOTAL = RK + RQ + RS + RA + RP + RU + RX + RO + RG + RB + RT;
 };
 
-// 16x16x32 operand whose 8 reduction values per lane are the stacked-tile
-// indices {4g..4g+3, 16+4g..16+4g+3} (g = lane / 16) past k0, from a row-major
-// [row][k] buffer: row row0 + lane % 16.
-__device__ __forceinline__ bf16x8 frag_st(const uint16_t* base, int pitch, int row0, int k0, int lane) {
-    const uint16_t* p = base + (row0 + (lane & 15)) * pitch + k0 + 4 * (lane >> 4);
-    const u16x4 lo = *reinterpret_cast<const u16x4*>(p);
-    const u16x4 hi = *reinterpret_cast<const u16x4*>(p + 16);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// The stacked-tile B operand of two 16x16 accumulator tiles a (first 16 rows)
-// and b (next 16), rounded to bf16 as hi + lo parts.
-__device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
-    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split_bf16x2(a[0], a[1], h0, l0);
-    split_bf16x2(a[2], a[3], h1, l1);
-    split_bf16x2(b[0], b[1], h2, l2);
-    split_bf16x2(b[2], b[3], h3, l3);
-    hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
-    lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
-}
-
 // SPLIT_S: the state enters K S^T as hi + lo bf16 (two MFMAs per step) instead of
 // one bf16 copy; used where no decay damps that rounding (the segment transitions
 // of the sequence-parallel path, which start from S0 = I).
@@ -578,14 +447,19 @@ __device__ __forceinline__ void split_stack(const f32x4& a, const f32x4& b, bf16
 // add at most a few powers of two.
 constexpr float RANGE_LOG2 = 100.f;
 
-template <int DK, int DV, int GATE, bool SPLIT_S = false>
+// CKPT (the chunked backward's forward pass): the state entering every chunk is
+// stored into ckpt ([chunk, H, d_v, d_k] fp32, global chunk numbering) and the
+// output side is left out (no q, no P, no O); a unit is also marked when one of
+// its tokens has a gate below 2^-5, since the backward's dalpha = dg / alpha would
+// amplify its rounding there.
+template <int DK, int DV, int GATE, bool SPLIT_S = false, bool CKPT = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
     const uint16_t* __restrict__ arec, int n_seq, int n_tok, int n_heads,
     uint16_t* __restrict__ o, float* __restrict__ S_T, int flags, float* __restrict__ glog_out,
-    int32_t* __restrict__ range_flags) {
+    int32_t* __restrict__ range_flags, float* __restrict__ ckpt = nullptr) {
     using SM = ScanSmem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -728,7 +602,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const int idx = ht + 256 * p;
             const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
             R[PK0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-            R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+            if constexpr (!CKPT)
+                R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
         }
         const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
         const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
@@ -787,18 +662,23 @@ __global__ __launch_bounds__(512) void scan_kernel(
     //   (the rows before this wave's), write G [t][i] and X^T [i][t] = V 2^{-G}
     //   (the chain waves' initial Y); wave 7 writes gamma.
     // Rows past the sequence end contribute log alpha = 0.
+    bool beyond = false;  // loader waves: some chunk of some row of the unit is beyond the range
     auto local_scan = [&](int n, int par, int ln) {
-        float run = 0.f;
+        float run = 0.f, lmin = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            if constexpr (GATE != GATE_NONE)
-                run += 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
+            if constexpr (GATE != GATE_NONE) {
+                const float l = 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
+                run += l;
+                if constexpr (CKPT) lmin = fminf(lmin, l);
+            }
             R[PL0 + r / 4][r % 4] = run;
         }
+        // (also true for a NaN gate)
+        if constexpr (CKPT) beyond = beyond || __builtin_amdgcn_ballot_w64(!(lmin >= -5.f)) != 0;
         Tot[(par * 4 + wave - 4) * BV + ln] = run;
     };
     float glog = 0.f;  // wave 7: this row's total log2-decay over the unit's chunks
-    bool beyond = false;  // wave 7: some chunk of some row of the unit is beyond the range
     auto finalize = [&](int par, int ln) {
         float carry = 0.f;
 #pragma unroll
@@ -833,7 +713,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
         for (int p = 0; p < NKQ; ++p) {
             const int idx = ht + 256 * p;
             *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PK0 + p]);
-            *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
+            if constexpr (!CKPT)
+                *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
         }
 #pragma unroll
         for (int p = 0; p < NA; ++p) stage_a(__builtin_bit_cast(u32x4, R[PA0 + p]), ht + 256 * p);
@@ -843,7 +724,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         prefetch(u.t0, chunk_len(u.t0), chunk0);
         local_scan(chunk_len(u.t0), 0, lane);
     }
-    if (chain) pack_state(lane);
+    if (chain && !CKPT) pack_state(lane);
 
     int64_t prev_tc = u.t0;
     int prev_n = 0;
@@ -859,6 +740,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o;
         const int g = ln >> 4, m16 = ln & 15;
+        if constexpr (CKPT) {
+            // the state entering this chunk, [i][j] rows of 16-byte pieces
+            if (chain) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    float* dst = ckpt + ((static_cast<int64_t>(gc) * H + h) * DV + i0 + rb + 16 * ib + m16) * DK + 4 * g;
+#pragma unroll
+                    for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[(ib) * NJ + (jt)];
+                }
+            }
+        }
         block_sync();  // the previous chunk is done with every buffer
 
         // ======== the loaders stage this chunk and finish its G; the out waves
@@ -866,7 +758,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         if (loader) {
             stage(ln);
             finalize(c & 1, ln);
-        } else if (outw) {
+        } else if (outw && !CKPT) {
             store_o(prev_tc, prev_n, ln);
         }
         block_sync();
@@ -958,6 +850,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     split_stack(U[ib][2 * m], U[ib][2 * m + 1], uh, ul);
                     R[CARRY0 + 2 * ib + m] = __builtin_bit_cast(f32x4, uh);
                     R[CARRY0 + 4 + 2 * ib + m] = __builtin_bit_cast(f32x4, ul);
+                    if constexpr (CKPT) continue;  // no out waves' copy
                     const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 4 * g) = uint2{wh[0], wh[1]};
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 16 + 4 * g) = uint2{wh[2], wh[3]};
@@ -966,6 +859,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 }
             }
         } else if (outw) {
+            if constexpr (!CKPT) {
             // ======== O^T = S Q^T for value rows rb + 16 ib + 4g + r (tile rows) and
             // tokens t = 16 tt + m16 (tile column); every Q fragment serves both blocks
             f32x4 Oacc[2][4];
@@ -990,8 +884,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) R[CARRY0 + 4 * ib + tt] = Oacc[ib][tt];
+            }
         } else {
-            if (wave >= 6) {
+            if (!CKPT && wave >= 6) {
             // ======== P = tril(Q K^T) hi/lo [t][s], formed transposed (32x32 tile
             // D[s][t], so each lane holds 4 consecutive s of one t).  P^T tiles
             // (s-tile, t-tile): wave 6 takes (0,0) and (1,1), wave 7 (0,1); (1,0) is
@@ -1066,8 +961,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int jt = 0; jt < NJ; ++jt) R[(ib) * NJ + (jt)] *= gm;
             }
-            pack_state(ln);
+            if constexpr (!CKPT) pack_state(ln);
         } else if (outw) {
+            if constexpr (!CKPT) {
             // ======== O^T += U^T P^T (P is lower triangular: t-tiles 0, 1 need s < 32),
             // then O = 2^{G} O, staged as bf16 [t][i]
             f32x4 Oacc[2][4];
@@ -1117,16 +1013,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
                                     __builtin_amdgcn_exp2f(g4[3]) * Oacc[ib][tt][3]);
                     *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
                 }
+            }
         }
         if (loader) local_scan(chunk_len(tc + C), (c + 1) & 1, ln);
         prev_tc = tc;
         prev_n = n;
     }
-    __shared__ int beyond_s;
-    if (wave == 7 && lane == 0) beyond_s = beyond ? 1 : 0;
+    __shared__ int beyond_s[4];
+    if (loader && lane == 0) beyond_s[wave - 4] = beyond ? 1 : 0;
     block_sync();
-    const bool unit_beyond = beyond_s != 0;
-    if (outw) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
+    const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
+    if (outw && !CKPT) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
     if (range_flags && tid == 0)
         range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
 
@@ -1238,7 +1135,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         const int64_t grid = std::min<int64_t>(mc * a.n_heads, 4 * static_cast<int64_t>(n_cu));
         hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok, a.n_heads,
-                           static_cast<int>(mc), arec);
+                           static_cast<int>(mc), arec, nullptr, 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int nsq, float* st,
@@ -1247,7 +1144,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(vv), al, s0, cu, cu ? order : nullptr, chunk_off, arec, nsq,
-                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog, rf);
+                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog, rf, nullptr);
         return hipGetLastError();
     };
     // Units with a chunk beyond the decay range (marked in rflags by the scan, S_T left
@@ -1288,6 +1185,58 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         hipSuccess)
         return e;
     return rf ? launch_prefill_range_fixup(a, rf, G, stream) : hipSuccess;
+}
+
+// The chunked backward's forward pass (see kda_backward_chunk.hip).
+template <int DK, int DV, int GATE>
+static hipError_t bwd_forward_t(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream) {
+    constexpr int NVB = DV / BV;
+    hipError_t e;
+    const int32_t* cu = a.cu_seqlens;
+    if (cu) {
+        if ((e = launch_schedule(cu, a.n_seq, b.order, stream)) != hipSuccess) return e;
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, cu, a.n_seq, a.n_tok, b.chunk_off);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    int dev = 0, n_cu = 0;
+    if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t sgrid = std::min<int64_t>(b.max_chunks * a.n_heads, 4 * static_cast<int64_t>(n_cu));
+    const uint16_t* k = static_cast<const uint16_t*>(a.k);
+    hipLaunchKernelGGL((chunk_solve_kernel<DK, false>), dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, stream, k,
+                       a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), b.rec,
+                       nullptr, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
+    // the state enters K S^T as hi + lo (SPLIT_S): the checkpoints feed dq and dk directly,
+    // where a single bf16 copy's rounding is not damped by any decay
+    hipLaunchKernelGGL((scan_kernel<DK, DV, GATE, true, true>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                       static_cast<const uint16_t*>(a.q), k, static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu,
+                       cu ? b.order : nullptr, b.chunk_off, b.rec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr, 0,
+                       nullptr, b.flags, b.sck);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_solve_kernel<DK, true>), dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, stream, k,
+                       a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), b.rec,
+                       b.flags, NVB);
+    return hipGetLastError();
+}
+
+template <int GATE>
+static hipError_t bwd_forward_g(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream) {
+    if (a.d_k == 128 && a.d_v == 128) return bwd_forward_t<128, 128, GATE>(a, b, stream);
+    if (a.d_k == 64 && a.d_v == 64) return bwd_forward_t<64, 64, GATE>(a, b, stream);
+    if (a.d_k == 128 && a.d_v == 64) return bwd_forward_t<128, 64, GATE>(a, b, stream);
+    if (a.d_k == 64 && a.d_v == 128) return bwd_forward_t<64, 128, GATE>(a, b, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_forward_pass(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream) {
+    switch (a.gate) {
+        case GATE_CHANNEL: return bwd_forward_g<GATE_CHANNEL>(a, b, stream);
+        case GATE_SCALAR: return bwd_forward_g<GATE_SCALAR>(a, b, stream);
+        case GATE_NONE: return bwd_forward_g<GATE_NONE>(a, b, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int GATE>

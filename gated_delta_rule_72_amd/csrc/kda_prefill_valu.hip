@@ -433,7 +433,7 @@ static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hi
         hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(L * R), 0, stream, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.alpha, a.beta, a.S0, a.cu_seqlens, order, a.n_seq, a.n_tok,
-                           a.n_heads, nullptr, nullptr, ckpt, nullptr, 1);
+                           a.n_heads, nullptr, nullptr, ckpt, range_flags, 1);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((prefill_staged_kernel<T, DK, DV, GATE, R, L, false>), dim3(static_cast<unsigned>(grid)), dim3(L * R),
@@ -453,40 +453,44 @@ static hipError_t launch_staged_r(const PrefillArgs& a, const int32_t* order, hi
 constexpr int kStagedSmallLanes = 16;
 template <typename T, int DK, int DV, int GATE>
 static hipError_t launch_staged(const PrefillArgs& a, const int32_t* order, hipStream_t stream,
-                                float* ckpt = nullptr) {
+                                float* ckpt = nullptr, const int32_t* range_flags = nullptr) {
     constexpr int64_t kCus = 256;
     const int64_t units = static_cast<int64_t>(a.n_seq) * a.n_heads;
-    if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream, ckpt);
+    if (units * (DV / 64) >= kCus) return launch_staged_r<T, DK, DV, GATE, 64>(a, order, stream, ckpt, range_flags);
     if (units * (DV / 32) >= kCus)
-        return launch_staged_r<T, DK, DV, GATE, 32, kStagedSmallLanes>(a, order, stream, ckpt);
-    return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream, ckpt);
+        return launch_staged_r<T, DK, DV, GATE, 32, kStagedSmallLanes>(a, order, stream, ckpt, range_flags);
+    return launch_staged_r<T, DK, DV, GATE, 16, kStagedSmallLanes>(a, order, stream, ckpt, range_flags);
 }
 
 template <typename T, int GATE>
-static hipError_t launch_ckpt_g(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_staged<T, 128, 128, GATE>(a, order, stream, ckpt);
-    if (a.d_k == 64 && a.d_v == 64) return launch_staged<T, 64, 64, GATE>(a, order, stream, ckpt);
-    if (a.d_k == 128 && a.d_v == 64) return launch_staged<T, 128, 64, GATE>(a, order, stream, ckpt);
-    if (a.d_k == 64 && a.d_v == 128) return launch_staged<T, 64, 128, GATE>(a, order, stream, ckpt);
+static hipError_t launch_ckpt_g(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream,
+                                const int32_t* rf) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_staged<T, 128, 128, GATE>(a, order, stream, ckpt, rf);
+    if (a.d_k == 64 && a.d_v == 64) return launch_staged<T, 64, 64, GATE>(a, order, stream, ckpt, rf);
+    if (a.d_k == 128 && a.d_v == 64) return launch_staged<T, 128, 64, GATE>(a, order, stream, ckpt, rf);
+    if (a.d_k == 64 && a.d_v == 128) return launch_staged<T, 64, 128, GATE>(a, order, stream, ckpt, rf);
     return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t launch_ckpt_t(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
+static hipError_t launch_ckpt_t(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream,
+                                const int32_t* rf) {
     switch (a.gate) {
-        case GATE_CHANNEL: return launch_ckpt_g<T, GATE_CHANNEL>(a, order, ckpt, stream);
-        case GATE_SCALAR: return launch_ckpt_g<T, GATE_SCALAR>(a, order, ckpt, stream);
-        case GATE_NONE: return launch_ckpt_g<T, GATE_NONE>(a, order, ckpt, stream);
-        case GATE_KEY: return launch_ckpt_g<T, GATE_KEY>(a, order, ckpt, stream);
+        case GATE_CHANNEL: return launch_ckpt_g<T, GATE_CHANNEL>(a, order, ckpt, stream, rf);
+        case GATE_SCALAR: return launch_ckpt_g<T, GATE_SCALAR>(a, order, ckpt, stream, rf);
+        case GATE_NONE: return launch_ckpt_g<T, GATE_NONE>(a, order, ckpt, stream, rf);
+        case GATE_KEY: return launch_ckpt_g<T, GATE_KEY>(a, order, ckpt, stream, rf);
     }
     return hipErrorInvalidValue;
 }
 
 // The backward's forward pass: the staged form run for its states only (a.o and
 // a.S_T null), storing the state entering every block of 16 tokens into ckpt.
-hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream) {
+hipError_t launch_prefill_checkpoints(const PrefillArgs& a, const int32_t* order, float* ckpt, hipStream_t stream,
+                                      const int32_t* range_flags) {
     static_assert(STAGE_TOKENS == STATE_CHECKPOINT_TOKENS, "checkpoint spacing");
-    return a.bf16 ? launch_ckpt_t<uint16_t>(a, order, ckpt, stream) : launch_ckpt_t<float>(a, order, ckpt, stream);
+    return a.bf16 ? launch_ckpt_t<uint16_t>(a, order, ckpt, stream, range_flags)
+                  : launch_ckpt_t<float>(a, order, ckpt, stream, range_flags);
 }
 
 #ifndef KDA_STAGED_MIN_TOKENS

@@ -264,15 +264,23 @@ def test_binding_checks_decode_shapes(L):
 
 
 def test_backward_workspace_size(L):
-    """Backward workspace, 256-byte aligned parts: the schedule (n_seq int32), a state
-    checkpoint every 16 tokens of every (sequence, head) -- slots n_seq + n_tok // 16 + 1,
-    H x d_v x d_k fp32 each -- and each wave's 16 states of 8 rows (d_k fp32 each); one
-    wave per 8 value rows, (sequence, head) pairs padded to a multiple of 8."""
+    """Backward workspace, 256-byte aligned parts: the schedule (n_seq int32), the chunk
+    offsets (n_seq + 1 int32) and the unit marks (n_seq x H x d_v / 64 int32), then one region
+    that is the larger of the chunked path's -- a 12 KiB solved record, the entering state and
+    the leaving-state gradient (d_v x d_k fp32 each) per (chunk, head), for n_tok // 64 + n_seq
+    chunks -- and the token-recurrent path's: a state checkpoint every 16 tokens of every
+    (sequence, head) (slots n_seq + n_tok // 16 + 1, H x d_v x d_k fp32 each) and each wave's
+    16 states of 8 rows (d_k fp32 each; one wave per 8 value rows, (sequence, head) pairs padded
+    to a multiple of 8)."""
     al = lambda x: (x + 255) // 256 * 256
 
     def size(n_seq, n_tok, H, dk, dv):
+        prefix = al(n_seq * 4) + al((n_seq + 1) * 4) + al(n_seq * H * (dv // 64) * 4)
+        mc = n_tok // 64 + n_seq
+        chunked = al(mc * H * 12288) + 2 * al(mc * H * dv * dk * 4)
         waves = (n_seq * H + 7) // 8 * 8 * (dv // 8)
-        return al(n_seq * 4) + (n_seq + n_tok // 16 + 1) * H * dv * dk * 4 + waves * 16 * 8 * dk * 4
+        recurrent = al(al((n_seq + n_tok // 16 + 1) * H * dv * dk * 4) + waves * 16 * 8 * dk * 4)
+        return prefix + max(chunked, recurrent)
 
     for shape in [(1, 256, 1, 64, 64), (4, 1000, 3, 128, 64), (3, 0, 2, 64, 128), (65, 4096, 8, 128, 128)]:
         assert L.kda_prefill_backward_workspace_size(*shape) == size(*shape)

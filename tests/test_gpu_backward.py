@@ -109,3 +109,64 @@ def test_backward_checkpoint_variants(torch_cuda, n_seq, H, dtype, gate):
     print(f"backward gate={gate} {n_seq} sequences of 20-60 tokens, H={H}, d=128, {dtype}", flush=True)
     inp = I.make_prefill(9300 + n_seq + H, lens, H, 128, 128, dtype, "exp_softplus", 0.02, gate)
     run(torch_cuda, inp, gate, True, seed=n_seq + H)
+
+
+# bf16 inputs with the value-channel, scalar or no gate take the chunked backward (64-token
+# chunks on the matrix cores): ragged last chunks, a length-1 and an empty sequence, dense
+# and packed calls, and all four (d_k, d_v) shapes.
+@pytest.mark.parametrize("gate", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("lens,H,dk,dv,varlen", [
+    ([200, 64, 1, 0, 130], 2, 128, 128, True),
+    ([256], 2, 64, 128, False),
+    ([300, 77], 3, 128, 64, True),
+    ([129, 64], 2, 64, 64, True),
+])
+def test_chunked_backward_matches_oracle(torch_cuda, gate, lens, H, dk, dv, varlen):
+    print(f"chunked backward gate={gate} lens={lens} H={H} dk={dk} dv={dv} varlen={varlen}", flush=True)
+    inp = I.make_prefill(9400 + sum(lens) + H + dk + dv, lens, H, dk, dv, "bf16", "exp_softplus", 0.02, gate)
+    run(torch_cuda, inp, gate, varlen, seed=sum(lens) + 7)
+
+
+# Units the chunked form cannot take -- a chunk decaying past 2^-100 (here alpha = 0 on one
+# token), a gate below 2^-5 (where dalpha = dg / alpha would amplify rounding), a beta of 0
+# (dbeta divides by beta) -- are handed to the token-recurrent backward as whole (sequence,
+# head) pairs, in the same call as the chunked units.
+@pytest.mark.parametrize("gate", ["channel", "scalar"])
+@pytest.mark.parametrize("kind", ["zero_gate", "small_gate", "zero_beta"])
+def test_chunked_backward_hands_over_marked_units(torch_cuda, gate, kind):
+    print(f"chunked backward, marked units: gate={gate} {kind}", flush=True)
+    inp = I.make_prefill(9500 + len(kind), [150, 100], 3, 128, 128, "bf16", "exp_softplus", 0.02, gate)
+    if kind == "zero_gate":
+        inp.alpha[50, 1] = 0.0            # sequence 0, head 1
+    elif kind == "small_gate":
+        if gate == "channel":
+            inp.alpha[170, 2, 7] = 0.01   # sequence 1, head 2, one value row
+        else:
+            inp.alpha[170, 2] = 0.01
+    else:
+        inp.beta[60, 0] = 0.0             # sequence 0, head 0
+    run(torch_cuda, inp, gate, True, seed=len(kind) + 11)
+
+
+def test_chunked_backward_batched_shape_sampled(torch_cuda):
+    """The batched workload's shape on a reduced batch (2 x 8192 tokens, 4 heads, d = 128,
+    bf16, its distributions): every gradient of two sampled (sequence, head) pairs against the
+    oracle run on that pair alone (heads are independent)."""
+    from gated_delta_rule_72_amd import kda
+    from oracle.backward import prefill_backward
+    inp = I.workload_prefill(3, H=4, seq_lens=[8192, 8192])
+    print("chunked backward, 2 x 8192 tokens, H=4, d=128, bf16: sampled pairs", flush=True)
+    dO, dS_T = I.make_backward_grads(9600, inp)
+    d = Hh.upload_prefill(inp)
+    g = kda.kda_prefill_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], None,
+                                 Hh.to_device(dO, "f32"), Hh.to_device(dS_T, "f32"), n_seq=2)
+    torch_cuda.cuda.synchronize()
+    for n, h in [(0, 1), (1, 3)]:
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        sub = lambda x: x[s:e, h:h + 1]
+        ref = prefill_backward(sub(inp.f32("q")), sub(inp.f32("k")), sub(inp.f32("v")), sub(inp.alpha),
+                               sub(inp.beta), inp.S0[n:n + 1, h:h + 1].astype(np.float64), [0, e - s], sub(dO),
+                               dS_T[n:n + 1, h:h + 1], "channel")
+        for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
+            Hh.check(f"{name}[{n},{h}]", Hh.from_device(g[name])[s:e, h], ref[name][:, 0], [(Ellipsis,)], TOL)
+        Hh.check(f"dS0[{n},{h}]", Hh.from_device(g["dS0"])[n, h], ref["dS0"][0, 0], [(Ellipsis,)], TOL)
