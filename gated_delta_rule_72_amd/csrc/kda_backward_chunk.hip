@@ -357,7 +357,9 @@ struct GradSmem {
     static constexpr int BUF = C * CP * 2;           // one [64][CP] bf16 buffer
     static constexpr int UA = 4 * BUF + DV * GP * 4; // phase A: T, P hi/lo; G^T
     static constexpr int UB = 10 * BUF;              // phase B: U, dO~, dY (hi/lo, 64 rows); dP, dKK hi/lo
-    static constexpr int RU = UA > UB ? UA : UB;
+    static constexpr int UO = 2 * C * (DV + 4) * 4;  // dV, dalpha rows [t][i] after phase A
+    static constexpr int RU0 = UA > UB ? UA : UB;
+    static constexpr int RU = RU0 > UO ? RU0 : UO;
     static constexpr int RS = (C + DV + 8 * DV + 2 * 8 * C) * 4;  // beta, gamma, cumsum totals, row partials
     static constexpr int TOTAL = RKQ + RU + RS;
 };
@@ -432,6 +434,35 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             if (GATE == GATE_SCALAR) dalpha[tok0 + tid * H] = 0.f;
         }
         return;
+    }
+
+    // phase A's own global inputs are issued first, so that they arrive under the staging:
+    // rows i = 16 w + m16 of S and D (key channels 8g + 32m .. +7), and V, dO at the tile
+    // rows t = 16 tt + 4g + e (one 4-byte or 2-byte load per value, past the chunk's end 0)
+    f32x4 pS[NM][2], pD[NM][2];
+    float pV[4][4], pdO[4][4];
+    if (wave < NWA) {
+        const int i = 16 * wave + m16;
+        const int64_t srow = ((static_cast<int64_t>(gc) * H + h) * DV + i) * DK + 8 * g;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                pS[m][x] = *reinterpret_cast<const f32x4*>(sck + srow + 32 * m + 4 * x);
+                pD[m][x] = *reinterpret_cast<const f32x4*>(gck + srow + 32 * m + 4 * x);
+            }
+        const auto rv = make_rsrc(v + tok0 * DV + i, ((n - 1) * row_v + 1) * 2);
+        const auto rdo = make_rsrc(dO + tok0 * DV + i, ((n - 1) * row_v + 1) * 4);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * g + e;
+                pV[tt][e] = bf16_bits_to_f32(
+                    static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, static_cast<int>(t * row_v) * 2, 0, 0)));
+                pdO[tt][e] =
+                    __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdo, static_cast<int>(t * row_v) * 4, 0, 0));
+            }
     }
 
     // ======== staging: K, Q, T, beta; the upper-right 32x32 block of T is zero
@@ -517,11 +548,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
     block_sync();
 
     // ======== phase A
-    // packs of U, dO~ and dY ([t] four per tile, hi and lo) for phase B
+    // packs of U, dO~ and dY ([t] four per tile, hi and lo) for phase B; dV and a value-channel
+    // dalpha at the tile rows, written out through LDS after the phase
     uint2 pU[4][2], pO[4][2], pY[4][2];
+    f32x4 rdV[4], rdA[4];
     if (wave < NWA) {
         const int i = 16 * wave + m16;
-        const int64_t srow = ((static_cast<int64_t>(gc) * H + h) * DV + i) * DK + 8 * g;
         // S (state entering the chunk) and D (gradient of the state leaving it), row i,
         // key channels 8g + 32m .. +7: the B operands of K S^T, Q S^T and K dZ^T
         bf16x8 sh[NM], sl[NM], zh[NM], zl[NM];
@@ -529,10 +561,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         float part = 0.f;  // sum_j dZ[i,j] S[i,j], then + sum_t U[t,i] (K dZ^T)[t,i]
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(sck + srow + 32 * m);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(sck + srow + 32 * m + 4);
-            f32x4 z0 = *reinterpret_cast<const f32x4*>(gck + srow + 32 * m);
-            f32x4 z1 = *reinterpret_cast<const f32x4*>(gck + srow + 32 * m + 4);
+            const f32x4 s0 = pS[m][0], s1 = pS[m][1];
+            f32x4 z0 = pD[m][0], z1 = pD[m][1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 z0[e] *= gm;
@@ -559,7 +589,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             }
         }
         // X = V e^{-G}, Y = X - K S^T, Yb = beta Y (tile rows t = 16 tt + 4g + r)
-        const auto rv = make_rsrc(v + tok0 * DV + i, ((n - 1) * row_v + 1) * 2);
         f32x4 X[4], Yb[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
@@ -567,10 +596,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * tt + 4 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * g + e;
-                const float vv =
-                    bf16_bits_to_f32(static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, static_cast<int>(t * row_v) * 2, 0, 0)));
-                X[tt][e] = vv * __builtin_amdgcn_exp2f(-G4[e]);
+                X[tt][e] = pV[tt][e] * __builtin_amdgcn_exp2f(-G4[e]);
                 Yb[tt][e] = b4[e] * (X[tt][e] - KS[tt][e]);
             }
         }
@@ -608,17 +634,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);  // the column's sum over all four groups
         // dO~ = dO e^{G}; dU = K dZ^T + P^T dO~
-        const auto rdo = make_rsrc(dO + tok0 * DV + i, ((n - 1) * row_v + 1) * 4);
         f32x4 dOt[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const f32x4 G4 = *reinterpret_cast<const f32x4*>(GT + i * GP + 16 * tt + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * g + e;
-                dOt[tt][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdo, static_cast<int>(t * row_v) * 4, 0, 0)) *
-                             __builtin_amdgcn_exp2f(G4[e]);
-            }
+            for (int e = 0; e < 4; ++e) dOt[tt][e] = pdO[tt][e] * __builtin_amdgcn_exp2f(G4[e]);
             split4(dOt[tt], pO[tt][0], pO[tt][1]);
         }
         split_stack(dOt[0], dOt[1], ah[0], al[0]);
@@ -658,7 +679,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         }
         // dV = dY e^{-G}; dG = dO~ O~ - dY X (+ the gradient through gamma on the last token);
         // dg = reverse cumulative sum of dG over the chunk; dalpha = dg / alpha
-        const auto rdv = make_rsrc(dv + tok0 * DV + i, ((n - 1) * row_v + 1) * 4);
         float dG[4][4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
@@ -666,8 +686,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tt + 4 * g + e;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dY[tt][e] * __builtin_amdgcn_exp2f(-G4[e])),
-                                                      rdv, static_cast<int>(t * row_v) * 4, 0, 0);
+                rdV[tt][e] = dY[tt][e] * __builtin_amdgcn_exp2f(-G4[e]);
                 dG[tt][e] = dOt[tt][e] * Ot[tt][e] - dY[tt][e] * X[tt][e] + (t == n - 1 ? part : 0.f);
             }
         }
@@ -692,7 +711,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
                     const int t = 16 * tt + 4 * g + e;
                     const float dg = loc[tt][e] + excl[tt] + carry;
                     if constexpr (GATE == GATE_CHANNEL) {
-                        if (t < n) dalpha[(tok0 + t * H) * DV + i] = dg / alpha[(tok0 + t * H) * DV + i];
+                        // alpha_t = 2^{G_t - G_{t-1}} from the staged log2-decays (rounding ~1e-7 |G|)
+                        const float gp = t > 0 ? GT[i * GP + t - 1] : 0.f;
+                        rdA[tt][e] = dg * __builtin_amdgcn_exp2f(gp - GT[i * GP + t]);
                     } else {
                         const float ps = sum16(dg);
                         if (m16 == 0) red2[wave * C + t] = ps;
@@ -703,6 +724,35 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         }
     }
     block_sync();  // phase A done: T, P and G^T are dead
+    {
+        // dV (and a value-channel dalpha) through LDS as whole token rows [t][i], stored as
+        // 16-byte pieces of each row: the tile layout has 4 tokens of one row per lane
+        constexpr int VP = DV + 4;
+        float* sv = reinterpret_cast<float*>(ur);
+        float* sa = sv + C * VP;
+        if (wave < NWA) {
+            const int i = 16 * wave + m16;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tt + 4 * g + e;
+                    sv[t * VP + i] = rdV[tt][e];
+                    if constexpr (GATE == GATE_CHANNEL) sa[t * VP + i] = rdA[tt][e];
+                }
+        }
+        block_sync();
+        const auto rdv = make_rsrc(dv + tok0 * DV, ((n - 1) * row_v + DV) * 4);
+        const auto rda = make_rsrc(dalpha + tok0 * DV, GATE == GATE_CHANNEL ? ((n - 1) * row_v + DV) * 4 : 0);
+        for (int x = tid; x < C * DV / 4; x += 512) {
+            const int t = x / (DV / 4), c4 = 4 * (x % (DV / 4));
+            const int off = static_cast<int>(t * row_v + c4) * 4;
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sv + t * VP + c4), rdv, off, 0, 0);
+            if constexpr (GATE == GATE_CHANNEL)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sa + t * VP + c4), rda, off, 0, 0);
+        }
+        block_sync();  // the staging rows are read before phase B reuses the space
+    }
     if (tid < n) {
         float sb = 0.f, sa = 0.f;
         for (int w = 0; w < NWA; ++w) {
