@@ -22,10 +22,13 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-c
                        [--no-scalar-gate] [--no-backward] [--no-workloads]
        python bench.py --workloads-only     (only the tiny fp32, single-layer and varlen prefill
                                              workloads, one JSON line)
-       python bench.py --traffic-probe      (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
-                                             a 1 GiB device copy for calibration, 3 prefill
-                                             launches, 3 scalar-gate prefill launches,
-                                             8 decode steps)
+       python bench.py --traffic-probe [main|extra|varlen]
+                                            (short run for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE:
+                                             a 1 GiB device copy for calibration, then: main = 3
+                                             prefill launches, 3 scalar-gate prefill launches,
+                                             8 decode steps; extra = 2 backward calls and 2
+                                             key-channel-gate prefill calls on the batched
+                                             workload; varlen = 2 varlen-workload prefill calls)
        python bench.py --summarize DIR      (print the per-kernel table of a rocprofv3 run)
 """
 from __future__ import annotations
@@ -50,6 +53,9 @@ PREFILL_BYTES_PER_HEAD_TOKEN = 768 + 512 + 4 + 256   # q,k,v bf16 + alpha fp32 +
 # with one gate per (token, head) (scalar gate): alpha is 4 bytes per head-token
 PREFILL_BYTES_PER_HEAD_TOKEN_SCALAR_GATE = 768 + 4 + 4 + 256
 PREFILL_FLOPS_PER_HEAD_TOKEN = 180224                # nominal chunked flops at C=64, d=128
+# backward, per head-token: q, k, v bf16, alpha, dO fp32 and beta in (768 + 512 + 512 + 4); dq, dk,
+# dv, dalpha fp32 and dbeta out (4 x 512 + 4)
+BACKWARD_BYTES_PER_HEAD_TOKEN = 768 + 512 + 512 + 4 + 4 * 512 + 4
 
 
 def log(*a):
@@ -88,12 +94,12 @@ def parse():
     p.add_argument("--no-workloads", action="store_true")
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--workloads-only", action="store_true")
-    p.add_argument("--traffic-probe", action="store_true")
+    p.add_argument("--traffic-probe", nargs="?", const="main", default=None, choices=("main", "extra", "varlen"))
     p.add_argument("--summarize", default=None)
     return p.parse_args()
 
 
-def traffic_probe():
+def traffic_probe(mode="main"):
     """Fixed, short GPU work for hardware-counter runs."""
     import torch
     from gated_delta_rule_72_amd import inputs as I
@@ -105,6 +111,32 @@ def traffic_probe():
     dst.copy_(src)  # calibration: reads 1 GiB, writes 1 GiB
     torch.cuda.synchronize()
     del src, dst
+    if mode == "extra":
+        inp = I.workload_prefill(3)
+        dO, dS_T = I.make_backward_grads(9300, inp)
+        q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+        alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
+        dO_d, dST_d = upload(dO, "f32", dev), upload(dS_T, "f32", dev)
+        for _ in range(2):
+            kda.kda_prefill_backward(q, k, v, alpha, beta, S0, None, dO_d, dST_d, n_seq=inp.n_seq)
+        torch.cuda.synchronize()
+        del alpha, dO_d, dST_d
+        alk = upload(I.workload_prefill(3, gate="key").alpha, "f32", dev)
+        for _ in range(2):
+            kda.kda_prefill_key_gate(q, k, v, alk, beta, S0, None, n_seq=inp.n_seq)
+        torch.cuda.synchronize()
+        print("traffic probe (extra) done", flush=True)
+        return
+    if mode == "varlen":
+        inp = I.workload_prefill(5)
+        q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
+        alpha, beta = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev)
+        cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+        for _ in range(2):
+            kda.kda_prefill(q, k, v, alpha, beta, None, cu)
+        torch.cuda.synchronize()
+        print("traffic probe (varlen) done", flush=True)
+        return
     inp = I.workload_prefill(3)
     q, k, v = (upload(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v"))
     alpha, beta, S0 = upload(inp.alpha, "f32", dev), upload(inp.beta, "f32", dev), upload(inp.S0, "f32", dev)
@@ -155,6 +187,45 @@ def summarize(path):
             print(f"{'kernel':70s} {'counter':>14s} {'dispatches':>10s} {'per_dispatch':>16s}")
             for name, cn, n, val in crow:
                 print(f"{name[:70]:70s} {cn:>14s} {n:10d} {val:16.1f}")
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (platform's name if absent)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def set_oracle_threads(n):
+    """Threads of the oracle's OpenMP runtime (libgomp, shared by the process)."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def hbm_copy_probe(torch, gib=1, reps=10):
+    """Attainable HBM bandwidth: torch's device copy of `gib` GiB (reads and writes it), timed
+    with HIP events; bytes moved = 2 x the buffer."""
+    n = (gib << 30) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(GBps=round(2 * (gib << 30) / (ms * 1e-3) / 1e9, 1), bytes_per_copy=2 * (gib << 30),
+                ms_per_copy=round(ms, 4), what="torch device copy of 1 GiB (read + write), HIP events")
 
 
 def upload(x, dtype, dev):
@@ -280,7 +351,7 @@ def cpu_baseline_prefill(inp, o_gpu, S_gpu):
     cpu = dict(value=round(tokens / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
                sample=f"one whole step of the batched prefill workload ({inp.n_seq} sequences x "
                       f"{tokens // inp.n_seq} tokens x {inp.H} heads), fp64 C oracle, {dt:.2f}s wall",
-               cpu_model=platform.processor() or platform.machine())
+               cpu_model=cpu_model())
     parity = dict(o_max_rel=worst[0], o_rms_rel=worst[1], S_max_rel=worst[2], S_rms_rel=worst[3],
                   scope=f"all {inp.n_seq} sequences x {inp.H} heads, worst (sequence, head) slice")
     return cpu, parity
@@ -425,6 +496,7 @@ def bench_key_gate(args, torch, kda, I):
                 ms_per_call=round(ms, 4), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
                 roofline=dict(bound="alu", achieved=round(tflops, 2), peak=FP32_VECTOR_PEAK_TFLOPS, unit="TFLOP/s",
                               frac=round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), flop_per_head_token=flops // (inp.n_tok * H),
+                              traffic=measured_traffic("key_gate"),
                               note="peak counts packed fp32, which the build does not emit; unpacked FMA peak is half"),
                 hbm_frac=round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 parity=dict(o_max_rel=m, o_rms_rel=r, S_max_rel=ms_, S_rms_rel=rs, scope="(sequence 1, head 7)"))
@@ -492,12 +564,21 @@ def bench_backward(args, torch, kda, I):
     for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
         worst = max(worst, rel(gk[name][s_:e_, h].cpu().numpy().astype(np.float64), refk[name][:, 0])[0])
     worst = max(worst, rel(gk["dS0"][n_, h].cpu().numpy().astype(np.float64), refk["dS0"][0, 0])[0])
+    alg = inp.n_tok * H * BACKWARD_BYTES_PER_HEAD_TOKEN + 3 * B * H * inp.dv * inp.dk * 4
+    gbs = alg / (ms * 1e-3) / 1e9
     return dict(workload="batched prefill workload (value-channel gate), kda_prefill_backward with dO and dS_T "
-                         "drawn N(0,1): token-recurrent backward kernel",
+                         "drawn N(0,1): chunked backward on bf16 MFMA (forward pass with state checkpoints, "
+                         "reverse state-gradient scan, per-(chunk, head) gradients)",
                 ms_per_call=round(ms, 3), tokens_per_s=round(inp.n_tok / (ms * 1e-3), 1),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("backward"),
+                              alg_bytes_per_launch=alg,
+                              note="algorithmic bytes: q, k, v bf16, alpha, dO fp32, beta in; dq, dk, dv, dalpha "
+                                   "fp32, dbeta out (3,848 B per head-token), S0, dS_T in and dS0 out"),
                 workspace_bytes=ws.numel(), parity=parity,
                 key_gate=dict(ms_per_call=round(ms_key, 3), tokens_per_s=round(inp.n_tok / (ms_key * 1e-3), 1),
-                              worst_max_rel=worst, scope=parity["scope"] + ", every gradient"))
+                              kernel="token-recurrent backward", worst_max_rel=worst,
+                              scope=parity["scope"] + ", every gradient"))
 
 
 def bench_multi_token_decode(args, torch, kda, I, T=4):
@@ -548,6 +629,23 @@ def bench_multi_token_decode(args, torch, kda, I, T=4):
                             scope="3 sampled (b, h) pairs, all tokens"))
 
 
+def oracle_timing(inp):
+    """The oracle on the whole workload, on all host threads and on one thread."""
+    import oracle
+    S0 = None if inp.S0 is None else inp.S0.astype(np.float64)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    res = {}
+    for label, n in (("all_threads", threads), ("single_thread", 1)):
+        set_oracle_threads(n)
+        t0 = time.perf_counter()
+        oracle.prefill(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.alpha, inp.beta, S0, inp.cu_seqlens)
+        dt = time.perf_counter() - t0
+        res[label] = dict(threads=n, seconds=round(dt, 3), tokens_per_s=round(inp.n_tok / dt, 1))
+    set_oracle_threads(threads)
+    res["cpu_model"] = cpu_model()
+    return res
+
+
 def bench_other_workloads(args, torch, kda, I):
     """Times kda_prefill on the tiny fp32, single-layer and varlen prefill workloads (the
     other prefill shapes) and on one long ragged sequence.  Each: inputs resident in HBM,
@@ -587,6 +685,21 @@ def bench_other_workloads(args, torch, kda, I):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
+        flushed = None
+        if name in ("tiny_f32", "single_layer_prefill"):
+            # each call after a 1 GiB scratch write, so neither L2 nor the 256 MB MALL holds its inputs
+            scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            times = []
+            for rep in range(args.steps):
+                scratch.fill_(float(rep))
+                e0.record()
+                step()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            del scratch
+            flushed = dict(ms_mean=round(float(np.mean(times)), 4), ms_median=round(float(np.median(times)), 4),
+                           what="each call timed alone after a 1 GiB scratch write")
         eb = 2 if dt == "bf16" else 4
         per_ht = (2 * dk + 2 * dv) * eb + dv * 4 + 4     # q, k, v, o + alpha + beta
         head_tokens = n_tok * H
@@ -599,6 +712,14 @@ def bench_other_workloads(args, torch, kda, I):
             alg_bytes=int(alg), achieved_GBps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
             parity=workload_parity(inp, o, S_T, [(0, 0), (n_seq // 2, H // 2), (n_seq - 1, H - 1)]
                                    if varlen else [(0, 0)] if name == "long_sequence" else None))
+        if flushed:
+            out[name]["flushed"] = flushed
+        if varlen:
+            out[name]["roofline"] = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                         frac=round(gbs / HBM_PEAK_GBS, 4),
+                                         traffic=measured_traffic("varlen_prefill"), alg_bytes_per_launch=int(alg))
+        if name in ("tiny_f32", "single_layer_prefill") and not args.no_cpu:
+            out[name]["cpu_oracle"] = oracle_timing(inp)
         log(f"[bench] {name}: {ms:.4f} ms per call, {n_tok / (ms * 1e-3):.4g} tokens/s, "
             f"{gbs / HBM_PEAK_GBS:.3f} of HBM")
         del q, k, v, alpha, beta, S0, cu, o, S_T, ws, inp
@@ -612,7 +733,7 @@ def main():
         summarize(args.summarize)
         return
     if args.traffic_probe:
-        traffic_probe()
+        traffic_probe(args.traffic_probe)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
@@ -626,6 +747,8 @@ def main():
     if args.workloads_only:
         print(json.dumps(dict(workloads=bench_other_workloads(args, torch, kda, I))), flush=True)
         return
+    copy_probe = hbm_copy_probe(torch)
+    log(f"[bench] HBM copy probe: {copy_probe['GBps']:.1f} GB/s")
     pre, inp, o, S_T = bench_prefill(args, torch, kda, I)
     log(f"[bench] prefill: {pre['tokens_per_s']:.4g} tokens/s, kernel {pre['launch_ms']['avg']:.3f} ms")
     line = dict(
@@ -635,7 +758,7 @@ def main():
         config=dict(workload="batched_prefill: B=4 sequences x T=8192 tokens, H=32, d_k=d_v=128, "
                              "bf16 q/k/v, fp32 alpha/beta/state, S0~N(0,0.02^2)",
                     global_batch=4, seq_len=8192, heads=32, d_k=128, d_v=128, chunk=64),
-        roofline=pre["roofline"], launch_ms=pre["launch_ms"],
+        roofline=pre["roofline"], launch_ms=pre["launch_ms"], hbm_copy_probe=copy_probe,
     )
     if not args.no_cpu:
         cpu, parity = cpu_baseline_prefill(inp, o, S_T)
