@@ -26,9 +26,11 @@ size_t elem_bytes(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
 
 bool valid_dtype(kda_dtype dt) { return dt == KDA_DTYPE_F32 || dt == KDA_DTYPE_BF16; }
 
-size_t workspace_need(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt) {
-    return dt == KDA_DTYPE_BF16 ? kda::prefill_bf16_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v)
-                                : kda::prefill_workspace_bytes(n_seq, true);
+size_t workspace_need(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v, kda_dtype dt,
+                      kda::Gate gate = kda::GATE_CHANNEL) {
+    if (dt != KDA_DTYPE_BF16) return kda::prefill_workspace_bytes(n_seq, true);
+    return gate == kda::GATE_KEY ? kda::prefill_keygate_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v)
+                                 : kda::prefill_bf16_workspace_bytes(n_seq, n_tok, n_heads, d_k, d_v);
 }
 
 // Shared body of kda_prefill and kda_prefill_scalar_gate.
@@ -73,7 +75,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const float
     if (S_T && S0 && S_T != S0 && ranges_overlap(S_T, s_bytes, S0, s_bytes))
         return KDA_ERR_INVALID_ARGUMENT;
     if (S0 && ranges_overlap(o, v_bytes, S0, s_bytes)) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = workspace_need(n_seq, n_tok, n_heads, d_k, d_v, dt);
+    const size_t need = workspace_need(n_seq, n_tok, n_heads, d_k, d_v, dt, gate);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     // the workspace is written by the call: it may overlap no other argument
     const Region all[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {alpha, a_bytes}, {beta, b_bytes},
@@ -199,6 +201,14 @@ size_t kda_prefill_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
         !valid_dtype(dt))
         return 0;
     return workspace_need(n_seq, n_tok, n_heads, d_k, d_v, dt);
+}
+
+size_t kda_prefill_key_gate_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k,
+                                           int32_t d_v, kda_dtype dt) {
+    if (n_seq < 1 || n_tok < 0 || n_heads < 1 || !supported_dim(d_k) || !supported_dim(d_v) ||
+        !valid_dtype(dt))
+        return 0;
+    return workspace_need(n_seq, n_tok, n_heads, d_k, d_v, dt, kda::GATE_KEY);
 }
 
 kda_status kda_prefill(const void* q, const void* k, const void* v, const float* alpha,

@@ -91,12 +91,22 @@ hipError_t launch_prefill_range_fixup(const PrefillArgs& a, const int32_t* range
 // sequence, no cu_seqlens) run token by token: multi-token decode.
 constexpr int RECURRENT_MAX_TOKENS = 16;
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// The chunked bf16 prefill with the gate on key channels (kda_prefill_keygate.hip).
+hipError_t launch_prefill_keygate(const PrefillArgs& a, hipStream_t stream);
+// chunk_off[m] = number of 64-token chunks of sequences 0 .. m-1 (m = 0 .. n_seq), from
+// cu_seqlens on the device (kda_prefill_mfma.hip).
+hipError_t launch_chunk_offsets(const int32_t* cu_seqlens, int n_seq, int n_tok, int32_t* chunk_off,
+                                hipStream_t stream);
 
 // Workspace bytes of the fp32 prefill (the varlen schedule) and of the bf16
 // prefill (schedule, chunk offsets, the per-(chunk, head) solved A blocks, and
 // for the sequence-parallel path the segment states).
 size_t prefill_workspace_bytes(int32_t n_seq, bool varlen);
 size_t prefill_bf16_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
+// The same for the bf16 prefill with the gate on key channels: schedule, chunk
+// offsets, unit flags, chunk marks, and two solved records (A and the decayed
+// Q K^T) per (chunk, head).
+size_t prefill_keygate_workspace_bytes(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v);
 
 // Backward of the token-recurrent prefill (kda_backward.hip): the gradients of
 // q, k, v, alpha, beta and S0 given those of o and S_T, for every gate.

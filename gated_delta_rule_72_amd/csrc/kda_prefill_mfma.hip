@@ -42,6 +42,7 @@
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_schedule.h"
+#include "kda_solve.h"
 
 namespace kda {
 
@@ -74,6 +75,12 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* __re
         __syncthreads();
     }
     if (tid == 0) chunk_off[n_seq] = carry;
+}
+
+hipError_t launch_chunk_offsets(const int32_t* cu_seqlens, int n_seq, int n_tok, int32_t* chunk_off,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, n_tok, chunk_off);
+    return hipGetLastError();
 }
 
 // ============================================================================
@@ -113,7 +120,6 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
     uint16_t* __restrict__ arec, int32_t* __restrict__ range_flags = nullptr, int n_vblk = 0) {
     constexpr int KP = DK + PAD;
-    constexpr int RP = 36;  // pitch of the 32x32 fp32 temporary
     constexpr int KX = (C * KP * 2 > C * LP * 4) ? C * KP * 2 : C * LP * 4;
     // K is dead once L is formed, so X reuses its space; the 32x32 temporary of
     // the last level reuses rows 0-16 of L, which only the 16-row level reads.
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     __shared__ __align__(16) unsigned char kx_[KX];  // K [t][j], then X = (I + L)^{-1} [t][s]
     __shared__ __align__(16) float Lf[C * LP];       // L [t][s]
     __shared__ __align__(16) float bs[C];
-    static_assert(32 * RP <= 17 * LP, "temporary fits in rows 0-16 of L");
+    static_assert(32 * SOLVE_RP <= 17 * LP, "temporary fits in rows 0-16 of L");
     uint16_t* Kc = reinterpret_cast<uint16_t*>(kx_);
     float* Xs = reinterpret_cast<float*>(kx_);
     float* Rtmp = Lf;
@@ -205,44 +211,7 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
             }
         }
         wave_lds_sync();
-        const int b = g16, c = m16;
-        const float* Lb = Lf + (16 * b) * LP + 16 * b;
-        // Each strictly lower row is loaded one row ahead of its use, so no LDS
-        // round trip sits inside the dependent substitution chain.  Piece p
-        // enumerates (row r = 1..15, columns s4..s4+3 < r + 3).
-        f32x4 lrow[36];
-        auto first_piece = [](int r) {
-            int p = 0;
-            for (int rr = 1; rr < r; ++rr) p += (rr + 3) / 4;
-            return p;
-        };
-        auto load_row = [&](int r) {
-#pragma unroll
-            for (int s4 = 0, p = first_piece(r); s4 < r; s4 += 4, ++p)
-                lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
-        };
-        auto solve_row = [&](int r) {
-            float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
-#pragma unroll
-            for (int s4 = 0, p = first_piece(r); s4 < r; s4 += 4, ++p) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (s4 + e < r) {
-                        if (e & 1) acc1 -= lrow[p][e] * x[s4 + e];
-                        else acc0 -= lrow[p][e] * x[s4 + e];
-                    }
-                }
-            }
-            x[r] = acc0 + acc1;  // zero for r < c
-        };
-        x[0] = c == 0 ? 1.f : 0.f;
-        load_row(1);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            if (r + 1 < 16) load_row(r + 1);
-            issue_fence();
-            solve_row(r);
-        }
+        solve_diag_blocks(Lf, lane, x);
     } else if (wave == 1) {
         f32x16 acc = {};
 #pragma unroll
@@ -278,105 +247,11 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
     }
-    block_sync();
-    if (wave == 0) {
-        const int b = g16, c = m16;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Xs[(16 * b + r) * LP + 16 * b + c] = x[r];
-    }
-    block_sync();
+    assemble_inverse(Xs, Lf, Rtmp, x, wave, lane);
 
-    // ---- 16-row level (waves 0, 1): X[R, Cc] = -T_R L[R, Cc] T_Cc for the 16x16
-    // blocks (16, 0) and (48, 32)
-    if (wave < 2) {
-        const int R = 16 * (2 * wave + 1), Cc = 16 * (2 * wave);
-        float la[4], xa[4], ta[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            la[kk] = Lf[(R + m16) * LP + Cc + 4 * kk + g16];
-            xa[kk] = Xs[(Cc + 4 * kk + g16) * LP + Cc + m16];
-            ta[kk] = Xs[(R + m16) * LP + R + 4 * g16 + kk];
-        }
-        issue_fence();
-        f32x4 y = {};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) y = mfma16f(la[kk], xa[kk], y);
-        // y (row 4*g16 + r, column m16) feeds the next product directly as its B
-        // operand: step r uses reduction index 4*g16 + r, matched on the A side
-        f32x4 z = {};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z = mfma16f(ta[r], y[r], z);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
-    }
-    block_sync();
-
-    // ---- 32-row level, first half: Y2 = L[32:64, 0:32] X[0:32, 0:32], one 16x16
-    // quadrant per wave
-    const int qr = wave >> 1, qc = wave & 1;
-    {
-        float la[8], xa[8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            la[kk] = Lf[(32 + 16 * qr + m16) * LP + 4 * kk + g16];
-            xa[kk] = Xs[(4 * kk + g16) * LP + 16 * qc + m16];
-        }
-        issue_fence();
-        f32x4 y = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            if (kk >= 4 * qc) y = mfma16f(la[kk], xa[kk], y);  // X[0:32, 0:32] is block-lower
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Rtmp[(16 * qr + 4 * g16 + r) * RP + 16 * qc + m16] = y[r];
-    }
-    block_sync();
-
-    // ---- second half: X[32:64, 0:32] = -X[32:64, 32:64] Y2
-    {
-        float xa[8], ra[8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            xa[kk] = Xs[(32 + 16 * qr + m16) * LP + 32 + 4 * kk + g16];
-            ra[kk] = Rtmp[(4 * kk + g16) * RP + 16 * qc + m16];
-        }
-        issue_fence();
-        f32x4 z = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            if (kk < 4 * (qr + 1)) z = mfma16f(xa[kk], ra[kk], z);  // X[32:64, 32:64] is block-lower
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xs[(32 + 16 * qr + 4 * g16 + r) * LP + 16 * qc + m16] = -z[r];
-    }
-    block_sync();
-
-    // ---- A = X diag(beta) -> the record.  Item = (block, row, 8-column piece);
-    // entries above the diagonal (never written in Xs) are selected away.
-    uint16_t* rec = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
-    for (int item = tid; item < 3 * 32 * 4; item += 256) {
-        const int blk = item >> 7, row = (item >> 2) & 31, c8 = 8 * (item & 3);
-        const int t = (blk == 0 ? 0 : 32) + row, s0 = (blk == 2 ? 32 : 0) + c8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + s0);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + s0 + 4);
-        float av[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xv = e < 4 ? x0[e] : x1[e - 4];
-            av[e] = s0 + e <= t ? (STORE_T ? xv : xv * (e < 4 ? b0[e] : b1[e - 4])) : 0.f;
-        }
-        u32x4 wh, wl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t a, b;
-            split_bf16x2(av[2 * e], av[2 * e + 1], a, b);
-            wh[e] = a;
-            wl[e] = b;
-        }
-        uint16_t* dst = rec + blk * 2 * A_BLOCK_ELEMS + row * 32 + c8;
-        *reinterpret_cast<u32x4*>(dst) = wh;
-        *reinterpret_cast<u32x4*>(dst + A_BLOCK_ELEMS) = wl;
-    }
+    // ---- A = X diag(beta) (STORE_T: X itself) -> the record
+    write_solve_record<!STORE_T>(arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2), Xs, bs,
+                                 tid);
     block_sync();  // X, read above, shares its space with the next item's K
     }
 }
@@ -1254,13 +1129,13 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     // calls keep the chunked path
     if (!a.cu_seqlens && a.n_tok > 0 && a.n_tok <= static_cast<int64_t>(RECURRENT_MAX_TOKENS) * a.n_seq)
         return launch_prefill_recurrent(a, stream);
-    // the key-channel gate takes the token-recurrent kernel (its decay falls inside
-    // K K^T, outside the chunk algebra above)
+    // the key-channel gate has its own chunk algebra (its decay falls inside K K^T):
+    // kda_prefill_keygate.hip
     switch (a.gate) {
         case GATE_CHANNEL: return launch_bf16_g<GATE_CHANNEL>(a, stream);
         case GATE_SCALAR: return launch_bf16_g<GATE_SCALAR>(a, stream);
         case GATE_NONE: return launch_bf16_g<GATE_NONE>(a, stream);
-        case GATE_KEY: return launch_prefill_recurrent(a, stream);
+        case GATE_KEY: return launch_prefill_keygate(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -565,6 +565,8 @@ static hipError_t launch_fixup_t(const PrefillArgs& a, const int32_t* range_flag
             return launch_staged_r<uint16_t, DK, DV, GATE_CHANNEL, 64>(a, nullptr, stream, nullptr, range_flags, G);
         case GATE_SCALAR:
             return launch_staged_r<uint16_t, DK, DV, GATE_SCALAR, 64>(a, nullptr, stream, nullptr, range_flags, G);
+        case GATE_KEY:
+            return launch_staged_r<uint16_t, DK, DV, GATE_KEY, 64>(a, nullptr, stream, nullptr, range_flags, G);
         default: return hipErrorInvalidValue;  // no gate: nothing decays, nothing is marked
     }
 }

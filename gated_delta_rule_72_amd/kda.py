@@ -26,7 +26,7 @@ EXPORTED = ("kda_abi_version", "kda_status_string", "kda_prefill_workspace_size"
             "kda_decode_step", "kda_prefill_scalar_gate", "kda_decode_step_scalar_gate",
             "kda_prefill_key_gate", "kda_decode_step_key_gate", "kda_prefill_backward_workspace_size",
             "kda_prefill_backward", "kda_prefill_backward_scalar_gate", "kda_prefill_backward_key_gate",
-            "kda_prefill_noalloc")
+            "kda_prefill_noalloc", "kda_prefill_key_gate_workspace_size")
 NOALLOC_MAX_WORKSPACE = 256 << 20  # KDA_PREFILL_NOALLOC_MAX_WORKSPACE
 
 _lib = None
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.kda_status_string.argtypes = [ctypes.c_int]
     L.kda_prefill_workspace_size.restype = sz
     L.kda_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    L.kda_prefill_key_gate_workspace_size.restype = sz
+    L.kda_prefill_key_gate_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     for name in ("kda_prefill", "kda_prefill_scalar_gate", "kda_prefill_key_gate"):
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
@@ -86,6 +88,10 @@ def status_string(status: int) -> str:
 
 def workspace_size(n_seq: int, n_tok: int, n_heads: int, d_k: int, d_v: int, dtype_code: int) -> int:
     return int(lib().kda_prefill_workspace_size(n_seq, n_tok, n_heads, d_k, d_v, dtype_code))
+
+
+def key_gate_workspace_size(n_seq: int, n_tok: int, n_heads: int, d_k: int, d_v: int, dtype_code: int) -> int:
+    return int(lib().kda_prefill_key_gate_workspace_size(n_seq, n_tok, n_heads, d_k, d_v, dtype_code))
 
 
 def _torch():
@@ -214,7 +220,8 @@ def _prefill(fn, q, k, v, alpha, beta, S0, cu_seqlens, n_seq, o, S_T, want_state
         S_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
     if S_T is not None:
         _expect("S_T", S_T, (n_seq, H, dv, dk), torch.float32)
-    ws_bytes = workspace_size(n_seq, n_tok, H, dk, dv, dt)
+    size_fn = key_gate_workspace_size if fn == "kda_prefill_key_gate" else workspace_size
+    ws_bytes = size_fn(n_seq, n_tok, H, dk, dv, dt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),

@@ -216,10 +216,20 @@ kda_status kda_decode_step_scalar_gate(const void* q, const void* k, const void*
  *
  *   alpha   [n_tok, n_heads, d_k] float32 (prefill) or [batch, n_heads, d_k]
  *           (decode), 16-byte aligned.
- * Every other argument, the workspace, the layouts, the conventions and the
- * errors are those of kda_prefill and kda_decode_step.  The prefill runs token
- * by token (no chunk solve), for both input types, and is exact for alpha = 0.
+ *   workspace  at least kda_prefill_key_gate_workspace_size(...) bytes.
+ * Every other argument, the layouts, the conventions and the errors are those
+ * of kda_prefill and kda_decode_step.  float32 input runs token by token.
+ * bf16 input runs chunkwise: within a 64-token chunk the decay acts on the
+ * contraction index of K K^T, so each chunk solves its own decayed system
+ * (I + strictly_lower(diag(beta) M))^{-1} diag(beta), M[t,r] = sum_j k_t[j] k_r[j]
+ * alpha_{r+1..t}[j], with 16-token sub-chunks bounding every exponent; a chunk
+ * in which some key channel decays by more than 2^-64 within 8 consecutive
+ * tokens (alpha = 0 included) sends its (sequence, head) to a token-by-token
+ * recomputation from S0, so the result is exact for any alpha in [0, 1].
  */
+size_t kda_prefill_key_gate_workspace_size(int32_t n_seq, int32_t n_tok, int32_t n_heads,
+                                           int32_t d_k, int32_t d_v, kda_dtype dt);
+
 kda_status kda_prefill_key_gate(const void* q, const void* k, const void* v,
                                 const float* alpha, const float* beta,
                                 const float* S0, const int32_t* cu_seqlens,

@@ -56,6 +56,28 @@ def test_workspace_size(L):
     assert L.kda_prefill_workspace_size(4, 1000, 16, 96, 128, 1) == 0
 
 
+def test_key_gate_workspace_size(L):
+    """The key-channel-gate prefill: fp32 as kda_prefill; bf16: schedule, chunk offsets,
+    one flag per (sequence, head, 64 value rows), one mark per (chunk, head), then two
+    12 KiB solved records per (chunk, head) -- A and the decayed Q K^T -- for at most
+    n_tok // 64 + n_seq chunks; every part 256-byte aligned, never split into segments."""
+    al = lambda x: (x + 255) // 256 * 256
+    rec = 3 * 2 * 32 * 32 * 2
+
+    def size(n_seq, n_tok, H, dv):
+        mc = n_tok // 64 + n_seq
+        return (al(n_seq * 4) + al((n_seq + 1) * 4) + al(n_seq * H * (dv // 64) * 4) + al(mc * H * 4)
+                + 2 * al(mc * H * rec))
+
+    assert L.kda_prefill_key_gate_workspace_size(64, 1000, 16, 128, 128, 0) == 256
+    assert L.kda_prefill_key_gate_workspace_size(64, 1000, 16, 128, 128, 1) == size(64, 1000, 16, 128)
+    assert L.kda_prefill_key_gate_workspace_size(1, 4096, 8, 128, 128, 1) == size(1, 4096, 8, 128)
+    assert L.kda_prefill_key_gate_workspace_size(4, 32768, 32, 128, 128, 1) == size(4, 32768, 32, 128)
+    assert L.kda_prefill_key_gate_workspace_size(3, 500, 2, 64, 128, 1) == size(3, 500, 2, 128)
+    assert L.kda_prefill_key_gate_workspace_size(0, 1000, 16, 128, 128, 1) == 0
+    assert L.kda_prefill_key_gate_workspace_size(4, 1000, 16, 96, 128, 1) == 0
+
+
 def test_workspace_size_of_split_calls(L):
     """Calls with few (sequence, head) units are split into G segments per sequence
     (G >= 8, units x G <= 256, on average two chunks or more per segment); their
