@@ -101,7 +101,7 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int x) {
 // rows of L and of the Pd record.
 // ============================================================================
 template <int DK>
-__global__ __launch_bounds__(256, 2) void keygate_solve_kernel(
+__global__ __launch_bounds__(256, 3) void keygate_solve_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_off,
     int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ arec, uint16_t* __restrict__ prec,
@@ -110,9 +110,12 @@ __global__ __launch_bounds__(256, 2) void keygate_solve_kernel(
     constexpr int RBP = DK + 4;      // pitch (fp32) of the right-operand bases
     constexpr int RB_BYTES = 3 * KG_SUB * RBP * 4;
     constexpr int XS_BYTES = C * LP * 4;
-    constexpr int UX = RB_BYTES > XS_BYTES ? RB_BYTES : XS_BYTES;
-    // the right-operand bases are dead once L is formed, so X reuses their space;
-    // the 32x32 temporary of the solve reuses rows 0-16 of L
+    constexpr int RFP = DK + PAD;    // pitch (bf16) of the one-reference right operands
+    constexpr int RF_BYTES = 2 * 3 * KG_SUB * RFP * 2;
+    constexpr int U1 = RB_BYTES > XS_BYTES ? RB_BYTES : XS_BYTES;
+    constexpr int UX = U1 > RF_BYTES ? U1 : RF_BYTES;
+    // the right operands (either form) are dead once L is formed, so X reuses their
+    // space; the 32x32 temporary of the solve reuses rows 0-16 of L
     __shared__ __align__(16) unsigned char rx_[UX];
     __shared__ __align__(16) float Lf[C * LP];
     __shared__ __align__(16) float Tt[4 * DK];  // sub-chunk totals of log2 alpha
@@ -120,6 +123,8 @@ __global__ __launch_bounds__(256, 2) void keygate_solve_kernel(
     __shared__ int marks[4];
     static_assert(32 * SOLVE_RP <= 17 * LP, "temporary fits in rows 0-16 of L");
     float* RBs = reinterpret_cast<float*>(rx_);  // [3][16][RBP]: K (.) 2^{T_b - P_b} of sub-chunks 0-2
+    uint16_t* RFh = reinterpret_cast<uint16_t*>(rx_);  // [48][RFP] hi, then lo: one-reference right operands
+    uint16_t* RFl = RFh + 3 * KG_SUB * RFP;
     float* Xs = reinterpret_cast<float*>(rx_);
 
     const int64_t H = n_heads;
@@ -174,31 +179,26 @@ __global__ __launch_bounds__(256, 2) void keygate_solve_kernel(
             P[kk][x] = v;
         }
 
-    // ---- the sub-chunk totals, the right-operand bases k_r 2^{T - P[r]} of sub-chunks
-    // 0-2, and the range check of the diagonal block's exponents P[t] - P[mid]
-    const int src_mid = ((lane & ~15) + KG_MID) * 4, src_end = ((lane & ~15) + 15) * 4;
-    auto bcast = [](int src, float v) { return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v))); };
-    bool bad = false;
-    float* rbase = RBs + (wave * KG_SUB + m16) * RBP;
+    // ---- the sub-chunk totals T (lane 15 of each row holds P[15]) and beta
+    if (m16 == 15) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-        float rb8[8];
+        for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const float pm = bcast(src_mid, P[kk][x]), pe = bcast(src_end, P[kk][x]);
-            // (false for NaN too)
-            bad = bad || !(P[kk][x] - pm <= KG_RANGE) || !(pm - P[kk][x] <= KG_RANGE);
-            if (m16 == 15) Tt[wave * DK + 32 * kk + 8 * g + x] = pe;
-            rb8[x] = kv(kk, x) * __builtin_amdgcn_exp2f(pe - P[kk][x]);
-        }
-        if (wave < 3) {
-            *reinterpret_cast<f32x4*>(rbase + 32 * kk + 8 * g) = f32x4{rb8[0], rb8[1], rb8[2], rb8[3]};
-            *reinterpret_cast<f32x4*>(rbase + 32 * kk + 8 * g + 4) = f32x4{rb8[4], rb8[5], rb8[6], rb8[7]};
-        }
+            for (int x = 0; x < 8; ++x) Tt[wave * DK + 32 * kk + 8 * g + x] = P[kk][x];
     }
-    const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-    if (lane == 0) marks[wave] = any_bad ? 1 : 0;
     if (g == 0) bs[t] = bt;
+    block_sync();  // totals
+
+    // ---- one reference for the whole chunk (the end of token 31) when both halves
+    // of the chunk decay by at most 2^-KG_RANGE on every channel; the same test on
+    // the same totals in every wave, so the choice is uniform.  (False for NaN.)
+    bool half_ok = true;
+#pragma unroll
+    for (int c = 0; c < DK / 64; ++c) {
+        const int j = (DK / 64) * lane + c;
+        half_ok = half_ok && Tt[j] + Tt[DK + j] >= -KG_RANGE && Tt[2 * DK + j] + Tt[3 * DK + j] >= -KG_RANGE;
+    }
+    const bool whole = __builtin_amdgcn_ballot_w64(!half_ok) == 0;
 
     uint16_t* prec_c = prec + static_cast<int64_t>(item) * (A_RECORD_BYTES / 2);
     // one transposed 16x16 block (rows r = 16 b + 4g + e, column t = 16 a + m16) into
@@ -221,78 +221,162 @@ __global__ __launch_bounds__(256, 2) void keygate_solve_kernel(
         *reinterpret_cast<uint2*>(dst) = wh;
         *reinterpret_cast<uint2*>(dst + A_BLOCK_ELEMS) = wl;
     };
-
-    // ---- diagonal block (a, a): left operands k_t, q_t times 2^{P[t] - P[mid]}, right
-    // operand k_r times 2^{P[mid] - P[r]}, all from this lane's registers
-    {
-        f32x4 mT = {}, pT = {};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            float lk[8], lq[8], rr[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float d = P[kk][x] - bcast(src_mid, P[kk][x]);
-                const float up = __builtin_amdgcn_exp2f(d), dn = __builtin_amdgcn_exp2f(-d);
-                lk[x] = kv(kk, x) * up;
-                lq[x] = qv(kk, x) * up;
-                rr[x] = kv(kk, x) * dn;
-            }
-            bf16x8 lkh, lkl, lqh, lql, rh, rl;
-            split8f(lk, lkh, lkl);
-            split8f(lq, lqh, lql);
-            split8f(rr, rh, rl);
-            mT = mfma_hilo(rh, rl, lkh, lkl, mT);
-            pT = mfma_hilo(rh, rl, lqh, lql, pT);
-        }
-        put_block(wave, mT, pT);
-    }
     // the zero quadrants of the Pd record: rows 0-15 x cols 16-31 and rows 32-47 x cols 48-63
     if (wave == 0 || wave == 2) {
         uint16_t* dst = prec_c + (wave == 0 ? 0 : 2) * 2 * A_BLOCK_ELEMS + m16 * 32 + 16 + 4 * g;
         *reinterpret_cast<uint2*>(dst) = uint2{0u, 0u};
         *reinterpret_cast<uint2*>(dst + A_BLOCK_ELEMS) = uint2{0u, 0u};
     }
-    block_sync();  // right-operand bases, totals, beta, marks
 
-    // ---- blocks (a, b), b < a: left operands k_t, q_t times 2^{P[t]}, right operands
-    // the bases of sub-chunk b times 2^{T_{b+1} + .. + T_{a-1}} (taken for b = a-1 down
-    // to 0, the sum growing by one total each step)
-    if (wave > 0) {
-        f32x4 mT[3] = {}, pT[3] = {};
+    bool any_bad = false;
+    if (whole) {
+        // ======== one reference: d_t = G_t - G_31 (a sum over the tokens between, from
+        // the local prefix and whole sub-chunk totals; |d_t| <= KG_RANGE), left operands
+        // k_t, q_t times 2^{d_t}, right operand k_r times 2^{-d_r}.  The right
+        // operands of sub-chunks 0-2 go to LDS (hi/lo) for the waves after them.
+        bf16x8 lkh[NK], lkl[NK], lqh[NK], lql[NK];
+        f32x4 mT = {}, pT = {};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            float lk[8], lq[8], carry[8];
+            const int j0 = 32 * kk + 8 * g;
+            float lk[8], lq[8], rr[8];
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const float up = __builtin_amdgcn_exp2f(P[kk][x]);
+                const int j = j0 + x;
+                const float d = wave == 0   ? (P[kk][x] - Tt[j]) - Tt[DK + j]
+                                : wave == 1 ? P[kk][x] - Tt[DK + j]
+                                : wave == 2 ? P[kk][x]
+                                            : P[kk][x] + Tt[2 * DK + j];
+                const float up = __builtin_amdgcn_exp2f(d), dn = __builtin_amdgcn_exp2f(-d);
                 lk[x] = kv(kk, x) * up;
                 lq[x] = qv(kk, x) * up;
-                carry[x] = 0.f;
+                rr[x] = kv(kk, x) * dn;
             }
-            bf16x8 lkh, lkl, lqh, lql;
-            split8f(lk, lkh, lkl);
-            split8f(lq, lqh, lql);
+            bf16x8 rh, rl;
+            split8f(lk, lkh[kk], lkl[kk]);
+            split8f(lq, lqh[kk], lql[kk]);
+            split8f(rr, rh, rl);
+            if (wave < 3) {
+                *reinterpret_cast<bf16x8*>(RFh + (KG_SUB * wave + m16) * RFP + j0) = rh;
+                *reinterpret_cast<bf16x8*>(RFl + (KG_SUB * wave + m16) * RFP + j0) = rl;
+            }
+            mT = mfma_hilo(rh, rl, lkh[kk], lkl[kk], mT);
+            pT = mfma_hilo(rh, rl, lqh[kk], lql[kk], pT);
+        }
+        put_block(wave, mT, pT);
+        block_sync();  // right operands
+        if (wave > 0) {
+            f32x4 mB[3] = {}, pB[3] = {};
 #pragma unroll
-            for (int b = 2; b >= 0; --b) {
-                if (b >= wave) continue;
-                const float* src = RBs + (b * KG_SUB + m16) * RBP + 32 * kk + 8 * g;
-                const f32x4 r0 = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 r1 = *reinterpret_cast<const f32x4*>(src + 4);
-                float rr[8];
+            for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
-                for (int x = 0; x < 8; ++x) rr[x] = (x < 4 ? r0[x] : r1[x - 4]) * __builtin_amdgcn_exp2f(carry[x]);
-                bf16x8 rh, rl;
-                split8f(rr, rh, rl);
-                mT[b] = mfma_hilo(rh, rl, lkh, lkl, mT[b]);
-                pT[b] = mfma_hilo(rh, rl, lqh, lql, pT[b]);
+                for (int b = 0; b < 3; ++b) {
+                    if (b >= wave) continue;
+                    const bf16x8 rh = frag16(RFh, RFP, KG_SUB * b, 32 * kk, lane);
+                    const bf16x8 rl = frag16(RFl, RFP, KG_SUB * b, 32 * kk, lane);
+                    mB[b] = mfma_hilo(rh, rl, lkh[kk], lkl[kk], mB[b]);
+                    pB[b] = mfma_hilo(rh, rl, lqh[kk], lql[kk], pB[b]);
+                }
+            }
 #pragma unroll
-                for (int x = 0; x < 8; ++x) carry[x] += Tt[b * DK + 32 * kk + 8 * g + x];
+            for (int b = 0; b < 3; ++b)
+                if (b < wave) put_block(b, mB[b], pB[b]);
+        }
+    } else {
+        // ======== sub-chunk references: the right-operand bases k_r 2^{T - P[r]} of
+        // sub-chunks 0-2, and the range check of the diagonal block's exponents
+        // P[t] - P[mid]
+        const int src_mid = ((lane & ~15) + KG_MID) * 4;
+        auto bcast = [](int src, float v) {
+            return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+        };
+        bool bad = false;
+        float* rbase = RBs + (wave * KG_SUB + m16) * RBP;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            float rb8[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float pm = bcast(src_mid, P[kk][x]), pe = Tt[wave * DK + 32 * kk + 8 * g + x];
+                // (false for NaN too)
+                bad = bad || !(P[kk][x] - pm <= KG_RANGE) || !(pm - P[kk][x] <= KG_RANGE);
+                rb8[x] = kv(kk, x) * __builtin_amdgcn_exp2f(pe - P[kk][x]);
+            }
+            if (wave < 3) {
+                *reinterpret_cast<f32x4*>(rbase + 32 * kk + 8 * g) = f32x4{rb8[0], rb8[1], rb8[2], rb8[3]};
+                *reinterpret_cast<f32x4*>(rbase + 32 * kk + 8 * g + 4) = f32x4{rb8[4], rb8[5], rb8[6], rb8[7]};
             }
         }
+        any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+
+        // ---- diagonal block (a, a): left operands k_t, q_t times 2^{P[t] - P[mid]}, right
+        // operand k_r times 2^{P[mid] - P[r]}, all from this lane's registers
+        {
+            f32x4 mT = {}, pT = {};
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
-            if (b < wave) put_block(b, mT[b], pT[b]);
+            for (int kk = 0; kk < NK; ++kk) {
+                float lk[8], lq[8], rr[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float d = P[kk][x] - bcast(src_mid, P[kk][x]);
+                    const float up = __builtin_amdgcn_exp2f(d), dn = __builtin_amdgcn_exp2f(-d);
+                    lk[x] = kv(kk, x) * up;
+                    lq[x] = qv(kk, x) * up;
+                    rr[x] = kv(kk, x) * dn;
+                }
+                bf16x8 lkh, lkl, lqh, lql, rh, rl;
+                split8f(lk, lkh, lkl);
+                split8f(lq, lqh, lql);
+                split8f(rr, rh, rl);
+                mT = mfma_hilo(rh, rl, lkh, lkl, mT);
+                pT = mfma_hilo(rh, rl, lqh, lql, pT);
+            }
+            put_block(wave, mT, pT);
+        }
+        block_sync();  // right-operand bases
+
+        // ---- blocks (a, b), b < a: left operands k_t, q_t times 2^{P[t]}, right operands
+        // the bases of sub-chunk b times 2^{T_{b+1} + .. + T_{a-1}} (taken for b = a-1
+        // down to 0, the sum growing by one total each step)
+        if (wave > 0) {
+            f32x4 mB[3] = {}, pB[3] = {};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                float lk[8], lq[8], carry[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float up = __builtin_amdgcn_exp2f(P[kk][x]);
+                    lk[x] = kv(kk, x) * up;
+                    lq[x] = qv(kk, x) * up;
+                    carry[x] = 0.f;
+                }
+                bf16x8 lkh, lkl, lqh, lql;
+                split8f(lk, lkh, lkl);
+                split8f(lq, lqh, lql);
+#pragma unroll
+                for (int b = 2; b >= 0; --b) {
+                    if (b >= wave) continue;
+                    const float* src = RBs + (b * KG_SUB + m16) * RBP + 32 * kk + 8 * g;
+                    const f32x4 r0 = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 r1 = *reinterpret_cast<const f32x4*>(src + 4);
+                    float rr[8];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x)
+                        rr[x] = (x < 4 ? r0[x] : r1[x - 4]) * __builtin_amdgcn_exp2f(carry[x]);
+                    bf16x8 rh, rl;
+                    split8f(rr, rh, rl);
+                    mB[b] = mfma_hilo(rh, rl, lkh, lkl, mB[b]);
+                    pB[b] = mfma_hilo(rh, rl, lqh, lql, pB[b]);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) carry[x] += Tt[b * DK + 32 * kk + 8 * g + x];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 3; ++b)
+                if (b < wave) put_block(b, mB[b], pB[b]);
+        }
     }
+    if (lane == 0) marks[wave] = any_bad ? 1 : 0;
     block_sync();  // L complete; the right-operand bases are dead (X takes their space)
     if (tid == 0) cmark[item] = marks[0] | marks[1] | marks[2] | marks[3];
 

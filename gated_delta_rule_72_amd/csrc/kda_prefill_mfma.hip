@@ -298,7 +298,8 @@ struct ScanSmem {
     static constexpr int RA = HILO;             // A hi/lo [t][s]
     static constexpr int RP = HILO;             // P hi/lo [t][s]
     static constexpr int RU = 2 * BV * CP * 2;  // U^T hi/lo [i][t]
-    static constexpr int XP = C + 8;            // pitch of X^T rows (fp32)
+    static constexpr int XP = C + 4;            // pitch of X^T rows (fp32; 4 mod 64 dwords: the
+                                                // loaders' row-per-lane writes are conflict-free)
     static constexpr int RX = BV * XP * 4;      // X^T [i][t] = V 2^{-G}, transposed
     static constexpr int RO = C * OP * 2;       // O [t][i], staged for the store
     static constexpr int RG = C * GP * 4;       // G [t][i] (log2 units)
@@ -531,11 +532,14 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // The log-decay cumsum G of a chunk is formed in two steps one phase apart,
     // so the prefix across waves never needs a barrier of its own:
     // local_scan -- each loader wave's inclusive prefix over its 16 token rows (in
-    //   registers: a lane holds one value row), kept in the alpha registers; the
-    //   wave's totals go to Tot[parity][wave - 4];
+    //   registers: a lane holds one value row), kept in the alpha registers, and
+    //   V 2^{-prefix}, kept in the V registers; the wave's totals go to
+    //   Tot[parity][wave - 4];
     // finalize   -- after a barrier, add the totals of the loader waves before
     //   (the rows before this wave's), write G [t][i] and X^T [i][t] = V 2^{-G}
-    //   (the chain waves' initial Y); wave 7 writes gamma.
+    //   = (V 2^{-prefix}) 2^{-carry} (the chain waves' initial Y: one exponential
+    //   per lane in this phase, which the chain waves wait for); wave 7 writes
+    //   gamma.
     // Rows past the sequence end contribute log alpha = 0.
     bool beyond = false;  // loader waves: some chunk of some row of the unit is beyond the range
     auto local_scan = [&](int n, int par, int ln) {
@@ -548,6 +552,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 if constexpr (CKPT) lmin = fminf(lmin, l);
             }
             R[PL0 + r / 4][r % 4] = run;
+            // V 2^{-prefix}: the part of X = V 2^{-G} this wave knows before the carry
+            R[PV0 + r / 4][r % 4] = bf16_bits_to_f32(static_cast<uint16_t>(__float_as_uint(R[PV0 + r / 4][r % 4]))) *
+                                    __builtin_amdgcn_exp2f(-run);
         }
         // (also true for a NaN gate)
         if constexpr (CKPT) beyond = beyond || __builtin_amdgcn_ballot_w64(!(lmin >= -5.f)) != 0;
@@ -562,16 +569,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
             carry += b < wave - 4 ? tb : 0.f;
         }
         float* xt = XT + ln * XP + 16 * (wave - 4);
+        const float ec = __builtin_amdgcn_exp2f(-carry);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float gv = R[PL0 + p][e] + carry;
-                Gs[(16 * (wave - 4) + 4 * p + e) * GP + ln] = gv;
-                x[e] = bf16_bits_to_f32(static_cast<uint16_t>(__float_as_uint(R[PV0 + p][e]))) * __builtin_amdgcn_exp2f(-gv);
-            }
-            *reinterpret_cast<f32x4*>(xt + 4 * p) = x;
+            for (int e = 0; e < 4; ++e) Gs[(16 * (wave - 4) + 4 * p + e) * GP + ln] = R[PL0 + p][e] + carry;
+            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[PV0 + p] * ec;
         }
         if (wave == 7) {
             const float tot = R[PL0 + 3][3] + carry;
@@ -806,18 +809,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
         if (chain) {
             // ======== S^T += K^T U, then the decay: the K^T operand (rows j,
-            // reduction t) comes from row-major K through the transposing read --
-            // in 16-lane group g, lane m16 addresses token row 32 m + 4g + m16/4
-            // (+16 for the second half) at key channels 16 jt + 4 (m16 % 4) .. +3
-            const uint16_t* ktb = Kc + (4 * g + (m16 >> 2)) * KP + 4 * (m16 & 3);
+            // reduction t) comes from row-major K through the transposing read
+            // (fragments of tile jt + 1 are read while tile jt computes)
+            bf16x8 kt[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) kt[0][m] = frag_tr_st(Kc, KP, 0, 32 * m, ln);
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt) {
-                bf16x8 kt[2];
+                if (jt + 1 < NJ) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const s16x4 t0 = lds_read_tr16(ktb + (32 * m) * KP + 16 * jt);
-                    const s16x4 t1 = lds_read_tr16(ktb + (32 * m + 16) * KP + 16 * jt);
-                    kt[m] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    for (int m = 0; m < 2; ++m) kt[(jt + 1) & 1][m] = frag_tr_st(Kc, KP, 16 * (jt + 1), 32 * m, ln);
                 }
                 issue_fence();
 #pragma unroll
@@ -826,8 +827,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     for (int ib = 0; ib < 2; ++ib) {
                         const bf16x8 uh = __builtin_bit_cast(bf16x8, R[CARRY0 + 2 * ib + m]);
                         const bf16x8 ul = __builtin_bit_cast(bf16x8, R[CARRY0 + 4 + 2 * ib + m]);
-                        R[(ib) * NJ + (jt)] = mfma16(kt[m], uh, R[(ib) * NJ + (jt)]);
-                        R[(ib) * NJ + (jt)] = mfma16(kt[m], ul, R[(ib) * NJ + (jt)]);
+                        R[(ib) * NJ + (jt)] = mfma16(kt[jt & 1][m], uh, R[(ib) * NJ + (jt)]);
+                        R[(ib) * NJ + (jt)] = mfma16(kt[jt & 1][m], ul, R[(ib) * NJ + (jt)]);
                     }
             }
 #pragma unroll
