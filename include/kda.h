@@ -250,9 +250,18 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
  * The transcript page ("Per dins de Kimi K3 ..."), where it turns to
  * training, says the model is trained with the chunk-wise parallel algorithm;
  * the gradients follow from the per-token steps of page "Kimi (AI)", section
- * "Kimi Delta Attention (KDA)", by the chain rule taken in reverse token
- * order (the recurrence's states are recomputed from checkpoints every 16
- * tokens, kept in the workspace).
+ * "Kimi Delta Attention (KDA)", by the chain rule.
+ *   bf16 inputs with the value-channel, scalar or no gate run chunkwise on
+ *   matrix cores: a forward pass keeps the state entering every 64-token chunk,
+ *   a reverse scan forms the gradient of the state leaving every chunk, and one
+ *   workgroup per (chunk, head) then forms every gradient of the chunk (the
+ *   chunk's transposed UT-form algebra).  A (sequence, head) with a chunk beyond
+ *   the forward's decay range, a gate below 2^-5 (dalpha = dg / alpha would
+ *   magnify rounding) or a |beta| below 2^-20 is recomputed instead by:
+ *   the token-recurrent backward, which serves fp32 inputs and the gate on key
+ *   channels too: the chain rule in reverse token order, states recomputed from
+ *   checkpoints every 16 tokens.
+ * Both keep their states in the workspace.
  *
  *   q, k, v, alpha, beta, S0, cu_seqlens, n_seq, n_tok, n_heads, d_k, d_v, dt:
  *               as for kda_prefill (the forward inputs of the call)
@@ -265,8 +274,10 @@ kda_status kda_decode_step_key_gate(const void* q, const void* k, const void* v,
  *   dS0         [n_seq, n_heads, d_v, d_k] float32 (written), or NULL
  *   workspace   device scratch of at least kda_prefill_backward_workspace_size
  *               bytes (never NULL), clobbered.
- * dq, dk, dbeta (and a scalar gate's dalpha) are sums over the value rows,
- * added up with float atomics: their last bits can differ from run to run.
+ * dq, dk, dbeta (and a scalar gate's dalpha) are sums over the value rows; the
+ * chunked path forms them whole in one workgroup, the token-recurrent path adds
+ * them up with float atomics, so there their last bits can differ from run to
+ * run.
  * No output may overlap an input, another output or the workspace.  The
  * arithmetic is fp32 for either input dtype.
  */
