@@ -446,6 +446,10 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
         b.sck = reinterpret_cast<float*>(ws + L.un + L.sck);
         b.gck = reinterpret_cast<float*>(ws + L.un + L.gck);
         b.max_chunks = static_cast<int64_t>(a.n_tok) / PREFILL_CHUNK_BF16 + a.n_seq;
+        // the marks start clear: the forward pass's solve and scan only set them
+        if ((e = fill_zero(reinterpret_cast<float*>(b.flags),
+                           static_cast<int64_t>(a.n_seq) * a.n_heads * (a.d_v / BWD_ROWS), stream)) != hipSuccess)
+            return e;
         if ((e = launch_backward_forward_pass(a, b, stream)) != hipSuccess) return e;
         if ((e = launch_backward_chunk_passes(a, b, stream)) != hipSuccess) return e;
         return launch_backward_recurrent(a, b.order, b.flags, ws + L.un, stream);

@@ -24,11 +24,11 @@
 // (checked in fp64 against the token-by-token chain rule of the backward oracle).
 //
 // Passes, all on the caller's stream:
-//   1. the forward: the chunk solve (A records), then the scan in its checkpoint
-//      variant, which stores the state entering every chunk (no outputs) and marks
-//      units beyond the factored form's range or with a gate below 2^-5;
-//   2. the solve again, storing T = (I + L)^{-1} (no beta factor) and marking units
-//      with |beta| below 2^-20;
+//   1. the forward: the chunk solve, storing both A and T = (I + L)^{-1} (no beta
+//      factor) and marking units with |beta| below 2^-20, then the scan in its
+//      checkpoint variant, which stores the state entering every chunk (no outputs)
+//      and marks units beyond the factored form's range or with a gate below 2^-5;
+//   2. (the marks are only ever set; they are cleared before pass 1);
 //   3. bwd_state_scan_kernel: per (sequence, head, 64 value rows), the chunks in
 //      reverse, carrying dL/dS^T in fp32 MFMA accumulators -- the forward scan's
 //      chain transposed (K dZ^T, T^T dU, K^T dY on the critical path) -- and
@@ -74,7 +74,7 @@ __device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 b
 
 __device__ __forceinline__ bool unit_marked(const int32_t* __restrict__ flags, int seq, int h, int64_t H, int nvb) {
     bool m = false;
-    for (int vb = 0; vb < nvb; ++vb) m = m || flags[(static_cast<int64_t>(seq) * H + h) * nvb + vb] != 0;
+    for (int vb = 0; vb < nvb; ++vb) m |= flags[(static_cast<int64_t>(seq) * H + h) * nvb + vb] != 0;
     return m;
 }
 
@@ -412,65 +412,51 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
 
     const int64_t H = n_heads;
     const int total = min(first_chunk(n_seq, n_seq, n_tok, chunk_off), max_chunks);
-    const int gc = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
-    if (gc >= total) return;
-    const ChunkRef ch = chunk_ref(gc, n_seq, n_tok, cu_seqlens, chunk_off);
-    const int n = ch.n;
-    const int64_t tok0 = ch.t0 * H + h;
+    const int n_items = total * n_heads;  // (chunk, head) pairs, chunk-major
     const int64_t row_qk = H * DK, row_v = H * DV;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, m16 = lane & 15;
 
-    if (unit_marked(range_flags, ch.seq, h, H, NVB)) {
-        // computed by the token-recurrent pass, which adds the row sums into zeros
-        for (int x = tid; x < n * DK; x += 512) {
-            const int64_t e = (tok0 + static_cast<int64_t>(x / DK) * H) * DK + x % DK;
-            dq[e] = 0.f;
-            dk[e] = 0.f;
-        }
-        if (tid < n) {
-            dbeta[tok0 + tid * H] = 0.f;
-            if (GATE == GATE_SCALAR) dalpha[tok0 + tid * H] = 0.f;
-        }
-        return;
-    }
-
-    // phase A's own global inputs are issued first, so that they arrive under the staging:
-    // rows i = 16 w + m16 of S and D (key channels 8g + 32m .. +7), and V, dO at the tile
-    // rows t = 16 tt + 4g + e (one 4-byte or 2-byte load per value, past the chunk's end 0)
+    // The workgroup stays resident (one per CU) and walks the items it + k gridDim.x; the
+    // next item's global inputs are loaded while the current one finishes.
+    struct Item {
+        int64_t tok0;
+        int gc, h, n;
+        int marked;  // computed by the token-recurrent pass instead
+    };
+    auto item_info = [&](int it) {
+        Item x;
+        x.gc = it / n_heads;
+        x.h = it % n_heads;
+        const ChunkRef ch = chunk_ref(x.gc, n_seq, n_tok, cu_seqlens, chunk_off);
+        x.n = ch.n;
+        x.tok0 = ch.t0 * H + x.h;
+        x.marked = unit_marked(range_flags, ch.seq, x.h, H, NVB);
+        return x;
+    };
+    constexpr int NRP = (A_RECORD_PIECES + 511) / 512;
+    u32x4 pk[NKQ], pq[NKQ], prec[NRP];
+    float pb, pa[NVB][8];
     f32x4 pS[NM][2], pD[NM][2];
     float pV[4][4], pdO[4][4];
-    if (wave < NWA) {
-        const int i = 16 * wave + m16;
-        const int64_t srow = ((static_cast<int64_t>(gc) * H + h) * DV + i) * DK + 8 * g;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                pS[m][x] = *reinterpret_cast<const f32x4*>(sck + srow + 32 * m + 4 * x);
-                pD[m][x] = *reinterpret_cast<const f32x4*>(gck + srow + 32 * m + 4 * x);
-            }
-        const auto rv = make_rsrc(v + tok0 * DV + i, ((n - 1) * row_v + 1) * 2);
-        const auto rdo = make_rsrc(dO + tok0 * DV + i, ((n - 1) * row_v + 1) * 4);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * g + e;
-                pV[tt][e] = bf16_bits_to_f32(
-                    static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, static_cast<int>(t * row_v) * 2, 0, 0)));
-                pdO[tt][e] =
-                    __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdo, static_cast<int>(t * row_v) * 4, 0, 0));
-            }
-    }
-
-    // ======== staging: K, Q, T, beta; the upper-right 32x32 block of T is zero
-    {
-        const int64_t bqk = ((n - 1) * row_qk + DK) * 2;
-        const auto rk_ = make_rsrc(k + tok0 * DK, bqk);
-        const auto rq_ = make_rsrc(q + tok0 * DK, bqk);
-        u32x4 pk[NKQ], pq[NKQ];
+    // The global inputs of the staging (K, Q, the T record, beta and alpha): loaded for the
+    // next item while the current one finishes.  All loads are buffer loads: ranges end at the
+    // chunk's last token, and an item that is not loaded (none left, or marked) gets empty
+    // ranges, so every register is written and every load returns 0 without touching memory.
+    // Each resource is uniform over the wave (a per-lane base would make the compiler loop over
+    // the distinct bases, waiting for each load in turn); the lane's position is in the offset.
+    auto fetch_stage = [&](const Item& x, bool valid) __attribute__((always_inline)) {
+        // offsets from an opaque copy of the thread index, recomputed at every call (hoisted
+        // out of the item loop they would hold registers throughout)
+        int tid_f = tid;
+        asm volatile("" : "+v"(tid_f));
+        const int tid = tid_f, lane = tid & 63;
+        const int g = lane >> 4, m16 = lane & 15;
+        const int nn = valid ? x.n : 0;
+        const int64_t bqk = nn > 0 ? ((nn - 1) * row_qk + DK) * 2 : 0;
+        const auto rk_ = make_rsrc(k + x.tok0 * DK, bqk);
+        const auto rq_ = make_rsrc(q + x.tok0 * DK, bqk);
 #pragma unroll
         for (int p = 0; p < NKQ; ++p) {
             const int idx = tid + 512 * p;
@@ -478,20 +464,112 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             pk[p] = __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0);
             pq[p] = __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0);
         }
-        const uint16_t* recp = trec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
-        for (int p = tid; p < A_RECORD_PIECES; p += 512)
-            *reinterpret_cast<u32x4*>(record_piece_dst(T_hi, T_lo, p)) = *reinterpret_cast<const u32x4*>(recp + 8 * p);
-        for (int x = tid; x < 32 * 32; x += 512) {
-            T_hi[(x >> 5) * CP + 32 + (x & 31)] = 0;
-            T_lo[(x >> 5) * CP + 32 + (x & 31)] = 0;
-        }
-        if (tid < C) bs[tid] = tid < n ? beta[tok0 + tid * H] : 0.f;
+        const auto rr_ = make_rsrc(trec + (static_cast<int64_t>(x.gc) * n_heads + x.h) * (A_RECORD_BYTES / 2),
+                                   valid ? A_RECORD_BYTES : 0);
 #pragma unroll
-        for (int p = 0; p < NKQ; ++p) {
-            const int idx = tid + 512 * p;
-            *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = pk[p];
-            *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * KP + 8 * (idx % PPR)) = pq[p];
+        for (int p = 0; p < NRP; ++p) prec[p] = __builtin_amdgcn_raw_buffer_load_b128(rr_, (tid + 512 * p) * 16, 0, 0);
+        const auto rb_ = make_rsrc(beta + x.tok0, nn > 0 ? ((nn - 1) * H + 1) * 4 : 0);
+        pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, static_cast<int>(tid * H) * 4, 0, 0));
+        // alpha at token rows t = 8 w + r, value rows i = lane + 64 xv
+        if constexpr (GATE != GATE_NONE) {
+            const auto ra_ = GATE == GATE_CHANNEL ? make_rsrc(alpha + x.tok0 * DV, nn > 0 ? ((nn - 1) * row_v + DV) * 4 : 0)
+                                                  : make_rsrc(alpha + x.tok0, nn > 0 ? ((nn - 1) * H + 1) * 4 : 0);
+#pragma unroll
+            for (int xv = 0; xv < NVB; ++xv)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int t = 8 * wave + r;
+                    const int off = GATE == GATE_CHANNEL ? static_cast<int>(t * row_v) + lane + 64 * xv : static_cast<int>(t * H);
+                    pa[xv][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra_, off * 4, 0, 0));
+                }
         }
+    };
+    // phase A's inputs: rows i = 16 w + m16 of S and D (key channels 8g + 32m .. +7), and V,
+    // dO at the tile rows t = 16 tt + 4g + e
+    auto fetch_a = [&](const Item& x) __attribute__((always_inline)) {
+        int tid_f = tid;
+        asm volatile("" : "+v"(tid_f));
+        const int lane = tid_f & 63;
+        const int g = lane >> 4, m16 = lane & 15;
+        const bool rows = wave < NWA;
+        const int nn = x.n;
+        const int i = 16 * wave + m16;
+        const int64_t unit = (static_cast<int64_t>(x.gc) * H + x.h) * DV * DK;
+        const auto rs_ = make_rsrc(sck + unit, rows ? DV * DK * 4 : 0);
+        const auto rz_ = make_rsrc(gck + unit, rows ? DV * DK * 4 : 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int off = (i * DK + 8 * g + 32 * m + 4 * hf) * 4;
+                pS[m][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_, off, 0, 0));
+                pD[m][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rz_, off, 0, 0));
+            }
+        const auto rv = make_rsrc(v + x.tok0 * DV, rows && nn > 0 ? ((nn - 1) * row_v + DV) * 2 : 0);
+        const auto rdo = make_rsrc(dO + x.tok0 * DV, rows && nn > 0 ? ((nn - 1) * row_v + DV) * 4 : 0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int off = static_cast<int>((16 * tt + 4 * g + e) * row_v) + i;
+                pV[tt][e] = bf16_bits_to_f32(
+                    static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, off * 2, 0, 0)));
+                pdO[tt][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdo, off * 4, 0, 0));
+            }
+    };
+
+    int it = blockIdx.x;
+    if (it >= n_items) return;
+    Item cur = item_info(it);
+    fetch_stage(cur, !cur.marked);
+    while (true) {
+    // the thread index passes through an empty asm every item, so the compiler cannot hoist
+    // the body's lane-dependent addresses out of the loop (they would stay live throughout)
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    {
+    const int tid = tid_o, lane = tid & 63;
+    const int g = lane >> 4, m16 = lane & 15;
+    const int it_next = it + static_cast<int>(gridDim.x);
+    if (cur.marked) {
+        // computed by the token-recurrent pass, which adds the row sums into zeros
+        for (int x = tid; x < cur.n * DK; x += 512) {
+            const int64_t e = (cur.tok0 + static_cast<int64_t>(x / DK) * H) * DK + x % DK;
+            dq[e] = 0.f;
+            dk[e] = 0.f;
+        }
+        if (tid < cur.n) {
+            dbeta[cur.tok0 + tid * H] = 0.f;
+            if (GATE == GATE_SCALAR) dalpha[cur.tok0 + tid * H] = 0.f;
+        }
+        if (it_next >= n_items) break;
+        it = it_next;
+        cur = item_info(it);
+        fetch_stage(cur, !cur.marked);
+        continue;
+    }
+    const int gc = cur.gc, h = cur.h, n = cur.n;
+    const int64_t tok0 = cur.tok0;
+    const bool more = it_next < n_items;
+    Item nxt = cur;
+    if (more) nxt = item_info(it_next);  // scalar loads, in flight under this item
+    fetch_a(cur);                        // arrives under the staging
+
+    // ======== staging: K, Q, T, beta; the upper-right 32x32 block of T is zero
+#pragma unroll
+    for (int p = 0; p < NRP; ++p)
+        if (tid + 512 * p < A_RECORD_PIECES)
+            *reinterpret_cast<u32x4*>(record_piece_dst(T_hi, T_lo, tid + 512 * p)) = prec[p];
+    for (int x = tid; x < 32 * 32; x += 512) {
+        T_hi[(x >> 5) * CP + 32 + (x & 31)] = 0;
+        T_lo[(x >> 5) * CP + 32 + (x & 31)] = 0;
+    }
+    if (tid < C) bs[tid] = tid < n ? pb : 0.f;
+#pragma unroll
+    for (int p = 0; p < NKQ; ++p) {
+        const int idx = tid + 512 * p;
+        *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = pk[p];
+        *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * KP + 8 * (idx % PPR)) = pq[p];
     }
     // G: wave w sums log2 alpha over token rows 8 w .. +7, lane = value row (two rows per lane at d_v = 128)
     float Gl[NVB][8];
@@ -501,9 +579,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         float run = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int t = 8 * wave + r;
-            if constexpr (GATE == GATE_CHANNEL) run += t < n ? __builtin_amdgcn_logf(alpha[(tok0 + t * H) * DV + i]) : 0.f;
-            if constexpr (GATE == GATE_SCALAR) run += t < n ? __builtin_amdgcn_logf(alpha[tok0 + t * H]) : 0.f;
+            if constexpr (GATE != GATE_NONE) run += 8 * wave + r < n ? __builtin_amdgcn_logf(pa[x][r]) : 0.f;
             Gl[x][r] = run;
         }
         Tot[wave * DV + i] = run;
@@ -724,6 +800,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         }
     }
     block_sync();  // phase A done: T, P and G^T are dead
+    // phase B's B operands of its first round (value rows 0-63 of S and D at this lane's key
+    // channel), issued now so that they arrive under the dV stores
+    const int jt = wave % NJT, tt0 = (wave / NJT) * TPW;
+    const int jc = 16 * jt + m16;  // this lane's key channel (B-operand column)
+    const float* sbase = sck + (static_cast<int64_t>(gc) * H + h) * DV * DK + jc;
+    const float* gbase = gck + (static_cast<int64_t>(gc) * H + h) * DV * DK + jc;
+    f32x4 cs[2][2], cz[2][2];  // [m][half]: rows 64 r + 32 m + 16 half + 4 g .. +3
+    auto load_sd = [&](int r) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t row = 64 * r + 32 * m + 16 * x + 4 * g + e;
+                    cs[m][x][e] = sbase[row * DK];
+                    cz[m][x][e] = gbase[row * DK];
+                }
+    };
+    load_sd(0);
     {
         // dV (and a value-channel dalpha) through LDS as whole token rows [t][i], stored as
         // 16-byte pieces of each row: the tile layout has 4 tokens of one row per lane
@@ -764,8 +860,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
     }
 
     // ======== phase B
-    const int jt = wave % NJT, tt0 = (wave / NJT) * TPW;
-    const int jc = 16 * jt + m16;  // this lane's key channel (B-operand column)
     f32x4 DQ[TPW], DK_[TPW];
 #pragma unroll
     for (int x = 0; x < TPW; ++x) DQ[x] = DK_[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -777,8 +871,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         tr = e < 1 ? 0 : e < 3 ? 1 : e < 6 ? 2 : 3;
         tc = e - tr * (tr + 1) / 2;
     };
-    const float* sbase = sck + (static_cast<int64_t>(gc) * H + h) * DV * DK + jc;
-    const float* gbase = gck + (static_cast<int64_t>(gc) * H + h) * DV * DK + jc;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         if (wave >= 4 * r && wave < 4 * r + 4) {
@@ -812,17 +904,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             }
         }
         // dq += dO~ S, dk += U dZ - dY S over this round's rows: B operands (column j, stacked rows i)
-        // read from the state and gradient checkpoints
+        // from the state and gradient checkpoints
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            f32x4 s0, s1, z0, z1;
+            const f32x4 s0 = cs[m][0], s1 = cs[m][1];
+            f32x4 z0 = cz[m][0], z1 = cz[m][1];
             const int ib = 64 * r + 32 * m + 4 * g;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                s0[e] = sbase[static_cast<int64_t>(ib + e) * DK];
-                s1[e] = sbase[static_cast<int64_t>(ib + 16 + e) * DK];
-                z0[e] = gbase[static_cast<int64_t>(ib + e) * DK] * gam[ib + e];
-                z1[e] = gbase[static_cast<int64_t>(ib + 16 + e) * DK] * gam[ib + 16 + e];
+                z0[e] *= gam[ib + e];
+                z1[e] *= gam[ib + 16 + e];
             }
             bf16x8 sh, sl, nh, nl, zh, zl;
             split8(s0, s1, sh, sl);
@@ -839,8 +930,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
                                nh, nl, DK_[x]);
             }
         }
+        if (r + 1 < NR) load_sd(r + 1);  // the next round's, under this round's barrier
         block_sync();  // the round's buffers are read
     }
+    fetch_stage(nxt, more && !nxt.marked);  // the next item's, under this item's last phase
     // dP (lower, diagonal kept) and dKK (strictly lower, negated) -> LDS [t][s]; their upper tiles are zero
     for (int x = tid; x < 6 * 256; x += 512) {
         const int tile = x >> 8, y = x & 255;
@@ -890,8 +983,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             }
         }
     }
-    const auto rq_ = make_rsrc(dq + tok0 * DK, ((n - 1) * row_qk + DK) * 4);
-    const auto rk_ = make_rsrc(dk + tok0 * DK, ((n - 1) * row_qk + DK) * 4);
+    const auto rdq = make_rsrc(dq + tok0 * DK, ((n - 1) * row_qk + DK) * 4);
+    const auto rdk = make_rsrc(dk + tok0 * DK, ((n - 1) * row_qk + DK) * 4);
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
 #pragma unroll
@@ -900,9 +993,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
             const int off = static_cast<int>(t * row_qk + jc) * 4;
             // (__float_as_uint on the element value: a bit_cast of an ext-vector subscript
             // reads element 0 with this compiler)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(DQ[x][e]), rq_, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(DK_[x][e]), rk_, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(DQ[x][e]), rdq, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(DK_[x][e]), rdk, off, 0, 0);
         }
+    }
+    if (!more) break;
+    it = it_next;
+    cur = nxt;
+    block_sync();  // every wave is done with this item's LDS before the next one's staging
+    }
     }
 }
 
@@ -917,7 +1016,11 @@ static hipError_t launch_bwd_chunk_t(const BackwardArgs& a, const BwdChunkBufs& 
                        a.dS0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_tok == 0) return e;
-    const int64_t grid2 = b.max_chunks * static_cast<int64_t>(a.n_heads);
+    // one resident workgroup per CU (the LDS allows no more), each looping over (chunk, head) items
+    int dev = 0, n_cu = 0;
+    if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t grid2 = std::min<int64_t>(b.max_chunks * static_cast<int64_t>(a.n_heads), n_cu);
     hipLaunchKernelGGL((bwd_chunk_grad_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid2)), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.alpha, a.beta, a.dO, a.cu_seqlens, b.chunk_off, b.rec,

@@ -139,14 +139,15 @@ struct BwdChunkBufs {
     int32_t* order;      // longest-first schedule (packed input) or null
     int32_t* chunk_off;  // first chunk of every sequence (packed input) or null
     int32_t* flags;      // [n_seq, H, d_v / 64]: units left to the token-recurrent pass
-    uint16_t* rec;       // solved records of every (chunk, head): A for the forward, then T
+    uint16_t* rec;       // solved T record of every (chunk, head)
     float* sck;          // [chunks, H, d_v, d_k] state entering every chunk
     float* gck;          // [chunks, H, d_v, d_k] gradient of the state leaving every chunk
     int64_t max_chunks;  // n_tok / 64 + n_seq: bound on the number of chunks
 };
 // The backward's forward pass (kda_prefill_mfma.hip): schedule and chunk offsets for
-// packed input, the chunk solve, the checkpoint scan (states into sck, range marks
-// into flags), and the solve again storing T into rec (marks for tiny beta).
+// packed input, the chunk solve (A records into the space of gck, which nothing
+// writes before the reverse scan; T records into rec; marks for tiny beta), and the
+// checkpoint scan (states into sck, range marks into flags).  The caller clears flags.
 hipError_t launch_backward_forward_pass(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream);
 // The chunked passes proper (kda_backward_chunk.hip): the reverse state-gradient scan
 // (gck, dS0) and the per-(chunk, head) gradients.

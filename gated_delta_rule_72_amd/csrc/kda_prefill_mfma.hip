@@ -109,16 +109,17 @@ __global__ __launch_bounds__(256) void segment_cu_kernel(const int32_t* __restri
 // 16x16 diagonal blocks by forward substitution, then X21 = -X22 L21 X11 at 16
 // and at 32 rows.
 // ============================================================================
-// STORE_T (the chunked backward): the record holds T = (I + L)^{-1} itself, without
-// the diag(beta) factor, and a chunk with a token whose |beta| is below 2^-20 marks
-// every row block of its (sequence, head) in range_flags (n_vblk blocks per
-// head): the backward divides by beta there and leaves such units to its
-// token-recurrent pass.
+// STORE_T (the chunked backward): a second record, in trec, holds T = (I + L)^{-1}
+// itself, without the diag(beta) factor, and a chunk with a token whose |beta| is
+// below 2^-20 marks every row block of its (sequence, head) in range_flags (n_vblk
+// blocks per head): the backward divides by beta there and leaves such units to
+// its token-recurrent pass.
 template <int DK, bool STORE_T = false>
 __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
-    uint16_t* __restrict__ arec, int32_t* __restrict__ range_flags = nullptr, int n_vblk = 0) {
+    uint16_t* __restrict__ arec, uint16_t* __restrict__ trec = nullptr, int32_t* __restrict__ range_flags = nullptr,
+    int n_vblk = 0) {
     constexpr int KP = DK + PAD;
     constexpr int KX = (C * KP * 2 > C * LP * 4) ? C * KP * 2 : C * LP * 4;
     // K is dead once L is formed, so X reuses its space; the 32x32 temporary of
@@ -249,9 +250,10 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     }
     assemble_inverse(Xs, Lf, Rtmp, x, wave, lane);
 
-    // ---- A = X diag(beta) (STORE_T: X itself) -> the record
-    write_solve_record<!STORE_T>(arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2), Xs, bs,
-                                 tid);
+    // ---- A = X diag(beta) -> the record (STORE_T: X itself -> the second record)
+    const int64_t rec_off = (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
+    write_solve_record<true>(arec + rec_off, Xs, bs, tid);
+    if constexpr (STORE_T) write_solve_record<false>(trec + rec_off, Xs, bs, tid);
     block_sync();  // X, read above, shares its space with the next item's K
     }
 }
@@ -900,7 +902,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
     block_sync();
     const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
     if (outw && !CKPT) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
-    if (range_flags && tid == 0)
+    // (CKPT: the backward zeroes the marks beforehand and its chunk solve may already have
+    // set some, so the scan only sets)
+    if (range_flags && tid == 0 && (!CKPT || unit_beyond))
         range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
 
     // the unit's total log2-decay per value row, when asked for (the sequence-parallel
@@ -1011,7 +1015,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         const int64_t grid = std::min<int64_t>(mc * a.n_heads, 4 * static_cast<int64_t>(n_cu));
         hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok, a.n_heads,
-                           static_cast<int>(mc), arec, nullptr, 0);
+                           static_cast<int>(mc), arec, nullptr, nullptr, 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int nsq, float* st,
@@ -1079,21 +1083,20 @@ static hipError_t bwd_forward_t(const BackwardArgs& a, const BwdChunkBufs& b, hi
     if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     const int64_t sgrid = std::min<int64_t>(b.max_chunks * a.n_heads, 4 * static_cast<int64_t>(n_cu));
     const uint16_t* k = static_cast<const uint16_t*>(a.k);
-    hipLaunchKernelGGL((chunk_solve_kernel<DK, false>), dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, stream, k,
-                       a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), b.rec,
-                       nullptr, 0);
+    // one solve writes both records: A (for the checkpoint scan) into the space of the state
+    // gradients, which only the reverse scan writes, after this pass; T into rec
+    uint16_t* arec = reinterpret_cast<uint16_t*>(b.gck);
+    hipLaunchKernelGGL((chunk_solve_kernel<DK, true>), dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, stream, k,
+                       a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), arec,
+                       b.rec, b.flags, NVB);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
     // the state enters K S^T as hi + lo (SPLIT_S): the checkpoints feed dq and dk directly,
     // where a single bf16 copy's rounding is not damped by any decay
     hipLaunchKernelGGL((scan_kernel<DK, DV, GATE, true, true>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(a.q), k, static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu,
-                       cu ? b.order : nullptr, b.chunk_off, b.rec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr, 0,
+                       cu ? b.order : nullptr, b.chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr, 0,
                        nullptr, b.flags, b.sck);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_solve_kernel<DK, true>), dim3(static_cast<unsigned>(sgrid)), dim3(256), 0, stream, k,
-                       a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), b.rec,
-                       b.flags, NVB);
     return hipGetLastError();
 }
 
