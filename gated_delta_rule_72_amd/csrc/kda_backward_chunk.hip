@@ -81,17 +81,23 @@ __device__ __forceinline__ bool unit_marked(const int32_t* __restrict__ flags, i
 }  // namespace
 
 // ============================================================================
-// bwd_state_scan_kernel: one workgroup of 4 waves per (sequence, head, block of 64
-// value rows); wave w owns value rows i0 + 16 w .. +15 and carries D^T (d_k x 16,
-// rows j = 16 jt + 4g + r of tile jt, column = the lane's row) in accumulators.
-// Per chunk, last to first: stage K, Q, T, beta; form G and dO~^T [i][t] and gamma
-// (each wave 16 token rows, a lane per value row); P = tril(Q K^T) (wave w the
-// t-tile w); then each wave: store D, dZ = D gamma, dU = K dZ + P^T dO~,
-// dYb = T^T dU, dY = beta dYb, D <- dZ + Q^T dO~ - K^T dY.  The next chunk's
-// inputs are loaded into registers while the current one is computed.
+// bwd_state_scan_kernel: one workgroup of 8 waves per (sequence, head, block of 64
+// value rows), chunks last to first.
+// - Chain waves (0-3): wave w owns value rows i0 + 16 w .. +15 and carries D^T (d_k x 16,
+//   rows j = 16 jt + 4g + r of tile jt, column = the lane's row) in accumulators.  Per
+//   chunk: store D, dZ = D gamma, dU = K dZ + P^T dO~, dYb = T^T dU, dY = beta dYb, then
+//   D <- dZ + Q^T dO~ - K^T dY.
+// - Helper waves (4-7) prepare the chunk before meanwhile: K and Q into the other of two
+//   buffers; G and dO~^T [i][t], gamma (helper h: token rows 16 h .. +15, a lane per value
+//   row); P = tril(Q K^T); T and beta.  Each of dO~^T and gamma, P, and T and beta has one
+//   buffer, rewritten once the chain has read it.  Each input's loads for the chunk after
+//   that are issued as soon as its registers are free.
+// Four barriers per chunk:  D | chain: D store, K dZ  -- helpers: stage K, Q; log2 alpha
+// prefix  | A | chain: P^T dO~  -- helpers: dO~^T, gamma  | B | chain: T^T dU  --
+// helpers: P  | C | chain: D update  -- helpers: T, beta  | D.
 // ============================================================================
 template <int DK, int DV, int GATE>
-__global__ __launch_bounds__(256) void bwd_state_scan_kernel(
+__global__ __launch_bounds__(512) void bwd_state_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ dO, const float* __restrict__ dS_T,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
@@ -103,10 +109,10 @@ __global__ __launch_bounds__(256) void bwd_state_scan_kernel(
     constexpr int NM = DK / 32;
     constexpr int XP = C + 8;              // pitch of dO~^T rows (fp32)
     constexpr int PPR = DK / 8;            // 16-byte pieces per row of q or k
-    constexpr int NKQ = C * PPR / 256;     // ... per thread
+    constexpr int NKQ = C * PPR / 256;     // ... per helper thread
     constexpr int NREC = A_RECORD_PIECES / 256;
-    __shared__ __align__(16) uint16_t Kc[C * KP];
-    __shared__ __align__(16) uint16_t Qc[C * KP];
+    __shared__ __align__(16) uint16_t Kc[2][C * KP];
+    __shared__ __align__(16) uint16_t Qc[2][C * KP];
     __shared__ __align__(16) uint16_t T_hi[C * CP];
     __shared__ __align__(16) uint16_t T_lo[C * CP];
     __shared__ __align__(16) uint16_t P_hi[C * CP];
@@ -122,53 +128,76 @@ __global__ __launch_bounds__(256) void bwd_state_scan_kernel(
     const int h = u.head;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wave < 4;
+    const int hw = wave & 3;      // chain: rows 16 hw ..; helper: token rows 16 hw ..
+    const int htid = tid & 255;   // thread index among the chain or the helper waves
     if (unit_marked(range_flags, u.seq, h, H, NVB)) {
         // the whole (sequence, head) goes to the token-recurrent pass: mark every block of it
         if (tid < NVB) range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + tid] = 1;
         return;
     }
     const int i0 = u.vblk * 64;
-    const int iw = i0 + 16 * wave;  // first value row of this wave
+    const int iw = i0 + 16 * hw;  // first value row of a chain wave
     const int64_t row_qk = H * DK, row_v = H * DV;
     const int chunk0 = first_chunk(u.seq, n_seq, n_tok, chunk_off);
     const int n_chunks = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
 
-    // the upper-right 32x32 block of T is not part of a record: zero, read as such
-    for (int x = tid; x < 32 * 32; x += 256) {
+    // the upper-right 32x32 block of T is not part of a record, and the helpers write only the
+    // 16x16 tiles of P on and below the diagonal: the rest is zeroed once and read as such
+    for (int x = tid; x < 32 * 32; x += 512) {
         T_hi[(x >> 5) * CP + 32 + (x & 31)] = 0;
         T_lo[(x >> 5) * CP + 32 + (x & 31)] = 0;
     }
+    for (int x = tid; x < C * C; x += 512) {
+        const int t = x / C, s = x % C;
+        if ((s >> 4) > (t >> 4)) P_hi[t * CP + s] = P_lo[t * CP + s] = 0;
+    }
 
+    // One register array holds each role's long-lived values -- the chain's D^T, or a
+    // helper's loaded inputs -- so the allocator, which cannot know that a wave keeps one
+    // role, does not keep both sets live at once (likewise X4: the chain's dU, a helper's
+    // log2-decay prefix).
+    constexpr int OK_ = 0, OQ = NKQ, OA = 2 * NKQ, OD = OA + 4, OR = OD + 4, OB = OR + NREC;
+    constexpr int NRR = OB + 1 > NJ ? OB + 1 : NJ;
+    f32x4 RR[NRR];
+    f32x4* R = RR;  // chain: D^T tiles
+    auto rk = [&](int p) -> f32x4& { return RR[OK_ + p]; };
+    auto rq = [&](int p) -> f32x4& { return RR[OQ + p]; };
+    auto rr = [&](int p) -> f32x4& { return RR[OR + p]; };
+    // scalar members (an element of a vector cannot be bound to a reference)
+    auto ra = [&](int r) { return RR[OA + (r >> 2)][r & 3]; };
+    auto rd = [&](int r) { return RR[OD + (r >> 2)][r & 3]; };
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + iw + (lane & 15)) * DK + 4 * (lane >> 4);
-    f32x4 R[NJ];
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt)
-        R[jt] = dS_T ? *reinterpret_cast<const f32x4*>(dS_T + s_base + 16 * jt) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < NRR; ++x) RR[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (chain && dS_T) {
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) R[jt] = *reinterpret_cast<const f32x4*>(dS_T + s_base + 16 * jt);
+    }
 
-    // ---- one chunk's inputs, in registers (a chunk index below 0 loads nothing)
-    u32x4 rk[NKQ], rq[NKQ], rr[NREC];
-    float ra[16], rd[16], rb;
+    // ---- a helper's inputs of one chunk, in registers (a chunk index outside 0 .. n_chunks - 1
+    // loads nothing)
     auto chunk_len = [&](int c) {
-        return c < 0 ? 0 : static_cast<int>(min<int64_t>(C, u.t1 - (u.t0 + static_cast<int64_t>(c) * C)));
+        return c < 0 || c >= n_chunks ? 0 : static_cast<int>(min<int64_t>(C, u.t1 - (u.t0 + static_cast<int64_t>(c) * C)));
     };
-    auto fetch = [&](int c) {
+    auto chunk_tok0 = [&](int c) { return (u.t0 + static_cast<int64_t>(c < 0 ? 0 : c) * C) * H + h; };
+    auto fetch_kq = [&](int c) {
         const int n = chunk_len(c);
-        const int cc = c < 0 ? 0 : c;
-        const int64_t tok0 = (u.t0 + static_cast<int64_t>(cc) * C) * H + h;
+        const int64_t tok0 = chunk_tok0(c);
         const int64_t bqk = n > 0 ? ((n - 1) * row_qk + DK) * 2 : 0;
         const auto rk_ = make_rsrc(k + tok0 * DK, bqk);
         const auto rq_ = make_rsrc(q + tok0 * DK, bqk);
 #pragma unroll
         for (int p = 0; p < NKQ; ++p) {
-            const int idx = tid + 256 * p;
+            const int idx = htid + 256 * p;
             const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
-            rk[p] = __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0);
-            rq[p] = __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0);
+            rk(p) = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0));
+            rq(p) = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
         }
-        const uint16_t* recp = trec + (static_cast<int64_t>(chunk0 + cc) * n_heads + h) * (A_RECORD_BYTES / 2);
-        const auto rr_ = make_rsrc(recp, n > 0 ? A_RECORD_BYTES : 0);
-#pragma unroll
-        for (int p = 0; p < NREC; ++p) rr[p] = __builtin_amdgcn_raw_buffer_load_b128(rr_, (tid + 256 * p) * 16, 0, 0);
+    };
+    auto fetch_ad = [&](int c) {
+        const int n = chunk_len(c);
+        const int64_t tok0 = chunk_tok0(c);
         const int64_t bv = n > 0 ? ((n - 1) * row_v + 64) * 4 : 0;
         const auto ra_ = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, bv)
                          : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, n > 0 ? ((n - 1) * H + 1) * 4 : 0)
@@ -176,165 +205,201 @@ __global__ __launch_bounds__(256) void bwd_state_scan_kernel(
         const auto rd_ = make_rsrc(dO + tok0 * DV + i0, bv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = 16 * wave + r;
+            const int t = 16 * hw + r;
             const int e = static_cast<int>(t * row_v + lane);
             if constexpr (GATE != GATE_NONE) {
                 const int ea = GATE == GATE_CHANNEL ? e : static_cast<int>(t * H);
-                ra[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra_, ea * 4, 0, 0));
+                RR[OA + (r >> 2)][r & 3] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra_, ea * 4, 0, 0));
             }
-            rd[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd_, e * 4, 0, 0));
+            RR[OD + (r >> 2)][r & 3] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd_, e * 4, 0, 0));
         }
-        const auto rb_ = make_rsrc(beta + tok0, n > 0 ? ((n - 1) * H + 1) * 4 : 0);
-        rb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, static_cast<int>(lane * H) * 4, 0, 0));
     };
-
-    fetch(n_chunks - 1);
-    for (int c = n_chunks - 1; c >= 0; --c) {
-        const int gc = chunk0 + c;
+    auto fetch_tb = [&](int c) {
         const int n = chunk_len(c);
+        const int64_t tok0 = chunk_tok0(c);
+        const uint16_t* recp = trec + (static_cast<int64_t>(chunk0 + (c < 0 ? 0 : c)) * n_heads + h) * (A_RECORD_BYTES / 2);
+        const auto rr_ = make_rsrc(recp, n > 0 ? A_RECORD_BYTES : 0);
+#pragma unroll
+        for (int p = 0; p < NREC; ++p)
+            rr(p) = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr_, (htid + 256 * p) * 16, 0, 0));
+        const auto rb_ = make_rsrc(beta + tok0, n > 0 ? ((n - 1) * H + 1) * 4 : 0);
+        RR[OB][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, static_cast<int>(lane * H) * 4, 0, 0));
+    };
+    if (!chain) {
+        fetch_kq(n_chunks - 1);
+        fetch_ad(n_chunks - 1);
+        fetch_tb(n_chunks - 1);
+    }
+
+    // Iteration c: the chain walks chunk c (none at c = n_chunks), the helpers prepare
+    // chunk c - 1 (none at c = 0).
+    for (int c = n_chunks; c >= 0; --c) {
+        const bool work = c < n_chunks;  // the chain has a chunk
+        const bool prep = c > 0;         // the helpers have one
+        const int cb = c & 1;            // K, Q buffer of chunk c; chunk c - 1 uses the other
+        const int nprep = chunk_len(c - 1);
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o, g = ln >> 4, m16 = ln & 15;
-        block_sync();  // the chunk after is done with every buffer
+        const uint16_t* Kw = Kc[cb];
+        const uint16_t* Qw = Qc[cb];
+        block_sync();  // D: chunk c is staged; the chain is done with chunk c + 1
 
-        // ======== stage, and each wave's prefix of log2 alpha over its 16 token rows
+        // ======== D -> A.  chain: D store, dZ = D gamma, dO~ operands, K dZ^T.  helpers: stage
+        // K, Q of chunk c - 1 (then load those of c - 2); log2-alpha prefix
+        f32x4 X4[4];
+        f32x4* dU = X4;  // chain
+        auto G16 = [&](int r) { return X4[r >> 2][r & 3]; };  // helpers: log2-decay prefix
+        bf16x8 oh[2], ol[2];
+        if (chain && work) {
+            float* dst = gck + ((static_cast<int64_t>(chunk0 + c) * H + h) * DV + iw + m16) * DK + 4 * g;
 #pragma unroll
-        for (int p = 0; p < NKQ; ++p) {
-            const int idx = tid + 256 * p;
-            *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = rk[p];
-            *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * KP + 8 * (idx % PPR)) = rq[p];
+            for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[jt];
+            const float gm = gam[16 * hw + m16];
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) R[jt] *= gm;  // dZ^T
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float* src = dOT + (16 * hw + m16) * XP + 32 * m + 4 * g;
+                split8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 16), oh[m], ol[m]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) dU[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                bf16x8 zh, zl;
+                split_stack(R[2 * m], R[2 * m + 1], zh, zl);
+                bf16x8 kf[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) kf[tt] = frag_st(Kw, KP, 16 * tt, 32 * m, ln);
+                issue_fence();
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    dU[tt] = mfma16(kf[tt], zh, dU[tt]);
+                    dU[tt] = mfma16(kf[tt], zl, dU[tt]);
+                }
+            }
         }
+        if (!chain && prep) {
 #pragma unroll
-        for (int p = 0; p < NREC; ++p) *reinterpret_cast<u32x4*>(record_piece_dst(T_hi, T_lo, tid + 256 * p)) = rr[p];
-        if (wave == 0) bs[ln] = rb;
-        float G16[16];
-        {
+            for (int p = 0; p < NKQ; ++p) {
+                const int idx = htid + 256 * p;
+                *reinterpret_cast<f32x4*>(Kc[cb ^ 1] + (idx / PPR) * KP + 8 * (idx % PPR)) = rk(p);
+                *reinterpret_cast<f32x4*>(Qc[cb ^ 1] + (idx / PPR) * KP + 8 * (idx % PPR)) = rq(p);
+            }
+            fetch_kq(c - 2);
             float run = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                if constexpr (GATE != GATE_NONE) run += 16 * wave + r < n ? __builtin_amdgcn_logf(ra[r]) : 0.f;
-                G16[r] = run;
+                if constexpr (GATE != GATE_NONE) run += 16 * hw + r < nprep ? __builtin_amdgcn_logf(ra(r)) : 0.f;
+                X4[r >> 2][r & 3] = run;
             }
-            Tot[wave * 64 + ln] = run;
+            Tot[hw * 64 + ln] = run;
         }
-        block_sync();
+        block_sync();  // A: the chain has read gamma and dO~^T; K, Q and the totals of c - 1 are in
 
-        // ======== G, dO~^T = (dO e^{G})^T, gamma; P = tril(Q K^T)
-        {
+        // ======== A -> B.  chain: dU += P^T dO~.  helpers: dO~^T = (dO e^{G})^T and gamma of c - 1
+        if (chain && work) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (st >= 2 && m == 0) continue;  // P^T[s][t] = 0 for t < s
+                    const bf16x8 ph = frag_tr_st(P_hi, CP, 16 * st, 32 * m, ln), pl = frag_tr_st(P_lo, CP, 16 * st, 32 * m, ln);
+                    dU[st] = mfma3(ph, pl, oh[m], ol[m], dU[st]);
+                }
+        }
+        if (!chain && prep) {
             float carry = 0.f;
 #pragma unroll
-            for (int w = 0; w < 3; ++w) carry += w < wave ? Tot[w * 64 + ln] : 0.f;
-            float* dst = dOT + ln * XP + 16 * wave;
+            for (int w = 0; w < 3; ++w) carry += w < hw ? Tot[w * 64 + ln] : 0.f;
+            float* dst = dOT + ln * XP + 16 * hw;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = rd[4 * p + e] * __builtin_amdgcn_exp2f(G16[4 * p + e] + carry);
+                for (int e = 0; e < 4; ++e) x[e] = rd(4 * p + e) * __builtin_amdgcn_exp2f(G16(4 * p + e) + carry);
                 *reinterpret_cast<f32x4*>(dst + 4 * p) = x;
             }
-            if (wave == 3) gam[ln] = __builtin_amdgcn_exp2f(G16[15] + carry);
+            if (hw == 3) gam[ln] = __builtin_amdgcn_exp2f(G16(15) + carry);
+            fetch_ad(c - 2);
         }
-        {
-            // D[s][t] = K Q^T tiles (s-tile st, t-tile = wave), kept where s <= t: lane holds four
-            // consecutive s of one t, written as P[t][s .. s+3]
-            const int tt = wave;
+        block_sync();  // B: the chain is done with P
+
+        // ======== B -> C.  chain: dYb = T^T dU, dY = beta dYb.  helpers: P of c - 1
+        f32x4 dY[4];
+        if (chain && work) {
+            bf16x8 uh[2], ul[2];
+            split_stack(dU[0], dU[1], uh[0], ul[0]);
+            split_stack(dU[2], dU[3], uh[1], ul[1]);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                uint2 wh = {0u, 0u}, wl = {0u, 0u};
-                if (st <= tt) {
+                dY[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (st >= 2 && m == 0) continue;  // T^T[s][t] = 0 for t < s
+                    const bf16x8 th = frag_tr_st(T_hi, CP, 16 * st, 32 * m, ln), tl = frag_tr_st(T_lo, CP, 16 * st, 32 * m, ln);
+                    dY[st] = mfma3(th, tl, uh[m], ul[m], dY[st]);
+                }
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * st + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dY[st][e] *= -b4[e];  // negated for the K^T product
+            }
+        }
+        if (!chain && prep) {
+            // P = tril(Q K^T) as D[s][t] = K Q^T tiles: the 10 tiles with s-tile <= t-tile,
+            // helper hw taking tiles hw, hw + 4, hw + 8; a lane holds four consecutive s of one
+            // t, written as P[t][s .. s+3]
+            const uint16_t* Kn = Kc[cb ^ 1];
+            const uint16_t* Qn = Qc[cb ^ 1];
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int e = hw + 4 * x;
+                if (e < 10) {
+                    const int tt = e < 1 ? 0 : e < 3 ? 1 : e < 6 ? 2 : 3;
+                    const int st = e - tt * (tt + 1) / 2;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int m = 0; m < NM; ++m)
-                        acc = mfma16(frag16(Kc, KP, 16 * st, 32 * m, ln), frag16(Qc, KP, 16 * tt, 32 * m, ln), acc);
+                        acc = mfma16(frag16(Kn, KP, 16 * st, 32 * m, ln), frag16(Qn, KP, 16 * tt, 32 * m, ln), acc);
                     const int t = 16 * tt + m16, s0 = 16 * st + 4 * g;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = s0 + e <= t ? acc[e] : 0.f;
+                    for (int q4 = 0; q4 < 4; ++q4) acc[q4] = s0 + q4 <= t ? acc[q4] : 0.f;
+                    uint2 wh, wl;
                     split4(acc, wh, wl);
+                    *reinterpret_cast<uint2*>(P_hi + (16 * tt + m16) * CP + 16 * st + 4 * g) = wh;
+                    *reinterpret_cast<uint2*>(P_lo + (16 * tt + m16) * CP + 16 * st + 4 * g) = wl;
                 }
-                *reinterpret_cast<uint2*>(P_hi + (16 * tt + m16) * CP + 16 * st + 4 * g) = wh;
-                *reinterpret_cast<uint2*>(P_lo + (16 * tt + m16) * CP + 16 * st + 4 * g) = wl;
             }
         }
-        fetch(c - 1);  // in flight while this chunk is computed
-        block_sync();
+        block_sync();  // C: the chain is done with T and beta
 
-        // ======== the chain of this wave's 16 value rows
-        {
-            float* dst = gck + ((static_cast<int64_t>(gc) * H + h) * DV + iw + m16) * DK + 4 * g;
+        // ======== C -> D.  chain: D^T <- dZ^T + Q^T dO~ - K^T dY.  helpers: T, beta of c - 1
+        if (chain && work) {
+            bf16x8 yh[2], yl[2];
+            split_stack(dY[0], dY[1], yh[0], yl[0]);
+            split_stack(dY[2], dY[3], yh[1], yl[1]);
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[jt];
-        }
-        const float gm = gam[16 * wave + m16];
+            for (int jt = 0; jt < NJ; ++jt) {
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) R[jt] *= gm;  // dZ^T
-        // dU = K dZ^T + P^T dO~  [t x i]
-        f32x4 dU[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) dU[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            bf16x8 zh, zl;
-            split_stack(R[2 * m], R[2 * m + 1], zh, zl);
-            bf16x8 kf[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) kf[tt] = frag_st(Kc, KP, 16 * tt, 32 * m, ln);
-            issue_fence();
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                dU[tt] = mfma16(kf[tt], zh, dU[tt]);
-                dU[tt] = mfma16(kf[tt], zl, dU[tt]);
+                for (int m = 0; m < 2; ++m) {
+                    const bf16x8 aq = frag_tr_st(Qw, KP, 16 * jt, 32 * m, ln);
+                    const bf16x8 ak = frag_tr_st(Kw, KP, 16 * jt, 32 * m, ln);
+                    R[jt] = mfma16(aq, oh[m], R[jt]);
+                    R[jt] = mfma16(aq, ol[m], R[jt]);
+                    R[jt] = mfma16(ak, yh[m], R[jt]);
+                    R[jt] = mfma16(ak, yl[m], R[jt]);
+                }
             }
         }
-        bf16x8 oh[2], ol[2];
+        if (!chain && prep) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const float* src = dOT + (16 * wave + m16) * XP + 32 * m + 4 * g;
-            split8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 16), oh[m], ol[m]);
-        }
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (st >= 2 && m == 0) continue;  // P^T[s][t] = 0 for t < s
-                const bf16x8 ph = frag_tr_st(P_hi, CP, 16 * st, 32 * m, ln), pl = frag_tr_st(P_lo, CP, 16 * st, 32 * m, ln);
-                dU[st] = mfma3(ph, pl, oh[m], ol[m], dU[st]);
-            }
-        // dYb = T^T dU, dY = beta (.) dYb (negated for the K^T product)
-        bf16x8 uh[2], ul[2];
-        split_stack(dU[0], dU[1], uh[0], ul[0]);
-        split_stack(dU[2], dU[3], uh[1], ul[1]);
-        f32x4 dY[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            dY[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                if (st >= 2 && m == 0) continue;  // T^T[s][t] = 0 for t < s
-                const bf16x8 th = frag_tr_st(T_hi, CP, 16 * st, 32 * m, ln), tl = frag_tr_st(T_lo, CP, 16 * st, 32 * m, ln);
-                dY[st] = mfma3(th, tl, uh[m], ul[m], dY[st]);
-            }
-            const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + 16 * st + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dY[st][e] *= -b4[e];
-        }
-        bf16x8 yh[2], yl[2];
-        split_stack(dY[0], dY[1], yh[0], yl[0]);
-        split_stack(dY[2], dY[3], yh[1], yl[1]);
-        // D^T <- dZ^T + Q^T dO~ - K^T dY
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const bf16x8 aq = frag_tr_st(Qc, KP, 16 * jt, 32 * m, ln);
-                const bf16x8 ak = frag_tr_st(Kc, KP, 16 * jt, 32 * m, ln);
-                R[jt] = mfma16(aq, oh[m], R[jt]);
-                R[jt] = mfma16(aq, ol[m], R[jt]);
-                R[jt] = mfma16(ak, yh[m], R[jt]);
-                R[jt] = mfma16(ak, yl[m], R[jt]);
-            }
+            for (int p = 0; p < NREC; ++p) *reinterpret_cast<f32x4*>(record_piece_dst(T_hi, T_lo, htid + 256 * p)) = rr(p);
+            if (hw == 0) bs[ln] = RR[OB][0];
+            fetch_tb(c - 2);
         }
     }
-    if (dS0) {
+    if (chain && dS0) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dS0 + s_base + 16 * jt) = R[jt];
     }
@@ -1010,7 +1075,7 @@ template <int DK, int DV, int GATE>
 static hipError_t launch_bwd_chunk_t(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream) {
     constexpr int NVB = DV / 64;
     const int64_t grid1 = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((bwd_state_scan_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid1)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_state_scan_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid1)), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.alpha, a.beta, a.dO,
                        a.dS_T, a.cu_seqlens, b.order, b.chunk_off, b.rec, b.flags, a.n_seq, a.n_tok, a.n_heads, b.gck,
                        a.dS0);
