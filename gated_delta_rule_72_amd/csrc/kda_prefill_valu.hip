@@ -280,10 +280,10 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const int h = u.head;
     if (range_flags) {
         static_assert(R <= 64 && 64 % R == 0, "a workgroup's rows lie in one block of 64");
+        // (no short-circuit: the flags are loaded together, not one after another)
         bool marked = false;
         for (int g = 0; g < flag_segs; ++g)
-            marked = marked ||
-                     range_flags[((static_cast<int64_t>(u.seq) * flag_segs + g) * H + h) * (DV / 64) + row0 / 64] != 0;
+            marked |= range_flags[((static_cast<int64_t>(u.seq) * flag_segs + g) * H + h) * (DV / 64) + row0 / 64] != 0;
         if (!marked) return;
     }
 

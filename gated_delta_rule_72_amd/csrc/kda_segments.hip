@@ -119,7 +119,7 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
     bool beyond = false;
     if (range_flags) {
         const int vb = (rblk * ROWS) / 64;  // the scan's block of 64 rows that holds these rows
-        for (int g = 0; g < G; ++g) beyond = beyond || range_flags[(seg_of(g) * H + h) * (DV / 64) + vb] != 0;
+        for (int g = 0; g < G; ++g) beyond |= range_flags[(seg_of(g) * H + h) * (DV / 64) + vb] != 0;
     }
     if (owner && S_T && !beyond)
         *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
