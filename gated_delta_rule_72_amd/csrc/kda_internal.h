@@ -69,6 +69,13 @@ inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32
     return g >= 8 ? g : 1;
 }
 
+// The bf16 prefill's scan in 32-token steps (kda_prefill_scan32.hip) for calls with one
+// scan per sequence: the A records of the 64-token chunk solve (their diagonal blocks),
+// the schedule (packed input) and the range marks as in the 64-token scan.
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32(const PrefillArgs& a, const int32_t* cu, const int32_t* order, const int32_t* chunk_off,
+                         const uint16_t* arec, int32_t* range_flags, hipStream_t stream);
+
 // Composes the segment states of the sequence-parallel prefill (kda_segments.hip).
 template <int DK, int DV>
 hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M,

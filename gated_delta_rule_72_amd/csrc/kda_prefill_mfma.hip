@@ -1031,8 +1031,8 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     // unwritten) are recomputed token by token; the pass returns at once for the others.
     // Without a gate nothing decays, so nothing can be marked.
     if (G == 1) {
-        if ((e = scan(scan_kernel<DK, DV, GATE>, NVB, a.v, a.alpha, a.S0, a.n_seq, a.S_T, 0, nullptr,
-                      GATE == GATE_NONE ? nullptr : rflags)) != hipSuccess)
+        if ((e = launch_scan32<DK, DV, GATE>(a, cu, order, chunk_off, arec, GATE == GATE_NONE ? nullptr : rflags,
+                                             stream)) != hipSuccess)
             return e;
         return GATE == GATE_NONE ? hipSuccess : launch_prefill_range_fixup(a, rflags, 1, stream);
     }

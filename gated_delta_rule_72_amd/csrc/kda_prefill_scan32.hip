@@ -1,0 +1,532 @@
+// kda_prefill_scan32.hip -- the S-dependent chunk products of the bf16 prefill
+// (value-channel, scalar or no gate) in steps of 32 tokens, with every staged
+// input double-buffered so that the staging of one step overlaps the matrix work
+// of the step before.
+//
+// The recurrence is that of page "Kimi (AI)", section "Kimi Delta Attention
+// (KDA)", in the chunk form of kda_prefill_mfma.hip, applied to half chunks: a
+// 64-token chunk's system (I + L) is lower triangular, so the two 32x32 diagonal
+// blocks of its solved record A = (I + L)^{-1} diag(beta) are exactly the solved
+// systems of its two halves.  The chunk solve therefore serves this scan
+// unchanged (blocks 0 and 2 of each record), and chunk numbering, workspaces and
+// range marks are those of the 64-token path.
+//
+// One workgroup of 8 waves per (sequence, head, block of 64 value rows), as in
+// scan_kernel:
+// - chain waves (0, 1) own 32 value rows each and keep S^T in fp32 accumulators;
+//   per step: Y = X - K S^T, U = A Y (A, Y as hi + lo), then
+//   S^T <- diag(gamma) (S^T + K^T U);
+// - out waves (2, 3): O^T = 2^G (S Q^T + U^T P^T) for the same rows, with P = tril(Q K^T)
+//   formed from the same K and Q fragments and kept in registers; O staged as bf16 rows
+//   and stored at the next step;
+// - loader waves (4-7) prepare the next step: K, Q and the A block into LDS, the
+//   log2-decay prefix G (8 token rows per wave, a lane per value row), X^T = V 2^{-G} and
+//   gamma; their loads are issued two steps ahead.
+// Two barriers per step.  B0: step s is staged.  Chain: Y, U, the U^T copy  --  out:
+// store O of s - 1, S Q^T and P  --  loaders: stage K, Q, A of s + 1, local prefix.  B1.
+// Chain: S^T update, the S copy for step s + 1  --  out: U^T P^T, 2^G, stage O  --
+// loaders: finish G, X^T, gamma of s + 1, load s + 3.
+// K, Q, A, X^T, G and gamma alternate between two buffers by step parity; the S copy,
+// the U^T copy and the O rows have one buffer each (written and read in alternate
+// phases).
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mfma.h"
+#include "kda_schedule.h"
+
+namespace kda {
+namespace {
+
+constexpr int H32 = 32;            // tokens per step
+template <int V>
+struct Parity {
+    static constexpr int value = V;
+};
+constexpr float RANGE32_LOG2 = 100.f;
+
+template <int DK>
+struct Scan32Smem {
+    static constexpr int KP = DK + PAD;       // K rows (bf16)
+    static constexpr int QP = DK + 2 * PAD;   // Q and S rows (bf16)
+    static constexpr int AP = H32 + PAD;      // A and U^T rows of 32 (bf16)
+    static constexpr int XP = H32 + 4;        // X^T rows (fp32)
+    static constexpr int GP = BV + 4;         // G rows (fp32)
+    static constexpr int OP = BV + PAD;       // O rows (bf16)
+    static constexpr int RK = H32 * KP * 2;
+    static constexpr int RQ = H32 * QP * 2;
+    static constexpr int RA = 2 * H32 * AP * 2;  // hi, lo
+    static constexpr int RX = BV * XP * 4;
+    static constexpr int RG = H32 * GP * 4;
+    static constexpr int RB = BV * 4;
+    static constexpr int RS = BV * QP * 2;
+    static constexpr int RU = 2 * BV * AP * 2;
+    static constexpr int RO = H32 * OP * 2;
+    static constexpr int RT = 2 * 4 * BV * 4;
+    static constexpr int TOTAL = 2 * (RK + RQ + RA + RX + RG + RB) + RS + RU + RO + RT;
+};
+
+template <int DK, int DV, int GATE>
+__global__ __launch_bounds__(512) void scan32_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
+    int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T,
+    int32_t* __restrict__ range_flags) {
+    using SM = Scan32Smem<DK>;
+    static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
+    static_assert(DK == 64 || DK == 128, "d_k");
+    constexpr int NVB = DV / BV;
+    constexpr int KP = SM::KP, QP = SM::QP, AP = SM::AP, XP = SM::XP, GP = SM::GP, OP = SM::OP;
+    constexpr int NJ = DK / 16;   // 16-row tiles of S^T along j
+    constexpr int NM = DK / 32;   // 32-wide reduction steps over j
+    constexpr int PPR = DK / 8;   // 16-byte pieces per row of q or k
+    constexpr int NKQ = H32 * PPR / 256;  // pieces of K (and of Q) per loader thread
+
+    __shared__ __align__(16) uint16_t Kb[2][H32 * KP];
+    __shared__ __align__(16) uint16_t Qb[2][H32 * QP];
+    __shared__ __align__(16) uint16_t Ab[2][2 * H32 * AP];  // hi rows, then lo rows
+    __shared__ __align__(16) float Xb[2][BV * XP];          // X^T [i][t]
+    __shared__ __align__(16) float Gb[2][H32 * GP];          // G [t][i] (log2 units)
+    __shared__ __align__(16) float gamb[2][BV];
+    __shared__ __align__(16) uint16_t Sx[BV * QP];           // S [i][j], bf16
+    __shared__ __align__(16) uint16_t Ux[2 * BV * AP];       // U^T [i][t] hi rows, then lo rows
+    __shared__ __align__(16) uint16_t Os[H32 * OP];          // O [t][i], bf16
+    __shared__ __align__(16) float Tot[2][BV][4];           // loader totals, per value row
+    __shared__ int beyond_s[4];
+
+    const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
+    if (!u.valid) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wave < 2;
+    const bool outw = wave == 2 || wave == 3;
+    const bool loader = wave >= 4;
+    const int rb = 32 * (wave & 1);  // first of the 32 value rows of a chain or out wave
+    const int lw = wave - 4;         // loader index: token rows 8 lw .. +7
+    const int64_t H = n_heads;
+    const int h = u.head;
+    const int i0 = u.vblk * BV;
+    const int64_t row_qk = H * DK, row_v = H * DV;
+    const int chunk0 = first_chunk(u.seq, n_seq, n_tok, chunk_off);
+    const int n_steps = static_cast<int>((u.t1 - u.t0 + H32 - 1) / H32);
+    // tokens of step s (0 outside the unit's steps)
+    auto step_len = [&](int s) {
+        return s < 0 ? 0
+                     : static_cast<int>(max<int64_t>(0, min<int64_t>(H32, u.t1 - (u.t0 + static_cast<int64_t>(s) * H32))));
+    };
+
+    // ---- one register array holds each role's long-lived values: the chain's S^T
+    // (at NJ ib + jt) and U^T packs (CU0 ..), the out waves' O^T accumulators and P
+    // operands (CU0 ..), the loaders' pieces of two steps (set x at LS0 + LSN x)
+    constexpr int CU0 = 2 * NJ;
+    constexpr int LK = 0, LQ = NKQ, LA = 2 * NKQ, LV = LA + 1, LL = LV + 2, LSN = LL + 2;
+    constexpr int LS0 = 0;
+    constexpr int RN = (CU0 + 8 > LS0 + 2 * LSN) ? CU0 + 8 : LS0 + 2 * LSN;
+    f32x4 R[RN];
+#pragma unroll
+    for (int x = 0; x < RN; ++x) R[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
+    if (chain && S0) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const float* src = S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
+        }
+    }
+    // negated bf16 copy of S as the B operand of K (-S)^T for the 32-wide j step m
+    auto neg_state = [&](int ib, int m) {
+        u32x4 w;
+        w[0] = pack_bf16(-R[ib * NJ + 2 * m][0], -R[ib * NJ + 2 * m][1]);
+        w[1] = pack_bf16(-R[ib * NJ + 2 * m][2], -R[ib * NJ + 2 * m][3]);
+        w[2] = pack_bf16(-R[ib * NJ + 2 * m + 1][0], -R[ib * NJ + 2 * m + 1][1]);
+        w[3] = pack_bf16(-R[ib * NJ + 2 * m + 1][2], -R[ib * NJ + 2 * m + 1][3]);
+        return __builtin_bit_cast(bf16x8, w);
+    };
+    // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
+    auto pack_state = [&](int ln) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * QP + 4 * (ln >> 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                uint2 w;
+                w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
+                w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
+                *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            }
+        }
+    };
+
+    // ---- a loader's loads of step s into register set x (a step past the end loads
+    // nothing: empty ranges).  Loader thread ht holds 16-byte pieces ht + 256 p of K and
+    // Q (row-major) and piece ht of the step's A block (32 rows of 4 pieces, hi then lo);
+    // V and alpha: token rows 8 lw .. +7, lane = value row.
+    auto fetch = [&](int s, int x) {
+        const int ht = tid - 256;
+        const int n = step_len(s);
+        const bool any = n > 0;
+        const int sc = any ? s : 0;
+        const int64_t tok0 = (u.t0 + static_cast<int64_t>(sc) * H32) * H + h;
+        const int64_t bqk = any ? ((n - 1) * row_qk + DK) * 2 : 0;
+        const auto rk_ = make_rsrc(k + tok0 * DK, bqk);
+        const auto rq_ = make_rsrc(q + tok0 * DK, bqk);
+        const int b0 = LS0 + LSN * x;
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int idx = ht + 256 * p;
+            const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
+            R[b0 + LK + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0));
+            R[b0 + LQ + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
+        }
+        // block 2 (s % 2) of the chunk's record: rows 0-31 x cols 0-31 for the first
+        // half, rows 32-63 x cols 32-63 for the second; each block is hi then lo
+        const uint16_t* blk = arec + (static_cast<int64_t>(chunk0 + sc / 2) * n_heads + h) * (A_RECORD_BYTES / 2) +
+                              (sc & 1) * 2 * (2 * A_BLOCK_ELEMS);
+        const auto ra_ = make_rsrc(blk, any ? 2 * A_BLOCK_ELEMS * 2 : 0);
+        R[b0 + LA] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, ht * 16, 0, 0));
+        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
+        const auto rl = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
+                        : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, any ? ((n - 1) * H + 1) * 4 : 0)
+                                              : make_rsrc(alpha, 0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int e = static_cast<int>((8 * lw + r) * row_v + lane);
+            // the bf16 bits, zero-extended (shifted into place where they are used)
+            R[b0 + LV + r / 4][r % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b16(rv, e * 2, 0, 0));
+            if constexpr (GATE != GATE_NONE) {
+                const int ea = GATE == GATE_CHANNEL ? e : static_cast<int>((8 * lw + r) * H);
+                R[b0 + LL + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ea * 4, 0, 0));
+            }
+        }
+    };
+    // stage K, Q and the A block of step s (set x) into buffer par
+    auto stage = [&](int x, int par, int ln) {
+        const int ht = ln + 64 * lw;
+        const int b0 = LS0 + LSN * x;
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int idx = ht + 256 * p;
+            *reinterpret_cast<f32x4*>(Kb[par] + (idx / PPR) * KP + 8 * (idx % PPR)) = R[b0 + LK + p];
+            *reinterpret_cast<f32x4*>(Qb[par] + (idx / PPR) * QP + 8 * (idx % PPR)) = R[b0 + LQ + p];
+        }
+        // piece ht: half ht / 128, row (ht / 4) % 32, columns 8 (ht % 4) ..
+        *reinterpret_cast<f32x4*>(Ab[par] + ((ht >> 7) * H32 + ((ht >> 2) & 31)) * AP + 8 * (ht & 3)) = R[b0 + LA];
+    };
+    // G in base-2 units (log2 alpha summed): each loader's inclusive prefix over its 8
+    // token rows, kept in the alpha registers, and V 2^{-prefix} in the V registers; the
+    // loader's total to Tot[par][lw].  Rows past the sequence end contribute 0.
+    auto local_scan = [&](int n, int x, int par, int ln) {
+        const int b0 = LS0 + LSN * x;
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (GATE != GATE_NONE)
+                run += 8 * lw + r < n ? __builtin_amdgcn_logf(R[b0 + LL + r / 4][r % 4]) : 0.f;
+            R[b0 + LL + r / 4][r % 4] = run;
+            R[b0 + LV + r / 4][r % 4] = __uint_as_float(__float_as_uint(R[b0 + LV + r / 4][r % 4]) << 16) *
+                                        __builtin_amdgcn_exp2f(-run);
+        }
+        Tot[par][ln][lw] = run;
+    };
+    bool beyond = false;  // wave 7: some step of some row of the unit is beyond the range
+    // after a barrier: add the totals of the loaders before, write G [t][i], X^T [i][t]
+    // and (wave 7) gamma
+    auto finalize = [&](int x, int par, int ln) {
+        const int b0 = LS0 + LSN * x;
+        const f32x4 tl = *reinterpret_cast<const f32x4*>(&Tot[par][ln][0]);
+        float carry = 0.f;
+#pragma unroll
+        for (int b = 0; b < 3; ++b) carry += b < lw ? tl[b] : 0.f;
+        const float ec = __builtin_amdgcn_exp2f(-carry);
+        float* xt = Xb[par] + ln * XP + 8 * lw;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] + carry;
+            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * ec;
+        }
+        if (lw == 3) {
+            const float tot = R[b0 + LL + 1][3] + carry;
+            gamb[par][ln] = __builtin_amdgcn_exp2f(tot);
+            // (also true for a NaN total)
+            beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= -RANGE32_LOG2)) != 0;
+        }
+    };
+    // staged O rows of a finished step -> global by the out waves, two 16-byte pieces
+    // per thread (n = 0: nothing is stored)
+    auto store_o = [&](int s, int ln) {
+        const int n = step_len(s);
+        const int64_t tc = u.t0 + static_cast<int64_t>(n > 0 ? s : 0) * H32;
+        const auto ro = make_rsrc(o + (tc * H + h) * DV + i0, n > 0 ? ((n - 1) * row_v + BV) * 2 : 0);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int idx = ln + 64 * (wave - 2) + 128 * p, t = idx >> 3, c = idx & 7;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(Os + t * OP + 8 * c);
+            __builtin_amdgcn_raw_buffer_store_b128(val, ro, static_cast<int>(t * row_v + 8 * c) * 2, 0, 0);
+        }
+    };
+
+    // one step; the parity (LDS buffers, register set) is a compile-time constant, so that
+    // the register array is indexed statically (a run-time index would put it in memory)
+    auto body = [&](int s, auto parity, auto role) __attribute__((always_inline)) {
+        constexpr int par = decltype(parity)::value;
+        constexpr int ROLE = decltype(role)::value;
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int ln = lane_o;
+        const int g = ln >> 4, m16 = ln & 15;
+        const uint16_t* Kc = Kb[par];
+        block_sync();  // B0: step s is staged
+
+        if constexpr (ROLE == 0) {
+            // ======== Y = X - K S^T, U = A Y for value rows i = rb + 16 ib + m16 (lane column);
+            // rows t = 16 tt + 4g + r of tile tt
+            f32x4 Y[2][2];
+            const float* XT = Xb[par];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    Y[ib][tt] = *reinterpret_cast<const f32x4*>(XT + (rb + 16 * ib + m16) * XP + 16 * tt + 4 * g);
+            bf16x8 kf[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) kf[0][tt] = frag_st(Kc, KP, 16 * tt, 0, ln);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m + 1 < NM) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) kf[(m + 1) & 1][tt] = frag_st(Kc, KP, 16 * tt, 32 * (m + 1), ln);
+                }
+                issue_fence();
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const bf16x8 sb = neg_state(ib, m);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
+                }
+            }
+            const uint16_t* Ah = Ab[par];
+            const uint16_t* Al = Ab[par] + H32 * AP;
+            bf16x8 af[2][2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                af[tt][0] = frag_st(Ah, AP, 16 * tt, 0, ln);
+                af[tt][1] = frag_st(Al, AP, 16 * tt, 0, ln);
+            }
+            issue_fence();
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                bf16x8 yh, yl;
+                split_stack(Y[ib][0], Y[ib][1], yh, yl);
+                f32x4 U[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    f32x4 acc = mfma16(af[tt][0], yh, f32x4{0.f, 0.f, 0.f, 0.f});
+                    acc = mfma16(af[tt][1], yh, acc);
+                    U[tt] = mfma16(af[tt][0], yl, acc);
+                }
+                // U^T packs (t = 4g .. +3 in words 0, 1; 16 + 4g .. +3 in words 2, 3) for the
+                // state update, and the U^T [i][t] copy for the out waves
+                bf16x8 uh, ul;
+                split_stack(U[0], U[1], uh, ul);
+                R[CU0 + ib] = __builtin_bit_cast(f32x4, uh);
+                R[CU0 + 2 + ib] = __builtin_bit_cast(f32x4, ul);
+                const int i = rb + 16 * ib + m16;
+                const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
+                *reinterpret_cast<uint2*>(Ux + i * AP + 4 * g) = uint2{wh[0], wh[1]};
+                *reinterpret_cast<uint2*>(Ux + i * AP + 16 + 4 * g) = uint2{wh[2], wh[3]};
+                *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 4 * g) = uint2{wl[0], wl[1]};
+                *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 16 + 4 * g) = uint2{wl[2], wl[3]};
+            }
+        } else if constexpr (ROLE == 1) {
+            // ======== the previous step's O out; O^T = S Q^T for value rows rb + 16 ib + 4g + r
+            // (tile rows) and tokens t = 16 tt + m16 (tile column)
+            store_o(s - 1, ln);  // (none before the first step)
+            // P = tril(Q K^T) as 16x16 tiles D[s][t] = K Q^T (a lane holds four consecutive s of
+            // one t): (t-tile, s-tile) = (0, 0), (1, 0), (1, 1) from the same K and Q fragments
+            const uint16_t* Qc = Qb[par];
+            f32x4 Oacc[2][2], Pt[3];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) Oacc[ib][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < 3; ++x) Pt[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                bf16x8 sf[2], qf[2], kf[2];
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) sf[ib] = frag16(Sx, QP, rb + 16 * ib, 32 * m, ln);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    qf[tt] = frag16(Qc, QP, 16 * tt, 32 * m, ln);
+                    kf[tt] = frag16(Kc, KP, 16 * tt, 32 * m, ln);
+                }
+                issue_fence();
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) Oacc[ib][tt] = mfma16(sf[ib], qf[tt], Oacc[ib][tt]);
+                Pt[0] = mfma16(kf[0], qf[0], Pt[0]);
+                Pt[1] = mfma16(kf[0], qf[1], Pt[1]);
+                Pt[2] = mfma16(kf[1], qf[1], Pt[2]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) R[CU0 + 2 * ib + tt] = Oacc[ib][tt];
+            // keep s <= t; then the stacked B operands of U^T P^T per t-tile (s-tile 0 for
+            // reduction indices 4g .., s-tile 1 for 16 + 4g ..; the tile (0, 1) is zero)
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int tt = x == 0 ? 0 : 1, st = x == 2 ? 1 : 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Pt[x][e] = 16 * st + 4 * g + e <= 16 * tt + m16 ? Pt[x][e] : 0.f;
+            }
+            bf16x8 ph, pl;
+            split_stack(Pt[0], f32x4{0.f, 0.f, 0.f, 0.f}, ph, pl);
+            R[CU0 + 4] = __builtin_bit_cast(f32x4, ph);
+            R[CU0 + 5] = __builtin_bit_cast(f32x4, pl);
+            split_stack(Pt[1], Pt[2], ph, pl);
+            R[CU0 + 6] = __builtin_bit_cast(f32x4, ph);
+            R[CU0 + 7] = __builtin_bit_cast(f32x4, pl);
+        } else {
+            // ======== the next step's K, Q, A and the local prefix of its log2-decays (past the
+            // last step: an empty step, which nothing reads; no branch keeps the compiler's
+            // counts of outstanding loads exact)
+            stage(par ^ 1, par ^ 1, ln);
+            local_scan(step_len(s + 1), par ^ 1, par ^ 1, ln);
+        }
+        block_sync();  // B1
+
+        if constexpr (ROLE == 0) {
+            // ======== S^T += K^T U, then the decay: the K^T operand (rows j, reduction t) from
+            // row-major K through the transposing read, tile jt + 1 read while jt computes
+            bf16x8 kt[2];
+            kt[0] = frag_tr_st(Kc, KP, 0, 0, ln);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) {
+                if (jt + 1 < NJ) kt[(jt + 1) & 1] = frag_tr_st(Kc, KP, 16 * (jt + 1), 0, ln);
+                issue_fence();
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + ib]), R[ib * NJ + jt]);
+                    R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + 2 + ib]), R[ib * NJ + jt]);
+                }
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                const float gm = gamb[par][rb + 16 * ib + m16];
+#pragma unroll
+                for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] *= gm;
+            }
+            pack_state(ln);
+        } else if constexpr (ROLE == 1) {
+            // ======== O^T += U^T P^T (U^T rows with the stacked reduction order of the P
+            // operands), then O = 2^{G} O staged as bf16 [t][i]
+            bf16x8 uh[2], ul[2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                uh[ib] = frag_st(Ux, AP, rb + 16 * ib, 0, ln);
+                ul[ib] = frag_st(Ux + BV * AP, AP, rb + 16 * ib, 0, ln);
+            }
+            issue_fence();
+            const float* Gc = Gb[par];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, R[CU0 + 4 + 2 * tt]);
+                const bf16x8 pl = __builtin_bit_cast(bf16x8, R[CU0 + 5 + 2 * tt]);
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    f32x4 acc = R[CU0 + 2 * ib + tt];
+                    acc = mfma16(uh[ib], ph, acc);
+                    acc = mfma16(ul[ib], ph, acc);
+                    acc = mfma16(uh[ib], pl, acc);
+                    const int t = 16 * tt + m16, i = rb + 16 * ib + 4 * g;
+                    const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gc + t * GP + i);
+                    uint2 w;
+                    w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[0]) * acc[0], __builtin_amdgcn_exp2f(g4[1]) * acc[1]);
+                    w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[2]) * acc[2], __builtin_amdgcn_exp2f(g4[3]) * acc[3]);
+                    *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
+                }
+            }
+        } else {
+            // ======== the next step's G, X^T and gamma; the loads of the step after the next
+            finalize(par ^ 1, par ^ 1, ln);
+            fetch(s + 3, par ^ 1);
+        }
+    };
+    // Each role runs its own copy of the loop (the same barriers in the same order), so
+    // the compiler counts each role's outstanding loads and stores on its own path: in one
+    // shared loop the role branches rejoin and it falls back to waiting for all of them,
+    // which would undo the loaders' loads two steps ahead.
+    auto run = [&](auto role) __attribute__((always_inline)) {
+        constexpr int ROLE = decltype(role)::value;
+        // prologue: step 0 staged, steps 1 and 2 in flight
+        if constexpr (ROLE == 2) {
+            fetch(0, 0);
+            fetch(1, 1);
+            stage(0, 0, lane);
+            local_scan(step_len(0), 0, 0, lane);
+        }
+        if constexpr (ROLE == 0) pack_state(lane);
+        block_sync();
+        if constexpr (ROLE == 2) {
+            finalize(0, 0, lane);
+            fetch(2, 0);
+        }
+        // an even number of steps, so that the loop body has no branch: a last step past the
+        // end is empty (K, X and U zero, gamma one) and leaves the state as it is
+        for (int s = 0; s < n_steps; s += 2) {
+            body(s, Parity<0>{}, role);
+            body(s + 1, Parity<1>{}, role);
+        }
+    };
+    if (chain) run(Parity<0>{});
+    else if (outw) run(Parity<1>{});
+    else run(Parity<2>{});
+    if (loader && lane == 0) beyond_s[lw] = beyond ? 1 : 0;
+    block_sync();
+    const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
+    if (outw) store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
+    if (range_flags && tid == 0) range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
+    if (S_T && chain && !unit_beyond) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[ib * NJ + jt];
+        }
+    }
+}
+
+}  // namespace
+
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32(const PrefillArgs& a, const int32_t* cu, const int32_t* order, const int32_t* chunk_off,
+                         const uint16_t* arec, int32_t* range_flags, hipStream_t stream) {
+    constexpr int NVB = DV / BV;
+    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
+    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu, cu ? order : nullptr, chunk_off, arec,
+                       a.n_seq, a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), a.S_T, range_flags);
+    return hipGetLastError();
+}
+
+#define KDA_SCAN32(DK, DV)                                                                                        \
+    template hipError_t launch_scan32<DK, DV, GATE_CHANNEL>(const PrefillArgs&, const int32_t*, const int32_t*, \
+                                                            const int32_t*, const uint16_t*, int32_t*, hipStream_t); \
+    template hipError_t launch_scan32<DK, DV, GATE_SCALAR>(const PrefillArgs&, const int32_t*, const int32_t*,  \
+                                                           const int32_t*, const uint16_t*, int32_t*, hipStream_t);  \
+    template hipError_t launch_scan32<DK, DV, GATE_NONE>(const PrefillArgs&, const int32_t*, const int32_t*,    \
+                                                         const int32_t*, const uint16_t*, int32_t*, hipStream_t);
+KDA_SCAN32(128, 128)
+KDA_SCAN32(64, 64)
+KDA_SCAN32(128, 64)
+KDA_SCAN32(64, 128)
+#undef KDA_SCAN32
+
+}  // namespace kda
