@@ -160,15 +160,20 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     };
 
     // ---- a loader's loads of step s into register set x (a step past the end loads
-    // nothing: empty ranges).  Loader thread ht holds 16-byte pieces ht + 256 p of K and
-    // Q (row-major) and piece ht of the step's A block (32 rows of 4 pieces, hi then lo);
-    // V and alpha: token rows 8 lw .. +7, lane = value row.
-    auto fetch = [&](int s, int x) {
+    // nothing: empty ranges), in two parts issued at different points: K, Q and the A block
+    // (loader thread ht holds 16-byte pieces ht + 256 p of K and Q, row-major, and piece ht
+    // of the step's A block: 32 rows of 4 pieces, hi then lo), then V and alpha (token rows
+    // 8 lw .. +7, lane = value row).
+    auto step_tok0 = [&](int s) {
+        const int sc = step_len(s) > 0 ? s : 0;
+        return (u.t0 + static_cast<int64_t>(sc) * H32) * H + h;
+    };
+    auto fetch_kqa = [&](int s, int x) {
         const int ht = tid - 256;
         const int n = step_len(s);
         const bool any = n > 0;
         const int sc = any ? s : 0;
-        const int64_t tok0 = (u.t0 + static_cast<int64_t>(sc) * H32) * H + h;
+        const int64_t tok0 = step_tok0(s);
         const int64_t bqk = any ? ((n - 1) * row_qk + DK) * 2 : 0;
         const auto rk_ = make_rsrc(k + tok0 * DK, bqk);
         const auto rq_ = make_rsrc(q + tok0 * DK, bqk);
@@ -186,6 +191,12 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                               (sc & 1) * 2 * (2 * A_BLOCK_ELEMS);
         const auto ra_ = make_rsrc(blk, any ? 2 * A_BLOCK_ELEMS * 2 : 0);
         R[b0 + LA] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, ht * 16, 0, 0));
+    };
+    auto fetch_vl = [&](int s, int x) {
+        const int n = step_len(s);
+        const bool any = n > 0;
+        const int64_t tok0 = step_tok0(s);
+        const int b0 = LS0 + LSN * x;
         const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
         const auto rl = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
                         : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, any ? ((n - 1) * H + 1) * 4 : 0)
@@ -200,6 +211,10 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 R[b0 + LL + r / 4][r % 4] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ea * 4, 0, 0));
             }
         }
+    };
+    auto fetch = [&](int s, int x) {
+        fetch_kqa(s, x);
+        fetch_vl(s, x);
     };
     // stage K, Q and the A block of step s (set x) into buffer par
     auto stage = [&](int x, int par, int ln) {
@@ -393,10 +408,11 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             R[CU0 + 6] = __builtin_bit_cast(f32x4, ph);
             R[CU0 + 7] = __builtin_bit_cast(f32x4, pl);
         } else {
-            // ======== the next step's K, Q, A and the local prefix of its log2-decays (past the
-            // last step: an empty step, which nothing reads; no branch keeps the compiler's
-            // counts of outstanding loads exact)
+            // ======== the next step's K, Q, A (then those loads of the step after the next) and
+            // the local prefix of its log2-decays (past the last step: an empty step, which
+            // nothing reads; no branch keeps the compiler's counts of outstanding loads exact)
             stage(par ^ 1, par ^ 1, ln);
+            fetch_kqa(s + 3, par ^ 1);
             local_scan(step_len(s + 1), par ^ 1, par ^ 1, ln);
         }
         block_sync();  // B1
@@ -453,9 +469,10 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 }
             }
         } else {
-            // ======== the next step's G, X^T and gamma; the loads of the step after the next
+            // ======== the next step's G, X^T and gamma; then the V and alpha loads of the step
+            // after the next
             finalize(par ^ 1, par ^ 1, ln);
-            fetch(s + 3, par ^ 1);
+            fetch_vl(s + 3, par ^ 1);
         }
     };
     // Each role runs its own copy of the loop (the same barriers in the same order), so
