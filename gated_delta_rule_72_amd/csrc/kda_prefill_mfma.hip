@@ -114,7 +114,9 @@ __global__ __launch_bounds__(256) void segment_cu_kernel(const int32_t* __restri
 // below 2^-20 marks every row block of its (sequence, head) in range_flags (n_vblk
 // blocks per head): the backward divides by beta there and leaves such units to
 // its token-recurrent pass.
-template <int DK, bool STORE_T = false>
+// HALVES (the 32-token scan): only the two diagonal 32x32 blocks of each record, the
+// solved systems of the chunk's two halves; block 1 is neither formed nor written.
+template <int DK, bool STORE_T = false, bool HALVES = false>
 __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_off, int n_seq, int n_tok, int n_heads, int max_chunks,
@@ -214,24 +216,26 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
         wave_lds_sync();
         solve_diag_blocks(Lf, lane, x);
     } else if (wave == 1) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int half = 0; half < DK / 64; ++half) {
-            bf16x8 fa[4], fb[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                fa[kk] = frag(Kc, KP, 32, 64 * half + 16 * kk, lane);
-                fb[kk] = frag(Kc, KP, 0, 64 * half + 16 * kk, lane);
+        if constexpr (!HALVES) {  // L (32..63, 0..31) only feeds the 32-row level
+            f32x16 acc = {};
+    #pragma unroll
+            for (int half = 0; half < DK / 64; ++half) {
+                bf16x8 fa[4], fb[4];
+    #pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    fa[kk] = frag(Kc, KP, 32, 64 * half + 16 * kk, lane);
+                    fb[kk] = frag(Kc, KP, 0, 64 * half + 16 * kk, lane);
+                }
+                issue_fence();
+    #pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma(fa[kk], fb[kk], acc);
             }
-            issue_fence();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma(fa[kk], fb[kk], acc);
+            f32x4 b4[4];
+    #pragma unroll
+            for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (lane >> 5));
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) Lf[(32 + acc_row(r, lane)) * LP + (lane & 31)] = b4[r >> 2][r & 3] * acc[r];
         }
-        f32x4 b4[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) b4[rb] = *reinterpret_cast<const f32x4*>(bs + 32 + 8 * rb + 4 * (lane >> 5));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Lf[(32 + acc_row(r, lane)) * LP + (lane & 31)] = b4[r >> 2][r & 3] * acc[r];
     } else {
         const int R = wave == 2 ? 16 : 48, Cc = R - 16;
         f32x4 d = {};
@@ -248,12 +252,12 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) Lf[(R + 4 * g16 + r) * LP + Cc + m16] = b4[r] * d[r];
     }
-    assemble_inverse(Xs, Lf, Rtmp, x, wave, lane);
+    assemble_inverse<HALVES>(Xs, Lf, Rtmp, x, wave, lane);
 
     // ---- A = X diag(beta) -> the record (STORE_T: X itself -> the second record)
     const int64_t rec_off = (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
-    write_solve_record<true>(arec + rec_off, Xs, bs, tid);
-    if constexpr (STORE_T) write_solve_record<false>(trec + rec_off, Xs, bs, tid);
+    write_solve_record<true, HALVES>(arec + rec_off, Xs, bs, tid);
+    if constexpr (STORE_T) write_solve_record<false, HALVES>(trec + rec_off, Xs, bs, tid);
     block_sync();  // X, read above, shares its space with the next item's K
     }
 }
@@ -1013,9 +1017,15 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         const int64_t grid = std::min<int64_t>(mc * a.n_heads, 4 * static_cast<int64_t>(n_cu));
-        hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok, a.n_heads,
-                           static_cast<int>(mc), arec, nullptr, nullptr, 0);
+        // one scan per sequence (the 32-token scan) needs only the records' diagonal blocks
+        if (G == 1)
+            hipLaunchKernelGGL((chunk_solve_kernel<DK, false, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                               stream, static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok,
+                               a.n_heads, static_cast<int>(mc), arec, nullptr, nullptr, 0);
+        else
+            hipLaunchKernelGGL((chunk_solve_kernel<DK>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                               static_cast<const uint16_t*>(a.k), a.beta, cu, chunk_off, nseq_eff, a.n_tok, a.n_heads,
+                               static_cast<int>(mc), arec, nullptr, nullptr, 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     auto scan = [&](auto kern, int nvb, const void* vv, const float* al, const float* s0, int nsq, float* st,

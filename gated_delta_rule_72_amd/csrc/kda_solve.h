@@ -66,7 +66,10 @@ __device__ __forceinline__ void solve_diag_blocks(const float* Lf, int lane, flo
 // makes it so): X = (I + L)^{-1} into Xs (pitch LP), from wave 0's diagonal-block
 // inverses x.  Xs may alias storage that is dead once L is formed; Rtmp (32 rows
 // of pitch SOLVE_RP) may alias rows 0-16 of Lf, which only the 16-row level reads.
+// HALVES: only the two diagonal 32x32 blocks (the inverses of the two 32-token halves'
+// systems); the 32-row level, and L's block (32..63, 0..31) it reads, are left out.
 // Ends with a barrier.
+template <bool HALVES = false>
 __device__ __forceinline__ void assemble_inverse(float* Xs, const float* Lf, float* Rtmp, const float (&x)[16],
                                                  int wave, int lane) {
     const int g16 = lane >> 4, m16 = lane & 15;
@@ -102,6 +105,7 @@ __device__ __forceinline__ void assemble_inverse(float* Xs, const float* Lf, flo
         for (int r = 0; r < 4; ++r) Xs[(R + 4 * g16 + r) * LP + Cc + m16] = -z[r];
     }
     block_sync();
+    if constexpr (HALVES) return;
 
     // ---- 32-row level, first half: Y2 = L[32:64, 0:32] X[0:32, 0:32], one 16x16
     // quadrant per wave
@@ -144,11 +148,13 @@ __device__ __forceinline__ void assemble_inverse(float* Xs, const float* Lf, flo
 
 // X (SCALE_BETA: X diag(beta)) -> the solved record at rec, by all 256 threads.
 // Item = (block, row, 8-column piece); entries above the diagonal (never
-// written in Xs) are selected away.
-template <bool SCALE_BETA>
+// written in Xs) are selected away.  HALVES: blocks 0 and 2 only (block 1 is
+// left unwritten).
+template <bool SCALE_BETA, bool HALVES = false>
 __device__ __forceinline__ void write_solve_record(uint16_t* rec, const float* Xs, const float* bs, int tid) {
-    for (int item = tid; item < 3 * 32 * 4; item += 256) {
-        const int blk = item >> 7, row = (item >> 2) & 31, c8 = 8 * (item & 3);
+    constexpr int NB = HALVES ? 2 : 3;
+    for (int item = tid; item < NB * 32 * 4; item += 256) {
+        const int blk = HALVES ? 2 * (item >> 7) : item >> 7, row = (item >> 2) & 31, c8 = 8 * (item & 3);
         const int t = (blk == 0 ? 0 : 32) + row, s0 = (blk == 2 ? 32 : 0) + c8;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
