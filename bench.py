@@ -30,6 +30,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-c
                                              key-channel-gate prefill calls on the batched
                                              workload; varlen = 2 varlen-workload prefill calls)
        python bench.py --summarize DIR      (print the per-kernel table of a rocprofv3 run)
+       python bench.py --write-traffic DIR  (profiles/traffic.json from the six --traffic-probe
+                                             counter runs under DIR: pmc_<probe>_<counter>/)
 """
 from __future__ import annotations
 
@@ -65,7 +67,6 @@ def log(*a):
 def measured_traffic(kernel):
     """HBM bytes per launch recorded in profiles/traffic.json, or None when the
     kernel's sources changed since the counters were taken."""
-    import hashlib
     import json
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -73,11 +74,7 @@ def measured_traffic(kernel):
     rec = json.load(open(path)).get(kernel)
     if not rec:
         return None
-    m = hashlib.sha256()
-    for f in rec["sources"]:
-        with open(os.path.join(ROOT, "gated_delta_rule_72_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    if m.hexdigest()[:16] != rec["source_sha256"]:
+    if source_hash(rec["sources"]) != rec["source_sha256"]:
         return None
     return int(1024 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]))
 
@@ -96,6 +93,7 @@ def parse():
     p.add_argument("--workloads-only", action="store_true")
     p.add_argument("--traffic-probe", nargs="?", const="main", default=None, choices=("main", "extra", "varlen"))
     p.add_argument("--summarize", default=None)
+    p.add_argument("--write-traffic", default=None, metavar="DIR")
     return p.parse_args()
 
 
@@ -187,6 +185,80 @@ def summarize(path):
             print(f"{'kernel':70s} {'counter':>14s} {'dispatches':>10s} {'per_dispatch':>16s}")
             for name, cn, n, val in crow:
                 print(f"{name[:70]:70s} {cn:>14s} {n:10d} {val:16.1f}")
+
+
+TRAFFIC_PREFILL_SOURCES = ["kda_prefill_mfma.hip", "kda_prefill_scan32.hip", "kda_mfma.h", "kda_solve.h",
+                           "kda_device.h", "kda_schedule.h", "kda_internal.h", "kda_prefill_valu.hip"]
+# call -> (probe, kernel-name pieces, one kernel per piece; None = every kda kernel of the probe, sources)
+TRAFFIC_CALLS = {
+    "prefill": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 0>",
+                         "prefill_staged_kernel<unsigned short, 128, 128, 0, 64, 8, false>"], TRAFFIC_PREFILL_SOURCES),
+    "prefill_scalar_gate": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 1>",
+                                     "prefill_staged_kernel<unsigned short, 128, 128, 1, 64, 8, false>"],
+                            TRAFFIC_PREFILL_SOURCES),
+    "decode": ("main", ["decode_step_kernel<unsigned short, 128, 128, 0>"], ["kda_decode.hip", "kda_device.h"]),
+    "backward": ("extra", ["chunk_solve_kernel<128, true, false>", "scan_kernel<128, 128, 0, true, true>",
+                           "bwd_state_scan_kernel<128, 128, 0>", "bwd_chunk_grad_kernel<128, 128, 0>",
+                           "backward_kernel<unsigned short, 128, 128, 0>"],
+                 TRAFFIC_PREFILL_SOURCES + ["kda_backward.hip", "kda_backward_chunk.hip"]),
+    "key_gate": ("extra", ["keygate_solve_kernel<128>", "keygate_scan_kernel<128, 128>",
+                           "prefill_staged_kernel<unsigned short, 128, 128, 3, 64, 8, false>"],
+                 ["kda_prefill_keygate.hip", "kda_mfma.h", "kda_solve.h", "kda_device.h", "kda_schedule.h",
+                  "kda_prefill_valu.hip"]),
+    "varlen_prefill": ("varlen", None, TRAFFIC_PREFILL_SOURCES + ["kda_schedule.hip", "kda_segments.hip"]),
+}
+
+
+def source_hash(files):
+    import hashlib
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_delta_rule_72_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def write_traffic(base):
+    """profiles/traffic.json from the six counter runs gpurun_out-style under `base`
+    (pmc_{main,extra,varlen}_{FETCH_SIZE,WRITE_SIZE}/p_results.db): per call, the KiB per
+    dispatch of its kernels summed, with the scale that makes the 1 GiB copy read and write
+    1 GiB."""
+    import json
+    import sqlite3
+
+    def per(mode, counter):
+        con = sqlite3.connect(os.path.join(base, f"pmc_{mode}_{counter}", "p_results.db"))
+        rows = con.execute("select name, sum(counter_value) / count(distinct dispatch_id) from pmc_events "
+                           "where counter_name = ? group by name", (counter,)).fetchall()
+        return dict(rows)
+
+    data = {m: (per(m, "FETCH_SIZE"), per(m, "WRITE_SIZE")) for m in ("main", "extra", "varlen")}
+    copy = "__amd_rocclr_copyBuffer"
+    fs, ws = 1048576.0 / data["main"][0][copy], 1048576.0 / data["main"][1][copy]
+    out = {"_doc": "HBM bytes per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed "
+                   "over the kernels of one call), scaled by the calibration of a 1 GiB copy; valid only while "
+                   "the kernel sources hash to source_sha256. Written by bench.py --write-traffic from the runs "
+                   "in traffic_kda_calls.md."}
+    for call, (mode, pieces, src) in TRAFFIC_CALLS.items():
+        f, w = data[mode]
+        if pieces is None:
+            names = [k for k in f if "kda::" in k]
+        else:
+            names = []
+            for piece in pieces:
+                ks = [k for k in f if piece + "(" in k]
+                if len(ks) != 1:
+                    sys.exit(f"{call}: {len(ks)} kernels match {piece!r}")
+                names.append(ks[0])
+        out[call] = dict(sources=src, source_sha256=source_hash(src), probe=mode,
+                         kernels=[n.split("(")[0].replace("void ", "").replace("kda::", "") for n in names],
+                         fetch_kib=round(sum(f[n] for n in names), 1), write_kib=round(sum(w.get(n, 0.0) for n in names), 1),
+                         fetch_scale=round(fs, 4), write_scale=round(ws, 4))
+        r, wr = 1024 * out[call]["fetch_kib"] * fs, 1024 * out[call]["write_kib"] * ws
+        print(f"{call:22s} read {r / 1e9:7.3f} GB  write {wr / 1e9:7.3f} GB  total {(r + wr) / 1e9:7.3f} GB")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
 
 
 def cpu_model():
@@ -301,7 +373,7 @@ def bench_prefill(args, torch, kda, I, gate="channel"):
         roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=round(achieved / HBM_PEAK_GBS, 4),
                       traffic=measured_traffic("prefill" if gate == "channel" else "prefill_scalar_gate"),
-                      kernel="prefill call: chunk_solve_kernel + scan_kernel",
+                      kernel="prefill call: chunk_solve_kernel (half-chunk blocks) + scan32_kernel",
                       alg_bytes_per_launch=alg_bytes,
                       mfma_nominal_tflops=round(nominal_tflops, 1),
                       mfma_nominal_frac=round(nominal_tflops / BF16_PEAK_TFLOPS, 4)),
@@ -733,6 +805,9 @@ def main():
         return
     if args.traffic_probe:
         traffic_probe(args.traffic_probe)
+        return
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "

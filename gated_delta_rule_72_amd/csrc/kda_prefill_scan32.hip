@@ -15,7 +15,9 @@
 // scan_kernel:
 // - chain waves (0, 1) own 32 value rows each and keep S^T in fp32 accumulators;
 //   per step: Y = X - K S^T, U = A Y (A, Y as hi + lo), then
-//   S^T <- diag(gamma) (S^T + K^T U);
+//   S^T <- diag(gamma) (S^T + K^T U).  They form -Y = K S^T - X from the staged -X and
+//   the bf16 copy of S that the S update already packed, and U = (-A)(-Y) from the
+//   staged -A, so no sign flips sit on their path;
 // - out waves (2, 3): O^T = 2^G (S Q^T + U^T P^T) for the same rows, with P = tril(Q K^T)
 //   formed from the same K and Q fragments and kept in registers; O staged as bf16 rows
 //   and stored at the next step;
@@ -117,12 +119,15 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     };
 
     // ---- one register array holds each role's long-lived values: the chain's S^T
-    // (at NJ ib + jt) and U^T packs (CU0 ..), the out waves' O^T accumulators and P
-    // operands (CU0 ..), the loaders' pieces of two steps (set x at LS0 + LSN x)
+    // (at NJ ib + jt), U^T packs (CU0 ..) and bf16 copy of S (SP0 ..), the out waves' O^T
+    // accumulators and P operands (CU0 ..), the loaders' pieces of two steps (set x at
+    // LS0 + LSN x)
     constexpr int CU0 = 2 * NJ;
+    constexpr int SP0 = CU0 + 4;
     constexpr int LK = 0, LQ = NKQ, LA = 2 * NKQ, LV = LA + 1, LL = LV + 2, LSN = LL + 2;
     constexpr int LS0 = 0;
-    constexpr int RN = (CU0 + 8 > LS0 + 2 * LSN) ? CU0 + 8 : LS0 + 2 * LSN;
+    constexpr int RC = (CU0 + 8 > SP0 + NJ) ? CU0 + 8 : SP0 + NJ;
+    constexpr int RN = (RC > LS0 + 2 * LSN) ? RC : LS0 + 2 * LSN;
     f32x4 R[RN];
 #pragma unroll
     for (int x = 0; x < RN; ++x) R[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -135,16 +140,9 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
         }
     }
-    // negated bf16 copy of S as the B operand of K (-S)^T for the 32-wide j step m
-    auto neg_state = [&](int ib, int m) {
-        u32x4 w;
-        w[0] = pack_bf16(-R[ib * NJ + 2 * m][0], -R[ib * NJ + 2 * m][1]);
-        w[1] = pack_bf16(-R[ib * NJ + 2 * m][2], -R[ib * NJ + 2 * m][3]);
-        w[2] = pack_bf16(-R[ib * NJ + 2 * m + 1][0], -R[ib * NJ + 2 * m + 1][1]);
-        w[3] = pack_bf16(-R[ib * NJ + 2 * m + 1][2], -R[ib * NJ + 2 * m + 1][3]);
-        return __builtin_bit_cast(bf16x8, w);
-    };
-    // S [i][j] for the out waves: lane holds j = 16 jt + 4g .. +3 of row i
+    // S [i][j] as bf16 for the out waves (lane holds j = 16 jt + 4g .. +3 of row i), and the
+    // same words kept as the B operands of K S^T: for the 32-wide j step m the stacked pair
+    // of tiles 2m, 2m + 1 is R[SP0 + (NJ / 2) ib + m]
     auto pack_state = [&](int ln) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
@@ -155,6 +153,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
                 w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
                 *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+                R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(w.x);
+                R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(w.y);
             }
         }
     };
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         fetch_kqa(s, x);
         fetch_vl(s, x);
     };
-    // stage K, Q and the A block of step s (set x) into buffer par
+    // stage K, Q and the A block of step s (set x) into buffer par, A with its sign flipped
     auto stage = [&](int x, int par, int ln) {
         const int ht = ln + 64 * lw;
         const int b0 = LS0 + LSN * x;
@@ -227,7 +227,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             *reinterpret_cast<f32x4*>(Qb[par] + (idx / PPR) * QP + 8 * (idx % PPR)) = R[b0 + LQ + p];
         }
         // piece ht: half ht / 128, row (ht / 4) % 32, columns 8 (ht % 4) ..
-        *reinterpret_cast<f32x4*>(Ab[par] + ((ht >> 7) * H32 + ((ht >> 2) & 31)) * AP + 8 * (ht & 3)) = R[b0 + LA];
+        const u32x4 na = __builtin_bit_cast(u32x4, R[b0 + LA]) ^ 0x80008000u;
+        *reinterpret_cast<u32x4*>(Ab[par] + ((ht >> 7) * H32 + ((ht >> 2) & 31)) * AP + 8 * (ht & 3)) = na;
     };
     // G in base-2 units (log2 alpha summed): each loader's inclusive prefix over its 8
     // token rows, kept in the alpha registers, and V 2^{-prefix} in the V registers; the
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         Tot[par][ln][lw] = run;
     };
     bool beyond = false;  // wave 7: some step of some row of the unit is beyond the range
-    // after a barrier: add the totals of the loaders before, write G [t][i], X^T [i][t]
+    // after a barrier: add the totals of the loaders before, write G [t][i], -X^T [i][t]
     // and (wave 7) gamma
     auto finalize = [&](int x, int par, int ln) {
         const int b0 = LS0 + LSN * x;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] + carry;
-            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * ec;
+            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * -ec;
         }
         if (lw == 3) {
             const float tot = R[b0 + LL + 1][3] + carry;
@@ -296,8 +297,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         block_sync();  // B0: step s is staged
 
         if constexpr (ROLE == 0) {
-            // ======== Y = X - K S^T, U = A Y for value rows i = rb + 16 ib + m16 (lane column);
-            // rows t = 16 tt + 4g + r of tile tt
+            // ======== -Y = K S^T - X, U = (-A)(-Y) for value rows i = rb + 16 ib + m16 (lane
+            // column); rows t = 16 tt + 4g + r of tile tt
             f32x4 Y[2][2];
             const float* XT = Xb[par];
 #pragma unroll
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 issue_fence();
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
-                    const bf16x8 sb = neg_state(ib, m);
+                    const bf16x8 sb = __builtin_bit_cast(bf16x8, R[SP0 + (NJ / 2) * ib + m]);
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
                 }
