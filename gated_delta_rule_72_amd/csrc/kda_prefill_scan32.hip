@@ -22,8 +22,8 @@
 //   formed from the same K and Q fragments and kept in registers; O staged as bf16 rows
 //   and stored at the next step;
 // - loader waves (4-7) prepare the next step: K, Q and the A block into LDS, the
-//   log2-decay prefix G (8 token rows per wave, a lane per value row), X^T = V 2^{-G} and
-//   gamma; their loads are issued two steps ahead.
+//   decay 2^G as prefix products of the gates (8 token rows per wave, a lane per value
+//   row), X^T = V 2^{-G} and gamma; their loads are issued two steps ahead.
 // Two barriers per step.  B0: step s is staged.  Chain: Y, U, the U^T copy  --  out:
 // store O of s - 1, S Q^T and P  --  loaders: stage K, Q, A of s + 1, local prefix.  B1.
 // Chain: S^T update, the S copy for step s + 1  --  out: U^T P^T, 2^G, stage O  --
@@ -44,7 +44,7 @@ template <int V>
 struct Parity {
     static constexpr int value = V;
 };
-constexpr float RANGE32_LOG2 = 100.f;
+constexpr float RANGE32_MIN = 0x1p-100f;  // least total decay of a step on the factored form
 
 template <int DK>
 struct Scan32Smem {
@@ -52,7 +52,7 @@ struct Scan32Smem {
     static constexpr int QP = DK + 2 * PAD;   // Q and S rows (bf16)
     static constexpr int AP = H32 + PAD;      // A and U^T rows of 32 (bf16)
     static constexpr int XP = H32 + 4;        // X^T rows (fp32)
-    static constexpr int GP = BV + 4;         // G rows (fp32)
+    static constexpr int GP = BV + 4;         // 2^G rows (fp32)
     static constexpr int OP = BV + PAD;       // O rows (bf16)
     static constexpr int RK = H32 * KP * 2;
     static constexpr int RQ = H32 * QP * 2;
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     __shared__ __align__(16) uint16_t Qb[2][H32 * QP];
     __shared__ __align__(16) uint16_t Ab[2][2 * H32 * AP];  // hi rows, then lo rows
     __shared__ __align__(16) float Xb[2][BV * XP];          // X^T [i][t]
-    __shared__ __align__(16) float Gb[2][H32 * GP];          // G [t][i] (log2 units)
+    __shared__ __align__(16) float Gb[2][H32 * GP];          // 2^G [t][i]
     __shared__ __align__(16) float gamb[2][BV];
     __shared__ __align__(16) uint16_t Sx[BV * QP];           // S [i][j], bf16
     __shared__ __align__(16) uint16_t Ux[2 * BV * AP];       // U^T [i][t] hi rows, then lo rows
@@ -230,44 +230,52 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         const u32x4 na = __builtin_bit_cast(u32x4, R[b0 + LA]) ^ 0x80008000u;
         *reinterpret_cast<u32x4*>(Ab[par] + ((ht >> 7) * H32 + ((ht >> 2) & 31)) * AP + 8 * (ht & 3)) = na;
     };
-    // G in base-2 units (log2 alpha summed): each loader's inclusive prefix over its 8
-    // token rows, kept in the alpha registers, and V 2^{-prefix} in the V registers; the
-    // loader's total to Tot[par][lw].  Rows past the sequence end contribute 0.
+    // The decay as products (no logarithms): each loader's inclusive prefix product of the
+    // gates over its 8 token rows, in the alpha registers, and V over that product in the V
+    // registers (one reciprocal, then suffix products); the loader's total to Tot[par][lw].
+    // Rows past the sequence end contribute 1.  Within a step nothing underflows: a step
+    // whose total decay is below 2^-100 marks the unit for the recurrent pass, and every
+    // prefix is at least the total.
     auto local_scan = [&](int n, int x, int par, int ln) {
         const int b0 = LS0 + LSN * x;
-        float run = 0.f;
+        float a[8];
+        float run = 1.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if constexpr (GATE != GATE_NONE)
-                run += 8 * lw + r < n ? __builtin_amdgcn_logf(R[b0 + LL + r / 4][r % 4]) : 0.f;
+            a[r] = GATE != GATE_NONE && 8 * lw + r < n ? R[b0 + LL + r / 4][r % 4] : 1.f;
+            run *= a[r];
             R[b0 + LL + r / 4][r % 4] = run;
-            R[b0 + LV + r / 4][r % 4] = __uint_as_float(__float_as_uint(R[b0 + LV + r / 4][r % 4]) << 16) *
-                                        __builtin_amdgcn_exp2f(-run);
+        }
+        float inv = __builtin_amdgcn_rcpf(run);  // 1 / prefix of row 7, then of rows 6, 5, ..
+#pragma unroll
+        for (int r = 7; r >= 0; --r) {
+            R[b0 + LV + r / 4][r % 4] = __uint_as_float(__float_as_uint(R[b0 + LV + r / 4][r % 4]) << 16) * inv;
+            inv *= a[r];
         }
         Tot[par][ln][lw] = run;
     };
     bool beyond = false;  // wave 7: some step of some row of the unit is beyond the range
-    // after a barrier: add the totals of the loaders before, write G [t][i], -X^T [i][t]
-    // and (wave 7) gamma
+    // after a barrier: multiply in the totals of the loaders before, write 2^G [t][i],
+    // -X^T [i][t] and (wave 7) gamma
     auto finalize = [&](int x, int par, int ln) {
         const int b0 = LS0 + LSN * x;
         const f32x4 tl = *reinterpret_cast<const f32x4*>(&Tot[par][ln][0]);
-        float carry = 0.f;
+        float carry = 1.f;
 #pragma unroll
-        for (int b = 0; b < 3; ++b) carry += b < lw ? tl[b] : 0.f;
-        const float ec = __builtin_amdgcn_exp2f(-carry);
+        for (int b = 0; b < 3; ++b) carry *= b < lw ? tl[b] : 1.f;
+        const float nic = -__builtin_amdgcn_rcpf(carry);
         float* xt = Xb[par] + ln * XP + 8 * lw;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] + carry;
-            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * -ec;
+            for (int e = 0; e < 4; ++e) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] * carry;
+            *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * nic;
         }
         if (lw == 3) {
-            const float tot = R[b0 + LL + 1][3] + carry;
-            gamb[par][ln] = __builtin_amdgcn_exp2f(tot);
+            const float tot = R[b0 + LL + 1][3] * carry;
+            gamb[par][ln] = tot;
             // (also true for a NaN total)
-            beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= -RANGE32_LOG2)) != 0;
+            beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= RANGE32_MIN)) != 0;
         }
     };
     // staged O rows of a finished step -> global by the out waves, two 16-byte pieces
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             R[CU0 + 7] = __builtin_bit_cast(f32x4, pl);
         } else {
             // ======== the next step's K, Q, A (then those loads of the step after the next) and
-            // the local prefix of its log2-decays (past the last step: an empty step, which
+            // the local prefix products of its gates (past the last step: an empty step, which
             // nothing reads; no branch keeps the compiler's counts of outstanding loads exact)
             stage(par ^ 1, par ^ 1, ln);
             fetch_kqa(s + 3, par ^ 1);
@@ -464,8 +472,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     const int t = 16 * tt + m16, i = rb + 16 * ib + 4 * g;
                     const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gc + t * GP + i);
                     uint2 w;
-                    w.x = pack_bf16(__builtin_amdgcn_exp2f(g4[0]) * acc[0], __builtin_amdgcn_exp2f(g4[1]) * acc[1]);
-                    w.y = pack_bf16(__builtin_amdgcn_exp2f(g4[2]) * acc[2], __builtin_amdgcn_exp2f(g4[3]) * acc[3]);
+                    w.x = pack_bf16(g4[0] * acc[0], g4[1] * acc[1]);
+                    w.y = pack_bf16(g4[2] * acc[2], g4[3] * acc[3]);
                     *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
                 }
             }
@@ -502,9 +510,13 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             body(s + 1, Parity<1>{}, role);
         }
     };
-    if (chain) run(Parity<0>{});
-    else if (outw) run(Parity<1>{});
+    // the chain waves are the critical path: they issue first on the SIMDs they share with loaders
+    if (chain) {
+        __builtin_amdgcn_s_setprio(3);
+        run(Parity<0>{});
+    } else if (outw) run(Parity<1>{});
     else run(Parity<2>{});
+    __builtin_amdgcn_s_setprio(0);
     if (loader && lane == 0) beyond_s[lw] = beyond ? 1 : 0;
     block_sync();
     const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
