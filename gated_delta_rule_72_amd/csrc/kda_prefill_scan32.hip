@@ -142,21 +142,28 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     }
     // S [i][j] as bf16 for the out waves (lane holds j = 16 jt + 4g .. +3 of row i), and the
     // same words kept as the B operands of K S^T: for the 32-wide j step m the stacked pair
-    // of tiles 2m, 2m + 1 is R[SP0 + (NJ / 2) ib + m]
-    auto pack_state = [&](int ln) {
+    // of tiles 2m, 2m + 1 is R[SP0 + (NJ / 2) ib + m]; tile jt of both row blocks, first
+    // scaled by gamma (the decay of the step)
+    auto pack_tile = [&](int jt, int ln) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
             uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * QP + 4 * (ln >> 4);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) {
-                uint2 w;
-                w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
-                w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
-                *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
-                R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(w.x);
-                R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(w.y);
-            }
+            uint2 w;
+            w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
+            w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
+            *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(w.x);
+            R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(w.y);
         }
+    };
+    auto scale_pack = [&](int jt, const float (&gm)[2], int ln) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) R[ib * NJ + jt] *= gm[ib];
+        pack_tile(jt, ln);
+    };
+    auto pack_state = [&](int ln) {
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) pack_tile(jt, ln);
     };
 
     // ---- a loader's loads of step s into register set x (a step past the end loads
@@ -428,7 +435,11 @@ __global__ __launch_bounds__(512) void scan32_kernel(
 
         if constexpr (ROLE == 0) {
             // ======== S^T += K^T U, then the decay: the K^T operand (rows j, reduction t) from
-            // row-major K through the transposing read, tile jt + 1 read while jt computes
+            // row-major K through the transposing read, tile jt + 1 read while jt computes;
+            // tile jt - 1 is scaled and packed while tile jt's products run
+            float gm[2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) gm[ib] = gamb[par][rb + 16 * ib + m16];
             bf16x8 kt[2];
             kt[0] = frag_tr_st(Kc, KP, 0, 0, ln);
 #pragma unroll
@@ -440,14 +451,9 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + ib]), R[ib * NJ + jt]);
                     R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + 2 + ib]), R[ib * NJ + jt]);
                 }
+                if (jt > 0) scale_pack(jt - 1, gm, ln);
             }
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const float gm = gamb[par][rb + 16 * ib + m16];
-#pragma unroll
-                for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] *= gm;
-            }
-            pack_state(ln);
+            scale_pack(NJ - 1, gm, ln);
         } else if constexpr (ROLE == 1) {
             // ======== O^T += U^T P^T (U^T rows with the stacked reduction order of the P
             // operands), then O = 2^{G} O staged as bf16 [t][i]
