@@ -49,7 +49,9 @@ constexpr float RANGE32_MIN = 0x1p-100f;  // least total decay of a step on the 
 template <int DK>
 struct Scan32Smem {
     static constexpr int KP = DK + PAD;       // K rows (bf16)
-    static constexpr int QP = DK + 2 * PAD;   // Q and S rows (bf16)
+    static constexpr int QP = DK + 2 * PAD;   // Q rows (bf16)
+    static constexpr int SXP = DK + PAD;      // S rows (bf16): 4 (mod 8) dwords, conflict-free for the
+                                              // chain's 8-byte writes (0 (mod 8) suits Q's 16-byte reads)
     static constexpr int AP = H32 + PAD;      // A and U^T rows of 32 (bf16)
     static constexpr int XP = H32 + 4;        // X^T rows (fp32)
     static constexpr int GP = BV + 4;         // 2^G rows (fp32)
@@ -60,7 +62,7 @@ struct Scan32Smem {
     static constexpr int RX = BV * XP * 4;
     static constexpr int RG = H32 * GP * 4;
     static constexpr int RB = BV * 4;
-    static constexpr int RS = BV * QP * 2;
+    static constexpr int RS = BV * SXP * 2;
     static constexpr int RU = 2 * BV * AP * 2;
     static constexpr int RO = H32 * OP * 2;
     static constexpr int RT = 2 * 4 * BV * 4;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
     constexpr int NVB = DV / BV;
-    constexpr int KP = SM::KP, QP = SM::QP, AP = SM::AP, XP = SM::XP, GP = SM::GP, OP = SM::OP;
+    constexpr int KP = SM::KP, QP = SM::QP, SXP = SM::SXP, AP = SM::AP, XP = SM::XP, GP = SM::GP, OP = SM::OP;
     constexpr int NJ = DK / 16;   // 16-row tiles of S^T along j
     constexpr int NM = DK / 32;   // 32-wide reduction steps over j
     constexpr int PPR = DK / 8;   // 16-byte pieces per row of q or k
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     __shared__ __align__(16) float Xb[2][BV * XP];          // X^T [i][t]
     __shared__ __align__(16) float Gb[2][H32 * GP];          // 2^G [t][i]
     __shared__ __align__(16) float gamb[2][BV];
-    __shared__ __align__(16) uint16_t Sx[BV * QP];           // S [i][j], bf16
+    __shared__ __align__(16) uint16_t Sx[BV * SXP];           // S [i][j], bf16
     __shared__ __align__(16) uint16_t Ux[2 * BV * AP];       // U^T [i][t] hi rows, then lo rows
     __shared__ __align__(16) uint16_t Os[H32 * OP];          // O [t][i], bf16
     __shared__ __align__(16) float Tot[2][BV][4];           // loader totals, per value row
@@ -132,14 +134,6 @@ __global__ __launch_bounds__(512) void scan32_kernel(
 #pragma unroll
     for (int x = 0; x < RN; ++x) R[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
-    if (chain && S0) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            const float* src = S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
-        }
-    }
     // S [i][j] as bf16 for the out waves (lane holds j = 16 jt + 4g .. +3 of row i), and the
     // same words kept as the B operands of K S^T: for the 32-wide j step m the stacked pair
     // of tiles 2m, 2m + 1 is R[SP0 + (NJ / 2) ib + m]; tile jt of both row blocks, first
@@ -147,7 +141,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     auto pack_tile = [&](int jt, int ln) {
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-            uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * QP + 4 * (ln >> 4);
+            uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * SXP + 4 * (ln >> 4);
             uint2 w;
             w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
             w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
@@ -389,7 +383,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             for (int m = 0; m < NM; ++m) {
                 bf16x8 sf[2], qf[2], kf[2];
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) sf[ib] = frag16(Sx, QP, rb + 16 * ib, 32 * m, ln);
+                for (int ib = 0; ib < 2; ++ib) sf[ib] = frag16(Sx, SXP, rb + 16 * ib, 32 * m, ln);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     qf[tt] = frag16(Qc, QP, 16 * tt, 32 * m, ln);
@@ -503,7 +497,18 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             stage(0, 0, lane);
             local_scan(step_len(0), 0, 0, lane);
         }
-        if constexpr (ROLE == 0) pack_state(lane);
+        if constexpr (ROLE == 0) {
+            if (S0) {
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const float* src =
+                        S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+#pragma unroll
+                    for (int jt = 0; jt < NJ; ++jt) R[ib * NJ + jt] = *reinterpret_cast<const f32x4*>(src + 16 * jt);
+                }
+            }
+            pack_state(lane);
+        }
         block_sync();
         if constexpr (ROLE == 2) {
             finalize(0, 0, lane);
@@ -516,25 +521,35 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             body(s + 1, Parity<1>{}, role);
         }
     };
-    // the chain waves are the critical path: they issue first on the SIMDs they share with loaders
+    // Each role ends in its own branch (one barrier each), so that values of one role are
+    // not kept live through the others' loops; the chain waves are the critical path and
+    // issue first on the SIMDs they share with loaders.
+    auto unit_beyond = [&]() {
+        return (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
+    };
     if (chain) {
         __builtin_amdgcn_s_setprio(3);
         run(Parity<0>{});
-    } else if (outw) run(Parity<1>{});
-    else run(Parity<2>{});
-    __builtin_amdgcn_s_setprio(0);
-    if (loader && lane == 0) beyond_s[lw] = beyond ? 1 : 0;
-    block_sync();
-    const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
-    if (outw) store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
-    if (range_flags && tid == 0) range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
-    if (S_T && chain && !unit_beyond) {
+        __builtin_amdgcn_s_setprio(0);
+        block_sync();
+        if (S_T && !unit_beyond()) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
+            for (int ib = 0; ib < 2; ++ib) {
+                float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
-            for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[ib * NJ + jt];
+                for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[ib * NJ + jt];
+            }
         }
+    } else if (outw) {
+        run(Parity<1>{});
+        block_sync();
+        store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
+    } else {
+        run(Parity<2>{});
+        if (lane == 0) beyond_s[lw] = beyond ? 1 : 0;
+        block_sync();
+        if (range_flags && lw == 0 && lane == 0)
+            range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond() ? 1 : 0;
     }
 }
 

@@ -18,12 +18,11 @@ namespace {
 
 constexpr int SOLVE_RP = 36;  // pitch of the 32x32 fp32 temporary of the 32-row level
 
-// Wave 0: the inverses of the four 16x16 unit-lower diagonal blocks of I + L.
-// Lane = (block b = lane / 16, column c = lane % 16); on return x[r] = row r of
-// column c of block b's inverse.  Reads only the diagonal blocks of Lf.
-__device__ __forceinline__ void solve_diag_blocks(const float* Lf, int lane, float (&x)[16]) {
-    const int b = lane >> 4, c = lane & 15;
-    const float* Lb = Lf + (16 * b) * LP + 16 * b;
+// The inverse of one 16x16 unit-lower block I + Lb (strictly lower part read from
+// Lb, fp32 rows of pitch PITCH), one column per lane: on return x[r] = row r of
+// column c of the inverse (zero above the diagonal).
+template <int PITCH>
+__device__ __forceinline__ void solve_block16(const float* Lb, int c, float (&x)[16]) {
     // Each strictly lower row is loaded one row ahead of its use, so no LDS
     // round trip sits inside the dependent substitution chain.  Piece p
     // enumerates (row r = 1..15, columns s4..s4+3 < r + 3).
@@ -36,7 +35,7 @@ __device__ __forceinline__ void solve_diag_blocks(const float* Lf, int lane, flo
     auto load_row = [&](int r) {
 #pragma unroll
         for (int s4 = 0, p = first_piece(r); s4 < r; s4 += 4, ++p)
-            lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * LP + s4);
+            lrow[p] = *reinterpret_cast<const f32x4*>(Lb + r * PITCH + s4);
     };
     auto solve_row = [&](int r) {
         float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
@@ -60,6 +59,14 @@ __device__ __forceinline__ void solve_diag_blocks(const float* Lf, int lane, flo
         issue_fence();
         solve_row(r);
     }
+}
+
+// Wave 0: the inverses of the four 16x16 unit-lower diagonal blocks of I + L.
+// Lane = (block b = lane / 16, column c = lane % 16); on return x[r] = row r of
+// column c of block b's inverse.  Reads only the diagonal blocks of Lf.
+__device__ __forceinline__ void solve_diag_blocks(const float* Lf, int lane, float (&x)[16]) {
+    const int b = lane >> 4, c = lane & 15;
+    solve_block16<LP>(Lf + (16 * b) * LP + 16 * b, c, x);
 }
 
 // All four waves, once L is complete in Lf (the call begins with the barrier that
