@@ -156,6 +156,12 @@ struct BwdChunkBufs {
 // writes before the reverse scan; T records into rec; marks for tiny beta), and the
 // checkpoint scan (states into sck, range marks into flags).  The caller clears flags.
 hipError_t launch_backward_forward_pass(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream);
+// Its checkpoint scan (kda_prefill_scan32.hip, 32-token steps): the state entering every
+// 64-token chunk into ckpt, range marks set in range_flags, the diagonal blocks of the
+// chunk solve's A records.
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32_ckpt(const BackwardArgs& a, const int32_t* order, const int32_t* chunk_off,
+                              const uint16_t* arec, int32_t* range_flags, float* ckpt, hipStream_t stream);
 // The chunked passes proper (kda_backward_chunk.hip): the reverse state-gradient scan
 // (gck, dS0) and the per-(chunk, head) gradients.
 hipError_t launch_backward_chunk_passes(const BackwardArgs& a, const BwdChunkBufs& b, hipStream_t stream);

@@ -1100,14 +1100,8 @@ static hipError_t bwd_forward_t(const BackwardArgs& a, const BwdChunkBufs& b, hi
                        a.beta, cu, b.chunk_off, a.n_seq, a.n_tok, a.n_heads, static_cast<int>(b.max_chunks), arec,
                        b.rec, b.flags, NVB);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    // the state enters K S^T as hi + lo (SPLIT_S): the checkpoints feed dq and dk directly,
-    // where a single bf16 copy's rounding is not damped by any decay
-    hipLaunchKernelGGL((scan_kernel<DK, DV, GATE, true, true>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       static_cast<const uint16_t*>(a.q), k, static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu,
-                       cu ? b.order : nullptr, b.chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr, 0,
-                       nullptr, b.flags, b.sck);
-    return hipGetLastError();
+    // the checkpoint scan in 32-token steps (the diagonal blocks of the A records)
+    return launch_scan32_ckpt<DK, DV, GATE>(a, b.order, b.chunk_off, arec, b.flags, b.sck, stream);
 }
 
 template <int GATE>

@@ -31,6 +31,16 @@
 // K, Q, A, X^T, G and gamma alternate between two buffers by step parity; the S copy,
 // the U^T copy and the O rows have one buffer each (written and read in alternate
 // phases).
+//
+// CKPT (the chunked backward's forward pass): the chain waves store the state entering
+// every 64-token chunk (every even step) into ckpt ([chunk, H, d_v, d_k] fp32, global
+// chunk numbering) and form K S^T from a hi + lo copy of the state (the checkpoints feed
+// dq and dk directly, where one bf16 copy's rounding is not damped by any decay); the
+// output side is left out (no q, no P, no O: the out waves only keep the barriers).  A
+// unit is marked when a 64-token chunk's decay is below 2^-100, the range of the
+// backward's chunk form, or one of its gates is below 2^-5 (the backward's
+// dalpha = dg / alpha would amplify its rounding there); marks are only set, since the
+// backward clears them beforehand and its chunk solve may already have set some.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -69,13 +79,13 @@ struct Scan32Smem {
     static constexpr int TOTAL = 2 * (RK + RQ + RA + RX + RG + RB) + RS + RU + RO + RT;
 };
 
-template <int DK, int DV, int GATE>
+template <int DK, int DV, int GATE, bool CKPT = false>
 __global__ __launch_bounds__(512) void scan32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
     int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T,
-    int32_t* __restrict__ range_flags) {
+    int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
     using SM = Scan32Smem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -103,10 +113,14 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool chain = wave < 2;
-    const bool outw = wave == 2 || wave == 3;
+    // chain waves and their 16-row blocks: two waves of 32 rows, or under CKPT (no out
+    // waves) four of 16, which halves each chain wave's dependent work per step
+    constexpr int NCH = CKPT ? 4 : 2;
+    constexpr int NIB = 4 / NCH;
+    const bool chain = wave < NCH;
+    const bool outw = !CKPT && (wave == 2 || wave == 3);
     const bool loader = wave >= 4;
-    const int rb = 32 * (wave & 1);  // first of the 32 value rows of a chain or out wave
+    const int rb = 16 * NIB * (wave & (NCH - 1));  // first of the value rows of a chain or out wave
     const int lw = wave - 4;         // loader index: token rows 8 lw .. +7
     const int64_t H = n_heads;
     const int h = u.head;
@@ -121,14 +135,16 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     };
 
     // ---- one register array holds each role's long-lived values: the chain's S^T
-    // (at NJ ib + jt), U^T packs (CU0 ..) and bf16 copy of S (SP0 ..), the out waves' O^T
-    // accumulators and P operands (CU0 ..), the loaders' pieces of two steps (set x at
-    // LS0 + LSN x)
-    constexpr int CU0 = 2 * NJ;
+    // (at NJ ib + jt), U^T packs (CU0 ..) and bf16 copy of S (SP0 .., then its lo part at
+    // SPL0 .. under CKPT), the out waves' O^T accumulators and P operands (CU0 ..), the
+    // loaders' pieces of two steps (set x at LS0 + LSN x)
+    constexpr int CU0 = NIB * NJ;
     constexpr int SP0 = CU0 + 4;
+    constexpr int SPL0 = SP0 + NIB * NJ / 2;
     constexpr int LK = 0, LQ = NKQ, LA = 2 * NKQ, LV = LA + 1, LL = LV + 2, LSN = LL + 2;
     constexpr int LS0 = 0;
-    constexpr int RC = (CU0 + 8 > SP0 + NJ) ? CU0 + 8 : SP0 + NJ;
+    constexpr int SPE = CKPT ? SPL0 + NIB * NJ / 2 : SP0 + NIB * NJ / 2;
+    constexpr int RC = (CU0 + 8 > SPE) ? CU0 + 8 : SPE;
     constexpr int RN = (RC > LS0 + 2 * LSN) ? RC : LS0 + 2 * LSN;
     f32x4 R[RN];
 #pragma unroll
@@ -140,19 +156,27 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     // scaled by gamma (the decay of the step)
     auto pack_tile = [&](int jt, int ln) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * SXP + 4 * (ln >> 4);
+        for (int ib = 0; ib < NIB; ++ib) {
             uint2 w;
-            w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
-            w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
-            *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            if constexpr (CKPT) {
+                uint2 wl;
+                split_bf16x2(R[ib * NJ + jt][0], R[ib * NJ + jt][1], w.x, wl.x);
+                split_bf16x2(R[ib * NJ + jt][2], R[ib * NJ + jt][3], w.y, wl.y);
+                R[SPL0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(wl.x);
+                R[SPL0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(wl.y);
+            } else {
+                uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * SXP + 4 * (ln >> 4);
+                w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
+                w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
+                *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
+            }
             R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(w.x);
             R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(w.y);
         }
     };
-    auto scale_pack = [&](int jt, const float (&gm)[2], int ln) {
+    auto scale_pack = [&](int jt, const float (&gm)[NIB], int ln) {
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) R[ib * NJ + jt] *= gm[ib];
+        for (int ib = 0; ib < NIB; ++ib) R[ib * NJ + jt] *= gm[ib];
         pack_tile(jt, ln);
     };
     auto pack_state = [&](int ln) {
@@ -184,7 +208,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             const int idx = ht + 256 * p;
             const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
             R[b0 + LK + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0));
-            R[b0 + LQ + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
+            if constexpr (!CKPT)
+                R[b0 + LQ + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
         }
         // block 2 (s % 2) of the chunk's record: rows 0-31 x cols 0-31 for the first
         // half, rows 32-63 x cols 32-63 for the second; each block is hi then lo
@@ -225,7 +250,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         for (int p = 0; p < NKQ; ++p) {
             const int idx = ht + 256 * p;
             *reinterpret_cast<f32x4*>(Kb[par] + (idx / PPR) * KP + 8 * (idx % PPR)) = R[b0 + LK + p];
-            *reinterpret_cast<f32x4*>(Qb[par] + (idx / PPR) * QP + 8 * (idx % PPR)) = R[b0 + LQ + p];
+            if constexpr (!CKPT)
+                *reinterpret_cast<f32x4*>(Qb[par] + (idx / PPR) * QP + 8 * (idx % PPR)) = R[b0 + LQ + p];
         }
         // piece ht: half ht / 128, row (ht / 4) % 32, columns 8 (ht % 4) ..
         const u32x4 na = __builtin_bit_cast(u32x4, R[b0 + LA]) ^ 0x80008000u;
@@ -237,16 +263,23 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     // Rows past the sequence end contribute 1.  Within a step nothing underflows: a step
     // whose total decay is below 2^-100 marks the unit for the recurrent pass, and every
     // prefix is at least the total.
+    // loaders: some step (CKPT: some 64-token chunk, or one gate) of some row of the unit is
+    // beyond the range
+    bool beyond = false;
+    float prev_tot = 1.f;  // wave 7, CKPT: the decay of the chunk's first step
     auto local_scan = [&](int n, int x, int par, int ln) {
         const int b0 = LS0 + LSN * x;
         float a[8];
-        float run = 1.f;
+        float run = 1.f, amin = 1.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             a[r] = GATE != GATE_NONE && 8 * lw + r < n ? R[b0 + LL + r / 4][r % 4] : 1.f;
             run *= a[r];
+            amin = fminf(amin, a[r]);
             R[b0 + LL + r / 4][r % 4] = run;
         }
+        // (also true for a NaN gate)
+        if constexpr (CKPT) beyond = beyond || __builtin_amdgcn_ballot_w64(!(amin >= 0x1p-5f)) != 0;
         float inv = __builtin_amdgcn_rcpf(run);  // 1 / prefix of row 7, then of rows 6, 5, ..
 #pragma unroll
         for (int r = 7; r >= 0; --r) {
@@ -255,7 +288,6 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         }
         Tot[par][ln][lw] = run;
     };
-    bool beyond = false;  // wave 7: some step of some row of the unit is beyond the range
     // after a barrier: multiply in the totals of the loaders before, write 2^G [t][i],
     // -X^T [i][t] and (wave 7) gamma
     auto finalize = [&](int x, int par, int ln) {
@@ -269,14 +301,21 @@ __global__ __launch_bounds__(512) void scan32_kernel(
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] * carry;
+            for (int e = 0; e < 4; ++e)
+                if constexpr (!CKPT) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] * carry;
             *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * nic;
         }
         if (lw == 3) {
             const float tot = R[b0 + LL + 1][3] * carry;
             gamb[par][ln] = tot;
             // (also true for a NaN total)
-            beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= RANGE32_MIN)) != 0;
+            if constexpr (CKPT) {
+                // a chunk is the step pair (even, odd): its decay is the product of theirs
+                if (par == 0) prev_tot = tot;
+                else beyond = beyond || __builtin_amdgcn_ballot_w64(!(prev_tot * tot >= RANGE32_MIN)) != 0;
+            } else {
+                beyond = beyond || __builtin_amdgcn_ballot_w64(!(tot >= RANGE32_MIN)) != 0;
+            }
         }
     };
     // staged O rows of a finished step -> global by the out waves, two 16-byte pieces
@@ -306,12 +345,22 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         block_sync();  // B0: step s is staged
 
         if constexpr (ROLE == 0) {
+            if constexpr (CKPT && par == 0) {
+                // the state entering chunk s / 2, [i][j] rows of 16-byte pieces
+#pragma unroll
+                for (int ib = 0; ib < NIB; ++ib) {
+                    float* dst = ckpt + ((static_cast<int64_t>(chunk0 + s / 2) * H + h) * DV + i0 + rb + 16 * ib + m16) * DK +
+                                 4 * g;
+#pragma unroll
+                    for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[ib * NJ + jt];
+                }
+            }
             // ======== -Y = K S^T - X, U = (-A)(-Y) for value rows i = rb + 16 ib + m16 (lane
             // column); rows t = 16 tt + 4g + r of tile tt
-            f32x4 Y[2][2];
+            f32x4 Y[NIB][2];
             const float* XT = Xb[par];
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
+            for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
                     Y[ib][tt] = *reinterpret_cast<const f32x4*>(XT + (rb + 16 * ib + m16) * XP + 16 * tt + 4 * g);
@@ -326,10 +375,15 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 }
                 issue_fence();
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
+                for (int ib = 0; ib < NIB; ++ib) {
                     const bf16x8 sb = __builtin_bit_cast(bf16x8, R[SP0 + (NJ / 2) * ib + m]);
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
+                    if constexpr (CKPT) {
+                        const bf16x8 sl = __builtin_bit_cast(bf16x8, R[SPL0 + (NJ / 2) * ib + m]);
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sl, Y[ib][tt]);
+                    }
                 }
             }
             const uint16_t* Ah = Ab[par];
@@ -342,7 +396,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             }
             issue_fence();
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
+            for (int ib = 0; ib < NIB; ++ib) {
                 bf16x8 yh, yl;
                 split_stack(Y[ib][0], Y[ib][1], yh, yl);
                 f32x4 U[2];
@@ -358,14 +412,16 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 split_stack(U[0], U[1], uh, ul);
                 R[CU0 + ib] = __builtin_bit_cast(f32x4, uh);
                 R[CU0 + 2 + ib] = __builtin_bit_cast(f32x4, ul);
-                const int i = rb + 16 * ib + m16;
-                const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
-                *reinterpret_cast<uint2*>(Ux + i * AP + 4 * g) = uint2{wh[0], wh[1]};
-                *reinterpret_cast<uint2*>(Ux + i * AP + 16 + 4 * g) = uint2{wh[2], wh[3]};
-                *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 4 * g) = uint2{wl[0], wl[1]};
-                *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 16 + 4 * g) = uint2{wl[2], wl[3]};
+                if constexpr (!CKPT) {
+                    const int i = rb + 16 * ib + m16;
+                    const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
+                    *reinterpret_cast<uint2*>(Ux + i * AP + 4 * g) = uint2{wh[0], wh[1]};
+                    *reinterpret_cast<uint2*>(Ux + i * AP + 16 + 4 * g) = uint2{wh[2], wh[3]};
+                    *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 4 * g) = uint2{wl[0], wl[1]};
+                    *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 16 + 4 * g) = uint2{wl[2], wl[3]};
+                }
             }
-        } else if constexpr (ROLE == 1) {
+        } else if constexpr (ROLE == 1 && !CKPT) {
             // ======== the previous step's O out; O^T = S Q^T for value rows rb + 16 ib + 4g + r
             // (tile rows) and tokens t = 16 tt + m16 (tile column)
             store_o(s - 1, ln);  // (none before the first step)
@@ -417,7 +473,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             split_stack(Pt[1], Pt[2], ph, pl);
             R[CU0 + 6] = __builtin_bit_cast(f32x4, ph);
             R[CU0 + 7] = __builtin_bit_cast(f32x4, pl);
-        } else {
+        } else if constexpr (ROLE == 2) {
             // ======== the next step's K, Q, A (then those loads of the step after the next) and
             // the local prefix products of its gates (past the last step: an empty step, which
             // nothing reads; no branch keeps the compiler's counts of outstanding loads exact)
@@ -431,9 +487,9 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             // ======== S^T += K^T U, then the decay: the K^T operand (rows j, reduction t) from
             // row-major K through the transposing read, tile jt + 1 read while jt computes;
             // tile jt - 1 is scaled and packed while tile jt's products run
-            float gm[2];
+            float gm[NIB];
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) gm[ib] = gamb[par][rb + 16 * ib + m16];
+            for (int ib = 0; ib < NIB; ++ib) gm[ib] = gamb[par][rb + 16 * ib + m16];
             bf16x8 kt[2];
             kt[0] = frag_tr_st(Kc, KP, 0, 0, ln);
 #pragma unroll
@@ -441,14 +497,14 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 if (jt + 1 < NJ) kt[(jt + 1) & 1] = frag_tr_st(Kc, KP, 16 * (jt + 1), 0, ln);
                 issue_fence();
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
+                for (int ib = 0; ib < NIB; ++ib) {
                     R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + ib]), R[ib * NJ + jt]);
                     R[ib * NJ + jt] = mfma16(kt[jt & 1], __builtin_bit_cast(bf16x8, R[CU0 + 2 + ib]), R[ib * NJ + jt]);
                 }
                 if (jt > 0) scale_pack(jt - 1, gm, ln);
             }
             scale_pack(NJ - 1, gm, ln);
-        } else if constexpr (ROLE == 1) {
+        } else if constexpr (ROLE == 1 && !CKPT) {
             // ======== O^T += U^T P^T (U^T rows with the stacked reduction order of the P
             // operands), then O = 2^{G} O staged as bf16 [t][i]
             bf16x8 uh[2], ul[2];
@@ -477,7 +533,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
                 }
             }
-        } else {
+        } else if constexpr (ROLE == 2) {
             // ======== the next step's G, X^T and gamma; then the V and alpha loads of the step
             // after the next
             finalize(par ^ 1, par ^ 1, ln);
@@ -500,7 +556,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         if constexpr (ROLE == 0) {
             if (S0) {
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
+                for (int ib = 0; ib < NIB; ++ib) {
                     const float* src =
                         S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
@@ -532,9 +588,9 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         run(Parity<0>{});
         __builtin_amdgcn_s_setprio(0);
         block_sync();
-        if (S_T && !unit_beyond()) {
+        if (!CKPT && S_T && !unit_beyond()) {
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
+            for (int ib = 0; ib < NIB; ++ib) {
                 float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
 #pragma unroll
                 for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[ib * NJ + jt];
@@ -543,12 +599,12 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     } else if (outw) {
         run(Parity<1>{});
         block_sync();
-        store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
+        if constexpr (!CKPT) store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
     } else {
         run(Parity<2>{});
         if (lane == 0) beyond_s[lw] = beyond ? 1 : 0;
         block_sync();
-        if (range_flags && lw == 0 && lane == 0)
+        if (range_flags && lw == 0 && lane == 0 && (!CKPT || unit_beyond()))
             range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond() ? 1 : 0;
     }
 }
@@ -563,7 +619,20 @@ hipError_t launch_scan32(const PrefillArgs& a, const int32_t* cu, const int32_t*
     hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu, cu ? order : nullptr, chunk_off, arec,
-                       a.n_seq, a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), a.S_T, range_flags);
+                       a.n_seq, a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), a.S_T, range_flags, nullptr);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32_ckpt(const BackwardArgs& a, const int32_t* order, const int32_t* chunk_off,
+                              const uint16_t* arec, int32_t* range_flags, float* ckpt, hipStream_t stream) {
+    constexpr int NVB = DV / BV;
+    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
+    const int32_t* cu = a.cu_seqlens;
+    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, true>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                       nullptr, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha, a.S0,
+                       cu, cu ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr,
+                       range_flags, ckpt);
     return hipGetLastError();
 }
 
@@ -579,5 +648,18 @@ KDA_SCAN32(64, 64)
 KDA_SCAN32(128, 64)
 KDA_SCAN32(64, 128)
 #undef KDA_SCAN32
+#define KDA_SCAN32_CKPT(DK, DV, GATE)                                                                               \
+    template hipError_t launch_scan32_ckpt<DK, DV, GATE>(const BackwardArgs&, const int32_t*, const int32_t*,      \
+                                                         const uint16_t*, int32_t*, float*, hipStream_t);
+#define KDA_SCAN32_CKPT_G(DK, DV)         \
+    KDA_SCAN32_CKPT(DK, DV, GATE_CHANNEL) \
+    KDA_SCAN32_CKPT(DK, DV, GATE_SCALAR)  \
+    KDA_SCAN32_CKPT(DK, DV, GATE_NONE)
+KDA_SCAN32_CKPT_G(128, 128)
+KDA_SCAN32_CKPT_G(64, 64)
+KDA_SCAN32_CKPT_G(128, 64)
+KDA_SCAN32_CKPT_G(64, 128)
+#undef KDA_SCAN32_CKPT_G
+#undef KDA_SCAN32_CKPT
 
 }  // namespace kda
