@@ -25,9 +25,10 @@
 //
 // Passes, all on the caller's stream:
 //   1. the forward: the chunk solve, storing both A and T = (I + L)^{-1} (no beta
-//      factor) and marking units with |beta| below 2^-20, then the scan in its
-//      checkpoint variant, which stores the state entering every chunk (no outputs)
-//      and marks units beyond the factored form's range or with a gate below 2^-5;
+//      factor) and marking units with |beta| below 2^-20, then the 32-token scan in
+//      its checkpoint variant, which stores the state entering every 64-token chunk
+//      (no outputs) and marks units beyond the factored form's range or with a gate
+//      below 2^-5;
 //   2. (the marks are only ever set; they are cleared before pass 1);
 //   3. bwd_state_scan_kernel: per (sequence, head, 64 value rows), the chunks in
 //      reverse, carrying dL/dS^T in fp32 MFMA accumulators -- the forward scan's

@@ -329,19 +329,14 @@ struct ScanSmem {
 // add at most a few powers of two.
 constexpr float RANGE_LOG2 = 100.f;
 
-// CKPT (the chunked backward's forward pass): the state entering every chunk is
-// stored into ckpt ([chunk, H, d_v, d_k] fp32, global chunk numbering) and the
-// output side is left out (no q, no P, no O); a unit is also marked when one of
-// its tokens has a gate below 2^-5, since the backward's dalpha = dg / alpha would
-// amplify its rounding there.
-template <int DK, int DV, int GATE, bool SPLIT_S = false, bool CKPT = false>
+template <int DK, int DV, int GATE, bool SPLIT_S = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off,
     const uint16_t* __restrict__ arec, int n_seq, int n_tok, int n_heads,
     uint16_t* __restrict__ o, float* __restrict__ S_T, int flags, float* __restrict__ glog_out,
-    int32_t* __restrict__ range_flags, float* __restrict__ ckpt = nullptr) {
+    int32_t* __restrict__ range_flags) {
     using SM = ScanSmem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -484,8 +479,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const int idx = ht + 256 * p;
             const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
             R[PK0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-            if constexpr (!CKPT)
-                R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+            R[PQ0 + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
         }
         const uint16_t* recp = arec + (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
         const auto rr = make_rsrc(recp, any ? A_RECORD_BYTES : 0);
@@ -549,21 +543,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // Rows past the sequence end contribute log alpha = 0.
     bool beyond = false;  // loader waves: some chunk of some row of the unit is beyond the range
     auto local_scan = [&](int n, int par, int ln) {
-        float run = 0.f, lmin = 0.f;
+        float run = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             if constexpr (GATE != GATE_NONE) {
                 const float l = 16 * (wave - 4) + r < n ? __builtin_amdgcn_logf(R[PL0 + r / 4][r % 4]) : 0.f;
                 run += l;
-                if constexpr (CKPT) lmin = fminf(lmin, l);
             }
             R[PL0 + r / 4][r % 4] = run;
             // V 2^{-prefix}: the part of X = V 2^{-G} this wave knows before the carry
             R[PV0 + r / 4][r % 4] = bf16_bits_to_f32(static_cast<uint16_t>(__float_as_uint(R[PV0 + r / 4][r % 4]))) *
                                     __builtin_amdgcn_exp2f(-run);
         }
-        // (also true for a NaN gate)
-        if constexpr (CKPT) beyond = beyond || __builtin_amdgcn_ballot_w64(!(lmin >= -5.f)) != 0;
         Tot[(par * 4 + wave - 4) * BV + ln] = run;
     };
     float glog = 0.f;  // wave 7: this row's total log2-decay over the unit's chunks
@@ -597,8 +588,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         for (int p = 0; p < NKQ; ++p) {
             const int idx = ht + 256 * p;
             *reinterpret_cast<u32x4*>(Kc + (idx / PPR) * KP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PK0 + p]);
-            if constexpr (!CKPT)
-                *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
+            *reinterpret_cast<u32x4*>(Qc + (idx / PPR) * QP + 8 * (idx % PPR)) = __builtin_bit_cast(u32x4, R[PQ0 + p]);
         }
 #pragma unroll
         for (int p = 0; p < NA; ++p) stage_a(__builtin_bit_cast(u32x4, R[PA0 + p]), ht + 256 * p);
@@ -608,7 +598,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         prefetch(u.t0, chunk_len(u.t0), chunk0);
         local_scan(chunk_len(u.t0), 0, lane);
     }
-    if (chain && !CKPT) pack_state(lane);
+    if (chain) pack_state(lane);
 
     int64_t prev_tc = u.t0;
     int prev_n = 0;
@@ -624,17 +614,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
         asm volatile("" : "+v"(lane_o));
         const int ln = lane_o;
         const int g = ln >> 4, m16 = ln & 15;
-        if constexpr (CKPT) {
-            // the state entering this chunk, [i][j] rows of 16-byte pieces
-            if (chain) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    float* dst = ckpt + ((static_cast<int64_t>(gc) * H + h) * DV + i0 + rb + 16 * ib + m16) * DK + 4 * g;
-#pragma unroll
-                    for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(dst + 16 * jt) = R[(ib) * NJ + (jt)];
-                }
-            }
-        }
         block_sync();  // the previous chunk is done with every buffer
 
         // ======== the loaders stage this chunk and finish its G; the out waves
@@ -642,7 +621,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         if (loader) {
             stage(ln);
             finalize(c & 1, ln);
-        } else if (outw && !CKPT) {
+        } else if (outw) {
             store_o(prev_tc, prev_n, ln);
         }
         block_sync();
@@ -734,7 +713,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     split_stack(U[ib][2 * m], U[ib][2 * m + 1], uh, ul);
                     R[CARRY0 + 2 * ib + m] = __builtin_bit_cast(f32x4, uh);
                     R[CARRY0 + 4 + 2 * ib + m] = __builtin_bit_cast(f32x4, ul);
-                    if constexpr (CKPT) continue;  // no out waves' copy
                     const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 4 * g) = uint2{wh[0], wh[1]};
                     *reinterpret_cast<uint2*>(Ux_hi + i * CP + 32 * m + 16 + 4 * g) = uint2{wh[2], wh[3]};
@@ -743,7 +721,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 }
             }
         } else if (outw) {
-            if constexpr (!CKPT) {
             // ======== O^T = S Q^T for value rows rb + 16 ib + 4g + r (tile rows) and
             // tokens t = 16 tt + m16 (tile column); every Q fragment serves both blocks
             f32x4 Oacc[2][4];
@@ -768,9 +745,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) R[CARRY0 + 4 * ib + tt] = Oacc[ib][tt];
-            }
         } else {
-            if (!CKPT && wave >= 6) {
+            if (wave >= 6) {
             // ======== P = tril(Q K^T) hi/lo [t][s], formed transposed (32x32 tile
             // D[s][t], so each lane holds 4 consecutive s of one t).  P^T tiles
             // (s-tile, t-tile): wave 6 takes (0,0) and (1,1), wave 7 (0,1); (1,0) is
@@ -843,9 +819,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int jt = 0; jt < NJ; ++jt) R[(ib) * NJ + (jt)] *= gm;
             }
-            if constexpr (!CKPT) pack_state(ln);
+            pack_state(ln);
         } else if (outw) {
-            if constexpr (!CKPT) {
             // ======== O^T += U^T P^T (P is lower triangular: t-tiles 0, 1 need s < 32),
             // then O = 2^{G} O, staged as bf16 [t][i]
             f32x4 Oacc[2][4];
@@ -895,7 +870,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
                                     __builtin_amdgcn_exp2f(g4[3]) * Oacc[ib][tt][3]);
                     *reinterpret_cast<uint2*>(Os + t * OP + i) = w;
                 }
-            }
         }
         if (loader) local_scan(chunk_len(tc + C), (c + 1) & 1, ln);
         prev_tc = tc;
@@ -905,10 +879,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
     if (loader && lane == 0) beyond_s[wave - 4] = beyond ? 1 : 0;
     block_sync();
     const bool unit_beyond = (beyond_s[0] | beyond_s[1] | beyond_s[2] | beyond_s[3]) != 0;
-    if (outw && !CKPT) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
-    // (CKPT: the backward zeroes the marks beforehand and its chunk solve may already have
-    // set some, so the scan only sets)
-    if (range_flags && tid == 0 && (!CKPT || unit_beyond))
+    if (outw) store_o(prev_tc, prev_n, lane);  // (n = 0: nothing is stored)
+    if (range_flags && tid == 0)
         range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond ? 1 : 0;
 
     // the unit's total log2-decay per value row, when asked for (the sequence-parallel
@@ -1034,7 +1006,7 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(vv), al, s0, cu, cu ? order : nullptr, chunk_off, arec, nsq,
-                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog, rf, nullptr);
+                           a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), st, flags, glog, rf);
         return hipGetLastError();
     };
     // Units with a chunk beyond the decay range (marked in rflags by the scan, S_T left
