@@ -191,13 +191,13 @@ TRAFFIC_PREFILL_SOURCES = ["kda_prefill_mfma.hip", "kda_prefill_scan32.hip", "kd
                            "kda_device.h", "kda_schedule.h", "kda_internal.h", "kda_prefill_valu.hip"]
 # call -> (probe, kernel-name pieces, one kernel per piece; None = every kda kernel of the probe, sources)
 TRAFFIC_CALLS = {
-    "prefill": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 0>",
+    "prefill": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 0, false>",
                          "prefill_staged_kernel<unsigned short, 128, 128, 0, 64, 8, false>"], TRAFFIC_PREFILL_SOURCES),
-    "prefill_scalar_gate": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 1>",
+    "prefill_scalar_gate": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 1, false>",
                                      "prefill_staged_kernel<unsigned short, 128, 128, 1, 64, 8, false>"],
                             TRAFFIC_PREFILL_SOURCES),
     "decode": ("main", ["decode_step_kernel<unsigned short, 128, 128, 0>"], ["kda_decode.hip", "kda_device.h"]),
-    "backward": ("extra", ["chunk_solve_kernel<128, true, false>", "scan_kernel<128, 128, 0, true, true>",
+    "backward": ("extra", ["chunk_solve_kernel<128, true, false>", "scan32_kernel<128, 128, 0, true>",
                            "bwd_state_scan_kernel<128, 128, 0>", "bwd_chunk_grad_kernel<128, 128, 0>",
                            "backward_kernel<unsigned short, 128, 128, 0>"],
                  TRAFFIC_PREFILL_SOURCES + ["kda_backward.hip", "kda_backward_chunk.hip"]),
