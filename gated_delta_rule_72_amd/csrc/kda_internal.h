@@ -69,16 +69,20 @@ inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32
     return g >= 8 ? g : 1;
 }
 
-// The bf16 prefill's scan in 32-token steps (kda_prefill_scan32.hip) for calls with one
-// scan per sequence: the A records of the 64-token chunk solve (their diagonal blocks),
-// the schedule (packed input) and the range marks as in the 64-token scan.
-template <int DK, int DV, int GATE>
-hipError_t launch_scan32(const PrefillArgs& a, const int32_t* cu, const int32_t* order, const int32_t* chunk_off,
-                         const uint16_t* arec, int32_t* range_flags, hipStream_t stream);
+// One pass of the bf16 prefill's scan in 32-token steps (kda_prefill_scan32.hip) over
+// n_units_seq sequences (or segments, through cu and the dense split), with the
+// diagonal blocks of the chunk solve's A records, the schedule (packed input) and the
+// range marks.  NOOUT: no outputs (o is not written); SPLIT: the state enters K S^T as
+// hi + lo bf16.  flags: SCAN_ZERO_V (v read as zero), SCAN_S0_IDENTITY (S0 = I, d_v = d_k).
+// gdecay (or null): every unit's total decay per value row, [n_units_seq, H, d_v].
+template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
+hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
+                              const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
+                              float* gdecay, int32_t* range_flags, hipStream_t stream);
 
 // Composes the segment states of the sequence-parallel prefill (kda_segments.hip).
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M,
+hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dS, const float* M,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, hipStream_t stream);
 

@@ -12,7 +12,7 @@ namespace kda {
 namespace {
 
 constexpr int C = PREFILL_CHUNK_BF16;  // 64 tokens per chunk
-// scan_kernel flags: v read as zero; S0 taken as the identity (d_v = d_k)
+// scan flags: v read as zero; S0 taken as the identity (d_v = d_k)
 constexpr int SCAN_ZERO_V = 1;
 constexpr int SCAN_S0_IDENTITY = 2;
 constexpr int BV = 64;                 // value rows per scan workgroup

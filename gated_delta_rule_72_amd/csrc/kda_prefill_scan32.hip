@@ -4,15 +4,20 @@
 // of the step before.
 //
 // The recurrence is that of page "Kimi (AI)", section "Kimi Delta Attention
-// (KDA)", in the chunk form of kda_prefill_mfma.hip, applied to half chunks: a
-// 64-token chunk's system (I + L) is lower triangular, so the two 32x32 diagonal
-// blocks of its solved record A = (I + L)^{-1} diag(beta) are exactly the solved
-// systems of its two halves.  The chunk solve therefore serves this scan
-// unchanged (blocks 0 and 2 of each record), and chunk numbering, workspaces and
-// range marks are those of the 64-token path.
+// (KDA)", in the chunk form written out in kda_prefill_mfma.hip, applied to half
+// chunks: a 64-token chunk's system (I + L) is lower triangular, so the two 32x32
+// diagonal blocks of its solved record A = (I + L)^{-1} diag(beta) are exactly the
+// solved systems of its two halves.  The chunk solve therefore serves this scan with
+// the records' diagonal blocks (0 and 2), and chunks are numbered as there.
 //
-// One workgroup of 8 waves per (sequence, head, block of 64 value rows), as in
-// scan_kernel:
+// A 16x16 MFMA accumulator tile holds, in lane (column n = l % 16, group g = l / 16),
+// rows 4g..4g+3.  Two tiles stacked along the row index give a lane the 8 rows
+// {4g..4g+3, 16+4g..16+4g+3}; taken as the 8 reduction indices of a
+// v_mfma_f32_16x16x32_bf16 B operand (the A operand reads the same indices, two
+// 8-byte pieces per lane), Y, U and S feed the next product straight from the
+// accumulators.
+//
+// One workgroup of 8 waves per (sequence, head, block of 64 value rows):
 // - chain waves (0, 1) own 32 value rows each and keep S^T in fp32 accumulators;
 //   per step: Y = X - K S^T, U = A Y (A, Y as hi + lo), then
 //   S^T <- diag(gamma) (S^T + K^T U).  They form -Y = K S^T - X from the staged -X and
@@ -54,7 +59,15 @@ template <int V>
 struct Parity {
     static constexpr int value = V;
 };
-constexpr float RANGE32_MIN = 0x1p-100f;  // least total decay of a step on the factored form
+// Range: X = V 2^{-G} and U grow like 2^{-G} inside a step, so the factored form holds
+// only while every row's decay over a step stays above RANGE32_MIN (alpha in [0, 1]: the
+// step's total is its smallest prefix).  Wave 7 checks each step's totals; a unit with
+// any step beyond the range (alpha = 0 gives 0) is marked in range_flags[unit] and does
+// not write S_T, so that S0 is intact when S_T aliases it, and a token-recurrent pass
+// recomputes exactly the marked units afterwards.  Above the limit 2^{-G} stays below
+// 2^{100}: fp32 and bf16 (same exponent range) keep it, and the products with A, P and
+// K add at most a few powers of two.
+constexpr float RANGE32_MIN = 0x1p-100f;
 
 template <int DK>
 struct Scan32Smem {
@@ -79,13 +92,14 @@ struct Scan32Smem {
     static constexpr int TOTAL = 2 * (RK + RQ + RA + RX + RG + RB) + RS + RU + RO + RT;
 };
 
-template <int DK, int DV, int GATE, bool CKPT = false>
+template <int DK, int DV, int GATE, bool NOOUT = false, bool SPLIT = false, bool CKPT = false>
 __global__ __launch_bounds__(512) void scan32_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
-    int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T,
-    int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
+    int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T, int flags,
+    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
+    static_assert(!CKPT || (NOOUT && SPLIT), "the checkpoint variant has no output side and splits the state");
     using SM = Scan32Smem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -113,12 +127,12 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // chain waves and their 16-row blocks: two waves of 32 rows, or under CKPT (no out
-    // waves) four of 16, which halves each chain wave's dependent work per step
-    constexpr int NCH = CKPT ? 4 : 2;
+    // chain waves and their 16-row blocks: two waves of 32 rows, or without an output side
+    // (no out waves) four of 16, which halves each chain wave's dependent work per step
+    constexpr int NCH = NOOUT ? 4 : 2;
     constexpr int NIB = 4 / NCH;
     const bool chain = wave < NCH;
-    const bool outw = !CKPT && (wave == 2 || wave == 3);
+    const bool outw = !NOOUT && (wave == 2 || wave == 3);
     const bool loader = wave >= 4;
     const int rb = 16 * NIB * (wave & (NCH - 1));  // first of the value rows of a chain or out wave
     const int lw = wave - 4;         // loader index: token rows 8 lw .. +7
@@ -136,14 +150,14 @@ __global__ __launch_bounds__(512) void scan32_kernel(
 
     // ---- one register array holds each role's long-lived values: the chain's S^T
     // (at NJ ib + jt), U^T packs (CU0 ..) and bf16 copy of S (SP0 .., then its lo part at
-    // SPL0 .. under CKPT), the out waves' O^T accumulators and P operands (CU0 ..), the
+    // SPL0 .. under SPLIT), the out waves' O^T accumulators and P operands (CU0 ..), the
     // loaders' pieces of two steps (set x at LS0 + LSN x)
     constexpr int CU0 = NIB * NJ;
     constexpr int SP0 = CU0 + 4;
     constexpr int SPL0 = SP0 + NIB * NJ / 2;
     constexpr int LK = 0, LQ = NKQ, LA = 2 * NKQ, LV = LA + 1, LL = LV + 2, LSN = LL + 2;
     constexpr int LS0 = 0;
-    constexpr int SPE = CKPT ? SPL0 + NIB * NJ / 2 : SP0 + NIB * NJ / 2;
+    constexpr int SPE = SPLIT ? SPL0 + NIB * NJ / 2 : SP0 + NIB * NJ / 2;
     constexpr int RC = (CU0 + 8 > SPE) ? CU0 + 8 : SPE;
     constexpr int RN = (RC > LS0 + 2 * LSN) ? RC : LS0 + 2 * LSN;
     f32x4 R[RN];
@@ -152,7 +166,17 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     const int64_t s_base = ((static_cast<int64_t>(u.seq) * H + h) * DV + i0) * DK;
     // (S0 is loaded here, before the role dispatch, rather than in the chain's own prologue:
     // measured with the fetch counters, that order costs the scan about 7% fewer HBM reads)
-    if (chain && S0) {
+    if (chain && (flags & SCAN_S0_IDENTITY)) {
+        // S0 = I (d_v = d_k): row i holds 1 at key channel i
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+            const int row = i0 + rb + 16 * ib + (lane & 15);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R[ib * NJ + jt][e] = row == 16 * jt + 4 * (lane >> 4) + e ? 1.f : 0.f;
+        }
+    } else if (chain && S0) {
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
             const float* src = S0 + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
@@ -168,16 +192,18 @@ __global__ __launch_bounds__(512) void scan32_kernel(
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
             uint2 w;
-            if constexpr (CKPT) {
+            if constexpr (SPLIT) {
                 uint2 wl;
                 split_bf16x2(R[ib * NJ + jt][0], R[ib * NJ + jt][1], w.x, wl.x);
                 split_bf16x2(R[ib * NJ + jt][2], R[ib * NJ + jt][3], w.y, wl.y);
                 R[SPL0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(wl.x);
                 R[SPL0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1) + 1] = __uint_as_float(wl.y);
             } else {
-                uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * SXP + 4 * (ln >> 4);
                 w.x = pack_bf16(R[ib * NJ + jt][0], R[ib * NJ + jt][1]);
                 w.y = pack_bf16(R[ib * NJ + jt][2], R[ib * NJ + jt][3]);
+            }
+            if constexpr (!NOOUT) {
+                uint16_t* dst = Sx + (rb + 16 * ib + (ln & 15)) * SXP + 4 * (ln >> 4);
                 *reinterpret_cast<uint2*>(dst + 16 * jt) = w;
             }
             R[SP0 + (NJ / 2) * ib + jt / 2][2 * (jt & 1)] = __uint_as_float(w.x);
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
             const int idx = ht + 256 * p;
             const int off = static_cast<int>((idx / PPR) * row_qk + 8 * (idx % PPR)) * 2;
             R[b0 + LK + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_, off, 0, 0));
-            if constexpr (!CKPT)
+            if constexpr (!NOOUT)
                 R[b0 + LQ + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
         }
         // block 2 (s % 2) of the chunk's record: rows 0-31 x cols 0-31 for the first
@@ -233,7 +259,8 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         const bool any = n > 0;
         const int64_t tok0 = step_tok0(s);
         const int b0 = LS0 + LSN * x;
-        const auto rv = make_rsrc(v + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 2 : 0);
+        // (v reads as zero when the flag asks for it: an empty range)
+        const auto rv = make_rsrc(v + tok0 * DV + i0, any && !(flags & SCAN_ZERO_V) ? ((n - 1) * row_v + BV) * 2 : 0);
         const auto rl = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
                         : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, any ? ((n - 1) * H + 1) * 4 : 0)
                                               : make_rsrc(alpha, 0);
@@ -260,7 +287,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         for (int p = 0; p < NKQ; ++p) {
             const int idx = ht + 256 * p;
             *reinterpret_cast<f32x4*>(Kb[par] + (idx / PPR) * KP + 8 * (idx % PPR)) = R[b0 + LK + p];
-            if constexpr (!CKPT)
+            if constexpr (!NOOUT)
                 *reinterpret_cast<f32x4*>(Qb[par] + (idx / PPR) * QP + 8 * (idx % PPR)) = R[b0 + LQ + p];
         }
         // piece ht: half ht / 128, row (ht / 4) % 32, columns 8 (ht % 4) ..
@@ -277,6 +304,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     // beyond the range
     bool beyond = false;
     float prev_tot = 1.f;  // wave 7, CKPT: the decay of the chunk's first step
+    float gprod = 1.f;     // wave 7: the row's total decay over the unit's steps
     auto local_scan = [&](int n, int x, int par, int ln) {
         const int b0 = LS0 + LSN * x;
         float a[8];
@@ -312,12 +340,13 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if constexpr (!CKPT) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] * carry;
+                if constexpr (!NOOUT) Gb[par][(8 * lw + 4 * p + e) * GP + ln] = R[b0 + LL + p][e] * carry;
             *reinterpret_cast<f32x4*>(xt + 4 * p) = R[b0 + LV + p] * nic;
         }
         if (lw == 3) {
             const float tot = R[b0 + LL + 1][3] * carry;
             gamb[par][ln] = tot;
+            gprod *= tot;  // (steps outside the unit contribute 1)
             // (also true for a NaN total)
             if constexpr (CKPT) {
                 // a chunk is the step pair (even, odd): its decay is the product of theirs
@@ -389,7 +418,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     const bf16x8 sb = __builtin_bit_cast(bf16x8, R[SP0 + (NJ / 2) * ib + m]);
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sb, Y[ib][tt]);
-                    if constexpr (CKPT) {
+                    if constexpr (SPLIT) {
                         const bf16x8 sl = __builtin_bit_cast(bf16x8, R[SPL0 + (NJ / 2) * ib + m]);
 #pragma unroll
                         for (int tt = 0; tt < 2; ++tt) Y[ib][tt] = mfma16(kf[m & 1][tt], sl, Y[ib][tt]);
@@ -422,7 +451,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 split_stack(U[0], U[1], uh, ul);
                 R[CU0 + ib] = __builtin_bit_cast(f32x4, uh);
                 R[CU0 + 2 + ib] = __builtin_bit_cast(f32x4, ul);
-                if constexpr (!CKPT) {
+                if constexpr (!NOOUT) {
                     const int i = rb + 16 * ib + m16;
                     const u32x4 wh = __builtin_bit_cast(u32x4, uh), wl = __builtin_bit_cast(u32x4, ul);
                     *reinterpret_cast<uint2*>(Ux + i * AP + 4 * g) = uint2{wh[0], wh[1]};
@@ -431,7 +460,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     *reinterpret_cast<uint2*>(Ux + (BV + i) * AP + 16 + 4 * g) = uint2{wl[2], wl[3]};
                 }
             }
-        } else if constexpr (ROLE == 1 && !CKPT) {
+        } else if constexpr (ROLE == 1 && !NOOUT) {
             // ======== the previous step's O out; O^T = S Q^T for value rows rb + 16 ib + 4g + r
             // (tile rows) and tokens t = 16 tt + m16 (tile column)
             store_o(s - 1, ln);  // (none before the first step)
@@ -514,7 +543,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                 if (jt > 0) scale_pack(jt - 1, gm, ln);
             }
             scale_pack(NJ - 1, gm, ln);
-        } else if constexpr (ROLE == 1 && !CKPT) {
+        } else if constexpr (ROLE == 1 && !NOOUT) {
             // ======== O^T += U^T P^T (U^T rows with the stacked reduction order of the P
             // operands), then O = 2^{G} O staged as bf16 [t][i]
             bf16x8 uh[2], ul[2];
@@ -587,7 +616,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         run(Parity<0>{});
         __builtin_amdgcn_s_setprio(0);
         block_sync();
-        if (!CKPT && S_T && !unit_beyond()) {
+        if (S_T && !unit_beyond()) {
 #pragma unroll
             for (int ib = 0; ib < NIB; ++ib) {
                 float* dst = S_T + s_base + static_cast<int64_t>(rb + 16 * ib + (lane & 15)) * DK + 4 * (lane >> 4);
@@ -598,27 +627,32 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     } else if (outw) {
         run(Parity<1>{});
         block_sync();
-        if constexpr (!CKPT) store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
+        if constexpr (!NOOUT) store_o(((n_steps + 1) & ~1) - 1, lane);  // (an empty last step stores nothing)
     } else {
         run(Parity<2>{});
         if (lane == 0) beyond_s[lw] = beyond ? 1 : 0;
         block_sync();
         if (range_flags && lw == 0 && lane == 0 && (!CKPT || unit_beyond()))
             range_flags[(static_cast<int64_t>(u.seq) * H + h) * NVB + u.vblk] = unit_beyond() ? 1 : 0;
+        // the unit's total decay per value row, when asked for (the sequence-parallel path
+        // composes segments with it)
+        if (gdecay && lw == 3) gdecay[(static_cast<int64_t>(u.seq) * H + h) * DV + i0 + lane] = gprod;
     }
 }
 
 }  // namespace
 
-template <int DK, int DV, int GATE>
-hipError_t launch_scan32(const PrefillArgs& a, const int32_t* cu, const int32_t* order, const int32_t* chunk_off,
-                         const uint16_t* arec, int32_t* range_flags, hipStream_t stream) {
+template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
+hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
+                              const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
+                              float* gdecay, int32_t* range_flags, hipStream_t stream) {
     constexpr int NVB = DV / BV;
-    const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
-    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.alpha, a.S0, cu, cu ? order : nullptr, chunk_off, arec,
-                       a.n_seq, a.n_tok, a.n_heads, static_cast<uint16_t*>(a.o), a.S_T, range_flags, nullptr);
+    const int64_t grid = prefill_grid(static_cast<int64_t>(n_units_seq) * a.n_heads, NVB);
+    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, NOOUT, SPLIT>), dim3(static_cast<unsigned>(grid)), dim3(512), 0,
+                       stream, NOOUT ? nullptr : static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha, S0, cu,
+                       cu ? order : nullptr, chunk_off, arec, n_units_seq, a.n_tok, a.n_heads,
+                       NOOUT ? nullptr : static_cast<uint16_t*>(a.o), S_T, flags, gdecay, range_flags, nullptr);
     return hipGetLastError();
 }
 
@@ -628,25 +662,35 @@ hipError_t launch_scan32_ckpt(const BackwardArgs& a, const int32_t* order, const
     constexpr int NVB = DV / BV;
     const int64_t grid = prefill_grid(static_cast<int64_t>(a.n_seq) * a.n_heads, NVB);
     const int32_t* cu = a.cu_seqlens;
-    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, true>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       nullptr, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha, a.S0,
-                       cu, cu ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr, nullptr,
-                       range_flags, ckpt);
+    hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, true, true, true>), dim3(static_cast<unsigned>(grid)), dim3(512),
+                       0, stream, nullptr, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       a.alpha, a.S0, cu, cu ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr,
+                       nullptr, 0, nullptr, range_flags, ckpt);
     return hipGetLastError();
 }
 
-#define KDA_SCAN32(DK, DV)                                                                                        \
-    template hipError_t launch_scan32<DK, DV, GATE_CHANNEL>(const PrefillArgs&, const int32_t*, const int32_t*, \
-                                                            const int32_t*, const uint16_t*, int32_t*, hipStream_t); \
-    template hipError_t launch_scan32<DK, DV, GATE_SCALAR>(const PrefillArgs&, const int32_t*, const int32_t*,  \
-                                                           const int32_t*, const uint16_t*, int32_t*, hipStream_t);  \
-    template hipError_t launch_scan32<DK, DV, GATE_NONE>(const PrefillArgs&, const int32_t*, const int32_t*,    \
-                                                         const int32_t*, const uint16_t*, int32_t*, hipStream_t);
+#define KDA_SCAN32_PASS(DK, DV, GATE, NOOUT, SPLIT)                                                                \
+    template hipError_t launch_scan32_pass<DK, DV, GATE, NOOUT, SPLIT>(                                           \
+        const PrefillArgs&, int, const int32_t*, const int32_t*, const int32_t*, const uint16_t*, const float*,  \
+        float*, int, float*, int32_t*, hipStream_t);
+// the output pass and the segments' end-state pass for each gate; the transitions' pass
+// (no gate, state split) where d_v = d_k
+#define KDA_SCAN32_G(DK, DV, GATE)             \
+    KDA_SCAN32_PASS(DK, DV, GATE, false, false) \
+    KDA_SCAN32_PASS(DK, DV, GATE, true, false)
+#define KDA_SCAN32(DK, DV)                  \
+    KDA_SCAN32_G(DK, DV, GATE_CHANNEL)      \
+    KDA_SCAN32_G(DK, DV, GATE_SCALAR)       \
+    KDA_SCAN32_G(DK, DV, GATE_NONE)
 KDA_SCAN32(128, 128)
 KDA_SCAN32(64, 64)
 KDA_SCAN32(128, 64)
 KDA_SCAN32(64, 128)
+KDA_SCAN32_PASS(128, 128, GATE_NONE, true, true)
+KDA_SCAN32_PASS(64, 64, GATE_NONE, true, true)
 #undef KDA_SCAN32
+#undef KDA_SCAN32_G
+#undef KDA_SCAN32_PASS
 #define KDA_SCAN32_CKPT(DK, DV, GATE)                                                                               \
     template hipError_t launch_scan32_ckpt<DK, DV, GATE>(const BackwardArgs&, const int32_t*, const int32_t*,      \
                                                          const uint16_t*, int32_t*, float*, hipStream_t);

@@ -25,20 +25,20 @@ namespace kda {
 // through LDS (4 rows per workgroup at d_k = 128, 8 at 64).
 // For segment g = 0 .. G-1 of sequence n:
 //     S_start[n G + g] = S                      (S = S0[n], or zeros, for g = 0)
-//     S = diag(2^{glog_g}) S M_g + dS_g
-// and S_T[n] = S after the last segment.  glog_g is the segment's total
-// log2-decay per value row, written by the scan that produced dS.  M_{g+1},
-// dS_{g+1} and glog_{g+1} are loaded into registers while segment g is
+//     S = diag(gamma_g) S M_g + dS_g
+// and S_T[n] = S after the last segment.  gamma_g is the segment's total decay
+// per value row (the product of its gates), written by the scan that produced dS.
+// M_{g+1}, dS_{g+1} and gamma_{g+1} are loaded into registers while segment g is
 // composed, so a step waits only for its own LDS products.
 // Layouts: dS, S_start [n_seq G, H, d_v, d_k]; M [n_seq G, H, d_k, d_k];
-// glog [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
+// gdecay [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
 // range_flags [n_seq G, H, d_v / 64] (or null): segments whose scan met a chunk
 // beyond the decay range of the factored form; their dS is not valid, so a
 // workgroup whose rows belong to such a segment leaves S_T unwritten (S0 stays
 // intact when S_T aliases it) for the token-recurrent pass that follows.
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void combine_segments_kernel(
-    const float* __restrict__ glog, const float* __restrict__ S0, const float* __restrict__ dS,
+    const float* __restrict__ gdecay, const float* __restrict__ S0, const float* __restrict__ dS,
     const float* __restrict__ M, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
     float* __restrict__ S_start, float* __restrict__ S_T) {
     constexpr int NT = 512;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if (owner && S0) s = *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off);
     f32x4 mreg[MP], dnext = {0.f, 0.f, 0.f, 0.f};
-    float lnext = 0.f;
+    float gnext = 1.f;
     auto load_next = [&](int g) {
         const int64_t sg = seg_of(g);
         const float* Mg = M + (sg * H + h) * DK * DK;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
         for (int p = 0; p < MP; ++p) mreg[p] = *reinterpret_cast<const f32x4*>(Mg + 4 * (tid + NT * p));
         if (owner) {
             dnext = *reinterpret_cast<const f32x4*>(dS + (sg * H + h) * DV * DK + row_off);
-            lnext = glog[(sg * H + h) * DV + i];
+            gnext = gdecay[(sg * H + h) * DV + i];
         }
     };
     load_next(0);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
 #pragma unroll
         for (int p = 0; p < MP; ++p) *reinterpret_cast<f32x4*>(Ms + 4 * (tid + NT * p)) = mreg[p];
         const f32x4 d = dnext;
-        const float gam = __builtin_amdgcn_exp2f(lnext);
+        const float gam = gnext;
         if (g + 1 < G) load_next(g + 1);
         __syncthreads();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -126,13 +126,13 @@ __global__ __launch_bounds__(512) void combine_segments_kernel(
 }
 
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* glog, const float* S0, const float* dS, const float* M,
+hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dS, const float* M,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, hipStream_t stream) {
     constexpr int NRB = DV / (512 / (DK / 4 * 4));
     const int64_t grid = static_cast<int64_t>(n_seq) * n_heads * NRB;
     hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       glog, S0, dS, M, range_flags, n_seq, G, n_heads, S_start, S_T);
+                       gdecay, S0, dS, M, range_flags, n_seq, G, n_heads, S_start, S_T);
     return hipGetLastError();
 }
 
