@@ -73,16 +73,19 @@ inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32
 // n_units_seq sequences (or segments, through cu and the dense split), with the
 // diagonal blocks of the chunk solve's A records, the schedule (packed input) and the
 // range marks.  NOOUT: no outputs (o is not written); SPLIT: the state enters K S^T as
-// hi + lo bf16.  flags: SCAN_ZERO_V (v read as zero), SCAN_S0_IDENTITY (S0 = I, d_v = d_k).
+// hi + lo bf16.  flags: SCAN_ZERO_V (v read as zero), SCAN_S0_IDENTITY (S0 = I, d_v = d_k),
+// SCAN_STATE_AFRAG / SCAN_STATE_DFRAG (S_T stored in MFMA fragment order, kda_mfma.h).
 // gdecay (or null): every unit's total decay per value row, [n_units_seq, H, d_v].
 template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
 hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
                               const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
                               float* gdecay, int32_t* range_flags, hipStream_t stream);
 
-// Composes the segment states of the sequence-parallel prefill (kda_segments.hip).
+// Composes the segment states of the sequence-parallel prefill (kda_segments.hip) from
+// every segment's transition (Mf) and end state from zero (dSf), both in MFMA fragment
+// order; G even.
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dS, const float* M,
+hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dSf, const float* Mf,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, hipStream_t stream);
 

@@ -12,9 +12,29 @@ namespace kda {
 namespace {
 
 constexpr int C = PREFILL_CHUNK_BF16;  // 64 tokens per chunk
-// scan flags: v read as zero; S0 taken as the identity (d_v = d_k)
+// scan flags: v read as zero; S0 taken as the identity (d_v = d_k); S_T stored in the
+// order of 16x16x32 MFMA fragments, as the A operand of S^T (hi and lo bf16 parts) or as
+// a 16x16 accumulator (fp32) -- the layouts the segment composition reads
 constexpr int SCAN_ZERO_V = 1;
 constexpr int SCAN_S0_IDENTITY = 2;
+constexpr int SCAN_STATE_AFRAG = 4;
+constexpr int SCAN_STATE_DFRAG = 8;
+
+// Fragment layouts of a d_v x d_k state S of one (sequence, head), 16-row blocks rb and
+// 16-column tiles w (NW = d_k / 16 of them), lane l = 16 g + i of a wave, 16 bytes per
+// lane, so that a wave reads 1 KB contiguous at a time:
+//  - accumulator (DFRAG), fp32: the f32x4 at index (rb NW + w) 64 + l holds
+//    S[16 rb + i][16 w + 4 g + e];
+//  - A operand of S^T (AFRAG, d_v = d_k), bf16: the 8 values at index ((kb 2 + part) NW
+//    + w) 64 + l (part 0 = hi, 1 = lo) hold that part of S[32 kb + 4 g + (e & 3) + 16 (e
+//    >> 2)][16 w + i], e = 0 .. 7: lane l's reduction values in the stacked order of a
+//    16x16x32 MFMA, ready to use.
+__device__ __forceinline__ int64_t dfrag_index(int rb, int w, int lane, int nw) {
+    return (static_cast<int64_t>(rb) * nw + w) * 64 + lane;
+}
+__device__ __forceinline__ int64_t afrag_index(int w, int kb, int part, int lane, int nw) {
+    return ((static_cast<int64_t>(kb) * 2 + part) * nw + w) * 64 + lane;
+}
 constexpr int BV = 64;                 // value rows per scan workgroup
 constexpr int PAD = 8;                 // bf16 row padding (16 bytes) against bank conflicts
 constexpr int CP = C + PAD;            // pitch of bf16 rows of length C

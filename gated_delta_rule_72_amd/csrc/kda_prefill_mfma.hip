@@ -372,27 +372,28 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     }
 
     // Sequence-parallel path (d_k = d_v, few units, long sequences), on the 32-token scan:
-    //   1. dS: each segment's end state from a zero start, and its total decay per value
-    //      row (no outputs);
+    //   1. dS: each segment's end state from a zero start (in accumulator fragment
+    //      order), and its total decay per value row (no outputs);
     //   2. M: each segment's key-side transition, from S0 = I with v = 0 and no gate,
     //      the state split hi + lo in K S^T (nothing decays, so its rounding would
-    //      otherwise reach the composed states in full; no outputs);
+    //      otherwise reach the composed states in full; no outputs), stored as the
+    //      A operands of M^T (fragment order, hi and lo bf16);
     //   3. the segments' true starting states (and S_T), in order per (sequence, head);
     //   4. every segment again from its starting state, writing o.
     // An empty segment has dS = 0, M = I and no decay.
     const size_t sb = segment_state_bytes(a.n_seq, a.n_heads, DK, DV, G);
     float* dS = reinterpret_cast<float*>(ws + L.seg);
-    float* Mt = reinterpret_cast<float*>(ws + L.seg + sb);
+    float* Mf = reinterpret_cast<float*>(ws + L.seg + sb);
     float* Sst = reinterpret_cast<float*>(ws + L.seg + 2 * sb);
     float* gdec = reinterpret_cast<float*>(ws + L.seg + 3 * sb);
-    if ((e = launch_scan32_pass<DK, DV, GATE, true, false>(a, ns, cu, order, chunk_off, arec, nullptr, dS, 0, gdec, rf,
-                                                           stream)) != hipSuccess)
+    if ((e = launch_scan32_pass<DK, DV, GATE, true, false>(a, ns, cu, order, chunk_off, arec, nullptr, dS,
+                                                           SCAN_STATE_DFRAG, gdec, rf, stream)) != hipSuccess)
         return e;
-    if ((e = launch_scan32_pass<DK, DK, GATE_NONE, true, true>(a, ns, cu, order, chunk_off, arec, nullptr, Mt,
-                                                               SCAN_ZERO_V | SCAN_S0_IDENTITY, nullptr, nullptr,
+    if ((e = launch_scan32_pass<DK, DK, GATE_NONE, true, true>(a, ns, cu, order, chunk_off, arec, nullptr, Mf,
+                                                               SCAN_ZERO_V | SCAN_S0_IDENTITY | SCAN_STATE_AFRAG, nullptr, nullptr,
                                                                stream)) != hipSuccess)
         return e;
-    if ((e = launch_combine_segments<DK, DV>(gdec, a.S0, dS, Mt, rf, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
+    if ((e = launch_combine_segments<DK, DV>(gdec, a.S0, dS, Mf, rf, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
         hipSuccess)
         return e;
     if ((e = launch_scan32_pass<DK, DV, GATE, false, false>(a, ns, cu, order, chunk_off, arec, Sst, nullptr, 0, nullptr,

@@ -279,12 +279,13 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const int64_t H = n_heads;
     const int h = u.head;
     if (range_flags) {
-        static_assert(R <= 64 && 64 % R == 0, "a workgroup's rows lie in one block of 64");
-        // (no short-circuit: the flags are loaded together, not one after another)
+        static_assert(R <= 64 && 64 % R == 0 && NT % 64 == 0, "a workgroup's rows lie in one block of 64; whole waves");
+        // one segment's flag per lane, so the flags are loaded together, not one after
+        // another; every wave reaches the same answer
         bool marked = false;
-        for (int g = 0; g < flag_segs; ++g)
+        for (int g = tid % 64; g < flag_segs; g += 64)
             marked |= range_flags[((static_cast<int64_t>(u.seq) * flag_segs + g) * H + h) * (DV / 64) + row0 / 64] != 0;
-        if (!marked) return;
+        if (__ballot(marked) == 0) return;
     }
 
     const int64_t s_row = ((static_cast<int64_t>(u.seq) * H + h) * DV + row0 + r) * DK;

@@ -13,126 +13,172 @@
 // every segment in parallel (two scans), this kernel walks the segments of
 // each (sequence, head) in order to get every segment's true starting state,
 // and a last scan reruns each segment from it.
-#include "kda_device.h"
-#include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 
-// One workgroup of 512 threads per (sequence, head, block of rows).  A row's
-// d_k outputs are d_k / 4 column groups of four key channels, and each product
-// S M is split over KS = 4 quarters of the reduction index k, so a thread
-// accumulates 4 columns over d_k / 4 values of k and the quarters are summed
-// through LDS (4 rows per workgroup at d_k = 128, 8 at 64).
-// For segment g = 0 .. G-1 of sequence n:
+// One workgroup per (sequence, head, block of 16 value rows r), one wave per 16
+// key columns c (d_k / 16 waves).  For segment g = 0 .. G-1 of sequence n:
 //     S_start[n G + g] = S                      (S = S0[n], or zeros, for g = 0)
 //     S = diag(gamma_g) S M_g + dS_g
-// and S_T[n] = S after the last segment.  gamma_g is the segment's total decay
-// per value row (the product of its gates), written by the scan that produced dS.
-// M_{g+1}, dS_{g+1} and gamma_{g+1} are loaded into registers while segment g is
-// composed, so a step waits only for its own LDS products.
-// Layouts: dS, S_start [n_seq G, H, d_v, d_k]; M [n_seq G, H, d_k, d_k];
+// and S_T[n] = S after the last segment (G even).  gamma_g is the segment's total
+// decay per value row (the product of its gates), written by the scan that produced dS.
+// Each step runs transposed, (S M)^T = M^T S^T, on v_mfma_f32_16x16x32_bf16 with
+// both fp32 operands split into hi + lo bf16 parts (hi hi + hi lo + lo hi, so a
+// term is off by about 2^-16 of its size, against 2^-8 for plain bf16):
+//   A = M^T [c][k]: the scan that produced M stored these operands, hi and lo parts
+//       already split, in fragment order (Mf below), so a wave reads each with one
+//       16-byte load per lane over 1 KB of whole 128-byte lines.  (One CU
+//       streams too few lines at a time from L2 to read a transition per step as
+//       rows: 16 lanes on 16 rows touch 16 lines with half of each.)
+//   B = S^T [k][r]: the accumulator tiles of the state.  Wave w holds rows
+//       16w .. 16w + 15 of S^T, i.e. lane (g, i) holds S[r0 + i][16w + 4g + j] in
+//       register j; two such tiles are exactly one stacked B operand, so each wave
+//       splits its tile, leaves it in LDS, and reads every tile back.
+// dS comes in accumulator order (dSf), one 16-byte load per lane as well.  M, dS and
+// gamma of the next two segments are in flight while a step runs.
+// Layouts, per (segment n G + g, head h) block of d_v d_k floats: Mf in the A-operand
+// fragment order of the transposed state, dSf in the accumulator fragment order (both
+// as the 32-token scan writes them with SCAN_STATE_AFRAG / SCAN_STATE_DFRAG); S_start
+// [n_seq G, H, d_v, d_k] row-major;
 // gdecay [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
 // range_flags [n_seq G, H, d_v / 64] (or null): segments whose scan met a chunk
 // beyond the decay range of the factored form; their dS is not valid, so a
 // workgroup whose rows belong to such a segment leaves S_T unwritten (S0 stays
 // intact when S_T aliases it) for the token-recurrent pass that follows.
 template <int DK, int DV>
-__global__ __launch_bounds__(512) void combine_segments_kernel(
-    const float* __restrict__ gdecay, const float* __restrict__ S0, const float* __restrict__ dS,
-    const float* __restrict__ M, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
+__global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
+    const float* __restrict__ gdecay, const float* __restrict__ S0, const float* __restrict__ dSf,
+    const float* __restrict__ Mf, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
     float* __restrict__ S_start, float* __restrict__ S_T) {
-    constexpr int NT = 512;
-    constexpr int KS = 4;                 // quarters of the reduction index
-    constexpr int CG = DK / 4;            // column groups per row
-    constexpr int ROWS = NT / (CG * KS);  // rows per workgroup
-    constexpr int NRB = DV / ROWS;        // row blocks per head
-    constexpr int KQ = DK / KS;           // values of k per quarter
-    constexpr int MP = DK * DK / 4 / NT;  // 16-byte pieces of M per thread
-    static_assert(DV % ROWS == 0, "rows per workgroup");
-    __shared__ __align__(16) float Ms[DK * DK];
-    __shared__ __align__(16) float Ss[ROWS * DK];
-    __shared__ __align__(16) float Ps[KS * ROWS * DK];  // partial sums per quarter
+    static_assert(DK == DV, "the transition M acts on the state's key side and has d_k rows");
+    constexpr int NW = DK / 16;  // waves: one 16-column tile of S each
+    constexpr int KB = DK / 32;  // stacked reduction blocks
+    constexpr int NRB = DV / 16;
+    __shared__ __align__(16) u32x4 X[2][NW][64];  // split state tiles, by step parity
 
+    // Workgroups go round-robin to the 8 XCDs (block b to XCD b % 8), and each XCD has
+    // its own L2: the NRB row blocks of a (sequence, head) read the same transitions,
+    // so they are given blocks of one residue mod 8 and share that XCD's L2 copy.
     const int b = blockIdx.x;
-    const int rblk = b % NRB, unit = b / NRB;
+    const int n_units = n_seq * n_heads;
+    const int n_comp = (n_units + 7) / 8 * 8 * NRB;  // composing workgroups; the rest warm the L2
+    if (b >= n_comp) {
+        // One CU fetches only so many lines from beyond its L2 at a time, too few to stream
+        // a 64 KB transition per step, so the workgroups past n_comp touch one word of
+        // every 128-byte line of the transitions and dS of the units on their XCD (x =
+        // b % 8, segment-major) first, and the composing workgroups find them in that L2.
+        const int x = b % 8, wj = (b - n_comp) / 8, nwj = (gridDim.x - n_comp) / 8;
+        const int upx = (n_units - x + 7) / 8;  // units u < n_units with u % 8 = x
+        const int64_t chunks = static_cast<int64_t>(upx) * 2 * G;
+        float acc = 0.f;
+        for (int64_t c = wj; c < chunks; c += nwj) {
+            const int kind = static_cast<int>(c & 1);
+            const int64_t q = c >> 1;
+            const int u = static_cast<int>(q % upx) * 8 + x, g = static_cast<int>(q / upx);
+            const int64_t sg = static_cast<int64_t>(u / n_heads) * G + g;
+            const float* base = (kind ? dSf : Mf) + (sg * n_heads + u % n_heads) * DK * DK;
+            for (int l = threadIdx.x; l < DK * DK / 32; l += blockDim.x) acc += base[32 * l];
+        }
+        asm volatile("" ::"v"(acc));  // (keeps the loads)
+        return;
+    }
+    const int rblk = (b / 8) % NRB, unit = (b / (8 * NRB)) * 8 + b % 8;
     const int h = unit % n_heads, n = unit / n_heads;
-    if (n >= n_seq) return;
-    const int tid = threadIdx.x;
-    const int c4 = 4 * (tid % CG), r = (tid / CG) % ROWS, q = tid / (CG * ROWS);
-    const bool owner = q == 0;  // the threads of quarter 0 hold the state
-    const int i = rblk * ROWS + r;  // value row
+    if (n >= n_seq) return;  // (the grid is rounded up to whole groups of 8 units)
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = lane & 15, gq = lane >> 4;
+    const int r = rblk * 16 + i;   // value row of this lane
+    const int c4 = 16 * w + 4 * gq;  // first of its four key columns
     const int64_t H = n_heads;
-    const int64_t row_off = static_cast<int64_t>(i) * DK + c4;
+    const int64_t row_off = static_cast<int64_t>(r) * DK + c4;
     auto seg_of = [&](int g) { return static_cast<int64_t>(n) * G + g; };
 
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if (owner && S0) s = *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off);
-    f32x4 mreg[MP], dnext = {0.f, 0.f, 0.f, 0.f};
-    float gnext = 1.f;
-    auto load_next = [&](int g) {
-        const int64_t sg = seg_of(g);
-        const float* Mg = M + (sg * H + h) * DK * DK;
-#pragma unroll
-        for (int p = 0; p < MP; ++p) mreg[p] = *reinterpret_cast<const f32x4*>(Mg + 4 * (tid + NT * p));
-        if (owner) {
-            dnext = *reinterpret_cast<const f32x4*>(dS + (sg * H + h) * DV * DK + row_off);
-            gnext = gdecay[(sg * H + h) * DV + i];
-        }
+    struct Next {
+        u32x4 m[KB][2];  // A operands of M^T, hi and lo bf16
+        f32x4 d;         // dS[r][c4 .. c4 + 3]
+        float gam;       // gamma[r]
     };
-    load_next(0);
-    for (int g = 0; g < G; ++g) {
-        if (owner) {
-            *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
-            *reinterpret_cast<f32x4*>(Ss + r * DK + c4) = s;
-        }
+    auto load = [&](Next& x, int g) {
+        const int64_t sg = seg_of(g);
+        const u32x4* Mg = reinterpret_cast<const u32x4*>(Mf + (sg * H + h) * DK * DK);
 #pragma unroll
-        for (int p = 0; p < MP; ++p) *reinterpret_cast<f32x4*>(Ms + 4 * (tid + NT * p)) = mreg[p];
-        const f32x4 d = dnext;
-        const float gam = gnext;
-        if (g + 1 < G) load_next(g + 1);
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int part = 0; part < 2; ++part) x.m[kb][part] = Mg[afrag_index(w, kb, part, lane, NW)];
+        x.d = reinterpret_cast<const f32x4*>(dSf + (sg * H + h) * DV * DK)[dfrag_index(rblk, w, lane, NW)];
+        x.gam = gdecay[(sg * H + h) * DV + r];
+    };
+
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const Next& x, int g) {
+        if (g > 0) *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
+        uint32_t h01, l01, h23, l23;
+        split_bf16x2(s[0], s[1], h01, l01);
+        split_bf16x2(s[2], s[3], h23, l23);
+        X[g & 1][w][lane] = u32x4{h01, h23, l01, l23};
         __syncthreads();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int kk = 0; kk < KQ; ++kk) {
-            const int k = q * KQ + kk;
-            const float sk = Ss[r * DK + k];
-            const f32x4 mk = *reinterpret_cast<const f32x4*>(Ms + k * DK + c4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += sk * mk[e];
+        for (int kb = 0; kb < KB; ++kb) {
+            const u32x4 t0 = X[g & 1][2 * kb][lane], t1 = X[g & 1][2 * kb + 1][lane];
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t1[0], t1[1]});
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{t0[2], t0[3], t1[2], t1[3]});
+            const bf16x8 a_hi = __builtin_bit_cast(bf16x8, x.m[kb][0]);
+            const bf16x8 a_lo = __builtin_bit_cast(bf16x8, x.m[kb][1]);
+            acc = mfma16(a_lo, bh, acc);
+            acc = mfma16(a_hi, bl, acc);
+            acc = mfma16(a_hi, bh, acc);
         }
-        *reinterpret_cast<f32x4*>(Ps + (q * ROWS + r) * DK + c4) = acc;
-        __syncthreads();  // partials complete; Ms and Ss are free for the next segment
-        if (owner) {
-            f32x4 t = *reinterpret_cast<const f32x4*>(Ps + r * DK + c4);
 #pragma unroll
-            for (int qq = 1; qq < KS; ++qq) {
-                const f32x4 pq = *reinterpret_cast<const f32x4*>(Ps + (qq * ROWS + r) * DK + c4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] += pq[e];
+        for (int j = 0; j < 4; ++j) s[j] = x.gam * acc[j] + x.d[j];
+    };
+    // Two sets of next-segment values in flight: segment g uses set g & 1, which is
+    // refilled with segment g + 2 once the step has consumed it.  The loop's first
+    // pass only loads (one load site per set, so the wait counts are the same on
+    // every pass) and takes the entering state and the range marks in (its store
+    // waits for them there, not at the top of a later pass).  The loads are unconditional (the last ones
+    // reread segment G - 1), so the sets stay in their registers instead of being
+    // copied, which would wait for them.  The scheduling barriers keep each reload
+    // after the step that reads the set: hoisted above it, the step splits the set
+    // early and so waits for both sets.
+    Next xa, xb;
+    bool beyond = false;  // a segment of these rows is marked beyond the decay range
+    for (int g = -2; g < G; g += 2) {
+        if (g >= 0) step(xa, g);
+        __builtin_amdgcn_sched_barrier(0);
+        load(xa, min(g + 2, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (g >= 0) step(xb, g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load(xb, min(g + 3, G - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (g < 0) {
+            // the segments' range marks, one per lane (read together, not one after another)
+            bool mark = false;
+            if (range_flags) {
+                const int vb = (rblk * 16) / 64;  // the scan's block of 64 rows that holds these rows
+                for (int gg = lane; gg < G; gg += 64) mark |= range_flags[(seg_of(gg) * H + h) * (DV / 64) + vb] != 0;
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] = gam * t[e] + d[e];
+            if (S0) s = *reinterpret_cast<const f32x4*>(S0 + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off);
+            *reinterpret_cast<f32x4*>(S_start + (seg_of(0) * H + h) * DV * DK + row_off) = s;
+            beyond = __ballot(mark) != 0;
         }
-        // Ps is rewritten only after the next segment's first barrier, which every
-        // owner reaches after reading it here
     }
-    bool beyond = false;
-    if (range_flags) {
-        const int vb = (rblk * ROWS) / 64;  // the scan's block of 64 rows that holds these rows
-        for (int g = 0; g < G; ++g) beyond |= range_flags[(seg_of(g) * H + h) * (DV / 64) + vb] != 0;
-    }
-    if (owner && S_T && !beyond)
+    if (S_T && !beyond)
         *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
 }
 
 template <int DK, int DV>
-hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dS, const float* M,
+hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dSf, const float* Mf,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, hipStream_t stream) {
-    constexpr int NRB = DV / (512 / (DK / 4 * 4));
-    const int64_t grid = static_cast<int64_t>(n_seq) * n_heads * NRB;
-    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
-                       gdecay, S0, dS, M, range_flags, n_seq, G, n_heads, S_start, S_T);
+    if (G < 2 || G % 2) return hipErrorInvalidValue;
+    // composing workgroups, then 24 L2-warming workgroups per XCD
+    const int64_t grid = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16) + 8 * 24;
+    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(64 * (DK / 16)), 0,
+                       stream,
+                       gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start, S_T);
     return hipGetLastError();
 }
 
