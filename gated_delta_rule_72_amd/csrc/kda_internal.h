@@ -81,6 +81,15 @@ hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32
                               const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
                               float* gdecay, int32_t* range_flags, hipStream_t stream);
 
+// The sequence-parallel prefill's two output-free passes in one launch (kda_prefill_scan32.hip):
+// every segment's end state from zero (dS, accumulator fragment order), its total decay per
+// value row (gdecay) and range marks, and its transition from S0 = I with v = 0 and no gate
+// (Mf, A-operand fragment order); d_v = d_k.
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32_pair(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
+                              const int32_t* chunk_off, const uint16_t* arec, float* dS, float* gdecay,
+                              int32_t* range_flags, float* Mf, hipStream_t stream);
+
 // Composes the segment states of the sequence-parallel prefill (kda_segments.hip) from
 // every segment's transition (Mf) and end state from zero (dSf), both in MFMA fragment
 // order; G even.

@@ -386,12 +386,8 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     float* Mf = reinterpret_cast<float*>(ws + L.seg + sb);
     float* Sst = reinterpret_cast<float*>(ws + L.seg + 2 * sb);
     float* gdec = reinterpret_cast<float*>(ws + L.seg + 3 * sb);
-    if ((e = launch_scan32_pass<DK, DV, GATE, true, false>(a, ns, cu, order, chunk_off, arec, nullptr, dS,
-                                                           SCAN_STATE_DFRAG, gdec, rf, stream)) != hipSuccess)
-        return e;
-    if ((e = launch_scan32_pass<DK, DK, GATE_NONE, true, true>(a, ns, cu, order, chunk_off, arec, nullptr, Mf,
-                                                               SCAN_ZERO_V | SCAN_S0_IDENTITY | SCAN_STATE_AFRAG, nullptr, nullptr,
-                                                               stream)) != hipSuccess)
+    if ((e = launch_scan32_pair<DK, DV, GATE>(a, ns, cu, order, chunk_off, arec, dS, gdec, rf, Mf, stream)) !=
+        hipSuccess)
         return e;
     if ((e = launch_combine_segments<DK, DV>(gdec, a.S0, dS, Mf, rf, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
         hipSuccess)

@@ -92,9 +92,11 @@ struct Scan32Smem {
     static constexpr int TOTAL = 2 * (RK + RQ + RA + RX + RG + RB) + RS + RU + RO + RT;
 };
 
-template <int DK, int DV, int GATE, bool NOOUT = false, bool SPLIT = false, bool CKPT = false>
-__global__ __launch_bounds__(512) void scan32_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+// The scan of the unit that workgroup `block` maps to (the kernels below).  alpha null with a
+// gate: every gate is 1 (the transitions' pass, launched together with a gated pass).
+template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT, bool CKPT>
+__device__ __forceinline__ void scan32_body(
+    int64_t block, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
     int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T, int flags,
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     __shared__ __align__(16) float Tot[2][BV][4];           // loader totals, per value row
     __shared__ int beyond_s[4];
 
-    const Unit u = map_unit(blockIdx.x, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
+    const Unit u = map_unit(block, n_seq, n_heads, NVB, n_tok, cu_seqlens, order);
     if (!u.valid) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -261,9 +263,12 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         const int b0 = LS0 + LSN * x;
         // (v reads as zero when the flag asks for it: an empty range)
         const auto rv = make_rsrc(v + tok0 * DV + i0, any && !(flags & SCAN_ZERO_V) ? ((n - 1) * row_v + BV) * 2 : 0);
-        const auto rl = GATE == GATE_CHANNEL ? make_rsrc(alpha + tok0 * DV + i0, any ? ((n - 1) * row_v + BV) * 4 : 0)
-                        : GATE == GATE_SCALAR ? make_rsrc(alpha + tok0, any ? ((n - 1) * H + 1) * 4 : 0)
-                                              : make_rsrc(alpha, 0);
+        // (without alpha -- a gated instantiation run with every gate 1 -- an empty range:
+        // the loads return 0 and touch no memory, and local_scan takes 1 for them)
+        const bool gl = any && alpha != nullptr;
+        const auto rl = GATE == GATE_CHANNEL && gl ? make_rsrc(alpha + tok0 * DV + i0, ((n - 1) * row_v + BV) * 4)
+                        : GATE == GATE_SCALAR && gl ? make_rsrc(alpha + tok0, ((n - 1) * H + 1) * 4)
+                                                    : make_rsrc(alpha, 0);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int e = static_cast<int>((8 * lw + r) * row_v + lane);
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         float run = 1.f, amin = 1.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            a[r] = GATE != GATE_NONE && 8 * lw + r < n ? R[b0 + LL + r / 4][r % 4] : 1.f;
+            a[r] = GATE != GATE_NONE && alpha && 8 * lw + r < n ? R[b0 + LL + r / 4][r % 4] : 1.f;
             run *= a[r];
             amin = fminf(amin, a[r]);
             R[b0 + LL + r / 4][r % 4] = run;
@@ -618,7 +623,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
         block_sync();
         if (S_T && !unit_beyond()) {
             float* st = S_T + (static_cast<int64_t>(u.seq) * H + h) * DV * DK;
-            if (NOOUT && (flags & SCAN_STATE_DFRAG)) {  // (the fragment orders only for the output-free passes)
+            if (NOOUT && SPLIT && !CKPT && (flags & SCAN_STATE_DFRAG)) {  // (fragment orders: the paired passes only)
                 // the chain registers are already in accumulator order: 1 KB per store
 #pragma unroll
                 for (int ib = 0; ib < NIB; ++ib)
@@ -626,7 +631,7 @@ __global__ __launch_bounds__(512) void scan32_kernel(
                     for (int jt = 0; jt < NJ; ++jt)
                         reinterpret_cast<f32x4*>(st)[dfrag_index((i0 + rb + 16 * ib) / 16, jt, lane, NJ)] =
                             R[ib * NJ + jt];
-            } else if (NOOUT && SPLIT && (flags & SCAN_STATE_AFRAG)) {
+            } else if (NOOUT && SPLIT && !CKPT && (flags & SCAN_STATE_AFRAG)) {
                 // Element (row rw + (lane & 15), column 16 jt + 4 (lane >> 4) + e) of S belongs
                 // to fragment lane 16 ((lane & 15) >> 2) + 4 (lane >> 4) + e at stacked position
                 // (lane & 3) + 4 ((rw / 16) & 1).  Each element is split into hi + lo bf16 (one
@@ -697,6 +702,48 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     }
 }
 
+template <int DK, int DV, int GATE, bool NOOUT = false, bool SPLIT = false, bool CKPT = false>
+__global__ __launch_bounds__(512) void scan32_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
+    int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T, int flags,
+    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
+    scan32_body<DK, DV, GATE, NOOUT, SPLIT, CKPT>(blockIdx.x, q, k, v, alpha, S0, cu_seqlens, order, chunk_off, arec,
+                                                  n_seq, n_tok, n_heads, o, S_T, flags, gdecay, range_flags, ckpt);
+}
+
+// The arguments of one output-free pass.
+struct Scan32PassArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* alpha;
+    const int32_t* cu_seqlens;
+    const int32_t* order;
+    const int32_t* chunk_off;
+    const uint16_t* arec;
+    int n_seq, n_tok, n_heads;
+    float* S_T;
+    int flags;
+    float* gdecay;
+    int32_t* range_flags;
+};
+
+// Two output-free passes with the state split (NOOUT, SPLIT), over units of the same
+// count, in one launch: blocks below nb1 run the first, the rest the second.  Both run the
+// same code on the same LDS variables (48 KB a workgroup), so a CU holds a workgroup of
+// each at once and the two passes' latency-bound steps overlap, where one after the other
+// they would each leave the CUs half used.
+template <int DK, int DV, int GATE>
+__global__ __launch_bounds__(512) void scan32_pair_kernel(Scan32PassArgs p1, Scan32PassArgs p2, int nb1) {
+    const bool first = static_cast<int>(blockIdx.x) < nb1;
+    const Scan32PassArgs& p = first ? p1 : p2;
+    scan32_body<DK, DV, GATE, true, true, false>(first ? blockIdx.x : blockIdx.x - nb1, nullptr, p.k, p.v, p.alpha,
+                                                 nullptr, p.cu_seqlens, p.order, p.chunk_off, p.arec, p.n_seq,
+                                                 p.n_tok, p.n_heads, nullptr, p.S_T, p.flags, p.gdecay,
+                                                 p.range_flags, nullptr);
+}
+
 }  // namespace
 
 template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
@@ -710,6 +757,39 @@ hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha, S0, cu,
                        cu ? order : nullptr, chunk_off, arec, n_units_seq, a.n_tok, a.n_heads,
                        NOOUT ? nullptr : static_cast<uint16_t*>(a.o), S_T, flags, gdecay, range_flags, nullptr);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int GATE>
+hipError_t launch_scan32_pair(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
+                              const int32_t* chunk_off, const uint16_t* arec, float* dS, float* gdecay,
+                              int32_t* range_flags, float* Mf, hipStream_t stream) {
+    static_assert(DK == DV, "the transitions are d_k x d_k");
+    constexpr int NVB = DV / BV;
+    const int64_t nb1 = prefill_grid(static_cast<int64_t>(n_units_seq) * a.n_heads, NVB);
+    Scan32PassArgs p1;
+    p1.k = static_cast<const uint16_t*>(a.k);
+    p1.v = static_cast<const uint16_t*>(a.v);
+    p1.alpha = a.alpha;
+    p1.cu_seqlens = cu;
+    p1.order = cu ? order : nullptr;
+    p1.chunk_off = chunk_off;
+    p1.arec = arec;
+    p1.n_seq = n_units_seq;
+    p1.n_tok = a.n_tok;
+    p1.n_heads = a.n_heads;
+    p1.S_T = dS;
+    p1.flags = SCAN_STATE_DFRAG;
+    p1.gdecay = gdecay;
+    p1.range_flags = range_flags;
+    Scan32PassArgs p2 = p1;
+    p2.alpha = nullptr;  // no gate
+    p2.S_T = Mf;
+    p2.flags = SCAN_ZERO_V | SCAN_S0_IDENTITY | SCAN_STATE_AFRAG;
+    p2.gdecay = nullptr;
+    p2.range_flags = nullptr;
+    hipLaunchKernelGGL((scan32_pair_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(2 * nb1)), dim3(512), 0, stream,
+                       p1, p2, static_cast<int>(nb1));
     return hipGetLastError();
 }
 
@@ -743,11 +823,20 @@ KDA_SCAN32(128, 128)
 KDA_SCAN32(64, 64)
 KDA_SCAN32(128, 64)
 KDA_SCAN32(64, 128)
-KDA_SCAN32_PASS(128, 128, GATE_NONE, true, true)
-KDA_SCAN32_PASS(64, 64, GATE_NONE, true, true)
 #undef KDA_SCAN32
 #undef KDA_SCAN32_G
 #undef KDA_SCAN32_PASS
+#define KDA_SCAN32_PAIR(DK, GATE)                                                                                   \
+    template hipError_t launch_scan32_pair<DK, DK, GATE>(const PrefillArgs&, int, const int32_t*, const int32_t*,  \
+                                                         const int32_t*, const uint16_t*, float*, float*, int32_t*, \
+                                                         float*, hipStream_t);
+KDA_SCAN32_PAIR(128, GATE_CHANNEL)
+KDA_SCAN32_PAIR(128, GATE_SCALAR)
+KDA_SCAN32_PAIR(128, GATE_NONE)
+KDA_SCAN32_PAIR(64, GATE_CHANNEL)
+KDA_SCAN32_PAIR(64, GATE_SCALAR)
+KDA_SCAN32_PAIR(64, GATE_NONE)
+#undef KDA_SCAN32_PAIR
 #define KDA_SCAN32_CKPT(DK, DV, GATE)                                                                               \
     template hipError_t launch_scan32_ckpt<DK, DV, GATE>(const BackwardArgs&, const int32_t*, const int32_t*,      \
                                                          const uint16_t*, int32_t*, float*, hipStream_t);

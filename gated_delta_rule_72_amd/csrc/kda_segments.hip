@@ -61,28 +61,6 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
     // its own L2: the NRB row blocks of a (sequence, head) read the same transitions,
     // so they are given blocks of one residue mod 8 and share that XCD's L2 copy.
     const int b = blockIdx.x;
-    const int n_units = n_seq * n_heads;
-    const int n_comp = (n_units + 7) / 8 * 8 * NRB;  // composing workgroups; the rest warm the L2
-    if (b >= n_comp) {
-        // One CU fetches only so many lines from beyond its L2 at a time, too few to stream
-        // a 64 KB transition per step, so the workgroups past n_comp touch one word of
-        // every 128-byte line of the transitions and dS of the units on their XCD (x =
-        // b % 8, segment-major) first, and the composing workgroups find them in that L2.
-        const int x = b % 8, wj = (b - n_comp) / 8, nwj = (gridDim.x - n_comp) / 8;
-        const int upx = (n_units - x + 7) / 8;  // units u < n_units with u % 8 = x
-        const int64_t chunks = static_cast<int64_t>(upx) * 2 * G;
-        float acc = 0.f;
-        for (int64_t c = wj; c < chunks; c += nwj) {
-            const int kind = static_cast<int>(c & 1);
-            const int64_t q = c >> 1;
-            const int u = static_cast<int>(q % upx) * 8 + x, g = static_cast<int>(q / upx);
-            const int64_t sg = static_cast<int64_t>(u / n_heads) * G + g;
-            const float* base = (kind ? dSf : Mf) + (sg * n_heads + u % n_heads) * DK * DK;
-            for (int l = threadIdx.x; l < DK * DK / 32; l += blockDim.x) acc += base[32 * l];
-        }
-        asm volatile("" ::"v"(acc));  // (keeps the loads)
-        return;
-    }
     const int rblk = (b / 8) % NRB, unit = (b / (8 * NRB)) * 8 + b % 8;
     const int h = unit % n_heads, n = unit / n_heads;
     if (n >= n_seq) return;  // (the grid is rounded up to whole groups of 8 units)
@@ -137,11 +115,12 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
     // refilled with segment g + 2 once the step has consumed it.  The loop's first
     // pass only loads (one load site per set, so the wait counts are the same on
     // every pass) and takes the entering state and the range marks in (its store
-    // waits for them there, not at the top of a later pass).  The loads are unconditional (the last ones
-    // reread segment G - 1), so the sets stay in their registers instead of being
-    // copied, which would wait for them.  The scheduling barriers keep each reload
-    // after the step that reads the set: hoisted above it, the step splits the set
-    // early and so waits for both sets.
+    // waits for them there, not at the top of a later pass).  The loads are
+    // unconditional (the last ones reread segment G - 1), so the sets stay in their
+    // registers instead of being copied, which would wait for them.  The scheduling
+    // barriers keep each reload after the step that reads the set: hoisted above it,
+    // the step splits the set early and so waits for both sets.  (Deeper prefetch
+    // measured slower: a step is bound by the CU's vector-memory issue, not latency.)
     Next xa, xb;
     bool beyond = false;  // a segment of these rows is marked beyond the decay range
     for (int g = -2; g < G; g += 2) {
@@ -174,8 +153,7 @@ hipError_t launch_combine_segments(const float* gdecay, const float* S0, const f
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, hipStream_t stream) {
     if (G < 2 || G % 2) return hipErrorInvalidValue;
-    // composing workgroups, then 24 L2-warming workgroups per XCD
-    const int64_t grid = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16) + 8 * 24;
+    const int64_t grid = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16);
     hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(64 * (DK / 16)), 0,
                        stream,
                        gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start, S_T);
