@@ -76,10 +76,14 @@ inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32
 // hi + lo bf16.  flags: SCAN_ZERO_V (v read as zero), SCAN_S0_IDENTITY (S0 = I, d_v = d_k),
 // SCAN_STATE_AFRAG / SCAN_STATE_DFRAG (S_T stored in MFMA fragment order, kda_mfma.h).
 // gdecay (or null): every unit's total decay per value row, [n_units_seq, H, d_v].
+// skip_flags (or null): range marks [n_units_seq, H, d_v / 64] of segments, skip_segs
+// consecutive units to a sequence; a unit is skipped (nothing written) when any segment
+// of its sequence is marked for its block of rows.
 template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
 hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
                               const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
-                              float* gdecay, int32_t* range_flags, hipStream_t stream);
+                              float* gdecay, int32_t* range_flags, hipStream_t stream,
+                              const int32_t* skip_flags = nullptr, int skip_segs = 1);
 
 // The sequence-parallel prefill's two output-free passes in one launch (kda_prefill_scan32.hip):
 // every segment's end state from zero (dS, accumulator fragment order), its total decay per
@@ -90,13 +94,26 @@ hipError_t launch_scan32_pair(const PrefillArgs& a, int n_units_seq, const int32
                               const int32_t* chunk_off, const uint16_t* arec, float* dS, float* gdecay,
                               int32_t* range_flags, float* Mf, hipStream_t stream);
 
+// The inputs and outputs of the token-recurrent recomputation that the segment
+// composition runs for units marked beyond the decay range (the call's own, not the
+// segments').
+struct SegmentFixupArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* alpha;
+    const float* beta;
+    const int32_t* cu_seqlens;
+    int n_tok;
+    uint16_t* o;
+};
 // Composes the segment states of the sequence-parallel prefill (kda_segments.hip) from
 // every segment's transition (Mf) and end state from zero (dSf), both in MFMA fragment
-// order; G even.
-template <int DK, int DV>
+// order; G even.  With range_flags it also recomputes the marked units token by token.
+template <int DK, int DV, int GATE>
 hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dSf, const float* Mf,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
-                                   float* S_T, hipStream_t stream);
+                                   float* S_T, const SegmentFixupArgs& fx, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

@@ -378,8 +378,9 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     //      the state split hi + lo in K S^T (nothing decays, so its rounding would
     //      otherwise reach the composed states in full; no outputs), stored as the
     //      A operands of M^T (fragment order, hi and lo bf16);
-    //   3. the segments' true starting states (and S_T), in order per (sequence, head);
-    //   4. every segment again from its starting state, writing o.
+    //   3. the segments' true starting states (and S_T), in order per (sequence, head),
+    //      and the token-recurrent recomputation of units marked beyond the decay range;
+    //   4. every segment again from its starting state, writing o (marked units skipped).
     // An empty segment has dS = 0, M = I and no decay.
     const size_t sb = segment_state_bytes(a.n_seq, a.n_heads, DK, DV, G);
     float* dS = reinterpret_cast<float*>(ws + L.seg);
@@ -389,13 +390,22 @@ static hipError_t launch_bf16_t(const PrefillArgs& a, hipStream_t stream) {
     if ((e = launch_scan32_pair<DK, DV, GATE>(a, ns, cu, order, chunk_off, arec, dS, gdec, rf, Mf, stream)) !=
         hipSuccess)
         return e;
-    if ((e = launch_combine_segments<DK, DV>(gdec, a.S0, dS, Mf, rf, a.n_seq, G, a.n_heads, Sst, a.S_T, stream)) !=
-        hipSuccess)
+    // marked units are recomputed token by token inside the composition's launch, and the
+    // output pass skips them
+    SegmentFixupArgs fx;
+    fx.q = static_cast<const uint16_t*>(a.q);
+    fx.k = static_cast<const uint16_t*>(a.k);
+    fx.v = static_cast<const uint16_t*>(a.v);
+    fx.alpha = a.alpha;
+    fx.beta = a.beta;
+    fx.cu_seqlens = a.cu_seqlens;
+    fx.n_tok = a.n_tok;
+    fx.o = static_cast<uint16_t*>(a.o);
+    if ((e = launch_combine_segments<DK, DV, GATE>(gdec, a.S0, dS, Mf, rf, a.n_seq, G, a.n_heads, Sst, a.S_T, fx,
+                                                   stream)) != hipSuccess)
         return e;
-    if ((e = launch_scan32_pass<DK, DV, GATE, false, false>(a, ns, cu, order, chunk_off, arec, Sst, nullptr, 0, nullptr,
-                                                            nullptr, stream)) != hipSuccess)
-        return e;
-    return rf ? launch_prefill_range_fixup(a, rf, G, stream) : hipSuccess;
+    return launch_scan32_pass<DK, DV, GATE, false, false>(a, ns, cu, order, chunk_off, arec, Sst, nullptr, 0, nullptr,
+                                                          nullptr, stream, rf, G);
 }
 
 // The chunked backward's forward pass (see kda_backward_chunk.hip).

@@ -100,7 +100,8 @@ __device__ __forceinline__ void scan32_body(
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
     int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T, int flags,
-    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
+    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt,
+    const int32_t* __restrict__ skip_flags, int skip_segs) {
     static_assert(!CKPT || (NOOUT && SPLIT), "the checkpoint variant has no output side and splits the state");
     using SM = Scan32Smem<DK>;
     static_assert(SM::TOTAL <= 160 * 1024, "LDS budget");
@@ -141,6 +142,14 @@ __device__ __forceinline__ void scan32_body(
     const int64_t H = n_heads;
     const int h = u.head;
     const int i0 = u.vblk * BV;
+    if (skip_flags) {
+        // a unit of a sequence that another pass recomputes token by token: any of the
+        // skip_segs segments of its sequence marked for this block of rows (one per lane)
+        const int64_t n0 = u.seq / skip_segs * static_cast<int64_t>(skip_segs);
+        bool m = false;
+        for (int g = lane; g < skip_segs; g += 64) m |= skip_flags[((n0 + g) * H + h) * NVB + u.vblk] != 0;
+        if (__ballot(m) != 0) return;
+    }
     const int64_t row_qk = H * DK, row_v = H * DV;
     const int chunk0 = first_chunk(u.seq, n_seq, n_tok, chunk_off);
     const int n_steps = static_cast<int>((u.t1 - u.t0 + H32 - 1) / H32);
@@ -708,9 +717,11 @@ __global__ __launch_bounds__(512) void scan32_kernel(
     const float* __restrict__ alpha, const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, const int32_t* __restrict__ chunk_off, const uint16_t* __restrict__ arec,
     int n_seq, int n_tok, int n_heads, uint16_t* __restrict__ o, float* __restrict__ S_T, int flags,
-    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt) {
+    float* __restrict__ gdecay, int32_t* __restrict__ range_flags, float* __restrict__ ckpt,
+    const int32_t* __restrict__ skip_flags, int skip_segs) {
     scan32_body<DK, DV, GATE, NOOUT, SPLIT, CKPT>(blockIdx.x, q, k, v, alpha, S0, cu_seqlens, order, chunk_off, arec,
-                                                  n_seq, n_tok, n_heads, o, S_T, flags, gdecay, range_flags, ckpt);
+                                                  n_seq, n_tok, n_heads, o, S_T, flags, gdecay, range_flags, ckpt,
+                                                  skip_flags, skip_segs);
 }
 
 // The arguments of one output-free pass.
@@ -741,7 +752,7 @@ __global__ __launch_bounds__(512) void scan32_pair_kernel(Scan32PassArgs p1, Sca
     scan32_body<DK, DV, GATE, true, true, false>(first ? blockIdx.x : blockIdx.x - nb1, nullptr, p.k, p.v, p.alpha,
                                                  nullptr, p.cu_seqlens, p.order, p.chunk_off, p.arec, p.n_seq,
                                                  p.n_tok, p.n_heads, nullptr, p.S_T, p.flags, p.gdecay,
-                                                 p.range_flags, nullptr);
+                                                 p.range_flags, nullptr, nullptr, 1);
 }
 
 }  // namespace
@@ -749,14 +760,16 @@ __global__ __launch_bounds__(512) void scan32_pair_kernel(Scan32PassArgs p1, Sca
 template <int DK, int DV, int GATE, bool NOOUT, bool SPLIT>
 hipError_t launch_scan32_pass(const PrefillArgs& a, int n_units_seq, const int32_t* cu, const int32_t* order,
                               const int32_t* chunk_off, const uint16_t* arec, const float* S0, float* S_T, int flags,
-                              float* gdecay, int32_t* range_flags, hipStream_t stream) {
+                              float* gdecay, int32_t* range_flags, hipStream_t stream, const int32_t* skip_flags,
+                              int skip_segs) {
     constexpr int NVB = DV / BV;
     const int64_t grid = prefill_grid(static_cast<int64_t>(n_units_seq) * a.n_heads, NVB);
     hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, NOOUT, SPLIT>), dim3(static_cast<unsigned>(grid)), dim3(512), 0,
                        stream, NOOUT ? nullptr : static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.alpha, S0, cu,
                        cu ? order : nullptr, chunk_off, arec, n_units_seq, a.n_tok, a.n_heads,
-                       NOOUT ? nullptr : static_cast<uint16_t*>(a.o), S_T, flags, gdecay, range_flags, nullptr);
+                       NOOUT ? nullptr : static_cast<uint16_t*>(a.o), S_T, flags, gdecay, range_flags, nullptr,
+                       skip_flags, skip_segs);
     return hipGetLastError();
 }
 
@@ -802,14 +815,14 @@ hipError_t launch_scan32_ckpt(const BackwardArgs& a, const int32_t* order, const
     hipLaunchKernelGGL((scan32_kernel<DK, DV, GATE, true, true, true>), dim3(static_cast<unsigned>(grid)), dim3(512),
                        0, stream, nullptr, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        a.alpha, a.S0, cu, cu ? order : nullptr, chunk_off, arec, a.n_seq, a.n_tok, a.n_heads, nullptr,
-                       nullptr, 0, nullptr, range_flags, ckpt);
+                       nullptr, 0, nullptr, range_flags, ckpt, nullptr, 1);
     return hipGetLastError();
 }
 
 #define KDA_SCAN32_PASS(DK, DV, GATE, NOOUT, SPLIT)                                                                \
     template hipError_t launch_scan32_pass<DK, DV, GATE, NOOUT, SPLIT>(                                           \
         const PrefillArgs&, int, const int32_t*, const int32_t*, const int32_t*, const uint16_t*, const float*,  \
-        float*, int, float*, int32_t*, hipStream_t);
+        float*, int, float*, int32_t*, hipStream_t, const int32_t*, int);
 // the output pass and the segments' end-state pass for each gate; the transitions' pass
 // (no gate, state split) where d_v = d_k
 #define KDA_SCAN32_G(DK, DV, GATE)             \

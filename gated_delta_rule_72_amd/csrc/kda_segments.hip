@@ -14,6 +14,7 @@
 // each (sequence, head) in order to get every segment's true starting state,
 // and a last scan reruns each segment from it.
 #include "kda_mfma.h"
+#include "kda_staged.h"
 
 namespace kda {
 
@@ -44,13 +45,17 @@ namespace kda {
 // gdecay [n_seq G, H, d_v]; S0, S_T [n_seq, H, d_v, d_k].
 // range_flags [n_seq G, H, d_v / 64] (or null): segments whose scan met a chunk
 // beyond the decay range of the factored form; their dS is not valid, so a
-// workgroup whose rows belong to such a segment leaves S_T unwritten (S0 stays
-// intact when S_T aliases it) for the token-recurrent pass that follows.
-template <int DK, int DV>
+// workgroup whose rows belong to such a segment leaves S_T unwritten.  The
+// workgroups past the composing ones are the token-recurrent recomputation of such
+// units (the staged form, kda_staged.h, over the whole sequence from S0, writing o
+// and S_T; a workgroup returns at once for an unmarked unit), run here rather than
+// after the output pass, which skips the marked units.  Their S_start is never read,
+// so the composing workgroups' read of S0 there does not matter when S_T aliases S0.
+template <int DK, int DV, int GATE>
 __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
     const float* __restrict__ gdecay, const float* __restrict__ S0, const float* __restrict__ dSf,
     const float* __restrict__ Mf, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
-    float* __restrict__ S_start, float* __restrict__ S_T) {
+    float* __restrict__ S_start, float* __restrict__ S_T, SegmentFixupArgs fx) {
     static_assert(DK == DV, "the transition M acts on the state's key side and has d_k rows");
     constexpr int NW = DK / 16;  // waves: one 16-column tile of S each
     constexpr int KB = DK / 32;  // stacked reduction blocks
@@ -61,6 +66,16 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
     // its own L2: the NRB row blocks of a (sequence, head) read the same transitions,
     // so they are given blocks of one residue mod 8 and share that XCD's L2 copy.
     const int b = blockIdx.x;
+    const int n_comp = (n_seq * n_heads + 7) / 8 * 8 * NRB;
+    if (b >= n_comp) {
+        // the fixup: rows per workgroup and lanes per row so that it has this kernel's
+        // workgroup size (64 x 8 lanes at d_k = 128, 16 x 16 at 64)
+        constexpr int FR = DK == 128 ? 64 : 16, FL = 64 * (DK / 16) / FR;
+        prefill_staged_body<uint16_t, DK, DV, GATE, FR, FL, false>(
+            b - n_comp, fx.q, fx.k, fx.v, fx.alpha, fx.beta, S0, fx.cu_seqlens, nullptr, n_seq, fx.n_tok, n_heads, fx.o,
+            S_T, nullptr, range_flags, G);
+        return;
+    }
     const int rblk = (b / 8) % NRB, unit = (b / (8 * NRB)) * 8 + b % 8;
     const int h = unit % n_heads, n = unit / n_heads;
     if (n >= n_seq) return;  // (the grid is rounded up to whole groups of 8 units)
@@ -148,21 +163,30 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
         *reinterpret_cast<f32x4*>(S_T + (static_cast<int64_t>(n) * H + h) * DV * DK + row_off) = s;
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int GATE>
 hipError_t launch_combine_segments(const float* gdecay, const float* S0, const float* dSf, const float* Mf,
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
-                                   float* S_T, hipStream_t stream) {
+                                   float* S_T, const SegmentFixupArgs& fx, hipStream_t stream) {
     if (G < 2 || G % 2) return hipErrorInvalidValue;
-    const int64_t grid = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16);
-    hipLaunchKernelGGL((combine_segments_kernel<DK, DV>), dim3(static_cast<unsigned>(grid)), dim3(64 * (DK / 16)), 0,
-                       stream,
-                       gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start, S_T);
+    constexpr int FR = DK == 128 ? 64 : 16;
+    const int64_t n_comp = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16);
+    const int64_t n_fix = range_flags ? prefill_grid(static_cast<int64_t>(n_seq) * n_heads, DV / FR) : 0;
+    hipLaunchKernelGGL((combine_segments_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(n_comp + n_fix)),
+                       dim3(64 * (DK / 16)), 0, stream, gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start,
+                       S_T, fx);
     return hipGetLastError();
 }
 
-template hipError_t launch_combine_segments<128, 128>(const float*, const float*, const float*, const float*,
-                                                      const int32_t*, int, int, int, float*, float*, hipStream_t);
-template hipError_t launch_combine_segments<64, 64>(const float*, const float*, const float*, const float*,
-                                                    const int32_t*, int, int, int, float*, float*, hipStream_t);
+#define KDA_COMBINE(DK, GATE)                                                                                      \
+    template hipError_t launch_combine_segments<DK, DK, GATE>(const float*, const float*, const float*,           \
+                                                              const float*, const int32_t*, int, int, int, float*, \
+                                                              float*, const SegmentFixupArgs&, hipStream_t);
+KDA_COMBINE(128, GATE_CHANNEL)
+KDA_COMBINE(128, GATE_SCALAR)
+KDA_COMBINE(128, GATE_NONE)
+KDA_COMBINE(64, GATE_CHANNEL)
+KDA_COMBINE(64, GATE_SCALAR)
+KDA_COMBINE(64, GATE_NONE)
+#undef KDA_COMBINE
 
 }  // namespace kda
