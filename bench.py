@@ -188,16 +188,17 @@ def summarize(path):
 
 
 TRAFFIC_PREFILL_SOURCES = ["kda_prefill_mfma.hip", "kda_prefill_scan32.hip", "kda_mfma.h", "kda_solve.h",
-                           "kda_device.h", "kda_schedule.h", "kda_internal.h", "kda_prefill_valu.hip"]
+                           "kda_device.h", "kda_schedule.h", "kda_internal.h", "kda_prefill_valu.hip",
+                           "kda_staged.h"]
 # call -> (probe, kernel-name pieces, one kernel per piece; None = every kda kernel of the probe, sources)
 TRAFFIC_CALLS = {
-    "prefill": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 0, false>",
+    "prefill": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 0, false, false, false>",
                          "prefill_staged_kernel<unsigned short, 128, 128, 0, 64, 8, false>"], TRAFFIC_PREFILL_SOURCES),
-    "prefill_scalar_gate": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 1, false>",
+    "prefill_scalar_gate": ("main", ["chunk_solve_kernel<128, false, true>", "scan32_kernel<128, 128, 1, false, false, false>",
                                      "prefill_staged_kernel<unsigned short, 128, 128, 1, 64, 8, false>"],
                             TRAFFIC_PREFILL_SOURCES),
     "decode": ("main", ["decode_step_kernel<unsigned short, 128, 128, 0>"], ["kda_decode.hip", "kda_device.h"]),
-    "backward": ("extra", ["chunk_solve_kernel<128, true, false>", "scan32_kernel<128, 128, 0, true>",
+    "backward": ("extra", ["chunk_solve_kernel<128, true, false>", "scan32_kernel<128, 128, 0, true, true, true>",
                            "bwd_state_scan_kernel<128, 128, 0>", "bwd_chunk_grad_kernel<128, 128, 0>",
                            "backward_kernel<unsigned short, 128, 128, 0>"],
                  TRAFFIC_PREFILL_SOURCES + ["kda_backward.hip", "kda_backward_chunk.hip"]),
@@ -251,7 +252,8 @@ def write_traffic(base):
                     sys.exit(f"{call}: {len(ks)} kernels match {piece!r}")
                 names.append(ks[0])
         out[call] = dict(sources=src, source_sha256=source_hash(src), probe=mode,
-                         kernels=[n.split("(")[0].replace("void ", "").replace("kda::", "") for n in names],
+                         kernels=[n.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+                                  .replace("kda::", "") for n in names],
                          fetch_kib=round(sum(f[n] for n in names), 1), write_kib=round(sum(w.get(n, 0.0) for n in names), 1),
                          fetch_scale=round(fs, 4), write_scale=round(ws, 4))
         r, wr = 1024 * out[call]["fetch_kib"] * fs, 1024 * out[call]["write_kib"] * ws
