@@ -56,17 +56,20 @@ constexpr int PREFILL_CHUNK_BF16 = 64;
 // per sequence).  Calls whose (sequence, head, 64-row block) units would leave
 // most of the 256 CUs idle have each sequence cut into G segments of whole
 // 64-token chunks (G a power of two, units x G at most 256 workgroups, on
-// average at least two chunks per segment).  Each segment is scanned three
-// times, so the split pays only from G = 8 on (measured: G = 2 is 1.7x slower
-// than one scan, G = 4 about even, G >= 8 faster).  Needs d_k = d_v.  Decided
-// from the sizes alone (the host never reads cu_seqlens).
+// average at least two chunks per segment).  Each segment is scanned twice more
+// than one scan would (its end state and transition, in one launch), so the split
+// pays from G = 4 on (measured, ms per call: 2 x 8192 tokens, 32 heads, G = 2:
+// 0.549 against 0.404 for one scan; G = 4: 1 x 8192, 32 heads, 0.308 against
+// 0.372; 2 x 4096, 16 heads, 0.154 against 0.194; 1 x 2048, 32 heads, 0.091
+// against 0.102).  Needs d_k = d_v.  Decided from the sizes alone (the host never
+// reads cu_seqlens).
 inline int prefill_segments(int32_t n_seq, int32_t n_tok, int32_t n_heads, int32_t d_k, int32_t d_v) {
     if (d_k != d_v || n_tok <= 0 || n_seq < 1) return 1;
     const int64_t units = static_cast<int64_t>(n_seq) * n_heads * (d_v / 64);
     const int64_t avg = n_tok / n_seq;
     int g = 1;
     while (units * 2 * g <= 256 && avg / (2 * g) >= 2 * 64) g *= 2;
-    return g >= 8 ? g : 1;
+    return g >= 4 ? g : 1;
 }
 
 // One pass of the bf16 prefill's scan in 32-token steps (kda_prefill_scan32.hip) over

@@ -80,11 +80,11 @@ def test_key_gate_workspace_size(L):
 
 def test_workspace_size_of_split_calls(L):
     """Calls with few (sequence, head) units are split into G segments per sequence
-    (G >= 8, units x G <= 256, on average two chunks or more per segment); their
+    (G >= 4, units x G <= 256, on average two chunks or more per segment); their
     workspace adds the segment bookkeeping and states.  Layout, 256-byte aligned parts:
     order NS int32, chunk offsets NS+1, segment offsets NS+1 (split calls only),
     decay-range marks NS x H x d/64 int32, A records (n_tok/64 + n_seq) x H x 12 KiB,
-    then dS, M, S_start (NS x H x d x d fp32 each) and the log2-decays (NS x H x d fp32),
+    then dS, M, S_start (NS x H x d x d fp32 each) and the total decays (NS x H x d fp32),
     NS = n_seq G."""
     al = lambda x: (x + 255) // 256 * 256
     rec = 3 * 2 * 32 * 32 * 2
@@ -100,13 +100,16 @@ def test_workspace_size_of_split_calls(L):
     assert L.kda_prefill_workspace_size(1, 65573, 4, 128, 128, 1) == split_size(1, 65573, 4, 128, 32)
     # d = 64, one head: 1 unit, 2048 tokens -> G = 16
     assert L.kda_prefill_workspace_size(1, 2048, 1, 64, 64, 1) == split_size(1, 2048, 1, 64, 16)
-    # not split: 256 units (the batched workload), G < 8 (two sequences of 8192 tokens,
-    # 32 heads), segments too short (512 tokens, 8 heads: G would be 4), d_k != d_v, fp32
+    # 512 tokens, 8 heads: 16 units, segments of two chunks -> G = 4
+    assert L.kda_prefill_workspace_size(1, 512, 8, 128, 128, 1) == split_size(1, 512, 8, 128, 4)
+    # not split: 256 units (the batched workload), G < 4 (two sequences of 8192 tokens,
+    # 32 heads: G would be 2), segments too short (256 tokens, 8 heads: G would be 2),
+    # d_k != d_v, fp32
     unsplit = lambda n_seq, n_tok, H, dv=128: (al(n_seq * 4) + al((n_seq + 1) * 4) + al(n_seq * H * (dv // 64) * 4)
                                                + al((n_tok // 64 + n_seq) * H * rec))
     assert L.kda_prefill_workspace_size(4, 32768, 32, 128, 128, 1) == unsplit(4, 32768, 32)
     assert L.kda_prefill_workspace_size(2, 16384, 32, 128, 128, 1) == unsplit(2, 16384, 32)
-    assert L.kda_prefill_workspace_size(1, 512, 8, 128, 128, 1) == unsplit(1, 512, 8)
+    assert L.kda_prefill_workspace_size(1, 256, 8, 128, 128, 1) == unsplit(1, 256, 8)
     assert L.kda_prefill_workspace_size(1, 1024, 8, 128, 128, 1) == split_size(1, 1024, 8, 128, 8)
     assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 64, 1) == unsplit(1, 4096, 8, 64)
     assert L.kda_prefill_workspace_size(1, 4096, 8, 128, 128, 0) == 256
