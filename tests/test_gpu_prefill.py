@@ -125,7 +125,8 @@ def test_dense_and_varlen_calls_agree_bit_for_bit(torch_cuda):
 
 # Sequence-parallel path: equal-length batches with few (sequence, head) units split
 # every sequence into G segments (dS, M, composition, rerun).  G per case:
-# [1024] x 2 heads at d=128 -> 8; [2048] x 1 head at d=64 -> 16; [2048, 2048] x 1 -> 16.
+# [1024] x 2 heads at d=128 -> 8; [2048] x 1 head at d=64 -> 16; [2048, 2048] x 1 -> 16;
+# [512] x 16 heads at d=128 -> 4 (the fewest segments the split takes, two chunks each).
 # With the workloads' gates (alpha ~ 0.93 per token) a segment's start state decays by
 # ~1e-4 over 128 tokens, so the composition through M is also checked with alpha = 1
 # ("ones": no decay), where every segment's start state depends on it in full.
@@ -135,6 +136,8 @@ def test_dense_and_varlen_calls_agree_bit_for_bit(torch_cuda):
     ([2048], 1, 64, 0.0, "exp_softplus"),
     ([2048, 2048], 1, 128, 0.02, "ones"),
     ([1024], 2, 64, 0.02, "ones"),
+    ([512], 16, 128, 0.02, "exp_softplus"),
+    ([512], 16, 128, 0.0, "ones"),
 ])
 def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0, alpha_kind):
     from gated_delta_rule_72_amd import kda
@@ -157,11 +160,13 @@ def test_sequence_parallel_path_matches_oracle(torch_cuda, gate, lens, H, d, s0,
 # Split calls that are not equal multiples of G chunks describe their segments by token
 # offsets built on the device: a ragged dense sequence (2100 tokens = 33 chunks, the last
 # partial, 2 heads: G = 16 segments of 3 chunks, the last 5 empty) and packed sequences
-# (G = 8; 77 tokens fill 2 of their 8 segments, and the empty sequence none).
+# (G = 8; 77 tokens fill 2 of their 8 segments, and the empty sequence none; with 16
+# heads G = 4, and the 700-token sequence's 11 chunks leave its last segment 2).
 @pytest.mark.parametrize("alpha_kind", ["exp_softplus", "ones"])
 @pytest.mark.parametrize("lens,H,varlen", [
     ([2100], 2, False),
     ([3000, 0, 1500, 77], 2, True),
+    ([1500, 700], 16, True),
 ])
 def test_sequence_parallel_path_ragged_and_packed(torch_cuda, lens, H, varlen, alpha_kind):
     print(f"prefill sequence-parallel (segment offsets) lens={lens} H={H} varlen={varlen} {alpha_kind}",
