@@ -188,6 +188,28 @@ __device__ __forceinline__ bf16x8 frag_tr_st(const uint16_t* base, int pitch, in
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// 4 x 4 transpose within each quad of lanes: quad lane j holds row j of the quad's block
+// in a[0 .. 3] before, and column j (a[e] = the former a[j] of quad lane e) after.  Two
+// butterfly stages -- DPP exchanges with the lane 1 and then 2 apart, selects on that lane
+// bit -- so no register is indexed by a lane-dependent value (the compiler turns such an
+// index into branches).
+__device__ __forceinline__ void quad_transpose4(u32x4& a, int lane) {
+    const bool b0 = lane & 1, b1 = lane & 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t rcv =
+            __builtin_amdgcn_mov_dpp(b0 ? a[2 * c] : a[2 * c + 1], 0xB1, 0xF, 0xF, true);  // quad lanes 1,0,3,2
+        a[2 * c] = b0 ? rcv : a[2 * c];
+        a[2 * c + 1] = b0 ? a[2 * c + 1] : rcv;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t rcv = __builtin_amdgcn_mov_dpp(b1 ? a[c] : a[c + 2], 0x4E, 0xF, 0xF, true);  // quad lanes 2,3,0,1
+        a[c] = b1 ? rcv : a[c];
+        a[c + 2] = b1 ? a[c + 2] : rcv;
+    }
+}
+
 // Where 16-byte piece `piece` of a solved record goes in a [t][s] hi/lo pair of
 // C x CP buffers: block b (rows 0-31 x cols 0-31, rows 32-63 x cols 0-31, rows
 // 32-63 x cols 32-63), half (hi, lo), row, 8-column group.

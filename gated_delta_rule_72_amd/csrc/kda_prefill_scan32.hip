@@ -646,11 +646,8 @@ __device__ __forceinline__ void scan32_body(
                 // (lane & 3) + 4 ((rw / 16) & 1).  Each element is split into hi + lo bf16 (one
                 // 32-bit word), and a 4 x 4 transpose of the words within each quad of lanes
                 // gives lane q the four positions of fragment lane ... + q: 8 bytes of hi and 8
-                // of lo per tile.  The transpose is two butterfly stages (DPP exchanges with the
-                // lane 1 and lane 2 apart, selects on that lane bit), with no lane-dependent
-                // register index.
+                // of lo per tile.
                 uint16_t* sb = reinterpret_cast<uint16_t*>(st);
-                const bool b0 = lane & 1, b1 = lane & 2;
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
                 for (int ib = 0; ib < NIB; ++ib) {
@@ -659,27 +656,14 @@ __device__ __forceinline__ void scan32_body(
                     const int hb = 4 * ((rw >> 4) & 1);
 #pragma unroll
                     for (int jt = 0; jt < NJ; ++jt) {
-                        uint32_t a[4];  // hi | lo << 16
+                        u32x4 a;  // hi | lo << 16
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             uint32_t hi, lo;
                             split_bf16x2(R[ib * NJ + jt][e], 0.f, hi, lo);
                             a[e] = (hi & 0xffffu) | (lo << 16);
                         }
-#pragma unroll
-                        for (int c = 0; c < 2; ++c) {  // 2 x 2 blocks across lanes 1 apart
-                            const uint32_t rcv =
-                                __builtin_amdgcn_mov_dpp(b0 ? a[2 * c] : a[2 * c + 1], 0xB1, 0xF, 0xF, true);  // quad 1,0,3,2
-                            a[2 * c] = b0 ? rcv : a[2 * c];
-                            a[2 * c + 1] = b0 ? a[2 * c + 1] : rcv;
-                        }
-#pragma unroll
-                        for (int c = 0; c < 2; ++c) {  // then across lanes 2 apart
-                            const uint32_t rcv =
-                                __builtin_amdgcn_mov_dpp(b1 ? a[c] : a[c + 2], 0x4E, 0xF, 0xF, true);  // quad 2,3,0,1
-                            a[c] = b1 ? rcv : a[c];
-                            a[c + 2] = b1 ? a[c + 2] : rcv;
-                        }
+                        quad_transpose4(a, lane);
                         const u32x2 hi2 = {(a[0] & 0xffffu) | (a[1] << 16), (a[2] & 0xffffu) | (a[3] << 16)};
                         const u32x2 lo2 = {(a[0] >> 16) | (a[1] & 0xffff0000u), (a[2] >> 16) | (a[3] & 0xffff0000u)};
                         *reinterpret_cast<u32x2*>(sb + afrag_index(jt, rw >> 5, 0, fl, NJ) * 8 + hb) = hi2;
