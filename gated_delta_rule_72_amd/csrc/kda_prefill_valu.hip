@@ -185,8 +185,9 @@ __global__ __launch_bounds__(L * R) void prefill_staged_kernel(
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
     T* __restrict__ o, float* __restrict__ S_T, float* __restrict__ ckpt,
     const int32_t* __restrict__ range_flags, int flag_segs) {
-    prefill_staged_body<T, DK, DV, GATE, R, L, CKPT>(blockIdx.x, q, k, v, alpha, beta, S0, cu_seqlens, order, n_seq,
-                                                     n_tok, n_heads, o, S_T, ckpt, range_flags, flag_segs);
+    __shared__ StageBuf<DK, GATE, R> buf[2];
+    prefill_staged_body<T, DK, DV, GATE, R, L, CKPT>(buf, blockIdx.x, q, k, v, alpha, beta, S0, cu_seqlens, order,
+                                                     n_seq, n_tok, n_heads, o, S_T, ckpt, range_flags, flag_segs);
 }
 
 template <typename T, int DK, int DV, int GATE, int R, int L = 8>

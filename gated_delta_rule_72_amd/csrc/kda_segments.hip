@@ -18,8 +18,9 @@
 
 namespace kda {
 
-// One workgroup per (sequence, head, block of 16 value rows r), one wave per 16
-// key columns c (d_k / 16 waves).  For segment g = 0 .. G-1 of sequence n:
+// One workgroup per (sequence, head, block of 16 value rows r): d_k / 16 composing waves,
+// one per 16 key columns c, and as many loader waves.  For segment g = 0 .. G-1 of
+// sequence n:
 //     S_start[n G + g] = S                      (S = S0[n], or zeros, for g = 0)
 //     S = diag(gamma_g) S M_g + dS_g
 // and S_T[n] = S after the last segment (G even).  gamma_g is the segment's total
@@ -28,16 +29,19 @@ namespace kda {
 // both fp32 operands split into hi + lo bf16 parts (hi hi + hi lo + lo hi, so a
 // term is off by about 2^-16 of its size, against 2^-8 for plain bf16):
 //   A = M^T [c][k]: the scan that produced M stored these operands, hi and lo parts
-//       already split, in fragment order (Mf below), so a wave reads each with one
-//       16-byte load per lane over 1 KB of whole 128-byte lines.  (One CU
-//       streams too few lines at a time from L2 to read a transition per step as
-//       rows: 16 lanes on 16 rows touch 16 lines with half of each.)
+//       already split, in fragment order (Mf below).  The loader waves copy each
+//       segment's 1 KB fragments into one of two LDS buffers two steps ahead (every
+//       load 1 KB contiguous), and a composing wave reads its operands from there.
+//       (A CU issues a transition's 64 loads per step slowly enough that a composing
+//       wave issuing them itself stalls its MFMA chain behind them.)
 //   B = S^T [k][r]: the accumulator tiles of the state.  Wave w holds rows
 //       16w .. 16w + 15 of S^T, i.e. lane (g, i) holds S[r0 + i][16w + 4g + j] in
 //       register j; two such tiles are exactly one stacked B operand, so each wave
 //       splits its tile, leaves it in LDS, and reads every tile back.
-// dS comes in accumulator order (dSf), one 16-byte load per lane as well.  M, dS and
-// gamma of the next two segments are in flight while a step runs.
+// dS comes in accumulator order (dSf), one 16-byte load per lane; dS and gamma of the
+// next two segments are in the composing waves' registers.  One barrier per step: before
+// it, the step's state tiles and transition fragments are written (state exchange and
+// fragment buffer both by step parity); after it, read.
 // Layouts, per (segment n G + g, head h) block of d_v d_k floats: Mf in the A-operand
 // fragment order of the transposed state, dSf in the accumulator fragment order (both
 // as the 32-token scan writes them with SCAN_STATE_AFRAG / SCAN_STATE_DFRAG); S_start
@@ -51,16 +55,33 @@ namespace kda {
 // and S_T; a workgroup returns at once for an unmarked unit), run here rather than
 // after the output pass, which skips the marked units.  Their S_start is never read,
 // so the composing workgroups' read of S0 there does not matter when S_T aliases S0.
+template <int DK>
+struct CombineShape {
+    static constexpr int NW = DK / 16;          // composing waves (and loader waves)
+    static constexpr int NT = 2 * 64 * NW;      // threads
+    static constexpr int KB = DK / 32;          // stacked reduction blocks
+    static constexpr int NF = NW * KB * 2;      // 1 KB fragments of one transition
+    static constexpr int FPL = NF / NW;         // fragments per loader wave
+    static constexpr int FR = 64, FL = NT / FR; // the fixup's rows and lanes per row
+    static constexpr int COMB_BYTES = (2 * NF + 2 * NW) * 1024;
+};
+
 template <int DK, int DV, int GATE>
-__global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
+__global__ __launch_bounds__(CombineShape<DK>::NT) void combine_segments_kernel(
     const float* __restrict__ gdecay, const float* __restrict__ S0, const float* __restrict__ dSf,
     const float* __restrict__ Mf, const int32_t* __restrict__ range_flags, int n_seq, int G, int n_heads,
     float* __restrict__ S_start, float* __restrict__ S_T, SegmentFixupArgs fx) {
     static_assert(DK == DV, "the transition M acts on the state's key side and has d_k rows");
-    constexpr int NW = DK / 16;  // waves: one 16-column tile of S each
-    constexpr int KB = DK / 32;  // stacked reduction blocks
+    using SH = CombineShape<DK>;
+    constexpr int NW = SH::NW, KB = SH::KB, NF = SH::NF, FPL = SH::FPL, FR = SH::FR, FL = SH::FL;
     constexpr int NRB = DV / 16;
-    __shared__ __align__(16) u32x4 X[2][NW][64];  // split state tiles, by step parity
+    using FixBuf = StageBuf<DK, GATE, FR>;
+    constexpr int SMEM = SH::COMB_BYTES > 2 * static_cast<int>(sizeof(FixBuf)) ? SH::COMB_BYTES
+                                                                              : 2 * static_cast<int>(sizeof(FixBuf));
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    __shared__ __align__(16) unsigned char smem[SMEM];
+    u32x4(*MB)[NF][64] = reinterpret_cast<u32x4(*)[NF][64]>(smem);                 // [parity][fragment][lane]
+    u32x4(*X)[NW][64] = reinterpret_cast<u32x4(*)[NW][64]>(smem + 2 * NF * 1024);  // [parity][tile][lane]
 
     // Workgroups go round-robin to the 8 XCDs (block b to XCD b % 8), and each XCD has
     // its own L2: the NRB row blocks of a (sequence, head) read the same transitions,
@@ -68,41 +89,76 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
     const int b = blockIdx.x;
     const int n_comp = (n_seq * n_heads + 7) / 8 * 8 * NRB;
     if (b >= n_comp) {
-        // the fixup: rows per workgroup and lanes per row so that it has this kernel's
-        // workgroup size (64 x 8 lanes at d_k = 128, 16 x 16 at 64)
-        constexpr int FR = DK == 128 ? 64 : 16, FL = 64 * (DK / 16) / FR;
+        // the fixup, 64 rows per workgroup with this kernel's threads as the lanes per row
         prefill_staged_body<uint16_t, DK, DV, GATE, FR, FL, false>(
-            b - n_comp, fx.q, fx.k, fx.v, fx.alpha, fx.beta, S0, fx.cu_seqlens, nullptr, n_seq, fx.n_tok, n_heads, fx.o,
-            S_T, nullptr, range_flags, G);
+            reinterpret_cast<FixBuf*>(smem), b - n_comp, fx.q, fx.k, fx.v, fx.alpha, fx.beta, S0, fx.cu_seqlens,
+            nullptr, n_seq, fx.n_tok, n_heads, fx.o, S_T, nullptr, range_flags, G);
         return;
     }
     const int rblk = (b / 8) % NRB, unit = (b / (8 * NRB)) * 8 + b % 8;
     const int h = unit % n_heads, n = unit / n_heads;
     if (n >= n_seq) return;  // (the grid is rounded up to whole groups of 8 units)
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int i = lane & 15, gq = lane >> 4;
-    const int r = rblk * 16 + i;   // value row of this lane
-    const int c4 = 16 * w + 4 * gq;  // first of its four key columns
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t H = n_heads;
-    const int64_t row_off = static_cast<int64_t>(r) * DK + c4;
     auto seg_of = [&](int g) { return static_cast<int64_t>(n) * G + g; };
 
+    // Both roles run G barriers, one per step, at the same points: a role's loop body is
+    // unrolled over the two parities and its first pass only loads (one load site per
+    // register set, so the wait counts are the same on every pass).  The loads are
+    // unconditional (the last ones reread segment G - 1), so the sets stay in their
+    // registers instead of being copied, which would wait for them; the scheduling
+    // barriers keep each reload after the code that reads the set.
+    if (w >= NW) {
+        // ---- loader wave: fragments lw FPL .. + FPL - 1 of every transition
+        const int lw = w - NW;
+        struct LSet {
+            u32x4 m[FPL];
+        };
+        auto lload = [&](LSet& x, int g) {
+            const u32x4* Mg = reinterpret_cast<const u32x4*>(Mf + (seg_of(g) * H + h) * DK * DK) + lw * FPL * 64;
+#pragma unroll
+            for (int p = 0; p < FPL; ++p) x.m[p] = Mg[p * 64 + lane];
+        };
+        auto lwrite = [&](const LSet& x, int par) {
+#pragma unroll
+            for (int p = 0; p < FPL; ++p) MB[par][lw * FPL + p][lane] = x.m[p];
+        };
+        // segment j's fragments go into buffer j & 1 before barrier j (which the composing
+        // step j waits for); that buffer was last read in step j - 2, before barrier j - 1
+        LSet la, lb;
+        for (int j = -2; j < G; j += 2) {
+            if (j >= 0) {
+                lwrite(la, 0);
+                __syncthreads();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lload(la, min(j + 2, G - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (j >= 0) {
+                lwrite(lb, 1);
+                __syncthreads();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lload(lb, min(j + 3, G - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+    }
+
+    // ---- composing wave w: key columns 16 w .. +15
+    const int i = lane & 15, gq = lane >> 4;
+    const int r = rblk * 16 + i;     // value row of this lane
+    const int c4 = 16 * w + 4 * gq;  // first of its four key columns
+    const int64_t row_off = static_cast<int64_t>(r) * DK + c4;
     struct Next {
-        u32x4 m[KB][2];  // A operands of M^T, hi and lo bf16
-        f32x4 d;         // dS[r][c4 .. c4 + 3]
-        float gam;       // gamma[r]
+        f32x4 d;    // dS[r][c4 .. c4 + 3]
+        float gam;  // gamma[r]
     };
     auto load = [&](Next& x, int g) {
         const int64_t sg = seg_of(g);
-        const u32x4* Mg = reinterpret_cast<const u32x4*>(Mf + (sg * H + h) * DK * DK);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int part = 0; part < 2; ++part) x.m[kb][part] = Mg[afrag_index(w, kb, part, lane, NW)];
         x.d = reinterpret_cast<const f32x4*>(dSf + (sg * H + h) * DV * DK)[dfrag_index(rblk, w, lane, NW)];
         x.gam = gdecay[(sg * H + h) * DV + r];
     };
-
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     auto step = [&](const Next& x, int g) {
         if (g > 0) *reinterpret_cast<f32x4*>(S_start + (seg_of(g) * H + h) * DV * DK + row_off) = s;
@@ -117,8 +173,8 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
             const u32x4 t0 = X[g & 1][2 * kb][lane], t1 = X[g & 1][2 * kb + 1][lane];
             const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t1[0], t1[1]});
             const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{t0[2], t0[3], t1[2], t1[3]});
-            const bf16x8 a_hi = __builtin_bit_cast(bf16x8, x.m[kb][0]);
-            const bf16x8 a_lo = __builtin_bit_cast(bf16x8, x.m[kb][1]);
+            const bf16x8 a_hi = __builtin_bit_cast(bf16x8, MB[g & 1][(kb * 2 + 0) * NW + w][lane]);
+            const bf16x8 a_lo = __builtin_bit_cast(bf16x8, MB[g & 1][(kb * 2 + 1) * NW + w][lane]);
             acc = mfma16(a_lo, bh, acc);
             acc = mfma16(a_hi, bl, acc);
             acc = mfma16(a_hi, bh, acc);
@@ -126,16 +182,6 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) s[j] = x.gam * acc[j] + x.d[j];
     };
-    // Two sets of next-segment values in flight: segment g uses set g & 1, which is
-    // refilled with segment g + 2 once the step has consumed it.  The loop's first
-    // pass only loads (one load site per set, so the wait counts are the same on
-    // every pass) and takes the entering state and the range marks in (its store
-    // waits for them there, not at the top of a later pass).  The loads are
-    // unconditional (the last ones reread segment G - 1), so the sets stay in their
-    // registers instead of being copied, which would wait for them.  The scheduling
-    // barriers keep each reload after the step that reads the set: hoisted above it,
-    // the step splits the set early and so waits for both sets.  (Deeper prefetch
-    // measured slower: a step is bound by the CU's vector-memory issue, not latency.)
     Next xa, xb;
     bool beyond = false;  // a segment of these rows is marked beyond the decay range
     for (int g = -2; g < G; g += 2) {
@@ -148,7 +194,8 @@ __global__ __launch_bounds__(64 * (DK / 16)) void combine_segments_kernel(
         load(xb, min(g + 3, G - 1));
         __builtin_amdgcn_sched_barrier(0);
         if (g < 0) {
-            // the segments' range marks, one per lane (read together, not one after another)
+            // the segments' range marks, one per lane (read together, not one after another),
+            // and the entering state (the store waits for both here, not at a later pass)
             bool mark = false;
             if (range_flags) {
                 const int vb = (rblk * 16) / 64;  // the scan's block of 64 rows that holds these rows
@@ -168,12 +215,12 @@ hipError_t launch_combine_segments(const float* gdecay, const float* S0, const f
                                    const int32_t* range_flags, int n_seq, int G, int n_heads, float* S_start,
                                    float* S_T, const SegmentFixupArgs& fx, hipStream_t stream) {
     if (G < 2 || G % 2) return hipErrorInvalidValue;
-    constexpr int FR = DK == 128 ? 64 : 16;
+    using SH = CombineShape<DK>;
     const int64_t n_comp = (static_cast<int64_t>(n_seq) * n_heads + 7) / 8 * 8 * (DV / 16);
-    const int64_t n_fix = range_flags ? prefill_grid(static_cast<int64_t>(n_seq) * n_heads, DV / FR) : 0;
+    const int64_t n_fix = range_flags ? prefill_grid(static_cast<int64_t>(n_seq) * n_heads, DV / SH::FR) : 0;
     hipLaunchKernelGGL((combine_segments_kernel<DK, DV, GATE>), dim3(static_cast<unsigned>(n_comp + n_fix)),
-                       dim3(64 * (DK / 16)), 0, stream, gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start,
-                       S_T, fx);
+                       dim3(SH::NT), 0, stream, gdecay, S0, dSf, Mf, range_flags, n_seq, G, n_heads, S_start, S_T,
+                       fx);
     return hipGetLastError();
 }
 

@@ -88,9 +88,11 @@ __device__ __forceinline__ float sum_lanes(float x) {
 // recomputation after the chunked bf16 scan, launch_prefill_range_fixup); a
 // workgroup returns at once unless one of the flag_segs segments of its
 // sequence is marked for its block of 64 value rows.
+// buf: the two LDS staging buffers (the caller's, so that a kernel with other work can
+// share its LDS with them).
 template <typename T, int DK, int DV, int GATE, int R, int L, bool CKPT>
 __device__ __forceinline__ void prefill_staged_body(
-    int64_t block, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    StageBuf<DK, GATE, R>* buf, int64_t block, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int n_seq, int n_tok, int n_heads,
@@ -104,7 +106,6 @@ __device__ __forceinline__ void prefill_staged_body(
     constexpr int VN = TB * R / 4;           // float4 groups of v (value-channel gates) per block
     constexpr int VG = (VN + NT - 1) / NT;
     static_assert(2 * TB <= NT && DV % R == 0, "staging shape");
-    __shared__ StageBuf<DK, GATE, R> buf[2];
 
     const Unit u = map_unit(block, n_seq, n_heads, DV / R, n_tok, cu_seqlens, order);
     if (!u.valid) return;
