@@ -45,6 +45,16 @@ constexpr int LP = C + 4;              // pitch of fp32 rows of length C
 constexpr int A_BLOCK_ELEMS = 32 * 32;
 constexpr int A_RECORD_BYTES = 3 * 2 * A_BLOCK_ELEMS * 2;
 constexpr int A_RECORD_PIECES = A_RECORD_BYTES / 16;  // 16-byte pieces
+// The records of the 32-token scan hold blocks 0 and 2 only, each packed: of a block's
+// 32 rows x 4 pieces of 8 columns, the 80 pieces that reach the diagonal (8 c <= row), in
+// bands of 8 rows (band r / 8 has r / 8 + 1 pieces a row), the hi pieces then the lo
+// pieces.  The all-zero pieces above the diagonal are neither written nor read.
+constexpr int A_TRI_PIECES = 80;
+constexpr int A_TRI_BLOCK_ELEMS = 2 * A_TRI_PIECES * 8;            // hi + lo, bf16
+constexpr int A_TRI_RECORD_BYTES = 2 * A_TRI_BLOCK_ELEMS * 2;      // blocks 0 and 2
+__host__ __device__ constexpr int tri_piece(int row, int c) {
+    return 8 * ((row >> 3) * ((row >> 3) + 1) / 2) + (row & 7) * ((row >> 3) + 1) + c;
+}
 // word 3 of a gfx9 buffer resource: raw (untyped) 32-bit data
 constexpr int kBufferWord3 = 0x00020000;
 

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(256) void segment_cu_kernel(const int32_t* __restri
 // blocks per head): the backward divides by beta there and leaves such units to
 // its token-recurrent pass.
 // HALVES (the 32-token scan): only the two diagonal 32x32 blocks of each record, the
-// solved systems of the chunk's two halves; block 1 is neither formed nor written.
+// solved systems of the chunk's two halves, packed (A_TRI_RECORD_BYTES a record); block
+// 1 is neither formed nor written.
 template <int DK, bool STORE_T = false, bool HALVES = false>
 __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     const uint16_t* __restrict__ k, const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256, 4) void chunk_solve_kernel(
     assemble_inverse<HALVES>(Xs, Lf, Rtmp, x, wave, lane);
 
     // ---- A = X diag(beta) -> the record (STORE_T: X itself -> the second record)
-    const int64_t rec_off = (static_cast<int64_t>(gc) * n_heads + h) * (A_RECORD_BYTES / 2);
+    const int64_t rec_off = (static_cast<int64_t>(gc) * n_heads + h) * ((HALVES ? A_TRI_RECORD_BYTES : A_RECORD_BYTES) / 2);
     write_solve_record<true, HALVES>(arec + rec_off, Xs, bs, tid);
     if constexpr (STORE_T) write_solve_record<false, HALVES>(trec + rec_off, Xs, bs, tid);
     block_sync();  // X, read above, shares its space with the next item's K

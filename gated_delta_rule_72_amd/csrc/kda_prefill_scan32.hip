@@ -259,11 +259,20 @@ __device__ __forceinline__ void scan32_body(
                 R[b0 + LQ + p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_, off, 0, 0));
         }
         // block 2 (s % 2) of the chunk's record: rows 0-31 x cols 0-31 for the first
-        // half, rows 32-63 x cols 32-63 for the second; each block is hi then lo
-        const uint16_t* blk = arec + (static_cast<int64_t>(chunk0 + sc / 2) * n_heads + h) * (A_RECORD_BYTES / 2) +
-                              (sc & 1) * 2 * (2 * A_BLOCK_ELEMS);
-        const auto ra_ = make_rsrc(blk, any ? 2 * A_BLOCK_ELEMS * 2 : 0);
-        R[b0 + LA] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, ht * 16, 0, 0));
+        // half, rows 32-63 x cols 32-63 for the second; each block is hi then lo.  The
+        // forward's records are packed (pieces above the diagonal left out: those threads
+        // read past the range, which returns zero); the backward's are whole.
+        constexpr bool TRI = !CKPT;
+        const int64_t rec = static_cast<int64_t>(chunk0 + sc / 2) * n_heads + h;
+        const uint16_t* blk = TRI ? arec + rec * (A_TRI_RECORD_BYTES / 2) + (sc & 1) * A_TRI_BLOCK_ELEMS
+                                  : arec + rec * (A_RECORD_BYTES / 2) + (sc & 1) * 2 * (2 * A_BLOCK_ELEMS);
+        constexpr int blk_bytes = TRI ? A_TRI_BLOCK_ELEMS * 2 : 2 * A_BLOCK_ELEMS * 2;
+        const auto ra_ = make_rsrc(blk, any ? blk_bytes : 0);
+        const int pc = ht & 3, prow = (ht >> 2) & 31;
+        const int aoff = !TRI ? ht * 16
+                         : pc > (prow >> 3) ? blk_bytes
+                                            : ((ht >> 7) * A_TRI_PIECES + tri_piece(prow, pc)) * 16;
+        R[b0 + LA] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, aoff, 0, 0));
     };
     auto fetch_vl = [&](int s, int x) {
         const int n = step_len(s);

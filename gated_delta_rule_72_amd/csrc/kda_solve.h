@@ -155,13 +155,14 @@ __device__ __forceinline__ void assemble_inverse(float* Xs, const float* Lf, flo
 
 // X (SCALE_BETA: X diag(beta)) -> the solved record at rec, by all 256 threads.
 // Item = (block, row, 8-column piece); entries above the diagonal (never
-// written in Xs) are selected away.  HALVES: blocks 0 and 2 only (block 1 is
-// left unwritten).
+// written in Xs) are selected away.  HALVES: blocks 0 and 2 only, in the packed
+// form of the 32-token scan's records (pieces above the diagonal left out).
 template <bool SCALE_BETA, bool HALVES = false>
 __device__ __forceinline__ void write_solve_record(uint16_t* rec, const float* Xs, const float* bs, int tid) {
     constexpr int NB = HALVES ? 2 : 3;
     for (int item = tid; item < NB * 32 * 4; item += 256) {
         const int blk = HALVES ? 2 * (item >> 7) : item >> 7, row = (item >> 2) & 31, c8 = 8 * (item & 3);
+        if (HALVES && (item & 3) > (row >> 3)) continue;  // all zero, not stored
         const int t = (blk == 0 ? 0 : 32) + row, s0 = (blk == 2 ? 32 : 0) + c8;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(Xs + t * LP + s0 + 4);
@@ -181,9 +182,15 @@ __device__ __forceinline__ void write_solve_record(uint16_t* rec, const float* X
             wh[e] = a;
             wl[e] = b;
         }
-        uint16_t* dst = rec + blk * 2 * A_BLOCK_ELEMS + row * 32 + c8;
-        *reinterpret_cast<u32x4*>(dst) = wh;
-        *reinterpret_cast<u32x4*>(dst + A_BLOCK_ELEMS) = wl;
+        if constexpr (HALVES) {
+            uint16_t* dst = rec + (item >> 7) * A_TRI_BLOCK_ELEMS + tri_piece(row, item & 3) * 8;
+            *reinterpret_cast<u32x4*>(dst) = wh;
+            *reinterpret_cast<u32x4*>(dst + A_TRI_PIECES * 8) = wl;
+        } else {
+            uint16_t* dst = rec + blk * 2 * A_BLOCK_ELEMS + row * 32 + c8;
+            *reinterpret_cast<u32x4*>(dst) = wh;
+            *reinterpret_cast<u32x4*>(dst + A_BLOCK_ELEMS) = wl;
+        }
     }
 }
 
