@@ -221,8 +221,12 @@ __global__ __launch_bounds__(512) void bwd_state_scan_kernel(
         const uint16_t* recp = trec + (static_cast<int64_t>(chunk0 + (c < 0 ? 0 : c)) * n_heads + h) * (A_RECORD_BYTES / 2);
         const auto rr_ = make_rsrc(recp, n > 0 ? A_RECORD_BYTES : 0);
 #pragma unroll
-        for (int p = 0; p < NREC; ++p)
-            rr(p) = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr_, (htid + 256 * p) * 16, 0, 0));
+        for (int p = 0; p < NREC; ++p) {
+            // (an all-zero piece reads past the range: zero, no memory traffic)
+            const int pc = htid + 256 * p;
+            const int off = record_piece_zero(pc) ? A_RECORD_BYTES : pc * 16;
+            rr(p) = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr_, off, 0, 0));
+        }
         const auto rb_ = make_rsrc(beta + tok0, n > 0 ? ((n - 1) * H + 1) * 4 : 0);
         RR[OB][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, static_cast<int>(lane * H) * 4, 0, 0));
     };
@@ -533,7 +537,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_grad_kernel(
         const auto rr_ = make_rsrc(trec + (static_cast<int64_t>(x.gc) * n_heads + x.h) * (A_RECORD_BYTES / 2),
                                    valid ? A_RECORD_BYTES : 0);
 #pragma unroll
-        for (int p = 0; p < NRP; ++p) prec[p] = __builtin_amdgcn_raw_buffer_load_b128(rr_, (tid + 512 * p) * 16, 0, 0);
+        for (int p = 0; p < NRP; ++p) {
+            // (all-zero pieces and pieces past the record read past the range: zero)
+            const int pc = tid + 512 * p;
+            const int off = pc >= A_RECORD_PIECES || record_piece_zero(pc) ? A_RECORD_BYTES : pc * 16;
+            prec[p] = __builtin_amdgcn_raw_buffer_load_b128(rr_, off, 0, 0);
+        }
         const auto rb_ = make_rsrc(beta + x.tok0, nn > 0 ? ((nn - 1) * H + 1) * 4 : 0);
         pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb_, static_cast<int>(tid * H) * 4, 0, 0));
         // alpha at token rows t = 8 w + r, value rows i = lane + 64 xv

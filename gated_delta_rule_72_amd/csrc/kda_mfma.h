@@ -52,6 +52,11 @@ constexpr int A_RECORD_PIECES = A_RECORD_BYTES / 16;  // 16-byte pieces
 constexpr int A_TRI_PIECES = 80;
 constexpr int A_TRI_BLOCK_ELEMS = 2 * A_TRI_PIECES * 8;            // hi + lo, bf16
 constexpr int A_TRI_RECORD_BYTES = 2 * A_TRI_BLOCK_ELEMS * 2;      // blocks 0 and 2
+// Piece p of a whole record (block p / 256, hi or lo, row (p / 4) % 32, 8 columns
+// 8 (p % 4) ..) lies entirely above the diagonal of a diagonal block: always zero.
+__host__ __device__ constexpr bool record_piece_zero(int p) {
+    return (p >> 8) != 1 && (p & 3) > (((p >> 2) & 31) >> 3);
+}
 __host__ __device__ constexpr int tri_piece(int row, int c) {
     return 8 * ((row >> 3) * ((row >> 3) + 1) / 2) + (row & 7) * ((row >> 3) + 1) + c;
 }

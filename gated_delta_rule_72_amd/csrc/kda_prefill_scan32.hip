@@ -260,8 +260,9 @@ __device__ __forceinline__ void scan32_body(
         }
         // block 2 (s % 2) of the chunk's record: rows 0-31 x cols 0-31 for the first
         // half, rows 32-63 x cols 32-63 for the second; each block is hi then lo.  The
-        // forward's records are packed (pieces above the diagonal left out: those threads
-        // read past the range, which returns zero); the backward's are whole.
+        // forward's records are packed (pieces above the diagonal left out), the backward's
+        // whole; either way the threads of all-zero pieces read past the range, which
+        // returns zero without touching memory.
         constexpr bool TRI = !CKPT;
         const int64_t rec = static_cast<int64_t>(chunk0 + sc / 2) * n_heads + h;
         const uint16_t* blk = TRI ? arec + rec * (A_TRI_RECORD_BYTES / 2) + (sc & 1) * A_TRI_BLOCK_ELEMS
@@ -269,9 +270,9 @@ __device__ __forceinline__ void scan32_body(
         constexpr int blk_bytes = TRI ? A_TRI_BLOCK_ELEMS * 2 : 2 * A_BLOCK_ELEMS * 2;
         const auto ra_ = make_rsrc(blk, any ? blk_bytes : 0);
         const int pc = ht & 3, prow = (ht >> 2) & 31;
-        const int aoff = !TRI ? ht * 16
-                         : pc > (prow >> 3) ? blk_bytes
-                                            : ((ht >> 7) * A_TRI_PIECES + tri_piece(prow, pc)) * 16;
+        const int aoff = pc > (prow >> 3) ? blk_bytes
+                         : TRI             ? ((ht >> 7) * A_TRI_PIECES + tri_piece(prow, pc)) * 16
+                                           : ht * 16;
         R[b0 + LA] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_, aoff, 0, 0));
     };
     auto fetch_vl = [&](int s, int x) {
